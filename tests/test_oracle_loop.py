@@ -1,0 +1,340 @@
+"""Whole-loop pins of the oracle: brute force, closed forms and the pages'
+invariants (MolmoBot PR "Correctness" table; LoongForge blog section 1).
+
+* brute force: a scalar pure-Python twin with an explicit [T, P+T] visibility
+  mask and -inf logits (the oracle instead drops masked rows);
+* Euler closed form: a constant-velocity head gives x_N = x_0 + N dt v = x_0 - v;
+* zero gates: with the gate chunks of every modulation zeroed the residual
+  stream never changes, so each step is a closed-form map of x;
+* masked / padded / pruned prefix rows leave the actions unchanged;
+* context K/V projected once == re-projected every step;
+* batched requests == each request alone;
+* the prefix matters: redrawing it moves the actions by far more than the
+  GPU parity tolerance, so the tolerance-level checks are not vacuous.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import ae_oracle as O
+from vla_flow_matching_amd import synth
+
+
+def tiny(**kw):
+    base = dict(n_layers=2, width=8, n_q_heads=2, n_kv_heads=1, head_dim=4, mlp_dim=6,
+                action_horizon=3, action_dim=2, n_steps=2, batch=2, prefix_len=5,
+                dtype="f32", proj_dtype="same", index=9)
+    base.update(kw)
+    return synth.Workload("tiny", **base)
+
+
+def small_c2(layers=2, steps=2, batch=1, **kw):
+    return synth.workload("c2", n_layers=layers, n_steps=steps, batch=batch, **kw)
+
+
+def run(w, W, K, V, m, x0, fp8=False):
+    return O.Expert(W, O.Params.like(w, fp8=fp8)).denoise(x0, K, V, m, w.n_steps)
+
+
+# --------------------------------------------------------------------------
+# Brute-force scalar twin
+# --------------------------------------------------------------------------
+
+def _bf_denoise(w, W, K, V, mask, x0):
+    """Scalar loops only; explicit visibility mask; independent of the oracle."""
+    L, D, Hq, Hkv, dh, Fd = w.n_layers, w.width, w.n_q_heads, w.n_kv_heads, w.head_dim, w.mlp_dim
+    T, A, N, B, P = w.action_horizon, w.action_dim, w.n_steps, w.batch, w.prefix_len
+    g = lambda name: np.asarray(W[name], dtype=np.float64)
+
+    def mv(vec, mat, bias=None):  # vec [in] @ mat [in, out]
+        out = [0.0] * mat.shape[1]
+        for j in range(mat.shape[1]):
+            acc = 0.0
+            for i in range(mat.shape[0]):
+                acc += vec[i] * mat[i, j]
+            out[j] = acc + (0.0 if bias is None else bias[j])
+        return out
+
+    def silu(z):
+        return z / (1.0 + math.exp(-z))
+
+    def norm(vec, scale, shift):
+        ms = sum(v * v for v in vec) / len(vec)
+        r = 1.0 / math.sqrt(ms + w.rms_eps)
+        return [vec[i] * r * (1.0 + scale[i]) + shift[i] for i in range(len(vec))]
+
+    def rot(vec, p):
+        half = len(vec) // 2
+        out = list(vec)
+        for j in range(half):
+            ang = p * w.rope_theta ** (-2.0 * j / len(vec))
+            a, b = vec[j], vec[j + half]
+            out[j] = a * math.cos(ang) - b * math.sin(ang)
+            out[j + half] = b * math.cos(ang) + a * math.sin(ang)
+        return out
+
+    x = [[[float(x0[b, i, a]) for a in range(A)] for i in range(T)] for b in range(B)]
+    for k in range(N):
+        t = 1.0 - k / N
+        half = D // 2
+        e = [0.0] * D
+        for i in range(half):
+            period = 4e-3 * (4.0 / 4e-3) ** (i / (half - 1))
+            e[i] = math.sin(2 * math.pi * t / period)
+            e[half + i] = math.cos(2 * math.pi * t / period)
+        c = [silu(z) for z in mv([silu(z) for z in mv(e, g("time_mlp.1.w"), g("time_mlp.1.b"))],
+                                 g("time_mlp.2.w"), g("time_mlp.2.b"))]
+        for b in range(B):
+            nv = int(sum(int(mask[b, j] != 0) for j in range(P)))
+            h = [mv(x[b][i], g("action_in.w"), g("action_in.b")) for i in range(T)]
+            for l in range(L):
+                mod = mv(c, g(f"layers.{l}.mod.w"), g(f"layers.{l}.mod.b"))
+                ch = [mod[j * D:(j + 1) * D] for j in range(6)]
+                u = [norm(h[i], ch[0], ch[1]) for i in range(T)]
+                qs = [mv(u[i], g(f"layers.{l}.q")) for i in range(T)]
+                ks = [mv(u[i], g(f"layers.{l}.k")) for i in range(T)]
+                vs = [mv(u[i], g(f"layers.{l}.v")) for i in range(T)]
+                o = [[0.0] * (Hq * dh) for _ in range(T)]
+                for hd in range(Hq):
+                    kv = hd // (Hq // Hkv)
+                    # all P + T keys, visibility by mask
+                    keys, vals, vis = [], [], []
+                    for j in range(P):
+                        keys.append([float(K[l, b, j, kv, d]) for d in range(dh)])
+                        vals.append([float(V[l, b, j, kv, d]) for d in range(dh)])
+                        vis.append(mask[b, j] != 0)
+                    for j in range(T):
+                        keys.append(rot(ks[j][kv * dh:(kv + 1) * dh], nv + j))
+                        vals.append(vs[j][kv * dh:(kv + 1) * dh])
+                        vis.append(True)
+                    for i in range(T):
+                        qv = rot(qs[i][hd * dh:(hd + 1) * dh], nv + i)
+                        logits = []
+                        for j in range(P + T):
+                            if vis[j]:
+                                logits.append(sum(qv[d] * keys[j][d] for d in range(dh)) / math.sqrt(dh))
+                            else:
+                                logits.append(-math.inf)
+                        mx = max(logits)
+                        ws = [math.exp(s - mx) if s != -math.inf else 0.0 for s in logits]
+                        tot = sum(ws)
+                        for d in range(dh):
+                            acc = 0.0
+                            for j in range(P + T):
+                                if ws[j] != 0.0:
+                                    acc += ws[j] * vals[j][d]
+                            o[i][hd * dh + d] = acc / tot
+                for i in range(T):
+                    ob = mv(o[i], g(f"layers.{l}.o"))
+                    h[i] = [h[i][d] + ch[2][d] * ob[d] for d in range(D)]
+                for i in range(T):
+                    u2 = norm(h[i], ch[3], ch[4])
+                    gt = mv(u2, g(f"layers.{l}.gate"))
+                    up = mv(u2, g(f"layers.{l}.up"))
+                    act = [0.5 * gt[f] * (1 + math.tanh(math.sqrt(2 / math.pi) * (gt[f] + 0.044715 * gt[f] ** 3))) * up[f]
+                           for f in range(Fd)]
+                    dn = mv(act, g(f"layers.{l}.down"))
+                    h[i] = [h[i][d] + ch[5][d] * dn[d] for d in range(D)]
+            fm = mv(c, g("final_mod.w"), g("final_mod.b"))
+            for i in range(T):
+                vv = mv(norm(h[i], fm[:D], fm[D:]), g("action_out.w"), g("action_out.b"))
+                x[b][i] = [x[b][i][a] - vv[a] / N for a in range(A)]
+    return np.array(x)
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 1), (4, 2)])
+def test_oracle_matches_brute_force(hq, hkv):
+    w = tiny(n_q_heads=hq, n_kv_heads=hkv, width=8 if hq == 2 else 16)
+    W = synth.make_weights(w, std=0.3)
+    mask = np.array([[1, 0, 1, 1, 0], [0, 1, 1, 1, 1]], np.uint8)
+    K, V, _ = synth.make_prefix(w, mask=mask, garbage="huge")
+    x0 = synth.make_noise(w)
+    ours = run(w, W, K, V, mask, x0)
+    ref = _bf_denoise(w, W, K, V, mask, x0)
+    assert np.abs(ours - x0).max() > 0.05  # the loop moved the actions
+    assert np.allclose(ours, ref, rtol=0, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c1", "c2small"])
+def test_constant_velocity_head_euler_closed_form(name):
+    w = synth.workload("c1") if name == "c1" else small_c2()
+    W = synth.make_weights(w)
+    vel = np.random.default_rng(7).standard_normal(w.action_dim)
+    W["action_out.w"] = np.zeros_like(W["action_out.w"])
+    W["action_out.b"] = vel.astype(np.float32)
+    K, V, m = synth.make_prefix(w)
+    x0 = synth.make_noise(w)
+    xN = run(w, W, K, V, m, x0)
+    # x_N = x_0 + N * dt * v = x_0 - v
+    assert np.allclose(xN, x0 - vel.astype(np.float32).astype(np.float64), rtol=0, atol=1e-14)
+
+
+def test_zero_gates_closed_form():
+    w = synth.workload("c1")
+    W = synth.make_weights(w)
+    D = w.width
+    for l in range(w.n_layers):
+        for ch in (2, 5):
+            W[f"layers.{l}.mod.w"][:, ch * D:(ch + 1) * D] = 0
+            W[f"layers.{l}.mod.b"][ch * D:(ch + 1) * D] = 0
+    K, V, m = synth.make_prefix(w)
+    x0 = synth.make_noise(w)
+    xN = run(w, W, K, V, m, x0)
+    # independent recursion with torch float64 pieces: h = x W_in + b_in never
+    # changes through the layers, v = rms_norm(h) (1 + s_f) + sh_f, W_out, b_out
+    tt = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    x = tt(x0)
+    for k in range(w.n_steps):
+        t = 1.0 - k / w.n_steps
+        half = D // 2
+        i = torch.arange(half, dtype=torch.float64)
+        period = 4e-3 * 1000.0 ** (i / (half - 1))
+        e = torch.cat([torch.sin(2 * math.pi * t / period), torch.cos(2 * math.pi * t / period)])
+        c = F.silu(F.silu(e @ tt(W["time_mlp.1.w"]) + tt(W["time_mlp.1.b"])) @ tt(W["time_mlp.2.w"]) + tt(W["time_mlp.2.b"]))
+        fm = c @ tt(W["final_mod.w"]) + tt(W["final_mod.b"])
+        h = x @ tt(W["action_in.w"]) + tt(W["action_in.b"])
+        u = F.rms_norm(h, (D,), eps=1e-6) * (1 + fm[:D]) + fm[D:]
+        x = x - (u @ tt(W["action_out.w"]) + tt(W["action_out.b"])) / w.n_steps
+    assert np.allclose(xN, x.numpy(), rtol=0, atol=1e-13)
+    # and the prefix is then irrelevant
+    K2, V2, _ = synth.make_prefix(w, mask=m, seed=4242)
+    assert np.array_equal(run(w, W, K2, V2, m, x0), xN)
+
+
+# --------------------------------------------------------------------------
+# Invariants (pages' correctness properties)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["huge", "nan", "inf"])
+def test_masked_rows_are_invisible(kind):
+    w = synth.workload("c1")
+    W = synth.make_weights(w)
+    K, V, m = synth.make_prefix(w)
+    x0 = synth.make_noise(w)
+    base = run(w, W, K, V, m, x0)
+    Kg, Vg = K.copy(), V.copy()
+    synth.fill_garbage(w, Kg, Vg, m, kind)
+    assert not np.array_equal(Kg, K)
+    assert np.array_equal(run(w, W, Kg, Vg, m, x0), base)
+
+
+def test_padding_is_invisible():
+    """MolmoBot PR Part 1: padding the prefix to a fixed length changes nothing."""
+    w = synth.workload("c1")
+    W = synth.make_weights(w)
+    K, V, m = synth.make_prefix(w)
+    x0 = synth.make_noise(w)
+    base = run(w, W, K, V, m, x0)
+    w2 = synth.workload("c1", prefix_len=160)
+    K2 = np.full((w.n_layers, 1, 160, 1, 64), np.nan, np.float32)
+    V2 = np.full_like(K2, np.nan)
+    K2[:, :, :64], V2[:, :, :64] = K, V
+    m2 = np.zeros((1, 160), np.uint8)
+    m2[:, :64] = m
+    assert np.array_equal(run(w2, W, K2, V2, m2, x0), base)
+
+
+@pytest.mark.parametrize("slot", [2, 1])
+def test_masked_camera_slot_equals_pruned(slot):
+    """LoongForge blog section 1: a masked 256-row camera slot (at the end of
+    the image block, or in the middle of it) gives the same actions as the
+    prefix with the slot pruned, since pads do not advance positions."""
+    w2 = small_c2(layers=2, steps=2)
+    w3 = synth.workload("c3", n_layers=2, n_steps=2)
+    W = synth.make_weights(w2)
+    K2, V2, m2 = synth.make_prefix(w2)
+    K3, V3, m3 = synth.insert_camera_slot(w3, K2, V2, m2, slot=slot)
+    x0 = synth.make_noise(w2)
+    a2 = run(w2, W, K2, V2, m2, x0)
+    a3 = run(w3, W, K3, V3, m3, x0)
+    assert m3.sum() == m2.sum()
+    assert np.array_equal(a2, a3)
+
+
+def test_kv_projected_once_equals_reprojected_every_step():
+    """MolmoBot PR Part 2 / Correctness: the per-query context K/V cache is
+    bitwise equal to re-projecting the context on every flow step."""
+    w = synth.workload("c1")
+    W = synth.make_weights(w)
+    rng = np.random.default_rng(77)
+    Dc = 96
+    hidden = [rng.standard_normal((1, w.prefix_len, Dc)) for _ in range(w.n_layers)]
+    wk = [rng.standard_normal((Dc, 64)) * 0.1 for _ in range(w.n_layers)]
+    wv = [rng.standard_normal((Dc, 64)) * 0.1 for _ in range(w.n_layers)]
+    m = synth.valid_masks(w)
+    m[0, 5] = 0  # a hole in the middle: positions must skip it
+    KV = [O.project_prefix_kv(hidden[l], wk[l], wv[l], m, 1, 10000.0) for l in range(w.n_layers)]
+    K = np.stack([k for k, _ in KV])
+    V = np.stack([v for _, v in KV])
+    x0 = synth.make_noise(w)
+    E = O.Expert(synth.make_weights(w), O.Params.like(w))
+    once = E.denoise(x0, K, V, m, w.n_steps)
+    calls = []
+
+    def reproject(l, b):
+        calls.append((l, b))
+        k, v = O.project_prefix_kv(hidden[l], wk[l], wv[l], m, 1, 10000.0)
+        idx = np.nonzero(m[b])[0]
+        return k[b, idx], v[b, idx]
+
+    every = E.integrate(x0, reproject, m.sum(1), w.n_steps)
+    assert len(calls) == w.n_steps * w.n_layers
+    assert np.array_equal(once, every)
+    # positions of the prefix skip the masked row
+    pos = O.prefix_positions(m[0])
+    assert pos[4] == 4 and pos[6] == 5
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_batched_equals_unbatched(fp8):
+    w = small_c2(layers=2, steps=2, batch=3)
+    w = synth.Workload(**{**w.__dict__, "name": "c5", "prefix_len": 640})
+    W = synth.make_weights(w)
+    m = synth.valid_masks(w, n_valid=(640, 521, 600))
+    K, V, _ = synth.make_prefix(w, mask=m, garbage="nan")
+    x0 = synth.make_noise(w)
+    batched = run(w, W, K, V, m, x0, fp8=fp8)
+    w1 = synth.Workload(**{**w.__dict__, "batch": 1})
+    for b in range(3):
+        alone = run(w1, W, K[:, b:b + 1], V[:, b:b + 1], m[b:b + 1], x0[b:b + 1], fp8=fp8)
+        # numpy's stacked matmul may block rows differently: rounding-level only
+        assert np.allclose(batched[b:b + 1], alone, rtol=0, atol=1e-12)
+
+
+def test_fp8_close_to_bf16():
+    """Context: MolmoBot PR Part 3 reports 0.39 % max / 0.11 % mean action
+    delta for fp8 on the LLM blocks.  Quantising this expert's QKV / MLP
+    weights and inputs moves the actions by a few percent at most."""
+    w = small_c2(layers=4, steps=4)
+    W = synth.make_weights(w)
+    K, V, m = synth.make_prefix(w)
+    x0 = synth.make_noise(w)
+    a = run(w, W, K, V, m, x0)
+    b = run(w, W, K, V, m, x0, fp8=True)
+    d = np.abs(a - b)
+    assert 0 < d.max() < 0.1 * np.abs(a).max()
+
+
+@pytest.mark.slow
+def test_prefix_matters_at_full_size():
+    """Guard: at the full Pi0.5-shaped (c2) and MolmoBot-shaped (c4) sizes,
+    redrawing every visible prefix row moves the actions by more than five
+    times the 2e-2 parity tolerance."""
+    for name in ("c2", "c4"):
+        w = synth.workload(name)
+        W = synth.make_weights(w)
+        K, V, m = synth.make_prefix(w)
+        x0 = synth.make_noise(w)
+        E = O.Expert(W, O.Params.like(w))
+        a = E.denoise(x0, K, V, m, w.n_steps)
+        K2, V2, _ = synth.make_prefix(w, mask=m, seed=99)
+        b = E.denoise(x0, K2, V2, m, w.n_steps)
+        assert np.abs(a - b).max() > 0.1, name
