@@ -1,0 +1,186 @@
+"""Benchmark of the action-expert denoise loop on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A "step" here is one whole denoise call: the time path, N Euler steps of the
+layer stack with attention over the resident prefix K/V, and the action
+updates, for one batch of synthetic inputs already resident in HBM.  The
+headline is the Pi0.5-shaped batch-1 workload (c2): action chunks/s.  The
+batched workload (c5, 16 requests) is measured as well and reported under
+"secondary".  Rank 0 prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def algorithmic_work(w, n_valid):
+    """Bytes a denoise call must move and FLOPs it must do (masked / padded
+    prefix rows excluded; activations excluded: they stay in L2 / MALL)."""
+    D, L, F, A, T, N = w.width, w.n_layers, w.mlp_dim, w.action_dim, w.action_horizon, w.n_steps
+    qd, kd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    esz = 2 if w.dtype == "bf16" else 4
+    layer_params = D * (qd + 2 * kd) + qd * D + 2 * D * F + F * D
+    step_params = L * layer_params + 2 * A * D
+    t_params = 6 * L * D * D + 2 * D * D + 2 * D * D
+    kv_bytes = L * int(np.sum(n_valid)) * 2 * kd * esz
+    bytes_call = N * (step_params * esz + kv_bytes) + t_params * esz
+    B = len(n_valid)
+    attn_flops = sum(4 * T * w.n_q_heads * w.head_dim * (int(n) + T) for n in n_valid) * L * N
+    flops_call = 2 * B * T * step_params * N + attn_flops + 2 * N * t_params
+    return bytes_call, flops_call
+
+
+def run_gpu(name, steps, warmup):
+    import torch
+
+    from vla_flow_matching_amd import binding, synth
+
+    w = synth.workload(name)
+    W = synth.make_weights(w)
+    K, V, m = synth.make_prefix(w, garbage="nan")
+    x0 = synth.make_noise(w)
+    ex = binding.ActionExpert(binding.make_config(w))
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    ex.load_weights(binding.weights_to_device(W, w.dtype))
+    del W
+    Kt = torch.from_numpy(K).to("cuda", dt)
+    Vt = torch.from_numpy(V).to("cuda", dt)
+    del K, V
+    ex.set_prefix_kv(Kt, Vt, torch.from_numpy(m).cuda())
+    x = torch.from_numpy(x0).cuda()
+    out = torch.empty_like(x)
+    for _ in range(warmup):
+        ex.denoise(x, w.n_steps, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        ex.denoise(x, w.n_steps, out=out)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / steps
+    assert torch.isfinite(out).all().item()
+    st = ex.stats()
+    ex.close()
+    return w, m.sum(axis=1), ms, wall, st
+
+
+def cpu_baseline(name, budget_s):
+    """The oracle as it stands, on this host's cores, over a bounded sample
+    of whole denoise calls of the same workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import ae_oracle as O
+    from vla_flow_matching_amd import synth
+
+    w = synth.workload(name)
+    W = synth.make_weights(w)
+    K, V, m = synth.make_prefix(w)
+    x0 = synth.make_noise(w)
+    E = O.Expert(W, O.Params.like(w))
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        E.denoise(x0, K, V, m, w.n_steps)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 8:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": calls * w.batch / el, "unit": "chunks/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{calls} whole {w.name} denoise call(s) ({w.n_steps} steps, batch {w.batch}) "
+                      f"in {el:.1f} s, NumPy float64 with {threads} BLAS threads "
+                      f"on {os.cpu_count()} host CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--secondary", default="c5", help="batched workload, or 'none'")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the denoise path shards by request with no "
+              "exchange, and this build runs and reports a single GPU's throughput "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    w, n_valid, ms, wall, st = run_gpu(args.workload, args.steps, args.warmup)
+    bytes_call, flops_call = algorithmic_work(w, n_valid)
+    gbs = bytes_call / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "action chunks/s (10-step denoise) at batch 1; % HBM roofline",
+        "value": w.batch / (ms * 1e-3),
+        "unit": "chunks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded random-init weights, N(0,1) prefix K/V and noise)",
+        "config": {
+            "workload": f"{w.name}: Pi0.5-shaped action expert, {w.n_layers} layers, width {w.width}, "
+                        f"{w.n_q_heads}/{w.n_kv_heads} heads x {w.head_dim}, MLP {w.mlp_dim}, "
+                        f"batch {w.batch}, prefix {w.prefix_len} ({int(n_valid.sum())} visible), "
+                        f"{w.action_horizon}x{w.action_dim} actions, {w.n_steps} Euler steps",
+            "batch": w.batch, "n_steps": w.n_steps, "prefix_len": w.prefix_len,
+            "n_valid": [int(v) for v in n_valid],
+        },
+        "denoise_steps_per_s": w.n_steps / (ms * 1e-3),
+        "roofline": {
+            "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "whole denoise call (one hipGraph replay)",
+            "algorithmic_bytes_per_launch": bytes_call,
+        },
+        "graph": {"captures": st["graph_captures"], "replays": st["graph_replays"]},
+        "wall_s_timed": wall,
+    }
+    if args.secondary != "none":
+        sec_steps = max(5, args.steps // 8)
+        w5, nv5, ms5, _, _ = run_gpu(args.secondary, sec_steps, max(2, args.warmup // 4))
+        b5, f5 = algorithmic_work(w5, nv5)
+        tf = f5 / (ms5 * 1e-3) / 1e12
+        line["secondary"] = {
+            "workload": f"{w5.name}: batch {w5.batch}, prefix {w5.prefix_len} (mean "
+                        f"{float(nv5.mean()):.0f} visible), {w5.n_steps} steps, {w5.dtype}",
+            "value": w5.batch / (ms5 * 1e-3), "unit": "chunks/s", "ms_per_call": ms5,
+            "calls": sec_steps,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                         "algorithmic_flops_per_launch": f5},
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * ae.h -- C ABI of the MI355X (gfx950) action-expert denoise library.
+ *
+ * The library runs the flow-matching action-expert loop of a Pi0.5 /
+ * MolmoBot-style vision-language-action model: given the VLM prefix K/V that
+ * the caller has already computed once per query, it integrates an action
+ * chunk from noise with N explicit Euler steps.  Each step runs the expert's
+ * decoder layers (time-conditioned adaRMS norm, merged Q/K/V with RoPE,
+ * attention of the action tokens over [visible prefix K/V | their own K/V],
+ * gated residual, gelu-gated MLP, gated residual), then the final norm, the
+ * action-out projection and x += dt * v.
+ *
+ * Sources (titles as on the pages):
+ *  - MolmoBot PR "Inference optimization for MolmoBot VLA: torch.compile +
+ *    CUDA graphs + action-expert KV cache", Part 2: the context K/V is
+ *    projected once per query and reused by every flow step; only the action
+ *    queries and the timestep change between steps.  Part 3: per-tensor
+ *    dynamic fp8 e4m3 linears.
+ *  - LoongForge blog "How to Speed Up VLA Training Step by Step: A 3x
+ *    Acceleration Case Study on Pi0.5", sections 1-3: adaRMS with
+ *    scale/shift/gate, gated residuals, gelu*up, rotate_half RoPE, the
+ *    attention mask (actions see every valid prefix token and each other;
+ *    padding and empty camera slots are invisible; pads do not advance
+ *    positions), the single KV head broadcast to all query heads.
+ *  - sglang PR 34599 summary, implementation items 1-4: merged Q/K/V and
+ *    gate/up projections (shard order q, k, v), layout computed once per call,
+ *    mutable prefix K/V and mask refreshed before an action-graph replay.
+ *
+ * Conventions
+ *  - Every entry point returns an ae_status.  No exception crosses the ABI.
+ *  - Every argument and shape check happens before any state change or HIP
+ *    call: a call that fails with AE_ERR_INVALID_ARGUMENT,
+ *    AE_ERR_SHAPE_MISMATCH, AE_ERR_NOT_READY or AE_ERR_UNSUPPORTED leaves the
+ *    handle exactly as it was.  ae_last_error() gives the handle's message.
+ *  - Device pointers are HIP device memory (e.g. from torch on ROCm).
+ *    Streams are hipStream_t passed as void*; NULL means the default stream.
+ *    All work is stream-ordered and asynchronous: no call synchronises the
+ *    host except ae_create / ae_destroy.
+ *  - One stream per handle at a time; the library does no locking.
+ *  - Weight matrices are [in_features, out_features] row-major (y = x W + b).
+ */
+#ifndef AE_H
+#define AE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ae_handle ae_handle;
+
+typedef enum {
+  AE_OK = 0,
+  AE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad value, unknown/missing weight */
+  AE_ERR_SHAPE_MISMATCH = 2,   /* a shape disagrees with the config or earlier call */
+  AE_ERR_NOT_READY = 3,        /* weights or prefix not set yet */
+  AE_ERR_OUT_OF_MEMORY = 4,    /* device allocation failed (ae_create only) */
+  AE_ERR_UNSUPPORTED = 5,      /* a config the kernels do not implement */
+  AE_ERR_HIP = 6               /* a HIP runtime call failed (e.g. no GPU) */
+} ae_status;
+
+typedef enum { AE_F32 = 0, AE_BF16 = 1, AE_FP8_E4M3 = 2 } ae_dtype;
+
+/* Expert shape and numerics.  Fixed for the life of a handle. */
+typedef struct {
+  int n_layers;         /* decoder layers L */
+  int width;            /* residual width D (multiple of 64) */
+  int n_q_heads;        /* Hq */
+  int n_kv_heads;       /* Hkv, divides Hq; query head h reads KV head h*Hkv/Hq */
+  int head_dim;         /* dh, multiple of 32, at most 256 */
+  int mlp_dim;          /* F (multiple of 64); gate and up are each [D, F] */
+  int action_horizon;   /* T action tokens per request */
+  int action_dim;       /* A action channels, at most 64 */
+  int max_prefix_len;   /* largest prefix_len ae_set_prefix_kv accepts */
+  int max_batch;        /* largest batch (requests) */
+  int max_steps;        /* largest Euler step count ae_denoise accepts */
+  ae_dtype act_dtype;   /* AE_F32 or AE_BF16: weights, prefix K/V, activations */
+  ae_dtype proj_weight_dtype; /* act_dtype, or AE_FP8_E4M3 for the q/k/v,
+                                 gate/up and down projections (bf16 only) */
+  float rope_theta;     /* RoPE base (10000) */
+  float rms_eps;        /* adaRMS epsilon (1e-6) */
+  int use_graphs;       /* 1: replay each (batch, steps) loop as a hipGraph; 0: launch directly */
+} ae_config;
+
+/* One named logical weight, caller-owned device memory, dtype = act_dtype.
+ * Names (all required; l = 0..L-1):
+ *   time_mlp.1.w [D,D]  time_mlp.1.b [D]  time_mlp.2.w [D,D]  time_mlp.2.b [D]
+ *   action_in.w [A,D]   action_in.b [D]   action_out.w [D,A]  action_out.b [A]
+ *   final_mod.w [D,2D]  final_mod.b [2D]
+ *   layers.l.q [D,Hq*dh]  layers.l.k [D,Hkv*dh]  layers.l.v [D,Hkv*dh]
+ *   layers.l.o [Hq*dh,D]  layers.l.gate [D,F]  layers.l.up [D,F]  layers.l.down [F,D]
+ *   layers.l.mod.w [D,6D] layers.l.mod.b [6D]  (chunks: scale_a, shift_a,
+ *   gate_a, scale_m, shift_m, gate_m) */
+typedef struct {
+  const char* name;
+  const void* data;
+  int ndim;
+  long long shape[4];
+  ae_dtype dtype;
+} ae_tensor_view;
+
+typedef struct {
+  long long denoise_calls;
+  long long prefix_sets;
+  long long graph_captures;
+  long long graph_replays;
+  long long eager_runs;
+  long long device_bytes;    /* bytes the handle holds on the device */
+} ae_stats;
+
+/* Validate the config, then allocate every device buffer the handle will
+ * ever use (weights, prefix K/V at max size, activations, scratch).
+ * Errors: INVALID_ARGUMENT / UNSUPPORTED (before any HIP call), HIP (no
+ * device), OUT_OF_MEMORY.  On error *out is NULL. */
+ae_status ae_create(const ae_config* cfg, ae_handle** out);
+
+/* Copy and pack the named weights (merged q|k|v and gate|up in the kernels'
+ * fragment order; fp8 codes with a static per-tensor scale when configured).
+ * All n views are validated (names, ranks, shapes, dtypes) before anything is
+ * written.  The caller may free its tensors once the stream passes the call.
+ * Drops captured graphs (they read the packed buffers by address, which stay
+ * fixed, so this is only for hygiene). */
+ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* stream);
+
+/* Ingest one query's prefix: K and V are [L][batch][prefix_len][Hkv][dh] in
+ * act_dtype, K already rotated at the prefix's own positions (the VLM's KV
+ * cache); valid_mask is [batch][prefix_len] uint8 (0 = invisible: padding or
+ * an empty camera slot, any pattern).  Device pointers.  The library copies
+ * the visible rows, in order, into its static buffers and computes, on the
+ * device, each request's visible count n_b (the action tokens sit at
+ * positions n_b .. n_b+T-1) and RoPE tables.  Invisible rows are never read
+ * into arithmetic.  prefix_len may be 0 (K, V, mask may then be NULL).  The
+ * caller may reuse its buffers once the stream passes the call. */
+ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* K,
+                           const void* V, const uint8_t* valid_mask, void* stream);
+
+/* Integrate: x_0 = noise, x_{k+1} = x_k + dt * v(x_k, t_k), t_k = (N-k)/N,
+ * dt = -1/N, N = steps; writes x_N.  noise and actions_out are device
+ * [batch][T][A] fp32 and may alias.  batch must equal the last
+ * ae_set_prefix_kv batch.  Asynchronous on `stream`. */
+ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps,
+                     float* actions_out, void* stream);
+
+ae_status ae_get_stats(const ae_handle* h, ae_stats* out);
+const char* ae_last_error(const ae_handle* h);
+const char* ae_status_string(ae_status s);
+void ae_destroy(ae_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AE_H */

@@ -1,0 +1,88 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry
+point include/ae.h declares, rejects bad configs before touching HIP, and
+reports the missing device as AE_ERR_HIP."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from vla_flow_matching_amd import binding, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "ae.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:ae_status|const char\*|void)\s+(ae_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from vla_flow_matching_amd import build
+        build.build(verbose=False)
+    return binding.load()
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.ae_status_string(0) == b"ok"
+    assert lib.ae_status_string(2) == b"shape mismatch"
+    assert lib.ae_status_string(99) == b"unknown status"
+
+
+def _create(lib, **changes):
+    cfg = binding.make_config(synth.workload("c1"))
+    for k, v in changes.items():
+        setattr(cfg, k, v)
+    h = ctypes.c_void_p()
+    st = lib.ae_create(ctypes.byref(cfg), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_layers", 0), ("width", 100), ("width", 0), ("n_kv_heads", 3), ("mlp_dim", 48),
+    ("action_dim", 65), ("max_batch", 0), ("max_steps", 0), ("max_steps", 65),
+    ("max_prefix_len", -1), ("act_dtype", 7), ("rope_theta", 0.0), ("use_graphs", 2),
+])
+def test_invalid_config_rejected_before_hip(lib, field, value):
+    st, h = _create(lib, **{field: value})
+    assert st == binding.AE_ERR_INVALID_ARGUMENT
+    assert not h.value
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("head_dim", 32)])
+def test_unsupported_config(lib, field, value):
+    st, h = _create(lib, **{field: value})
+    assert st == binding.AE_ERR_UNSUPPORTED
+    assert not h.value
+
+
+def test_null_arguments(lib):
+    assert lib.ae_create(None, None) == binding.AE_ERR_INVALID_ARGUMENT
+    h = ctypes.c_void_p()
+    assert lib.ae_create(None, ctypes.byref(h)) == binding.AE_ERR_INVALID_ARGUMENT
+    assert lib.ae_load_weights(None, None, 0, None) == binding.AE_ERR_INVALID_ARGUMENT
+    assert lib.ae_set_prefix_kv(None, 1, 0, None, None, None, None) == binding.AE_ERR_INVALID_ARGUMENT
+    assert lib.ae_denoise(None, None, 1, 1, None, None) == binding.AE_ERR_INVALID_ARGUMENT
+    assert lib.ae_get_stats(None, None) == binding.AE_ERR_INVALID_ARGUMENT
+    lib.ae_destroy(None)
+
+
+def test_no_gpu_reports_hip_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, h = _create(lib)
+    assert st == binding.AE_ERR_HIP
+    assert not h.value

@@ -1,0 +1,162 @@
+// Device-side building blocks shared by the kernels: element types, the
+// 16x16 MFMA fragment conventions, conversions and cross-workgroup sync.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ae {
+
+typedef uint16_t bf16_t;  // storage type of bfloat16 values
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Conversions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf2f(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+// Element type traits: storage <-> fp32.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ float to_f(bf16_t v) { return bf2f(v); }
+  static __device__ __forceinline__ bf16_t from_f(float v) { return f2bf(v); }
+};
+
+// ---------------------------------------------------------------------------
+// 16x16 MFMA fragments.
+//
+// A fragment is 16 bytes per lane.  With E elements per lane (bf16: 8,
+// fp32: 4), one fragment covers a 16 x (4E) block: lane l holds row
+// (l % 16) and the E consecutive k indices 4E-block-local E*(l/16) .. +E-1.
+// The A operand (rows = output rows) and the B operand (rows = output
+// columns, i.e. B^T) use the same lane map, so any order in which the
+// hardware consumes the E values of a lane is matched on both sides.
+// The 16x16 fp32 result: lane l, element i -> row 4*(l/16)+i, column l%16.
+// ---------------------------------------------------------------------------
+
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16_t> {
+  static constexpr int E = 8;      // elements per lane per fragment
+  static constexpr int KSTEP = 32; // k covered by one fragment
+  static __device__ __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int E = 4;
+  static constexpr int KSTEP = 16;
+  // four 16x16x4 MFMAs, element i of every lane forming k-slice i
+  static __device__ __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    return c;
+  }
+};
+
+// Pack 8 fp32 values into a bf16 fragment, or 4 fp32 values into an fp32 one.
+__device__ __forceinline__ uint4 pack_frag_bf16(const float* v) {
+  uint4 r;
+  r.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+  r.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
+  r.z = static_cast<uint32_t>(f2bf(v[4])) | (static_cast<uint32_t>(f2bf(v[5])) << 16);
+  r.w = static_cast<uint32_t>(f2bf(v[6])) | (static_cast<uint32_t>(f2bf(v[7])) << 16);
+  return r;
+}
+
+__device__ __forceinline__ uint4 pack_frag_f32(const float* v) {
+  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3]));
+}
+
+template <typename T> __device__ __forceinline__ uint4 pack_frag(const float* v);
+template <> __device__ __forceinline__ uint4 pack_frag<bf16_t>(const float* v) { return pack_frag_bf16(v); }
+template <> __device__ __forceinline__ uint4 pack_frag<float>(const float* v) { return pack_frag_f32(v); }
+
+// Unpack a fragment into E fp32 values.
+template <typename T> __device__ __forceinline__ void unpack_frag(uint4 f, float* v);
+template <> __device__ __forceinline__ void unpack_frag<bf16_t>(uint4 f, float* v) {
+  const uint32_t w[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <> __device__ __forceinline__ void unpack_frag<float>(uint4 f, float* v) {
+  v[0] = __uint_as_float(f.x); v[1] = __uint_as_float(f.y);
+  v[2] = __uint_as_float(f.z); v[3] = __uint_as_float(f.w);
+}
+
+// ---------------------------------------------------------------------------
+// Reductions within a wave (64 lanes)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Sum over the 16 lanes sharing l / 16 (one "row" of a 16x16 fragment).
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup completion counting (split-K / split-KV fix-up).
+//
+// Every workgroup of a group publishes its partial, then arrives on the
+// group's counter; the last to arrive reduces all partials in a fixed order
+// (so the result does not depend on arrival order) and resets the counter to
+// zero for the next launch.  Returns true in every thread of the last one.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bool arrive_last(int* counter, int expected, int* s_flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int last = (old == expected - 1);
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  bool last = *s_flag != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * x * (1.0f + tanhf(k0 * (x + 0.044715f * x * x * x)));
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+}  // namespace ae

@@ -1,0 +1,113 @@
+// Host-side launch interface of the action-expert kernels (internal to the
+// library; the public surface is include/ae.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ae {
+
+enum Dt { DT_F32 = 0, DT_BF16 = 1 };
+
+// Prologue of a projection GEMM: A is a bf16/fp32 activation matrix, or the
+// fp32 residual h normalised on the fly by adaRMS.
+enum Prologue { PRO_NONE = 0, PRO_ADARMS = 1 };
+// Epilogue: RoPE + q / K-cache / V-cache scatter; gelu(gate) * up; gated
+// residual update of h (+ row sums of squares for the next adaRMS).
+enum Epilogue { EPI_QKV = 0, EPI_GELU = 1, EPI_RESID = 2 };
+// Column order of a packed weight.
+enum PackMode { PACK_PLAIN = 0, PACK_QKV = 1, PACK_GU = 2 };
+
+constexpr int kTileM = 64;  // rows per GEMM tile
+constexpr int kTileN = 64;  // packed columns per GEMM tile (two 32-column pairs)
+
+struct GemmArgs {
+  // A operand
+  const void* A;  // PRO_NONE: [M][lda] of the element type; PRO_ADARMS: fp32 h
+  int lda;
+  int M, K;
+  // packed weight fragments and tiling
+  const uint4* W;
+  int n_tiles, m_tiles, k_frags, ksplit;
+  // adaRMS
+  const float* ssq;  // [ssq_tiles][ldssq] partial row sums of h^2
+  int ssq_tiles, ldssq;
+  const float* scale;
+  const float* shift;
+  float eps;
+  // split-K scratch (zeroed counters, self-resetting)
+  float* partial;
+  int* counters;
+  // EPI_RESID
+  float* h;
+  int ldh;
+  const float* gate;
+  float* ssq_out;
+  // EPI_GELU
+  void* out;
+  int ldo;
+  // EPI_QKV
+  void* q;
+  int ldq;
+  void* kcache;   // layer's [Bmax][Hkv][S_max][dh]
+  void* vtcache;  // layer's [Bmax][Hkv][dh][S_max]
+  const int* n_valid;
+  const float* rope_cos;  // [B][T][dh/2]
+  const float* rope_sin;
+  int T, Hq, Hkv, dh, S_max;
+};
+
+struct AttnArgs {
+  const void* q;
+  int ldq;
+  const void* kcache;
+  const void* vtcache;
+  int S_max;
+  const int* n_valid;
+  void* o;
+  int ldo;
+  int T, Hq, Hkv, dh;
+  int batch, n_qg, nsplit, kc_len;
+  float scale_log2;
+  float* partial;
+  int* counters;
+};
+
+// Split-K / grid planning shared by the runtime and the launchers.
+struct GemmPlan {
+  int m_tiles, n_tiles, k_frags, ksplit, blocks;
+};
+GemmPlan plan_gemm(Dt dt, int M, int N, int K, int target_blocks);
+int kstep_of(Dt dt);
+
+hipError_t launch_gemm(Dt dt, Prologue pro, Epilogue epi, const GemmArgs& a, int blocks,
+                       hipStream_t s);
+hipError_t launch_attention(Dt dt, const AttnArgs& a, hipStream_t s);
+size_t attention_partial_floats(int dh, int items, int nsplit);
+
+hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s);
+// Y[m][n] = act(sum_k X[m][k] W[k][n] + b[n]), m < M <= 16; act 0 none, 1 SiLU.
+// grid.y = n_mat matrices with strides (W, b, Y advance by the given strides).
+hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const void* W, int ldw,
+                            const void* b, int N, float* Y, int ldy, int act, int n_mat,
+                            size_t w_stride, size_t b_stride, size_t y_stride, hipStream_t s);
+
+hipError_t launch_action_in(const float* x, int M, int A, const float* w_in, const float* b_in,
+                            float* h, int D, float* ssq, int ldssq, hipStream_t s);
+hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, const float* scale,
+                             const float* shift, float eps, const float* w_out,
+                             const float* b_out, float dt, hipStream_t s);
+
+hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_idx, int* n_valid,
+                              int T, int dh, float theta, float* rope_cos, float* rope_sin,
+                              hipStream_t s);
+hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx, int L,
+                              int batch, int P, int Hkv, int dh, int Bmax, int S_max,
+                              void* kcache, void* vtcache, hipStream_t s);
+
+hipError_t launch_pack(Dt dt, PackMode mode, const void* s0, const void* s1, const void* s2,
+                       int K, int N, int ld0, int ld1, int ld2, int Hq, int Hkv, int dh,
+                       uint4* dst, hipStream_t s);
+hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s);
+
+}  // namespace ae

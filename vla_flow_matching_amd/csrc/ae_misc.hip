@@ -1,0 +1,311 @@
+// The small kernels around the layer stack: the time path (once per call),
+// the action-in and final-norm / action-out / Euler kernels (once per step),
+// and prefix ingest (once per query).
+#include <math.h>
+
+#include "ae_device.h"
+#include "ae_kernels.h"
+
+namespace ae {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Time path.  Step k evaluates the velocity at t_k = (N - k)/N; its
+// sinusoidal embedding is [sin(2 pi t / P_i) | cos(2 pi t / P_i)], i < D/2,
+// with periods P_i geometric from 4e-3 to 4.0.  Computed in double: the
+// angles reach ~1.6e3 rad at t = 1.  The whole path depends only on t, so
+// it runs once per call (sglang PR summary, implementation item 2).
+// ---------------------------------------------------------------------------
+
+__global__ void tpath_sinusoid_kernel(float* e, int n_steps, int width) {
+  const int k = blockIdx.x;
+  const int half = width / 2;
+  const double t = static_cast<double>(n_steps - k) / static_cast<double>(n_steps);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double frac = static_cast<double>(i) / static_cast<double>(half - 1);
+    const double period = 4e-3 * pow(1000.0, frac);
+    const double ang = 2.0 * M_PI * t / period;
+    e[static_cast<size_t>(k) * width + i] = static_cast<float>(sin(ang));
+    e[static_cast<size_t>(k) * width + half + i] = static_cast<float>(cos(ang));
+  }
+}
+
+// Y[m][n] = act(sum_k X[m][k] W[k][n] + b[n]) for m < M <= 16: a few rows
+// against a wide weight, read once, 8 columns per thread, X staged in LDS.
+constexpr int kGemvCols = 8;
+constexpr int kGemvThreads = 64;
+constexpr int kGemvK = 256;
+
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* w);
+template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* w) {
+  unpack_frag<bf16_t>(*reinterpret_cast<const uint4*>(p), w);
+}
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* w) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGemvThreads) void gemv_rows_kernel(
+    const float* X, int ldx, int M, int K, const T* W, int ldw, const T* bias, int N, float* Y,
+    int ldy, int act, size_t w_stride, size_t b_stride, size_t y_stride) {
+  __shared__ float sx[16][kGemvK];
+  const int mat = blockIdx.y;
+  W += mat * w_stride;
+  bias += mat * b_stride;
+  Y += mat * y_stride;
+  const int n0 = (blockIdx.x * kGemvThreads + threadIdx.x) * kGemvCols;
+  float acc[16][kGemvCols];
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+#pragma unroll
+    for (int c = 0; c < kGemvCols; ++c) acc[m][c] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += kGemvK) {
+    const int kn = min(kGemvK, K - k0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < M * kGemvK; i += kGemvThreads) {
+      const int m = i / kGemvK, kk = i % kGemvK;
+      sx[m][kk] = kk < kn ? X[static_cast<size_t>(m) * ldx + k0 + kk] : 0.0f;
+    }
+    __syncthreads();
+    if (n0 < N) {
+      for (int kk = 0; kk < kn; ++kk) {
+        float w[kGemvCols];
+        load8<T>(W + static_cast<size_t>(k0 + kk) * ldw + n0, w);
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          if (m < M) {
+            const float xv = sx[m][kk];
+#pragma unroll
+            for (int c = 0; c < kGemvCols; ++c) acc[m][c] = fmaf(xv, w[c], acc[m][c]);
+          }
+      }
+    }
+  }
+  if (n0 >= N) return;
+  float bv[kGemvCols];
+  load8<T>(bias + n0, bv);
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+    if (m < M)
+#pragma unroll
+      for (int c = 0; c < kGemvCols; ++c) {
+        float y = acc[m][c] + bv[c];
+        if (act == 1) y = silu(y);
+        Y[static_cast<size_t>(m) * ldy + n0 + c] = y;
+      }
+}
+
+// ---------------------------------------------------------------------------
+// Action-in projection h = x W_in + b_in, plus per-64-column partial row sums
+// of h^2 for the first layer's adaRMS.  grid (M, D/64), 64 threads.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(64) void action_in_kernel(const float* x, int A, const float* w_in,
+                                                       const float* b_in, float* h, int D,
+                                                       float* ssq, int ldssq) {
+  const int m = blockIdx.x;
+  const int n = blockIdx.y * 64 + threadIdx.x;
+  float acc = 0.0f;
+  for (int a = 0; a < A; ++a) acc = fmaf(x[m * A + a], w_in[a * D + n], acc);
+  acc += b_in[n];
+  h[static_cast<size_t>(m) * D + n] = acc;
+  const float sq = wave_sum(acc * acc);
+  if (threadIdx.x == 0) ssq[blockIdx.y * ldssq + m] = sq;
+}
+
+// ---------------------------------------------------------------------------
+// Final adaRMS, action-out projection and the Euler update of one row:
+// v = adaRMS(h; scale_f, shift_f) W_out + b_out, x += dt v.  grid M, 256
+// threads; the row is normalised in fp32 and kept in LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxWidth = 4096;
+
+__global__ __launch_bounds__(256) void action_out_kernel(float* x, int A, const float* h, int D,
+                                                         const float* scale, const float* shift,
+                                                         float eps, const float* w_out,
+                                                         const float* b_out, float dt) {
+  __shared__ float su[kMaxWidth];
+  __shared__ float sred[4];
+  const int m = blockIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const float* hr = h + static_cast<size_t>(m) * D;
+  float ss = 0.0f;
+  for (int k = threadIdx.x; k < D; k += 256) {
+    const float v = hr[k];
+    su[k] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) sred[wave] = ss;
+  __syncthreads();
+  const float tot = sred[0] + sred[1] + sred[2] + sred[3];
+  const float r = 1.0f / sqrtf(tot / static_cast<float>(D) + eps);
+  for (int k = threadIdx.x; k < D; k += 256) su[k] = su[k] * r * (1.0f + scale[k]) + shift[k];
+  __syncthreads();
+  for (int a = wave; a < A; a += 4) {
+    float s = 0.0f;
+    for (int k = lane; k < D; k += kWave) s = fmaf(su[k], w_out[static_cast<size_t>(k) * A + a], s);
+    s = wave_sum(s);
+    if (lane == 0) x[m * A + a] += dt * (s + b_out[a]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefix ingest.
+// scan: per request, the visible count n_b and each visible row's compacted
+// index (prefix order kept); then the RoPE tables of the action tokens at
+// positions n_b + t (pads do not advance positions: LoongForge blog,
+// section 1), computed in double.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void prefix_scan_kernel(const uint8_t* mask, int P, int* comp_idx,
+                                                          int* n_valid, int T, int dh, float theta,
+                                                          float* rope_cos, float* rope_sin) {
+  __shared__ int s_cnt[256];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int chunk = (P + 255) / 256;
+  const int j0 = min(P, tid * chunk), j1 = min(P, j0 + chunk);
+  int c = 0;
+  for (int j = j0; j < j1; ++j) c += mask[static_cast<size_t>(b) * P + j] != 0;
+  s_cnt[tid] = c;
+  __syncthreads();
+  // inclusive scan (Hillis-Steele)
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? s_cnt[tid - off] : 0;
+    __syncthreads();
+    s_cnt[tid] += v;
+    __syncthreads();
+  }
+  int run = s_cnt[tid] - c;
+  for (int j = j0; j < j1; ++j) {
+    const bool vis = mask[static_cast<size_t>(b) * P + j] != 0;
+    comp_idx[static_cast<size_t>(b) * P + j] = vis ? run : -1;
+    run += vis;
+  }
+  const int nv = s_cnt[255];
+  if (tid == 0) n_valid[b] = nv;
+  const int half = dh / 2;
+  for (int i = tid; i < T * half; i += 256) {
+    const int t = i / half, j = i % half;
+    const double w = pow(static_cast<double>(theta), -2.0 * j / dh);
+    const double ph = static_cast<double>(nv + t) * w;
+    rope_cos[(static_cast<size_t>(b) * T + t) * half + j] = static_cast<float>(cos(ph));
+    rope_sin[(static_cast<size_t>(b) * T + t) * half + j] = static_cast<float>(sin(ph));
+  }
+}
+
+// copy: visible rows of K -> cache rows comp_idx (row-major [key][dh]);
+// V -> transposed cache [dh][key] through an LDS tile.  grid (L*B*Hkv,
+// ceil(P/32)), 256 threads.
+constexpr int kCopyRows = 32;
+
+template <typename T>
+__global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V, const int* comp_idx,
+                                                          int batch, int P, int Hkv, int dh,
+                                                          int Bmax, int S_max, T* kcache,
+                                                          T* vtcache) {
+  __shared__ T sv[kCopyRows][256 + 2];
+  __shared__ int sci[kCopyRows];
+  const int lbg = blockIdx.x;
+  const int g = lbg % Hkv;
+  const int b = (lbg / Hkv) % batch;
+  const int l = lbg / (Hkv * batch);
+  const int j0 = blockIdx.y * kCopyRows;
+  const int nrows = min(kCopyRows, P - j0);
+  if (threadIdx.x < kCopyRows)
+    sci[threadIdx.x] = threadIdx.x < nrows ? comp_idx[static_cast<size_t>(b) * P + j0 + threadIdx.x] : -1;
+  __syncthreads();
+  const size_t src_row0 = ((static_cast<size_t>(l) * batch + b) * P + j0) * Hkv + g;
+  const size_t cache_bg = (static_cast<size_t>(l) * Bmax + b) * Hkv + g;
+  T* kdst = kcache + cache_bg * S_max * dh;
+  T* vdst = vtcache + cache_bg * dh * S_max;
+  for (int i = threadIdx.x; i < nrows * dh; i += 256) {
+    const int r = i / dh, d = i % dh;
+    const int ci = sci[r];
+    if (ci < 0) continue;  // invisible row: never read
+    const size_t src = (src_row0 + static_cast<size_t>(r) * Hkv) * dh + d;
+    kdst[static_cast<size_t>(ci) * dh + d] = K[src];
+    sv[r][d] = V[src];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrows * dh; i += 256) {
+    const int d = i / nrows, r = i % nrows;
+    const int ci = sci[r];
+    if (ci < 0) continue;
+    vdst[static_cast<size_t>(d) * S_max + ci] = sv[r][d];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s) {
+  hipLaunchKernelGGL(tpath_sinusoid_kernel, dim3(n_steps), dim3(256), 0, s, e, n_steps, width);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const void* W, int ldw,
+                            const void* b, int N, float* Y, int ldy, int act, int n_mat,
+                            size_t w_stride, size_t b_stride, size_t y_stride, hipStream_t s) {
+  if (M < 1 || M > 16 || N % kGemvCols) return hipErrorInvalidValue;
+  const int cols_per_block = kGemvThreads * kGemvCols;
+  dim3 grid((N + cols_per_block - 1) / cols_per_block, n_mat), block(kGemvThreads);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(gemv_rows_kernel<bf16_t>, grid, block, 0, s, X, ldx, M, K,
+                       static_cast<const bf16_t*>(W), ldw, static_cast<const bf16_t*>(b), N, Y,
+                       ldy, act, w_stride, b_stride, y_stride);
+  else
+    hipLaunchKernelGGL(gemv_rows_kernel<float>, grid, block, 0, s, X, ldx, M, K,
+                       static_cast<const float*>(W), ldw, static_cast<const float*>(b), N, Y, ldy,
+                       act, w_stride, b_stride, y_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_action_in(const float* x, int M, int A, const float* w_in, const float* b_in,
+                            float* h, int D, float* ssq, int ldssq, hipStream_t s) {
+  hipLaunchKernelGGL(action_in_kernel, dim3(M, D / 64), dim3(64), 0, s, x, A, w_in, b_in, h, D,
+                     ssq, ldssq);
+  return hipGetLastError();
+}
+
+hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, const float* scale,
+                             const float* shift, float eps, const float* w_out,
+                             const float* b_out, float dt, hipStream_t s) {
+  if (D > kMaxWidth) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(action_out_kernel, dim3(M), dim3(256), 0, s, x, A, h, D, scale, shift, eps,
+                     w_out, b_out, dt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_idx, int* n_valid,
+                              int T, int dh, float theta, float* rope_cos, float* rope_sin,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(prefix_scan_kernel, dim3(batch), dim3(256), 0, s, mask, P, comp_idx, n_valid,
+                     T, dh, theta, rope_cos, rope_sin);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx, int L,
+                              int batch, int P, int Hkv, int dh, int Bmax, int S_max,
+                              void* kcache, void* vtcache, hipStream_t s) {
+  if (P == 0) return hipSuccess;
+  if (dh > 256) return hipErrorInvalidValue;
+  dim3 grid(L * batch * Hkv, (P + kCopyRows - 1) / kCopyRows), block(256);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(prefix_copy_kernel<bf16_t>, grid, block, 0, s,
+                       static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V), comp_idx,
+                       batch, P, Hkv, dh, Bmax, S_max, static_cast<bf16_t*>(kcache),
+                       static_cast<bf16_t*>(vtcache));
+  else
+    hipLaunchKernelGGL(prefix_copy_kernel<float>, grid, block, 0, s, static_cast<const float*>(K),
+                       static_cast<const float*>(V), comp_idx, batch, P, Hkv, dh, Bmax, S_max,
+                       static_cast<float*>(kcache), static_cast<float*>(vtcache));
+  return hipGetLastError();
+}
+
+}  // namespace ae
