@@ -28,9 +28,12 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 
 
-def algorithmic_work(w, n_valid):
+def algorithmic_work(w, n_valid, with_time_path=False):
     """Bytes a denoise call must move and FLOPs it must do (masked / padded
-    prefix rows excluded; activations excluded: they stay in L2 / MALL)."""
+    prefix rows excluded; activations excluded: they stay in L2 / MALL).
+    The time path (time MLP + every layer's modulation) depends only on the
+    step count and the weights; the library keeps its table across calls, so
+    a steady-state call does not include it."""
     D, L, F, A, T, N = w.width, w.n_layers, w.mlp_dim, w.action_dim, w.action_horizon, w.n_steps
     qd, kd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
     esz = 2 if w.dtype == "bf16" else 4
@@ -38,10 +41,10 @@ def algorithmic_work(w, n_valid):
     step_params = L * layer_params + 2 * A * D
     t_params = 6 * L * D * D + 2 * D * D + 2 * D * D
     kv_bytes = L * int(np.sum(n_valid)) * 2 * kd * esz
-    bytes_call = N * (step_params * esz + kv_bytes) + t_params * esz
+    bytes_call = N * (step_params * esz + kv_bytes) + (t_params * esz if with_time_path else 0)
     B = len(n_valid)
     attn_flops = sum(4 * T * w.n_q_heads * w.head_dim * (int(n) + T) for n in n_valid) * L * N
-    flops_call = 2 * B * T * step_params * N + attn_flops + 2 * N * t_params
+    flops_call = 2 * B * T * step_params * N + attn_flops + (2 * N * t_params if with_time_path else 0)
     return bytes_call, flops_call
 
 

@@ -106,8 +106,10 @@ typedef struct {
   long long prefix_sets;
   long long graph_captures;
   long long graph_replays;
-  long long eager_runs;
+  long long eager_runs;      /* calls launched directly instead of replaying a graph */
   long long device_bytes;    /* bytes the handle holds on the device */
+  long long device_errors;   /* nonzero: a persistent-kernel barrier timed out (results invalid) */
+  long long persistent;      /* workgroups of the whole-call kernel used when batch*T <= 64; 0: none */
 } ae_stats;
 
 /* Validate the config, then allocate every device buffer the handle will
@@ -143,6 +145,8 @@ ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* 
 ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps,
                      float* actions_out, void* stream);
 
+/* Counters, plus the device error flag; reading the flag synchronises with
+ * the device (the one call besides create/destroy that does). */
 ae_status ae_get_stats(const ae_handle* h, ae_stats* out);
 const char* ae_last_error(const ae_handle* h);
 const char* ae_status_string(ae_status s);

@@ -42,7 +42,8 @@ class TensorView(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [("denoise_calls", ctypes.c_longlong), ("prefix_sets", ctypes.c_longlong),
                 ("graph_captures", ctypes.c_longlong), ("graph_replays", ctypes.c_longlong),
-                ("eager_runs", ctypes.c_longlong), ("device_bytes", ctypes.c_longlong)]
+                ("eager_runs", ctypes.c_longlong), ("device_bytes", ctypes.c_longlong),
+                ("device_errors", ctypes.c_longlong), ("persistent", ctypes.c_longlong)]
 
 
 class AeError(RuntimeError):

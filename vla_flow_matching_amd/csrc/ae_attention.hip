@@ -190,10 +190,10 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
     if (active) {
 #pragma unroll
       for (int d = 0; d < ND; ++d)
-        *reinterpret_cast<f32x4*>(mine + (d * kWave + lane) * 4) = acc[d];
+        st_dev4(reinterpret_cast<f32x4*>(mine + (d * kWave + lane) * 4), acc[d]);
       if (grp == 0) {
-        mine[ND * kWave * 4 + lane] = m_run;
-        mine[ND * kWave * 4 + 16 + lane] = l_run;
+        st_dev(mine + ND * kWave * 4 + lane, m_run);
+        st_dev(mine + ND * kWave * 4 + 16 + lane, l_run);
       }
     }
     if (!arrive_last(p.counters + item, p.nsplit, &s_flag)) return;
@@ -201,20 +201,20 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
       float mx = -INFINITY;
       for (int s2 = 0; s2 < p.nsplit; ++s2) {
         const float* ps = p.partial + (static_cast<size_t>(item) * p.nsplit + s2) * 4 * PW + wave * PW;
-        mx = fmaxf(mx, __builtin_nontemporal_load(ps + ND * kWave * 4 + lane % 16));
+        mx = fmaxf(mx, ld_dev(ps + ND * kWave * 4 + lane % 16));
       }
 #pragma unroll
       for (int d = 0; d < ND; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
       l_run = 0.0f;
       for (int s2 = 0; s2 < p.nsplit; ++s2) {
         const float* ps = p.partial + (static_cast<size_t>(item) * p.nsplit + s2) * 4 * PW + wave * PW;
-        const float ms = __builtin_nontemporal_load(ps + ND * kWave * 4 + lane % 16);
+        const float ms = ld_dev(ps + ND * kWave * 4 + lane % 16);
         if (ms == -INFINITY) continue;
         const float w = exp2f(ms - mx);
-        l_run += w * __builtin_nontemporal_load(ps + ND * kWave * 4 + 16 + lane % 16);
+        l_run += w * ld_dev(ps + ND * kWave * 4 + 16 + lane % 16);
 #pragma unroll
         for (int d = 0; d < ND; ++d)
-          acc[d] += w * __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ps + (d * kWave + lane) * 4));
+          acc[d] += w * ld_dev4(reinterpret_cast<const f32x4*>(ps + (d * kWave + lane) * 4));
       }
     }
   }

@@ -129,28 +129,91 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Cross-workgroup completion counting (split-K / split-KV fix-up).
+// Cross-workgroup exchange (split-K / split-KV fix-up).
 //
-// Every workgroup of a group publishes its partial, then arrives on the
-// group's counter; the last to arrive reduces all partials in a fixed order
-// (so the result does not depend on arrival order) and resets the counter to
-// zero for the next launch.  Returns true in every thread of the last one.
+// Partials are written and read with relaxed device-scope atomic accesses,
+// which are coherent across the XCDs' separate L2s on their own (they carry
+// the device-scope cache policy).  An agent-scope release/acquire fence
+// would instead write back / invalidate the whole L2 of the XCD, once per
+// wave, which costs tens of microseconds per launch.  Ordering comes from
+// waiting for this thread's outstanding memory operations before the
+// workgroup arrives on the group counter; the last workgroup to arrive
+// reads the partials only after its counter update returned.
 // ---------------------------------------------------------------------------
 
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev4(f32x4* p, f32x4 v) {
+  float* q = reinterpret_cast<float*>(p);
+  st_dev(q, v[0]); st_dev(q + 1, v[1]); st_dev(q + 2, v[2]); st_dev(q + 3, v[3]);
+}
+__device__ __forceinline__ f32x4 ld_dev4(const f32x4* p) {
+  const float* q = reinterpret_cast<const float*>(p);
+  return f32x4{ld_dev(q), ld_dev(q + 1), ld_dev(q + 2), ld_dev(q + 3)};
+}
+
+// Every workgroup of a group publishes its partial (st_dev), then arrives
+// on the group's counter; the last to arrive reduces all partials in a fixed
+// order (so the result does not depend on arrival order) and resets the
+// counter to zero for the next launch.  Returns true in every thread of the
+// last workgroup.
 __device__ __forceinline__ bool arrive_last(int* counter, int expected, int* s_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
   __syncthreads();
   if (threadIdx.x == 0) {
-    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int last = (old == expected - 1);
     if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *s_flag = last;
   }
   __syncthreads();
-  bool last = *s_flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
+  return *s_flag != 0;
 }
+
+// ---------------------------------------------------------------------------
+// Device-coherent 16/8/4-byte buffer accesses (device-scope cache policy):
+// what one workgroup stores this way, another workgroup on any XCD reads
+// this way, once the store has been acknowledged.  Used for every
+// activation exchanged between workgroups inside one launch.  Offsets are
+// bytes from the resource base (< 2 GiB).
+// ---------------------------------------------------------------------------
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kCohPolicy = 16;  // device scope
+
+struct Coh {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ explicit Coh(const void* base)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000)) {}
+  __device__ __forceinline__ uint4 ld16(uint32_t off) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCohPolicy));
+  }
+  __device__ __forceinline__ uint2 ld8(uint32_t off) const {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCohPolicy));
+  }
+  __device__ __forceinline__ uint32_t ld4(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCohPolicy);
+  }
+  __device__ __forceinline__ void st16(uint32_t off, uint4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCohPolicy);
+  }
+  __device__ __forceinline__ void st8(uint32_t off, uint2 v) const {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, kCohPolicy);
+  }
+  __device__ __forceinline__ void st4(uint32_t off, uint32_t v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kCohPolicy);
+  }
+  __device__ __forceinline__ void st2(uint32_t off, uint16_t v) const {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kCohPolicy);
+  }
+  __device__ __forceinline__ float ldf(uint32_t off) const { return __uint_as_float(ld4(off)); }
+  __device__ __forceinline__ void stf(uint32_t off, float v) const { st4(off, __float_as_uint(v)); }
+};
 
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)

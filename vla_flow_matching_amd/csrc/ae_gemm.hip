@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     f32x4* mine = part + static_cast<size_t>(ti.s) * (MT * NB * kWave);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      if (i < mtr) mine[(i * NB + jc) * kWave + lane] = v[i];
+      if (i < mtr) st_dev4(&mine[(i * NB + jc) * kWave + lane], v[i]);
     if (!arrive_last(p.counters + ti.tile, p.ksplit, &s_flag)) return;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
         f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < p.ksplit; ++s) {
           const f32x4* ps = part + static_cast<size_t>(s) * (MT * NB * kWave);
-          tot += __builtin_nontemporal_load(&ps[(i * NB + jc) * kWave + lane]);
+          tot += ld_dev4(&ps[(i * NB + jc) * kWave + lane]);
         }
         v[i] = tot;
       }
@@ -325,7 +325,8 @@ namespace {
 
 template <typename T>
 __global__ void pack_kernel(int mode, const T* s0, const T* s1, const T* s2, int K, int N,
-                            int ld0, int ld1, int ld2, int Hq, int Hkv, int dh, uint4* dst) {
+                            int ld0, int ld1, int ld2, int Hq, int Hkv, int dh, uint4* dst,
+                            int kvalid, int nvalid) {
   constexpr int E = Mma<T>::E;
   constexpr int KSTEP = Mma<T>::KSTEP;
   const int k_frags = K / KSTEP;
@@ -359,43 +360,57 @@ __global__ void pack_kernel(int mode, const T* s0, const T* s1, const T* s2, int
     }
     float v[E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = Elem<T>::to_f(src[static_cast<size_t>(k0 + i) * ld + col]);
+    for (int i = 0; i < E; ++i)
+      v[i] = (k0 + i < kvalid && col < nvalid) ? Elem<T>::to_f(src[static_cast<size_t>(k0 + i) * ld + col])
+                                               : 0.0f;
     dst[g] = pack_frag<T>(v);
   }
 }
 
+// dst = fp32(src), or with cols > 0 the transpose of src [n / cols][cols]
 template <typename T>
-__global__ void to_f32_kernel(const T* src, float* dst, size_t n) {
+__global__ void to_f32_kernel(const T* src, float* dst, size_t n, int cols) {
   for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    dst[i] = Elem<T>::to_f(src[i]);
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    if (cols > 0) {
+      const size_t rows = n / cols, r = i / cols, c = i % cols;
+      dst[c * rows + r] = Elem<T>::to_f(src[i]);
+    } else {
+      dst[i] = Elem<T>::to_f(src[i]);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_pack(Dt dt, PackMode mode, const void* s0, const void* s1, const void* s2,
                        int K, int N, int ld0, int ld1, int ld2, int Hq, int Hkv, int dh,
-                       uint4* dst, hipStream_t s) {
+                       uint4* dst, hipStream_t s, int kvalid, int nvalid) {
   dim3 grid(1024), block(256);
+  if (kvalid < 0) kvalid = K;
+  if (nvalid < 0) nvalid = N;
   if (dt == DT_BF16)
     hipLaunchKernelGGL(pack_kernel<bf16_t>, grid, block, 0, s, static_cast<int>(mode),
                        static_cast<const bf16_t*>(s0), static_cast<const bf16_t*>(s1),
-                       static_cast<const bf16_t*>(s2), K, N, ld0, ld1, ld2, Hq, Hkv, dh, dst);
+                       static_cast<const bf16_t*>(s2), K, N, ld0, ld1, ld2, Hq, Hkv, dh, dst,
+                       kvalid, nvalid);
   else
     hipLaunchKernelGGL(pack_kernel<float>, grid, block, 0, s, static_cast<int>(mode),
                        static_cast<const float*>(s0), static_cast<const float*>(s1),
-                       static_cast<const float*>(s2), K, N, ld0, ld1, ld2, Hq, Hkv, dh, dst);
+                       static_cast<const float*>(s2), K, N, ld0, ld1, ld2, Hq, Hkv, dh, dst,
+                       kvalid, nvalid);
   return hipGetLastError();
 }
 
-hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s) {
+hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, int transpose_cols,
+                         hipStream_t s) {
   dim3 grid(256), block(256);
   if (dt == DT_BF16)
     hipLaunchKernelGGL(to_f32_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t*>(src),
-                       dst, n);
+                       dst, n, transpose_cols);
   else
     hipLaunchKernelGGL(to_f32_kernel<float>, grid, block, 0, s, static_cast<const float*>(src),
-                       dst, n);
+                       dst, n, transpose_cols);
   return hipGetLastError();
 }
 

@@ -105,9 +105,55 @@ hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* co
                               int batch, int P, int Hkv, int dh, int Bmax, int S_max,
                               void* kcache, void* vtcache, hipStream_t s);
 
+// Pack logical [K][N] row-major sources into MFMA fragment order; rows
+// k >= kvalid and columns n >= nvalid (PACK_PLAIN) read as zero (padding).
 hipError_t launch_pack(Dt dt, PackMode mode, const void* s0, const void* s1, const void* s2,
                        int K, int N, int ld0, int ld1, int ld2, int Hq, int Hkv, int dh,
-                       uint4* dst, hipStream_t s);
-hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s);
+                       uint4* dst, hipStream_t s, int kvalid = -1, int nvalid = -1);
+// fp32 copy of src (n elements); transpose_cols > 0 also transposes a
+// [n / transpose_cols][transpose_cols] matrix.
+hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, int transpose_cols,
+                         hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Persistent whole-call kernel (batch * T <= 64 rows)
+// ---------------------------------------------------------------------------
+
+struct PGemm {
+  int n_tiles, k_frags, ksplit;
+};
+
+struct PersistArgs {
+  int M, D, L, n_steps, T, A, Hq, Hkv, dh, F, S_max, qdim, ssq_tiles, ldssq, batch, G;
+  float eps, dt, scale_log2;
+  const uint4 *wqkv, *wo, *wgu, *wd;
+  size_t sqkv, so, sgu, sd;
+  const uint4* win_p;   // W_in packed: K = A (padded), N = D
+  const uint4* wout_p;  // W_out packed: K = D, N = A (padded to 16s)
+  int a_frags, a_blocks;
+  const float *b_in, *b_out;
+  const float *mod, *fmod;
+  void *kcache, *vtcache;
+  size_t kv_layer;  // elements per layer of each cache
+  const int* n_valid;
+  const float *rope_cos, *rope_sin;
+  float *x, *h, *ssq;
+  void *q, *o, *act;
+  float* gpart;
+  int* gcnt;
+  float* apart;
+  int* acnt;   // attention split counters (= pcnt + GEMM tile counters)
+  int* pcnt;   // monotonic split counters: q, o, gate/up, down tiles, then attention items
+  int n_acnt;  // attention items
+  int* flags;  // [G] barrier generations
+  int* err;    // device error flag (a barrier timed out)
+  PGemm pq, po, pg, pd;
+  int n_qg, nsplit, kc_len;
+};
+
+int persist_kpw();
+int persist_max_grid();
+int persist_blocks_per_cu(Dt dt, int dh);
+hipError_t launch_persist(Dt dt, const PersistArgs& a, hipStream_t s);
 
 }  // namespace ae

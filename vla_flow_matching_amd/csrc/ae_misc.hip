@@ -32,20 +32,23 @@ __global__ void tpath_sinusoid_kernel(float* e, int n_steps, int width) {
 }
 
 // Y[m][n] = act(sum_k X[m][k] W[k][n] + b[n]) for m < M <= 16: a few rows
-// against a wide weight, read once, 8 columns per thread, X staged in LDS.
-constexpr int kGemvCols = 8;
-constexpr int kGemvThreads = 64;
+// against a wide weight that is read once.  Two columns per thread, 512 per
+// block; the k loop keeps 16 independent weight loads in flight per thread.
+constexpr int kGemvThreads = 256;
+constexpr int kGemvCols = 2;
 constexpr int kGemvK = 256;
+constexpr int kGemvUnroll = 16;
 
-template <typename T> __device__ __forceinline__ void load8(const T* p, float* w);
-template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* w) {
-  unpack_frag<bf16_t>(*reinterpret_cast<const uint4*>(p), w);
+template <typename T> __device__ __forceinline__ void load2(const T* p, float* w);
+template <> __device__ __forceinline__ void load2<bf16_t>(const bf16_t* p, float* w) {
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+  w[0] = __uint_as_float(v << 16);
+  w[1] = __uint_as_float(v & 0xffff0000u);
 }
-template <> __device__ __forceinline__ void load8<float>(const float* p, float* w) {
-  float4 a = reinterpret_cast<const float4*>(p)[0];
-  float4 b = reinterpret_cast<const float4*>(p)[1];
-  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+template <> __device__ __forceinline__ void load2<float>(const float* p, float* w) {
+  const float2 v = *reinterpret_cast<const float2*>(p);
+  w[0] = v.x;
+  w[1] = v.y;
 }
 
 template <typename T>
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_rows_kernel(
   bias += mat * b_stride;
   Y += mat * y_stride;
   const int n0 = (blockIdx.x * kGemvThreads + threadIdx.x) * kGemvCols;
+  const bool live = n0 < N;
   float acc[16][kGemvCols];
 #pragma unroll
   for (int m = 0; m < 16; ++m)
@@ -71,23 +75,28 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_rows_kernel(
       sx[m][kk] = kk < kn ? X[static_cast<size_t>(m) * ldx + k0 + kk] : 0.0f;
     }
     __syncthreads();
-    if (n0 < N) {
-      for (int kk = 0; kk < kn; ++kk) {
-        float w[kGemvCols];
-        load8<T>(W + static_cast<size_t>(k0 + kk) * ldw + n0, w);
+    if (!live) continue;
+    for (int kk = 0; kk < kn; kk += kGemvUnroll) {
+      float w[kGemvUnroll][kGemvCols];
+#pragma unroll
+      for (int u = 0; u < kGemvUnroll; ++u) {
+        if (kk + u < kn) load2<T>(W + static_cast<size_t>(k0 + kk + u) * ldw + n0, w[u]);
+        else w[u][0] = w[u][1] = 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kGemvUnroll; ++u)
 #pragma unroll
         for (int m = 0; m < 16; ++m)
           if (m < M) {
-            const float xv = sx[m][kk];
+            const float xv = sx[m][kk + u];
 #pragma unroll
-            for (int c = 0; c < kGemvCols; ++c) acc[m][c] = fmaf(xv, w[c], acc[m][c]);
+            for (int c = 0; c < kGemvCols; ++c) acc[m][c] = fmaf(xv, w[u][c], acc[m][c]);
           }
-      }
     }
   }
-  if (n0 >= N) return;
+  if (!live) return;
   float bv[kGemvCols];
-  load8<T>(bias + n0, bv);
+  load2<T>(bias + n0, bv);
 #pragma unroll
   for (int m = 0; m < 16; ++m)
     if (m < M)
@@ -120,14 +129,15 @@ __global__ __launch_bounds__(64) void action_in_kernel(const float* x, int A, co
 // ---------------------------------------------------------------------------
 // Final adaRMS, action-out projection and the Euler update of one row:
 // v = adaRMS(h; scale_f, shift_f) W_out + b_out, x += dt v.  grid M, 256
-// threads; the row is normalised in fp32 and kept in LDS.
+// threads; the row is normalised in fp32 and kept in LDS; W_out is held
+// transposed ([A][D]) so each wave streams one output's weights.
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxWidth = 4096;
 
 __global__ __launch_bounds__(256) void action_out_kernel(float* x, int A, const float* h, int D,
                                                          const float* scale, const float* shift,
-                                                         float eps, const float* w_out,
+                                                         float eps, const float* w_out_t,
                                                          const float* b_out, float dt) {
   __shared__ float su[kMaxWidth];
   __shared__ float sred[4];
@@ -149,7 +159,8 @@ __global__ __launch_bounds__(256) void action_out_kernel(float* x, int A, const 
   __syncthreads();
   for (int a = wave; a < A; a += 4) {
     float s = 0.0f;
-    for (int k = lane; k < D; k += kWave) s = fmaf(su[k], w_out[static_cast<size_t>(k) * A + a], s);
+    const float* wr = w_out_t + static_cast<size_t>(a) * D;  // W_out^T row a: coalesced
+    for (int k = lane; k < D; k += kWave) s = fmaf(su[k], wr[k], s);
     s = wave_sum(s);
     if (lane == 0) x[m * A + a] += dt * (s + b_out[a]);
   }
@@ -252,7 +263,7 @@ hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s
 hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const void* W, int ldw,
                             const void* b, int N, float* Y, int ldy, int act, int n_mat,
                             size_t w_stride, size_t b_stride, size_t y_stride, hipStream_t s) {
-  if (M < 1 || M > 16 || N % kGemvCols) return hipErrorInvalidValue;
+  if (M < 1 || M > 16 || N % kGemvCols || ldw % kGemvCols) return hipErrorInvalidValue;
   const int cols_per_block = kGemvThreads * kGemvCols;
   dim3 grid((N + cols_per_block - 1) / cols_per_block, n_mat), block(kGemvThreads);
   if (dt == DT_BF16)

@@ -1,0 +1,1061 @@
+// The whole denoise call as ONE persistent, cooperatively launched kernel for
+// the small-batch regime (batch * T <= 64 rows: one GEMM row tile).
+//
+// At batch 1 every projection is a skinny GEMM whose weights are streamed
+// once per step (MolmoBot PR Part 2: only the action queries and the
+// timestep change between flow steps), so the loop is bound by HBM and by
+// the dependency chain between phases, not by arithmetic.  Separate kernels
+// would pay a launch, a ramp-up and a tail per phase (5 per layer); here every
+// workgroup stays resident for the whole call and walks the same phase list:
+//
+//   IN                      h = x W_in + b_in                (row tiles)
+//   per step, per layer:
+//     Q   adaRMS(h) . W_qkv -> RoPE -> q, K/V-cache rows    (split-K)
+//     A   masked GQA attention over [prefix | actions]      (split-KV)
+//     O   h += gate_a * (o . W_o)                           (split-K)
+//     G   act = gelu(adaRMS(h) . W_g) * (adaRMS(h) . W_u)   (split-K)
+//     D   h += gate_m * (act . W_d)                         (split-K)
+//   OUT+IN  v = adaRMS_f(h) W_out + b_out; x += dt v; next h (row tiles)
+//
+// Latency, not bandwidth, is what the exchange between phases costs, so the
+// code keeps every chain of dependent memory round trips short:
+//  * phases are separated by a flag barrier: each workgroup publishes its own
+//    generation word and a waiting wave reads all words in one round;
+//  * before waiting, a workgroup issues the weight loads of its next task
+//    into registers, so the HBM stream runs through the synchronisation;
+//  * split reductions are distributed: every workgroup of a split group
+//    publishes its partial tile, counts itself in on the tile's counter, waits
+//    for the others, and then reduces only its own slice of rows (in split
+//    order, so results are bitwise reproducible) and applies the epilogue to
+//    it.  No single workgroup pulls the whole group's partials.
+//  * activations that cross workgroups use device-coherent 16-byte accesses,
+//    issued together and consumed afterwards; weights, the prefix K/V and the
+//    time-path tables are read-only in this kernel and use cached loads.
+// Counters only grow during a launch (targets are multiples of the split
+// count), and a fill kernel zeroes them and the barrier words before it.
+// Every wait is bounded: after ~0.2 s a device error flag is raised and the
+// kernel drains without waiting again.
+#include "ae_device.h"
+#include "ae_kernels.h"
+
+namespace ae {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKpw = 4;  // max k-fragments per wave per GEMM task (weights held in registers)
+constexpr int kMaxG = 512;
+constexpr long kSpinLimit = 400000;
+constexpr int kTileF = kTileM * kTileN;  // floats of one partial tile
+
+__device__ __forceinline__ int ld_flag(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool dev_error(const PersistArgs& p) { return ld_flag(p.err) != 0; }
+
+__device__ __forceinline__ void raise_error(const PersistArgs& p) {
+  __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void bar_arrive(const PersistArgs& p, int gen) {
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(p.flags + blockIdx.x, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// All workgroups have arrived at generation `gen`.  Wave 0 polls every
+// word in one round of loads per poll.
+__device__ __forceinline__ void bar_wait(const PersistArgs& p, int gen) {
+  if (threadIdx.x < kWave) {
+    const Coh cf(p.flags);
+    long spins = 0;
+    if (!dev_error(p)) {
+      for (;;) {
+        int v[kMaxG / kWave];
+#pragma unroll
+        for (int j = 0; j < kMaxG / kWave; ++j) {
+          const int i = threadIdx.x + j * kWave;
+          v[j] = i < p.G ? static_cast<int>(cf.ld4(4u * i)) : gen;
+        }
+        int ok = 1;
+#pragma unroll
+        for (int j = 0; j < kMaxG / kWave; ++j) ok &= v[j] >= gen;
+        if (__all(ok)) break;
+        if (++spins > kSpinLimit) {
+          if (threadIdx.x == 0) raise_error(p);
+          break;
+        }
+        if ((spins & 255) == 0 && dev_error(p)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Count this workgroup into a split group and wait until `target` members
+// have (thread 0 spins; the caller has already waited for its own stores).
+__device__ __forceinline__ void group_join(const PersistArgs& p, int* counter, int target) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int v = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    long spins = 0;
+    while (v < target) {
+      if (++spins > kSpinLimit || ((spins & 255) == 0 && dev_error(p))) {
+        raise_error(p);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      v = ld_flag(counter);
+    }
+  }
+  __syncthreads();
+}
+
+// Row slice of split member s out of n over `rows` rows.
+__device__ __forceinline__ void row_slice(int s, int n, int rows, int& r0, int& r1) {
+  r0 = (s * rows) / n;
+  r1 = ((s + 1) * rows) / n;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM phase: one 64-row tile, n-tiles x K splits over workgroups, the K
+// range of a task split again over the four waves
+// ---------------------------------------------------------------------------
+
+struct GemmLayer {
+  const uint4* W;
+  const void* A;  // PRO_NONE: T [M][lda]; PRO_ADARMS: fp32 h [M][lda]
+  int lda;
+  const float* scale;
+  const float* shift;
+  const float* gate;
+  void* kc;  // layer's K cache
+  void* vt;  // layer's V^T cache
+};
+
+// adaRMS prologue data in one round of loads: per-row reciprocal RMS of h
+// (from the per-64-column partial sums of squares) and the modulation
+// scale / shift of the task's k range [k_lo, k_lo + k_len) (k_len <= 512).
+__device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, float* s_r,
+                                         const float* scale, const float* shift, int k_lo, int k_len,
+                                         float* s_sc, float* s_sh) {
+  const Coh cs(p.ssq);
+  const int n = p.M * p.ssq_tiles;  // <= 64 rows x 64 tiles
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = threadIdx.x + j * kThreads;
+    v[j] = i < n ? cs.ldf(4u * ((i / p.M) * p.ldssq + i % p.M)) : 0.0f;
+  }
+  float sc[2], sh[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = threadIdx.x + j * kThreads;
+    sc[j] = i < k_len ? scale[k_lo + i] : 0.0f;
+    sh[j] = i < k_len ? shift[k_lo + i] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = threadIdx.x + j * kThreads;
+    if (i < n) s_part[i] = v[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = threadIdx.x + j * kThreads;
+    s_sc[i] = 1.0f + sc[j];
+    s_sh[i] = sh[j];
+  }
+  __syncthreads();
+  if (threadIdx.x < p.M) {
+    float acc = 0.0f;
+    for (int q = 0; q < p.ssq_tiles; ++q) acc += s_part[q * p.M + threadIdx.x];
+    s_r[threadIdx.x] = 1.0f / sqrtf(acc / static_cast<float>(p.D) + p.eps);
+  }
+  __syncthreads();
+}
+
+template <typename T, int PRO, int EPI>
+__device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g, const GemmLayer& ly,
+                                           int* counters, int it, int gen_wait, char* smem) {
+  using MM = Mma<T>;
+  constexpr int E = MM::E;
+  constexpr int KSTEP = MM::KSTEP;
+  constexpr int MT = kTileM / 16;
+  constexpr int NB = kTileN / 16;
+  constexpr int AW = PRO == PRO_ADARMS ? E / 4 : 1;  // 16-byte A loads per fragment
+  constexpr int kRw = kTileM / 4;                     // epilogue rows per wave at most
+  auto s_red = reinterpret_cast<f32x4 (*)[MT * NB][kWave]>(smem);
+  auto s_y = reinterpret_cast<float (*)[kTileN + 1]>(smem);
+  float* s_r = reinterpret_cast<float*>(smem + 4 * MT * NB * kWave * sizeof(f32x4));
+  float* s_part = s_r + kTileM;        // [ssq_tiles * M] (<= 64 * 64)
+  float* s_sc = s_part + 64 * 64;      // 1 + scale over the task's k range (<= 512)
+  float* s_sh = s_sc + 512;            // shift over the task's k range
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int rows = p.M;
+  const int mtr = (rows + 15) / 16;
+  const int n_tasks = g.n_tiles * g.ksplit;
+  const Coh coh_a(ly.A);
+  bool waited = false;
+
+  for (int t = blockIdx.x; t < n_tasks; t += p.G) {
+    const int nt = t / g.ksplit, s = t % g.ksplit;
+    const int kf0 = static_cast<int>((static_cast<long long>(s) * g.k_frags) / g.ksplit);
+    const int kf1 = static_cast<int>((static_cast<long long>(s + 1) * g.k_frags) / g.ksplit);
+    const int cnt = kf1 - kf0 > wave ? (kf1 - kf0 - wave + 3) / 4 : 0;
+
+    // Every load below is issued unconditionally at a clamped, valid address
+    // and masked where it is used: a guarded load would make the compiler
+    // wait for it on the spot, one round trip per element.
+
+    // weights of this task -> registers, before waiting for the inputs
+    uint4 wb[kKpw][NB];
+    const uint4* Wt = ly.W + static_cast<size_t>(nt) * NB * g.k_frags * kWave + lane;
+#pragma unroll
+    for (int c = 0; c < kKpw; ++c) {
+      const int kf = min(kf0 + wave + 4 * c, g.k_frags - 1);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) wb[c][j] = Wt[(static_cast<size_t>(j) * g.k_frags + kf) * kWave];
+    }
+
+    if (!waited) {
+      bar_wait(p, gen_wait);
+      waited = true;
+    }
+
+    // A operand of the task, all in flight together
+    const int arow = lane % 16;
+    const int acol = E * (lane / 16);
+    uint4 araw[kKpw][MT][AW];
+#pragma unroll
+    for (int c = 0; c < kKpw; ++c)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int row = min(16 * i + arow, rows - 1);
+        const int k = min(kf0 + wave + 4 * c, g.k_frags - 1) * KSTEP + acol;
+#pragma unroll
+        for (int q = 0; q < AW; ++q)
+          araw[c][i][q] = coh_a.ld16((PRO == PRO_ADARMS ? 4u : static_cast<uint32_t>(sizeof(T))) *
+                                     (row * ly.lda + k + 4 * q));
+      }
+    const int k_lo = kf0 * KSTEP;
+    float rr[MT];
+    if (PRO == PRO_ADARMS) {
+      load_rms(p, s_part, s_r, ly.scale, ly.shift, k_lo, (kf1 - kf0) * KSTEP, s_sc, s_sh);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) rr[i] = s_r[min(16 * i + arow, rows - 1)];
+    }
+
+    f32x4 acc[MT][NB];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int c = 0; c < kKpw; ++c) {
+      if (c < cnt) {
+        const int kk = (kf0 + wave + 4 * c) * KSTEP + acol - k_lo;
+        uint4 a[MT];
+        if (PRO == PRO_ADARMS) {
+          float4 sv[AW], bv[AW];
+#pragma unroll
+          for (int q = 0; q < AW; ++q) {
+            sv[q] = *reinterpret_cast<const float4*>(s_sc + kk + 4 * q);
+            bv[q] = *reinterpret_cast<const float4*>(s_sh + kk + 4 * q);
+          }
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            float v[E];
+#pragma unroll
+            for (int q = 0; q < AW; ++q) {
+              const uint4 hv = araw[c][i][q];
+              v[4 * q + 0] = __uint_as_float(hv.x) * rr[i] * sv[q].x + bv[q].x;
+              v[4 * q + 1] = __uint_as_float(hv.y) * rr[i] * sv[q].y + bv[q].y;
+              v[4 * q + 2] = __uint_as_float(hv.z) * rr[i] * sv[q].z + bv[q].z;
+              v[4 * q + 3] = __uint_as_float(hv.w) * rr[i] * sv[q].w + bv[q].w;
+            }
+            a[i] = 16 * i + arow < rows ? pack_frag<T>(v) : make_uint4(0, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < MT; ++i) a[i] = 16 * i + arow < rows ? araw[c][i][0] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          if (i < mtr)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = MM::mma(a[i], wb[c][j], acc[i][j]);
+      }
+    }
+
+    // the four waves' K slices -> one tile in LDS (row-major s_y)
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      if (i < mtr)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) s_red[wave][i * NB + j][lane] = acc[i][j];
+    __syncthreads();
+    f32x4 v[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < mtr)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v[i] += s_red[w][i * NB + wave][lane];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      if (i < mtr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_y[16 * i + 4 * (lane / 16) + e][16 * wave + lane % 16] = v[i][e];
+    __syncthreads();
+
+    int r0 = 0, r1 = rows;
+    if (g.ksplit > 1) row_slice(s, g.ksplit, rows, r0, r1);
+
+    // epilogue inputs of this member's rows (row r0 + wave + 4i, lane =
+    // column), issued now so they arrive while the group assembles
+    float ein[kRw], ecs[kRw], esn[kRw];
+    int enb[kRw];
+    const int pph = p.dh / 32, half = p.dh / 2;
+    int seg = 0, head = 0, jrot = 0;
+    const bool hi = (lane & 16) != 0;
+    if (EPI == EPI_QKV) {
+      const int P = 2 * nt + lane / 32, pq = p.Hq * pph, pk = p.Hkv * pph;
+      int pi;
+      if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
+      else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
+      else { seg = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
+      jrot = 16 * pi + lane % 16;
+    }
+    if (EPI != EPI_GELU) {
+      const Coh ch(p.h);
+#pragma unroll
+      for (int i = 0; i < kRw; ++i) {
+        const int row = min(r0 + wave + 4 * i, rows - 1);
+        if (EPI == EPI_RESID) {
+          ein[i] = ch.ldf(4u * (row * p.D + nt * kTileN + lane));
+        } else {
+          const int req = row / p.T, tt = row % p.T;
+          const size_t ti2 = (static_cast<size_t>(req) * p.T + tt) * half + jrot;
+          ecs[i] = p.rope_cos[ti2];
+          esn[i] = p.rope_sin[ti2];
+          enb[i] = p.n_valid[req];
+        }
+      }
+    }
+    const float gn = EPI == EPI_RESID ? ly.gate[nt * kTileN + lane] : 0.0f;
+
+    if (g.ksplit > 1) {
+      // publish the partial (row-major, 16-byte stores), join the group,
+      // then reduce this member's row slice over all members in order
+      const Coh cp(p.gpart + static_cast<size_t>(nt) * g.ksplit * kTileF);
+      for (int i = tid; i < rows * (kTileN / 4); i += kThreads) {
+        const int r = i / (kTileN / 4), c4 = 4 * (i % (kTileN / 4));
+        cp.st16(4u * (s * kTileF + r * kTileN + c4),
+                make_uint4(__float_as_uint(s_y[r][c4]), __float_as_uint(s_y[r][c4 + 1]),
+                           __float_as_uint(s_y[r][c4 + 2]), __float_as_uint(s_y[r][c4 + 3])));
+      }
+      group_join(p, counters + nt, g.ksplit * (it + 1));
+      const int n4 = (r1 - r0) * (kTileN / 4);  // 16-byte chunks of the slice
+      for (int i = tid; i < n4; i += kThreads) {
+        const int r = r0 + i / (kTileN / 4), c4 = 4 * (i % (kTileN / 4));
+        const uint32_t off = 4u * (r * kTileN + c4);
+        f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint4 buf[8];
+        for (int s0 = 0; s0 < g.ksplit; s0 += 8) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) buf[j] = cp.ld16(off + 4u * min(s0 + j, g.ksplit - 1) * kTileF);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (s0 + j < g.ksplit)
+              tot += f32x4{__uint_as_float(buf[j].x), __uint_as_float(buf[j].y), __uint_as_float(buf[j].z),
+                           __uint_as_float(buf[j].w)};
+        }
+        s_y[r][c4] = tot[0];
+        s_y[r][c4 + 1] = tot[1];
+        s_y[r][c4 + 2] = tot[2];
+        s_y[r][c4 + 3] = tot[3];
+      }
+      __syncthreads();
+    }
+
+    if (EPI == EPI_RESID) {
+      const Coh ch(p.h), cq(p.ssq);
+#pragma unroll
+      for (int i = 0; i < kRw; ++i) {
+        const int row = r0 + wave + 4 * i;
+        if (row >= r1) continue;
+        const float hn = ein[i] + gn * s_y[row][lane];
+        ch.stf(4u * (row * p.D + nt * kTileN + lane), hn);
+        const float sq = wave_sum(hn * hn);
+        if (lane == 0) cq.stf(4u * (nt * p.ldssq + row), sq);
+      }
+    } else if (EPI == EPI_GELU) {
+      // lanes 32p + jj (jj < 16) hold gate, 32p + 16 + jj the matching up
+      const Coh co(p.act);
+      for (int row = r0 + wave; row < r1; row += 4) {
+        const float y = s_y[row][lane];
+        const float other = __shfl_xor(y, 16, kWave);
+        if (!hi) {
+          const int f = (2 * nt + lane / 32) * 16 + lane % 16;
+          const float a = gelu_tanh(y) * other;
+          if (sizeof(T) == 2) co.st2(2u * (row * p.F + f), f2bf(a));
+          else co.stf(4u * (row * p.F + f), a);
+        }
+      }
+    } else {  // EPI_QKV: lanes 32p + jj and 32p + 16 + jj are a rotation pair
+      const Coh cqo(p.q);
+      const int col = (hi ? half : 0) + jrot;  // column within the head
+#pragma unroll
+      for (int i = 0; i < kRw; ++i) {
+        const int row = r0 + wave + 4 * i;
+        if (row >= r1) continue;
+        const float y = s_y[row][lane];
+        const float other = __shfl_xor(y, 16, kWave);
+        // (a, b) -> (a cos - b sin, b cos + a sin); v is not rotated
+        const float cs = seg < 2 ? ecs[i] : 1.0f, sn = seg < 2 ? esn[i] : 0.0f;
+        const float val = hi ? y * cs + other * sn : y * cs - other * sn;
+        if (seg == 0) {
+          const uint32_t off = sizeof(T) * (row * p.qdim + head * p.dh + col);
+          if (sizeof(T) == 2) cqo.st2(off, f2bf(val));
+          else cqo.stf(off, val);
+        } else {
+          const int req = row / p.T;
+          const int key = enb[i] + row % p.T;
+          const size_t bgi = static_cast<size_t>(req) * p.Hkv + head;
+          if (seg == 1) {
+            const Coh ck(static_cast<T*>(ly.kc) + bgi * p.S_max * p.dh);
+            const uint32_t off = sizeof(T) * (key * p.dh + col);
+            if (sizeof(T) == 2) ck.st2(off, f2bf(val));
+            else ck.stf(off, val);
+          } else {
+            const Coh cv(static_cast<T*>(ly.vt) + bgi * p.dh * p.S_max);
+            const uint32_t off = sizeof(T) * (col * p.S_max + key);
+            if (sizeof(T) == 2) cv.st2(off, f2bf(val));
+            else cv.stf(off, val);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention phase: S^T = K Q^T per 16-key block, online softmax per query
+// column, O^T = V^T P^T; split over keys, distributed merge.
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ uint4 vt_frag(const T* vrow, const Coh& cv, uint32_t row_off, bool coh,
+                                         int kb0, int grp, int k_end);
+
+template <>
+__device__ __forceinline__ uint4 vt_frag<bf16_t>(const bf16_t* vrow, const Coh& cv, uint32_t row_off,
+                                                 bool coh, int kb0, int grp, int k_end) {
+  const int ka = kb0 + 4 * grp, kb = kb0 + 16 + 4 * grp;
+  uint2 lo, hi;
+  if (coh) {
+    lo = cv.ld8(row_off + 2u * ka);
+    hi = cv.ld8(row_off + 2u * kb);
+  } else {
+    lo = *reinterpret_cast<const uint2*>(vrow + ka);
+    hi = *reinterpret_cast<const uint2*>(vrow + kb);
+  }
+  uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k0 = (i < 2 ? ka : kb) + 2 * (i % 2);
+    if (k0 >= k_end) w[i] = 0u;
+    else if (k0 + 1 >= k_end) w[i] &= 0x0000ffffu;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <>
+__device__ __forceinline__ uint4 vt_frag<float>(const float* vrow, const Coh& cv, uint32_t row_off,
+                                                bool coh, int kb0, int grp, int k_end) {
+  const int ka = kb0 + 4 * grp;
+  uint4 v = coh ? cv.ld16(row_off + 4u * ka) : *reinterpret_cast<const uint4*>(vrow + ka);
+  if (ka + 0 >= k_end) v.x = 0u;
+  if (ka + 1 >= k_end) v.y = 0u;
+  if (ka + 2 >= k_end) v.z = 0u;
+  if (ka + 3 >= k_end) v.w = 0u;
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4_coh(const Coh& c, uint32_t off, const float* v);
+template <>
+__device__ __forceinline__ void store4_coh<bf16_t>(const Coh& c, uint32_t off, const float* v) {
+  uint2 w;
+  w.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+  w.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
+  c.st8(off, w);
+}
+template <>
+__device__ __forceinline__ void store4_coh<float>(const Coh& c, uint32_t off, const float* v) {
+  c.st16(off, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                         __float_as_uint(v[3])));
+}
+
+template <typename T, int DH>
+__device__ __forceinline__ void attention_phase(const PersistArgs& p, const void* kc_l, const void* vt_l,
+                                                int it, int gen_wait, char* smem) {
+  using MM = Mma<T>;
+  constexpr int E = MM::E, KSTEP = MM::KSTEP;
+  constexpr int NF = DH / KSTEP, ND = DH / 16, NBLK = KSTEP / 16;
+  constexpr int PW = ND * kWave * 4 + 32;  // floats of one wave's partial: O^T, then m[16], l[16]
+
+  const int G = p.Hq / p.Hkv;
+  const int R = p.T * G;
+  const int n_items = p.batch * p.Hkv * p.n_qg;
+  const int n_tasks = n_items * p.nsplit;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, grp = lane / 16;
+  bool waited = false;
+
+  for (int task = blockIdx.x; task < n_tasks; task += p.G) {
+    const int item = task / p.nsplit, s = task % p.nsplit;
+    const int qg = item % p.n_qg, bg = item / p.n_qg, g = bg % p.Hkv, b = bg / p.Hkv;
+    if (!waited) {
+      bar_wait(p, gen_wait);
+      waited = true;
+    }
+    const int nv = p.n_valid[b];
+    const int len = nv + p.T;
+    const int k_begin = s * p.kc_len;
+    const int k_end = min(k_begin + p.kc_len, len);
+    const T* Kb = static_cast<const T*>(kc_l) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
+    const T* Vb = static_cast<const T*>(vt_l) + static_cast<size_t>(b * p.Hkv + g) * DH * p.S_max;
+    const Coh ck(Kb), cv(Vb), cq(p.q), co(p.o);
+
+    const int qr0 = (qg * 4 + wave) * 16;
+    const bool active = qr0 < R;
+    const int myq = qr0 + lane % 16;
+    const bool qvalid = myq < R;
+    const int hh = qvalid ? myq / p.T : 0;
+    const int tt = qvalid ? myq % p.T : 0;
+    // Q^T fragments of this wave's 16 query rows, parked in LDS for the key loop
+    auto s_q = reinterpret_cast<uint4 (*)[NF][kWave]>(smem);  // [4 waves][NF][64]
+    {
+      const uint32_t qoff = sizeof(T) * ((b * p.T + tt) * p.qdim + (g * G + hh) * DH + E * grp);
+      uint4 qf[NF];
+#pragma unroll
+      for (int kf = 0; kf < NF; ++kf)
+        qf[kf] = qvalid ? cq.ld16(qoff + sizeof(T) * kf * KSTEP) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int kf = 0; kf < NF; ++kf) s_q[wave][kf][lane] = qf[kf];
+    }
+    f32x4 acc[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    if (active) {
+      for (int kb0 = k_begin; kb0 < k_end; kb0 += KSTEP) {
+        const bool coh = kb0 + KSTEP > nv;  // block holds action rows written this launch
+        // K and V^T fragments of the block, all issued before use
+        uint4 kfr[NBLK][NF];
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+          const int key = kb0 + 16 * blk + lane % 16;
+          const bool kv = key < k_end;
+          const int kr = kv ? key : 0;
+#pragma unroll
+          for (int kf = 0; kf < NF; ++kf) {
+            const int col = kf * KSTEP + E * grp;
+            uint4 f = make_uint4(0, 0, 0, 0);
+            if (kv)
+              f = coh ? ck.ld16(sizeof(T) * (kr * DH + col))
+                      : *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(kr) * DH + col);
+            kfr[blk][kf] = f;
+          }
+        }
+        uint4 vfr[ND];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int vr = 16 * d + lane % 16;
+          vfr[d] = vt_frag<T>(Vb + static_cast<size_t>(vr) * p.S_max, cv, sizeof(T) * vr * p.S_max, coh,
+                              kb0, grp, k_end);
+        }
+        f32x4 st[NBLK];
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+          st[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(kfr[blk][kf], s_q[wave][kf][lane], st[blk]);
+        }
+        float sv[NBLK * 4];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb0 + 16 * blk + 4 * grp + i;
+            const float x = key < k_end ? st[blk][i] * p.scale_log2 : -INFINITY;
+            sv[blk * 4 + i] = x;
+            cmax = fmaxf(cmax, x);
+          }
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = exp2f(m_run - m_new);
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NBLK * 4; ++i) {
+          sv[i] = exp2f(sv[i] - m_new);
+          psum += sv[i];
+        }
+        psum += __shfl_xor(psum, 16, kWave);
+        psum += __shfl_xor(psum, 32, kWave);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        const uint4 pf = pack_frag<T>(sv);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) acc[d] = MM::mma(vfr[d], pf, acc[d] * alpha);
+        __builtin_amdgcn_sched_barrier(0);  // one key block's fragments live at a time
+      }
+    }
+    // acc[d][i] = O^T[dim 16 d + 4 grp + i][query lane % 16] (unnormalised)
+
+    if (p.nsplit == 1) {
+      if (active && qvalid) {
+        const float inv = 1.0f / l_run;
+        const uint32_t obase = sizeof(T) * ((b * p.T + tt) * p.qdim + (g * G + hh) * DH);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          float v[4] = {acc[d][0] * inv, acc[d][1] * inv, acc[d][2] * inv, acc[d][3] * inv};
+          store4_coh<T>(co, obase + sizeof(T) * (16 * d + 4 * grp), v);
+        }
+      }
+      continue;
+    }
+
+    // publish (O^T, m, l) of this split, join the item's group
+    const Coh cpart(p.apart + static_cast<size_t>(item) * p.nsplit * 4 * PW);
+    if (active) {
+      const uint32_t wbase = 4u * ((s * 4 + wave) * PW);
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+        cpart.st16(wbase + 16u * (d * kWave + lane),
+                   make_uint4(__float_as_uint(acc[d][0]), __float_as_uint(acc[d][1]),
+                              __float_as_uint(acc[d][2]), __float_as_uint(acc[d][3])));
+      if (grp == 0) {
+        cpart.stf(wbase + 4u * (ND * kWave * 4 + lane), m_run);
+        cpart.stf(wbase + 4u * (ND * kWave * 4 + 16 + lane), l_run);
+      }
+    }
+    group_join(p, p.acnt + item, p.nsplit * (it + 1));
+
+    // distributed merge: units (wave w of the item, d block) dealt to members
+    const int n_units = 4 * ND;
+    for (int u = s * 4 + wave; u < n_units; u += 4 * p.nsplit) {
+      const int w = u / ND, d = u % ND;
+      const int uq0 = (qg * 4 + w) * 16;
+      if (uq0 >= R) continue;
+      const int q = uq0 + lane % 16;
+      float mx = -INFINITY;
+      for (int s0 = 0; s0 < p.nsplit; s0 += 8) {
+        float mv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          mv[j] = s0 + j < p.nsplit ? cpart.ldf(4u * (((s0 + j) * 4 + w) * PW + ND * kWave * 4 + lane % 16))
+                                   : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, mv[j]);
+      }
+      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+      float lsum = 0.0f;
+      for (int s0 = 0; s0 < p.nsplit; s0 += 8) {
+        float mv[8], lv[8];
+        uint4 av[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool ok = s0 + j < p.nsplit;
+          const uint32_t wb = 4u * (((s0 + j) * 4 + w) * PW);
+          mv[j] = ok ? cpart.ldf(wb + 4u * (ND * kWave * 4 + lane % 16)) : -INFINITY;
+          lv[j] = ok ? cpart.ldf(wb + 4u * (ND * kWave * 4 + 16 + lane % 16)) : 0.0f;
+          av[j] = ok ? cpart.ld16(wb + 16u * (d * kWave + lane)) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (mv[j] == -INFINITY) continue;  // an empty split
+          const float wgt = exp2f(mv[j] - mx);
+          lsum += wgt * lv[j];
+          o += wgt * f32x4{__uint_as_float(av[j].x), __uint_as_float(av[j].y), __uint_as_float(av[j].z),
+                           __uint_as_float(av[j].w)};
+        }
+      }
+      if (q < R) {
+        const int h2 = q / p.T, t2 = q % p.T;
+        const float inv = 1.0f / lsum;
+        float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+        store4_coh<T>(co, sizeof(T) * ((b * p.T + t2) * p.qdim + (g * G + h2) * DH + 16 * d + 4 * grp), v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// OUT + IN phase, one task per 16-row tile:
+//   OUT: v = adaRMS(h; scale_f, shift_f) . W_out + b_out, x += dt v
+//   IN:  h = x . W_in + b_in, and h's per-64-column row sums of squares
+// For bf16 weights, the fp32 operand (u or x) is split into a bf16 high
+// part and a bf16 remainder, both multiplied on the MFMA units, which keeps
+// these two projections at ~fp32 accuracy (the weights are exact in bf16).
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ void split_frag(const float* v, uint4& hi, uint4& lo);
+template <>
+__device__ __forceinline__ void split_frag<bf16_t>(const float* v, uint4& hi, uint4& lo) {
+  float h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = bf2f(f2bf(v[i]));
+    l[i] = v[i] - h[i];
+  }
+  hi = pack_frag_bf16(h);
+  lo = pack_frag_bf16(l);
+}
+template <>
+__device__ __forceinline__ void split_frag<float>(const float* v, uint4& hi, uint4& lo) {
+  hi = pack_frag_f32(v);
+  lo = make_uint4(0, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool do_out, bool do_in,
+                                            int gen_wait, char* smem) {
+  using MM = Mma<T>;
+  constexpr int E = MM::E, KSTEP = MM::KSTEP;
+  constexpr bool kSplit = sizeof(T) == 2;
+  constexpr int KPW_OUT = 8;   // h / W_out fragments per wave per chunk
+  constexpr int CPW_IN = 16;   // W_in column blocks per wave per chunk
+  constexpr int kAF = 32 / KSTEP;  // fragments covering A <= 32
+  constexpr int kAB = 2;           // W_out column blocks covering A <= 32
+  float* s_x = reinterpret_cast<float*>(smem);        // [16][64]
+  float* s_r = s_x + 16 * 64;                         // [16]
+  float* s_part = s_r + 16;                           // [ssq_tiles][16]
+  float* s_f = s_part + 64 * 16;                      // [2][D]: 1 + scale_f, shift_f
+  f32x4* s_red = reinterpret_cast<f32x4*>(s_f + 2 * 4096);  // [4 waves][4 blocks][64]
+  float* s_sq = reinterpret_cast<float*>(s_red);             // [16 slots][16 rows] (IN part)
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n_tasks = (p.M + 15) / 16;
+  const Coh cx(p.x), ch(p.h), cs(p.ssq);
+  const int row = lane % 16;
+  const int kfr = p.D / KSTEP;       // h / W_out fragments
+  const int nb = p.D / 16;           // W_in column blocks
+  bool waited = false;
+
+  for (int task = blockIdx.x; task < n_tasks; task += p.G) {
+    const int m0 = task * 16;
+    const int rows = min(16, p.M - m0);
+
+    // weights of the first chunk of each part, before waiting
+    uint4 wo[KPW_OUT][kAB];
+#define AE_ISSUE_WOUT(c0)                                                                   \
+  _Pragma("unroll") for (int c = 0; c < KPW_OUT; ++c) {                                      \
+    const int kf = wave + 4 * ((c0) + c);                                                   \
+    _Pragma("unroll") for (int j = 0; j < kAB; ++j) wo[c][j] =                               \
+        (do_out && kf < kfr && j < p.a_blocks)                                              \
+            ? p.wout_p[(static_cast<size_t>(j) * kfr + kf) * kWave + lane]                  \
+            : make_uint4(0, 0, 0, 0);                                                       \
+  }
+    uint4 wi[CPW_IN][kAF];
+    float bi[CPW_IN];
+#define AE_ISSUE_WIN(q0)                                                                    \
+  _Pragma("unroll") for (int q = 0; q < CPW_IN; ++q) {                                       \
+    const int cb = wave + 4 * ((q0) + q);                                                   \
+    bi[q] = (do_in && cb < nb) ? p.b_in[16 * cb + lane % 16] : 0.0f;                        \
+    _Pragma("unroll") for (int f = 0; f < kAF; ++f) wi[q][f] =                               \
+        (do_in && cb < nb && f < p.a_frags)                                                 \
+            ? p.win_p[(static_cast<size_t>(cb) * p.a_frags + f) * kWave + lane]             \
+            : make_uint4(0, 0, 0, 0);                                                       \
+  }
+    AE_ISSUE_WOUT(0)
+
+    if (!waited) {
+      bar_wait(p, gen_wait);
+      waited = true;
+    }
+    // x rows, the rows' partial sums of squares, the final modulation and
+    // (OUT) this wave's first h fragments, all in flight together
+    float xv[4], pv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + j * kThreads, r = i / 64, a = i % 64;
+      xv[j] = (r < rows && a < p.A) ? cx.ldf(4u * ((m0 + r) * p.A + a)) : 0.0f;
+      const int q = i / 16, r2 = i % 16;
+      pv[j] = (do_out && q < p.ssq_tiles && r2 < rows) ? cs.ldf(4u * (q * p.ldssq + m0 + r2)) : 0.0f;
+    }
+    uint4 hraw[KPW_OUT][E / 4];
+#define AE_ISSUE_H(c0)                                                                      \
+  _Pragma("unroll") for (int c = 0; c < KPW_OUT; ++c) {                                      \
+    const int kf = wave + 4 * ((c0) + c);                                                   \
+    const int k = kf * KSTEP + E * (lane / 16);                                             \
+    _Pragma("unroll") for (int q = 0; q < E / 4; ++q) hraw[c][q] =                           \
+        (do_out && kf < kfr && row < rows) ? ch.ld16(4u * ((m0 + row) * p.D + k + 4 * q))   \
+                                           : make_uint4(0, 0, 0, 0);                        \
+  }
+    AE_ISSUE_H(0)
+    if (do_out) {
+      const float* sf = p.fmod + static_cast<size_t>(step) * 2 * p.D;
+      for (int i = tid; i < 2 * p.D; i += kThreads) s_f[i] = i < p.D ? 1.0f + sf[i] : sf[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + j * kThreads;
+      s_x[i] = xv[j];
+      if (i / 16 < p.ssq_tiles) s_part[i] = pv[j];
+    }
+    __syncthreads();
+    if (do_out && tid < rows) {
+      float acc = 0.0f;
+      for (int q = 0; q < p.ssq_tiles; ++q) acc += s_part[q * 16 + tid];
+      s_r[tid] = 1.0f / sqrtf(acc / static_cast<float>(p.D) + p.eps);
+    }
+    __syncthreads();
+
+    if (do_out) {
+      const float rr = row < rows ? s_r[row] : 0.0f;
+      f32x4 acc[kAB];
+#pragma unroll
+      for (int j = 0; j < kAB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; wave + 4 * c0 < kfr; c0 += KPW_OUT) {
+        if (c0 > 0) {
+          AE_ISSUE_WOUT(c0)
+          AE_ISSUE_H(c0)
+        }
+#pragma unroll
+        for (int c = 0; c < KPW_OUT; ++c) {
+          const int kf = wave + 4 * (c0 + c);
+          if (kf >= kfr) continue;
+          const int k = kf * KSTEP + E * (lane / 16);
+          float v[E];
+#pragma unroll
+          for (int q = 0; q < E / 4; ++q) {
+            const uint4 hv = hraw[c][q];
+            const float hx[4] = {__uint_as_float(hv.x), __uint_as_float(hv.y), __uint_as_float(hv.z),
+                                 __uint_as_float(hv.w)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[4 * q + e] = row < rows ? hx[e] * rr * s_f[k + 4 * q + e] + s_f[p.D + k + 4 * q + e] : 0.0f;
+          }
+          uint4 hi, lo;
+          split_frag<T>(v, hi, lo);
+#pragma unroll
+          for (int j = 0; j < kAB; ++j)
+            if (j < p.a_blocks) {
+              acc[j] = MM::mma(hi, wo[c][j], acc[j]);
+              if (kSplit) acc[j] = MM::mma(lo, wo[c][j], acc[j]);
+            }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kAB; ++j) s_red[(wave * 4 + j) * kWave + lane] = acc[j];
+      __syncthreads();
+      // x += dt (v + b_out); result row 4*(lane/16)+e, column 16 j + lane % 16
+      {
+        const int j = tid / kWave, ln = tid % kWave;
+        if (j < p.a_blocks) {
+          const f32x4 v = s_red[(0 * 4 + j) * kWave + ln] + s_red[(1 * 4 + j) * kWave + ln] +
+                          s_red[(2 * 4 + j) * kWave + ln] + s_red[(3 * 4 + j) * kWave + ln];
+          const int a = 16 * j + ln % 16;
+          const float bo = a < p.A ? p.b_out[a] : 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * (ln / 16) + e;
+            if (r < rows && a < p.A) {
+              const float xn = s_x[r * 64 + a] + p.dt * (v[e] + bo);
+              s_x[r * 64 + a] = xn;
+              cx.stf(4u * ((m0 + r) * p.A + a), xn);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    if (do_in) {
+      // h[16 x D] = x[16 x A] . W_in + b_in; wave w takes column blocks w + 4q
+      AE_ISSUE_WIN(0)
+      uint4 ahi[kAF], alo[kAF];
+#pragma unroll
+      for (int f = 0; f < kAF; ++f) {
+        float v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = s_x[row * 64 + f * KSTEP + E * (lane / 16) + e];
+        split_frag<T>(v, ahi[f], alo[f]);
+      }
+      for (int q0 = 0; wave + 4 * q0 < nb; q0 += CPW_IN) {
+        if (q0 > 0) {
+          AE_ISSUE_WIN(q0)
+        }
+#pragma unroll
+        for (int q = 0; q < CPW_IN; ++q) {
+          const int cb = wave + 4 * (q0 + q);
+          // 64-column tile cb / 4 is assembled from the four waves' blocks
+          float sq[4] = {0.f, 0.f, 0.f, 0.f};
+          if (cb < nb) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int f = 0; f < kAF; ++f)
+              if (f < p.a_frags) {
+                acc = MM::mma(ahi[f], wi[q][f], acc);
+                if (kSplit) acc = MM::mma(alo[f], wi[q][f], acc);
+              }
+            const int n = 16 * cb + lane % 16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * (lane / 16) + e;
+              const float hv = acc[e] + bi[q];
+              if (r < rows) {
+                ch.stf(4u * ((m0 + r) * p.D + n), hv);
+                sq[e] = hv * hv;
+              }
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sq[e] = row16_sum(sq[e]);
+          if (lane % 16 == 0)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_sq[(q * 4 + wave) * 16 + 4 * (lane / 16) + e] = sq[e];
+          __builtin_amdgcn_sched_barrier(0);  // one output block at a time
+        }
+        __syncthreads();
+        // tile (q0 + q): blocks 4 (q0 + q) + w, w = 0..3
+        for (int i = tid; i < CPW_IN * 16; i += kThreads) {
+          const int q = i / 16, r = i % 16;
+          const int tile = q0 + q;
+          if (r < rows && 64 * tile < p.D) {
+            float t = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) t += s_sq[(q * 4 + w) * 16 + r];
+            cs.stf(4u * (tile * p.ldssq + m0 + r), t);
+          }
+        }
+        __syncthreads();
+      }
+    }
+    __syncthreads();
+  }
+#undef AE_ISSUE_WOUT
+#undef AE_ISSUE_WIN
+#undef AE_ISSUE_H
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs p) {
+  // gemm: 64 KiB reduction / tile + rms scratch; out/in: smaller
+  __shared__ __attribute__((aligned(16))) char smem[4 * (kTileM / 16) * (kTileN / 16) * kWave * 16 + 24 * 1024];
+  const size_t kv_layer = p.kv_layer;
+  int* cq = p.pcnt;
+  int* co = cq + p.pq.n_tiles;
+  int* cg = co + p.po.n_tiles;
+  int* cd = cg + p.pg.n_tiles;
+  int gen = 0;
+  outin_phase<T>(p, 0, false, true, 0, smem);  // h from x_0
+  bar_arrive(p, ++gen);
+  for (int k = 0; k < p.n_steps; ++k) {
+    for (int l = 0; l < p.L; ++l) {
+      const int it = k * p.L + l;
+      const float* md = p.mod + (static_cast<size_t>(k) * p.L + l) * 6 * p.D;
+      void* kc = static_cast<char*>(p.kcache) + l * kv_layer * sizeof(T);
+      void* vt = static_cast<char*>(p.vtcache) + l * kv_layer * sizeof(T);
+      GemmLayer ly;
+      ly.kc = kc;
+      ly.vt = vt;
+      ly.gate = nullptr;
+
+      ly.W = p.wqkv + l * p.sqkv; ly.A = p.h; ly.lda = p.D; ly.scale = md; ly.shift = md + p.D;
+      gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, p.pq, ly, cq, it, gen, smem);
+      bar_arrive(p, ++gen);
+
+      attention_phase<T, DH>(p, kc, vt, it, gen, smem);
+      bar_arrive(p, ++gen);
+
+      ly.W = p.wo + l * p.so; ly.A = p.o; ly.lda = p.qdim; ly.gate = md + 2 * p.D;
+      gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.po, ly, co, it, gen, smem);
+      bar_arrive(p, ++gen);
+
+      ly.W = p.wgu + l * p.sgu; ly.A = p.h; ly.lda = p.D; ly.scale = md + 3 * p.D; ly.shift = md + 4 * p.D;
+      gemm_phase<T, PRO_ADARMS, EPI_GELU>(p, p.pg, ly, cg, it, gen, smem);
+      bar_arrive(p, ++gen);
+
+      ly.W = p.wd + l * p.sd; ly.A = p.act; ly.lda = p.F; ly.gate = md + 5 * p.D;
+      gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.pd, ly, cd, it, gen, smem);
+      bar_arrive(p, ++gen);
+    }
+    outin_phase<T>(p, k, true, k + 1 < p.n_steps, gen, smem);
+    bar_arrive(p, ++gen);
+  }
+}
+
+template <typename T, int DH>
+hipError_t launch_p(const PersistArgs& a, hipStream_t s) {
+  void* args[] = {const_cast<PersistArgs*>(&a)};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(persist_kernel<T, DH>), dim3(a.G),
+                                    dim3(kThreads), args, 0, s);
+}
+
+template <typename T, int DH>
+int occupancy_p() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persist_kernel<T, DH>, kThreads, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+__global__ void fill_int_kernel(int* a, int na, int* b, int nb) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < na + nb; i += gridDim.x * blockDim.x) {
+    if (i < na) a[i] = 0;
+    else b[i - na] = 0;
+  }
+}
+
+}  // namespace
+
+int persist_kpw() { return kKpw; }
+int persist_max_grid() { return kMaxG; }
+
+int persist_blocks_per_cu(Dt dt, int dh) {
+  if (dt == DT_BF16) {
+    if (dh == 64) return occupancy_p<bf16_t, 64>();
+    if (dh == 128) return occupancy_p<bf16_t, 128>();
+    if (dh == 256) return occupancy_p<bf16_t, 256>();
+  } else {
+    if (dh == 64) return occupancy_p<float, 64>();
+    if (dh == 128) return occupancy_p<float, 128>();
+    if (dh == 256) return occupancy_p<float, 256>();
+  }
+  return 0;
+}
+
+hipError_t launch_persist(Dt dt, const PersistArgs& a, hipStream_t s) {
+  if (a.G < 1 || a.G > kMaxG) return hipErrorInvalidValue;
+  const int n_cnt = a.pq.n_tiles + a.po.n_tiles + a.pg.n_tiles + a.pd.n_tiles;
+  hipLaunchKernelGGL(fill_int_kernel, dim3(4), dim3(256), 0, s, a.flags, a.G, a.pcnt, n_cnt + a.n_acnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dt == DT_BF16) {
+    if (a.dh == 64) return launch_p<bf16_t, 64>(a, s);
+    if (a.dh == 128) return launch_p<bf16_t, 128>(a, s);
+    if (a.dh == 256) return launch_p<bf16_t, 256>(a, s);
+  } else {
+    if (a.dh == 64) return launch_p<float, 64>(a, s);
+    if (a.dh == 128) return launch_p<float, 128>(a, s);
+    if (a.dh == 256) return launch_p<float, 256>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ae

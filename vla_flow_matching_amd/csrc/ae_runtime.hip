@@ -65,8 +65,17 @@ struct ae_handle {
   float *gpart = nullptr, *apart = nullptr;
   int *gcnt = nullptr, *acnt = nullptr;
 
+  // persistent whole-call kernel (batch * T <= 64)
+  uint4 *win_p = nullptr, *wout_p = nullptr;
+  int a_frags = 0, a_blocks = 0;
+  int *flags = nullptr, *derr = nullptr;
+  int* pcnt = nullptr;  // the persistent kernel's monotonic split counters
+  int G = 0;              // resident workgroups of the persistent kernel (0: unavailable)
+  bool persist_graph = true;  // cooperative launch can be captured
+
   bool weights_loaded = false;
   int prefix_batch = -1;
+  int table_steps = -1;  // step count the modulation table currently holds
   hipStream_t cap_stream = nullptr;
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
   ae_stats stats{};
@@ -178,6 +187,42 @@ LayerPlans plan_layer(const ae_handle* h, int M) {
   return p;
 }
 
+// Persistent path: one row tile; split K so that the tasks of a phase cover
+// the resident workgroups once and every wave holds at most persist_kpw()
+// weight fragments in registers.
+PGemm plan_pgemm(const ae_handle* h, int N, int K) {
+  PGemm g;
+  g.n_tiles = N / kTileN;
+  g.k_frags = K / kstep_of(h->dt);
+  int s = h->G / g.n_tiles;
+  const int kpw = persist_kpw();
+  const int min_s = (g.k_frags + 4 * kpw - 1) / (4 * kpw);
+  if (s < min_s) s = min_s;
+  if (s > g.k_frags) s = g.k_frags;
+  if (s < 1) s = 1;
+  g.ksplit = s;
+  return g;
+}
+
+struct PersistPlans {
+  PGemm q, o, g, d;
+};
+
+PersistPlans plan_persist(const ae_handle* h) {
+  PersistPlans p;
+  p.q = plan_pgemm(h, h->qkv_n, h->D);
+  p.o = plan_pgemm(h, h->D, h->qdim);
+  p.g = plan_pgemm(h, 2 * h->F, h->D);
+  p.d = plan_pgemm(h, h->D, h->F);
+  return p;
+}
+
+// The whole-call kernel covers one 64-row tile and action_dim <= 32; other
+// shapes run the per-phase kernels.
+bool use_persist(const ae_handle* h, int batch) {
+  return h->G > 0 && batch * h->T <= kTileM && h->A <= 32;
+}
+
 size_t gemm_scratch_floats(const GemmPlan& g) {
   return g.ksplit > 1 ? static_cast<size_t>(g.m_tiles) * g.n_tiles * g.ksplit * kTileM * kTileN : 0;
 }
@@ -205,13 +250,12 @@ GemmArgs base_gemm(const ae_handle* h, const GemmPlan& g, int M, int K) {
     if (e_ != hipSuccess) return hip_fail(h, e_, #call);     \
   } while (0)
 
-// Enqueue one whole denoise call (t-path + steps) reading and writing the
-// static buffers; used both directly and under stream capture.
-ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
-  const int D = h->D, L = h->L, M = batch * h->T;
-  const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
-
-  // time path, once per call
+// The time path: sinusoidal embeddings of t_k, the time MLP and every
+// layer's modulation (scale/shift/gate) plus the final norm's, for all steps
+// of a call.  It depends only on the step count and the weights, so its table
+// is kept and recomputed only when the step count changes or weights load.
+ae_status enqueue_tpath(ae_handle* h, int steps, hipStream_t s) {
+  const int D = h->D, L = h->L;
   AE_LAUNCH(launch_tpath_sinusoid(h->e, steps, D, s));
   for (int r0 = 0; r0 < steps; r0 += 16) {
     const int mr = std::min(16, steps - r0);
@@ -226,7 +270,14 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
                                h->fmod_b, 2 * D, h->fmod + static_cast<size_t>(r0) * 2 * D, 2 * D, 0,
                                1, 0, 0, 0, s));
   }
+  return AE_OK;
+}
 
+// Enqueue the N Euler steps of one denoise call, reading and writing the
+// static buffers; used both directly and under stream capture.
+ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
+  const int D = h->D, L = h->L, M = batch * h->T;
+  const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const LayerPlans lp = plan_layer(h, M);
   const AttnPlan ap = plan_attention(h, batch);
   const float dt = -1.0f / static_cast<float>(steps);
@@ -276,6 +327,35 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
                                 h->b_out, dt, s));
   }
   return AE_OK;
+}
+
+PersistArgs persist_args(const ae_handle* h, int batch, int steps) {
+  PersistArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.M = batch * h->T; a.D = h->D; a.L = h->L; a.n_steps = steps; a.T = h->T; a.A = h->A;
+  a.Hq = h->Hq; a.Hkv = h->Hkv; a.dh = h->dh; a.F = h->F; a.S_max = h->S_max; a.qdim = h->qdim;
+  a.ssq_tiles = h->ssq_tiles; a.ldssq = h->Mmax; a.batch = batch; a.G = h->G;
+  a.eps = h->cfg.rms_eps;
+  a.dt = -1.0f / static_cast<float>(steps);
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->dh)));
+  a.wqkv = h->wqkv; a.wo = h->wo; a.wgu = h->wgu; a.wd = h->wd;
+  a.sqkv = h->sqkv; a.so = h->so; a.sgu = h->sgu; a.sd = h->sd;
+  a.win_p = h->win_p; a.wout_p = h->wout_p; a.a_frags = h->a_frags; a.a_blocks = h->a_blocks;
+  a.b_in = h->b_in; a.b_out = h->b_out; a.mod = h->mod; a.fmod = h->fmod;
+  a.kcache = h->kcache; a.vtcache = h->vtcache;
+  a.kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh;
+  a.n_valid = h->n_valid; a.rope_cos = h->rope_cos; a.rope_sin = h->rope_sin;
+  a.x = h->x; a.h = h->h; a.ssq = h->ssq; a.q = h->q; a.o = h->o; a.act = h->act;
+  a.gpart = h->gpart; a.gcnt = h->gcnt; a.apart = h->apart; a.acnt = h->acnt;
+  a.flags = h->flags; a.err = h->derr;
+  a.pcnt = h->pcnt;
+  const PersistPlans pp = plan_persist(h);
+  a.pq = pp.q; a.po = pp.o; a.pg = pp.g; a.pd = pp.d;
+  const AttnPlan ap = plan_attention(h, batch);
+  a.n_qg = ap.n_qg; a.nsplit = ap.nsplit; a.kc_len = ap.kc_len;
+  a.n_acnt = ap.items;
+  a.acnt = h->pcnt + pp.q.n_tiles + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
+  return a;
 }
 
 void drop_graphs(ae_handle* h) {
@@ -339,6 +419,13 @@ const char* ae_last_error(const ae_handle* h) { return h ? h->err.c_str() : "nul
 ae_status ae_get_stats(const ae_handle* h, ae_stats* out) {
   if (!h || !out) return AE_ERR_INVALID_ARGUMENT;
   *out = h->stats;
+  int derr = 0;
+  if (h->derr && hipMemcpy(&derr, h->derr, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    derr = -1;
+  }
+  out->device_errors = derr;
+  out->persistent = h->G > 0 ? h->G : 0;
   return AE_OK;
 }
 
@@ -389,6 +476,18 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   h->Mmax = h->Bmax * h->T;
 
   const int ks = kstep_of(h->dt);
+  {
+    // the persistent kernel needs every workgroup resident at once
+    int dev = 0, coop = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        coop && persist_blocks_per_cu(h->dt, h->dh) >= 1)
+      h->G = std::min(cus, persist_max_grid());
+    (void)hipGetLastError();
+  }
+  h->a_frags = (h->A + ks - 1) / ks;
+  h->a_blocks = (h->A + 15) / 16;
   const size_t es = h->esz;
   const size_t D = h->D, L = h->L, F = h->F, A = h->A;
   ae_status st = AE_OK;
@@ -451,6 +550,29 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
     if (ap.nsplit > 1) afl = std::max(afl, attention_partial_floats(h->dh, ap.items, ap.nsplit));
     acn = std::max(acn, static_cast<size_t>(ap.items));
   }
+  if (h->G > 0) {
+    const PersistPlans pp = plan_persist(h);
+    for (const PGemm* g : {&pp.q, &pp.o, &pp.g, &pp.d}) {
+      if (g->ksplit > 1)
+        gfl = std::max(gfl, static_cast<size_t>(g->n_tiles) * g->ksplit * kTileM * kTileN);
+      gcn = std::max(gcn, static_cast<size_t>(g->n_tiles));
+    }
+  }
+  AE_ALLOC(h->win_p, elems_packed(h->a_frags * ks, h->D, ks) * 16);
+  AE_ALLOC(h->wout_p, elems_packed(h->D, 16 * h->a_blocks, ks) * 16);
+  AE_ALLOC(h->flags, static_cast<size_t>(h->G > 0 ? h->G : 1) * 4);
+  {
+    size_t n = 1;
+    if (h->G > 0) {
+      const PersistPlans pp = plan_persist(h);
+      n = static_cast<size_t>(pp.q.n_tiles) + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
+      int items = 0;
+      for (int b = 1; b <= h->Bmax && b * h->T <= kTileM; ++b) items = std::max(items, plan_attention(h, b).items);
+      n += items;
+    }
+    AE_ALLOC(h->pcnt, n * 4);
+  }
+  AE_ALLOC(h->derr, 4);
   AE_ALLOC(h->gpart, gfl * 4);
   AE_ALLOC(h->gcnt, gcn * 4);
   AE_ALLOC(h->apart, afl * 4);
@@ -517,16 +639,24 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
   };
   drop_graphs(h);
   h->weights_loaded = false;
+  h->table_steps = -1;
   AE_HIP(h, cp(h->tw1, "time_mlp.1.w", D * D * es));
   AE_HIP(h, cp(h->tb1, "time_mlp.1.b", D * es));
   AE_HIP(h, cp(h->tw2, "time_mlp.2.w", D * D * es));
   AE_HIP(h, cp(h->tb2, "time_mlp.2.b", D * es));
   AE_HIP(h, cp(h->fmod_w, "final_mod.w", D * 2 * D * es));
   AE_HIP(h, cp(h->fmod_b, "final_mod.b", 2 * D * es));
-  AE_HIP(h, launch_to_f32(h->dt, get("action_in.w"), h->w_in, static_cast<size_t>(h->A) * D, st));
-  AE_HIP(h, launch_to_f32(h->dt, get("action_in.b"), h->b_in, D, st));
-  AE_HIP(h, launch_to_f32(h->dt, get("action_out.w"), h->w_out, static_cast<size_t>(h->A) * D, st));
-  AE_HIP(h, launch_to_f32(h->dt, get("action_out.b"), h->b_out, h->A, st));
+  AE_HIP(h, launch_to_f32(h->dt, get("action_in.w"), h->w_in, static_cast<size_t>(h->A) * D, 0, st));
+  AE_HIP(h, launch_to_f32(h->dt, get("action_in.b"), h->b_in, D, 0, st));
+  AE_HIP(h, launch_to_f32(h->dt, get("action_out.w"), h->w_out, static_cast<size_t>(h->A) * D, h->A, st));
+  AE_HIP(h, launch_to_f32(h->dt, get("action_out.b"), h->b_out, h->A, 0, st));
+  {
+    const int ks = kstep_of(h->dt);
+    AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get("action_in.w"), nullptr, nullptr, h->a_frags * ks, h->D,
+                          h->D, 0, 0, h->Hq, h->Hkv, h->dh, h->win_p, st, h->A, h->D));
+    AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get("action_out.w"), nullptr, nullptr, h->D, 16 * h->a_blocks,
+                          h->A, 0, 0, h->Hq, h->Hkv, h->dh, h->wout_p, st, h->D, h->A));
+  }
   for (int l = 0; l < h->L; ++l) {
     const std::string p = "layers." + std::to_string(l) + ".";
     AE_HIP(h, cp(static_cast<char*>(h->mod_w) + l * D * 6 * D * es, p + "mod.w", D * 6 * D * es));
@@ -580,27 +710,42 @@ ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, flo
                 "steps " + std::to_string(steps) + " outside [1, " + std::to_string(h->Nmax) + "]");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t xbytes = static_cast<size_t>(batch) * h->T * h->A * 4;
+  if (h->table_steps != steps) {
+    h->table_steps = -1;
+    ae_status s = enqueue_tpath(h, steps, st);
+    if (s != AE_OK) return s;
+    h->table_steps = steps;
+  }
   AE_HIP(h, hipMemcpyAsync(h->x, noise, xbytes, hipMemcpyDeviceToDevice, st));
+  const bool persist = use_persist(h, batch);
+  auto enqueue = [&](hipStream_t s) -> ae_status {
+    if (persist) {
+      const PersistArgs a = persist_args(h, batch, steps);
+      const hipError_t e = launch_persist(h->dt, a, s);
+      return e == hipSuccess ? AE_OK : hip_fail(h, e, "launch_persist");
+    }
+    return enqueue_loop(h, batch, steps, s);
+  };
   bool ran = false;
-  if (h->cfg.use_graphs) {
+  if (h->cfg.use_graphs && !(persist && !h->persist_graph)) {
     const auto key = std::make_pair(batch, steps);
     auto it = h->graphs.find(key);
     if (it == h->graphs.end() && static_cast<int>(h->graphs.size()) < kMaxGraphs) {
       AE_HIP(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeRelaxed));
-      ae_status s = enqueue_loop(h, batch, steps, h->cap_stream);
+      ae_status s = enqueue(h->cap_stream);
       hipGraph_t graph = nullptr;
       hipError_t e = hipStreamEndCapture(h->cap_stream, &graph);
-      if (s != AE_OK) {
-        if (graph) (void)hipGraphDestroy(graph);
-        return s;
-      }
-      if (e != hipSuccess) return hip_fail(h, e, "hipStreamEndCapture");
       hipGraphExec_t exec = nullptr;
-      e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-      (void)hipGraphDestroy(graph);
-      if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
-      it = h->graphs.emplace(key, exec).first;
-      h->stats.graph_captures++;
+      if (s == AE_OK && e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      if (graph) (void)hipGraphDestroy(graph);
+      if (s != AE_OK || e != hipSuccess) {
+        (void)hipGetLastError();
+        if (!persist) return s != AE_OK ? s : hip_fail(h, e, "graph capture");
+        h->persist_graph = false;  // cooperative launches not capturable here: launch directly
+      } else {
+        it = h->graphs.emplace(key, exec).first;
+        h->stats.graph_captures++;
+      }
     }
     if (it != h->graphs.end()) {
       AE_HIP(h, hipGraphLaunch(it->second, st));
@@ -609,7 +754,7 @@ ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, flo
     }
   }
   if (!ran) {
-    ae_status s = enqueue_loop(h, batch, steps, st);
+    ae_status s = enqueue(st);
     if (s != AE_OK) return s;
     h->stats.eager_runs++;
   }
