@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 
 # Sources the whole-call kernel is compiled from; a stored counter reading
 # is reported only while their digest is the one it was taken with.
@@ -74,6 +75,17 @@ def algorithmic_work(w, n_valid, with_time_path=False):
     attn_flops = sum(4 * T * w.n_q_heads * w.head_dim * (int(n) + T) for n in n_valid) * L * N
     flops_call = 2 * B * T * step_params * N + attn_flops + (2 * N * t_params if with_time_path else 0)
     return bytes_call, flops_call
+
+
+def fp8_flops_split(w, n_valid):
+    """(FLOPs of the e4m3 GEMMs: QKV, gate/up, down; all other FLOPs) per call."""
+    D, L, F, T, N = w.width, w.n_layers, w.mlp_dim, w.action_horizon, w.n_steps
+    qd, kd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    B = len(n_valid)
+    fp8_params = L * (D * (qd + 2 * kd) + 2 * D * F + F * D)
+    f8 = 2 * B * T * fp8_params * N
+    _, total = algorithmic_work(w, n_valid)
+    return f8, total - f8
 
 
 def run_gpu(name, steps, warmup):
@@ -149,6 +161,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--secondary", default="c5", help="batched workload, or 'none'")
+    ap.add_argument("--fp8", default="c5fp8", help="batched fp8 workload, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,6 +224,24 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
                          "algorithmic_flops_per_launch": f5},
+        }
+    if args.fp8 != "none":
+        sec_steps = max(5, args.steps // 8)
+        w8, nv8, ms8, _, _ = run_gpu(args.fp8, sec_steps, max(2, args.warmup // 4))
+        b8, f8 = algorithmic_work(w8, nv8)
+        fl8 = fp8_flops_split(w8, nv8)
+        # mixed peak: the fp8 GEMMs at the fp8 rate, the rest at the bf16 rate
+        t_peak = fl8[0] / (FP8_PEAK_TFLOPS * 1e12) + fl8[1] / (BF16_PEAK_TFLOPS * 1e12)
+        line["secondary_fp8"] = {
+            "workload": f"{w8.name}: batch {w8.batch}, prefix {w8.prefix_len}, {w8.n_steps} steps, "
+                        "e4m3 QKV / gate-up / down (per-tensor weight scale, per-request activation "
+                        "scale), bf16 attention and O-proj",
+            "value": w8.batch / (ms8 * 1e-3), "unit": "chunks/s", "ms_per_call": ms8, "calls": sec_steps,
+            "roofline": {"bound": "mfma (mixed fp8 / bf16 peak)",
+                         "achieved": f8 / (ms8 * 1e-3) / 1e12, "unit": "TFLOP/s",
+                         "peak_time_ms": t_peak * 1e3, "frac": t_peak / (ms8 * 1e-3),
+                         "algorithmic_flops_per_launch": f8,
+                         "fp8_flops": fl8[0], "bf16_flops": fl8[1]},
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)

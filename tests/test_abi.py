@@ -68,6 +68,17 @@ def test_unsupported_config(lib, field, value):
     assert not h.value
 
 
+def test_fp8_projection_configs(lib):
+    """fp8 e4m3 projections need bf16 activations and 128-multiple GEMM
+    widths; a valid fp8 config passes every check and then finds no device."""
+    st, h = _create(lib, proj_weight_dtype=binding.AE_FP8_E4M3)
+    assert st == binding.AE_ERR_UNSUPPORTED and not h.value
+    st, h = _create(lib, proj_weight_dtype=binding.AE_FP8_E4M3, act_dtype=binding.AE_BF16, width=192)
+    assert st == binding.AE_ERR_UNSUPPORTED and not h.value
+    st, h = _create(lib, proj_weight_dtype=binding.AE_FP8_E4M3, act_dtype=binding.AE_BF16)
+    assert st == binding.AE_ERR_HIP and not h.value
+
+
 def test_null_arguments(lib):
     assert lib.ae_create(None, None) == binding.AE_ERR_INVALID_ARGUMENT
     h = ctypes.c_void_p()

@@ -258,6 +258,72 @@ def test_c5_batched_full():
     assert err <= TOL_BF16
 
 
+@pytest.mark.parametrize("name,batch", [("c5", 2), ("c5", 3), ("c5fp8", 3)])
+def test_batched_tiles_small(name, batch):
+    """The batched path at reduced depth: 100 / 150 action rows leave a ragged
+    128-row tile; every request against the oracle (fp8: the oracle's e4m3
+    emulation with per-request activation scales)."""
+    _need_gpu()
+    w = synth.workload(name, batch=batch, n_layers=2, n_steps=2)
+    say(f"[case] {name} batch {batch}, 2 layers, 2 steps")
+    W = synth.make_weights(w)
+    g = Gpu(w, W)
+    m = synth.valid_masks(w)
+    K, V, _ = synth.make_prefix(w, mask=m, garbage="nan")
+    x0 = synth.make_noise(w)
+    Kc, Vc = K.copy(), V.copy()
+    Kc[:, m == 0] = 0.0
+    Vc[:, m == 0] = 0.0
+    check(g.run(K, V, m, x0), oracle(w, W, Kc, Vc, m, x0), TOL_BF16, f"{name} batch {batch}")
+
+
+def fp8_tolerance(w, W, K, V, m, x0, ref):
+    """Tolerance for a whole fp8 denoise call, derived from the arithmetic:
+    every projection input is re-coded to e4m3 each layer, so a difference
+    far below bf16 resolution upstream flips codes near rounding midpoints
+    and the flips compound over layers and steps.  The oracle's own output
+    moves by the returned floor / 2 when the noise is perturbed by a relative
+    1e-6 (the bf16 loop moves by ~1e-6 under the same perturbation); an
+    implementation whose intermediates differ from the oracle's by rounding
+    is held to twice that floor, and never to less than the bf16 tolerance."""
+    rng = np.random.default_rng(11)
+    x1 = (x0 * (1.0 + 1e-6 * rng.standard_normal(x0.shape))).astype(np.float32)
+    floor = float(np.abs(oracle(w, W, K, V, m, x1) - ref).max())
+    say(f"[fp8] oracle response to a 1e-6 relative noise perturbation: {floor:.3e}")
+    return max(TOL_BF16, 2.0 * floor)
+
+
+def test_c5_fp8_full():
+    """c5 with e4m3 QKV / gate-up / down weights (static per tensor) and
+    per-request dynamic activation scales: sampled requests against the
+    oracle's emulation, and a request batched against the same one alone."""
+    _need_gpu()
+    w = synth.workload("c5fp8")
+    say("[case] c5 fp8 full: batch 16, prefix 1024")
+    W = synth.make_weights(w)
+    g = Gpu(w, W)
+    m = synth.valid_masks(w)
+    K, V, _ = synth.make_prefix(w, mask=m, garbage="nan")
+    x0 = synth.make_noise(w)
+    out = g.run(K, V, m, x0)
+    assert np.isfinite(out).all()
+    w1 = synth.workload("c5fp8", batch=1)
+    tols = []
+    for b in (0, 15):
+        Kc, Vc = K[:, b:b + 1].copy(), V[:, b:b + 1].copy()
+        Kc[:, m[b:b + 1] == 0] = 0
+        Vc[:, m[b:b + 1] == 0] = 0
+        ref = oracle(w1, W, Kc, Vc, m[b:b + 1], x0[b:b + 1])
+        tols.append(fp8_tolerance(w1, W, Kc, Vc, m[b:b + 1], x0[b:b + 1], ref))
+        check(out[b:b + 1], ref, tols[-1], f"c5 fp8 request {b} (n={int(m[b].sum())})")
+    g1 = Gpu(w1, W)
+    b = 7
+    alone = g1.run(K[:, b:b + 1], V[:, b:b + 1], m[b:b + 1], x0[b:b + 1])
+    err = float(np.abs(alone - out[b:b + 1]).max())
+    say(f"[parity] c5 fp8 batched vs alone, request {b}: {err:.3e} (tol {max(tols):.3e})")
+    assert err <= max(tols)
+
+
 # --------------------------------------------------------------------------
 # reproducibility (MolmoBot PR "Correctness": replay stability, A-B-A)
 # --------------------------------------------------------------------------

@@ -116,6 +116,69 @@ hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, int trans
                          hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Batched tiled GEMM (128 x 128 tiles through LDS) with bf16 or fp8 e4m3
+// operands, and the row-norm / quantise passes in front of it.
+// ---------------------------------------------------------------------------
+
+enum Operand { OP_BF16 = 0, OP_FP8 = 1 };
+
+struct TGemmArgs {
+  const void* A;  // [M][lda] operand-typed rows (bf16 or e4m3 codes)
+  size_t lda_bytes;
+  int M, N, K;
+  const uint4* W;  // packed weights (bf16 fragments or fp8 chunks)
+  int n_tiles, m_tiles, ksplit;
+  float* partial;
+  int* counters;
+  // fp8: per-row activation scale and per-tensor weight scales
+  const float* sx_row;
+  const float* sw;
+  // EPI_RESID
+  float* h;
+  int ldh;
+  const float* gate;
+  // EPI_GELU (fp8: fp32 out plus per-(n-tile, row) max |out|)
+  void* out;
+  int ldo;
+  float* rowmax;
+  int ldp;
+  // EPI_QKV
+  void* q;
+  int ldq;
+  void* kcache;
+  void* vtcache;
+  const int* n_valid;
+  const float* rope_cos;
+  const float* rope_sin;
+  int T, Hq, Hkv, dh, S_max;
+};
+
+struct TGemmPlan {
+  int m_tiles, n_tiles, ksplit, blocks;
+};
+TGemmPlan plan_tgemm(int M, int N, int K, int kc, int target_blocks);
+int tgemm_kc(int op);
+size_t tgemm_partial_floats(const TGemmPlan& g);
+hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a, int blocks, hipStream_t s);
+
+// mode 0: u = adaRMS(h) as bf16 rows; mode 1: per-row r and max |u|
+hipError_t launch_rownorm(const float* h, int M, int D, const float* scale, const float* shift,
+                          float eps, int mode, uint16_t* u, float* r, float* rowmax, hipStream_t s);
+// e4m3 codes of fp32 rows (src) or of u recomputed from h and r (src null),
+// scaled per request by the amax over rowmax[n_part][ldp] of its rows
+hipError_t launch_quant(const float* src, const float* h, const float* r, const float* scale,
+                        const float* shift, int M, int K, int T, const float* rowmax, int n_part,
+                        int ldp, uint8_t* codes, float* sx_row, hipStream_t s);
+// fp8 weights: per-tensor amax (atomic max of the bit patterns into a zeroed
+// word), the (448 / amax, amax / 448) pairs, and the packed codes
+hipError_t launch_weight_amax(const uint16_t* w, size_t n, unsigned* out, hipStream_t s);
+hipError_t launch_fp8_scales(const unsigned* amax_bits, int n, float* mul, float* scale,
+                             hipStream_t s);
+hipError_t launch_pack_fp8(PackMode mode, const uint16_t* s0, const uint16_t* s1, const uint16_t* s2,
+                           int K, int N, int ld0, int ld1, int ld2, int Hq, int Hkv, int dh,
+                           const float* mul3, uint4* dst, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Persistent whole-call kernel (batch * T <= 64 rows)
 // ---------------------------------------------------------------------------
 

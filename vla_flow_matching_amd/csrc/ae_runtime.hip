@@ -65,6 +65,14 @@ struct ae_handle {
   float *gpart = nullptr, *apart = nullptr;
   int *gcnt = nullptr, *acnt = nullptr;
 
+  // batched tiled path: bf16, or fp8 e4m3 QKV / gate-up / down projections
+  bool tiled = false;
+  bool fp8 = false;
+  void* ubuf = nullptr;  // GEMM input rows: adaRMS output (bf16) or e4m3 codes
+  float *rrow = nullptr, *rowmax = nullptr, *sxrow = nullptr;
+  unsigned* wamax = nullptr;             // [L][6] amax bits of q, k, v, gate, up, down
+  float *wmul = nullptr, *wsc = nullptr;  // [L][6] 448 / amax and amax / 448
+
   // persistent whole-call kernel (batch * T <= 64)
   uint4 *win_p = nullptr, *wout_p = nullptr;
   int a_frags = 0, a_blocks = 0;
@@ -139,9 +147,12 @@ std::string unsupported_config(const ae_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
     return "head_dim must be 64, 128 or 256";
   if (c->proj_weight_dtype != c->act_dtype) {
-    if (c->proj_weight_dtype == AE_FP8_E4M3 && c->act_dtype == AE_BF16)
-      return "fp8 projections are not implemented yet";
-    return "proj_weight_dtype must equal act_dtype (or be AE_FP8_E4M3 with bf16)";
+    if (c->proj_weight_dtype != AE_FP8_E4M3 || c->act_dtype != AE_BF16)
+      return "proj_weight_dtype must equal act_dtype (or be AE_FP8_E4M3 with bf16)";
+    const int qkv_n = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+    if (c->width % 128 || c->mlp_dim % 128 || qkv_n % 128)
+      return "fp8 projections need width, mlp_dim and (n_q_heads + 2 n_kv_heads) * head_dim "
+             "to be multiples of 128";
   }
   return "";
 }
@@ -220,7 +231,34 @@ PersistPlans plan_persist(const ae_handle* h) {
 // The whole-call kernel covers one 64-row tile and action_dim <= 32; other
 // shapes run the per-phase kernels.
 bool use_persist(const ae_handle* h, int batch) {
-  return h->G > 0 && batch * h->T <= kTileM && h->A <= 32;
+  return h->G > 0 && !h->fp8 && batch * h->T <= kTileM && h->A <= 32;
+}
+
+// The batched tiled path: the four projection GEMMs of a layer.
+struct TPlans {
+  int op;
+  TGemmPlan qkv, o, gu, d;
+};
+
+TPlans plan_tlayer(const ae_handle* h, int M) {
+  TPlans p;
+  p.op = h->fp8 ? OP_FP8 : OP_BF16;
+  const int kc = tgemm_kc(p.op), kb = tgemm_kc(OP_BF16);
+  p.qkv = plan_tgemm(M, h->qkv_n, h->D, kc, kTargetBlocks);
+  p.o = plan_tgemm(M, h->D, h->qdim, kb, kTargetBlocks);
+  p.gu = plan_tgemm(M, 2 * h->F, h->D, kc, kTargetBlocks);
+  p.d = plan_tgemm(M, h->D, h->F, kc, kTargetBlocks);
+  return p;
+}
+
+TGemmArgs base_tgemm(const ae_handle* h, const TGemmPlan& g, int M, int N, int K) {
+  TGemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.M = M; a.N = N; a.K = K;
+  a.n_tiles = g.n_tiles; a.m_tiles = g.m_tiles; a.ksplit = g.ksplit;
+  a.partial = h->gpart; a.counters = h->gcnt;
+  a.sx_row = h->sxrow;
+  return a;
 }
 
 size_t gemm_scratch_floats(const GemmPlan& g) {
@@ -275,7 +313,10 @@ ae_status enqueue_tpath(ae_handle* h, int steps, hipStream_t s) {
 
 // Enqueue the N Euler steps of one denoise call, reading and writing the
 // static buffers; used both directly and under stream capture.
+ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s);
+
 ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
+  if (h->tiled) return enqueue_loop_tiled(h, batch, steps, s);
   const int D = h->D, L = h->L, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const LayerPlans lp = plan_layer(h, M);
@@ -321,6 +362,85 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
       g.A = h->act; g.lda = h->F; g.W = h->wd + l * h->sd;
       g.h = h->h; g.ldh = D; g.gate = md + 5 * D; g.ssq_out = h->ssq;
       AE_LAUNCH(launch_gemm(h->dt, PRO_NONE, EPI_RESID, g, lp.d.blocks, s));
+    }
+    const float* fm = h->fmod + static_cast<size_t>(k) * 2 * D;
+    AE_LAUNCH(launch_action_out(h->x, M, h->A, h->h, D, fm, fm + D, h->cfg.rms_eps, h->w_out,
+                                h->b_out, dt, s));
+  }
+  return AE_OK;
+}
+
+// The N Euler steps on the batched tiled path.  Per layer: adaRMS rows (and
+// for fp8 their per-request codes), QKV + RoPE, attention, O-proj + gated
+// residual, adaRMS rows, gate/up + gelu, (fp8: codes of the activations),
+// down + gated residual.
+ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) {
+  const int D = h->D, L = h->L, F = h->F, M = batch * h->T;
+  const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
+  const TPlans tp = plan_tlayer(h, M);
+  const AttnPlan ap = plan_attention(h, batch);
+  const float dt = -1.0f / static_cast<float>(steps);
+  const float eps = h->cfg.rms_eps;
+  const bool f8 = h->fp8;
+  const size_t ob = f8 ? 1 : 2;  // operand bytes
+  uint16_t* ub16 = static_cast<uint16_t*>(h->ubuf);
+  uint8_t* ub8 = static_cast<uint8_t*>(h->ubuf);
+  auto norm_rows = [&](const float* sc, const float* sh) -> ae_status {
+    if (!f8) {
+      AE_LAUNCH(launch_rownorm(h->h, M, D, sc, sh, eps, 0, ub16, nullptr, nullptr, s));
+    } else {
+      AE_LAUNCH(launch_rownorm(h->h, M, D, sc, sh, eps, 1, nullptr, h->rrow, h->rowmax, s));
+      AE_LAUNCH(launch_quant(nullptr, h->h, h->rrow, sc, sh, M, D, h->T, h->rowmax, 1, h->Mmax, ub8,
+                             h->sxrow, s));
+    }
+    return AE_OK;
+  };
+  for (int k = 0; k < steps; ++k) {
+    AE_LAUNCH(launch_action_in(h->x, M, h->A, h->w_in, h->b_in, h->h, D, h->ssq, h->Mmax, s));
+    for (int l = 0; l < L; ++l) {
+      const float* md = h->mod + (static_cast<size_t>(k) * L + l) * 6 * D;
+      char* kc = static_cast<char*>(h->kcache) + l * kv_layer;
+      char* vc = static_cast<char*>(h->vtcache) + l * kv_layer;
+      ae_status r = norm_rows(md, md + D);
+      if (r != AE_OK) return r;
+
+      TGemmArgs g = base_tgemm(h, tp.qkv, M, h->qkv_n, D);
+      g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wqkv + l * h->sqkv; g.sw = h->wsc + 6 * l;
+      g.q = h->q; g.ldq = h->qdim; g.kcache = kc; g.vtcache = vc; g.n_valid = h->n_valid;
+      g.rope_cos = h->rope_cos; g.rope_sin = h->rope_sin;
+      g.T = h->T; g.Hq = h->Hq; g.Hkv = h->Hkv; g.dh = h->dh; g.S_max = h->S_max;
+      AE_LAUNCH(launch_tgemm(tp.op, EPI_QKV, g, tp.qkv.blocks, s));
+
+      AttnArgs at;
+      std::memset(&at, 0, sizeof(at));
+      at.q = h->q; at.ldq = h->qdim; at.kcache = kc; at.vtcache = vc; at.S_max = h->S_max;
+      at.n_valid = h->n_valid; at.o = h->o; at.ldo = h->qdim;
+      at.T = h->T; at.Hq = h->Hq; at.Hkv = h->Hkv; at.dh = h->dh;
+      at.batch = batch; at.n_qg = ap.n_qg; at.nsplit = ap.nsplit; at.kc_len = ap.kc_len;
+      at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->dh)));
+      at.partial = h->apart; at.counters = h->acnt;
+      AE_LAUNCH(launch_attention(h->dt, at, s));
+
+      g = base_tgemm(h, tp.o, M, D, h->qdim);
+      g.A = h->o; g.lda_bytes = static_cast<size_t>(h->qdim) * 2; g.W = h->wo + l * h->so;
+      g.h = h->h; g.ldh = D; g.gate = md + 2 * D;
+      AE_LAUNCH(launch_tgemm(OP_BF16, EPI_RESID, g, tp.o.blocks, s));
+
+      r = norm_rows(md + 3 * D, md + 4 * D);
+      if (r != AE_OK) return r;
+      g = base_tgemm(h, tp.gu, M, 2 * F, D);
+      g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wgu + l * h->sgu; g.sw = h->wsc + 6 * l + 3;
+      g.out = h->act; g.ldo = F; g.rowmax = h->rowmax; g.ldp = h->Mmax;
+      AE_LAUNCH(launch_tgemm(tp.op, EPI_GELU, g, tp.gu.blocks, s));
+      if (f8)
+        AE_LAUNCH(launch_quant(static_cast<const float*>(h->act), nullptr, nullptr, nullptr, nullptr, M, F,
+                               h->T, h->rowmax, tp.gu.n_tiles, h->Mmax, ub8, h->sxrow, s));
+
+      g = base_tgemm(h, tp.d, M, D, F);
+      g.A = f8 ? h->ubuf : h->act; g.lda_bytes = F * ob; g.W = h->wd + l * h->sd;
+      g.sw = h->wsc + 6 * l + 5;
+      g.h = h->h; g.ldh = D; g.gate = md + 5 * D;
+      AE_LAUNCH(launch_tgemm(tp.op, EPI_RESID, g, tp.d.blocks, s));
     }
     const float* fm = h->fmod + static_cast<size_t>(k) * 2 * D;
     AE_LAUNCH(launch_action_out(h->x, M, h->A, h->h, D, fm, fm + D, h->cfg.rms_eps, h->w_out,
@@ -474,6 +594,9 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   h->qkv_n = h->qdim + 2 * h->kvdim;
   h->ssq_tiles = h->D / 64;
   h->Mmax = h->Bmax * h->T;
+  h->fp8 = cfg->proj_weight_dtype == AE_FP8_E4M3;
+  h->tiled = h->dt == DT_BF16 && h->D % 128 == 0 && h->qkv_n % 128 == 0 && (2 * h->F) % 128 == 0 &&
+             h->qdim % 64 == 0 && h->F % 64 == 0;
 
   const int ks = kstep_of(h->dt);
   {
@@ -532,7 +655,16 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   AE_ALLOC(h->ssq, static_cast<size_t>(h->ssq_tiles) * Mm * 4);
   AE_ALLOC(h->q, Mm * h->qdim * es);
   AE_ALLOC(h->o, Mm * h->qdim * es);
-  AE_ALLOC(h->act, Mm * F * es);
+  AE_ALLOC(h->act, Mm * F * (h->fp8 ? 4 : es));
+  if (h->tiled) {
+    AE_ALLOC(h->ubuf, Mm * std::max(D, F) * (h->fp8 ? 1 : 2));
+    AE_ALLOC(h->rrow, Mm * 4);
+    AE_ALLOC(h->sxrow, Mm * 4);
+    AE_ALLOC(h->rowmax, Mm * std::max<size_t>(1, 2 * F / 128) * 4);
+    AE_ALLOC(h->wamax, L * 6 * 4);
+    AE_ALLOC(h->wmul, L * 6 * 4);
+    AE_ALLOC(h->wsc, L * 6 * 4);
+  }
   AE_ALLOC(h->e, static_cast<size_t>(h->Nmax) * D * 4);
   AE_ALLOC(h->z, static_cast<size_t>(h->Nmax) * D * 4);
   AE_ALLOC(h->c, static_cast<size_t>(h->Nmax) * D * 4);
@@ -545,6 +677,13 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
     for (const GemmPlan* g : {&lp.qkv, &lp.o, &lp.gu, &lp.d}) {
       gfl = std::max(gfl, gemm_scratch_floats(*g));
       gcn = std::max(gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
+    }
+    if (h->tiled) {
+      const TPlans tp = plan_tlayer(h, b * h->T);
+      for (const TGemmPlan* g : {&tp.qkv, &tp.o, &tp.gu, &tp.d}) {
+        gfl = std::max(gfl, tgemm_partial_floats(*g));
+        gcn = std::max(gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
+      }
     }
     const AttnPlan ap = plan_attention(h, b);
     if (ap.nsplit > 1) afl = std::max(afl, attention_partial_floats(h->dh, ap.items, ap.nsplit));
@@ -657,14 +796,37 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
     AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get("action_out.w"), nullptr, nullptr, h->D, 16 * h->a_blocks,
                           h->A, 0, 0, h->Hq, h->Hkv, h->dh, h->wout_p, st, h->D, h->A));
   }
+  if (h->fp8) {
+    // per-tensor amax of q, k, v, gate, up, down -> (448 / amax, amax / 448)
+    AE_HIP(h, hipMemsetAsync(h->wamax, 0, static_cast<size_t>(h->L) * 6 * 4, st));
+    const char* names[6] = {"q", "k", "v", "gate", "up", "down"};
+    const size_t sizes[6] = {D * h->qdim, D * h->kvdim, D * h->kvdim, D * h->F, D * h->F,
+                             static_cast<size_t>(h->F) * D};
+    for (int l = 0; l < h->L; ++l)
+      for (int i = 0; i < 6; ++i)
+        AE_HIP(h, launch_weight_amax(static_cast<const uint16_t*>(get("layers." + std::to_string(l) + "." + names[i])),
+                                     sizes[i], h->wamax + 6 * l + i, st));
+    AE_HIP(h, launch_fp8_scales(h->wamax, h->L * 6, h->wmul, h->wsc, st));
+  }
   for (int l = 0; l < h->L; ++l) {
     const std::string p = "layers." + std::to_string(l) + ".";
     AE_HIP(h, cp(static_cast<char*>(h->mod_w) + l * D * 6 * D * es, p + "mod.w", D * 6 * D * es));
     AE_HIP(h, cp(static_cast<char*>(h->mod_b) + l * 6 * D * es, p + "mod.b", 6 * D * es));
-    AE_HIP(h, launch_pack(h->dt, PACK_QKV, get(p + "q"), get(p + "k"), get(p + "v"), h->D, h->qkv_n,
-                          h->qdim, h->kvdim, h->kvdim, h->Hq, h->Hkv, h->dh, h->wqkv + l * h->sqkv, st));
     AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get(p + "o"), nullptr, nullptr, h->qdim, h->D, h->D, 0,
                           0, h->Hq, h->Hkv, h->dh, h->wo + l * h->so, st));
+    if (h->fp8) {
+      auto b16 = [&](const std::string& nm) { return static_cast<const uint16_t*>(get(nm)); };
+      AE_HIP(h, launch_pack_fp8(PACK_QKV, b16(p + "q"), b16(p + "k"), b16(p + "v"), h->D, h->qkv_n,
+                                h->qdim, h->kvdim, h->kvdim, h->Hq, h->Hkv, h->dh, h->wmul + 6 * l,
+                                h->wqkv + l * h->sqkv, st));
+      AE_HIP(h, launch_pack_fp8(PACK_GU, b16(p + "gate"), b16(p + "up"), nullptr, h->D, 2 * h->F, h->F,
+                                h->F, 0, h->Hq, h->Hkv, h->dh, h->wmul + 6 * l + 3, h->wgu + l * h->sgu, st));
+      AE_HIP(h, launch_pack_fp8(PACK_PLAIN, b16(p + "down"), nullptr, nullptr, h->F, h->D, h->D, 0, 0,
+                                h->Hq, h->Hkv, h->dh, h->wmul + 6 * l + 5, h->wd + l * h->sd, st));
+      continue;
+    }
+    AE_HIP(h, launch_pack(h->dt, PACK_QKV, get(p + "q"), get(p + "k"), get(p + "v"), h->D, h->qkv_n,
+                          h->qdim, h->kvdim, h->kvdim, h->Hq, h->Hkv, h->dh, h->wqkv + l * h->sqkv, st));
     AE_HIP(h, launch_pack(h->dt, PACK_GU, get(p + "gate"), get(p + "up"), nullptr, h->D, 2 * h->F,
                           h->F, h->F, 0, h->Hq, h->Hkv, h->dh, h->wgu + l * h->sgu, st));
     AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get(p + "down"), nullptr, nullptr, h->F, h->D, h->D, 0,

@@ -1,0 +1,667 @@
+// Batched projection GEMMs (many action rows: B * T > 64): Y = A . W on the
+// MFMA units with 128 x 128 output tiles staged through LDS, for bf16
+// operands and for the fp8 e4m3 variant of the QKV / gate-up / down
+// projections (MolmoBot PR, Part 3: per-tensor dynamic fp8, amax -> cast ->
+// scaled matmul; LoongForge blog, section 7: inputs and weights quantised,
+// the product restored with both scales).
+//
+// Around the GEMM:
+// * rownorm_kernel forms the adaRMS input u = h * r * (1 + scale) + shift of
+//   every row once (LoongForge blog, section 2), as bf16, or - for fp8 - only
+//   the per-row r and max |u| that the request-wide scale needs.
+// * quant_kernel turns fp32 rows (u recomputed bit-identically, or the
+//   gelu * up activations) into e4m3 codes with the per-request scale
+//   amax / 448, deciding every code in fp32.
+// * The GEMM epilogues are the expert's: RoPE + q / K / V^T scatter, gelu of
+//   the gate half times the up half, and the gated residual h += gate * y.
+//   In fp8 mode y = acc * s_x(request) * s_w(tensor) first.
+//
+// A is row-major [M][lda] in the operand type; W is pre-packed in fragment
+// order so that one 128-byte k-chunk of a 16-column group is 2 KiB
+// contiguous.  Rows beyond M read a clamped (valid) row and are never
+// stored.  Split-K partials are reduced in a fixed order by the last
+// workgroup of a tile, so results do not depend on scheduling.
+#include "ae_device.h"
+#include "ae_kernels.h"
+
+namespace ae {
+
+namespace {
+
+constexpr int kTT = 256;     // threads per GEMM workgroup (2 x 2 waves)
+constexpr int kBM = 128;     // tile rows
+constexpr int kBN = 128;     // tile columns
+constexpr int kXcd = 8;
+constexpr int kChunkU4 = 1024;  // uint4 per staged operand chunk (16 KiB)
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// OCP e4m3fn encoding (round to nearest even, saturating at +-448,
+// subnormal step 2^-9): the code of the e4m3 value nearest to v.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // below the smallest normal 2^-6 the spacing is 2^-9: code = a / 2^-9
+    code = static_cast<uint32_t>(rintf(a * 512.0f));
+  } else {
+    // keep 3 fraction bits of the fp32 value, ties to even
+    const uint32_t ab = __float_as_uint(a);
+    uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) & 0xFFF00000u;
+    if (__uint_as_float(r) > 448.0f) r = __float_as_uint(448.0f);
+    code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  }
+  return sign | code;
+}
+
+// 16 fp32 values -> 16 codes (one uint4), value i in byte i.
+__device__ __forceinline__ uint4 e4m3_pack16(const float* v, float mul) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = e4m3_code(v[4 * j] * mul) | (e4m3_code(v[4 * j + 1] * mul) << 8) |
+           (e4m3_code(v[4 * j + 2] * mul) << 16) | (e4m3_code(v[4 * j + 3] * mul) << 24);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// fp8 scale pair from an amax: (448 / a, a / 448) with a = max(amax, 1e-12),
+// both divisions correctly rounded fp32.
+__device__ __forceinline__ float fp8_mul(float amax) { return 448.0f / fmaxf(amax, 1e-12f); }
+__device__ __forceinline__ float fp8_scale(float amax) { return fmaxf(amax, 1e-12f) / 448.0f; }
+
+// adaRMS of one element; the one expression both the norm and the quantiser
+// evaluate, so the fp32 u they see is the same value.
+__device__ __forceinline__ float ada(float h, float r, float sc, float sh) {
+  return h * r * (1.0f + sc) + sh;
+}
+
+// ---------------------------------------------------------------------------
+// Row norm: one wave per row, 4 rows per workgroup.
+// mode 0: u -> bf16 [M][D].  mode 1: r[row] and rowmax[row] = max_k |u|.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ h, int M, int D,
+                                                      const float* __restrict__ scale,
+                                                      const float* __restrict__ shift, float eps,
+                                                      int mode, bf16_t* __restrict__ u,
+                                                      float* __restrict__ r_out,
+                                                      float* __restrict__ rowmax) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= M) return;
+  const float4* hr = reinterpret_cast<const float4*>(h + static_cast<size_t>(row) * D);
+  const int n4 = D / 4;
+  float ss = 0.0f;
+  for (int i = lane; i < n4; i += kWave) {
+    const float4 v = hr[i];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  const float4* sc4 = reinterpret_cast<const float4*>(scale);
+  const float4* sh4 = reinterpret_cast<const float4*>(shift);
+  if (mode == 0) {
+    uint2* ur = reinterpret_cast<uint2*>(u + static_cast<size_t>(row) * D);
+    for (int i = lane; i < n4; i += kWave) {
+      const float4 v = hr[i], s = sc4[i], b = sh4[i];
+      const float o0 = ada(v.x, r, s.x, b.x), o1 = ada(v.y, r, s.y, b.y);
+      const float o2 = ada(v.z, r, s.z, b.z), o3 = ada(v.w, r, s.w, b.w);
+      ur[i] = make_uint2(static_cast<uint32_t>(f2bf(o0)) | (static_cast<uint32_t>(f2bf(o1)) << 16),
+                         static_cast<uint32_t>(f2bf(o2)) | (static_cast<uint32_t>(f2bf(o3)) << 16));
+    }
+  } else {
+    float mx = 0.0f;
+    for (int i = lane; i < n4; i += kWave) {
+      const float4 v = hr[i], s = sc4[i], b = sh4[i];
+      mx = fmaxf(mx, fabsf(ada(v.x, r, s.x, b.x)));
+      mx = fmaxf(mx, fabsf(ada(v.y, r, s.y, b.y)));
+      mx = fmaxf(mx, fabsf(ada(v.z, r, s.z, b.z)));
+      mx = fmaxf(mx, fabsf(ada(v.w, r, s.w, b.w)));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    if (lane == 0) {
+      r_out[row] = r;
+      rowmax[row] = mx;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantiser: one wave per row.  The request's amax is the max of
+// rowmax[p][rows of the request] over the n_part partial columns; the row
+// is then coded with 448 / amax.  src == nullptr: the row is u recomputed
+// from h, r and the modulation; otherwise src [M][K] fp32.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ src,
+                                                    const float* __restrict__ h,
+                                                    const float* __restrict__ r_in,
+                                                    const float* __restrict__ scale,
+                                                    const float* __restrict__ shift, int M, int K,
+                                                    int T, const float* __restrict__ rowmax,
+                                                    int n_part, int ldp, uint8_t* __restrict__ codes,
+                                                    float* __restrict__ sx_row) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= M) return;
+  const int r0 = (row / T) * T;
+  float mx = 0.0f;
+  for (int i = lane; i < n_part * T; i += kWave) {
+    const int p = i / T, t = i % T;
+    mx = fmaxf(mx, rowmax[static_cast<size_t>(p) * ldp + r0 + t]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  const float mul = fp8_mul(mx);
+  if (lane == 0) sx_row[row] = fp8_scale(mx);
+  const int n16 = K / 16;
+  uint4* out = reinterpret_cast<uint4*>(codes + static_cast<size_t>(row) * K);
+  for (int i = lane; i < n16; i += kWave) {
+    float v[16];
+    if (src) {
+      const float4* s4 = reinterpret_cast<const float4*>(src + static_cast<size_t>(row) * K) + 4 * i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 x = s4[j];
+        v[4 * j] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
+      }
+    } else {
+      const float r = r_in[row];
+      const float4* h4 = reinterpret_cast<const float4*>(h + static_cast<size_t>(row) * K) + 4 * i;
+      const float4* c4 = reinterpret_cast<const float4*>(scale) + 4 * i;
+      const float4* b4 = reinterpret_cast<const float4*>(shift) + 4 * i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 x = h4[j], s = c4[j], b = b4[j];
+        v[4 * j] = ada(x.x, r, s.x, b.x);
+        v[4 * j + 1] = ada(x.y, r, s.y, b.y);
+        v[4 * j + 2] = ada(x.z, r, s.z, b.z);
+        v[4 * j + 3] = ada(x.w, r, s.w, b.w);
+      }
+    }
+    out[i] = e4m3_pack16(v, mul);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The tiled GEMM.
+//
+// Operand chunk in LDS (16 KiB): [8 groups of 16 rows or columns][2 slots]
+// [64 lanes][16 bytes].  bf16: slot s is k-fragment s of the 64-wide
+// chunk, lane l holds row l%16, k = 32s + 8(l/16) .. +7.  fp8: the chunk is
+// one 128-wide k-fragment of the 16x16x128 MFMA; lane l holds row l%16 and
+// k = 32(l/16) .. +31, slot s its bytes 16s .. 16s+15.  A and B use the same
+// map, so the hardware pairs matching k on both sides.
+// ---------------------------------------------------------------------------
+template <int OP> struct TOp;
+template <> struct TOp<OP_BF16> {
+  static constexpr int KC = 64;  // k per chunk
+  static __device__ __forceinline__ int slot_lane(int kc, int r16, int& lane) {
+    lane = r16 + 16 * (kc & 3);
+    return kc >> 2;
+  }
+};
+template <> struct TOp<OP_FP8> {
+  static constexpr int KC = 128;
+  static __device__ __forceinline__ int slot_lane(int kc, int r16, int& lane) {
+    lane = r16 + 16 * (kc >> 1);
+    return kc & 1;
+  }
+};
+
+__device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x4 c) {
+  const i32x8 a = {static_cast<int>(a0.x), static_cast<int>(a0.y), static_cast<int>(a0.z),
+                   static_cast<int>(a0.w), static_cast<int>(a1.x), static_cast<int>(a1.y),
+                   static_cast<int>(a1.z), static_cast<int>(a1.w)};
+  const i32x8 b = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z),
+                   static_cast<int>(b0.w), static_cast<int>(b1.x), static_cast<int>(b1.y),
+                   static_cast<int>(b1.z), static_cast<int>(b1.w)};
+  // formats 0/0: e4m3 on both sides; scales 127 = 2^0 (no block scaling)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// One staged chunk times the wave's 64 x 64 block of the tile.
+template <int OP>
+__device__ __forceinline__ void tg_compute(const uint4* A, const uint4* B, int wm, int wn, int lane,
+                                           f32x4 (&acc)[4][4]) {
+  if (OP == OP_BF16) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = A[((4 * wm + i) * 2 + s) * kWave + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = B[((4 * wn + j) * 2 + s) * kWave + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+    }
+  } else {
+    uint4 a[4][2], b[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) a[i][s] = A[((4 * wm + i) * 2 + s) * kWave + lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) b[j][s] = B[((4 * wn + j) * 2 + s) * kWave + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp8(a[i][0], a[i][1], b[j][0], b[j][1], acc[i][j]);
+  }
+}
+
+// Tile decode: the m-tiles and K splits of one n-tile run on one XCD
+// (workgroups are dealt to the 8 XCDs round-robin) so they share its L2.
+__device__ __forceinline__ bool tile_of(int bid, int n_tiles, int m_tiles, int ksplit, int& nt,
+                                        int& mt, int& s) {
+  const int xcd = bid % kXcd;
+  int idx = bid / kXcd;
+  s = idx % ksplit;
+  idx /= ksplit;
+  mt = idx % m_tiles;
+  idx /= m_tiles;
+  nt = idx * kXcd + xcd;
+  return nt < n_tiles;
+}
+
+template <int OP, int EPI>
+__global__ __launch_bounds__(kTT) void tgemm_kernel(TGemmArgs p) {
+  using O = TOp<OP>;
+  constexpr int KC = O::KC;
+  // two stages of A and B chunks; the finished tile reuses the space
+  __shared__ __attribute__((aligned(16))) uint4 s_buf[kBM * (kBN + 1) / 4 + 4];
+  static_assert(sizeof(s_buf) >= 4 * kChunkU4 * sizeof(uint4), "stages fit");
+  // stage st: A chunk at s_buf + st * kChunkU4, B chunk at s_buf + (2 + st) * kChunkU4
+  auto s_y = reinterpret_cast<float (*)[kBN + 1]>(s_buf);
+  __shared__ int s_flag;
+
+  int nt, mt, ks;
+  if (!tile_of(blockIdx.x, p.n_tiles, p.m_tiles, p.ksplit, nt, mt, ks)) return;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = mt * kBM;
+  const int rows = min(kBM, p.M - m0);
+  const int n_chunks = p.K / KC;
+  const int c0 = static_cast<int>((static_cast<long long>(ks) * n_chunks) / p.ksplit);
+  const int c1 = static_cast<int>((static_cast<long long>(ks + 1) * n_chunks) / p.ksplit);
+
+  // staging map: item i = tid + 256 j; A: row i/8, 16-byte column i%8;
+  // B: column group i/128, uint4 i%128 of that group's 2 KiB.
+  const uint8_t* Ab = static_cast<const uint8_t*>(p.A);
+  uint32_t a_off[4], b_off[4];
+  int a_lds[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + kTT * j;
+    const int row = i >> 3, kc = i & 7;
+    const int grow = min(m0 + row, p.M - 1);
+    a_off[j] = static_cast<uint32_t>(grow) * static_cast<uint32_t>(p.lda_bytes) + 16u * kc;
+    int ln;
+    const int slot = O::slot_lane(kc, row & 15, ln);
+    a_lds[j] = ((row >> 4) * 2 + slot) * kWave + ln;
+    b_off[j] = static_cast<uint32_t>(i >> 7) * n_chunks * 128u + (i & 127);
+  }
+  const uint4* Wt = p.W + static_cast<size_t>(nt) * 8 * n_chunks * 128;
+
+  // one chunk's staging registers: four A and four B 16-byte values per
+  // thread (native vectors, so they stay in registers across iterations)
+  struct Stage {
+    u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
+  };
+  const u32x4* Wv = reinterpret_cast<const u32x4*>(Wt);
+  u32x4* sv = reinterpret_cast<u32x4*>(s_buf);
+#define TG_LOAD(R, c)                                                              \
+  do {                                                                             \
+    const uint32_t co_ = static_cast<uint32_t>(c) * 128u;                          \
+    R.a0 = *reinterpret_cast<const u32x4*>(Ab + a_off[0] + co_);                   \
+    R.a1 = *reinterpret_cast<const u32x4*>(Ab + a_off[1] + co_);                   \
+    R.a2 = *reinterpret_cast<const u32x4*>(Ab + a_off[2] + co_);                   \
+    R.a3 = *reinterpret_cast<const u32x4*>(Ab + a_off[3] + co_);                   \
+    R.b0 = Wv[b_off[0] + co_];                                                     \
+    R.b1 = Wv[b_off[1] + co_];                                                     \
+    R.b2 = Wv[b_off[2] + co_];                                                     \
+    R.b3 = Wv[b_off[3] + co_];                                                     \
+  } while (0)
+#define TG_STORE(R, st)                                                            \
+  do {                                                                             \
+    u32x4* sa_ = sv + (st) * kChunkU4;                                             \
+    u32x4* sb_ = sv + (2 + (st)) * kChunkU4 + tid;                                 \
+    sa_[a_lds[0]] = R.a0; sa_[a_lds[1]] = R.a1; sa_[a_lds[2]] = R.a2; sa_[a_lds[3]] = R.a3; \
+    sb_[0] = R.b0; sb_[kTT] = R.b1; sb_[2 * kTT] = R.b2; sb_[3 * kTT] = R.b3;      \
+  } while (0)
+#define TG_COMPUTE(st) tg_compute<OP>(s_buf + (st) * kChunkU4, s_buf + (2 + (st)) * kChunkU4, wm, wn, lane, acc)
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Two LDS stages and two register sets: while chunk c is multiplied from
+  // LDS, chunk c+1 waits in registers for its stage and chunk c+2 is in
+  // flight.  Every split holds at least one chunk (plan_tgemm); chunk
+  // indices past the split are clamped, so the tail re-loads its last chunk
+  // into a stage nobody reads.
+  Stage r0, r1;
+  TG_LOAD(r0, c0);
+  TG_STORE(r0, 0);
+  TG_LOAD(r0, min(c0 + 1, c1 - 1));
+  __syncthreads();
+  int c = c0;
+  for (; c + 1 < c1; c += 2) {
+    TG_LOAD(r1, min(c + 2, c1 - 1));
+    TG_COMPUTE(0);
+    TG_STORE(r0, 1);
+    __syncthreads();
+    TG_LOAD(r0, min(c + 3, c1 - 1));
+    TG_COMPUTE(1);
+    TG_STORE(r1, 0);
+    __syncthreads();
+  }
+  if (c < c1) {
+    TG_COMPUTE(0);  // odd chunk count: the last chunk sits in stage 0
+    __syncthreads();  // every wave is done with the stages before s_y reuses them
+  }
+#undef TG_LOAD
+#undef TG_STORE
+#undef TG_COMPUTE
+
+  // accumulators -> LDS tile (row-major)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s_y[64 * wm + 16 * i + 4 * (lane / 16) + e][64 * wn + 16 * j + lane % 16] = acc[i][j][e];
+  __syncthreads();
+
+  if (p.ksplit > 1) {
+    // publish this split's rows of the tile (16-byte device-coherent
+    // stores), then the last of the tile's splits sums all of them in split
+    // order
+    const int tile = nt * p.m_tiles + mt;
+    const Coh cp(p.partial + static_cast<size_t>(tile) * p.ksplit * (kBM * kBN));
+    const int n4 = rows * (kBN / 4);
+    for (int i = tid; i < n4; i += kTT) {
+      const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
+      cp.st16(4u * (static_cast<uint32_t>(ks) * (kBM * kBN) + r * kBN + c4),
+              make_uint4(__float_as_uint(s_y[r][c4]), __float_as_uint(s_y[r][c4 + 1]),
+                         __float_as_uint(s_y[r][c4 + 2]), __float_as_uint(s_y[r][c4 + 3])));
+    }
+    if (!arrive_last(p.counters + tile, p.ksplit, &s_flag)) return;
+    for (int i = tid; i < n4; i += kTT) {
+      const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
+      const uint32_t off = 4u * (r * kBN + c4);
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < p.ksplit; q0 += 8) {
+        uint4 buf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          buf[j] = cp.ld16(off + 4u * static_cast<uint32_t>(min(q0 + j, p.ksplit - 1)) * (kBM * kBN));
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (q0 + j < p.ksplit)
+            t += f32x4{__uint_as_float(buf[j].x), __uint_as_float(buf[j].y), __uint_as_float(buf[j].z),
+                       __uint_as_float(buf[j].w)};
+      }
+      s_y[r][c4] = t[0]; s_y[r][c4 + 1] = t[1]; s_y[r][c4 + 2] = t[2]; s_y[r][c4 + 3] = t[3];
+    }
+    __syncthreads();
+  }
+
+  // column pair structure of the packed layout: packed column pc of this
+  // tile is pair P = 4 nt + pc / 32, half pc / 16 % 2, index pc % 16
+  if (EPI == EPI_RESID) {
+    // h += gate * y (fp8: y = acc * s_x * s_w); two columns per lane
+    for (int row = wave; row < rows; row += 4) {
+      const int m = m0 + row;
+      const float sx = OP == OP_FP8 ? p.sx_row[m] * p.sw[0] : 1.0f;
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        const int n = nt * kBN + 64 * hc + lane;
+        float* hp = p.h + static_cast<size_t>(m) * p.ldh + n;
+        *hp = *hp + p.gate[n] * (s_y[row][64 * hc + lane] * sx);
+      }
+    }
+  } else if (EPI == EPI_GELU) {
+    // lanes: 64 = 4 pairs x 16; gate half at 32 pr + jj, up half at +16
+    const int pr = lane / 16, jj = lane % 16;
+    const int f = (4 * nt + pr) * 16 + jj;
+    for (int row = wave; row < rows; row += 4) {
+      const int m = m0 + row;
+      float g = s_y[row][32 * pr + jj], u = s_y[row][32 * pr + 16 + jj];
+      if (OP == OP_FP8) {
+        const float sx = p.sx_row[m];
+        g = g * (sx * p.sw[0]);
+        u = u * (sx * p.sw[1]);
+      }
+      const float a = gelu_tanh(g) * u;
+      if (OP == OP_FP8) {
+        static_cast<float*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = a;
+        float mx = fabsf(a);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        if (lane == 0) p.rowmax[static_cast<size_t>(nt) * p.ldp + m] = mx;
+      } else {
+        static_cast<bf16_t*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = f2bf(a);
+      }
+    }
+  } else {  // EPI_QKV
+    const int pph = p.dh / 32;
+    const int pq = p.Hq * pph, pk = p.Hkv * pph;
+    const int half = p.dh / 2;
+    const int pr = lane / 16, jj = lane % 16;
+    const int P = 4 * nt + pr;
+    int seg, head, pi;
+    if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
+    else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
+    else { seg = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
+    const int j = 16 * pi + jj;
+    const float sw = OP == OP_FP8 ? p.sw[seg] : 1.0f;
+    bf16_t* qo = static_cast<bf16_t*>(p.q);
+    bf16_t* kc = static_cast<bf16_t*>(p.kcache);
+    bf16_t* vt = static_cast<bf16_t*>(p.vtcache);
+    for (int row = wave; row < rows; row += 4) {
+      const int m = m0 + row;
+      const int req = m / p.T, t = m % p.T;
+      float a = s_y[row][32 * pr + jj], b = s_y[row][32 * pr + 16 + jj];
+      if (OP == OP_FP8) {
+        const float sc = p.sx_row[m] * sw;
+        a *= sc;
+        b *= sc;
+      }
+      if (seg < 2) {
+        const size_t ti2 = (static_cast<size_t>(req) * p.T + t) * half + j;
+        const float cs = p.rope_cos[ti2], sn = p.rope_sin[ti2];
+        const float ra = a * cs - b * sn;
+        const float rb = b * cs + a * sn;
+        a = ra;
+        b = rb;
+      }
+      if (seg == 0) {
+        bf16_t* dst = qo + static_cast<size_t>(m) * p.ldq + head * p.dh;
+        dst[j] = f2bf(a);
+        dst[half + j] = f2bf(b);
+      } else {
+        const int key = p.n_valid[req] + t;
+        const size_t base = static_cast<size_t>(req) * p.Hkv + head;
+        if (seg == 1) {
+          bf16_t* dst = kc + (base * p.S_max + key) * p.dh;
+          dst[j] = f2bf(a);
+          dst[half + j] = f2bf(b);
+        } else {
+          bf16_t* dst = vt + base * p.dh * p.S_max;
+          dst[static_cast<size_t>(j) * p.S_max + key] = f2bf(a);
+          dst[static_cast<size_t>(half + j) * p.S_max + key] = f2bf(b);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp8 weights: per-tensor amax, then codes packed in the GEMM's chunk order
+// [N/16][K/128][2 slots][64 lanes][16 B] (columns reordered like the bf16
+// packing: PACK_QKV rope pairs, PACK_GU gate/up pairs).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void amax_kernel(const bf16_t* __restrict__ w, size_t n,
+                                                   unsigned* __restrict__ out) {
+  float mx = 0.0f;
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    mx = fmaxf(mx, fabsf(bf2f(w[i])));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  // non-negative floats order like their bit patterns
+  if (threadIdx.x % kWave == 0) atomicMax(out, __float_as_uint(mx));
+}
+
+__global__ void scales_kernel(const unsigned* __restrict__ amax_bits, int n, float* __restrict__ mul,
+                              float* __restrict__ scale) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float a = __uint_as_float(amax_bits[i]);
+    mul[i] = fp8_mul(a);
+    scale[i] = fp8_scale(a);
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_fp8_kernel(int mode, const bf16_t* s0, const bf16_t* s1,
+                                                       const bf16_t* s2, int K, int N, int ld0,
+                                                       int ld1, int ld2, int Hq, int Hkv, int dh,
+                                                       const float* __restrict__ mul3,
+                                                       uint4* __restrict__ dst) {
+  const int kch = K / 128;
+  const size_t total = static_cast<size_t>(N / 16) * kch * 2 * kWave;
+  for (size_t g = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; g < total;
+       g += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const int lane = static_cast<int>(g % kWave);
+    const int slot = static_cast<int>((g / kWave) % 2);
+    const size_t fr = g / (2 * kWave);
+    const int kf = static_cast<int>(fr % kch);
+    const int nb = static_cast<int>(fr / kch);
+    const int pc = 16 * nb + lane % 16;
+    const int k0 = kf * 128 + 32 * (lane / 16) + 16 * slot;
+    const bf16_t* src;
+    int ld, col, which;
+    if (mode == PACK_PLAIN) {
+      src = s0; ld = ld0; col = pc; which = 0;
+    } else {
+      const int P = pc / 32, hf = (pc / 16) % 2, jj = pc % 16;
+      if (mode == PACK_GU) {
+        src = hf ? s1 : s0; ld = hf ? ld1 : ld0; col = 16 * P + jj; which = hf;
+      } else {
+        const int pph = dh / 32, pq = Hq * pph, pk = Hkv * pph;
+        int seg, head, pi;
+        if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
+        else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
+        else { seg = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
+        src = seg == 0 ? s0 : (seg == 1 ? s1 : s2);
+        ld = seg == 0 ? ld0 : (seg == 1 ? ld1 : ld2);
+        col = head * dh + hf * (dh / 2) + 16 * pi + jj;
+        which = seg;
+      }
+    }
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = bf2f(src[static_cast<size_t>(k0 + i) * ld + col]);
+    dst[g] = e4m3_pack16(v, mul3[which]);
+  }
+}
+
+// bf16 weights in the same chunk order: [N/16][K/32][64 lanes][16 B] is
+// already it (two consecutive k-fragments are one 64-wide chunk), so the
+// bf16 GEMM reads the packing the other kernels use.
+
+}  // namespace
+
+hipError_t launch_rownorm(const float* h, int M, int D, const float* scale, const float* shift,
+                          float eps, int mode, bf16_t* u, float* r, float* rowmax, hipStream_t s) {
+  if (D % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rownorm_kernel, dim3((M + 3) / 4), dim3(256), 0, s, h, M, D, scale, shift, eps,
+                     mode, u, r, rowmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(const float* src, const float* h, const float* r, const float* scale,
+                        const float* shift, int M, int K, int T, const float* rowmax, int n_part,
+                        int ldp, uint8_t* codes, float* sx_row, hipStream_t s) {
+  if (K % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_kernel, dim3((M + 3) / 4), dim3(256), 0, s, src, h, r, scale, shift, M, K,
+                     T, rowmax, n_part, ldp, codes, sx_row);
+  return hipGetLastError();
+}
+
+TGemmPlan plan_tgemm(int M, int N, int K, int kc, int target_blocks) {
+  TGemmPlan g;
+  g.m_tiles = (M + kBM - 1) / kBM;
+  g.n_tiles = N / kBN;
+  const int chunks = K / kc;
+  const int tiles = g.m_tiles * g.n_tiles;
+  int s = (target_blocks + tiles - 1) / tiles;
+  const int max_s = chunks / 2 > 0 ? chunks / 2 : 1;  // at least two chunks per split
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  g.ksplit = s;
+  const int nt_hi = (g.n_tiles + kXcd - 1) / kXcd;
+  g.blocks = kXcd * g.ksplit * g.m_tiles * nt_hi;
+  return g;
+}
+
+int tgemm_kc(int op) { return op == OP_FP8 ? TOp<OP_FP8>::KC : TOp<OP_BF16>::KC; }
+
+size_t tgemm_partial_floats(const TGemmPlan& g) {
+  return g.ksplit > 1 ? static_cast<size_t>(g.m_tiles) * g.n_tiles * g.ksplit * kBM * kBN : 0;
+}
+
+hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a, int blocks, hipStream_t s) {
+  if (a.K % tgemm_kc(op) || a.N % kBN) return hipErrorInvalidValue;
+  dim3 grid(blocks), block(kTT);
+#define AE_TG(OPV, EPV)                                                  \
+  if (op == OPV && epi == EPV) {                                         \
+    hipLaunchKernelGGL((tgemm_kernel<OPV, EPV>), grid, block, 0, s, a);  \
+    return hipGetLastError();                                            \
+  }
+  AE_TG(OP_BF16, EPI_QKV)
+  AE_TG(OP_BF16, EPI_GELU)
+  AE_TG(OP_BF16, EPI_RESID)
+  AE_TG(OP_FP8, EPI_QKV)
+  AE_TG(OP_FP8, EPI_GELU)
+  AE_TG(OP_FP8, EPI_RESID)
+#undef AE_TG
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_weight_amax(const bf16_t* w, size_t n, unsigned* out, hipStream_t s) {
+  hipLaunchKernelGGL(amax_kernel, dim3(512), dim3(256), 0, s, w, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_scales(const unsigned* amax_bits, int n, float* mul, float* scale,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(scales_kernel, dim3((n + 63) / 64), dim3(64), 0, s, amax_bits, n, mul, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fp8(PackMode mode, const bf16_t* s0, const bf16_t* s1, const bf16_t* s2,
+                           int K, int N, int ld0, int ld1, int ld2, int Hq, int Hkv, int dh,
+                           const float* mul3, uint4* dst, hipStream_t s) {
+  if (K % 128 || N % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_fp8_kernel, dim3(1024), dim3(256), 0, s, static_cast<int>(mode), s0, s1,
+                     s2, K, N, ld0, ld1, ld2, Hq, Hkv, dh, mul3, dst);
+  return hipGetLastError();
+}
+
+}  // namespace ae
