@@ -38,12 +38,12 @@ __device__ __forceinline__ uint4 load_vt_frag<bf16_t>(const bf16_t* vrow, int kb
   uint2 lo = *reinterpret_cast<const uint2*>(vrow + ka);
   uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb);
   uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
-  const int base[2] = {ka, kb};
+  // keys at or past k_end are zeroed with selects (a branch would wait for
+  // each load on its own)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int k0 = base[i / 2] + 2 * (i % 2);
-    if (k0 >= k_end) w[i] &= 0x00000000u;
-    else if (k0 + 1 >= k_end) w[i] &= 0x0000ffffu;
+    const int k0 = (i < 2 ? ka : kb) + 2 * (i % 2);
+    w[i] &= k0 >= k_end ? 0u : (k0 + 1 >= k_end ? 0x0000ffffu : 0xffffffffu);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -53,13 +53,9 @@ template <>
 __device__ __forceinline__ uint4 load_vt_frag<float>(const float* vrow, int kb0, int grp,
                                                      int k_end) {
   const int ka = kb0 + 4 * grp;
-  float4 v = *reinterpret_cast<const float4*>(vrow + ka);
-  if (ka + 0 >= k_end) v.x = 0.f;
-  if (ka + 1 >= k_end) v.y = 0.f;
-  if (ka + 2 >= k_end) v.z = 0.f;
-  if (ka + 3 >= k_end) v.w = 0.f;
-  return make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
-                    __float_as_uint(v.w));
+  const uint4 v = *reinterpret_cast<const uint4*>(vrow + ka);
+  return make_uint4(v.x & (ka + 0 >= k_end ? 0u : 0xffffffffu), v.y & (ka + 1 >= k_end ? 0u : 0xffffffffu),
+                    v.z & (ka + 2 >= k_end ? 0u : 0xffffffffu), v.w & (ka + 3 >= k_end ? 0u : 0xffffffffu));
 }
 
 template <typename T>
@@ -123,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
                     (g * G + hh) * DH + E * grp;
 #pragma unroll
     for (int kf = 0; kf < NF; ++kf)
-      qf[kf] = qvalid ? *reinterpret_cast<const uint4*>(qrow + kf * KSTEP) : make_uint4(0, 0, 0, 0);
+      qf[kf] = *reinterpret_cast<const uint4*>(qrow + kf * KSTEP);  // rows past R: a valid row, unused
   }
 
   f32x4 acc[ND];
@@ -137,12 +133,12 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk) {
         st[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int key = kb0 + 16 * blk + lane % 16;
-        const bool kv = key < k_end;
-        const T* krow = Kb + static_cast<size_t>(kv ? key : 0) * DH + E * grp;
+        // keys past the split read its last key; their scores are masked below
+        const int key = min(kb0 + 16 * blk + lane % 16, k_end - 1);
+        const T* krow = Kb + static_cast<size_t>(key) * DH + E * grp;
 #pragma unroll
         for (int kf = 0; kf < NF; ++kf) {
-          uint4 kfr = kv ? *reinterpret_cast<const uint4*>(krow + kf * KSTEP) : make_uint4(0, 0, 0, 0);
+          const uint4 kfr = *reinterpret_cast<const uint4*>(krow + kf * KSTEP);
           st[blk] = MM::mma(kfr, qf[kf], st[blk]);
         }
       }

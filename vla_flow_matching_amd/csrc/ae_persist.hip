@@ -145,18 +145,19 @@ __device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, fl
                                          float* s_sc, float* s_sh) {
   const Coh cs(p.ssq);
   const int n = p.M * p.ssq_tiles;  // <= 64 rows x 64 tiles
+  // loads at clamped indices, all in flight together; masked at use
   float v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int i = threadIdx.x + j * kThreads;
-    v[j] = i < n ? cs.ldf(4u * ((i / p.M) * p.ldssq + i % p.M)) : 0.0f;
+    const int i = min(static_cast<int>(threadIdx.x) + j * kThreads, n - 1);
+    v[j] = cs.ldf(4u * ((i / p.M) * p.ldssq + i % p.M));
   }
   float sc[2], sh[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int i = threadIdx.x + j * kThreads;
-    sc[j] = i < k_len ? scale[k_lo + i] : 0.0f;
-    sh[j] = i < k_len ? shift[k_lo + i] : 0.0f;
+    const int i = min(static_cast<int>(threadIdx.x) + j * kThreads, k_len - 1);
+    sc[j] = scale[k_lo + i];
+    sh[j] = shift[k_lo + i];
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -470,11 +471,12 @@ __device__ __forceinline__ uint4 vt_frag<bf16_t>(const bf16_t* vrow, const Coh& 
     hi = *reinterpret_cast<const uint2*>(vrow + kb);
   }
   uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+  // keys at or past k_end are zeroed with selects (no branch: a branch
+  // would wait for each load on its own)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k0 = (i < 2 ? ka : kb) + 2 * (i % 2);
-    if (k0 >= k_end) w[i] = 0u;
-    else if (k0 + 1 >= k_end) w[i] &= 0x0000ffffu;
+    w[i] &= k0 >= k_end ? 0u : (k0 + 1 >= k_end ? 0x0000ffffu : 0xffffffffu);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -484,10 +486,10 @@ __device__ __forceinline__ uint4 vt_frag<float>(const float* vrow, const Coh& cv
                                                 bool coh, int kb0, int grp, int k_end) {
   const int ka = kb0 + 4 * grp;
   uint4 v = coh ? cv.ld16(row_off + 4u * ka) : *reinterpret_cast<const uint4*>(vrow + ka);
-  if (ka + 0 >= k_end) v.x = 0u;
-  if (ka + 1 >= k_end) v.y = 0u;
-  if (ka + 2 >= k_end) v.z = 0u;
-  if (ka + 3 >= k_end) v.w = 0u;
+  v.x &= ka + 0 >= k_end ? 0u : 0xffffffffu;
+  v.y &= ka + 1 >= k_end ? 0u : 0xffffffffu;
+  v.z &= ka + 2 >= k_end ? 0u : 0xffffffffu;
+  v.w &= ka + 3 >= k_end ? 0u : 0xffffffffu;
   return v;
 }
 
@@ -506,6 +508,41 @@ __device__ __forceinline__ void store4_coh<float>(const Coh& c, uint32_t off, co
                          __float_as_uint(v[3])));
 }
 
+constexpr int kMergeBatch = 16;  // attention splits merged per round of loads
+constexpr int kStageBlk = 2;     // key blocks staged in LDS at a time
+
+// Load one key block's K fragments (S^T = K Q^T operands) and V^T fragments
+// (O^T = V^T P^T operands) into LDS in fragment order; the four waves share
+// the loads.  Keys past k_end read clamped rows (K: scores masked later) or
+// are zeroed (V^T).
+template <typename T, int DH>
+__device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, const Coh& ck, const Coh& cv, bool coh,
+                                         int S_max, int kb0, int k_end, uint4* dst) {
+  using MM = Mma<T>;
+  constexpr int E = MM::E, KSTEP = MM::KSTEP;
+  constexpr int NF = DH / KSTEP, ND = DH / 16, NBLK = KSTEP / 16;
+  constexpr int NK = NBLK * NF, FPB = NK + ND;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, grp = lane / 16;
+  uint4 v[FPB / 4];
+#pragma unroll
+  for (int j = 0; j < FPB / 4; ++j) {
+    const int f = 4 * j + wave;
+    if (j < NK / 4) {
+      const int blk = f / NF, kf = f % NF;
+      const int kr = min(kb0 + 16 * blk + lane % 16, k_end - 1);
+      const int col = kf * KSTEP + E * grp;
+      v[j] = coh ? ck.ld16(sizeof(T) * (kr * DH + col))
+                 : *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(kr) * DH + col);
+    } else {
+      const int vr = 16 * (f - NK) + lane % 16;
+      v[j] = vt_frag<T>(Vb + static_cast<size_t>(vr) * S_max, cv, sizeof(T) * vr * S_max, coh, kb0, grp,
+                        k_end);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < FPB / 4; ++j) dst[(4 * j + wave) * kWave + lane] = v[j];
+}
+
 template <typename T, int DH>
 __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void* kc_l, const void* vt_l,
                                                 int it, int gen_wait, char* smem) {
@@ -521,20 +558,39 @@ __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, grp = lane / 16;
   bool waited = false;
 
+  constexpr int FPB = NBLK * NF + ND;  // 1 KiB fragments per key block: K, then V^T
+  static_assert(FPB % 4 == 0 && (NBLK * NF) % 4 == 0, "fragments split evenly over 4 waves");
+  // LDS: Q^T fragments [4 waves][NF][64], then kStageBlk staged key blocks [FPB][64]
+  auto s_q = reinterpret_cast<uint4 (*)[NF][kWave]>(smem);
+  uint4* s_kv = reinterpret_cast<uint4*>(smem + 4 * NF * kWave * sizeof(uint4));
+
   for (int task = blockIdx.x; task < n_tasks; task += p.G) {
     const int item = task / p.nsplit, s = task % p.nsplit;
     const int qg = item % p.n_qg, bg = item / p.n_qg, g = bg % p.Hkv, b = bg / p.Hkv;
-    if (!waited) {
-      bar_wait(p, gen_wait);
-      waited = true;
-    }
-    const int nv = p.n_valid[b];
+    // uniform across the workgroup: keeps the per-block choice between the
+    // cached and the coherent K/V path a scalar branch
+    const int nv = __builtin_amdgcn_readfirstlane(p.n_valid[b]);
     const int len = nv + p.T;
     const int k_begin = s * p.kc_len;
     const int k_end = min(k_begin + p.kc_len, len);
+    const int n_blk = k_end > k_begin ? (k_end - k_begin + KSTEP - 1) / KSTEP : 0;
     const T* Kb = static_cast<const T*>(kc_l) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
     const T* Vb = static_cast<const T*>(vt_l) + static_cast<size_t>(b * p.Hkv + g) * DH * p.S_max;
     const Coh ck(Kb), cv(Vb), cq(p.q), co(p.o);
+
+    // Key blocks made only of prefix rows do not depend on this step's QKV
+    // phase: the first ones are staged before the barrier wait, so their
+    // loads overlap the wait.  Blocks holding action rows follow after it.
+    int staged = 0;
+    if (!waited) {
+      while (staged < n_blk && staged < kStageBlk && k_begin + (staged + 1) * KSTEP <= nv) {
+        stage_kv<T, DH>(Kb, Vb, ck, cv, false, p.S_max, k_begin + staged * KSTEP, k_end,
+                        s_kv + staged * FPB * kWave);
+        ++staged;
+      }
+      bar_wait(p, gen_wait);
+      waited = true;
+    }
 
     const int qr0 = (qg * 4 + wave) * 16;
     const bool active = qr0 < R;
@@ -543,13 +599,12 @@ __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void
     const int hh = qvalid ? myq / p.T : 0;
     const int tt = qvalid ? myq % p.T : 0;
     // Q^T fragments of this wave's 16 query rows, parked in LDS for the key loop
-    auto s_q = reinterpret_cast<uint4 (*)[NF][kWave]>(smem);  // [4 waves][NF][64]
     {
       const uint32_t qoff = sizeof(T) * ((b * p.T + tt) * p.qdim + (g * G + hh) * DH + E * grp);
       uint4 qf[NF];
 #pragma unroll
       for (int kf = 0; kf < NF; ++kf)
-        qf[kf] = qvalid ? cq.ld16(qoff + sizeof(T) * kf * KSTEP) : make_uint4(0, 0, 0, 0);
+        qf[kf] = cq.ld16(qoff + sizeof(T) * kf * KSTEP);  // rows past R: a valid row, unused
 #pragma unroll
       for (int kf = 0; kf < NF; ++kf) s_q[wave][kf][lane] = qf[kf];
     }
@@ -558,70 +613,58 @@ __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void
     for (int d = 0; d < ND; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    if (active) {
-      for (int kb0 = k_begin; kb0 < k_end; kb0 += KSTEP) {
-        const bool coh = kb0 + KSTEP > nv;  // block holds action rows written this launch
-        // K and V^T fragments of the block, all issued before use
-        uint4 kfr[NBLK][NF];
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) {
-          const int key = kb0 + 16 * blk + lane % 16;
-          const bool kv = key < k_end;
-          const int kr = kv ? key : 0;
-#pragma unroll
-          for (int kf = 0; kf < NF; ++kf) {
-            const int col = kf * KSTEP + E * grp;
-            uint4 f = make_uint4(0, 0, 0, 0);
-            if (kv)
-              f = coh ? ck.ld16(sizeof(T) * (kr * DH + col))
-                      : *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(kr) * DH + col);
-            kfr[blk][kf] = f;
-          }
-        }
-        uint4 vfr[ND];
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const int vr = 16 * d + lane % 16;
-          vfr[d] = vt_frag<T>(Vb + static_cast<size_t>(vr) * p.S_max, cv, sizeof(T) * vr * p.S_max, coh,
-                              kb0, grp, k_end);
-        }
-        f32x4 st[NBLK];
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) {
-          st[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(kfr[blk][kf], s_q[wave][kf][lane], st[blk]);
-        }
-        float sv[NBLK * 4];
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kb0 + 16 * blk + 4 * grp + i;
-            const float x = key < k_end ? st[blk][i] * p.scale_log2 : -INFINITY;
-            sv[blk * 4 + i] = x;
-            cmax = fmaxf(cmax, x);
-          }
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
-        const float m_new = fmaxf(m_run, cmax);
-        const float alpha = exp2f(m_run - m_new);
-        float psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NBLK * 4; ++i) {
-          sv[i] = exp2f(sv[i] - m_new);
-          psum += sv[i];
-        }
-        psum += __shfl_xor(psum, 16, kWave);
-        psum += __shfl_xor(psum, 32, kWave);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        const uint4 pf = pack_frag<T>(sv);
-#pragma unroll
-        for (int d = 0; d < ND; ++d) acc[d] = MM::mma(vfr[d], pf, acc[d] * alpha);
-        __builtin_amdgcn_sched_barrier(0);  // one key block's fragments live at a time
+    for (int c0 = 0; c0 < n_blk; c0 += kStageBlk) {
+      // stage the rest of this round's blocks (coherently where they hold
+      // action rows written by this launch)
+      for (int bi = max(staged, c0); bi < min(c0 + kStageBlk, n_blk); ++bi) {
+        const int kb0 = k_begin + bi * KSTEP;
+        stage_kv<T, DH>(Kb, Vb, ck, cv, kb0 + KSTEP > nv, p.S_max, kb0, k_end,
+                        s_kv + (bi - c0) * FPB * kWave);
       }
+      staged = 0;
+      __syncthreads();
+      if (active) {
+        for (int bi = c0; bi < min(c0 + kStageBlk, n_blk); ++bi) {
+          const int kb0 = k_begin + bi * KSTEP;
+          const uint4* fr = s_kv + (bi - c0) * FPB * kWave + lane;
+          f32x4 st[NBLK];
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk) {
+            st[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(fr[(blk * NF + kf) * kWave], s_q[wave][kf][lane], st[blk]);
+          }
+          float sv[NBLK * 4];
+          float cmax = -INFINITY;
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kb0 + 16 * blk + 4 * grp + i;
+              const float x = key < k_end ? st[blk][i] * p.scale_log2 : -INFINITY;
+              sv[blk * 4 + i] = x;
+              cmax = fmaxf(cmax, x);
+            }
+          cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
+          cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
+          const float m_new = fmaxf(m_run, cmax);
+          const float alpha = exp2f(m_run - m_new);
+          float psum = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NBLK * 4; ++i) {
+            sv[i] = exp2f(sv[i] - m_new);
+            psum += sv[i];
+          }
+          psum += __shfl_xor(psum, 16, kWave);
+          psum += __shfl_xor(psum, 32, kWave);
+          l_run = l_run * alpha + psum;
+          m_run = m_new;
+          const uint4 pf = pack_frag<T>(sv);
+#pragma unroll
+          for (int d = 0; d < ND; ++d) acc[d] = MM::mma(fr[(NBLK * NF + d) * kWave], pf, acc[d] * alpha);
+        }
+      }
+      __syncthreads();  // staged blocks are dead before the next round overwrites them
     }
     // acc[d][i] = O^T[dim 16 d + 4 grp + i][query lane % 16] (unnormalised)
 
@@ -661,36 +704,31 @@ __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void
       const int uq0 = (qg * 4 + w) * 16;
       if (uq0 >= R) continue;
       const int q = uq0 + lane % 16;
+      // every split's (m, l, O^T piece) requested at once (clamped split
+      // index, masked at use), then combined in split order
       float mx = -INFINITY;
-      for (int s0 = 0; s0 < p.nsplit; s0 += 8) {
-        float mv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          mv[j] = s0 + j < p.nsplit ? cpart.ldf(4u * (((s0 + j) * 4 + w) * PW + ND * kWave * 4 + lane % 16))
-                                   : -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, mv[j]);
-      }
       f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
       float lsum = 0.0f;
-      for (int s0 = 0; s0 < p.nsplit; s0 += 8) {
-        float mv[8], lv[8];
-        uint4 av[8];
+      for (int s0 = 0; s0 < p.nsplit; s0 += kMergeBatch) {
+        float mv[kMergeBatch], lv[kMergeBatch];
+        uint4 av[kMergeBatch];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bool ok = s0 + j < p.nsplit;
-          const uint32_t wb = 4u * (((s0 + j) * 4 + w) * PW);
-          mv[j] = ok ? cpart.ldf(wb + 4u * (ND * kWave * 4 + lane % 16)) : -INFINITY;
-          lv[j] = ok ? cpart.ldf(wb + 4u * (ND * kWave * 4 + 16 + lane % 16)) : 0.0f;
-          av[j] = ok ? cpart.ld16(wb + 16u * (d * kWave + lane)) : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const uint32_t wb = 4u * ((min(s0 + j, p.nsplit - 1) * 4 + w) * PW);
+          mv[j] = cpart.ldf(wb + 4u * (ND * kWave * 4 + lane % 16));
+          lv[j] = cpart.ldf(wb + 4u * (ND * kWave * 4 + 16 + lane % 16));
+          av[j] = cpart.ld16(wb + 16u * (d * kWave + lane));
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (mv[j] == -INFINITY) continue;  // an empty split
-          const float wgt = exp2f(mv[j] - mx);
-          lsum += wgt * lv[j];
-          o += wgt * f32x4{__uint_as_float(av[j].x), __uint_as_float(av[j].y), __uint_as_float(av[j].z),
-                           __uint_as_float(av[j].w)};
+        for (int j = 0; j < kMergeBatch; ++j) {
+          // an empty split (m = -inf) or a clamped repeat carries no weight
+          if (s0 + j >= p.nsplit || mv[j] == -INFINITY) continue;
+          const float m_new = fmaxf(mx, mv[j]);
+          const float a_old = exp2f(mx - m_new), a_new = exp2f(mv[j] - m_new);
+          lsum = lsum * a_old + lv[j] * a_new;
+          o = o * a_old + a_new * f32x4{__uint_as_float(av[j].x), __uint_as_float(av[j].y),
+                                        __uint_as_float(av[j].z), __uint_as_float(av[j].w)};
+          mx = m_new;
         }
       }
       if (q < R) {
@@ -953,10 +991,21 @@ __device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool
 #undef AE_ISSUE_H
 }
 
+// LDS of the whole-call kernel: the largest phase's need (GEMM: 64 KiB
+// reduction tile + rms / modulation scratch; attention: Q^T fragments and
+// kStageBlk staged key blocks).
+template <typename T, int DH>
+constexpr int smem_bytes() {
+  constexpr int gemm = 4 * (kTileM / 16) * (kTileN / 16) * kWave * 16 + 24 * 1024;
+  constexpr int nf = DH / Mma<T>::KSTEP, fpb = (Mma<T>::KSTEP / 16) * nf + DH / 16;
+  constexpr int attn = (4 * nf + kStageBlk * fpb) * kWave * 16;
+  return gemm > attn ? gemm : attn;
+}
+
 template <typename T, int DH>
 __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs p) {
   // gemm: 64 KiB reduction / tile + rms scratch; out/in: smaller
-  __shared__ __attribute__((aligned(16))) char smem[4 * (kTileM / 16) * (kTileN / 16) * kWave * 16 + 24 * 1024];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<T, DH>()];
   const size_t kv_layer = p.kv_layer;
   int* cq = p.pcnt;
   int* co = cq + p.pq.n_tiles;

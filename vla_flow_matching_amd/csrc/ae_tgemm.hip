@@ -33,6 +33,7 @@ constexpr int kBM = 128;     // tile rows
 constexpr int kBN = 128;     // tile columns
 constexpr int kXcd = 8;
 constexpr int kChunkU4 = 1024;  // uint4 per staged operand chunk (16 KiB)
+constexpr int kMaxSplit = 8;    // K splits of one tile at most
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -227,6 +228,16 @@ __device__ __forceinline__ f32x4 mfma_fp8(uint4 a0, uint4 a1, uint4 b0, uint4 b1
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// Position of A-fragment lane l of slot s inside its 1 KiB LDS block.  The
+// staging threads write 16-byte pieces of two rows x eight k-pieces per 16
+// lanes; XOR-ing the row bits with (k group, slot) spreads those 16 writes
+// over all 64 banks, and a reading wave's 16-lane groups still cover 16
+// distinct bank quads.
+__device__ __forceinline__ int swz(int l, int s) {
+  const int q = l >> 4;
+  return 16 * q + ((l & 15) ^ ((2 * q + 8 * s) & 15));
+}
+
 // One staged chunk times the wave's 64 x 64 block of the tile.
 template <int OP>
 __device__ __forceinline__ void tg_compute(const uint4* A, const uint4* B, int wm, int wn, int lane,
@@ -236,7 +247,7 @@ __device__ __forceinline__ void tg_compute(const uint4* A, const uint4* B, int w
     for (int s = 0; s < 2; ++s) {
       uint4 a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = A[((4 * wm + i) * 2 + s) * kWave + lane];
+      for (int i = 0; i < 4; ++i) a[i] = A[((4 * wm + i) * 2 + s) * kWave + swz(lane, s)];
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = B[((4 * wn + j) * 2 + s) * kWave + lane];
 #pragma unroll
@@ -249,7 +260,7 @@ __device__ __forceinline__ void tg_compute(const uint4* A, const uint4* B, int w
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) a[i][s] = A[((4 * wm + i) * 2 + s) * kWave + lane];
+      for (int s = 0; s < 2; ++s) a[i][s] = A[((4 * wm + i) * 2 + s) * kWave + swz(lane, s)];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(kTT) void tgemm_kernel(TGemmArgs p) {
     a_off[j] = static_cast<uint32_t>(grow) * static_cast<uint32_t>(p.lda_bytes) + 16u * kc;
     int ln;
     const int slot = O::slot_lane(kc, row & 15, ln);
-    a_lds[j] = ((row >> 4) * 2 + slot) * kWave + ln;
+    a_lds[j] = ((row >> 4) * 2 + slot) * kWave + swz(ln, slot);
     b_off[j] = static_cast<uint32_t>(i >> 7) * n_chunks * 128u + (i & 127);
   }
   const uint4* Wt = p.W + static_cast<size_t>(nt) * 8 * n_chunks * 128;
@@ -401,22 +412,31 @@ __global__ __launch_bounds__(kTT) void tgemm_kernel(TGemmArgs p) {
                          __float_as_uint(s_y[r][c4 + 2]), __float_as_uint(s_y[r][c4 + 3])));
     }
     if (!arrive_last(p.counters + tile, p.ksplit, &s_flag)) return;
-    for (int i = tid; i < n4; i += kTT) {
-      const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
-      const uint32_t off = 4u * (r * kBN + c4);
-      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int q0 = 0; q0 < p.ksplit; q0 += 8) {
-        uint4 buf[8];
+    // four 16-byte pieces per thread per round, all splits' loads in
+    // flight together (ksplit <= kMaxSplit)
+    for (int i0 = tid; i0 < n4; i0 += 4 * kTT) {
+      uint4 buf[4][kMaxSplit];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          buf[j] = cp.ld16(off + 4u * static_cast<uint32_t>(min(q0 + j, p.ksplit - 1)) * (kBM * kBN));
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(i0 + u * kTT, n4 - 1);
+        const uint32_t off = 4u * ((i / (kBN / 4)) * kBN + 4 * (i % (kBN / 4)));
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (q0 + j < p.ksplit)
-            t += f32x4{__uint_as_float(buf[j].x), __uint_as_float(buf[j].y), __uint_as_float(buf[j].z),
-                       __uint_as_float(buf[j].w)};
+        for (int q = 0; q < kMaxSplit; ++q)
+          buf[u][q] = cp.ld16(off + 4u * static_cast<uint32_t>(min(q, p.ksplit - 1)) * (kBM * kBN));
       }
-      s_y[r][c4] = t[0]; s_y[r][c4 + 1] = t[1]; s_y[r][c4 + 2] = t[2]; s_y[r][c4 + 3] = t[3];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kTT;
+        if (i >= n4) break;
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < kMaxSplit; ++q)
+          if (q < p.ksplit)
+            t += f32x4{__uint_as_float(buf[u][q].x), __uint_as_float(buf[u][q].y),
+                       __uint_as_float(buf[u][q].z), __uint_as_float(buf[u][q].w)};
+        const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
+        s_y[r][c4] = t[0]; s_y[r][c4 + 1] = t[1]; s_y[r][c4 + 2] = t[2]; s_y[r][c4 + 3] = t[3];
+      }
     }
     __syncthreads();
   }
@@ -611,7 +631,8 @@ TGemmPlan plan_tgemm(int M, int N, int K, int kc, int target_blocks) {
   const int chunks = K / kc;
   const int tiles = g.m_tiles * g.n_tiles;
   int s = (target_blocks + tiles - 1) / tiles;
-  const int max_s = chunks / 2 > 0 ? chunks / 2 : 1;  // at least two chunks per split
+  int max_s = chunks / 2 > 0 ? chunks / 2 : 1;  // at least two chunks per split
+  if (max_s > kMaxSplit) max_s = kMaxSplit;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   g.ksplit = s;
