@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
+constexpr int kQB = 2;  // 16-row query blocks per wave
 
 template <typename T>
 __device__ __forceinline__ uint4 load_vt_frag(const T* vrow, int kb0, int grp, int k_end);
@@ -72,15 +73,54 @@ __device__ __forceinline__ void store4<float>(float* dst, const float* v) {
   *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Stage one key block (KSTEP keys) into LDS in fragment order: NBLK * NF K
+// fragments (S^T = K Q^T operands), then ND V^T fragments (O^T = V^T P^T
+// operands), 1 KiB each; the four waves load a quarter each.  Keys past
+// k_end read a clamped row (K: their scores are masked) or are zeroed (V^T).
+template <typename T, int DH>
+struct KvBlock {
+  using MM = Mma<T>;
+  static constexpr int E = MM::E, KSTEP = MM::KSTEP;
+  static constexpr int NF = DH / KSTEP, ND = DH / 16, NBLK = KSTEP / 16;
+  static constexpr int NK = NBLK * NF, FPB = NK + ND, PER_WAVE = FPB / 4;
+  static_assert(FPB % 4 == 0 && NK % 4 == 0, "fragments split evenly over 4 waves");
+
+  static __device__ __forceinline__ void load(const T* Kb, const T* Vb, int S_max, int kb0, int k_end,
+                                              uint4 (&v)[PER_WAVE]) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, grp = lane / 16;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int f = 4 * j + wave;
+      if (j < NK / 4) {
+        const int blk = f / NF, kf = f % NF;
+        const int kr = min(kb0 + 16 * blk + lane % 16, k_end - 1);
+        v[j] = *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(kr) * DH + kf * KSTEP + E * grp);
+      } else {
+        const int vr = 16 * (f - NK) + lane % 16;
+        v[j] = load_vt_frag<T>(Vb + static_cast<size_t>(vr) * S_max, kb0, grp, k_end);
+      }
+    }
+  }
+  static __device__ __forceinline__ void store(uint4* dst, const uint4 (&v)[PER_WAVE]) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) dst[(4 * j + wave) * kWave + lane] = v[j];
+  }
+};
+
+// One workgroup = 4 waves x kQB query blocks of 16 rows of one (request, KV
+// group), over one split of the keys.  Key blocks are staged through two LDS
+// buffers shared by the waves (the next block's loads are in flight while
+// the current one is multiplied), so every K/V byte crosses from L2 once per
+// workgroup.
 template <typename T, int DH>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
+  using KV = KvBlock<T, DH>;
   using MM = Mma<T>;
-  constexpr int E = MM::E;
-  constexpr int KSTEP = MM::KSTEP;
-  constexpr int NF = DH / KSTEP;    // Q^T fragments along head_dim
-  constexpr int ND = DH / 16;       // O^T row blocks
-  constexpr int NBLK = KSTEP / 16;  // 16-key S^T blocks per P^T fragment
-  constexpr int PW = ND * kWave * 4 + 32;  // floats of one wave's partial
+  constexpr int E = KV::E, KSTEP = KV::KSTEP, NF = KV::NF, ND = KV::ND, NBLK = KV::NBLK;
+  constexpr int NK = KV::NK, FPB = KV::FPB;
+  constexpr int PW = ND * kWave * 4 + 32;  // floats of one query block's partial
+  __shared__ uint4 s_kv[2][FPB * kWave];
   __shared__ int s_flag;
 
   const int G = p.Hq / p.Hkv;
@@ -99,48 +139,63 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int grp = lane / 16;
-  const int qr0 = (qg * 4 + wave) * 16;
-  const bool active = qr0 < R;
   const int len = p.n_valid[b] + p.T;
   const int k_begin = s * p.kc_len;
   const int k_end = min(k_begin + p.kc_len, len);
+  const int n_blk = k_end > k_begin ? (k_end - k_begin + KSTEP - 1) / KSTEP : 0;
 
   const T* Kb = static_cast<const T*>(p.kcache) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
   const T* Vb = static_cast<const T*>(p.vtcache) + static_cast<size_t>(b * p.Hkv + g) * DH * p.S_max;
 
-  const int myq = qr0 + lane % 16;
-  const bool qvalid = myq < R;
-  const int hh = qvalid ? myq / p.T : 0;
-  const int tt = qvalid ? myq % p.T : 0;
-
-  uint4 qf[NF];
-  {
-    const T* qrow = static_cast<const T*>(p.q) + static_cast<size_t>(b * p.T + tt) * p.ldq +
-                    (g * G + hh) * DH + E * grp;
+  // query rows of this wave: blocks (qg * 4 + wave) * kQB + c, 16 rows each
+  uint4 qf[kQB][NF];
+  int hh[kQB], tt[kQB];
+  bool qvalid[kQB];
 #pragma unroll
-    for (int kf = 0; kf < NF; ++kf)
-      qf[kf] = *reinterpret_cast<const uint4*>(qrow + kf * KSTEP);  // rows past R: a valid row, unused
+  for (int c = 0; c < kQB; ++c) {
+    const int myq = ((qg * 4 + wave) * kQB + c) * 16 + lane % 16;
+    qvalid[c] = myq < R;
+    const int q = min(myq, R - 1);  // rows past R read a valid row, never stored
+    hh[c] = q / p.T;
+    tt[c] = q % p.T;
+    const T* qrow = static_cast<const T*>(p.q) + static_cast<size_t>(b * p.T + tt[c]) * p.ldq +
+                    (g * G + hh[c]) * DH + E * grp;
+#pragma unroll
+    for (int kf = 0; kf < NF; ++kf) qf[c][kf] = *reinterpret_cast<const uint4*>(qrow + kf * KSTEP);
   }
 
-  f32x4 acc[ND];
+  f32x4 acc[kQB][ND];
+  float m_run[kQB], l_run[kQB];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int c = 0; c < kQB; ++c) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) acc[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.0f;
+  }
 
-  if (active) {
-    for (int kb0 = k_begin; kb0 < k_end; kb0 += KSTEP) {
+  uint4 stage[KV::PER_WAVE];
+  if (n_blk > 0) {
+    KV::load(Kb, Vb, p.S_max, k_begin, k_end, stage);
+    KV::store(s_kv[0], stage);
+  }
+  __syncthreads();
+  for (int bi = 0; bi < n_blk; ++bi) {
+    const int kb0 = k_begin + bi * KSTEP;
+    // next block in flight (the last iteration re-reads its own block)
+    KV::load(Kb, Vb, p.S_max, k_begin + min(bi + 1, n_blk - 1) * KSTEP, k_end, stage);
+    const uint4* fr = s_kv[bi & 1] + lane;
+    uint4 kfr[NK];
+#pragma unroll
+    for (int f = 0; f < NK; ++f) kfr[f] = fr[f * kWave];
+#pragma unroll
+    for (int c = 0; c < kQB; ++c) {
       f32x4 st[NBLK];
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk) {
         st[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // keys past the split read its last key; their scores are masked below
-        const int key = min(kb0 + 16 * blk + lane % 16, k_end - 1);
-        const T* krow = Kb + static_cast<size_t>(key) * DH + E * grp;
 #pragma unroll
-        for (int kf = 0; kf < NF; ++kf) {
-          const uint4 kfr = *reinterpret_cast<const uint4*>(krow + kf * KSTEP);
-          st[blk] = MM::mma(kfr, qf[kf], st[blk]);
-        }
+        for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(kfr[blk * NF + kf], qf[c][kf], st[blk]);
       }
       // st[blk][i] = S^T[key kb0 + 16 blk + 4 grp + i][query lane % 16]
       float sv[NBLK * 4];
@@ -156,8 +211,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
         }
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = exp2f(m_run - m_new);
+      const float m_new = fmaxf(m_run[c], cmax);
+      const float alpha = exp2f(m_run[c] - m_new);
       float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < NBLK * 4; ++i) {
@@ -166,61 +221,74 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
       }
       psum += __shfl_xor(psum, 16, kWave);
       psum += __shfl_xor(psum, 32, kWave);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run[c] = l_run[c] * alpha + psum;
+      m_run[c] = m_new;
       const uint4 pf = pack_frag<T>(sv);
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        acc[d] *= alpha;
-        const T* vrow = Vb + static_cast<size_t>(16 * d + lane % 16) * p.S_max;
-        const uint4 vf = load_vt_frag<T>(vrow, kb0, grp, k_end);
-        acc[d] = MM::mma(vf, pf, acc[d]);
-      }
+      for (int d = 0; d < ND; ++d) acc[c][d] = MM::mma(fr[(NK + d) * kWave], pf, acc[c][d] * alpha);
     }
+    KV::store(s_kv[(bi + 1) & 1], stage);
+    __syncthreads();
   }
-  // acc[d][i] = O^T[dim 16 d + 4 grp + i][query lane % 16] (unnormalised)
+  // acc[c][d][i] = O^T[dim 16 d + 4 grp + i][query lane % 16 of block c] (unnormalised)
 
   if (p.nsplit > 1) {
-    float* part = p.partial + (static_cast<size_t>(item) * p.nsplit + s) * 4 * PW;
-    float* mine = part + wave * PW;
-    if (active) {
+    // publish every query block's (O^T, m, l), then the last split of the
+    // item merges them in split order
+    const size_t per_split = static_cast<size_t>(4 * kQB) * PW;
+    float* part = p.partial + static_cast<size_t>(item) * p.nsplit * per_split;
+    const Coh cp(part);
+#pragma unroll
+    for (int c = 0; c < kQB; ++c) {
+      const uint32_t wb = 4u * static_cast<uint32_t>(s * per_split + (wave * kQB + c) * PW);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
-        st_dev4(reinterpret_cast<f32x4*>(mine + (d * kWave + lane) * 4), acc[d]);
+        cp.st16(wb + 16u * (d * kWave + lane),
+                make_uint4(__float_as_uint(acc[c][d][0]), __float_as_uint(acc[c][d][1]),
+                           __float_as_uint(acc[c][d][2]), __float_as_uint(acc[c][d][3])));
       if (grp == 0) {
-        st_dev(mine + ND * kWave * 4 + lane, m_run);
-        st_dev(mine + ND * kWave * 4 + 16 + lane, l_run);
+        cp.stf(wb + 4u * (ND * kWave * 4 + lane), m_run[c]);
+        cp.stf(wb + 4u * (ND * kWave * 4 + 16 + lane), l_run[c]);
       }
     }
     if (!arrive_last(p.counters + item, p.nsplit, &s_flag)) return;
-    if (active) {
-      float mx = -INFINITY;
-      for (int s2 = 0; s2 < p.nsplit; ++s2) {
-        const float* ps = p.partial + (static_cast<size_t>(item) * p.nsplit + s2) * 4 * PW + wave * PW;
-        mx = fmaxf(mx, ld_dev(ps + ND * kWave * 4 + lane % 16));
-      }
 #pragma unroll
-      for (int d = 0; d < ND; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-      l_run = 0.0f;
+    for (int c = 0; c < kQB; ++c) {
+      float mx = -INFINITY, lsum = 0.0f;
+      f32x4 o[ND];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int s2 = 0; s2 < p.nsplit; ++s2) {
-        const float* ps = p.partial + (static_cast<size_t>(item) * p.nsplit + s2) * 4 * PW + wave * PW;
-        const float ms = ld_dev(ps + ND * kWave * 4 + lane % 16);
-        if (ms == -INFINITY) continue;
-        const float w = exp2f(ms - mx);
-        l_run += w * ld_dev(ps + ND * kWave * 4 + 16 + lane % 16);
+        const uint32_t wb = 4u * static_cast<uint32_t>(s2 * per_split + (wave * kQB + c) * PW);
+        const float ms = cp.ldf(wb + 4u * (ND * kWave * 4 + lane % 16));
+        const float ls = cp.ldf(wb + 4u * (ND * kWave * 4 + 16 + lane % 16));
+        uint4 av[ND];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) av[d] = cp.ld16(wb + 16u * (d * kWave + lane));
+        if (ms == -INFINITY) continue;  // an empty split
+        const float m_new = fmaxf(mx, ms);
+        const float a_old = exp2f(mx - m_new), a_new = exp2f(ms - m_new);
+        lsum = lsum * a_old + ls * a_new;
 #pragma unroll
         for (int d = 0; d < ND; ++d)
-          acc[d] += w * ld_dev4(reinterpret_cast<const f32x4*>(ps + (d * kWave + lane) * 4));
+          o[d] = o[d] * a_old + a_new * f32x4{__uint_as_float(av[d].x), __uint_as_float(av[d].y),
+                                              __uint_as_float(av[d].z), __uint_as_float(av[d].w)};
+        mx = m_new;
       }
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[c][d] = o[d];
+      l_run[c] = lsum;
     }
   }
 
-  if (active && qvalid) {
-    const float inv = 1.0f / l_run;
-    T* orow = static_cast<T*>(p.o) + static_cast<size_t>(b * p.T + tt) * p.ldo + (g * G + hh) * DH;
+#pragma unroll
+  for (int c = 0; c < kQB; ++c) {
+    if (!qvalid[c]) continue;
+    const float inv = 1.0f / l_run[c];
+    T* orow = static_cast<T*>(p.o) + static_cast<size_t>(b * p.T + tt[c]) * p.ldo + (g * G + hh[c]) * DH;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-      float v[4] = {acc[d][0] * inv, acc[d][1] * inv, acc[d][2] * inv, acc[d][3] * inv};
+      float v[4] = {acc[c][d][0] * inv, acc[c][d][1] * inv, acc[c][d][2] * inv, acc[c][d][3] * inv};
       store4<T>(orow + 16 * d + 4 * grp, v);
     }
   }
@@ -240,10 +308,12 @@ hipError_t launch_dh(const AttnArgs& a, int blocks, hipStream_t s) {
 
 }  // namespace
 
-size_t attention_partial_floats(int dh, int items, int nsplit) {
+size_t attention_partial_floats(int dh, int items, int nsplit, int rows_per_item) {
   const size_t pw = static_cast<size_t>(dh / 16) * kWave * 4 + 32;
-  return static_cast<size_t>(items) * nsplit * 4 * pw;
+  return static_cast<size_t>(items) * nsplit * (rows_per_item / 16) * pw;
 }
+
+int attention_rows_per_item() { return 4 * kQB * 16; }
 
 hipError_t launch_attention(Dt dt, const AttnArgs& a, hipStream_t s) {
   const int items = a.batch * a.Hkv * a.n_qg;

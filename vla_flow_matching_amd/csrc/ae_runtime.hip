@@ -166,10 +166,12 @@ struct AttnPlan {
   int n_qg, nsplit, kc_len, items;
 };
 
-AttnPlan plan_attention(const ae_handle* h, int batch) {
+// rows: query rows one item covers (64 in the whole-call kernel, the batched
+// kernel's attention_rows_per_item() otherwise)
+AttnPlan plan_attention(const ae_handle* h, int batch, int rows) {
   AttnPlan a;
   const int R = h->T * (h->Hq / h->Hkv);
-  a.n_qg = (R + 63) / 64;
+  a.n_qg = (R + rows - 1) / rows;
   a.items = batch * h->Hkv * a.n_qg;
   const int kstep = kstep_of(h->dt);
   const int max_keys = h->Pmax + h->T;
@@ -320,7 +322,7 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
   const int D = h->D, L = h->L, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const LayerPlans lp = plan_layer(h, M);
-  const AttnPlan ap = plan_attention(h, batch);
+  const AttnPlan ap = plan_attention(h, batch, attention_rows_per_item());
   const float dt = -1.0f / static_cast<float>(steps);
   for (int k = 0; k < steps; ++k) {
     AE_LAUNCH(launch_action_in(h->x, M, h->A, h->w_in, h->b_in, h->h, D, h->ssq, h->Mmax, s));
@@ -378,7 +380,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
   const int D = h->D, L = h->L, F = h->F, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const TPlans tp = plan_tlayer(h, M);
-  const AttnPlan ap = plan_attention(h, batch);
+  const AttnPlan ap = plan_attention(h, batch, attention_rows_per_item());
   const float dt = -1.0f / static_cast<float>(steps);
   const float eps = h->cfg.rms_eps;
   const bool f8 = h->fp8;
@@ -471,7 +473,7 @@ PersistArgs persist_args(const ae_handle* h, int batch, int steps) {
   a.pcnt = h->pcnt;
   const PersistPlans pp = plan_persist(h);
   a.pq = pp.q; a.po = pp.o; a.pg = pp.g; a.pd = pp.d;
-  const AttnPlan ap = plan_attention(h, batch);
+  const AttnPlan ap = plan_attention(h, batch, kTileM);
   a.n_qg = ap.n_qg; a.nsplit = ap.nsplit; a.kc_len = ap.kc_len;
   a.n_acnt = ap.items;
   a.acnt = h->pcnt + pp.q.n_tiles + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
@@ -685,9 +687,14 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
         gcn = std::max(gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
       }
     }
-    const AttnPlan ap = plan_attention(h, b);
-    if (ap.nsplit > 1) afl = std::max(afl, attention_partial_floats(h->dh, ap.items, ap.nsplit));
+    const int rows = attention_rows_per_item();
+    const AttnPlan ap = plan_attention(h, b, rows);
+    if (ap.nsplit > 1) afl = std::max(afl, attention_partial_floats(h->dh, ap.items, ap.nsplit, rows));
     acn = std::max(acn, static_cast<size_t>(ap.items));
+    if (h->G > 0 && b * h->T <= kTileM) {  // the whole-call kernel's attention scratch
+      const AttnPlan pa = plan_attention(h, b, kTileM);
+      if (pa.nsplit > 1) afl = std::max(afl, attention_partial_floats(h->dh, pa.items, pa.nsplit, kTileM));
+    }
   }
   if (h->G > 0) {
     const PersistPlans pp = plan_persist(h);
@@ -706,7 +713,7 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
       const PersistPlans pp = plan_persist(h);
       n = static_cast<size_t>(pp.q.n_tiles) + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
       int items = 0;
-      for (int b = 1; b <= h->Bmax && b * h->T <= kTileM; ++b) items = std::max(items, plan_attention(h, b).items);
+      for (int b = 1; b <= h->Bmax && b * h->T <= kTileM; ++b) items = std::max(items, plan_attention(h, b, kTileM).items);
       n += items;
     }
     AE_ALLOC(h->pcnt, n * 4);
