@@ -205,13 +205,14 @@ struct PersistArgs {
   const float *rope_cos, *rope_sin;
   float *x, *h, *ssq;
   void *q, *o, *act;
-  float* gpart;
+  float* gpart;  // split-K partials as (value, generation) packets
   int* gcnt;
   float* apart;
   int* acnt;   // attention split counters (= pcnt + GEMM tile counters)
   int* pcnt;   // monotonic split counters: q, o, gate/up, down tiles, then attention items
   int n_acnt;  // attention items
   int* flags;  // [G] barrier generations
+  uint32_t* genp;  // generation base of the split-K packets (one word)
   int* err;    // device error flag (a barrier timed out)
   PGemm pq, po, pg, pd;
   int n_qg, nsplit, kc_len;

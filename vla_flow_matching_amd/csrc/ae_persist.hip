@@ -181,7 +181,7 @@ __device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, fl
 
 template <typename T, int PRO, int EPI>
 __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g, const GemmLayer& ly,
-                                           int* counters, int it, int gen_wait, char* smem) {
+                                           uint32_t llgen, int gen_wait, char* smem) {
   using MM = Mma<T>;
   constexpr int E = MM::E;
   constexpr int KSTEP = MM::KSTEP;
@@ -354,35 +354,47 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
     const float gn = EPI == EPI_RESID ? ly.gate[nt * kTileN + lane] : 0.0f;
 
     if (g.ksplit > 1) {
-      // publish the partial (row-major, 16-byte stores), join the group,
-      // then reduce this member's row slice over all members in order
-      const Coh cp(p.gpart + static_cast<size_t>(nt) * g.ksplit * kTileF);
-      for (int i = tid; i < rows * (kTileN / 4); i += kThreads) {
-        const int r = i / (kTileN / 4), c4 = 4 * (i % (kTileN / 4));
-        cp.st16(4u * (s * kTileF + r * kTileN + c4),
-                make_uint4(__float_as_uint(s_y[r][c4]), __float_as_uint(s_y[r][c4 + 1]),
-                           __float_as_uint(s_y[r][c4 + 2]), __float_as_uint(s_y[r][c4 + 3])));
+      // Publish the partial as (value, llgen) 8-byte packets, then reduce
+      // this member's row slice over all members in order.  Each packet
+      // carries its own generation, so the reducer polls the data itself:
+      // no store drain, counter or group wait sits between the members'
+      // stores and the reduction.
+      const Coh cp(reinterpret_cast<uint2*>(p.gpart) + static_cast<size_t>(nt) * g.ksplit * kTileF);
+      for (int i = tid; i < rows * (kTileN / 2); i += kThreads) {
+        const int r = i / (kTileN / 2), c2 = 2 * (i % (kTileN / 2));
+        cp.st16(8u * (s * kTileF + r * kTileN + c2),
+                make_uint4(__float_as_uint(s_y[r][c2]), llgen, __float_as_uint(s_y[r][c2 + 1]), llgen));
       }
-      group_join(p, counters + nt, g.ksplit * (it + 1));
-      const int n4 = (r1 - r0) * (kTileN / 4);  // 16-byte chunks of the slice
-      for (int i = tid; i < n4; i += kThreads) {
-        const int r = r0 + i / (kTileN / 4), c4 = 4 * (i % (kTileN / 4));
-        const uint32_t off = 4u * (r * kTileN + c4);
-        f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
-        uint4 buf[8];
+      const int n2 = (r1 - r0) * (kTileN / 2);  // packet pairs of the slice
+      for (int i = tid; i < n2; i += kThreads) {
+        const int r = r0 + i / (kTileN / 2), c2 = 2 * (i % (kTileN / 2));
+        const uint32_t off = 8u * (r * kTileN + c2);
+        float t0 = 0.0f, t1 = 0.0f;
         for (int s0 = 0; s0 < g.ksplit; s0 += 8) {
+          uint4 buf[8];
+          long spins = 0;
+          for (;;) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) buf[j] = cp.ld16(off + 4u * min(s0 + j, g.ksplit - 1) * kTileF);
+            for (int j = 0; j < 8; ++j) buf[j] = cp.ld16(off + 8u * min(s0 + j, g.ksplit - 1) * kTileF);
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ok = ok && buf[j].y == llgen && buf[j].w == llgen;
+            if (ok) break;
+            if (++spins > kSpinLimit || ((spins & 255) == 0 && dev_error(p))) {
+              raise_error(p);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if (s0 + j < g.ksplit)
-              tot += f32x4{__uint_as_float(buf[j].x), __uint_as_float(buf[j].y), __uint_as_float(buf[j].z),
-                           __uint_as_float(buf[j].w)};
+            if (s0 + j < g.ksplit) {
+              t0 += __uint_as_float(buf[j].x);
+              t1 += __uint_as_float(buf[j].z);
+            }
         }
-        s_y[r][c4] = tot[0];
-        s_y[r][c4 + 1] = tot[1];
-        s_y[r][c4 + 2] = tot[2];
-        s_y[r][c4 + 3] = tot[3];
+        s_y[r][c2] = t0;
+        s_y[r][c2 + 1] = t1;
       }
       __syncthreads();
     }
@@ -1007,10 +1019,9 @@ __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs p) {
   // gemm: 64 KiB reduction / tile + rms scratch; out/in: smaller
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<T, DH>()];
   const size_t kv_layer = p.kv_layer;
-  int* cq = p.pcnt;
-  int* co = cq + p.pq.n_tiles;
-  int* cg = co + p.po.n_tiles;
-  int* cd = cg + p.pg.n_tiles;
+  // generation base of this launch's split-K packets (advanced by the
+  // counter fill that precedes every launch)
+  const uint32_t gbase = __builtin_amdgcn_readfirstlane(*p.genp);
   int gen = 0;
   outin_phase<T>(p, 0, false, true, 0, smem);  // h from x_0
   bar_arrive(p, ++gen);
@@ -1026,22 +1037,22 @@ __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs p) {
       ly.gate = nullptr;
 
       ly.W = p.wqkv + l * p.sqkv; ly.A = p.h; ly.lda = p.D; ly.scale = md; ly.shift = md + p.D;
-      gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, p.pq, ly, cq, it, gen, smem);
+      gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, p.pq, ly, gbase + 8 * it + 1, gen, smem);
       bar_arrive(p, ++gen);
 
       attention_phase<T, DH>(p, kc, vt, it, gen, smem);
       bar_arrive(p, ++gen);
 
       ly.W = p.wo + l * p.so; ly.A = p.o; ly.lda = p.qdim; ly.gate = md + 2 * p.D;
-      gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.po, ly, co, it, gen, smem);
+      gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.po, ly, gbase + 8 * it + 2, gen, smem);
       bar_arrive(p, ++gen);
 
       ly.W = p.wgu + l * p.sgu; ly.A = p.h; ly.lda = p.D; ly.scale = md + 3 * p.D; ly.shift = md + 4 * p.D;
-      gemm_phase<T, PRO_ADARMS, EPI_GELU>(p, p.pg, ly, cg, it, gen, smem);
+      gemm_phase<T, PRO_ADARMS, EPI_GELU>(p, p.pg, ly, gbase + 8 * it + 3, gen, smem);
       bar_arrive(p, ++gen);
 
       ly.W = p.wd + l * p.sd; ly.A = p.act; ly.lda = p.F; ly.gate = md + 5 * p.D;
-      gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.pd, ly, cd, it, gen, smem);
+      gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.pd, ly, gbase + 8 * it + 4, gen, smem);
       bar_arrive(p, ++gen);
     }
     outin_phase<T>(p, k, true, k + 1 < p.n_steps, gen, smem);
@@ -1064,10 +1075,17 @@ int occupancy_p() {
   return n;
 }
 
-__global__ void fill_int_kernel(int* a, int na, int* b, int nb) {
+// Zero the barrier flags and split counters, and advance the packet
+// generation base past every generation the previous launch used.
+__global__ void fill_int_kernel(PersistArgs args, uint32_t stride) {
+  const int na = args.G;
+  const int nb = args.pq.n_tiles + args.po.n_tiles + args.pg.n_tiles + args.pd.n_tiles + args.n_acnt;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < na + nb; i += gridDim.x * blockDim.x) {
-    if (i < na) a[i] = 0;
-    else b[i - na] = 0;
+    if (i < na) args.flags[i] = 0;
+    else args.pcnt[i - na] = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    args.genp[0] += stride;
   }
 }
 
@@ -1092,7 +1110,9 @@ int persist_blocks_per_cu(Dt dt, int dh) {
 hipError_t launch_persist(Dt dt, const PersistArgs& a, hipStream_t s) {
   if (a.G < 1 || a.G > kMaxG) return hipErrorInvalidValue;
   const int n_cnt = a.pq.n_tiles + a.po.n_tiles + a.pg.n_tiles + a.pd.n_tiles;
-  hipLaunchKernelGGL(fill_int_kernel, dim3(4), dim3(256), 0, s, a.flags, a.G, a.pcnt, n_cnt + a.n_acnt);
+  const uint32_t stride = 8u * static_cast<uint32_t>(a.n_steps * a.L) + 8u;
+  (void)n_cnt;
+  hipLaunchKernelGGL(fill_int_kernel, dim3(4), dim3(256), 0, s, a, stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dt == DT_BF16) {

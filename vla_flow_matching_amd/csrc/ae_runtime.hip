@@ -78,6 +78,7 @@ struct ae_handle {
   int a_frags = 0, a_blocks = 0;
   int *flags = nullptr, *derr = nullptr;
   int* pcnt = nullptr;  // the persistent kernel's monotonic split counters
+  uint32_t* genp = nullptr;  // its split-K packet generation base
   int G = 0;              // resident workgroups of the persistent kernel (0: unavailable)
   bool persist_graph = true;  // cooperative launch can be captured
 
@@ -469,7 +470,7 @@ PersistArgs persist_args(const ae_handle* h, int batch, int steps) {
   a.n_valid = h->n_valid; a.rope_cos = h->rope_cos; a.rope_sin = h->rope_sin;
   a.x = h->x; a.h = h->h; a.ssq = h->ssq; a.q = h->q; a.o = h->o; a.act = h->act;
   a.gpart = h->gpart; a.gcnt = h->gcnt; a.apart = h->apart; a.acnt = h->acnt;
-  a.flags = h->flags; a.err = h->derr;
+  a.flags = h->flags; a.err = h->derr; a.genp = h->genp;
   a.pcnt = h->pcnt;
   const PersistPlans pp = plan_persist(h);
   a.pq = pp.q; a.po = pp.o; a.pg = pp.g; a.pd = pp.d;
@@ -699,8 +700,8 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   if (h->G > 0) {
     const PersistPlans pp = plan_persist(h);
     for (const PGemm* g : {&pp.q, &pp.o, &pp.g, &pp.d}) {
-      if (g->ksplit > 1)
-        gfl = std::max(gfl, static_cast<size_t>(g->n_tiles) * g->ksplit * kTileM * kTileN);
+      if (g->ksplit > 1)  // (value, generation) packets: two words per value
+        gfl = std::max(gfl, 2 * static_cast<size_t>(g->n_tiles) * g->ksplit * kTileM * kTileN);
       gcn = std::max(gcn, static_cast<size_t>(g->n_tiles));
     }
   }
@@ -719,6 +720,7 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
     AE_ALLOC(h->pcnt, n * 4);
   }
   AE_ALLOC(h->derr, 4);
+  AE_ALLOC(h->genp, 4);
   AE_ALLOC(h->gpart, gfl * 4);
   AE_ALLOC(h->gcnt, gcn * 4);
   AE_ALLOC(h->apart, afl * 4);
