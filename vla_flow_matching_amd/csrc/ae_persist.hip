@@ -137,12 +137,29 @@ struct GemmLayer {
   void* vt;  // layer's V^T cache
 };
 
-// adaRMS prologue data in one round of loads: per-row reciprocal RMS of h
-// (from the per-64-column partial sums of squares) and the modulation
-// scale / shift of the task's k range [k_lo, k_lo + k_len) (k_len <= 512).
-__device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, float* s_r,
-                                         const float* scale, const float* shift, int k_lo, int k_len,
+// Modulation scale / shift of a task's k range [k_lo, k_lo + k_len)
+// (k_len <= 512) into LDS.  They depend only on the step, so this runs
+// before the barrier wait and its loads overlap it.
+__device__ __forceinline__ void load_mod(const float* scale, const float* shift, int k_lo, int k_len,
                                          float* s_sc, float* s_sh) {
+  float sc[2], sh[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = min(static_cast<int>(threadIdx.x) + j * kThreads, k_len - 1);
+    sc[j] = scale[k_lo + i];
+    sh[j] = shift[k_lo + i];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = threadIdx.x + j * kThreads;
+    s_sc[i] = 1.0f + sc[j];
+    s_sh[i] = sh[j];
+  }
+}
+
+// Per-row reciprocal RMS of h from the per-64-column partial sums of
+// squares, in one round of loads.
+__device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, float* s_r) {
   const Coh cs(p.ssq);
   const int n = p.M * p.ssq_tiles;  // <= 64 rows x 64 tiles
   // loads at clamped indices, all in flight together; masked at use
@@ -152,23 +169,10 @@ __device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, fl
     const int i = min(static_cast<int>(threadIdx.x) + j * kThreads, n - 1);
     v[j] = cs.ldf(4u * ((i / p.M) * p.ldssq + i % p.M));
   }
-  float sc[2], sh[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = min(static_cast<int>(threadIdx.x) + j * kThreads, k_len - 1);
-    sc[j] = scale[k_lo + i];
-    sh[j] = shift[k_lo + i];
-  }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int i = threadIdx.x + j * kThreads;
     if (i < n) s_part[i] = v[j];
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = threadIdx.x + j * kThreads;
-    s_sc[i] = 1.0f + sc[j];
-    s_sh[i] = sh[j];
   }
   __syncthreads();
   if (threadIdx.x < p.M) {
@@ -223,6 +227,10 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
       for (int j = 0; j < NB; ++j) wb[c][j] = Wt[(static_cast<size_t>(j) * g.k_frags + kf) * kWave];
     }
 
+    const int k_lo = kf0 * KSTEP;
+    if (PRO == PRO_ADARMS) load_mod(ly.scale, ly.shift, k_lo, (kf1 - kf0) * KSTEP, s_sc, s_sh);
+    const float gn = EPI == EPI_RESID ? ly.gate[nt * kTileN + lane] : 0.0f;
+
     if (!waited) {
       bar_wait(p, gen_wait);
       waited = true;
@@ -243,10 +251,9 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
           araw[c][i][q] = coh_a.ld16((PRO == PRO_ADARMS ? 4u : static_cast<uint32_t>(sizeof(T))) *
                                      (row * ly.lda + k + 4 * q));
       }
-    const int k_lo = kf0 * KSTEP;
     float rr[MT];
     if (PRO == PRO_ADARMS) {
-      load_rms(p, s_part, s_r, ly.scale, ly.shift, k_lo, (kf1 - kf0) * KSTEP, s_sc, s_sh);
+      load_rms(p, s_part, s_r);
 #pragma unroll
       for (int i = 0; i < MT; ++i) rr[i] = s_r[min(16 * i + arow, rows - 1)];
     }
@@ -351,8 +358,6 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
         }
       }
     }
-    const float gn = EPI == EPI_RESID ? ly.gate[nt * kTileN + lane] : 0.0f;
-
     if (g.ksplit > 1) {
       // Publish the partial as (value, llgen) 8-byte packets, then reduce
       // this member's row slice over all members in order.  Each packet

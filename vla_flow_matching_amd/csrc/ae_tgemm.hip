@@ -287,7 +287,7 @@ __device__ __forceinline__ bool tile_of(int bid, int n_tiles, int m_tiles, int k
 }
 
 template <int OP, int EPI>
-__global__ __launch_bounds__(kTT) void tgemm_kernel(TGemmArgs p) {
+__global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   using O = TOp<OP>;
   constexpr int KC = O::KC;
   // two stages of A and B chunks; the finished tile reuses the space
@@ -370,12 +370,16 @@ __global__ __launch_bounds__(kTT) void tgemm_kernel(TGemmArgs p) {
   TG_LOAD(r0, min(c0 + 1, c1 - 1));
   __syncthreads();
   int c = c0;
+  // (the scheduling barriers keep each chunk's global loads ahead of the
+  // multiply instead of letting them sink to their LDS stores)
   for (; c + 1 < c1; c += 2) {
     TG_LOAD(r1, min(c + 2, c1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
     TG_COMPUTE(0);
     TG_STORE(r0, 1);
     __syncthreads();
     TG_LOAD(r0, min(c + 3, c1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
     TG_COMPUTE(1);
     TG_STORE(r1, 0);
     __syncthreads();
