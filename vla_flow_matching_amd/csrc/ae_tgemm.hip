@@ -238,37 +238,34 @@ __device__ __forceinline__ int swz(int l, int s) {
   return 16 * q + ((l & 15) ^ ((2 * q + 8 * s) & 15));
 }
 
-// One staged chunk times the wave's 64 x 64 block of the tile.
+// One chunk times the wave's 64 x 64 block of the tile: A fragments from the
+// LDS stage, B fragments (four 16-column groups x two slots) from registers.
 template <int OP>
-__device__ __forceinline__ void tg_compute(const uint4* A, const uint4* B, int wm, int wn, int lane,
+__device__ __forceinline__ void tg_compute(const uint4* A, const u32x4 (&B)[4][2], int wm, int lane,
                                            f32x4 (&acc)[4][4]) {
   if (OP == OP_BF16) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      uint4 a[4], b[4];
+      uint4 a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = A[((4 * wm + i) * 2 + s) * kWave + swz(lane, s)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = B[((4 * wn + j) * 2 + s) * kWave + lane];
-#pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(a[i], __builtin_bit_cast(uint4, B[j][s]), acc[i][j]);
     }
   } else {
-    uint4 a[4][2], b[4][2];
+    uint4 a[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int s = 0; s < 2; ++s) a[i][s] = A[((4 * wm + i) * 2 + s) * kWave + swz(lane, s)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) b[j][s] = B[((4 * wn + j) * 2 + s) * kWave + lane];
-#pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp8(a[i][0], a[i][1], b[j][0], b[j][1], acc[i][j]);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = mfma_fp8(a[i][0], a[i][1], __builtin_bit_cast(uint4, B[j][0]),
+                             __builtin_bit_cast(uint4, B[j][1]), acc[i][j]);
   }
 }
 
@@ -290,10 +287,9 @@ template <int OP, int EPI>
 __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   using O = TOp<OP>;
   constexpr int KC = O::KC;
-  // two stages of A and B chunks; the finished tile reuses the space
+  // two stages of A chunks; the finished tile reuses the space
   __shared__ __attribute__((aligned(16))) uint4 s_buf[kBM * (kBN + 1) / 4 + 4];
-  static_assert(sizeof(s_buf) >= 4 * kChunkU4 * sizeof(uint4), "stages fit");
-  // stage st: A chunk at s_buf + st * kChunkU4, B chunk at s_buf + (2 + st) * kChunkU4
+  static_assert(sizeof(s_buf) >= 2 * kChunkU4 * sizeof(uint4), "stages fit");
   auto s_y = reinterpret_cast<float (*)[kBN + 1]>(s_buf);
   __shared__ int s_flag;
 
@@ -307,10 +303,9 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   const int c0 = static_cast<int>((static_cast<long long>(ks) * n_chunks) / p.ksplit);
   const int c1 = static_cast<int>((static_cast<long long>(ks + 1) * n_chunks) / p.ksplit);
 
-  // staging map: item i = tid + 256 j; A: row i/8, 16-byte column i%8;
-  // B: column group i/128, uint4 i%128 of that group's 2 KiB.
+  // A staging map: item i = tid + 256 j: row i/8, 16-byte column i%8.
   const uint8_t* Ab = static_cast<const uint8_t*>(p.A);
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[4];
   int a_lds[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -321,37 +316,40 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
     int ln;
     const int slot = O::slot_lane(kc, row & 15, ln);
     a_lds[j] = ((row >> 4) * 2 + slot) * kWave + swz(ln, slot);
-    b_off[j] = static_cast<uint32_t>(i >> 7) * n_chunks * 128u + (i & 127);
   }
-  const uint4* Wt = p.W + static_cast<size_t>(nt) * 8 * n_chunks * 128;
-
-  // one chunk's staging registers: four A and four B 16-byte values per
-  // thread (native vectors, so they stay in registers across iterations)
-  struct Stage {
-    u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
-  };
-  const u32x4* Wv = reinterpret_cast<const u32x4*>(Wt);
+  // B fragments go straight to registers: wave (wm, wn) reads the 2 KiB
+  // chunk of each of its four 16-column groups (slot s, lane) itself, so
+  // only A passes through LDS.
+  const u32x4* Wv = reinterpret_cast<const u32x4*>(p.W) +
+                    (static_cast<size_t>(nt) * 8 + 4 * wn) * n_chunks * 128 + lane;
   u32x4* sv = reinterpret_cast<u32x4*>(s_buf);
-#define TG_LOAD(R, c)                                                              \
+
+  struct AStage {
+    u32x4 a0, a1, a2, a3;
+  };
+  struct BStage {
+    u32x4 b[4][2];
+  };
+#define TG_LOAD_A(R, c)                                                            \
   do {                                                                             \
     const uint32_t co_ = static_cast<uint32_t>(c) * 128u;                          \
     R.a0 = *reinterpret_cast<const u32x4*>(Ab + a_off[0] + co_);                   \
     R.a1 = *reinterpret_cast<const u32x4*>(Ab + a_off[1] + co_);                   \
     R.a2 = *reinterpret_cast<const u32x4*>(Ab + a_off[2] + co_);                   \
     R.a3 = *reinterpret_cast<const u32x4*>(Ab + a_off[3] + co_);                   \
-    R.b0 = Wv[b_off[0] + co_];                                                     \
-    R.b1 = Wv[b_off[1] + co_];                                                     \
-    R.b2 = Wv[b_off[2] + co_];                                                     \
-    R.b3 = Wv[b_off[3] + co_];                                                     \
   } while (0)
-#define TG_STORE(R, st)                                                            \
+#define TG_LOAD_B(R, c)                                                            \
+  do {                                                                             \
+    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                               \
+      _Pragma("unroll") for (int s_ = 0; s_ < 2; ++s_)                             \
+        R.b[j_][s_] = Wv[(static_cast<size_t>(j_) * n_chunks + (c)) * 128 + s_ * 64]; \
+  } while (0)
+#define TG_STORE_A(R, st)                                                          \
   do {                                                                             \
     u32x4* sa_ = sv + (st) * kChunkU4;                                             \
-    u32x4* sb_ = sv + (2 + (st)) * kChunkU4 + tid;                                 \
     sa_[a_lds[0]] = R.a0; sa_[a_lds[1]] = R.a1; sa_[a_lds[2]] = R.a2; sa_[a_lds[3]] = R.a3; \
-    sb_[0] = R.b0; sb_[kTT] = R.b1; sb_[2 * kTT] = R.b2; sb_[3 * kTT] = R.b3;      \
   } while (0)
-#define TG_COMPUTE(st) tg_compute<OP>(s_buf + (st) * kChunkU4, s_buf + (2 + (st)) * kChunkU4, wm, wn, lane, acc)
+#define TG_COMPUTE(st, RB) tg_compute<OP>(s_buf + (st) * kChunkU4, RB, wm, lane, acc)
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -359,37 +357,41 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Two LDS stages and two register sets: while chunk c is multiplied from
-  // LDS, chunk c+1 waits in registers for its stage and chunk c+2 is in
-  // flight.  Every split holds at least one chunk (plan_tgemm); chunk
-  // indices past the split are clamped, so the tail re-loads its last chunk
-  // into a stage nobody reads.
-  Stage r0, r1;
-  TG_LOAD(r0, c0);
-  TG_STORE(r0, 0);
-  TG_LOAD(r0, min(c0 + 1, c1 - 1));
+  // Iteration c: LDS stage c%2 holds A(c), registers hold B(c); A(c+1) and
+  // B(c+1) are in flight and A(c+2) is issued.  Every split holds at least
+  // one chunk (plan_tgemm); chunk indices past the split are clamped (the
+  // tail re-loads its last chunk into a stage nobody reads).
+  AStage a0, a1;
+  BStage b0, b1;
+  TG_LOAD_A(a0, c0);
+  TG_LOAD_B(b0, c0);
+  TG_STORE_A(a0, 0);
+  TG_LOAD_A(a1, min(c0 + 1, c1 - 1));
   __syncthreads();
   int c = c0;
   // (the scheduling barriers keep each chunk's global loads ahead of the
-  // multiply instead of letting them sink to their LDS stores)
+  // multiply instead of letting them sink to their uses)
   for (; c + 1 < c1; c += 2) {
-    TG_LOAD(r1, min(c + 2, c1 - 1));
+    TG_LOAD_B(b1, c + 1);
+    TG_LOAD_A(a0, min(c + 2, c1 - 1));
     __builtin_amdgcn_sched_barrier(0);
-    TG_COMPUTE(0);
-    TG_STORE(r0, 1);
+    TG_COMPUTE(0, b0.b);
+    TG_STORE_A(a1, 1);
     __syncthreads();
-    TG_LOAD(r0, min(c + 3, c1 - 1));
+    TG_LOAD_B(b0, min(c + 2, c1 - 1));
+    TG_LOAD_A(a1, min(c + 3, c1 - 1));
     __builtin_amdgcn_sched_barrier(0);
-    TG_COMPUTE(1);
-    TG_STORE(r1, 0);
+    TG_COMPUTE(1, b1.b);
+    TG_STORE_A(a0, 0);
     __syncthreads();
   }
   if (c < c1) {
-    TG_COMPUTE(0);  // odd chunk count: the last chunk sits in stage 0
-    __syncthreads();  // every wave is done with the stages before s_y reuses them
+    TG_COMPUTE(0, b0.b);  // odd chunk count: the last chunk sits in stage 0
+    __syncthreads();      // every wave is done with the stages before s_y reuses them
   }
-#undef TG_LOAD
-#undef TG_STORE
+#undef TG_LOAD_A
+#undef TG_LOAD_B
+#undef TG_STORE_A
 #undef TG_COMPUTE
 
   // accumulators -> LDS tile (row-major)
