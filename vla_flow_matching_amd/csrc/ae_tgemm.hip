@@ -19,8 +19,9 @@
 // A is row-major [M][lda] in the operand type; W is pre-packed in fragment
 // order so that one 128-byte k-chunk of a 16-column group is 2 KiB
 // contiguous.  Rows beyond M read a clamped (valid) row and are never
-// stored.  Split-K partials are reduced in a fixed order by the last
-// workgroup of a tile, so results do not depend on scheduling.
+// stored.  Split-K partials are summed in split order by a second kernel
+// (one workgroup per 16 rows of a tile), so results do not depend on
+// scheduling.
 #include "ae_device.h"
 #include "ae_kernels.h"
 
@@ -283,6 +284,102 @@ __device__ __forceinline__ bool tile_of(int bid, int n_tiles, int m_tiles, int k
   return nt < n_tiles;
 }
 
+// The GEMM epilogues on rows [m0, m0 + rows) of n-tile nt, the finished
+// values in s_y (row-major, relative to m0); wave w takes rows w, w + 4, ...
+template <int OP, int EPI>
+__device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, int rows,
+                                            float (*s_y)[kBN + 1]) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  // column pair structure of the packed layout: packed column pc of this
+  // tile is pair P = 4 nt + pc / 32, half pc / 16 % 2, index pc % 16
+  if (EPI == EPI_RESID) {
+    // h += gate * y (fp8: y = acc * s_x * s_w); two columns per lane
+    for (int row = wave; row < rows; row += 4) {
+      const int m = m0 + row;
+      const float sx = OP == OP_FP8 ? p.sx_row[m] * p.sw[0] : 1.0f;
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        const int n = nt * kBN + 64 * hc + lane;
+        float* hp = p.h + static_cast<size_t>(m) * p.ldh + n;
+        *hp = *hp + p.gate[n] * (s_y[row][64 * hc + lane] * sx);
+      }
+    }
+  } else if (EPI == EPI_GELU) {
+    // lanes: 64 = 4 pairs x 16; gate half at 32 pr + jj, up half at +16
+    const int pr = lane / 16, jj = lane % 16;
+    const int f = (4 * nt + pr) * 16 + jj;
+    for (int row = wave; row < rows; row += 4) {
+      const int m = m0 + row;
+      float g = s_y[row][32 * pr + jj], u = s_y[row][32 * pr + 16 + jj];
+      if (OP == OP_FP8) {
+        const float sx = p.sx_row[m];
+        g = g * (sx * p.sw[0]);
+        u = u * (sx * p.sw[1]);
+      }
+      const float a = gelu_tanh(g) * u;
+      if (OP == OP_FP8) {
+        static_cast<float*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = a;
+        float mx = fabsf(a);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        if (lane == 0) p.rowmax[static_cast<size_t>(nt) * p.ldp + m] = mx;
+      } else {
+        static_cast<bf16_t*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = f2bf(a);
+      }
+    }
+  } else {  // EPI_QKV
+    const int pph = p.dh / 32;
+    const int pq = p.Hq * pph, pk = p.Hkv * pph;
+    const int half = p.dh / 2;
+    const int pr = lane / 16, jj = lane % 16;
+    const int P = 4 * nt + pr;
+    int seg, head, pi;
+    if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
+    else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
+    else { seg = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
+    const int j = 16 * pi + jj;
+    const float sw = OP == OP_FP8 ? p.sw[seg] : 1.0f;
+    bf16_t* qo = static_cast<bf16_t*>(p.q);
+    bf16_t* kc = static_cast<bf16_t*>(p.kcache);
+    bf16_t* vt = static_cast<bf16_t*>(p.vtcache);
+    for (int row = wave; row < rows; row += 4) {
+      const int m = m0 + row;
+      const int req = m / p.T, t = m % p.T;
+      float a = s_y[row][32 * pr + jj], b = s_y[row][32 * pr + 16 + jj];
+      if (OP == OP_FP8) {
+        const float sc = p.sx_row[m] * sw;
+        a *= sc;
+        b *= sc;
+      }
+      if (seg < 2) {
+        const size_t ti2 = (static_cast<size_t>(req) * p.T + t) * half + j;
+        const float cs = p.rope_cos[ti2], sn = p.rope_sin[ti2];
+        const float ra = a * cs - b * sn;
+        const float rb = b * cs + a * sn;
+        a = ra;
+        b = rb;
+      }
+      if (seg == 0) {
+        bf16_t* dst = qo + static_cast<size_t>(m) * p.ldq + head * p.dh;
+        dst[j] = f2bf(a);
+        dst[half + j] = f2bf(b);
+      } else {
+        const int key = p.n_valid[req] + t;
+        const size_t base = static_cast<size_t>(req) * p.Hkv + head;
+        if (seg == 1) {
+          bf16_t* dst = kc + (base * p.S_max + key) * p.dh;
+          dst[j] = f2bf(a);
+          dst[half + j] = f2bf(b);
+        } else {
+          bf16_t* dst = vt + base * p.dh * p.S_max;
+          dst[static_cast<size_t>(j) * p.S_max + key] = f2bf(a);
+          dst[static_cast<size_t>(half + j) * p.S_max + key] = f2bf(b);
+        }
+      }
+    }
+  }
+}
+
 template <int OP, int EPI>
 __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   using O = TOp<OP>;
@@ -291,7 +388,6 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint4 s_buf[kBM * (kBN + 1) / 4 + 4];
   static_assert(sizeof(s_buf) >= 2 * kChunkU4 * sizeof(uint4), "stages fit");
   auto s_y = reinterpret_cast<float (*)[kBN + 1]>(s_buf);
-  __shared__ int s_flag;
 
   int nt, mt, ks;
   if (!tile_of(blockIdx.x, p.n_tiles, p.m_tiles, p.ksplit, nt, mt, ks)) return;
@@ -405,136 +501,60 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   __syncthreads();
 
   if (p.ksplit > 1) {
-    // publish this split's rows of the tile (16-byte device-coherent
-    // stores), then the last of the tile's splits sums all of them in split
-    // order
-    const int tile = nt * p.m_tiles + mt;
-    const Coh cp(p.partial + static_cast<size_t>(tile) * p.ksplit * (kBM * kBN));
+    // this split's rows of the tile -> partial scratch; the reduce kernel
+    // that follows sums the splits in order and applies the epilogue
+    float* part = p.partial + (static_cast<size_t>(nt * p.m_tiles + mt) * p.ksplit + ks) * (kBM * kBN);
     const int n4 = rows * (kBN / 4);
     for (int i = tid; i < n4; i += kTT) {
       const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
-      cp.st16(4u * (static_cast<uint32_t>(ks) * (kBM * kBN) + r * kBN + c4),
-              make_uint4(__float_as_uint(s_y[r][c4]), __float_as_uint(s_y[r][c4 + 1]),
-                         __float_as_uint(s_y[r][c4 + 2]), __float_as_uint(s_y[r][c4 + 3])));
+      *reinterpret_cast<float4*>(part + r * kBN + c4) =
+          make_float4(s_y[r][c4], s_y[r][c4 + 1], s_y[r][c4 + 2], s_y[r][c4 + 3]);
     }
-    if (!arrive_last(p.counters + tile, p.ksplit, &s_flag)) return;
-    // four 16-byte pieces per thread per round, all splits' loads in
-    // flight together (ksplit <= kMaxSplit)
-    for (int i0 = tid; i0 < n4; i0 += 4 * kTT) {
-      uint4 buf[4][kMaxSplit];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = min(i0 + u * kTT, n4 - 1);
-        const uint32_t off = 4u * ((i / (kBN / 4)) * kBN + 4 * (i % (kBN / 4)));
-#pragma unroll
-        for (int q = 0; q < kMaxSplit; ++q)
-          buf[u][q] = cp.ld16(off + 4u * static_cast<uint32_t>(min(q, p.ksplit - 1)) * (kBM * kBN));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kTT;
-        if (i >= n4) break;
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < kMaxSplit; ++q)
-          if (q < p.ksplit)
-            t += f32x4{__uint_as_float(buf[u][q].x), __uint_as_float(buf[u][q].y),
-                       __uint_as_float(buf[u][q].z), __uint_as_float(buf[u][q].w)};
-        const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
-        s_y[r][c4] = t[0]; s_y[r][c4 + 1] = t[1]; s_y[r][c4 + 2] = t[2]; s_y[r][c4 + 3] = t[3];
-      }
-    }
-    __syncthreads();
+    return;
   }
+  tg_epilogue<OP, EPI>(p, nt, m0, rows, s_y);
+}
 
-  // column pair structure of the packed layout: packed column pc of this
-  // tile is pair P = 4 nt + pc / 32, half pc / 16 % 2, index pc % 16
-  if (EPI == EPI_RESID) {
-    // h += gate * y (fp8: y = acc * s_x * s_w); two columns per lane
-    for (int row = wave; row < rows; row += 4) {
-      const int m = m0 + row;
-      const float sx = OP == OP_FP8 ? p.sx_row[m] * p.sw[0] : 1.0f;
+// Sum of a tile's K-split partials for kRedRows rows (in split order), then
+// the epilogue of those rows.  One workgroup per (tile, row slice).
+constexpr int kRedRows = 16;
+
+template <int OP, int EPI>
+__global__ __launch_bounds__(kTT) void tgemm_reduce_kernel(TGemmArgs p) {
+  __shared__ float s_y[kRedRows][kBN + 1];
+  const int slices = kBM / kRedRows;
+  const int tile = blockIdx.x / slices, sl = blockIdx.x % slices;
+  const int nt = tile / p.m_tiles, mt = tile % p.m_tiles;
+  const int m0 = mt * kBM + sl * kRedRows;
+  const int rows = min(kRedRows, p.M - m0);
+  if (rows <= 0) return;
+  const int tid = threadIdx.x;
+  const float* part = p.partial + static_cast<size_t>(tile) * p.ksplit * (kBM * kBN) + sl * kRedRows * kBN;
+  // kRedRows x kBN floats = 512 float4, two per thread, every split in flight
+  float4 v[2][kMaxSplit];
 #pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
-        const int n = nt * kBN + 64 * hc + lane;
-        float* hp = p.h + static_cast<size_t>(m) * p.ldh + n;
-        *hp = *hp + p.gate[n] * (s_y[row][64 * hc + lane] * sx);
-      }
-    }
-  } else if (EPI == EPI_GELU) {
-    // lanes: 64 = 4 pairs x 16; gate half at 32 pr + jj, up half at +16
-    const int pr = lane / 16, jj = lane % 16;
-    const int f = (4 * nt + pr) * 16 + jj;
-    for (int row = wave; row < rows; row += 4) {
-      const int m = m0 + row;
-      float g = s_y[row][32 * pr + jj], u = s_y[row][32 * pr + 16 + jj];
-      if (OP == OP_FP8) {
-        const float sx = p.sx_row[m];
-        g = g * (sx * p.sw[0]);
-        u = u * (sx * p.sw[1]);
-      }
-      const float a = gelu_tanh(g) * u;
-      if (OP == OP_FP8) {
-        static_cast<float*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = a;
-        float mx = fabsf(a);
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + u * kTT;
+    const int r = min(i / (kBN / 4), rows - 1), c4 = 4 * (i % (kBN / 4));
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-        if (lane == 0) p.rowmax[static_cast<size_t>(nt) * p.ldp + m] = mx;
-      } else {
-        static_cast<bf16_t*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = f2bf(a);
-      }
-    }
-  } else {  // EPI_QKV
-    const int pph = p.dh / 32;
-    const int pq = p.Hq * pph, pk = p.Hkv * pph;
-    const int half = p.dh / 2;
-    const int pr = lane / 16, jj = lane % 16;
-    const int P = 4 * nt + pr;
-    int seg, head, pi;
-    if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
-    else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
-    else { seg = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
-    const int j = 16 * pi + jj;
-    const float sw = OP == OP_FP8 ? p.sw[seg] : 1.0f;
-    bf16_t* qo = static_cast<bf16_t*>(p.q);
-    bf16_t* kc = static_cast<bf16_t*>(p.kcache);
-    bf16_t* vt = static_cast<bf16_t*>(p.vtcache);
-    for (int row = wave; row < rows; row += 4) {
-      const int m = m0 + row;
-      const int req = m / p.T, t = m % p.T;
-      float a = s_y[row][32 * pr + jj], b = s_y[row][32 * pr + 16 + jj];
-      if (OP == OP_FP8) {
-        const float sc = p.sx_row[m] * sw;
-        a *= sc;
-        b *= sc;
-      }
-      if (seg < 2) {
-        const size_t ti2 = (static_cast<size_t>(req) * p.T + t) * half + j;
-        const float cs = p.rope_cos[ti2], sn = p.rope_sin[ti2];
-        const float ra = a * cs - b * sn;
-        const float rb = b * cs + a * sn;
-        a = ra;
-        b = rb;
-      }
-      if (seg == 0) {
-        bf16_t* dst = qo + static_cast<size_t>(m) * p.ldq + head * p.dh;
-        dst[j] = f2bf(a);
-        dst[half + j] = f2bf(b);
-      } else {
-        const int key = p.n_valid[req] + t;
-        const size_t base = static_cast<size_t>(req) * p.Hkv + head;
-        if (seg == 1) {
-          bf16_t* dst = kc + (base * p.S_max + key) * p.dh;
-          dst[j] = f2bf(a);
-          dst[half + j] = f2bf(b);
-        } else {
-          bf16_t* dst = vt + base * p.dh * p.S_max;
-          dst[static_cast<size_t>(j) * p.S_max + key] = f2bf(a);
-          dst[static_cast<size_t>(half + j) * p.S_max + key] = f2bf(b);
-        }
-      }
-    }
+    for (int q = 0; q < kMaxSplit; ++q)
+      v[u][q] = *reinterpret_cast<const float4*>(part + static_cast<size_t>(min(q, p.ksplit - 1)) * (kBM * kBN) +
+                                                 r * kBN + c4);
   }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + u * kTT;
+    const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q)
+      if (q < p.ksplit) {
+        t.x += v[u][q].x; t.y += v[u][q].y; t.z += v[u][q].z; t.w += v[u][q].w;
+      }
+    s_y[r][c4] = t.x; s_y[r][c4 + 1] = t.y; s_y[r][c4 + 2] = t.z; s_y[r][c4 + 3] = t.w;
+  }
+  __syncthreads();
+  tg_epilogue<OP, EPI>(p, nt, m0, rows, s_y);
 }
 
 // ---------------------------------------------------------------------------
@@ -656,10 +676,13 @@ size_t tgemm_partial_floats(const TGemmPlan& g) {
 hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a, int blocks, hipStream_t s) {
   if (a.K % tgemm_kc(op) || a.N % kBN) return hipErrorInvalidValue;
   dim3 grid(blocks), block(kTT);
-#define AE_TG(OPV, EPV)                                                  \
-  if (op == OPV && epi == EPV) {                                         \
-    hipLaunchKernelGGL((tgemm_kernel<OPV, EPV>), grid, block, 0, s, a);  \
-    return hipGetLastError();                                            \
+#define AE_TG(OPV, EPV)                                                                     \
+  if (op == OPV && epi == EPV) {                                                            \
+    hipLaunchKernelGGL((tgemm_kernel<OPV, EPV>), grid, block, 0, s, a);                     \
+    if (a.ksplit > 1)                                                                       \
+      hipLaunchKernelGGL((tgemm_reduce_kernel<OPV, EPV>),                                   \
+                         dim3(a.n_tiles * a.m_tiles * (kBM / kRedRows)), block, 0, s, a);   \
+    return hipGetLastError();                                                               \
   }
   AE_TG(OP_BF16, EPI_QKV)
   AE_TG(OP_BF16, EPI_GELU)
