@@ -18,6 +18,7 @@ enum Epilogue { EPI_QKV = 0, EPI_GELU = 1, EPI_RESID = 2 };
 // Column order of a packed weight.
 enum PackMode { PACK_PLAIN = 0, PACK_QKV = 1, PACK_GU = 2 };
 
+constexpr int kMaxSteps = 64;  // Euler steps of one call at most
 constexpr int kTileM = 64;  // rows per GEMM tile
 constexpr int kTileN = 64;  // packed columns per GEMM tile (two 32-column pairs)
 

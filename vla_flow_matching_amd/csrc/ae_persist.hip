@@ -1115,7 +1115,10 @@ int persist_blocks_per_cu(Dt dt, int dh) {
 hipError_t launch_persist(Dt dt, const PersistArgs& a, hipStream_t s) {
   if (a.G < 1 || a.G > kMaxG) return hipErrorInvalidValue;
   const int n_cnt = a.pq.n_tiles + a.po.n_tiles + a.pg.n_tiles + a.pd.n_tiles;
-  const uint32_t stride = 8u * static_cast<uint32_t>(a.n_steps * a.L) + 8u;
+  // every launch of a handle advances by the range the longest launch can
+  // use (8 generations per layer step, at most kMaxSteps steps), so no two
+  // launches ever share a generation
+  const uint32_t stride = 8u * static_cast<uint32_t>(kMaxSteps * a.L) + 8u;
   (void)n_cnt;
   hipLaunchKernelGGL(fill_int_kernel, dim3(4), dim3(256), 0, s, a, stride);
   hipError_t e = hipGetLastError();

@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kTargetBlocks = 256;  // one workgroup per CU at least
 constexpr int kMaxGraphs = 16;
-constexpr int kMaxSteps = 64;
+
 
 struct Buf {
   void* p = nullptr;
