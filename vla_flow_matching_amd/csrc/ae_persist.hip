@@ -158,28 +158,27 @@ __device__ __forceinline__ void load_mod(const float* scale, const float* shift,
 }
 
 // Per-row reciprocal RMS of h from the per-64-column partial sums of
-// squares, in one round of loads.
+// squares: four threads per row each add every fourth partial (all loads in
+// flight at once), two shuffles finish the row sum.  Rows <= 64, partials
+// <= 64.
 __device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, float* s_r) {
+  (void)s_part;
   const Coh cs(p.ssq);
-  const int n = p.M * p.ssq_tiles;  // <= 64 rows x 64 tiles
-  // loads at clamped indices, all in flight together; masked at use
+  const int row = threadIdx.x / 4, part = threadIdx.x % 4;
+  const int rc = min(row, p.M - 1);
   float v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int i = min(static_cast<int>(threadIdx.x) + j * kThreads, n - 1);
-    v[j] = cs.ldf(4u * ((i / p.M) * p.ldssq + i % p.M));
+    const int q = min(part + 4 * j, p.ssq_tiles - 1);
+    v[j] = cs.ldf(4u * (q * p.ldssq + rc));
   }
+  float acc = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int i = threadIdx.x + j * kThreads;
-    if (i < n) s_part[i] = v[j];
-  }
-  __syncthreads();
-  if (threadIdx.x < p.M) {
-    float acc = 0.0f;
-    for (int q = 0; q < p.ssq_tiles; ++q) acc += s_part[q * p.M + threadIdx.x];
-    s_r[threadIdx.x] = 1.0f / sqrtf(acc / static_cast<float>(p.D) + p.eps);
-  }
+  for (int j = 0; j < 16; ++j)
+    if (part + 4 * j < p.ssq_tiles) acc += v[j];
+  acc += __shfl_xor(acc, 1, kWave);
+  acc += __shfl_xor(acc, 2, kWave);
+  if (part == 0 && row < p.M) s_r[row] = 1.0f / sqrtf(acc / static_cast<float>(p.D) + p.eps);
   __syncthreads();
 }
 
