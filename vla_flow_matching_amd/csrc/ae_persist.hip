@@ -820,20 +820,16 @@ __device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool
   _Pragma("unroll") for (int c = 0; c < KPW_OUT; ++c) {                                      \
     const int kf = wave + 4 * ((c0) + c);                                                   \
     _Pragma("unroll") for (int j = 0; j < kAB; ++j) wo[c][j] =                               \
-        (do_out && kf < kfr && j < p.a_blocks)                                              \
-            ? p.wout_p[(static_cast<size_t>(j) * kfr + kf) * kWave + lane]                  \
-            : make_uint4(0, 0, 0, 0);                                                       \
+        p.wout_p[(static_cast<size_t>(min(j, p.a_blocks - 1)) * kfr + min(kf, kfr - 1)) * kWave + lane]; \
   }
     uint4 wi[CPW_IN][kAF];
     float bi[CPW_IN];
 #define AE_ISSUE_WIN(q0)                                                                    \
   _Pragma("unroll") for (int q = 0; q < CPW_IN; ++q) {                                       \
     const int cb = wave + 4 * ((q0) + q);                                                   \
-    bi[q] = (do_in && cb < nb) ? p.b_in[16 * cb + lane % 16] : 0.0f;                        \
+    bi[q] = p.b_in[16 * min(cb, nb - 1) + lane % 16];                                       \
     _Pragma("unroll") for (int f = 0; f < kAF; ++f) wi[q][f] =                               \
-        (do_in && cb < nb && f < p.a_frags)                                                 \
-            ? p.win_p[(static_cast<size_t>(cb) * p.a_frags + f) * kWave + lane]             \
-            : make_uint4(0, 0, 0, 0);                                                       \
+        p.win_p[(static_cast<size_t>(min(cb, nb - 1)) * p.a_frags + min(f, p.a_frags - 1)) * kWave + lane]; \
   }
     AE_ISSUE_WOUT(0)
 
@@ -847,9 +843,12 @@ __device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = tid + j * kThreads, r = i / 64, a = i % 64;
-      xv[j] = (r < rows && a < p.A) ? cx.ldf(4u * ((m0 + r) * p.A + a)) : 0.0f;
+      // loads at clamped (valid) indices, masked at use
+      xv[j] = cx.ldf(4u * ((m0 + min(r, rows - 1)) * p.A + min(a, p.A - 1)));
       const int q = i / 16, r2 = i % 16;
-      pv[j] = (do_out && q < p.ssq_tiles && r2 < rows) ? cs.ldf(4u * (q * p.ldssq + m0 + r2)) : 0.0f;
+      pv[j] = cs.ldf(4u * (min(q, p.ssq_tiles - 1) * p.ldssq + m0 + min(r2, rows - 1)));
+      if (!(r < rows && a < p.A)) xv[j] = 0.0f;
+      if (!(do_out && q < p.ssq_tiles && r2 < rows)) pv[j] = 0.0f;
     }
     uint4 hraw[KPW_OUT][E / 4];
 #define AE_ISSUE_H(c0)                                                                      \
@@ -857,8 +856,7 @@ __device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool
     const int kf = wave + 4 * ((c0) + c);                                                   \
     const int k = kf * KSTEP + E * (lane / 16);                                             \
     _Pragma("unroll") for (int q = 0; q < E / 4; ++q) hraw[c][q] =                           \
-        (do_out && kf < kfr && row < rows) ? ch.ld16(4u * ((m0 + row) * p.D + k + 4 * q))   \
-                                           : make_uint4(0, 0, 0, 0);                        \
+        ch.ld16(4u * ((m0 + min(row, rows - 1)) * p.D + min(k, p.D - E) + 4 * q));          \
   }
     AE_ISSUE_H(0)
     if (do_out) {
