@@ -27,6 +27,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kQB = 2;  // 16-row query blocks per wave
+constexpr int kMergeBatch = 2;  // key splits merged per round of loads
 
 template <typename T>
 __device__ __forceinline__ uint4 load_vt_frag(const T* vrow, int kb0, int grp, int k_end);
@@ -258,22 +259,31 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
       f32x4 o[ND];
 #pragma unroll
       for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < p.nsplit; ++s2) {
-        const uint32_t wb = 4u * static_cast<uint32_t>(s2 * per_split + (wave * kQB + c) * PW);
-        const float ms = cp.ldf(wb + 4u * (ND * kWave * 4 + lane % 16));
-        const float ls = cp.ldf(wb + 4u * (ND * kWave * 4 + 16 + lane % 16));
-        uint4 av[ND];
+      for (int s0 = 0; s0 < p.nsplit; s0 += kMergeBatch) {
+        // every split of the batch requested at once (clamped index)
+        float ms[kMergeBatch], ls[kMergeBatch];
+        uint4 av[kMergeBatch][ND];
 #pragma unroll
-        for (int d = 0; d < ND; ++d) av[d] = cp.ld16(wb + 16u * (d * kWave + lane));
-        if (ms == -INFINITY) continue;  // an empty split
-        const float m_new = fmaxf(mx, ms);
-        const float a_old = exp2f(mx - m_new), a_new = exp2f(ms - m_new);
-        lsum = lsum * a_old + ls * a_new;
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const int s2 = min(s0 + j, p.nsplit - 1);
+          const uint32_t wb = 4u * static_cast<uint32_t>(s2 * per_split + (wave * kQB + c) * PW);
+          ms[j] = cp.ldf(wb + 4u * (ND * kWave * 4 + lane % 16));
+          ls[j] = cp.ldf(wb + 4u * (ND * kWave * 4 + 16 + lane % 16));
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
-          o[d] = o[d] * a_old + a_new * f32x4{__uint_as_float(av[d].x), __uint_as_float(av[d].y),
-                                              __uint_as_float(av[d].z), __uint_as_float(av[d].w)};
-        mx = m_new;
+          for (int d = 0; d < ND; ++d) av[j][d] = cp.ld16(wb + 16u * (d * kWave + lane));
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          if (s0 + j >= p.nsplit || ms[j] == -INFINITY) continue;  // repeat or empty split
+          const float m_new = fmaxf(mx, ms[j]);
+          const float a_old = exp2f(mx - m_new), a_new = exp2f(ms[j] - m_new);
+          lsum = lsum * a_old + ls[j] * a_new;
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+            o[d] = o[d] * a_old + a_new * f32x4{__uint_as_float(av[j][d].x), __uint_as_float(av[j][d].y),
+                                                __uint_as_float(av[j][d].z), __uint_as_float(av[j][d].w)};
+          mx = m_new;
+        }
       }
 #pragma unroll
       for (int d = 0; d < ND; ++d) acc[c][d] = o[d];
@@ -314,6 +324,13 @@ size_t attention_partial_floats(int dh, int items, int nsplit, int rows_per_item
 }
 
 int attention_rows_per_item() { return 4 * kQB * 16; }
+
+// Key splits per item at most (each split writes, and the merge re-reads, a
+// full fp32 O^T per query row).
+int attention_max_splits(int items) {
+  (void)items;
+  return 8;
+}
 
 hipError_t launch_attention(Dt dt, const AttnArgs& a, hipStream_t s) {
   const int items = a.batch * a.Hkv * a.n_qg;

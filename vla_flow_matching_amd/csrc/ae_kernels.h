@@ -88,6 +88,8 @@ hipError_t launch_attention(Dt dt, const AttnArgs& a, hipStream_t s);
 size_t attention_partial_floats(int dh, int items, int nsplit, int rows_per_item);
 // query rows one item of the batched attention kernel covers
 int attention_rows_per_item();
+// key splits the batched attention kernel uses at most for `items` items
+int attention_max_splits(int items);
 
 hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s);
 // Y[m][n] = act(sum_k X[m][k] W[k][n] + b[n]), m < M <= 16; act 0 none, 1 SiLU.

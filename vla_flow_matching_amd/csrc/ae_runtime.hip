@@ -169,7 +169,7 @@ struct AttnPlan {
 
 // rows: query rows one item covers (64 in the whole-call kernel, the batched
 // kernel's attention_rows_per_item() otherwise)
-AttnPlan plan_attention(const ae_handle* h, int batch, int rows) {
+AttnPlan plan_attention(const ae_handle* h, int batch, int rows, int max_splits = 1 << 30) {
   AttnPlan a;
   const int R = h->T * (h->Hq / h->Hkv);
   a.n_qg = (R + rows - 1) / rows;
@@ -179,12 +179,21 @@ AttnPlan plan_attention(const ae_handle* h, int batch, int rows) {
   int ns = (kTargetBlocks + a.items - 1) / a.items;
   const int max_ns = (max_keys + 63) / 64;
   if (ns > max_ns) ns = max_ns;
+  if (ns > max_splits) ns = max_splits;
   if (ns < 1) ns = 1;
   int kc = (max_keys + ns - 1) / ns;
   kc = (kc + kstep - 1) / kstep * kstep;
   a.kc_len = kc;
   a.nsplit = (max_keys + kc - 1) / kc;
   return a;
+}
+
+// The batched attention kernel's plan.
+AttnPlan plan_attention_batched(const ae_handle* h, int batch) {
+  const int rows = attention_rows_per_item();
+  const int R = h->T * (h->Hq / h->Hkv);
+  const int items = batch * h->Hkv * ((R + rows - 1) / rows);
+  return plan_attention(h, batch, rows, attention_max_splits(items));
 }
 
 // The projection GEMMs of one layer: qkv, o, gate/up, down.
@@ -323,7 +332,7 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
   const int D = h->D, L = h->L, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const LayerPlans lp = plan_layer(h, M);
-  const AttnPlan ap = plan_attention(h, batch, attention_rows_per_item());
+  const AttnPlan ap = plan_attention_batched(h, batch);
   const float dt = -1.0f / static_cast<float>(steps);
   for (int k = 0; k < steps; ++k) {
     AE_LAUNCH(launch_action_in(h->x, M, h->A, h->w_in, h->b_in, h->h, D, h->ssq, h->Mmax, s));
@@ -381,7 +390,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
   const int D = h->D, L = h->L, F = h->F, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const TPlans tp = plan_tlayer(h, M);
-  const AttnPlan ap = plan_attention(h, batch, attention_rows_per_item());
+  const AttnPlan ap = plan_attention_batched(h, batch);
   const float dt = -1.0f / static_cast<float>(steps);
   const float eps = h->cfg.rms_eps;
   const bool f8 = h->fp8;
@@ -689,7 +698,7 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
       }
     }
     const int rows = attention_rows_per_item();
-    const AttnPlan ap = plan_attention(h, b, rows);
+    const AttnPlan ap = plan_attention_batched(h, b);
     if (ap.nsplit > 1) afl = std::max(afl, attention_partial_floats(h->dh, ap.items, ap.nsplit, rows));
     acn = std::max(acn, static_cast<size_t>(ap.items));
     if (h->G > 0 && b * h->T <= kTileM) {  // the whole-call kernel's attention scratch
