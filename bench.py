@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -36,10 +37,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "persist_kernel_c2_traffic.txt")
 
 
 def kernel_digest():
+    """Digest of the persistent kernel's code: comments and layout are
+    stripped first, so only a change to what compiles invalidates a stored
+    counter reading."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "vla_flow_matching_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "vla_flow_matching_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -23,16 +23,20 @@
 //    generation word and a waiting wave reads all words in one round;
 //  * before waiting, a workgroup issues the weight loads of its next task
 //    into registers, so the HBM stream runs through the synchronisation;
-//  * split reductions are distributed: every workgroup of a split group
-//    publishes its partial tile, counts itself in on the tile's counter, waits
-//    for the others, and then reduces only its own slice of rows (in split
-//    order, so results are bitwise reproducible) and applies the epilogue to
-//    it.  No single workgroup pulls the whole group's partials.
+//  * split-K reductions are distributed: every workgroup of a split group
+//    publishes its partial tile as (value, generation) packets, one 16-byte
+//    store per two values, then reduces only its own slice of rows: it reads
+//    that slice of every member's partial until all packets carry the
+//    phase's generation (no separate counter round trip), sums in member
+//    order (bitwise reproducible) and applies the epilogue.  Attention's key
+//    splits join on a per-item counter instead and merge the same way.
 //  * activations that cross workgroups use device-coherent 16-byte accesses,
 //    issued together and consumed afterwards; weights, the prefix K/V and the
 //    time-path tables are read-only in this kernel and use cached loads.
 // Counters only grow during a launch (targets are multiples of the split
-// count), and a fill kernel zeroes them and the barrier words before it.
+// count); a fill kernel zeroes them and the barrier words before it and
+// advances the generation base past every generation the previous launch
+// can have written, so stale packets never match.
 // Every wait is bounded: after ~0.2 s a device error flag is raised and the
 // kernel drains without waiting again.
 #include "ae_device.h"
