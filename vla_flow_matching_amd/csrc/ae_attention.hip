@@ -26,26 +26,29 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
-constexpr int kQB = 2;  // 16-row query blocks per wave
+constexpr int kQB = 1;  // 16-row query blocks per wave
 constexpr int kMergeBatch = 2;  // key splits merged per round of loads
 
 template <typename T>
-__device__ __forceinline__ uint4 load_vt_frag(const T* vrow, int kb0, int grp, int k_end);
+__device__ __forceinline__ uint4 load_vt_frag(const T* vrow, int kb0, int grp, int k_end, bool tail);
 
 // bf16: keys {kb0 + 4g + i} and {kb0 + 16 + 4g + i}, i < 4 (two 16-key blocks)
+// `tail` (uniform): the block reaches past k_end, whose keys are zeroed with
+// selects (a branch would wait for each load on its own); full blocks skip
+// the masking.
 template <>
 __device__ __forceinline__ uint4 load_vt_frag<bf16_t>(const bf16_t* vrow, int kb0, int grp,
-                                                      int k_end) {
+                                                      int k_end, bool tail) {
   const int ka = kb0 + 4 * grp, kb = kb0 + 16 + 4 * grp;
   uint2 lo = *reinterpret_cast<const uint2*>(vrow + ka);
   uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb);
   uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
-  // keys at or past k_end are zeroed with selects (a branch would wait for
-  // each load on its own)
+  if (tail) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k0 = (i < 2 ? ka : kb) + 2 * (i % 2);
-    w[i] &= k0 >= k_end ? 0u : (k0 + 1 >= k_end ? 0x0000ffffu : 0xffffffffu);
+    for (int i = 0; i < 4; ++i) {
+      const int k0 = (i < 2 ? ka : kb) + 2 * (i % 2);
+      w[i] &= k0 >= k_end ? 0u : (k0 + 1 >= k_end ? 0x0000ffffu : 0xffffffffu);
+    }
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -53,9 +56,10 @@ __device__ __forceinline__ uint4 load_vt_frag<bf16_t>(const bf16_t* vrow, int kb
 // fp32: keys {kb0 + 4g + i}, i < 4 (one 16-key block)
 template <>
 __device__ __forceinline__ uint4 load_vt_frag<float>(const float* vrow, int kb0, int grp,
-                                                     int k_end) {
+                                                     int k_end, bool tail) {
   const int ka = kb0 + 4 * grp;
   const uint4 v = *reinterpret_cast<const uint4*>(vrow + ka);
+  if (!tail) return v;
   return make_uint4(v.x & (ka + 0 >= k_end ? 0u : 0xffffffffu), v.y & (ka + 1 >= k_end ? 0u : 0xffffffffu),
                     v.z & (ka + 2 >= k_end ? 0u : 0xffffffffu), v.w & (ka + 3 >= k_end ? 0u : 0xffffffffu));
 }
@@ -89,6 +93,7 @@ struct KvBlock {
   static __device__ __forceinline__ void load(const T* Kb, const T* Vb, int S_max, int kb0, int k_end,
                                               uint4 (&v)[PER_WAVE]) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, grp = lane / 16;
+    const bool tail = kb0 + KSTEP > k_end;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int f = 4 * j + wave;
@@ -98,7 +103,7 @@ struct KvBlock {
         v[j] = *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(kr) * DH + kf * KSTEP + E * grp);
       } else {
         const int vr = 16 * (f - NK) + lane % 16;
-        v[j] = load_vt_frag<T>(Vb + static_cast<size_t>(vr) * S_max, kb0, grp, k_end);
+        v[j] = load_vt_frag<T>(Vb + static_cast<size_t>(vr) * S_max, kb0, grp, k_end, tail);
       }
     }
   }
@@ -109,13 +114,74 @@ struct KvBlock {
   }
 };
 
+// One staged key block (KSTEP keys at kb0; fr = the block's LDS fragments
+// + lane) against the wave's kQB query blocks: S^T = K Q^T on the MFMA units,
+// the online softmax per query column, O^T += V^T P^T.
+template <typename T, int DH, int QB>
+__device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, float scale_log2,
+                                           const uint4 (&qf)[QB][DH / Mma<T>::KSTEP],
+                                           f32x4 (&acc)[QB][DH / 16], float (&m_run)[QB], float (&l_run)[QB]) {
+  using KV = KvBlock<T, DH>;
+  using MM = Mma<T>;
+  constexpr int KSTEP = KV::KSTEP, NF = KV::NF, ND = KV::ND, NBLK = KV::NBLK, NK = KV::NK;
+  const int grp = (threadIdx.x % kWave) / 16;
+#pragma unroll
+  for (int c = 0; c < QB; ++c) {
+    f32x4 st[NBLK];
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      st[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(fr[(blk * NF + kf) * kWave], qf[c][kf], st[blk]);
+    }
+    // st[blk][i] = S^T[key kb0 + 16 blk + 4 grp + i][query lane % 16]
+    float sv[NBLK * 4];
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[blk * 4 + i] = st[blk][i] * scale_log2;
+    if (kb0 + KSTEP > k_end) {  // ragged last block (uniform branch)
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb0 + 16 * blk + 4 * grp + i >= k_end) sv[blk * 4 + i] = -INFINITY;
+    }
+    float cmax = sv[0];
+#pragma unroll
+    for (int i = 1; i < NBLK * 4; ++i) cmax = fmaxf(cmax, sv[i]);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
+    if (!__all(cmax <= m_run[c] + kSoftmaxSlack)) {  // move the reference max
+      const float m_new = fmaxf(m_run[c], cmax);
+      const float alpha = exp2_hw(m_run[c] - m_new);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[c][d] *= alpha;
+      l_run[c] *= alpha;
+      m_run[c] = m_new;
+    }
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NBLK * 4; ++i) {
+      sv[i] = exp2_hw(sv[i] - m_run[c]);
+      psum += sv[i];
+    }
+    psum += __shfl_xor(psum, 16, kWave);
+    psum += __shfl_xor(psum, 32, kWave);
+    l_run[c] += psum;
+    const uint4 pf = pack_frag<T>(sv);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) acc[c][d] = MM::mma(fr[(NK + d) * kWave], pf, acc[c][d]);
+  }
+}
+
 // One workgroup = 4 waves x kQB query blocks of 16 rows of one (request, KV
 // group), over one split of the keys.  Key blocks are staged through two LDS
 // buffers shared by the waves (the next block's loads are in flight while
 // the current one is multiplied), so every K/V byte crosses from L2 once per
 // workgroup.
 template <typename T, int DH>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
+__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs p) {
   using KV = KvBlock<T, DH>;
   using MM = Mma<T>;
   constexpr int E = KV::E, KSTEP = KV::KSTEP, NF = KV::NF, ND = KV::ND, NBLK = KV::NBLK;
@@ -182,52 +248,9 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
   }
   __syncthreads();
   for (int bi = 0; bi < n_blk; ++bi) {
-    const int kb0 = k_begin + bi * KSTEP;
-    // next block in flight (the last iteration re-reads its own block)
     KV::load(Kb, Vb, p.S_max, k_begin + min(bi + 1, n_blk - 1) * KSTEP, k_end, stage);
-    const uint4* fr = s_kv[bi & 1] + lane;
-    uint4 kfr[NK];
-#pragma unroll
-    for (int f = 0; f < NK; ++f) kfr[f] = fr[f * kWave];
-#pragma unroll
-    for (int c = 0; c < kQB; ++c) {
-      f32x4 st[NBLK];
-#pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) {
-        st[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(kfr[blk * NF + kf], qf[c][kf], st[blk]);
-      }
-      // st[blk][i] = S^T[key kb0 + 16 blk + 4 grp + i][query lane % 16]
-      float sv[NBLK * 4];
-      float cmax = -INFINITY;
-#pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb0 + 16 * blk + 4 * grp + i;
-          const float x = key < k_end ? st[blk][i] * p.scale_log2 : -INFINITY;
-          sv[blk * 4 + i] = x;
-          cmax = fmaxf(cmax, x);
-        }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
-      const float m_new = fmaxf(m_run[c], cmax);
-      const float alpha = exp2f(m_run[c] - m_new);
-      float psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NBLK * 4; ++i) {
-        sv[i] = exp2f(sv[i] - m_new);
-        psum += sv[i];
-      }
-      psum += __shfl_xor(psum, 16, kWave);
-      psum += __shfl_xor(psum, 32, kWave);
-      l_run[c] = l_run[c] * alpha + psum;
-      m_run[c] = m_new;
-      const uint4 pf = pack_frag<T>(sv);
-#pragma unroll
-      for (int d = 0; d < ND; ++d) acc[c][d] = MM::mma(fr[(NK + d) * kWave], pf, acc[c][d] * alpha);
-    }
+    attn_block<T, DH, kQB>(s_kv[bi & 1] + lane, k_begin + bi * KSTEP, k_end, p.scale_log2, qf, acc, m_run,
+                           l_run);
     KV::store(s_kv[(bi + 1) & 1], stage);
     __syncthreads();
   }
@@ -276,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs p) {
         for (int j = 0; j < kMergeBatch; ++j) {
           if (s0 + j >= p.nsplit || ms[j] == -INFINITY) continue;  // repeat or empty split
           const float m_new = fmaxf(mx, ms[j]);
-          const float a_old = exp2f(mx - m_new), a_new = exp2f(ms[j] - m_new);
+          const float a_old = exp2_hw(mx - m_new), a_new = exp2_hw(ms[j] - m_new);
           lsum = lsum * a_old + ls[j] * a_new;
 #pragma unroll
           for (int d = 0; d < ND; ++d)
@@ -325,11 +348,12 @@ size_t attention_partial_floats(int dh, int items, int nsplit, int rows_per_item
 
 int attention_rows_per_item() { return 4 * kQB * 16; }
 
-// Key splits per item at most (each split writes, and the merge re-reads, a
-// full fp32 O^T per query row).
+// Key splits per item at most: each split writes, and the last one re-reads,
+// a full fp32 O^T per query row, and that merge runs in one workgroup per
+// item, so few long splits beat many short ones.
 int attention_max_splits(int items) {
   (void)items;
-  return 8;
+  return 2;
 }
 
 hipError_t launch_attention(Dt dt, const AttnArgs& a, hipStream_t s) {

@@ -111,6 +111,17 @@ template <> __device__ __forceinline__ void unpack_frag<float>(uint4 f, float* v
   v[2] = __uint_as_float(f.z); v[3] = __uint_as_float(f.w);
 }
 
+// Hardware base-2 exponential (one v_exp_f32).  Results below 2^-126 may
+// flush to zero; in a softmax that only drops terms more than 2^126 times
+// smaller than the largest one.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax slack (log2 units): the running reference max of a query
+// only moves when a new score exceeds it by more than this, so the rescale
+// of the output accumulators is skipped for almost every key block.  Terms
+// then reach at most 2^kSoftmaxSlack; the final ratio is unchanged.
+constexpr float kSoftmaxSlack = 8.0f;
+
 // ---------------------------------------------------------------------------
 // Reductions within a wave (64 lanes)
 // ---------------------------------------------------------------------------

@@ -655,33 +655,42 @@ __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void
             for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(fr[(blk * NF + kf) * kWave], s_q[wave][kf][lane], st[blk]);
           }
           float sv[NBLK * 4];
-          float cmax = -INFINITY;
 #pragma unroll
           for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kb0 + 16 * blk + 4 * grp + i;
-              const float x = key < k_end ? st[blk][i] * p.scale_log2 : -INFINITY;
-              sv[blk * 4 + i] = x;
-              cmax = fmaxf(cmax, x);
-            }
+            for (int i = 0; i < 4; ++i) sv[blk * 4 + i] = st[blk][i] * p.scale_log2;
+          if (kb0 + KSTEP > k_end) {  // ragged last block (uniform branch)
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (kb0 + 16 * blk + 4 * grp + i >= k_end) sv[blk * 4 + i] = -INFINITY;
+          }
+          float cmax = sv[0];
+#pragma unroll
+          for (int i = 1; i < NBLK * 4; ++i) cmax = fmaxf(cmax, sv[i]);
           cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
           cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
-          const float m_new = fmaxf(m_run, cmax);
-          const float alpha = exp2f(m_run - m_new);
+          if (!__all(cmax <= m_run + kSoftmaxSlack)) {  // move the reference max
+            const float m_new = fmaxf(m_run, cmax);
+            const float alpha = exp2_hw(m_run - m_new);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+          }
           float psum = 0.0f;
 #pragma unroll
           for (int i = 0; i < NBLK * 4; ++i) {
-            sv[i] = exp2f(sv[i] - m_new);
+            sv[i] = exp2_hw(sv[i] - m_run);
             psum += sv[i];
           }
           psum += __shfl_xor(psum, 16, kWave);
           psum += __shfl_xor(psum, 32, kWave);
-          l_run = l_run * alpha + psum;
-          m_run = m_new;
+          l_run += psum;
           const uint4 pf = pack_frag<T>(sv);
 #pragma unroll
-          for (int d = 0; d < ND; ++d) acc[d] = MM::mma(fr[(NBLK * NF + d) * kWave], pf, acc[d] * alpha);
+          for (int d = 0; d < ND; ++d) acc[d] = MM::mma(fr[(NBLK * NF + d) * kWave], pf, acc[d]);
         }
       }
       __syncthreads();  // staged blocks are dead before the next round overwrites them
@@ -744,7 +753,7 @@ __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void
           // an empty split (m = -inf) or a clamped repeat carries no weight
           if (s0 + j >= p.nsplit || mv[j] == -INFINITY) continue;
           const float m_new = fmaxf(mx, mv[j]);
-          const float a_old = exp2f(mx - m_new), a_new = exp2f(mv[j] - m_new);
+          const float a_old = exp2_hw(mx - m_new), a_new = exp2_hw(mv[j] - m_new);
           lsum = lsum * a_old + lv[j] * a_new;
           o = o * a_old + a_new * f32x4{__uint_as_float(av[j].x), __uint_as_float(av[j].y),
                                         __uint_as_float(av[j].z), __uint_as_float(av[j].w)};
