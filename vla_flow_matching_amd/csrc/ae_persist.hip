@@ -70,30 +70,29 @@ __device__ __forceinline__ void bar_arrive(const PersistArgs& p, int gen) {
 }
 
 // All workgroups have arrived at generation `gen`.  Wave 0 polls every
-// word in one round of loads per poll.
+// word, and the device error flag, in one round of loads per poll (the flag
+// rides along, so a wait costs no extra round trip); it gives up once the
+// flag is set or after kSpinLimit polls.
 __device__ __forceinline__ void bar_wait(const PersistArgs& p, int gen) {
   if (threadIdx.x < kWave) {
-    const Coh cf(p.flags);
+    const Coh cf(p.flags), ce(p.err);
+    constexpr int kPer = kMaxG / kWave;
     long spins = 0;
-    if (!dev_error(p)) {
-      for (;;) {
-        int v[kMaxG / kWave];
+    for (;;) {
+      int v[kPer];
 #pragma unroll
-        for (int j = 0; j < kMaxG / kWave; ++j) {
-          const int i = threadIdx.x + j * kWave;
-          v[j] = i < p.G ? static_cast<int>(cf.ld4(4u * i)) : gen;
-        }
-        int ok = 1;
+      for (int j = 0; j < kPer; ++j)
+        v[j] = static_cast<int>(cf.ld4(4u * min(static_cast<int>(threadIdx.x) + j * kWave, p.G - 1)));
+      const int err = static_cast<int>(ce.ld4(0));
+      int ok = 1;
 #pragma unroll
-        for (int j = 0; j < kMaxG / kWave; ++j) ok &= v[j] >= gen;
-        if (__all(ok)) break;
-        if (++spins > kSpinLimit) {
-          if (threadIdx.x == 0) raise_error(p);
-          break;
-        }
-        if ((spins & 255) == 0 && dev_error(p)) break;
-        __builtin_amdgcn_s_sleep(1);
+      for (int j = 0; j < kPer; ++j) ok &= v[j] >= gen;
+      if (__all(ok) || err != 0) break;
+      if (++spins > kSpinLimit) {
+        if (threadIdx.x == 0) raise_error(p);
+        break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
