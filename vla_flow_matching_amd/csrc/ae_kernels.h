@@ -92,6 +92,10 @@ int attention_rows_per_item();
 int attention_max_splits(int items);
 
 hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s);
+// out[k][l][n] = sum_d mod[k][l][which][d] * W_l[d][n] for packed weights
+// (n in packed column order), steps k < n_steps, layers l < L.
+hipError_t launch_shift_bias(Dt dt, const uint4* W, size_t layer_stride, int K, int N, const float* mod,
+                             int n_steps, int L, int D, int which, float* out, hipStream_t s);
 // Y[m][n] = act(sum_k X[m][k] W[k][n] + b[n]), m < M <= 16; act 0 none, 1 SiLU.
 // grid.y = n_mat matrices with strides (W, b, Y advance by the given strides).
 hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const void* W, int ldw,
@@ -208,6 +212,9 @@ struct PersistArgs {
   const float *rope_cos, *rope_sin;
   float *x, *h, *ssq;
   void *q, *o, *act;
+  void* ha;              // T [M][D]: h (1 + scale) of the norm that reads h next
+  const float *bq, *bg;  // [steps][L][N]: shift W of the QKV and gate/up norms
+  int qkv_n;
   float* gpart;  // split-K partials as (value, generation) packets
   int* gcnt;
   float* apart;

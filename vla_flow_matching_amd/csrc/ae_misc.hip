@@ -253,7 +253,52 @@ __global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V
   }
 }
 
+// The shift term of a norm folded through the next projection:
+// out[k][l][n] = sum_d mod[k][l][which][d] W_l[d][n] (adaRMS(h) W =
+// r (h (1 + scale)) W + shift W), read straight from the packed fragments, so
+// n is in packed column order.  One wave per (16-column block, layer): lane
+// (g, j) holds k-slot g of column j; fp32 sums, one step at a time.
+template <typename T>
+__global__ void shift_bias_kernel(const uint4* W, size_t layer_stride, int K, int N, const float* mod,
+                                  int n_steps, int L, int D, int which, float* out) {
+  constexpr int E = Mma<T>::E, KSTEP = Mma<T>::KSTEP;
+  const int nb = blockIdx.x, l = blockIdx.y, lane = threadIdx.x, g = lane / 16;
+  const int k_frags = K / KSTEP;
+  const uint4* Wf = W + l * layer_stride + static_cast<size_t>(nb) * k_frags * kWave + lane;
+  for (int k = 0; k < n_steps; ++k) {
+    const float* sh = mod + ((static_cast<size_t>(k) * L + l) * 6 + which) * D;
+    float acc = 0.0f;
+    for (int kf = 0; kf < k_frags; ++kf) {
+      const uint4 w = Wf[static_cast<size_t>(kf) * kWave];
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      const int d0 = kf * KSTEP + E * g;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float wv = sizeof(T) == 2 ? __uint_as_float((wd[i / 2] >> (16 * (i % 2))) << 16)
+                                        : __uint_as_float(wd[i % 4]);
+        acc += sh[d0 + i] * wv;
+      }
+    }
+    acc += __shfl_xor(acc, 16, kWave);
+    acc += __shfl_xor(acc, 32, kWave);
+    if (lane < 16) out[(static_cast<size_t>(k) * L + l) * N + 16 * nb + lane] = acc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_shift_bias(Dt dt, const uint4* W, size_t layer_stride, int K, int N, const float* mod,
+                             int n_steps, int L, int D, int which, float* out, hipStream_t s) {
+  if (N % 16 || K % 32 || K > D || n_steps < 1 || L < 1) return hipErrorInvalidValue;
+  dim3 grid(N / 16, L), block(kWave);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(shift_bias_kernel<bf16_t>, grid, block, 0, s, W, layer_stride, K, N, mod, n_steps, L,
+                       D, which, out);
+  else
+    hipLaunchKernelGGL(shift_bias_kernel<float>, grid, block, 0, s, W, layer_stride, K, N, mod, n_steps, L, D,
+                       which, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s) {
   hipLaunchKernelGGL(tpath_sinusoid_kernel, dim3(n_steps), dim3(256), 0, s, e, n_steps, width);

@@ -129,52 +129,39 @@ __device__ __forceinline__ void row_slice(int s, int n, int rows, int& r0, int& 
 // range of a task split again over the four waves
 // ---------------------------------------------------------------------------
 
+// PRO_ADARMS here: A is the shadow ha = T(h (1 + scale)) of the adaRMS
+// input, and the norm finishes after the product, per output element:
+//   adaRMS(h) W = r_row * (h (1 + scale)) W + shift W,   r_row = 1 / rms(h_row),
+// with shift W (`bias`) precomputed per step and layer and r_row from the
+// partial sums of squares.  The product can then start as soon as A lands.
 struct GemmLayer {
   const uint4* W;
-  const void* A;  // PRO_NONE: T [M][lda]; PRO_ADARMS: fp32 h [M][lda]
+  const void* A;  // T [M][lda]
   int lda;
-  const float* scale;
-  const float* shift;
-  const float* gate;
+  const float* bias;  // PRO_ADARMS: shift W, per packed column
+  const float* gate;  // EPI_RESID: gate per column
+  const float* nsc;   // EPI_RESID: the next norm's scale (writes ha), or null
   void* kc;  // layer's K cache
   void* vt;  // layer's V^T cache
 };
 
-// Modulation scale / shift of a task's k range [k_lo, k_lo + k_len)
-// (k_len <= 512) into LDS.  They depend only on the step, so this runs
-// before the barrier wait and its loads overlap it.
-__device__ __forceinline__ void load_mod(const float* scale, const float* shift, int k_lo, int k_len,
-                                         float* s_sc, float* s_sh) {
-  float sc[2], sh[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = min(static_cast<int>(threadIdx.x) + j * kThreads, k_len - 1);
-    sc[j] = scale[k_lo + i];
-    sh[j] = shift[k_lo + i];
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = threadIdx.x + j * kThreads;
-    s_sc[i] = 1.0f + sc[j];
-    s_sh[i] = sh[j];
-  }
-}
-
 // Per-row reciprocal RMS of h from the per-64-column partial sums of
-// squares: four threads per row each add every fourth partial (all loads in
-// flight at once), two shuffles finish the row sum.  Rows <= 64, partials
-// <= 64.
-__device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, float* s_r) {
-  (void)s_part;
+// squares: four threads per row each load every fourth partial (issued early,
+// all in flight together), and finish_rms adds them up (two shuffles) into
+// s_r.  Rows <= 64, partials <= 64.
+__device__ __forceinline__ void issue_rms(const PersistArgs& p, float (&v)[16]) {
   const Coh cs(p.ssq);
   const int row = threadIdx.x / 4, part = threadIdx.x % 4;
   const int rc = min(row, p.M - 1);
-  float v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int q = min(part + 4 * j, p.ssq_tiles - 1);
     v[j] = cs.ldf(4u * (q * p.ldssq + rc));
   }
+}
+
+__device__ __forceinline__ void finish_rms(const PersistArgs& p, const float (&v)[16], float* s_r) {
+  const int row = threadIdx.x / 4, part = threadIdx.x % 4;
   float acc = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j)
@@ -182,7 +169,6 @@ __device__ __forceinline__ void load_rms(const PersistArgs& p, float* s_part, fl
   acc += __shfl_xor(acc, 1, kWave);
   acc += __shfl_xor(acc, 2, kWave);
   if (part == 0 && row < p.M) s_r[row] = 1.0f / sqrtf(acc / static_cast<float>(p.D) + p.eps);
-  __syncthreads();
 }
 
 template <typename T, int PRO, int EPI>
@@ -193,14 +179,11 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
   constexpr int KSTEP = MM::KSTEP;
   constexpr int MT = kTileM / 16;
   constexpr int NB = kTileN / 16;
-  constexpr int AW = PRO == PRO_ADARMS ? E / 4 : 1;  // 16-byte A loads per fragment
-  constexpr int kRw = kTileM / 4;                     // epilogue rows per wave at most
+  constexpr int kRw = kTileM / 4;  // epilogue rows per wave at most
   auto s_red = reinterpret_cast<f32x4 (*)[MT * NB][kWave]>(smem);
   auto s_y = reinterpret_cast<float (*)[kTileN + 1]>(smem);
+  // row 1/rms (PRO_ADARMS), past the reduction tile
   float* s_r = reinterpret_cast<float*>(smem + 4 * MT * NB * kWave * sizeof(f32x4));
-  float* s_part = s_r + kTileM;        // [ssq_tiles * M] (<= 64 * 64)
-  float* s_sc = s_part + 64 * 64;      // 1 + scale over the task's k range (<= 512)
-  float* s_sh = s_sc + 512;            // shift over the task's k range
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int rows = p.M;
@@ -229,9 +212,10 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
       for (int j = 0; j < NB; ++j) wb[c][j] = Wt[(static_cast<size_t>(j) * g.k_frags + kf) * kWave];
     }
 
-    const int k_lo = kf0 * KSTEP;
-    if (PRO == PRO_ADARMS) load_mod(ly.scale, ly.shift, k_lo, (kf1 - kf0) * KSTEP, s_sc, s_sh);
+    // per-column epilogue constants (they depend only on the step)
     const float gn = EPI == EPI_RESID ? ly.gate[nt * kTileN + lane] : 0.0f;
+    const float nsc = EPI == EPI_RESID && ly.nsc ? 1.0f + ly.nsc[nt * kTileN + lane] : 0.0f;
+    const float bs = PRO == PRO_ADARMS ? ly.bias[nt * kTileN + lane] : 0.0f;
 
     if (!waited) {
       bar_wait(p, gen_wait);
@@ -241,24 +225,19 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
     // A operand of the task, all in flight together
     const int arow = lane % 16;
     const int acol = E * (lane / 16);
-    uint4 araw[kKpw][MT][AW];
+    uint4 araw[kKpw][MT];
 #pragma unroll
     for (int c = 0; c < kKpw; ++c)
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const int row = min(16 * i + arow, rows - 1);
         const int k = min(kf0 + wave + 4 * c, g.k_frags - 1) * KSTEP + acol;
-#pragma unroll
-        for (int q = 0; q < AW; ++q)
-          araw[c][i][q] = coh_a.ld16((PRO == PRO_ADARMS ? 4u : static_cast<uint32_t>(sizeof(T))) *
-                                     (row * ly.lda + k + 4 * q));
+        araw[c][i] = coh_a.ld16(static_cast<uint32_t>(sizeof(T)) * (row * ly.lda + k));
       }
-    float rr[MT];
-    if (PRO == PRO_ADARMS) {
-      load_rms(p, s_part, s_r);
-#pragma unroll
-      for (int i = 0; i < MT; ++i) rr[i] = s_r[min(16 * i + arow, rows - 1)];
-    }
+    // the rows' partial sums of squares ride in the same round of loads and
+    // are only needed by the epilogue
+    float rv[16];
+    if (PRO == PRO_ADARMS) issue_rms(p, rv);
 
     f32x4 acc[MT][NB];
 #pragma unroll
@@ -269,32 +248,9 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
 #pragma unroll
     for (int c = 0; c < kKpw; ++c) {
       if (c < cnt) {
-        const int kk = (kf0 + wave + 4 * c) * KSTEP + acol - k_lo;
         uint4 a[MT];
-        if (PRO == PRO_ADARMS) {
-          float4 sv[AW], bv[AW];
 #pragma unroll
-          for (int q = 0; q < AW; ++q) {
-            sv[q] = *reinterpret_cast<const float4*>(s_sc + kk + 4 * q);
-            bv[q] = *reinterpret_cast<const float4*>(s_sh + kk + 4 * q);
-          }
-#pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            float v[E];
-#pragma unroll
-            for (int q = 0; q < AW; ++q) {
-              const uint4 hv = araw[c][i][q];
-              v[4 * q + 0] = __uint_as_float(hv.x) * rr[i] * sv[q].x + bv[q].x;
-              v[4 * q + 1] = __uint_as_float(hv.y) * rr[i] * sv[q].y + bv[q].y;
-              v[4 * q + 2] = __uint_as_float(hv.z) * rr[i] * sv[q].z + bv[q].z;
-              v[4 * q + 3] = __uint_as_float(hv.w) * rr[i] * sv[q].w + bv[q].w;
-            }
-            a[i] = 16 * i + arow < rows ? pack_frag<T>(v) : make_uint4(0, 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < MT; ++i) a[i] = 16 * i + arow < rows ? araw[c][i][0] : make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < MT; ++i) a[i] = 16 * i + arow < rows ? araw[c][i] : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
           if (i < mtr)
@@ -318,6 +274,7 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
 #pragma unroll
         for (int w = 0; w < 4; ++w) v[i] += s_red[w][i * NB + wave][lane];
     }
+    if (PRO == PRO_ADARMS) finish_rms(p, rv, s_r);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -407,13 +364,18 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
     }
 
     if (EPI == EPI_RESID) {
-      const Coh ch(p.h), cq(p.ssq);
+      const Coh ch(p.h), cq(p.ssq), cha(p.ha);
 #pragma unroll
       for (int i = 0; i < kRw; ++i) {
         const int row = r0 + wave + 4 * i;
         if (row >= r1) continue;
         const float hn = ein[i] + gn * s_y[row][lane];
         ch.stf(4u * (row * p.D + nt * kTileN + lane), hn);
+        if (ly.nsc) {
+          const uint32_t off = sizeof(T) * (row * p.D + nt * kTileN + lane);
+          if (sizeof(T) == 2) cha.st2(off, f2bf(hn * nsc));
+          else cha.stf(off, hn * nsc);
+        }
         const float sq = wave_sum(hn * hn);
         if (lane == 0) cq.stf(4u * (nt * p.ldssq + row), sq);
       }
@@ -421,7 +383,7 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
       // lanes 32p + jj (jj < 16) hold gate, 32p + 16 + jj the matching up
       const Coh co(p.act);
       for (int row = r0 + wave; row < r1; row += 4) {
-        const float y = s_y[row][lane];
+        const float y = PRO == PRO_ADARMS ? s_y[row][lane] * s_r[row] + bs : s_y[row][lane];
         const float other = __shfl_xor(y, 16, kWave);
         if (!hi) {
           const int f = (2 * nt + lane / 32) * 16 + lane % 16;
@@ -437,7 +399,7 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
       for (int i = 0; i < kRw; ++i) {
         const int row = r0 + wave + 4 * i;
         if (row >= r1) continue;
-        const float y = s_y[row][lane];
+        const float y = PRO == PRO_ADARMS ? s_y[row][lane] * s_r[row] + bs : s_y[row][lane];
         const float other = __shfl_xor(y, 16, kWave);
         // (a, b) -> (a cos - b sin, b cos + a sin); v is not rotated
         const float cs = seg < 2 ? ecs[i] : 1.0f, sn = seg < 2 ? esn[i] : 0.0f;
@@ -816,10 +778,12 @@ __device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool
   float* s_sq = reinterpret_cast<float*>(s_red);             // [16 slots][16 rows] (IN part)
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n_tasks = (p.M + 15) / 16;
-  const Coh cx(p.x), ch(p.h), cs(p.ssq);
+  const Coh cx(p.x), ch(p.h), cs(p.ssq), cha(p.ha);
   const int row = lane % 16;
   const int kfr = p.D / KSTEP;       // h / W_out fragments
   const int nb = p.D / 16;           // W_in column blocks
+  // the first layer's attention norm scale at the step the new h feeds
+  const float* sc_in = p.mod + static_cast<size_t>(do_out ? step + 1 : 0) * p.L * 6 * p.D;
   bool waited = false;
 
   for (int task = blockIdx.x; task < n_tasks; task += p.G) {
@@ -835,11 +799,12 @@ __device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool
         p.wout_p[(static_cast<size_t>(min(j, p.a_blocks - 1)) * kfr + min(kf, kfr - 1)) * kWave + lane]; \
   }
     uint4 wi[CPW_IN][kAF];
-    float bi[CPW_IN];
+    float bi[CPW_IN], si[CPW_IN];
 #define AE_ISSUE_WIN(q0)                                                                    \
   _Pragma("unroll") for (int q = 0; q < CPW_IN; ++q) {                                       \
     const int cb = wave + 4 * ((q0) + q);                                                   \
     bi[q] = p.b_in[16 * min(cb, nb - 1) + lane % 16];                                       \
+    si[q] = sc_in[16 * min(cb, nb - 1) + lane % 16];                                        \
     _Pragma("unroll") for (int f = 0; f < kAF; ++f) wi[q][f] =                               \
         p.win_p[(static_cast<size_t>(min(cb, nb - 1)) * p.a_frags + min(f, p.a_frags - 1)) * kWave + lane]; \
   }
@@ -984,6 +949,9 @@ __device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool
               const float hv = acc[e] + bi[q];
               if (r < rows) {
                 ch.stf(4u * ((m0 + r) * p.D + n), hv);
+                const float ha = hv * (1.0f + si[q]);
+                if (sizeof(T) == 2) cha.st2(sizeof(T) * ((m0 + r) * p.D + n), f2bf(ha));
+                else cha.stf(sizeof(T) * ((m0 + r) * p.D + n), ha);
                 sq[e] = hv * hv;
               }
             }
@@ -1049,23 +1017,27 @@ __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs p) {
       ly.kc = kc;
       ly.vt = vt;
       ly.gate = nullptr;
+      ly.nsc = nullptr;
 
-      ly.W = p.wqkv + l * p.sqkv; ly.A = p.h; ly.lda = p.D; ly.scale = md; ly.shift = md + p.D;
+      ly.W = p.wqkv + l * p.sqkv; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bq + static_cast<size_t>(it) * p.qkv_n;
       gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, p.pq, ly, gbase + 8 * it + 1, gen, smem);
       bar_arrive(p, ++gen);
 
       attention_phase<T, DH>(p, kc, vt, it, gen, smem);
       bar_arrive(p, ++gen);
 
-      ly.W = p.wo + l * p.so; ly.A = p.o; ly.lda = p.qdim; ly.gate = md + 2 * p.D;
+      ly.W = p.wo + l * p.so; ly.A = p.o; ly.lda = p.qdim; ly.gate = md + 2 * p.D; ly.nsc = md + 3 * p.D;
       gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.po, ly, gbase + 8 * it + 2, gen, smem);
       bar_arrive(p, ++gen);
 
-      ly.W = p.wgu + l * p.sgu; ly.A = p.h; ly.lda = p.D; ly.scale = md + 3 * p.D; ly.shift = md + 4 * p.D;
+      ly.W = p.wgu + l * p.sgu; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bg + static_cast<size_t>(it) * 2 * p.F;
       gemm_phase<T, PRO_ADARMS, EPI_GELU>(p, p.pg, ly, gbase + 8 * it + 3, gen, smem);
       bar_arrive(p, ++gen);
 
+      // the next layer's attention norm scale (the last layer's h goes to
+      // the final norm, which reads h itself)
       ly.W = p.wd + l * p.sd; ly.A = p.act; ly.lda = p.F; ly.gate = md + 5 * p.D;
+      ly.nsc = l + 1 < p.L ? md + 6 * p.D : nullptr;
       gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.pd, ly, gbase + 8 * it + 4, gen, smem);
       bar_arrive(p, ++gen);
     }

@@ -60,6 +60,10 @@ struct ae_handle {
   float *x = nullptr, *h = nullptr, *e = nullptr, *z = nullptr, *c = nullptr;
   float *mod = nullptr, *fmod = nullptr, *ssq = nullptr;
   void *q = nullptr, *o = nullptr, *act = nullptr;
+  // whole-call kernel: the modulated shadow of h, and the norms' shift terms
+  // folded through W_qkv / W_gate-up ([steps][L][N], packed column order)
+  void* ha = nullptr;
+  float *bq = nullptr, *bg = nullptr;
 
   // split scratch
   float *gpart = nullptr, *apart = nullptr;
@@ -320,6 +324,10 @@ ae_status enqueue_tpath(ae_handle* h, int steps, hipStream_t s) {
                                h->fmod_b, 2 * D, h->fmod + static_cast<size_t>(r0) * 2 * D, 2 * D, 0,
                                1, 0, 0, 0, s));
   }
+  if (h->bq) {  // shift W of the attention (row 1) and MLP (row 4) norms
+    AE_LAUNCH(launch_shift_bias(h->dt, h->wqkv, h->sqkv, D, h->qkv_n, h->mod, steps, L, D, 1, h->bq, s));
+    AE_LAUNCH(launch_shift_bias(h->dt, h->wgu, h->sgu, D, 2 * h->F, h->mod, steps, L, D, 4, h->bg, s));
+  }
   return AE_OK;
 }
 
@@ -478,6 +486,7 @@ PersistArgs persist_args(const ae_handle* h, int batch, int steps) {
   a.kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh;
   a.n_valid = h->n_valid; a.rope_cos = h->rope_cos; a.rope_sin = h->rope_sin;
   a.x = h->x; a.h = h->h; a.ssq = h->ssq; a.q = h->q; a.o = h->o; a.act = h->act;
+  a.ha = h->ha; a.bq = h->bq; a.bg = h->bg; a.qkv_n = h->qkv_n;
   a.gpart = h->gpart; a.gcnt = h->gcnt; a.apart = h->apart; a.acnt = h->acnt;
   a.flags = h->flags; a.err = h->derr; a.genp = h->genp;
   a.pcnt = h->pcnt;
@@ -668,6 +677,11 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   AE_ALLOC(h->q, Mm * h->qdim * es);
   AE_ALLOC(h->o, Mm * h->qdim * es);
   AE_ALLOC(h->act, Mm * F * (h->fp8 ? 4 : es));
+  if (!h->fp8) {
+    AE_ALLOC(h->ha, Mm * D * es);
+    AE_ALLOC(h->bq, static_cast<size_t>(h->Nmax) * L * h->qkv_n * 4);
+    AE_ALLOC(h->bg, static_cast<size_t>(h->Nmax) * L * 2 * F * 4);
+  }
   if (h->tiled) {
     AE_ALLOC(h->ubuf, Mm * std::max(D, F) * (h->fp8 ? 1 : 2));
     AE_ALLOC(h->rrow, Mm * 4);
