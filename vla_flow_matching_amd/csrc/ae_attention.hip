@@ -150,8 +150,8 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
     float cmax = sv[0];
 #pragma unroll
     for (int i = 1; i < NBLK * 4; ++i) cmax = fmaxf(cmax, sv[i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
+    cmax = xor16_max(cmax);
+    cmax = xor32_max(cmax);
     if (!__all(cmax <= m_run[c] + kSoftmaxSlack)) {  // move the reference max
       const float m_new = fmaxf(m_run[c], cmax);
       const float alpha = exp2_hw(m_run[c] - m_new);
@@ -166,8 +166,8 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
       sv[i] = exp2_hw(sv[i] - m_run[c]);
       psum += sv[i];
     }
-    psum += __shfl_xor(psum, 16, kWave);
-    psum += __shfl_xor(psum, 32, kWave);
+    psum = xor16_sum(psum);
+    psum = xor32_sum(psum);
     l_run[c] += psum;
     const uint4 pf = pack_frag<T>(sv);
 #pragma unroll

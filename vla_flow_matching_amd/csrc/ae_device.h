@@ -126,18 +126,51 @@ constexpr float kSoftmaxSlack = 8.0f;
 // Reductions within a wave (64 lanes)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+
+// Combine lane l with lane l ^ 32 (resp. l ^ 16) through gfx950's lane
+// swaps (one VALU op each instead of a round trip through the LDS crossbar).
+// Both partners get the same value: the lower lane's operand comes first.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The value of lane l ^ 16 (resp. l ^ 32).
+__device__ __forceinline__ float xor16_swap(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+// Rotate within each 16-lane row by N lanes (DPP row_ror).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes sharing l / 16 (one "row" of a 16x16 fragment):
+// rotate-and-add by 8, 4, 2, 1 within the row, every lane ends with the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
   return v;
 }
 
-// Sum over the 16 lanes sharing l / 16 (one "row" of a 16x16 fragment).
-__device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
+// Sum over the wave (64 lanes), every lane ends with the sum.
+__device__ __forceinline__ float wave_sum(float v) { return xor32_sum(xor16_sum(row16_sum(v))); }
 
 // ---------------------------------------------------------------------------
 // Cross-workgroup exchange (split-K / split-KV fix-up).

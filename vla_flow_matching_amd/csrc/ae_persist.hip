@@ -384,7 +384,7 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
       const Coh co(p.act);
       for (int row = r0 + wave; row < r1; row += 4) {
         const float y = PRO == PRO_ADARMS ? s_y[row][lane] * s_r[row] + bs : s_y[row][lane];
-        const float other = __shfl_xor(y, 16, kWave);
+        const float other = xor16_swap(y);
         if (!hi) {
           const int f = (2 * nt + lane / 32) * 16 + lane % 16;
           const float a = gelu_tanh(y) * other;
@@ -400,7 +400,7 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
         const int row = r0 + wave + 4 * i;
         if (row >= r1) continue;
         const float y = PRO == PRO_ADARMS ? s_y[row][lane] * s_r[row] + bs : s_y[row][lane];
-        const float other = __shfl_xor(y, 16, kWave);
+        const float other = xor16_swap(y);
         // (a, b) -> (a cos - b sin, b cos + a sin); v is not rotated
         const float cs = seg < 2 ? ecs[i] : 1.0f, sn = seg < 2 ? esn[i] : 0.0f;
         const float val = hi ? y * cs + other * sn : y * cs - other * sn;
@@ -630,8 +630,8 @@ __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void
           float cmax = sv[0];
 #pragma unroll
           for (int i = 1; i < NBLK * 4; ++i) cmax = fmaxf(cmax, sv[i]);
-          cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
-          cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
+          cmax = xor16_max(cmax);
+          cmax = xor32_max(cmax);
           if (!__all(cmax <= m_run + kSoftmaxSlack)) {  // move the reference max
             const float m_new = fmaxf(m_run, cmax);
             const float alpha = exp2_hw(m_run - m_new);
@@ -646,8 +646,8 @@ __device__ __forceinline__ void attention_phase(const PersistArgs& p, const void
             sv[i] = exp2_hw(sv[i] - m_run);
             psum += sv[i];
           }
-          psum += __shfl_xor(psum, 16, kWave);
-          psum += __shfl_xor(psum, 32, kWave);
+          psum = xor16_sum(psum);
+          psum = xor32_sum(psum);
           l_run += psum;
           const uint4 pf = pack_frag<T>(sv);
 #pragma unroll
