@@ -52,17 +52,38 @@ constexpr int kMaxG = 512;
 constexpr long kSpinLimit = 400000;
 constexpr int kTileF = kTileM * kTileN;  // floats of one partial tile
 
+// The kernel's arguments, read in place from the kernarg segment.  Every
+// phase takes a fresh copy of the segment pointer (laundered through an
+// empty asm), so the compiler reloads the fields a phase needs with scalar
+// loads at its start instead of holding every argument live in registers
+// across the whole call.
+using KArgs = const __attribute__((address_space(4))) PersistArgs;
+
+__device__ __forceinline__ PGemm plan_of(const __attribute__((address_space(4))) PGemm& g) {
+  PGemm r;
+  r.n_tiles = g.n_tiles;
+  r.k_frags = g.k_frags;
+  r.ksplit = g.ksplit;
+  return r;
+}
+
+__device__ __forceinline__ KArgs& kargs() {
+  KArgs* a = (KArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(a));
+  return *a;
+}
+
 __device__ __forceinline__ int ld_flag(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ bool dev_error(const PersistArgs& p) { return ld_flag(p.err) != 0; }
+__device__ __forceinline__ bool dev_error(KArgs& p) { return ld_flag(p.err) != 0; }
 
-__device__ __forceinline__ void raise_error(const PersistArgs& p) {
+__device__ __forceinline__ void raise_error(KArgs& p) {
   __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void bar_arrive(const PersistArgs& p, int gen) {
+__device__ __forceinline__ void bar_arrive(KArgs& p, int gen) {
   __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are acknowledged
   __syncthreads();
   if (threadIdx.x == 0)
@@ -73,7 +94,7 @@ __device__ __forceinline__ void bar_arrive(const PersistArgs& p, int gen) {
 // word, and the device error flag, in one round of loads per poll (the flag
 // rides along, so a wait costs no extra round trip); it gives up once the
 // flag is set or after kSpinLimit polls.
-__device__ __forceinline__ void bar_wait(const PersistArgs& p, int gen) {
+__device__ __forceinline__ void bar_wait(KArgs& p, int gen) {
   if (threadIdx.x < kWave) {
     const Coh cf(p.flags), ce(p.err);
     constexpr int kPer = kMaxG / kWave;
@@ -100,7 +121,7 @@ __device__ __forceinline__ void bar_wait(const PersistArgs& p, int gen) {
 
 // Count this workgroup into a split group and wait until `target` members
 // have (thread 0 spins; the caller has already waited for its own stores).
-__device__ __forceinline__ void group_join(const PersistArgs& p, int* counter, int target) {
+__device__ __forceinline__ void group_join(KArgs& p, int* counter, int target) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -149,7 +170,7 @@ struct GemmLayer {
 // squares: four threads per row each load every fourth partial (issued early,
 // all in flight together), and finish_rms adds them up (two shuffles) into
 // s_r.  Rows <= 64, partials <= 64.
-__device__ __forceinline__ void issue_rms(const PersistArgs& p, float (&v)[16]) {
+__device__ __forceinline__ void issue_rms(KArgs& p, float (&v)[16]) {
   const Coh cs(p.ssq);
   const int row = threadIdx.x / 4, part = threadIdx.x % 4;
   const int rc = min(row, p.M - 1);
@@ -160,7 +181,7 @@ __device__ __forceinline__ void issue_rms(const PersistArgs& p, float (&v)[16]) 
   }
 }
 
-__device__ __forceinline__ void finish_rms(const PersistArgs& p, const float (&v)[16], float* s_r) {
+__device__ __forceinline__ void finish_rms(KArgs& p, const float (&v)[16], float* s_r) {
   const int row = threadIdx.x / 4, part = threadIdx.x % 4;
   float acc = 0.0f;
 #pragma unroll
@@ -172,7 +193,7 @@ __device__ __forceinline__ void finish_rms(const PersistArgs& p, const float (&v
 }
 
 template <typename T, int PRO, int EPI>
-__device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g, const GemmLayer& ly,
+__device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLayer& ly,
                                            uint32_t llgen, int gen_wait, char* smem) {
   using MM = Mma<T>;
   constexpr int E = MM::E;
@@ -363,6 +384,7 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
       __syncthreads();
     }
 
+    const Coh cvt(ly.vt);
     if (EPI == EPI_RESID) {
       const Coh ch(p.h), cq(p.ssq), cha(p.ha);
 #pragma unroll
@@ -392,7 +414,41 @@ __device__ __forceinline__ void gemm_phase(const PersistArgs& p, const PGemm& g,
           else co.stf(4u * (row * p.F + f), a);
         }
       }
-    } else {  // EPI_QKV: lanes 32p + jj and 32p + 16 + jj are a rotation pair
+    } else if (2 * nt >= (p.Hq + p.Hkv) * pph) {
+      // EPI_QKV, a V tile (not rotated): V^T rows are head columns, so the
+      // member's rows are a run of consecutive keys per column.  Lane
+      // (column c / 8, key j = lane % 8) stores column c's key j: one store
+      // instruction covers eight columns' runs instead of 64 scattered keys.
+      const int pv0 = (p.Hq + p.Hkv) * pph;
+      float bsv[2];
+      int colv[2], bgv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int lc = (wave + 4 * u) * 8 + lane / 8;  // tile column
+        const int P = 2 * nt + lc / 32 - pv0;
+        bsv[u] = PRO == PRO_ADARMS ? ly.bias[nt * kTileN + lc] : 0.0f;
+        colv[u] = ((lc & 16) ? half : 0) + 16 * (P % pph) + lc % 16;
+        bgv[u] = P / pph;  // head
+      }
+      for (int rb = r0; rb < r1; rb += 8) {
+        const int row = rb + lane % 8;
+        const int rc = min(row, r1 - 1);
+        const int req = rc / p.T;
+        const int key = p.n_valid[req] + rc % p.T;
+        const float rs = PRO == PRO_ADARMS ? s_r[rc] : 1.0f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int lc = (wave + 4 * u) * 8 + lane / 8;
+          const float y = PRO == PRO_ADARMS ? s_y[rc][lc] * rs + bsv[u] : s_y[rc][lc];
+          const uint32_t bgi = static_cast<uint32_t>(req * p.Hkv + bgv[u]);
+          const uint32_t off = sizeof(T) * ((bgi * p.dh + colv[u]) * p.S_max + key);
+          if (row < r1) {
+            if (sizeof(T) == 2) cvt.st2(off, f2bf(y));
+            else cvt.stf(off, y);
+          }
+        }
+      }
+    } else {  // EPI_QKV (q or k): lanes 32p + jj and 32p + 16 + jj are a rotation pair
       const Coh cqo(p.q);
       const int col = (hi ? half : 0) + jrot;  // column within the head
 #pragma unroll
@@ -525,7 +581,7 @@ __device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, const Coh& ck
 }
 
 template <typename T, int DH>
-__device__ __forceinline__ void attention_phase(const PersistArgs& p, const void* kc_l, const void* vt_l,
+__device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, const void* vt_l,
                                                 int it, int gen_wait, char* smem) {
   using MM = Mma<T>;
   constexpr int E = MM::E, KSTEP = MM::KSTEP;
@@ -761,7 +817,7 @@ __device__ __forceinline__ void split_frag<float>(const float* v, uint4& hi, uin
 }
 
 template <typename T>
-__device__ __forceinline__ void outin_phase(const PersistArgs& p, int step, bool do_out, bool do_in,
+__device__ __forceinline__ void outin_phase(KArgs& p, int step, bool do_out, bool do_in,
                                             int gen_wait, char* smem) {
   using MM = Mma<T>;
   constexpr int E = MM::E, KSTEP = MM::KSTEP;
@@ -997,52 +1053,70 @@ constexpr int smem_bytes() {
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs p) {
+__global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs) {
   // gemm: 64 KiB reduction / tile + rms scratch; out/in: smaller
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<T, DH>()];
-  const size_t kv_layer = p.kv_layer;
   // generation base of this launch's split-K packets (advanced by the
   // counter fill that precedes every launch)
-  const uint32_t gbase = __builtin_amdgcn_readfirstlane(*p.genp);
+  const uint32_t gbase = __builtin_amdgcn_readfirstlane(*kargs().genp);
   int gen = 0;
-  outin_phase<T>(p, 0, false, true, 0, smem);  // h from x_0
-  bar_arrive(p, ++gen);
-  for (int k = 0; k < p.n_steps; ++k) {
-    for (int l = 0; l < p.L; ++l) {
-      const int it = k * p.L + l;
-      const float* md = p.mod + (static_cast<size_t>(k) * p.L + l) * 6 * p.D;
-      void* kc = static_cast<char*>(p.kcache) + l * kv_layer * sizeof(T);
-      void* vt = static_cast<char*>(p.vtcache) + l * kv_layer * sizeof(T);
-      GemmLayer ly;
-      ly.kc = kc;
-      ly.vt = vt;
-      ly.gate = nullptr;
-      ly.nsc = nullptr;
-
-      ly.W = p.wqkv + l * p.sqkv; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bq + static_cast<size_t>(it) * p.qkv_n;
-      gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, p.pq, ly, gbase + 8 * it + 1, gen, smem);
-      bar_arrive(p, ++gen);
-
-      attention_phase<T, DH>(p, kc, vt, it, gen, smem);
-      bar_arrive(p, ++gen);
-
-      ly.W = p.wo + l * p.so; ly.A = p.o; ly.lda = p.qdim; ly.gate = md + 2 * p.D; ly.nsc = md + 3 * p.D;
-      gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.po, ly, gbase + 8 * it + 2, gen, smem);
-      bar_arrive(p, ++gen);
-
-      ly.W = p.wgu + l * p.sgu; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bg + static_cast<size_t>(it) * 2 * p.F;
-      gemm_phase<T, PRO_ADARMS, EPI_GELU>(p, p.pg, ly, gbase + 8 * it + 3, gen, smem);
-      bar_arrive(p, ++gen);
-
-      // the next layer's attention norm scale (the last layer's h goes to
-      // the final norm, which reads h itself)
-      ly.W = p.wd + l * p.sd; ly.A = p.act; ly.lda = p.F; ly.gate = md + 5 * p.D;
-      ly.nsc = l + 1 < p.L ? md + 6 * p.D : nullptr;
-      gemm_phase<T, PRO_NONE, EPI_RESID>(p, p.pd, ly, gbase + 8 * it + 4, gen, smem);
-      bar_arrive(p, ++gen);
+  outin_phase<T>(kargs(), 0, false, true, 0, smem);  // h from x_0
+  bar_arrive(kargs(), ++gen);
+  for (int k = 0; k < kargs().n_steps; ++k) {
+    for (int l = 0; l < kargs().L; ++l) {
+      const int it = k * kargs().L + l;
+      {
+        KArgs& p = kargs();
+        GemmLayer ly;
+        ly.kc = static_cast<char*>(p.kcache) + l * p.kv_layer * sizeof(T);
+        ly.vt = static_cast<char*>(p.vtcache) + l * p.kv_layer * sizeof(T);
+        ly.gate = nullptr;
+        ly.nsc = nullptr;
+        ly.W = p.wqkv + l * p.sqkv; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bq + static_cast<size_t>(it) * p.qkv_n;
+        gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, plan_of(p.pq), ly, gbase + 8 * it + 1, gen, smem);
+        bar_arrive(p, ++gen);
+      }
+      {
+        KArgs& p = kargs();
+        attention_phase<T, DH>(p, static_cast<char*>(p.kcache) + l * p.kv_layer * sizeof(T),
+                               static_cast<char*>(p.vtcache) + l * p.kv_layer * sizeof(T), it, gen, smem);
+        bar_arrive(p, ++gen);
+      }
+      {
+        KArgs& p = kargs();
+        const float* md = p.mod + static_cast<size_t>(it) * 6 * p.D;
+        GemmLayer ly;
+        ly.kc = ly.vt = nullptr;
+        ly.bias = nullptr;
+        ly.W = p.wo + l * p.so; ly.A = p.o; ly.lda = p.qdim; ly.gate = md + 2 * p.D; ly.nsc = md + 3 * p.D;
+        gemm_phase<T, PRO_NONE, EPI_RESID>(p, plan_of(p.po), ly, gbase + 8 * it + 2, gen, smem);
+        bar_arrive(p, ++gen);
+      }
+      {
+        KArgs& p = kargs();
+        GemmLayer ly;
+        ly.kc = ly.vt = nullptr;
+        ly.gate = ly.nsc = nullptr;
+        ly.W = p.wgu + l * p.sgu; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bg + static_cast<size_t>(it) * 2 * p.F;
+        gemm_phase<T, PRO_ADARMS, EPI_GELU>(p, plan_of(p.pg), ly, gbase + 8 * it + 3, gen, smem);
+        bar_arrive(p, ++gen);
+      }
+      {
+        // the next layer's attention norm scale (the last layer's h goes to
+        // the final norm, which reads h itself)
+        KArgs& p = kargs();
+        const float* md = p.mod + static_cast<size_t>(it) * 6 * p.D;
+        GemmLayer ly;
+        ly.kc = ly.vt = nullptr;
+        ly.bias = nullptr;
+        ly.W = p.wd + l * p.sd; ly.A = p.act; ly.lda = p.F; ly.gate = md + 5 * p.D;
+        ly.nsc = l + 1 < p.L ? md + 6 * p.D : nullptr;
+        gemm_phase<T, PRO_NONE, EPI_RESID>(p, plan_of(p.pd), ly, gbase + 8 * it + 4, gen, smem);
+        bar_arrive(p, ++gen);
+      }
     }
-    outin_phase<T>(p, k, true, k + 1 < p.n_steps, gen, smem);
-    bar_arrive(p, ++gen);
+    outin_phase<T>(kargs(), k, true, k + 1 < kargs().n_steps, gen, smem);
+    bar_arrive(kargs(), ++gen);
   }
 }
 
