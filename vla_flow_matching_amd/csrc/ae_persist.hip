@@ -552,15 +552,21 @@ constexpr int kStageBlk = 2;     // key blocks staged in LDS at a time
 // (O^T = V^T P^T operands) into LDS in fragment order; the four waves share
 // the loads.  Keys past k_end read clamped rows (K: scores masked later) or
 // are zeroed (V^T).
+// stage_load issues this wave's loads of a block into registers and
+// stage_store parks them in LDS; stage_kv does both.
 template <typename T, int DH>
-__device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, const Coh& ck, const Coh& cv, bool coh,
-                                         int S_max, int kb0, int k_end, uint4* dst) {
+constexpr int kv_frags_per_wave() {
+  return ((Mma<T>::KSTEP / 16) * (DH / Mma<T>::KSTEP) + DH / 16) / 4;
+}
+
+template <typename T, int DH>
+__device__ __forceinline__ void stage_load(const T* Kb, const T* Vb, const Coh& ck, const Coh& cv, bool coh,
+                                           int S_max, int kb0, int k_end, uint4 (&v)[kv_frags_per_wave<T, DH>()]) {
   using MM = Mma<T>;
   constexpr int E = MM::E, KSTEP = MM::KSTEP;
   constexpr int NF = DH / KSTEP, ND = DH / 16, NBLK = KSTEP / 16;
   constexpr int NK = NBLK * NF, FPB = NK + ND;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, grp = lane / 16;
-  uint4 v[FPB / 4];
 #pragma unroll
   for (int j = 0; j < FPB / 4; ++j) {
     const int f = 4 * j + wave;
@@ -576,8 +582,21 @@ __device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, const Coh& ck
                         k_end);
     }
   }
+}
+
+template <typename T, int DH>
+__device__ __forceinline__ void stage_store(uint4* dst, const uint4 (&v)[kv_frags_per_wave<T, DH>()]) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int j = 0; j < FPB / 4; ++j) dst[(4 * j + wave) * kWave + lane] = v[j];
+  for (int j = 0; j < kv_frags_per_wave<T, DH>(); ++j) dst[(4 * j + wave) * kWave + lane] = v[j];
+}
+
+template <typename T, int DH>
+__device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, const Coh& ck, const Coh& cv, bool coh,
+                                         int S_max, int kb0, int k_end, uint4* dst) {
+  uint4 v[kv_frags_per_wave<T, DH>()];
+  stage_load<T, DH>(Kb, Vb, ck, cv, coh, S_max, kb0, k_end, v);
+  stage_store<T, DH>(dst, v);
 }
 
 template <typename T, int DH>
@@ -616,14 +635,17 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
     const Coh ck(Kb), cv(Vb), cq(p.q), co(p.o);
 
     // Key blocks made only of prefix rows do not depend on this step's QKV
-    // phase: the first ones are staged before the barrier wait, so their
-    // loads overlap the wait.  Blocks holding action rows follow after it.
-    int staged = 0;
+    // phase: waves 1..3 stage their share of the first ones before the
+    // barrier wait, so those loads overlap it.  Wave 0 polls the barrier (a
+    // wave's loads return in order), so its share follows the wait, in the
+    // same round of loads as the queries and the first round's blocks that
+    // hold action rows.
+    int pre = 0;
     if (!waited) {
-      while (staged < n_blk && staged < kStageBlk && k_begin + (staged + 1) * KSTEP <= nv) {
-        stage_kv<T, DH>(Kb, Vb, ck, cv, false, p.S_max, k_begin + staged * KSTEP, k_end,
-                        s_kv + staged * FPB * kWave);
-        ++staged;
+      while (pre < n_blk && pre < kStageBlk && k_begin + (pre + 1) * KSTEP <= nv) {
+        if (wave != 0)
+          stage_kv<T, DH>(Kb, Vb, ck, cv, false, p.S_max, k_begin + pre * KSTEP, k_end, s_kv + pre * FPB * kWave);
+        ++pre;
       }
       bar_wait(p, gen_wait);
       waited = true;
@@ -635,16 +657,30 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
     const bool qvalid = myq < R;
     const int hh = qvalid ? myq / p.T : 0;
     const int tt = qvalid ? myq % p.T : 0;
-    // Q^T fragments of this wave's 16 query rows, parked in LDS for the key loop
+    // Q^T fragments of this wave's 16 query rows (parked in LDS for the key
+    // loop) and the first round's key blocks still to stage, all in flight
+    // together
+    const int nfirst = min(kStageBlk, n_blk);
     {
       const uint32_t qoff = sizeof(T) * ((b * p.T + tt) * p.qdim + (g * G + hh) * DH + E * grp);
       uint4 qf[NF];
 #pragma unroll
       for (int kf = 0; kf < NF; ++kf)
         qf[kf] = cq.ld16(qoff + sizeof(T) * kf * KSTEP);  // rows past R: a valid row, unused
+      uint4 kv[kStageBlk][kv_frags_per_wave<T, DH>()];
+#pragma unroll
+      for (int bi = 0; bi < kStageBlk; ++bi) {
+        const int kb0 = k_begin + bi * KSTEP;
+        if (bi < nfirst && (bi >= pre || wave == 0))
+          stage_load<T, DH>(Kb, Vb, ck, cv, kb0 + KSTEP > nv, p.S_max, kb0, k_end, kv[bi]);
+      }
+#pragma unroll
+      for (int bi = 0; bi < kStageBlk; ++bi)
+        if (bi < nfirst && (bi >= pre || wave == 0)) stage_store<T, DH>(s_kv + bi * FPB * kWave, kv[bi]);
 #pragma unroll
       for (int kf = 0; kf < NF; ++kf) s_q[wave][kf][lane] = qf[kf];
     }
+    int staged = nfirst;
     f32x4 acc[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
