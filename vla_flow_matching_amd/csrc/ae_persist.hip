@@ -616,9 +616,8 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
 
   constexpr int FPB = NBLK * NF + ND;  // 1 KiB fragments per key block: K, then V^T
   static_assert(FPB % 4 == 0 && (NBLK * NF) % 4 == 0, "fragments split evenly over 4 waves");
-  // LDS: Q^T fragments [4 waves][NF][64], then kStageBlk staged key blocks [FPB][64]
-  auto s_q = reinterpret_cast<uint4 (*)[NF][kWave]>(smem);
-  uint4* s_kv = reinterpret_cast<uint4*>(smem + 4 * NF * kWave * sizeof(uint4));
+  // LDS: kStageBlk staged key blocks [FPB][64]
+  uint4* s_kv = reinterpret_cast<uint4*>(smem);
 
   for (int task = blockIdx.x; task < n_tasks; task += p.G) {
     const int item = task / p.nsplit, s = task % p.nsplit;
@@ -657,13 +656,13 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
     const bool qvalid = myq < R;
     const int hh = qvalid ? myq / p.T : 0;
     const int tt = qvalid ? myq % p.T : 0;
-    // Q^T fragments of this wave's 16 query rows (parked in LDS for the key
-    // loop) and the first round's key blocks still to stage, all in flight
-    // together
+    // Q^T fragments of this wave's 16 query rows (kept in registers for the
+    // key loop) and the first round's key blocks still to stage, all in
+    // flight together
     const int nfirst = min(kStageBlk, n_blk);
+    uint4 qf[NF];
     {
       const uint32_t qoff = sizeof(T) * ((b * p.T + tt) * p.qdim + (g * G + hh) * DH + E * grp);
-      uint4 qf[NF];
 #pragma unroll
       for (int kf = 0; kf < NF; ++kf)
         qf[kf] = cq.ld16(qoff + sizeof(T) * kf * KSTEP);  // rows past R: a valid row, unused
@@ -677,8 +676,6 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
 #pragma unroll
       for (int bi = 0; bi < kStageBlk; ++bi)
         if (bi < nfirst && (bi >= pre || wave == 0)) stage_store<T, DH>(s_kv + bi * FPB * kWave, kv[bi]);
-#pragma unroll
-      for (int kf = 0; kf < NF; ++kf) s_q[wave][kf][lane] = qf[kf];
     }
     int staged = nfirst;
     f32x4 acc[ND];
@@ -700,12 +697,20 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
         for (int bi = c0; bi < min(c0 + kStageBlk, n_blk); ++bi) {
           const int kb0 = k_begin + bi * KSTEP;
           const uint4* fr = s_kv + (bi - c0) * FPB * kWave + lane;
+          // the block's K and V^T fragments into registers up front, so the
+          // LDS reads overlap each other rather than each one the MFMA
+          // that consumes it
+          uint4 kfr[NBLK * NF], vfr[ND];
+#pragma unroll
+          for (int f = 0; f < NBLK * NF; ++f) kfr[f] = fr[f * kWave];
+#pragma unroll
+          for (int d = 0; d < ND; ++d) vfr[d] = fr[(NBLK * NF + d) * kWave];
           f32x4 st[NBLK];
 #pragma unroll
           for (int blk = 0; blk < NBLK; ++blk) {
             st[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(fr[(blk * NF + kf) * kWave], s_q[wave][kf][lane], st[blk]);
+            for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(kfr[blk * NF + kf], qf[kf], st[blk]);
           }
           float sv[NBLK * 4];
 #pragma unroll
@@ -743,7 +748,7 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
           l_run += psum;
           const uint4 pf = pack_frag<T>(sv);
 #pragma unroll
-          for (int d = 0; d < ND; ++d) acc[d] = MM::mma(fr[(NBLK * NF + d) * kWave], pf, acc[d]);
+          for (int d = 0; d < ND; ++d) acc[d] = MM::mma(vfr[d], pf, acc[d]);
         }
       }
       __syncthreads();  // staged blocks are dead before the next round overwrites them
@@ -1084,7 +1089,7 @@ template <typename T, int DH>
 constexpr int smem_bytes() {
   constexpr int gemm = 4 * (kTileM / 16) * (kTileN / 16) * kWave * 16 + 24 * 1024;
   constexpr int nf = DH / Mma<T>::KSTEP, fpb = (Mma<T>::KSTEP / 16) * nf + DH / 16;
-  constexpr int attn = (4 * nf + kStageBlk * fpb) * kWave * 16;
+  constexpr int attn = kStageBlk * fpb * kWave * 16;
   return gemm > attn ? gemm : attn;
 }
 
