@@ -153,6 +153,14 @@ __device__ __forceinline__ float xor16_swap(float x) {
   return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
 }
 
+// The value of lane l ^ 1 (resp. l ^ 2) (DPP quad permutes).
+__device__ __forceinline__ float xor1_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float xor2_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+}
+
 // Rotate within each 16-lane row by N lanes (DPP row_ror).
 template <int N>
 __device__ __forceinline__ float row_ror(float x) {

@@ -187,8 +187,8 @@ __device__ __forceinline__ void finish_rms(KArgs& p, const float (&v)[16], float
 #pragma unroll
   for (int j = 0; j < 16; ++j)
     if (part + 4 * j < p.ssq_tiles) acc += v[j];
-  acc += __shfl_xor(acc, 1, kWave);
-  acc += __shfl_xor(acc, 2, kWave);
+  acc += xor1_swap(acc);
+  acc += xor2_swap(acc);
   if (part == 0 && row < p.M) s_r[row] = 1.0f / sqrtf(acc / static_cast<float>(p.D) + p.eps);
 }
 
@@ -308,9 +308,12 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
     if (g.ksplit > 1) row_slice(s, g.ksplit, rows, r0, r1);
 
     // epilogue inputs of this member's rows (row r0 + wave + 4i, lane =
-    // column), issued now so they arrive while the group assembles
+    // column): loaded only for the wave's own rows, and after the partial
+    // is published (outstanding loads would hold up those stores), so they
+    // arrive while the group assembles
     float ein[kRw], ecs[kRw], esn[kRw];
     int enb[kRw];
+    const int nrw = r1 - r0 > wave ? (r1 - r0 - wave + 3) / 4 : 0;  // the wave's rows
     const int pph = p.dh / 32, half = p.dh / 2;
     int seg = 0, head = 0, jrot = 0;
     const bool hi = (lane & 16) != 0;
@@ -322,21 +325,26 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
       else { seg = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
       jrot = 16 * pi + lane % 16;
     }
-    if (EPI != EPI_GELU) {
-      const Coh ch(p.h);
-#pragma unroll
-      for (int i = 0; i < kRw; ++i) {
-        const int row = min(r0 + wave + 4 * i, rows - 1);
-        if (EPI == EPI_RESID) {
-          ein[i] = ch.ldf(4u * (row * p.D + nt * kTileN + lane));
-        } else {
-          const int req = row / p.T, tt = row % p.T;
-          const size_t ti2 = (static_cast<size_t>(req) * p.T + tt) * half + jrot;
-          ecs[i] = p.rope_cos[ti2];
-          esn[i] = p.rope_sin[ti2];
-          enb[i] = p.n_valid[req];
-        }
-      }
+#define AE_EPI_LOADS                                                                  \
+  if (EPI != EPI_GELU) {                                                              \
+    const Coh ch(p.h);                                                                \
+    _Pragma("unroll") for (int i = 0; i < kRw; ++i) {                                  \
+      if (i < nrw) {                                                                  \
+        const int row = r0 + wave + 4 * i;                                            \
+        if (EPI == EPI_RESID) {                                                       \
+          ein[i] = ch.ldf(4u * (row * p.D + nt * kTileN + lane));                     \
+        } else {                                                                      \
+          const int req = row / p.T, tt = row % p.T;                                  \
+          const size_t ti2 = (static_cast<size_t>(req) * p.T + tt) * half + jrot;     \
+          ecs[i] = p.rope_cos[ti2];                                                   \
+          esn[i] = p.rope_sin[ti2];                                                   \
+          enb[i] = p.n_valid[req];                                                    \
+        }                                                                             \
+      }                                                                               \
+    }                                                                                 \
+  }
+    if (g.ksplit == 1) {
+      AE_EPI_LOADS
     }
     if (g.ksplit > 1) {
       // Publish the partial as (value, llgen) 8-byte packets, then reduce
@@ -350,6 +358,8 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
         cp.st16(8u * (s * kTileF + r * kTileN + c2),
                 make_uint4(__float_as_uint(s_y[r][c2]), llgen, __float_as_uint(s_y[r][c2 + 1]), llgen));
       }
+      AE_EPI_LOADS
+#undef AE_EPI_LOADS
       const int n2 = (r1 - r0) * (kTileN / 2);  // packet pairs of the slice
       for (int i = tid; i < n2; i += kThreads) {
         const int r = r0 + i / (kTileN / 2), c2 = 2 * (i % (kTileN / 2));
@@ -359,11 +369,14 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
           uint4 buf[8];
           long spins = 0;
           for (;;) {
+            // (only the group's members: the bound is uniform)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) buf[j] = cp.ld16(off + 8u * min(s0 + j, g.ksplit - 1) * kTileF);
+            for (int j = 0; j < 8; ++j)
+              if (s0 + j < g.ksplit) buf[j] = cp.ld16(off + 8u * (s0 + j) * kTileF);
             bool ok = true;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ok = ok && buf[j].y == llgen && buf[j].w == llgen;
+            for (int j = 0; j < 8; ++j)
+              if (s0 + j < g.ksplit) ok = ok && buf[j].y == llgen && buf[j].w == llgen;
             if (ok) break;
             if (++spins > kSpinLimit || ((spins & 255) == 0 && dev_error(p))) {
               raise_error(p);
