@@ -102,8 +102,11 @@ hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const 
                             const void* b, int N, float* Y, int ldy, int act, int n_mat,
                             size_t w_stride, size_t b_stride, size_t y_stride, hipStream_t s);
 
+// (ha, sc optional: ha = bf16(h (1 + sc)) for a norm applied after the
+// next product)
 hipError_t launch_action_in(const float* x, int M, int A, const float* w_in, const float* b_in,
-                            float* h, int D, float* ssq, int ldssq, hipStream_t s);
+                            float* h, int D, float* ssq, int ldssq, hipStream_t s,
+                            uint16_t* ha = nullptr, const float* sc = nullptr);
 hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, const float* scale,
                              const float* shift, float eps, const float* w_out,
                              const float* b_out, float dt, hipStream_t s);
@@ -161,6 +164,17 @@ struct TGemmArgs {
   const float* rope_cos;
   const float* rope_sin;
   int T, Hq, Hkv, dh, S_max;
+  // bf16 norm after the product (A = bf16(h (1 + scale))): EPI_QKV / EPI_GELU
+  // finish with y = r_row acc + bias[col], r_row from the row sums of squares
+  // ssq[ssq_tiles][ldssq] (64-column partials over K columns); EPI_RESID
+  // writes those partials of the new h and, when nsc is set, the next norm's
+  // ha = bf16(h (1 + nsc))
+  const float* bias;
+  float* ssq;
+  int ldssq, ssq_tiles;
+  float eps;
+  const float* nsc;
+  uint16_t* ha;
 };
 
 struct TGemmPlan {

@@ -115,13 +115,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_rows_kernel(
 
 __global__ __launch_bounds__(64) void action_in_kernel(const float* x, int A, const float* w_in,
                                                        const float* b_in, float* h, int D,
-                                                       float* ssq, int ldssq) {
+                                                       float* ssq, int ldssq, uint16_t* ha,
+                                                       const float* sc) {
   const int m = blockIdx.x;
   const int n = blockIdx.y * 64 + threadIdx.x;
   float acc = 0.0f;
   for (int a = 0; a < A; ++a) acc = fmaf(x[m * A + a], w_in[a * D + n], acc);
   acc += b_in[n];
   h[static_cast<size_t>(m) * D + n] = acc;
+  if (ha) ha[static_cast<size_t>(m) * D + n] = f2bf(acc * (1.0f + sc[n]));
   const float sq = wave_sum(acc * acc);
   if (threadIdx.x == 0) ssq[blockIdx.y * ldssq + m] = sq;
 }
@@ -323,9 +325,11 @@ hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const 
 }
 
 hipError_t launch_action_in(const float* x, int M, int A, const float* w_in, const float* b_in,
-                            float* h, int D, float* ssq, int ldssq, hipStream_t s) {
+                            float* h, int D, float* ssq, int ldssq, hipStream_t s, uint16_t* ha,
+                            const float* sc) {
+  if ((ha == nullptr) != (sc == nullptr)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(action_in_kernel, dim3(M, D / 64), dim3(64), 0, s, x, A, w_in, b_in, h, D,
-                     ssq, ldssq);
+                     ssq, ldssq, ha, sc);
   return hipGetLastError();
 }
 

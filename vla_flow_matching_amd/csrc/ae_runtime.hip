@@ -390,10 +390,13 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
   return AE_OK;
 }
 
-// The N Euler steps on the batched tiled path.  Per layer: adaRMS rows (and
-// for fp8 their per-request codes), QKV + RoPE, attention, O-proj + gated
-// residual, adaRMS rows, gate/up + gelu, (fp8: codes of the activations),
-// down + gated residual.
+// The N Euler steps on the batched tiled path.  Per layer: (fp8: adaRMS rows
+// and their per-request codes), QKV + RoPE, attention, O-proj + gated
+// residual, (fp8: adaRMS rows and codes), gate/up + gelu, (fp8: codes of the
+// activations), down + gated residual.  In bf16 the norms run after the
+// product: the residual epilogues (and action-in) write the shadow
+// ha = bf16(h (1 + scale)) of the next norm with h's row sums of squares, and
+// QKV / gate-up finish with 1 / rms and the precomputed shift W.
 ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) {
   const int D = h->D, L = h->L, F = h->F, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
@@ -415,17 +418,33 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
     }
     return AE_OK;
   };
+  uint16_t* ha = static_cast<uint16_t*>(h->ha);
+  // the bf16 norm-after-product inputs of a QKV / gate-up product
+  auto post_norm = [&](TGemmArgs& g, const float* bias) {
+    g.A = ha; g.lda_bytes = static_cast<size_t>(D) * 2;
+    g.bias = bias; g.ssq = h->ssq; g.ldssq = h->Mmax; g.ssq_tiles = h->ssq_tiles; g.eps = eps;
+  };
+  // ... and the outputs of a residual epilogue feeding one
+  auto resid_out = [&](TGemmArgs& g, const float* next_scale) {
+    g.ssq = h->ssq; g.ldssq = h->Mmax; g.nsc = next_scale; g.ha = ha;
+  };
   for (int k = 0; k < steps; ++k) {
-    AE_LAUNCH(launch_action_in(h->x, M, h->A, h->w_in, h->b_in, h->h, D, h->ssq, h->Mmax, s));
+    const float* md0 = h->mod + static_cast<size_t>(k) * L * 6 * D;
+    AE_LAUNCH(launch_action_in(h->x, M, h->A, h->w_in, h->b_in, h->h, D, h->ssq, h->Mmax, s,
+                               f8 ? nullptr : ha, f8 ? nullptr : md0));
     for (int l = 0; l < L; ++l) {
       const float* md = h->mod + (static_cast<size_t>(k) * L + l) * 6 * D;
+      const size_t it = static_cast<size_t>(k) * L + l;
       char* kc = static_cast<char*>(h->kcache) + l * kv_layer;
       char* vc = static_cast<char*>(h->vtcache) + l * kv_layer;
-      ae_status r = norm_rows(md, md + D);
-      if (r != AE_OK) return r;
+      if (f8) {
+        ae_status r = norm_rows(md, md + D);
+        if (r != AE_OK) return r;
+      }
 
       TGemmArgs g = base_tgemm(h, tp.qkv, M, h->qkv_n, D);
       g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wqkv + l * h->sqkv; g.sw = h->wsc + 6 * l;
+      if (!f8) post_norm(g, h->bq + it * h->qkv_n);
       g.q = h->q; g.ldq = h->qdim; g.kcache = kc; g.vtcache = vc; g.n_valid = h->n_valid;
       g.rope_cos = h->rope_cos; g.rope_sin = h->rope_sin;
       g.T = h->T; g.Hq = h->Hq; g.Hkv = h->Hkv; g.dh = h->dh; g.S_max = h->S_max;
@@ -444,13 +463,17 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
       g = base_tgemm(h, tp.o, M, D, h->qdim);
       g.A = h->o; g.lda_bytes = static_cast<size_t>(h->qdim) * 2; g.W = h->wo + l * h->so;
       g.h = h->h; g.ldh = D; g.gate = md + 2 * D;
+      if (!f8) resid_out(g, md + 3 * D);
       AE_LAUNCH(launch_tgemm(OP_BF16, EPI_RESID, g, tp.o.blocks, s));
 
-      r = norm_rows(md + 3 * D, md + 4 * D);
-      if (r != AE_OK) return r;
+      if (f8) {
+        ae_status r = norm_rows(md + 3 * D, md + 4 * D);
+        if (r != AE_OK) return r;
+      }
       g = base_tgemm(h, tp.gu, M, 2 * F, D);
       g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wgu + l * h->sgu; g.sw = h->wsc + 6 * l + 3;
       g.out = h->act; g.ldo = F; g.rowmax = h->rowmax; g.ldp = h->Mmax;
+      if (!f8) post_norm(g, h->bg + it * 2 * F);
       AE_LAUNCH(launch_tgemm(tp.op, EPI_GELU, g, tp.gu.blocks, s));
       if (f8)
         AE_LAUNCH(launch_quant(static_cast<const float*>(h->act), nullptr, nullptr, nullptr, nullptr, M, F,
@@ -460,6 +483,9 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
       g.A = f8 ? h->ubuf : h->act; g.lda_bytes = F * ob; g.W = h->wd + l * h->sd;
       g.sw = h->wsc + 6 * l + 5;
       g.h = h->h; g.ldh = D; g.gate = md + 5 * D;
+      // the next layer's attention norm (the last layer's h goes to the
+      // final norm, which reads h itself)
+      if (!f8) resid_out(g, l + 1 < L ? md + 6 * D : nullptr);
       AE_LAUNCH(launch_tgemm(tp.op, EPI_RESID, g, tp.d.blocks, s));
     }
     const float* fm = h->fmod + static_cast<size_t>(k) * 2 * D;

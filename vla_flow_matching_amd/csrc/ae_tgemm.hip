@@ -286,52 +286,151 @@ __device__ __forceinline__ bool tile_of(int bid, int n_tiles, int m_tiles, int k
 
 // The GEMM epilogues on rows [m0, m0 + rows) of n-tile nt, the finished
 // values in s_y (row-major, relative to m0); wave w takes rows w, w + 4, ...
-template <int OP, int EPI>
+// s_r[row] = 1 / rms of row m0 + row from its 64-column partial sums of
+// squares over K columns.  TPR threads per row each add every TPR-th partial
+// (a fixed, unrolled set of loads, all in flight at once: norm_issue) and the
+// row's threads combine with lane swaps (norm_finish); rows <= kTT / TPR,
+// partials <= 64.
+template <int TPR>
+struct RowNorm {
+  static_assert(TPR == 2 || TPR == 4 || TPR == 16, "threads per row (a quad, or a whole 16-lane row)");
+  static constexpr int kPer = 64 / TPR;
+  float v[kPer];
+
+  __device__ __forceinline__ void issue(const TGemmArgs& p, int m0, int rows) {
+    const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
+    const int m = m0 + min(row, rows - 1);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = min(part + TPR * j, p.ssq_tiles - 1);
+      v[j] = p.ssq[static_cast<size_t>(q) * p.ldssq + m];
+    }
+  }
+  // (the caller synchronises before reading s_r)
+  __device__ __forceinline__ void finish(const TGemmArgs& p, int rows, float* s_r) const {
+    const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (part + TPR * j < p.ssq_tiles) t += v[j];
+    t += xor1_swap(t);
+    if (TPR >= 4) t += xor2_swap(t);
+    if (TPR == 16) {  // the four quad sums of the 16-lane row
+      t += row_ror<4>(t);
+      t += row_ror<8>(t);
+    }
+    if (part == 0 && row < rows) s_r[row] = 1.0f / sqrtf(t / static_cast<float>(p.K) + p.eps);
+  }
+};
+
+// (s_r: LDS scratch of >= rows floats for the norm after the product.)
+// Rows go in batches of kEB per wave: a batch's loads are all issued before
+// any of its stores, and per-column constants are loaded once, so a row
+// never waits for its own round trip behind the previous row's stores.
+constexpr int kEB = 8;
+
+// (R_READY: s_r was filled before the product)
+template <int OP, int EPI, int TPR, bool R_READY>
 __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, int rows,
-                                            float (*s_y)[kBN + 1]) {
+                                            float (*s_y)[kBN + 1], float* s_r) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const bool post_norm = OP == OP_BF16 && EPI != EPI_RESID && p.bias != nullptr;
+  if (post_norm && !R_READY) {
+    RowNorm<TPR> rn;
+    rn.issue(p, m0, rows);
+    rn.finish(p, rows, s_r);
+    __syncthreads();
+  }
   // column pair structure of the packed layout: packed column pc of this
   // tile is pair P = 4 nt + pc / 32, half pc / 16 % 2, index pc % 16
+  const int pr = lane / 16, jj = lane % 16;
+  float bias_a = 0.0f, bias_b = 0.0f;
+  if (post_norm) {
+    bias_a = p.bias[nt * kBN + 32 * pr + jj];
+    bias_b = p.bias[nt * kBN + 32 * pr + 16 + jj];
+  }
   if (EPI == EPI_RESID) {
-    // h += gate * y (fp8: y = acc * s_x * s_w); two columns per lane
-    for (int row = wave; row < rows; row += 4) {
-      const int m = m0 + row;
-      const float sx = OP == OP_FP8 ? p.sx_row[m] * p.sw[0] : 1.0f;
+    // h += gate * y (fp8: y = acc * s_x * s_w); two columns per lane; then,
+    // for a norm applied after the next product, the row sums of squares
+    // per 64 columns and the modulated bf16 shadow
+    float gt[2], ns[2];
 #pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
-        const int n = nt * kBN + 64 * hc + lane;
-        float* hp = p.h + static_cast<size_t>(m) * p.ldh + n;
-        *hp = *hp + p.gate[n] * (s_y[row][64 * hc + lane] * sx);
+    for (int hc = 0; hc < 2; ++hc) {
+      const int n = nt * kBN + 64 * hc + lane;
+      gt[hc] = p.gate[n];
+      ns[hc] = p.nsc ? 1.0f + p.nsc[n] : 0.0f;
+    }
+    for (int rb = wave; rb < rows; rb += 4 * kEB) {
+      float hv[kEB][2], sxv[kEB];
+#pragma unroll
+      for (int i = 0; i < kEB; ++i) {
+        const int m = m0 + min(rb + 4 * i, rows - 1);
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) hv[i][hc] = p.h[static_cast<size_t>(m) * p.ldh + nt * kBN + 64 * hc + lane];
+        sxv[i] = OP == OP_FP8 ? p.sx_row[m] * p.sw[0] : 1.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < kEB; ++i) {
+        const int row = rb + 4 * i;
+        if (row >= rows) break;
+        const int m = m0 + row;
+        float sq[2];
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) {
+          const int n = nt * kBN + 64 * hc + lane;
+          const float hn = hv[i][hc] + gt[hc] * (s_y[row][64 * hc + lane] * sxv[i]);
+          p.h[static_cast<size_t>(m) * p.ldh + n] = hn;
+          sq[hc] = hn * hn;
+          if (p.nsc) p.ha[static_cast<size_t>(m) * p.ldh + n] = f2bf(hn * ns[hc]);
+        }
+        if (p.ssq) {
+#pragma unroll
+          for (int hc = 0; hc < 2; ++hc) {
+            const float t = wave_sum(sq[hc]);
+            if (lane == 0) p.ssq[static_cast<size_t>(2 * nt + hc) * p.ldssq + m] = t;
+          }
+        }
       }
     }
   } else if (EPI == EPI_GELU) {
     // lanes: 64 = 4 pairs x 16; gate half at 32 pr + jj, up half at +16
-    const int pr = lane / 16, jj = lane % 16;
     const int f = (4 * nt + pr) * 16 + jj;
-    for (int row = wave; row < rows; row += 4) {
-      const int m = m0 + row;
-      float g = s_y[row][32 * pr + jj], u = s_y[row][32 * pr + 16 + jj];
-      if (OP == OP_FP8) {
-        const float sx = p.sx_row[m];
-        g = g * (sx * p.sw[0]);
-        u = u * (sx * p.sw[1]);
-      }
-      const float a = gelu_tanh(g) * u;
-      if (OP == OP_FP8) {
-        static_cast<float*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = a;
-        float mx = fabsf(a);
+    const float sw0 = OP == OP_FP8 ? p.sw[0] : 1.0f, sw1 = OP == OP_FP8 ? p.sw[1] : 1.0f;
+    for (int rb = wave; rb < rows; rb += 4 * kEB) {
+      float sxv[kEB];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-        if (lane == 0) p.rowmax[static_cast<size_t>(nt) * p.ldp + m] = mx;
-      } else {
-        static_cast<bf16_t*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = f2bf(a);
+      for (int i = 0; i < kEB; ++i) sxv[i] = OP == OP_FP8 ? p.sx_row[m0 + min(rb + 4 * i, rows - 1)] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < kEB; ++i) {
+        const int row = rb + 4 * i;
+        if (row >= rows) break;
+        const int m = m0 + row;
+        float g = s_y[row][32 * pr + jj], u = s_y[row][32 * pr + 16 + jj];
+        if (post_norm) {
+          const float r = s_r[row];
+          g = g * r + bias_a;
+          u = u * r + bias_b;
+        }
+        if (OP == OP_FP8) {
+          g = g * (sxv[i] * sw0);
+          u = u * (sxv[i] * sw1);
+        }
+        const float a = gelu_tanh(g) * u;
+        if (OP == OP_FP8) {
+          static_cast<float*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = a;
+          float mx = fabsf(a);
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+          if (lane == 0) p.rowmax[static_cast<size_t>(nt) * p.ldp + m] = mx;
+        } else {
+          static_cast<bf16_t*>(p.out)[static_cast<size_t>(m) * p.ldo + f] = f2bf(a);
+        }
       }
     }
   } else {  // EPI_QKV
     const int pph = p.dh / 32;
     const int pq = p.Hq * pph, pk = p.Hkv * pph;
     const int half = p.dh / 2;
-    const int pr = lane / 16, jj = lane % 16;
     const int P = 4 * nt + pr;
     int seg, head, pi;
     if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
@@ -342,38 +441,58 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
     bf16_t* qo = static_cast<bf16_t*>(p.q);
     bf16_t* kc = static_cast<bf16_t*>(p.kcache);
     bf16_t* vt = static_cast<bf16_t*>(p.vtcache);
-    for (int row = wave; row < rows; row += 4) {
-      const int m = m0 + row;
-      const int req = m / p.T, t = m % p.T;
-      float a = s_y[row][32 * pr + jj], b = s_y[row][32 * pr + 16 + jj];
-      if (OP == OP_FP8) {
-        const float sc = p.sx_row[m] * sw;
-        a *= sc;
-        b *= sc;
-      }
-      if (seg < 2) {
+    for (int rb = wave; rb < rows; rb += 4 * kEB) {
+      float csv[kEB], snv[kEB], sxv[kEB];
+      int nvv[kEB];
+#pragma unroll
+      for (int i = 0; i < kEB; ++i) {
+        const int m = m0 + min(rb + 4 * i, rows - 1);
+        const int req = m / p.T, t = m % p.T;
         const size_t ti2 = (static_cast<size_t>(req) * p.T + t) * half + j;
-        const float cs = p.rope_cos[ti2], sn = p.rope_sin[ti2];
-        const float ra = a * cs - b * sn;
-        const float rb = b * cs + a * sn;
-        a = ra;
-        b = rb;
+        csv[i] = p.rope_cos[ti2];
+        snv[i] = p.rope_sin[ti2];
+        nvv[i] = p.n_valid[req];
+        sxv[i] = OP == OP_FP8 ? p.sx_row[m] : 1.0f;
       }
-      if (seg == 0) {
-        bf16_t* dst = qo + static_cast<size_t>(m) * p.ldq + head * p.dh;
-        dst[j] = f2bf(a);
-        dst[half + j] = f2bf(b);
-      } else {
-        const int key = p.n_valid[req] + t;
-        const size_t base = static_cast<size_t>(req) * p.Hkv + head;
-        if (seg == 1) {
-          bf16_t* dst = kc + (base * p.S_max + key) * p.dh;
+#pragma unroll
+      for (int i = 0; i < kEB; ++i) {
+        const int row = rb + 4 * i;
+        if (row >= rows) break;
+        const int m = m0 + row;
+        const int req = m / p.T, t = m % p.T;
+        float a = s_y[row][32 * pr + jj], b = s_y[row][32 * pr + 16 + jj];
+        if (post_norm) {
+          const float r = s_r[row];
+          a = a * r + bias_a;
+          b = b * r + bias_b;
+        }
+        if (OP == OP_FP8) {
+          const float sc = sxv[i] * sw;
+          a *= sc;
+          b *= sc;
+        }
+        if (seg < 2) {
+          const float ra = a * csv[i] - b * snv[i];
+          const float rb2 = b * csv[i] + a * snv[i];
+          a = ra;
+          b = rb2;
+        }
+        if (seg == 0) {
+          bf16_t* dst = qo + static_cast<size_t>(m) * p.ldq + head * p.dh;
           dst[j] = f2bf(a);
           dst[half + j] = f2bf(b);
         } else {
-          bf16_t* dst = vt + base * p.dh * p.S_max;
-          dst[static_cast<size_t>(j) * p.S_max + key] = f2bf(a);
-          dst[static_cast<size_t>(half + j) * p.S_max + key] = f2bf(b);
+          const int key = nvv[i] + t;
+          const size_t base = static_cast<size_t>(req) * p.Hkv + head;
+          if (seg == 1) {
+            bf16_t* dst = kc + (base * p.S_max + key) * p.dh;
+            dst[j] = f2bf(a);
+            dst[half + j] = f2bf(b);
+          } else {
+            bf16_t* dst = vt + base * p.dh * p.S_max;
+            dst[static_cast<size_t>(j) * p.S_max + key] = f2bf(a);
+            dst[static_cast<size_t>(half + j) * p.S_max + key] = f2bf(b);
+          }
         }
       }
     }
@@ -385,7 +504,8 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   using O = TOp<OP>;
   constexpr int KC = O::KC;
   // two stages of A chunks; the finished tile reuses the space
-  __shared__ __attribute__((aligned(16))) uint4 s_buf[kBM * (kBN + 1) / 4 + 4];
+  // (+ 1 / rms of the tile's rows past the finished tile)
+  __shared__ __attribute__((aligned(16))) uint4 s_buf[kBM * (kBN + 1) / 4 + kBM / 4];
   static_assert(sizeof(s_buf) >= 2 * kChunkU4 * sizeof(uint4), "stages fit");
   auto s_y = reinterpret_cast<float (*)[kBN + 1]>(s_buf);
 
@@ -398,6 +518,12 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   const int n_chunks = p.K / KC;
   const int c0 = static_cast<int>((static_cast<long long>(ks) * n_chunks) / p.ksplit);
   const int c1 = static_cast<int>((static_cast<long long>(ks + 1) * n_chunks) / p.ksplit);
+  // the rows' 1 / rms for a norm after the product (into LDS past the
+  // finished tile): loads issued after the first chunk's, summed after the
+  // K loop
+  float* s_r = reinterpret_cast<float*>(s_buf) + kBM * (kBN + 1);
+  const bool norm_here = OP == OP_BF16 && EPI != EPI_RESID && p.bias != nullptr && p.ksplit == 1;
+  RowNorm<kTT / kBM> rn;
 
   // A staging map: item i = tid + 256 j: row i/8, 16-byte column i%8.
   const uint8_t* Ab = static_cast<const uint8_t*>(p.A);
@@ -463,6 +589,7 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   TG_LOAD_B(b0, c0);
   TG_STORE_A(a0, 0);
   TG_LOAD_A(a1, min(c0 + 1, c1 - 1));
+  if (norm_here) rn.issue(p, m0, rows);
   __syncthreads();
   int c = c0;
   // (the scheduling barriers keep each chunk's global loads ahead of the
@@ -485,6 +612,7 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
     TG_COMPUTE(0, b0.b);  // odd chunk count: the last chunk sits in stage 0
     __syncthreads();      // every wave is done with the stages before s_y reuses them
   }
+  if (norm_here) rn.finish(p, rows, s_r);  // (read after the s_y barrier below)
 #undef TG_LOAD_A
 #undef TG_LOAD_B
 #undef TG_STORE_A
@@ -512,7 +640,7 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
     }
     return;
   }
-  tg_epilogue<OP, EPI>(p, nt, m0, rows, s_y);
+  tg_epilogue<OP, EPI, kTT / kBM, true>(p, nt, m0, rows, s_y, s_r);
 }
 
 // Sum of a tile's K-split partials for kRedRows rows (in split order), then
@@ -522,6 +650,7 @@ constexpr int kRedRows = 16;
 template <int OP, int EPI>
 __global__ __launch_bounds__(kTT) void tgemm_reduce_kernel(TGemmArgs p) {
   __shared__ float s_y[kRedRows][kBN + 1];
+  __shared__ float s_r[kRedRows];
   const int slices = kBM / kRedRows;
   const int tile = blockIdx.x / slices, sl = blockIdx.x % slices;
   const int nt = tile / p.m_tiles, mt = tile % p.m_tiles;
@@ -554,7 +683,7 @@ __global__ __launch_bounds__(kTT) void tgemm_reduce_kernel(TGemmArgs p) {
     s_y[r][c4] = t.x; s_y[r][c4 + 1] = t.y; s_y[r][c4 + 2] = t.z; s_y[r][c4 + 3] = t.w;
   }
   __syncthreads();
-  tg_epilogue<OP, EPI>(p, nt, m0, rows, s_y);
+  tg_epilogue<OP, EPI, kTT / kRedRows, false>(p, nt, m0, rows, s_y, s_r);
 }
 
 // ---------------------------------------------------------------------------
