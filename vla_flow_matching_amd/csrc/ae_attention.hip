@@ -28,41 +28,7 @@ constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kQB = 1;  // 16-row query blocks per wave
 constexpr int kMergeBatch = 2;  // key splits merged per round of loads
-
-template <typename T>
-__device__ __forceinline__ uint4 load_vt_frag(const T* vrow, int kb0, int grp, int k_end, bool tail);
-
-// bf16: keys {kb0 + 4g + i} and {kb0 + 16 + 4g + i}, i < 4 (two 16-key blocks)
-// `tail` (uniform): the block reaches past k_end, whose keys are zeroed with
-// selects (a branch would wait for each load on its own); full blocks skip
-// the masking.
-template <>
-__device__ __forceinline__ uint4 load_vt_frag<bf16_t>(const bf16_t* vrow, int kb0, int grp,
-                                                      int k_end, bool tail) {
-  const int ka = kb0 + 4 * grp, kb = kb0 + 16 + 4 * grp;
-  uint2 lo = *reinterpret_cast<const uint2*>(vrow + ka);
-  uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb);
-  uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
-  if (tail) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k0 = (i < 2 ? ka : kb) + 2 * (i % 2);
-      w[i] &= k0 >= k_end ? 0u : (k0 + 1 >= k_end ? 0x0000ffffu : 0xffffffffu);
-    }
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// fp32: keys {kb0 + 4g + i}, i < 4 (one 16-key block)
-template <>
-__device__ __forceinline__ uint4 load_vt_frag<float>(const float* vrow, int kb0, int grp,
-                                                     int k_end, bool tail) {
-  const int ka = kb0 + 4 * grp;
-  const uint4 v = *reinterpret_cast<const uint4*>(vrow + ka);
-  if (!tail) return v;
-  return make_uint4(v.x & (ka + 0 >= k_end ? 0u : 0xffffffffu), v.y & (ka + 1 >= k_end ? 0u : 0xffffffffu),
-                    v.z & (ka + 2 >= k_end ? 0u : 0xffffffffu), v.w & (ka + 3 >= k_end ? 0u : 0xffffffffu));
-}
+constexpr int kStages = 3;      // LDS key-block buffers
 
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, const float* v);
@@ -78,39 +44,50 @@ __device__ __forceinline__ void store4<float>(float* dst, const float* v) {
   *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// Stage one key block (KSTEP keys) into LDS in fragment order: NBLK * NF K
-// fragments (S^T = K Q^T operands), then ND V^T fragments (O^T = V^T P^T
-// operands), 1 KiB each; the four waves load a quarter each.  Keys past
-// k_end read a clamped row (K: their scores are masked) or are zeroed (V^T).
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte-per-lane copy from global memory straight into LDS (lane l's
+// bytes land at lds_dst + 16 l).  Issued as inline assembly so that the
+// compiler neither moves it nor adds waits for it; the caller waits with
+// wait_vm before a barrier.
+__device__ __forceinline__ void dma16(const void* g, const uint4* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void_t*)(lds_dst))));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// One key block (KSTEP keys) in LDS, in the cache's fragment order (the
+// key-block layout): NBLK * NF K fragments (S^T = K Q^T operands), then ND
+// V^T fragments (O^T = V^T P^T operands), 1 KiB each, each a contiguous run
+// of the cache; each wave copies a quarter.  Keys of the last block past
+// k_end are copied as they are: their scores are masked, and the cache holds
+// finite values there (zeros or another split's keys), so their zero P
+// contributes nothing.
 template <typename T, int DH>
 struct KvBlock {
   using MM = Mma<T>;
+  using LY = KvLayout<T>;
   static constexpr int E = MM::E, KSTEP = MM::KSTEP;
   static constexpr int NF = DH / KSTEP, ND = DH / 16, NBLK = KSTEP / 16;
   static constexpr int NK = NBLK * NF, FPB = NK + ND, PER_WAVE = FPB / 4;
   static_assert(FPB % 4 == 0 && NK % 4 == 0, "fragments split evenly over 4 waves");
 
-  static __device__ __forceinline__ void load(const T* Kb, const T* Vb, int S_max, int kb0, int k_end,
-                                              uint4 (&v)[PER_WAVE]) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, grp = lane / 16;
-    const bool tail = kb0 + KSTEP > k_end;
+  // Kb / Vb: the (request, head)'s K and V caches; kb0: the block's first key
+  static __device__ __forceinline__ void issue(const T* Kb, const T* Vb, int kb0, uint4* dst) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const size_t blk0 = static_cast<size_t>(kb0 / KSTEP) * LY::block_elems(DH);
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int f = 4 * j + wave;
-      if (j < NK / 4) {
-        const int blk = f / NF, kf = f % NF;
-        const int kr = min(kb0 + 16 * blk + lane % 16, k_end - 1);
-        v[j] = *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(kr) * DH + kf * KSTEP + E * grp);
-      } else {
-        const int vr = 16 * (f - NK) + lane % 16;
-        v[j] = load_vt_frag<T>(Vb + static_cast<size_t>(vr) * S_max, kb0, grp, k_end, tail);
-      }
+      const T* src = j < NK / 4 ? Kb + blk0 + (f * kWave + lane) * E : Vb + blk0 + ((f - NK) * kWave + lane) * E;
+      dma16(src, dst + f * kWave);
     }
-  }
-  static __device__ __forceinline__ void store(uint4* dst, const uint4 (&v)[PER_WAVE]) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) dst[(4 * j + wave) * kWave + lane] = v[j];
   }
 };
 
@@ -134,7 +111,8 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
 #pragma unroll
       for (int kf = 0; kf < NF; ++kf) st[blk] = MM::mma(fr[(blk * NF + kf) * kWave], qf[c][kf], st[blk]);
     }
-    // st[blk][i] = S^T[key kb0 + 16 blk + 4 grp + i][query lane % 16]
+    // st[blk][i] = S^T[key kb0 + key_of(blk, 4 grp + i)][query lane % 16]: the
+    // lane's keys kb0 + E grp .. in order
     float sv[NBLK * 4];
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
@@ -145,7 +123,7 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
       for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (kb0 + 16 * blk + 4 * grp + i >= k_end) sv[blk * 4 + i] = -INFINITY;
+          if (kb0 + KvLayout<T>::key_of(blk, 4 * grp + i) >= k_end) sv[blk * 4 + i] = -INFINITY;
     }
     float cmax = sv[0];
 #pragma unroll
@@ -176,28 +154,30 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
 }
 
 // One workgroup = 4 waves x kQB query blocks of 16 rows of one (request, KV
-// group), over one split of the keys.  Key blocks are staged through two LDS
-// buffers shared by the waves (the next block's loads are in flight while
-// the current one is multiplied), so every K/V byte crosses from L2 once per
-// workgroup.
+// group), over one split of the keys.  Key blocks are copied straight into
+// LDS buffers shared by the waves, two blocks ahead of the one being
+// multiplied, so every K/V byte crosses from L2 once per workgroup.
 template <typename T, int DH>
-__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs p) {
+__global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   using KV = KvBlock<T, DH>;
   using MM = Mma<T>;
   constexpr int E = KV::E, KSTEP = KV::KSTEP, NF = KV::NF, ND = KV::ND, NBLK = KV::NBLK;
   constexpr int NK = KV::NK, FPB = KV::FPB;
   constexpr int PW = ND * kWave * 4 + 32;  // floats of one query block's partial
-  __shared__ uint4 s_kv[2][FPB * kWave];
+  __shared__ uint4 s_kv[kStages][FPB * kWave];
   __shared__ int s_flag;
 
   const int G = p.Hq / p.Hkv;
   const int R = p.T * G;
   const int n_items = p.batch * p.Hkv * p.n_qg;
-  const int bid = blockIdx.x;
-  int idx = bid / kXcds;
-  const int s = idx % p.nsplit;
-  const int item = (idx / p.nsplit) * kXcds + bid % kXcds;
-  if (item >= n_items) return;
+  // XCD x (= block index mod 8) runs the contiguous range [x C, x C + C) of
+  // the units ordered by (item, split), so the query groups of a request
+  // share one L2 and the splits of an item one XCD.
+  const int n_units = n_items * p.nsplit, C = (n_units + kXcds - 1) / kXcds;
+  const int li = blockIdx.x / kXcds, u = (blockIdx.x % kXcds) * C + li;
+  if (li >= C || u >= n_units) return;
+  const int s = u % p.nsplit;
+  const int item = u / p.nsplit;
   const int qg = item % p.n_qg;
   const int bg = item / p.n_qg;
   const int g = bg % p.Hkv;
@@ -212,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs p) {
   const int n_blk = k_end > k_begin ? (k_end - k_begin + KSTEP - 1) / KSTEP : 0;
 
   const T* Kb = static_cast<const T*>(p.kcache) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
-  const T* Vb = static_cast<const T*>(p.vtcache) + static_cast<size_t>(b * p.Hkv + g) * DH * p.S_max;
+  const T* Vb = static_cast<const T*>(p.vtcache) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
 
   // query rows of this wave: blocks (qg * 4 + wave) * kQB + c, 16 rows each
   uint4 qf[kQB][NF];
@@ -241,18 +221,19 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs p) {
     l_run[c] = 0.0f;
   }
 
-  uint4 stage[KV::PER_WAVE];
-  if (n_blk > 0) {
-    KV::load(Kb, Vb, p.S_max, k_begin, k_end, stage);
-    KV::store(s_kv[0], stage);
-  }
-  __syncthreads();
+  // Key blocks stream through a ring of kStages LDS buffers, copied two
+  // blocks ahead of the one being multiplied.
+  if (n_blk > 0) KV::issue(Kb, Vb, k_begin, s_kv[0]);
+  if (n_blk > 1) KV::issue(Kb, Vb, k_begin + KSTEP, s_kv[1]);
   for (int bi = 0; bi < n_blk; ++bi) {
-    KV::load(Kb, Vb, p.S_max, k_begin + min(bi + 1, n_blk - 1) * KSTEP, k_end, stage);
-    attn_block<T, DH, kQB>(s_kv[bi & 1] + lane, k_begin + bi * KSTEP, k_end, p.scale_log2, qf, acc, m_run,
+    if (bi + 1 < n_blk)
+      wait_vm<KV::PER_WAVE>();  // block bi landed; block bi + 1 may still be in flight
+    else
+      wait_vm<0>();
+    __syncthreads();  // every wave's copies of block bi are visible; block bi - 1's buffer is free
+    if (bi + 2 < n_blk) KV::issue(Kb, Vb, k_begin + (bi + 2) * KSTEP, s_kv[(bi + 2) % kStages]);
+    attn_block<T, DH, kQB>(s_kv[bi % kStages] + lane, k_begin + bi * KSTEP, k_end, p.scale_log2, qf, acc, m_run,
                            l_run);
-    KV::store(s_kv[(bi + 1) & 1], stage);
-    __syncthreads();
   }
   // acc[c][d][i] = O^T[dim 16 d + 4 grp + i][query lane % 16 of block c] (unnormalised)
 
@@ -358,7 +339,7 @@ int attention_max_splits(int items) {
 
 hipError_t launch_attention(Dt dt, const AttnArgs& a, hipStream_t s) {
   const int items = a.batch * a.Hkv * a.n_qg;
-  const int blocks = kXcds * a.nsplit * ((items + kXcds - 1) / kXcds);
+  const int blocks = kXcds * ((items * a.nsplit + kXcds - 1) / kXcds);
   if (dt == DT_BF16) return launch_dh<bf16_t>(a, blocks, s);
   return launch_dh<float>(a, blocks, s);
 }

@@ -77,6 +77,43 @@ template <> struct Mma<float> {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Key-block K / V cache layout.
+//
+// The keys of one (request, KV head) are stored in blocks of KB = KSTEP keys
+// (bf16: 32, fp32: 16), each block in the fragment order the attention
+// kernels multiply from, so that one block is one contiguous run per
+// operand: the K cache holds NBLK * NF fragments per block (S^T = K Q^T
+// A-operands, fragment blk * NF + kf = keys of 16-row tile blk, dims
+// kf * KSTEP ..), the V cache ND = dh / 16 fragments (O^T = V^T P^T
+// A-operands, fragment fd = dims 16 fd .. 16 fd + 15).
+//
+// Row r of tile blk is block-local key key_of(blk, r) = E (r / 4) + 4 blk +
+// r % 4.  The 16x16 S^T result puts rows 4 g .. 4 g + 3 in lane group g, so
+// lane group g ends up with keys E g .. E g + E - 1 in order over the NBLK
+// tiles: exactly the k-slice of a P^T fragment, whose V^T partner is the
+// contiguous key run E g .. E g + E - 1 of one dim.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct KvLayout {
+  static constexpr int E = Mma<T>::E, KB = Mma<T>::KSTEP, NBLK = KB / 16;
+  static __host__ __device__ __forceinline__ int key_of(int blk, int r) { return E * (r / 4) + 4 * blk + r % 4; }
+  // element offset of K[key][c] within one (request, head)'s cache of dh columns
+  static __host__ __device__ __forceinline__ size_t k_off(int key, int c, int dh) {
+    const int j = key / KB, kk = key % KB;
+    const int r = 4 * (kk / E) + kk % 4, blk = (kk % E) / 4;
+    const int nf = dh / KB, kf = c / KB, g = (c % KB) / E;
+    return ((static_cast<size_t>(j) * NBLK * nf + blk * nf + kf) * 64 + g * 16 + r) * E + c % E;
+  }
+  // element offset of V[key][d]
+  static __host__ __device__ __forceinline__ size_t v_off(int key, int d, int dh) {
+    const int j = key / KB, kk = key % KB;
+    return ((static_cast<size_t>(j) * (dh / 16) + d / 16) * 64 + (kk / E) * 16 + d % 16) * E + kk % E;
+  }
+  // elements of one key block of the K (or V) cache: KB * dh
+  static __host__ __device__ __forceinline__ size_t block_elems(int dh) { return static_cast<size_t>(KB) * dh; }
+};
+
 // Pack 8 fp32 values into a bf16 fragment, or 4 fp32 values into an fp32 one.
 __device__ __forceinline__ uint4 pack_frag_bf16(const float* v) {
   uint4 r;

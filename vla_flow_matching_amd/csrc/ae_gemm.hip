@@ -258,14 +258,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
       } else {
         const int key = p.n_valid[req] + t;
         const size_t base = static_cast<size_t>(req) * p.Hkv + head;
+        using LY = KvLayout<T>;
+        T* dst = (seg == 1 ? kc : vt) + base * p.S_max * p.dh;
         if (seg == 1) {
-          T* dst = kc + (base * p.S_max + key) * p.dh;
-          dst[j] = Elem<T>::from_f(a);
-          dst[half + j] = Elem<T>::from_f(b);
+          dst[LY::k_off(key, j, p.dh)] = Elem<T>::from_f(a);
+          dst[LY::k_off(key, half + j, p.dh)] = Elem<T>::from_f(b);
         } else {
-          T* dst = vt + base * p.dh * p.S_max;
-          dst[static_cast<size_t>(j) * p.S_max + key] = Elem<T>::from_f(a);
-          dst[static_cast<size_t>(half + j) * p.S_max + key] = Elem<T>::from_f(b);
+          dst[LY::v_off(key, j, p.dh)] = Elem<T>::from_f(a);
+          dst[LY::v_off(key, half + j, p.dh)] = Elem<T>::from_f(b);
         }
       }
     }

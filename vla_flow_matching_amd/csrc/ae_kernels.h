@@ -50,8 +50,8 @@ struct GemmArgs {
   // EPI_QKV
   void* q;
   int ldq;
-  void* kcache;   // layer's [Bmax][Hkv][S_max][dh]
-  void* vtcache;  // layer's [Bmax][Hkv][dh][S_max]
+  void* kcache;   // layer's K cache, [Bmax][Hkv] x S_max keys x dh (key-block layout)
+  void* vtcache;  // layer's V cache, same shape and layout family
   const int* n_valid;
   const float* rope_cos;  // [B][T][dh/2]
   const float* rope_sin;
@@ -114,9 +114,9 @@ hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, cons
 hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_idx, int* n_valid,
                               int T, int dh, float theta, float* rope_cos, float* rope_sin,
                               hipStream_t s);
-hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx, int L,
-                              int batch, int P, int Hkv, int dh, int Bmax, int S_max,
-                              void* kcache, void* vtcache, hipStream_t s);
+hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx,
+                              const int* n_valid, int n_act, int L, int batch, int P, int Hkv, int dh,
+                              int Bmax, int S_max, void* kcache, void* vtcache, hipStream_t s);
 
 // Pack logical [K][N] row-major sources into MFMA fragment order; rows
 // k >= kvalid and columns n >= nvalid (PACK_PLAIN) read as zero (padding).

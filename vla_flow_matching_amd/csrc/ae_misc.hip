@@ -213,17 +213,19 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(const uint8_t* mask, i
   }
 }
 
-// copy: visible rows of K -> cache rows comp_idx (row-major [key][dh]);
-// V -> transposed cache [dh][key] through an LDS tile.  grid (L*B*Hkv,
-// ceil(P/32)), 256 threads.
+// copy: visible row j of K and V -> cache key comp_idx[j] (key-block layout,
+// KvLayout).  grid (L*B*Hkv, max(1, ceil(P/32))), 256 threads.  The first
+// row block of each (layer, request, head) also zeroes the keys past the
+// request's (n_valid + n_act .. S_max): attention multiplies whole key
+// blocks and relies on the cache being finite there.
 constexpr int kCopyRows = 32;
 
 template <typename T>
 __global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V, const int* comp_idx,
-                                                          int batch, int P, int Hkv, int dh,
-                                                          int Bmax, int S_max, T* kcache,
-                                                          T* vtcache) {
-  __shared__ T sv[kCopyRows][256 + 2];
+                                                          const int* n_valid, int n_act, int batch, int P,
+                                                          int Hkv, int dh, int Bmax, int S_max,
+                                                          T* kcache, T* vtcache) {
+  using LY = KvLayout<T>;
   __shared__ int sci[kCopyRows];
   const int lbg = blockIdx.x;
   const int g = lbg % Hkv;
@@ -237,21 +239,22 @@ __global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V
   const size_t src_row0 = ((static_cast<size_t>(l) * batch + b) * P + j0) * Hkv + g;
   const size_t cache_bg = (static_cast<size_t>(l) * Bmax + b) * Hkv + g;
   T* kdst = kcache + cache_bg * S_max * dh;
-  T* vdst = vtcache + cache_bg * dh * S_max;
+  T* vdst = vtcache + cache_bg * S_max * dh;
   for (int i = threadIdx.x; i < nrows * dh; i += 256) {
     const int r = i / dh, d = i % dh;
     const int ci = sci[r];
     if (ci < 0) continue;  // invisible row: never read
     const size_t src = (src_row0 + static_cast<size_t>(r) * Hkv) * dh + d;
-    kdst[static_cast<size_t>(ci) * dh + d] = K[src];
-    sv[r][d] = V[src];
+    kdst[LY::k_off(ci, d, dh)] = K[src];
+    vdst[LY::v_off(ci, d, dh)] = V[src];
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < nrows * dh; i += 256) {
-    const int d = i / nrows, r = i % nrows;
-    const int ci = sci[r];
-    if (ci < 0) continue;
-    vdst[static_cast<size_t>(d) * S_max + ci] = sv[r][d];
+  if (blockIdx.y == 0) {
+    const int z0 = min(n_valid[b] + n_act, S_max);
+    for (int i = threadIdx.x; i < (S_max - z0) * dh; i += 256) {
+      const int key = z0 + i / dh, d = i % dh;
+      kdst[LY::k_off(key, d, dh)] = T(0);
+      vdst[LY::v_off(key, d, dh)] = T(0);
+    }
   }
 }
 
@@ -350,21 +353,20 @@ hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_i
   return hipGetLastError();
 }
 
-hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx, int L,
-                              int batch, int P, int Hkv, int dh, int Bmax, int S_max,
-                              void* kcache, void* vtcache, hipStream_t s) {
-  if (P == 0) return hipSuccess;
+hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx,
+                              const int* n_valid, int n_act, int L, int batch, int P, int Hkv, int dh,
+                              int Bmax, int S_max, void* kcache, void* vtcache, hipStream_t s) {
   if (dh > 256) return hipErrorInvalidValue;
-  dim3 grid(L * batch * Hkv, (P + kCopyRows - 1) / kCopyRows), block(256);
+  dim3 grid(L * batch * Hkv, P > 0 ? (P + kCopyRows - 1) / kCopyRows : 1), block(256);
   if (dt == DT_BF16)
     hipLaunchKernelGGL(prefix_copy_kernel<bf16_t>, grid, block, 0, s,
-                       static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V), comp_idx,
-                       batch, P, Hkv, dh, Bmax, S_max, static_cast<bf16_t*>(kcache),
+                       static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V), comp_idx, n_valid,
+                       n_act, batch, P, Hkv, dh, Bmax, S_max, static_cast<bf16_t*>(kcache),
                        static_cast<bf16_t*>(vtcache));
   else
     hipLaunchKernelGGL(prefix_copy_kernel<float>, grid, block, 0, s, static_cast<const float*>(K),
-                       static_cast<const float*>(V), comp_idx, batch, P, Hkv, dh, Bmax, S_max,
-                       static_cast<float*>(kcache), static_cast<float*>(vtcache));
+                       static_cast<const float*>(V), comp_idx, n_valid, n_act, batch, P, Hkv, dh, Bmax,
+                       S_max, static_cast<float*>(kcache), static_cast<float*>(vtcache));
   return hipGetLastError();
 }
 

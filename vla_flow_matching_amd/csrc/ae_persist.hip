@@ -454,7 +454,8 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
           const int lc = (wave + 4 * u) * 8 + lane / 8;
           const float y = PRO == PRO_ADARMS ? s_y[rc][lc] * rs + bsv[u] : s_y[rc][lc];
           const uint32_t bgi = static_cast<uint32_t>(req * p.Hkv + bgv[u]);
-          const uint32_t off = sizeof(T) * ((bgi * p.dh + colv[u]) * p.S_max + key);
+          const uint32_t off =
+              sizeof(T) * (bgi * p.S_max * p.dh + static_cast<uint32_t>(KvLayout<T>::v_off(key, colv[u], p.dh)));
           if (row < r1) {
             if (sizeof(T) == 2) cvt.st2(off, f2bf(y));
             else cvt.stf(off, y);
@@ -483,12 +484,12 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
           const size_t bgi = static_cast<size_t>(req) * p.Hkv + head;
           if (seg == 1) {
             const Coh ck(static_cast<T*>(ly.kc) + bgi * p.S_max * p.dh);
-            const uint32_t off = sizeof(T) * (key * p.dh + col);
+            const uint32_t off = sizeof(T) * static_cast<uint32_t>(KvLayout<T>::k_off(key, col, p.dh));
             if (sizeof(T) == 2) ck.st2(off, f2bf(val));
             else ck.stf(off, val);
           } else {
-            const Coh cv(static_cast<T*>(ly.vt) + bgi * p.dh * p.S_max);
-            const uint32_t off = sizeof(T) * (col * p.S_max + key);
+            const Coh cv(static_cast<T*>(ly.vt) + bgi * p.S_max * p.dh);
+            const uint32_t off = sizeof(T) * static_cast<uint32_t>(KvLayout<T>::v_off(key, col, p.dh));
             if (sizeof(T) == 2) cv.st2(off, f2bf(val));
             else cv.stf(off, val);
           }
@@ -503,45 +504,6 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
 // Attention phase: S^T = K Q^T per 16-key block, online softmax per query
 // column, O^T = V^T P^T; split over keys, distributed merge.
 // ---------------------------------------------------------------------------
-
-template <typename T>
-__device__ __forceinline__ uint4 vt_frag(const T* vrow, const Coh& cv, uint32_t row_off, bool coh,
-                                         int kb0, int grp, int k_end);
-
-template <>
-__device__ __forceinline__ uint4 vt_frag<bf16_t>(const bf16_t* vrow, const Coh& cv, uint32_t row_off,
-                                                 bool coh, int kb0, int grp, int k_end) {
-  const int ka = kb0 + 4 * grp, kb = kb0 + 16 + 4 * grp;
-  uint2 lo, hi;
-  if (coh) {
-    lo = cv.ld8(row_off + 2u * ka);
-    hi = cv.ld8(row_off + 2u * kb);
-  } else {
-    lo = *reinterpret_cast<const uint2*>(vrow + ka);
-    hi = *reinterpret_cast<const uint2*>(vrow + kb);
-  }
-  uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
-  // keys at or past k_end are zeroed with selects (no branch: a branch
-  // would wait for each load on its own)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k0 = (i < 2 ? ka : kb) + 2 * (i % 2);
-    w[i] &= k0 >= k_end ? 0u : (k0 + 1 >= k_end ? 0x0000ffffu : 0xffffffffu);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-template <>
-__device__ __forceinline__ uint4 vt_frag<float>(const float* vrow, const Coh& cv, uint32_t row_off,
-                                                bool coh, int kb0, int grp, int k_end) {
-  const int ka = kb0 + 4 * grp;
-  uint4 v = coh ? cv.ld16(row_off + 4u * ka) : *reinterpret_cast<const uint4*>(vrow + ka);
-  v.x &= ka + 0 >= k_end ? 0u : 0xffffffffu;
-  v.y &= ka + 1 >= k_end ? 0u : 0xffffffffu;
-  v.z &= ka + 2 >= k_end ? 0u : 0xffffffffu;
-  v.w &= ka + 3 >= k_end ? 0u : 0xffffffffu;
-  return v;
-}
 
 template <typename T>
 __device__ __forceinline__ void store4_coh(const Coh& c, uint32_t off, const float* v);
@@ -562,9 +524,10 @@ constexpr int kMergeBatch = 16;  // attention splits merged per round of loads
 constexpr int kStageBlk = 2;     // key blocks staged in LDS at a time
 
 // Load one key block's K fragments (S^T = K Q^T operands) and V^T fragments
-// (O^T = V^T P^T operands) into LDS in fragment order; the four waves share
-// the loads.  Keys past k_end read clamped rows (K: scores masked later) or
-// are zeroed (V^T).
+// (O^T = V^T P^T operands) into LDS; the cache holds them in that fragment
+// order (the key-block layout), so each is one contiguous 1 KiB run, and the
+// four waves share the loads.  Keys of the last block past k_end are loaded
+// as they are: their scores are masked, and the cache is finite there.
 // stage_load issues this wave's loads of a block into registers and
 // stage_store parks them in LDS; stage_kv does both.
 template <typename T, int DH>
@@ -574,26 +537,22 @@ constexpr int kv_frags_per_wave() {
 
 template <typename T, int DH>
 __device__ __forceinline__ void stage_load(const T* Kb, const T* Vb, const Coh& ck, const Coh& cv, bool coh,
-                                           int S_max, int kb0, int k_end, uint4 (&v)[kv_frags_per_wave<T, DH>()]) {
+                                           int kb0, uint4 (&v)[kv_frags_per_wave<T, DH>()]) {
   using MM = Mma<T>;
   constexpr int E = MM::E, KSTEP = MM::KSTEP;
   constexpr int NF = DH / KSTEP, ND = DH / 16, NBLK = KSTEP / 16;
   constexpr int NK = NBLK * NF, FPB = NK + ND;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, grp = lane / 16;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const uint32_t blk0 = static_cast<uint32_t>(kb0 / KSTEP * KvLayout<T>::block_elems(DH));
 #pragma unroll
   for (int j = 0; j < FPB / 4; ++j) {
     const int f = 4 * j + wave;
-    if (j < NK / 4) {
-      const int blk = f / NF, kf = f % NF;
-      const int kr = min(kb0 + 16 * blk + lane % 16, k_end - 1);
-      const int col = kf * KSTEP + E * grp;
-      v[j] = coh ? ck.ld16(sizeof(T) * (kr * DH + col))
-                 : *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(kr) * DH + col);
-    } else {
-      const int vr = 16 * (f - NK) + lane % 16;
-      v[j] = vt_frag<T>(Vb + static_cast<size_t>(vr) * S_max, cv, sizeof(T) * vr * S_max, coh, kb0, grp,
-                        k_end);
-    }
+    const bool isk = j < NK / 4;
+    const uint32_t e = blk0 + static_cast<uint32_t>(((isk ? f : f - NK) * kWave + lane) * E);
+    if (coh)
+      v[j] = (isk ? ck : cv).ld16(sizeof(T) * e);
+    else
+      v[j] = *reinterpret_cast<const uint4*>((isk ? Kb : Vb) + e);
   }
 }
 
@@ -606,9 +565,9 @@ __device__ __forceinline__ void stage_store(uint4* dst, const uint4 (&v)[kv_frag
 
 template <typename T, int DH>
 __device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, const Coh& ck, const Coh& cv, bool coh,
-                                         int S_max, int kb0, int k_end, uint4* dst) {
+                                         int kb0, uint4* dst) {
   uint4 v[kv_frags_per_wave<T, DH>()];
-  stage_load<T, DH>(Kb, Vb, ck, cv, coh, S_max, kb0, k_end, v);
+  stage_load<T, DH>(Kb, Vb, ck, cv, coh, kb0, v);
   stage_store<T, DH>(dst, v);
 }
 
@@ -643,7 +602,7 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
     const int k_end = min(k_begin + p.kc_len, len);
     const int n_blk = k_end > k_begin ? (k_end - k_begin + KSTEP - 1) / KSTEP : 0;
     const T* Kb = static_cast<const T*>(kc_l) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
-    const T* Vb = static_cast<const T*>(vt_l) + static_cast<size_t>(b * p.Hkv + g) * DH * p.S_max;
+    const T* Vb = static_cast<const T*>(vt_l) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
     const Coh ck(Kb), cv(Vb), cq(p.q), co(p.o);
 
     // Key blocks made only of prefix rows do not depend on this step's QKV
@@ -656,7 +615,7 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
     if (!waited) {
       while (pre < n_blk && pre < kStageBlk && k_begin + (pre + 1) * KSTEP <= nv) {
         if (wave != 0)
-          stage_kv<T, DH>(Kb, Vb, ck, cv, false, p.S_max, k_begin + pre * KSTEP, k_end, s_kv + pre * FPB * kWave);
+          stage_kv<T, DH>(Kb, Vb, ck, cv, false, k_begin + pre * KSTEP, s_kv + pre * FPB * kWave);
         ++pre;
       }
       bar_wait(p, gen_wait);
@@ -684,7 +643,7 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
       for (int bi = 0; bi < kStageBlk; ++bi) {
         const int kb0 = k_begin + bi * KSTEP;
         if (bi < nfirst && (bi >= pre || wave == 0))
-          stage_load<T, DH>(Kb, Vb, ck, cv, kb0 + KSTEP > nv, p.S_max, kb0, k_end, kv[bi]);
+          stage_load<T, DH>(Kb, Vb, ck, cv, kb0 + KSTEP > nv, kb0, kv[bi]);
       }
 #pragma unroll
       for (int bi = 0; bi < kStageBlk; ++bi)
@@ -701,8 +660,7 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
       // action rows written by this launch)
       for (int bi = max(staged, c0); bi < min(c0 + kStageBlk, n_blk); ++bi) {
         const int kb0 = k_begin + bi * KSTEP;
-        stage_kv<T, DH>(Kb, Vb, ck, cv, kb0 + KSTEP > nv, p.S_max, kb0, k_end,
-                        s_kv + (bi - c0) * FPB * kWave);
+        stage_kv<T, DH>(Kb, Vb, ck, cv, kb0 + KSTEP > nv, kb0, s_kv + (bi - c0) * FPB * kWave);
       }
       staged = 0;
       __syncthreads();
@@ -735,7 +693,7 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
             for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                if (kb0 + 16 * blk + 4 * grp + i >= k_end) sv[blk * 4 + i] = -INFINITY;
+                if (kb0 + KvLayout<T>::key_of(blk, 4 * grp + i) >= k_end) sv[blk * 4 + i] = -INFINITY;
           }
           float cmax = sv[0];
 #pragma unroll

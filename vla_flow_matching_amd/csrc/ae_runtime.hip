@@ -908,8 +908,8 @@ ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   AE_HIP(h, launch_prefix_scan(valid_mask, batch, prefix_len, h->comp_idx, h->n_valid, h->T, h->dh,
                                h->cfg.rope_theta, h->rope_cos, h->rope_sin, st));
-  AE_HIP(h, launch_prefix_copy(h->dt, K, V, h->comp_idx, h->L, batch, prefix_len, h->Hkv, h->dh,
-                               h->Bmax, h->S_max, h->kcache, h->vtcache, st));
+  AE_HIP(h, launch_prefix_copy(h->dt, K, V, h->comp_idx, h->n_valid, h->T, h->L, batch, prefix_len,
+                               h->Hkv, h->dh, h->Bmax, h->S_max, h->kcache, h->vtcache, st));
   h->prefix_batch = batch;
   h->stats.prefix_sets++;
   return AE_OK;

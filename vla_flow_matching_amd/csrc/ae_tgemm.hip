@@ -484,14 +484,14 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
         } else {
           const int key = nvv[i] + t;
           const size_t base = static_cast<size_t>(req) * p.Hkv + head;
+          using LY = KvLayout<bf16_t>;
+          bf16_t* dst = (seg == 1 ? kc : vt) + base * p.S_max * p.dh;
           if (seg == 1) {
-            bf16_t* dst = kc + (base * p.S_max + key) * p.dh;
-            dst[j] = f2bf(a);
-            dst[half + j] = f2bf(b);
+            dst[LY::k_off(key, j, p.dh)] = f2bf(a);
+            dst[LY::k_off(key, half + j, p.dh)] = f2bf(b);
           } else {
-            bf16_t* dst = vt + base * p.dh * p.S_max;
-            dst[static_cast<size_t>(j) * p.S_max + key] = f2bf(a);
-            dst[static_cast<size_t>(half + j) * p.S_max + key] = f2bf(b);
+            dst[LY::v_off(key, j, p.dh)] = f2bf(a);
+            dst[LY::v_off(key, half + j, p.dh)] = f2bf(b);
           }
         }
       }
