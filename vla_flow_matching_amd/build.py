@@ -4,7 +4,7 @@
 
 Each .hip source is compiled with hipcc for gfx950 only and linked into
 ``vla_flow_matching_amd/libae.so``.  Packed-fp32 VALU instructions are turned
-off for all device code.
+off for all device code; ``EXTRA`` adds per-source code-generation options.
 """
 
 from __future__ import annotations
@@ -31,6 +31,11 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
+# Per-source additions.  The attention kernel keeps its MFMA accumulators in
+# ordinary VGPRs: it rescales them with VALU multiplies, and accumulators
+# held in AGPRs would be copied across every key block.
+EXTRA = {"ae_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -41,7 +46,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

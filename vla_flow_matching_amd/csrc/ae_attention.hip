@@ -46,14 +46,13 @@ __device__ __forceinline__ void store4<float>(float* dst, const float* v) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// One 16-byte-per-lane copy from global memory straight into LDS (lane l's
-// bytes land at lds_dst + 16 l).  Issued as inline assembly so that the
-// compiler neither moves it nor adds waits for it; the caller waits with
+// One fragment copied from global memory straight into LDS: lane l's 16
+// bytes at g + lane16 (= 16 l) land at LDS byte address lds + 16 l; g and
+// lds are wave-uniform (scalar registers).  Issued as inline assembly so that
+// the compiler neither moves it nor adds waits for it; the caller waits with
 // wait_vm before a barrier.
-__device__ __forceinline__ void dma16(const void* g, const uint4* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void_t*)(lds_dst))));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void dma_frag(const void* g, uint32_t lds, uint32_t lane16) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(lane16), "s"(g), "s"(lds) : "memory", "m0");
 }
 
 // Wait until at most N of this wave's vector-memory operations are in flight.
@@ -78,15 +77,17 @@ struct KvBlock {
   static constexpr int NK = NBLK * NF, FPB = NK + ND, PER_WAVE = FPB / 4;
   static_assert(FPB % 4 == 0 && NK % 4 == 0, "fragments split evenly over 4 waves");
 
-  // Kb / Vb: the (request, head)'s K and V caches; kb0: the block's first key
-  static __device__ __forceinline__ void issue(const T* Kb, const T* Vb, int kb0, uint4* dst) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  // Kb / Vb: the (request, head)'s K and V caches; kb0: the block's first
+  // key; lds: the LDS byte address of the block's buffer; wave: this wave's
+  // index (scalar); lane16 = 16 * lane
+  static __device__ __forceinline__ void issue(const T* Kb, const T* Vb, int kb0, uint32_t lds, int wave,
+                                               uint32_t lane16) {
     const size_t blk0 = static_cast<size_t>(kb0 / KSTEP) * LY::block_elems(DH);
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int f = 4 * j + wave;
-      const T* src = j < NK / 4 ? Kb + blk0 + (f * kWave + lane) * E : Vb + blk0 + ((f - NK) * kWave + lane) * E;
-      dma16(src, dst + f * kWave);
+      const T* src = j < NK / 4 ? Kb + blk0 + f * kWave * E : Vb + blk0 + (f - NK) * kWave * E;
+      dma_frag(src, lds + static_cast<uint32_t>(f * kWave * 16), lane16);
     }
   }
 };
@@ -223,15 +224,20 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
 
   // Key blocks stream through a ring of kStages LDS buffers, copied two
   // blocks ahead of the one being multiplied.
-  if (n_blk > 0) KV::issue(Kb, Vb, k_begin, s_kv[0]);
-  if (n_blk > 1) KV::issue(Kb, Vb, k_begin + KSTEP, s_kv[1]);
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void_t*)(&s_kv[0][0])));
+  constexpr uint32_t kStageBytes = FPB * kWave * 16;
+  const uint32_t lane16 = 16u * lane;
+  if (n_blk > 0) KV::issue(Kb, Vb, k_begin, lds0, swave, lane16);
+  if (n_blk > 1) KV::issue(Kb, Vb, k_begin + KSTEP, lds0 + kStageBytes, swave, lane16);
   for (int bi = 0; bi < n_blk; ++bi) {
     if (bi + 1 < n_blk)
       wait_vm<KV::PER_WAVE>();  // block bi landed; block bi + 1 may still be in flight
     else
       wait_vm<0>();
     __syncthreads();  // every wave's copies of block bi are visible; block bi - 1's buffer is free
-    if (bi + 2 < n_blk) KV::issue(Kb, Vb, k_begin + (bi + 2) * KSTEP, s_kv[(bi + 2) % kStages]);
+    if (bi + 2 < n_blk)
+      KV::issue(Kb, Vb, k_begin + (bi + 2) * KSTEP, lds0 + ((bi + 2) % kStages) * kStageBytes, swave, lane16);
     attn_block<T, DH, kQB>(s_kv[bi % kStages] + lane, k_begin + bi * KSTEP, k_end, p.scale_log2, qf, acc, m_run,
                            l_run);
   }
