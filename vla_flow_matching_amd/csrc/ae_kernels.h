@@ -141,6 +141,7 @@ struct TGemmArgs {
   int M, N, K;
   const uint4* W;  // packed weights (bf16 fragments or fp8 chunks)
   int n_tiles, m_tiles, ksplit;
+  int bm;  // tile rows (32)
   float* partial;
   int* counters;
   // fp8: per-row activation scale and per-tensor weight scales
@@ -179,6 +180,7 @@ struct TGemmArgs {
 
 struct TGemmPlan {
   int m_tiles, n_tiles, ksplit, blocks;
+  int bm;  // tile rows
 };
 TGemmPlan plan_tgemm(int M, int N, int K, int kc, int target_blocks);
 int tgemm_kc(int op);

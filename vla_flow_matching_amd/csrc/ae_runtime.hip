@@ -271,7 +271,7 @@ TGemmArgs base_tgemm(const ae_handle* h, const TGemmPlan& g, int M, int N, int K
   TGemmArgs a;
   std::memset(&a, 0, sizeof(a));
   a.M = M; a.N = N; a.K = K;
-  a.n_tiles = g.n_tiles; a.m_tiles = g.m_tiles; a.ksplit = g.ksplit;
+  a.n_tiles = g.n_tiles; a.m_tiles = g.m_tiles; a.ksplit = g.ksplit; a.bm = g.bm;
   a.partial = h->gpart; a.counters = h->gcnt;
   a.sx_row = h->sxrow;
   return a;

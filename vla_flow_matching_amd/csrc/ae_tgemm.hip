@@ -1,5 +1,7 @@
 // Batched projection GEMMs (many action rows: B * T > 64): Y = A . W on the
-// MFMA units with 128 x 128 output tiles staged through LDS, for bf16
+// MFMA units with BM x 128 output tiles (BM = 32 rows: many small tiles in
+// flight, K split only where they cannot fill the GPU) staged through LDS,
+// for bf16
 // operands and for the fp8 e4m3 variant of the QKV / gate-up / down
 // projections (MolmoBot PR, Part 3: per-tensor dynamic fp8, amax -> cast ->
 // scaled matmul; LoongForge blog, section 7: inputs and weights quantised,
@@ -29,11 +31,9 @@ namespace ae {
 
 namespace {
 
-constexpr int kTT = 256;     // threads per GEMM workgroup (2 x 2 waves)
-constexpr int kBM = 128;     // tile rows
+constexpr int kTT = 256;     // threads per GEMM workgroup (4 waves, 32 columns each)
 constexpr int kBN = 128;     // tile columns
 constexpr int kXcd = 8;
-constexpr int kChunkU4 = 1024;  // uint4 per staged operand chunk (16 KiB)
 constexpr int kMaxSplit = 8;    // K splits of one tile at most
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -239,32 +239,33 @@ __device__ __forceinline__ int swz(int l, int s) {
   return 16 * q + ((l & 15) ^ ((2 * q + 8 * s) & 15));
 }
 
-// One chunk times the wave's 64 x 64 block of the tile: A fragments from the
-// LDS stage, B fragments (four 16-column groups x two slots) from registers.
-template <int OP>
-__device__ __forceinline__ void tg_compute(const uint4* A, const u32x4 (&B)[4][2], int wm, int lane,
-                                           f32x4 (&acc)[4][4]) {
+// One chunk times the wave's BM x 32 block of the tile (RT = BM / 16 row
+// tiles x two 16-column groups): A fragments from the LDS stage, B fragments
+// (two 16-column groups x two slots) from registers.
+template <int OP, int RT>
+__device__ __forceinline__ void tg_compute(const uint4* A, const u32x4 (&B)[2][2], int lane,
+                                           f32x4 (&acc)[RT][2]) {
   if (OP == OP_BF16) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      uint4 a[4];
+      uint4 a[RT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = A[((4 * wm + i) * 2 + s) * kWave + swz(lane, s)];
+      for (int i = 0; i < RT; ++i) a[i] = A[(i * 2 + s) * kWave + swz(lane, s)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(a[i], __builtin_bit_cast(uint4, B[j][s]), acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(a[i], __builtin_bit_cast(uint4, B[j][s]), acc[i][j]);
     }
   } else {
-    uint4 a[4][2];
+    uint4 a[RT][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) a[i][s] = A[((4 * wm + i) * 2 + s) * kWave + swz(lane, s)];
+      for (int s = 0; s < 2; ++s) a[i][s] = A[(i * 2 + s) * kWave + swz(lane, s)];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = mfma_fp8(a[i][0], a[i][1], __builtin_bit_cast(uint4, B[j][0]),
                              __builtin_bit_cast(uint4, B[j][1]), acc[i][j]);
   }
@@ -499,38 +500,47 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
   }
 }
 
-template <int OP, int EPI>
+// threads per row of the row-norm sums (RowNorm): rows <= kTT / TPR
+template <int BM>
+constexpr int norm_tpr() {
+  return BM >= 128 ? 2 : 4;
+}
+
+template <int OP, int EPI, int BM>
 __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   using O = TOp<OP>;
   constexpr int KC = O::KC;
+  constexpr int RT = BM / 16;              // 16-row tiles per wave
+  constexpr int NA = BM / 32;              // A staging pieces per thread per chunk
+  constexpr int kStageU4 = BM * 8;         // uint4 per staged A chunk
+  constexpr int kTileU4 = BM * (kBN + 1) / 4 + BM / 4;
+  constexpr int kBufU4 = kTileU4 > 2 * kStageU4 ? kTileU4 : 2 * kStageU4;
   // two stages of A chunks; the finished tile reuses the space
   // (+ 1 / rms of the tile's rows past the finished tile)
-  __shared__ __attribute__((aligned(16))) uint4 s_buf[kBM * (kBN + 1) / 4 + kBM / 4];
-  static_assert(sizeof(s_buf) >= 2 * kChunkU4 * sizeof(uint4), "stages fit");
+  __shared__ __attribute__((aligned(16))) uint4 s_buf[kBufU4];
   auto s_y = reinterpret_cast<float (*)[kBN + 1]>(s_buf);
 
   int nt, mt, ks;
   if (!tile_of(blockIdx.x, p.n_tiles, p.m_tiles, p.ksplit, nt, mt, ks)) return;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = mt * kBM;
-  const int rows = min(kBM, p.M - m0);
+  const int m0 = mt * BM;
+  const int rows = min(BM, p.M - m0);
   const int n_chunks = p.K / KC;
   const int c0 = static_cast<int>((static_cast<long long>(ks) * n_chunks) / p.ksplit);
   const int c1 = static_cast<int>((static_cast<long long>(ks + 1) * n_chunks) / p.ksplit);
   // the rows' 1 / rms for a norm after the product (into LDS past the
   // finished tile): loads issued after the first chunk's, summed after the
   // K loop
-  float* s_r = reinterpret_cast<float*>(s_buf) + kBM * (kBN + 1);
+  float* s_r = reinterpret_cast<float*>(s_buf) + BM * (kBN + 1);
   const bool norm_here = OP == OP_BF16 && EPI != EPI_RESID && p.bias != nullptr && p.ksplit == 1;
-  RowNorm<kTT / kBM> rn;
+  RowNorm<norm_tpr<BM>()> rn;
 
   // A staging map: item i = tid + 256 j: row i/8, 16-byte column i%8.
   const uint8_t* Ab = static_cast<const uint8_t*>(p.A);
-  uint32_t a_off[4];
-  int a_lds[4];
+  uint32_t a_off[NA];
+  int a_lds[NA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NA; ++j) {
     const int i = tid + kTT * j;
     const int row = i >> 3, kc = i & 7;
     const int grow = min(m0 + row, p.M - 1);
@@ -539,45 +549,43 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
     const int slot = O::slot_lane(kc, row & 15, ln);
     a_lds[j] = ((row >> 4) * 2 + slot) * kWave + swz(ln, slot);
   }
-  // B fragments go straight to registers: wave (wm, wn) reads the 2 KiB
-  // chunk of each of its four 16-column groups (slot s, lane) itself, so
-  // only A passes through LDS.
+  // B fragments go straight to registers: wave w reads the 2 KiB chunk of
+  // each of its two 16-column groups (32 w .. 32 w + 31 of the tile) itself,
+  // so every weight byte is read once per tile and only A passes through LDS.
   const u32x4* Wv = reinterpret_cast<const u32x4*>(p.W) +
-                    (static_cast<size_t>(nt) * 8 + 4 * wn) * n_chunks * 128 + lane;
+                    (static_cast<size_t>(nt) * 8 + 2 * wave) * n_chunks * 128 + lane;
   u32x4* sv = reinterpret_cast<u32x4*>(s_buf);
 
   struct AStage {
-    u32x4 a0, a1, a2, a3;
+    u32x4 a[NA];
   };
   struct BStage {
-    u32x4 b[4][2];
+    u32x4 b[2][2];
   };
 #define TG_LOAD_A(R, c)                                                            \
   do {                                                                             \
     const uint32_t co_ = static_cast<uint32_t>(c) * 128u;                          \
-    R.a0 = *reinterpret_cast<const u32x4*>(Ab + a_off[0] + co_);                   \
-    R.a1 = *reinterpret_cast<const u32x4*>(Ab + a_off[1] + co_);                   \
-    R.a2 = *reinterpret_cast<const u32x4*>(Ab + a_off[2] + co_);                   \
-    R.a3 = *reinterpret_cast<const u32x4*>(Ab + a_off[3] + co_);                   \
+    _Pragma("unroll") for (int j_ = 0; j_ < NA; ++j_)                              \
+      R.a[j_] = *reinterpret_cast<const u32x4*>(Ab + a_off[j_] + co_);             \
   } while (0)
 #define TG_LOAD_B(R, c)                                                            \
   do {                                                                             \
-    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                               \
+    _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                               \
       _Pragma("unroll") for (int s_ = 0; s_ < 2; ++s_)                             \
         R.b[j_][s_] = Wv[(static_cast<size_t>(j_) * n_chunks + (c)) * 128 + s_ * 64]; \
   } while (0)
 #define TG_STORE_A(R, st)                                                          \
   do {                                                                             \
-    u32x4* sa_ = sv + (st) * kChunkU4;                                             \
-    sa_[a_lds[0]] = R.a0; sa_[a_lds[1]] = R.a1; sa_[a_lds[2]] = R.a2; sa_[a_lds[3]] = R.a3; \
+    u32x4* sa_ = sv + (st) * kStageU4;                                             \
+    _Pragma("unroll") for (int j_ = 0; j_ < NA; ++j_) sa_[a_lds[j_]] = R.a[j_];    \
   } while (0)
-#define TG_COMPUTE(st, RB) tg_compute<OP>(s_buf + (st) * kChunkU4, RB, wm, lane, acc)
+#define TG_COMPUTE(st, RB) tg_compute<OP, RT>(s_buf + (st) * kStageU4, RB, lane, acc)
 
-  f32x4 acc[4][4];
+  f32x4 acc[RT][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Iteration c: LDS stage c%2 holds A(c), registers hold B(c); A(c+1) and
   // B(c+1) are in flight and A(c+2) is issued.  Every split holds at least
@@ -620,18 +628,18 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
 
   // accumulators -> LDS tile (row-major)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        s_y[64 * wm + 16 * i + 4 * (lane / 16) + e][64 * wn + 16 * j + lane % 16] = acc[i][j][e];
+        s_y[16 * i + 4 * (lane / 16) + e][32 * wave + 16 * j + lane % 16] = acc[i][j][e];
   __syncthreads();
 
   if (p.ksplit > 1) {
     // this split's rows of the tile -> partial scratch; the reduce kernel
     // that follows sums the splits in order and applies the epilogue
-    float* part = p.partial + (static_cast<size_t>(nt * p.m_tiles + mt) * p.ksplit + ks) * (kBM * kBN);
+    float* part = p.partial + (static_cast<size_t>(nt * p.m_tiles + mt) * p.ksplit + ks) * (BM * kBN);
     const int n4 = rows * (kBN / 4);
     for (int i = tid; i < n4; i += kTT) {
       const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
@@ -640,25 +648,25 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
     }
     return;
   }
-  tg_epilogue<OP, EPI, kTT / kBM, true>(p, nt, m0, rows, s_y, s_r);
+  tg_epilogue<OP, EPI, norm_tpr<BM>(), true>(p, nt, m0, rows, s_y, s_r);
 }
 
 // Sum of a tile's K-split partials for kRedRows rows (in split order), then
 // the epilogue of those rows.  One workgroup per (tile, row slice).
 constexpr int kRedRows = 16;
 
-template <int OP, int EPI>
+template <int OP, int EPI, int BM>
 __global__ __launch_bounds__(kTT) void tgemm_reduce_kernel(TGemmArgs p) {
   __shared__ float s_y[kRedRows][kBN + 1];
   __shared__ float s_r[kRedRows];
-  const int slices = kBM / kRedRows;
+  const int slices = BM / kRedRows;
   const int tile = blockIdx.x / slices, sl = blockIdx.x % slices;
   const int nt = tile / p.m_tiles, mt = tile % p.m_tiles;
-  const int m0 = mt * kBM + sl * kRedRows;
+  const int m0 = mt * BM + sl * kRedRows;
   const int rows = min(kRedRows, p.M - m0);
   if (rows <= 0) return;
   const int tid = threadIdx.x;
-  const float* part = p.partial + static_cast<size_t>(tile) * p.ksplit * (kBM * kBN) + sl * kRedRows * kBN;
+  const float* part = p.partial + static_cast<size_t>(tile) * p.ksplit * (BM * kBN) + sl * kRedRows * kBN;
   // kRedRows x kBN floats = 512 float4, two per thread, every split in flight
   float4 v[2][kMaxSplit];
 #pragma unroll
@@ -667,7 +675,7 @@ __global__ __launch_bounds__(kTT) void tgemm_reduce_kernel(TGemmArgs p) {
     const int r = min(i / (kBN / 4), rows - 1), c4 = 4 * (i % (kBN / 4));
 #pragma unroll
     for (int q = 0; q < kMaxSplit; ++q)
-      v[u][q] = *reinterpret_cast<const float4*>(part + static_cast<size_t>(min(q, p.ksplit - 1)) * (kBM * kBN) +
+      v[u][q] = *reinterpret_cast<const float4*>(part + static_cast<size_t>(min(q, p.ksplit - 1)) * (BM * kBN) +
                                                  r * kBN + c4);
   }
 #pragma unroll
@@ -779,13 +787,19 @@ hipError_t launch_quant(const float* src, const float* h, const float* r, const 
   return hipGetLastError();
 }
 
+// The row tile: 32 rows.  At these row counts (at most a few hundred) the
+// kernel is bound by load latency rather than operand reuse, so more and
+// smaller tiles in flight win (800 x 1024 x 2048: 10 us with 32-row tiles,
+// 16 us with 128-row tiles split over K).  K is split only when the tiles
+// cover less than three quarters of the target.
 TGemmPlan plan_tgemm(int M, int N, int K, int kc, int target_blocks) {
   TGemmPlan g;
-  g.m_tiles = (M + kBM - 1) / kBM;
   g.n_tiles = N / kBN;
+  g.bm = 32;
+  g.m_tiles = (M + g.bm - 1) / g.bm;
   const int chunks = K / kc;
   const int tiles = g.m_tiles * g.n_tiles;
-  int s = (target_blocks + tiles - 1) / tiles;
+  int s = 4 * tiles >= 3 * target_blocks ? 1 : (target_blocks + tiles - 1) / tiles;
   int max_s = chunks / 2 > 0 ? chunks / 2 : 1;  // at least two chunks per split
   if (max_s > kMaxSplit) max_s = kMaxSplit;
   if (s > max_s) s = max_s;
@@ -799,26 +813,28 @@ TGemmPlan plan_tgemm(int M, int N, int K, int kc, int target_blocks) {
 int tgemm_kc(int op) { return op == OP_FP8 ? TOp<OP_FP8>::KC : TOp<OP_BF16>::KC; }
 
 size_t tgemm_partial_floats(const TGemmPlan& g) {
-  return g.ksplit > 1 ? static_cast<size_t>(g.m_tiles) * g.n_tiles * g.ksplit * kBM * kBN : 0;
+  return g.ksplit > 1 ? static_cast<size_t>(g.m_tiles) * g.n_tiles * g.ksplit * g.bm * kBN : 0;
 }
 
 hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a, int blocks, hipStream_t s) {
   if (a.K % tgemm_kc(op) || a.N % kBN) return hipErrorInvalidValue;
   dim3 grid(blocks), block(kTT);
-#define AE_TG(OPV, EPV)                                                                     \
-  if (op == OPV && epi == EPV) {                                                            \
-    hipLaunchKernelGGL((tgemm_kernel<OPV, EPV>), grid, block, 0, s, a);                     \
+#define AE_TG(OPV, EPV, BMV)                                                                \
+  if (op == OPV && epi == EPV && a.bm == BMV) {                                             \
+    hipLaunchKernelGGL((tgemm_kernel<OPV, EPV, BMV>), grid, block, 0, s, a);                \
     if (a.ksplit > 1)                                                                       \
-      hipLaunchKernelGGL((tgemm_reduce_kernel<OPV, EPV>),                                   \
-                         dim3(a.n_tiles * a.m_tiles * (kBM / kRedRows)), block, 0, s, a);   \
+      hipLaunchKernelGGL((tgemm_reduce_kernel<OPV, EPV, BMV>),                              \
+                         dim3(a.n_tiles * a.m_tiles * (BMV / kRedRows)), block, 0, s, a);   \
     return hipGetLastError();                                                               \
   }
-  AE_TG(OP_BF16, EPI_QKV)
-  AE_TG(OP_BF16, EPI_GELU)
-  AE_TG(OP_BF16, EPI_RESID)
-  AE_TG(OP_FP8, EPI_QKV)
-  AE_TG(OP_FP8, EPI_GELU)
-  AE_TG(OP_FP8, EPI_RESID)
+#define AE_TG_BM(OPV, EPV) AE_TG(OPV, EPV, 32)
+  AE_TG_BM(OP_BF16, EPI_QKV)
+  AE_TG_BM(OP_BF16, EPI_GELU)
+  AE_TG_BM(OP_BF16, EPI_RESID)
+  AE_TG_BM(OP_FP8, EPI_QKV)
+  AE_TG_BM(OP_FP8, EPI_GELU)
+  AE_TG_BM(OP_FP8, EPI_RESID)
+#undef AE_TG_BM
 #undef AE_TG
   return hipErrorInvalidValue;
 }
