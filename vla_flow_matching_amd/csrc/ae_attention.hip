@@ -24,11 +24,12 @@ namespace ae {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves: 4 row groups x 2 key halves
+constexpr int kRowWaves = 4;
 constexpr int kXcds = 8;
 constexpr int kQB = 1;  // 16-row query blocks per wave
 constexpr int kMergeBatch = 2;  // key splits merged per round of loads
-constexpr int kStages = 3;      // LDS key-block buffers
+constexpr int kSlots = 2;       // LDS slots of one step (two key blocks) each
 
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, const float* v);
@@ -61,33 +62,35 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// One key block (KSTEP keys) in LDS, in the cache's fragment order (the
+// Key blocks (KSTEP keys) in LDS, in the cache's fragment order (the
 // key-block layout): NBLK * NF K fragments (S^T = K Q^T operands), then ND
 // V^T fragments (O^T = V^T P^T operands), 1 KiB each, each a contiguous run
-// of the cache; each wave copies a quarter.  Keys of the last block past
-// k_end are copied as they are: their scores are masked, and the cache holds
-// finite values there (zeros or another split's keys), so their zero P
-// contributes nothing.
+// of the cache.  A step is two consecutive blocks; the eight waves copy an
+// eighth of its fragments each.  Keys of the last block past k_end are
+// copied as they are: their scores are masked, and the cache holds finite
+// values there (zeros or another split's keys), so their zero P contributes
+// nothing.
 template <typename T, int DH>
 struct KvBlock {
   using MM = Mma<T>;
   using LY = KvLayout<T>;
   static constexpr int E = MM::E, KSTEP = MM::KSTEP;
   static constexpr int NF = DH / KSTEP, ND = DH / 16, NBLK = KSTEP / 16;
-  static constexpr int NK = NBLK * NF, FPB = NK + ND, PER_WAVE = FPB / 4;
-  static_assert(FPB % 4 == 0 && NK % 4 == 0, "fragments split evenly over 4 waves");
+  static constexpr int NK = NBLK * NF, FPB = NK + ND;
+  static_assert(FPB % 8 == 0 && NK % 4 == 0, "a step's fragments split evenly over 8 waves");
 
-  // Kb / Vb: the (request, head)'s K and V caches; kb0: the block's first
-  // key; lds: the LDS byte address of the block's buffer; wave: this wave's
-  // index (scalar); lane16 = 16 * lane
-  static __device__ __forceinline__ void issue(const T* Kb, const T* Vb, int kb0, uint32_t lds, int wave,
-                                               uint32_t lane16) {
-    const size_t blk0 = static_cast<size_t>(kb0 / KSTEP) * LY::block_elems(DH);
+  // Kb / Vb: the (request, head)'s K and V caches; kb0: the step's first
+  // key; nb: its blocks (1 or 2); lds: the LDS byte address of its slot;
+  // wave: this wave's index (scalar); lane16 = 16 * lane
+  static __device__ __forceinline__ void issue_step(const T* Kb, const T* Vb, int kb0, int nb, uint32_t lds,
+                                                    int wave, uint32_t lane16) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int f = 4 * j + wave;
-      const T* src = j < NK / 4 ? Kb + blk0 + f * kWave * E : Vb + blk0 + (f - NK) * kWave * E;
-      dma_frag(src, lds + static_cast<uint32_t>(f * kWave * 16), lane16);
+    for (int j = 0; j < 2 * FPB / 8; ++j) {
+      const int x = 8 * j + wave, hb = x / FPB, f = x % FPB;
+      if (hb >= nb) break;  // (x grows with j: the rest belongs to the absent block too)
+      const size_t blk0 = static_cast<size_t>(kb0 / KSTEP + hb) * LY::block_elems(DH);
+      const T* src = f < NK ? Kb + blk0 + f * kWave * E : Vb + blk0 + (f - NK) * kWave * E;
+      dma_frag(src, lds + static_cast<uint32_t>(x * kWave * 16), lane16);
     }
   }
 };
@@ -154,10 +157,12 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
   }
 }
 
-// One workgroup = 4 waves x kQB query blocks of 16 rows of one (request, KV
-// group), over one split of the keys.  Key blocks are copied straight into
-// LDS buffers shared by the waves, two blocks ahead of the one being
-// multiplied, so every K/V byte crosses from L2 once per workgroup.
+// One workgroup = 4 row groups x kQB query blocks of 16 rows of one (request,
+// KV group), over one split of the keys, with two waves per row group that
+// take alternate key blocks (two independent waves per SIMD hide each
+// other's softmax and LDS latency).  Key blocks are copied straight into LDS
+// slots shared by the waves, one step of two blocks ahead, so every K/V byte
+// crosses from L2 once per workgroup.
 template <typename T, int DH>
 __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   using KV = KvBlock<T, DH>;
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   constexpr int E = KV::E, KSTEP = KV::KSTEP, NF = KV::NF, ND = KV::ND, NBLK = KV::NBLK;
   constexpr int NK = KV::NK, FPB = KV::FPB;
   constexpr int PW = ND * kWave * 4 + 32;  // floats of one query block's partial
-  __shared__ uint4 s_kv[kStages][FPB * kWave];
+  __shared__ uint4 s_kv[kSlots][2 * FPB * kWave];
   __shared__ int s_flag;
 
   const int G = p.Hq / p.Hkv;
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   const int g = bg % p.Hkv;
   const int b = bg / p.Hkv;
 
-  const int wave = threadIdx.x / kWave;
+  const int wave = threadIdx.x / kWave, rg = wave % kRowWaves, kh = wave / kRowWaves;
   const int lane = threadIdx.x % kWave;
   const int grp = lane / 16;
   const int len = p.n_valid[b] + p.T;
@@ -195,13 +200,14 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   const T* Kb = static_cast<const T*>(p.kcache) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
   const T* Vb = static_cast<const T*>(p.vtcache) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
 
-  // query rows of this wave: blocks (qg * 4 + wave) * kQB + c, 16 rows each
+  // query rows of this wave's row group: blocks (qg * 4 + rg) * kQB + c, 16
+  // rows each (both key halves hold the same rows)
   uint4 qf[kQB][NF];
   int hh[kQB], tt[kQB];
   bool qvalid[kQB];
 #pragma unroll
   for (int c = 0; c < kQB; ++c) {
-    const int myq = ((qg * 4 + wave) * kQB + c) * 16 + lane % 16;
+    const int myq = ((qg * 4 + rg) * kQB + c) * 16 + lane % 16;
     qvalid[c] = myq < R;
     const int q = min(myq, R - 1);  // rows past R read a valid row, never stored
     hh[c] = q / p.T;
@@ -222,26 +228,61 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
     l_run[c] = 0.0f;
   }
 
-  // Key blocks stream through a ring of kStages LDS buffers, copied two
-  // blocks ahead of the one being multiplied.
+  // Steps of two key blocks: the waves of key half kh take block 2 t + kh of
+  // step t, so each SIMD runs two independent waves.  Steps stream through
+  // kSlots LDS slots, copied one step ahead of the one being multiplied.
   const int swave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void_t*)(&s_kv[0][0])));
-  constexpr uint32_t kStageBytes = FPB * kWave * 16;
+  constexpr uint32_t kSlotBytes = 2 * FPB * kWave * 16;
   const uint32_t lane16 = 16u * lane;
-  if (n_blk > 0) KV::issue(Kb, Vb, k_begin, lds0, swave, lane16);
-  if (n_blk > 1) KV::issue(Kb, Vb, k_begin + KSTEP, lds0 + kStageBytes, swave, lane16);
-  for (int bi = 0; bi < n_blk; ++bi) {
-    if (bi + 1 < n_blk)
-      wait_vm<KV::PER_WAVE>();  // block bi landed; block bi + 1 may still be in flight
-    else
-      wait_vm<0>();
-    __syncthreads();  // every wave's copies of block bi are visible; block bi - 1's buffer is free
-    if (bi + 2 < n_blk)
-      KV::issue(Kb, Vb, k_begin + (bi + 2) * KSTEP, lds0 + ((bi + 2) % kStages) * kStageBytes, swave, lane16);
-    attn_block<T, DH, kQB>(s_kv[bi % kStages] + lane, k_begin + bi * KSTEP, k_end, p.scale_log2, qf, acc, m_run,
-                           l_run);
+  const int n_steps = (n_blk + 1) / 2;
+  if (n_steps > 0) KV::issue_step(Kb, Vb, k_begin, min(2, n_blk), lds0, swave, lane16);
+  for (int t = 0; t < n_steps; ++t) {
+    wait_vm<0>();     // this wave's copies of step t landed
+    __syncthreads();  // every wave's have; step t - 1's slot is free
+    if (t + 1 < n_steps)
+      KV::issue_step(Kb, Vb, k_begin + 2 * (t + 1) * KSTEP, min(2, n_blk - 2 * (t + 1)),
+                     lds0 + ((t + 1) % kSlots) * kSlotBytes, swave, lane16);
+    const int bi = 2 * t + kh;
+    if (bi < n_blk)
+      attn_block<T, DH, kQB>(s_kv[t % kSlots] + kh * FPB * kWave + lane, k_begin + bi * KSTEP, k_end,
+                             p.scale_log2, qf, acc, m_run, l_run);
   }
   // acc[c][d][i] = O^T[dim 16 d + 4 grp + i][query lane % 16 of block c] (unnormalised)
+
+  // Key half 1 hands its (O^T, m, l) to key half 0 of the same rows through
+  // LDS (the slots are free once every wave is past the loop); half 0
+  // combines them, and from here on only half 0 carries the rows.
+  __syncthreads();
+  {
+    uint4* xo = &s_kv[0][0] + rg * (kQB * ND + 1) * kWave;
+    if (kh == 1) {
+#pragma unroll
+      for (int c = 0; c < kQB; ++c)
+#pragma unroll
+        for (int d = 0; d < ND; ++d) xo[(c * ND + d) * kWave + lane] = __builtin_bit_cast(uint4, acc[c][d]);
+      xo[kQB * ND * kWave + lane] =
+          make_uint4(__float_as_uint(m_run[0]), __float_as_uint(l_run[0]),
+                     __float_as_uint(kQB > 1 ? m_run[kQB - 1] : 0.0f), __float_as_uint(kQB > 1 ? l_run[kQB - 1] : 0.0f));
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const uint4 ml = xo[kQB * ND * kWave + lane];
+#pragma unroll
+      for (int c = 0; c < kQB; ++c) {
+        const float m1 = __uint_as_float(c == 0 ? ml.x : ml.z), l1 = __uint_as_float(c == 0 ? ml.y : ml.w);
+        const float m_new = fmaxf(m_run[c], m1);
+        if (m_new != -INFINITY) {  // (both halves empty: nothing to combine)
+          const float a0 = exp2_hw(m_run[c] - m_new), a1 = exp2_hw(m1 - m_new);
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+            acc[c][d] = acc[c][d] * a0 + a1 * __builtin_bit_cast(f32x4, xo[(c * ND + d) * kWave + lane]);
+          l_run[c] = l_run[c] * a0 + l1 * a1;
+          m_run[c] = m_new;
+        }
+      }
+    }
+  }
 
   if (p.nsplit > 1) {
     // publish every query block's (O^T, m, l), then the last split of the
@@ -251,7 +292,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
     const Coh cp(part);
 #pragma unroll
     for (int c = 0; c < kQB; ++c) {
-      const uint32_t wb = 4u * static_cast<uint32_t>(s * per_split + (wave * kQB + c) * PW);
+      if (kh != 0) break;
+      const uint32_t wb = 4u * static_cast<uint32_t>(s * per_split + (rg * kQB + c) * PW);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
         cp.st16(wb + 16u * (d * kWave + lane),
@@ -265,6 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
     if (!arrive_last(p.counters + item, p.nsplit, &s_flag)) return;
 #pragma unroll
     for (int c = 0; c < kQB; ++c) {
+      if (kh != 0) break;
       float mx = -INFINITY, lsum = 0.0f;
       f32x4 o[ND];
 #pragma unroll
@@ -276,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
           const int s2 = min(s0 + j, p.nsplit - 1);
-          const uint32_t wb = 4u * static_cast<uint32_t>(s2 * per_split + (wave * kQB + c) * PW);
+          const uint32_t wb = 4u * static_cast<uint32_t>(s2 * per_split + (rg * kQB + c) * PW);
           ms[j] = cp.ldf(wb + 4u * (ND * kWave * 4 + lane % 16));
           ls[j] = cp.ldf(wb + 4u * (ND * kWave * 4 + 16 + lane % 16));
 #pragma unroll
@@ -303,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
 
 #pragma unroll
   for (int c = 0; c < kQB; ++c) {
-    if (!qvalid[c]) continue;
+    if (kh != 0 || !qvalid[c]) continue;
     const float inv = 1.0f / l_run[c];
     T* orow = static_cast<T*>(p.o) + static_cast<size_t>(b * p.T + tt[c]) * p.ldo + (g * G + hh[c]) * DH;
 #pragma unroll
