@@ -81,50 +81,74 @@ __device__ __forceinline__ float ada(float h, float r, float sc, float sh) {
 }
 
 // ---------------------------------------------------------------------------
-// Row norm: one wave per row, 4 rows per workgroup.
-// mode 0: u -> bf16 [M][D].  mode 1: r[row] and rowmax[row] = max_k |u|.
+// Sum / max over a 256-thread workgroup (lane swaps within each wave, then
+// the four wave results through LDS); every thread gets the result.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_sum(float v, float* s_red) {
+  v = wave_sum(v);
+  __syncthreads();  // (s_red may still be read by a previous call)
+  if (threadIdx.x % kWave == 0) s_red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  return (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+}
+
+__device__ __forceinline__ float block_max(float v, float* s_red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) s_red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+}
+
+// ---------------------------------------------------------------------------
+// Row norm: one 256-thread workgroup per row (all of a row's loads in
+// flight at once).  mode 0: u -> bf16 [M][D].  mode 1: r[row] and
+// rowmax[row] = max_k |u|.  D <= 4 * 256 * kNormPer.
+// ---------------------------------------------------------------------------
+constexpr int kNormPer = 4;  // float4 per thread held across the two passes (D <= 4096)
+
 __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ h, int M, int D,
                                                       const float* __restrict__ scale,
                                                       const float* __restrict__ shift, float eps,
                                                       int mode, bf16_t* __restrict__ u,
                                                       float* __restrict__ r_out,
                                                       float* __restrict__ rowmax) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= M) return;
+  __shared__ float s_red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
   const float4* hr = reinterpret_cast<const float4*>(h + static_cast<size_t>(row) * D);
   const int n4 = D / 4;
+  float4 v[kNormPer];
   float ss = 0.0f;
-  for (int i = lane; i < n4; i += kWave) {
-    const float4 v = hr[i];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int i = tid + 256 * j;
+    v[j] = i < n4 ? hr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
   }
-  ss = wave_sum(ss);
+  ss = block_sum(ss, s_red);
   const float r = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
   const float4* sc4 = reinterpret_cast<const float4*>(scale);
   const float4* sh4 = reinterpret_cast<const float4*>(shift);
-  if (mode == 0) {
-    uint2* ur = reinterpret_cast<uint2*>(u + static_cast<size_t>(row) * D);
-    for (int i = lane; i < n4; i += kWave) {
-      const float4 v = hr[i], s = sc4[i], b = sh4[i];
-      const float o0 = ada(v.x, r, s.x, b.x), o1 = ada(v.y, r, s.y, b.y);
-      const float o2 = ada(v.z, r, s.z, b.z), o3 = ada(v.w, r, s.w, b.w);
-      ur[i] = make_uint2(static_cast<uint32_t>(f2bf(o0)) | (static_cast<uint32_t>(f2bf(o1)) << 16),
-                         static_cast<uint32_t>(f2bf(o2)) | (static_cast<uint32_t>(f2bf(o3)) << 16));
-    }
-  } else {
-    float mx = 0.0f;
-    for (int i = lane; i < n4; i += kWave) {
-      const float4 v = hr[i], s = sc4[i], b = sh4[i];
-      mx = fmaxf(mx, fabsf(ada(v.x, r, s.x, b.x)));
-      mx = fmaxf(mx, fabsf(ada(v.y, r, s.y, b.y)));
-      mx = fmaxf(mx, fabsf(ada(v.z, r, s.z, b.z)));
-      mx = fmaxf(mx, fabsf(ada(v.w, r, s.w, b.w)));
-    }
+  float mx = 0.0f;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-    if (lane == 0) {
+  for (int j = 0; j < kNormPer; ++j) {
+    const int i = tid + 256 * j;
+    if (i >= n4) break;
+    const float4 s = sc4[i], b = sh4[i];
+    const float o0 = ada(v[j].x, r, s.x, b.x), o1 = ada(v[j].y, r, s.y, b.y);
+    const float o2 = ada(v[j].z, r, s.z, b.z), o3 = ada(v[j].w, r, s.w, b.w);
+    if (mode == 0) {
+      reinterpret_cast<uint2*>(u + static_cast<size_t>(row) * D)[i] =
+          make_uint2(static_cast<uint32_t>(f2bf(o0)) | (static_cast<uint32_t>(f2bf(o1)) << 16),
+                     static_cast<uint32_t>(f2bf(o2)) | (static_cast<uint32_t>(f2bf(o3)) << 16));
+    } else {
+      mx = fmaxf(fmaxf(mx, fmaxf(fabsf(o0), fabsf(o1))), fmaxf(fabsf(o2), fabsf(o3)));
+    }
+  }
+  if (mode != 0) {
+    mx = block_max(mx, s_red);
+    if (tid == 0) {
       r_out[row] = r;
       rowmax[row] = mx;
     }
@@ -132,10 +156,10 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Quantiser: one wave per row.  The request's amax is the max of
-// rowmax[p][rows of the request] over the n_part partial columns; the row
-// is then coded with 448 / amax.  src == nullptr: the row is u recomputed
-// from h, r and the modulation; otherwise src [M][K] fp32.
+// Quantiser: one 256-thread workgroup per row.  The request's amax is the
+// max of rowmax[p][rows of the request] over the n_part partial columns; the
+// row is then coded with 448 / amax.  src == nullptr: the row is u
+// recomputed from h, r and the modulation; otherwise src [M][K] fp32.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ src,
                                                     const float* __restrict__ h,
@@ -145,22 +169,20 @@ __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ sr
                                                     int T, const float* __restrict__ rowmax,
                                                     int n_part, int ldp, uint8_t* __restrict__ codes,
                                                     float* __restrict__ sx_row) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= M) return;
+  __shared__ float s_red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
   const int r0 = (row / T) * T;
   float mx = 0.0f;
-  for (int i = lane; i < n_part * T; i += kWave) {
+  for (int i = tid; i < n_part * T; i += 256) {
     const int p = i / T, t = i % T;
     mx = fmaxf(mx, rowmax[static_cast<size_t>(p) * ldp + r0 + t]);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  mx = block_max(mx, s_red);
   const float mul = fp8_mul(mx);
-  if (lane == 0) sx_row[row] = fp8_scale(mx);
+  if (tid == 0) sx_row[row] = fp8_scale(mx);
   const int n16 = K / 16;
   uint4* out = reinterpret_cast<uint4*>(codes + static_cast<size_t>(row) * K);
-  for (int i = lane; i < n16; i += kWave) {
+  for (int i = tid; i < n16; i += 256) {
     float v[16];
     if (src) {
       const float4* s4 = reinterpret_cast<const float4*>(src + static_cast<size_t>(row) * K) + 4 * i;
@@ -772,9 +794,9 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(int mode, const bf16_t* s
 
 hipError_t launch_rownorm(const float* h, int M, int D, const float* scale, const float* shift,
                           float eps, int mode, bf16_t* u, float* r, float* rowmax, hipStream_t s) {
-  if (D % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rownorm_kernel, dim3((M + 3) / 4), dim3(256), 0, s, h, M, D, scale, shift, eps,
-                     mode, u, r, rowmax);
+  if (D % 4 || D > 4 * 256 * kNormPer) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rownorm_kernel, dim3(M), dim3(256), 0, s, h, M, D, scale, shift, eps, mode, u, r,
+                     rowmax);
   return hipGetLastError();
 }
 
@@ -782,8 +804,8 @@ hipError_t launch_quant(const float* src, const float* h, const float* r, const 
                         const float* shift, int M, int K, int T, const float* rowmax, int n_part,
                         int ldp, uint8_t* codes, float* sx_row, hipStream_t s) {
   if (K % 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_kernel, dim3((M + 3) / 4), dim3(256), 0, s, src, h, r, scale, shift, M, K,
-                     T, rowmax, n_part, ldp, codes, sx_row);
+  hipLaunchKernelGGL(quant_kernel, dim3(M), dim3(256), 0, s, src, h, r, scale, shift, M, K, T, rowmax,
+                     n_part, ldp, codes, sx_row);
   return hipGetLastError();
 }
 
