@@ -187,9 +187,9 @@ int tgemm_kc(int op);
 size_t tgemm_partial_floats(const TGemmPlan& g);
 hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a, int blocks, hipStream_t s);
 
-// mode 0: u = adaRMS(h) as bf16 rows; mode 1: per-row r and max |u|
+// per-row r = 1 / rms(h) and max |adaRMS(h)| (the fp8 inputs' norm)
 hipError_t launch_rownorm(const float* h, int M, int D, const float* scale, const float* shift,
-                          float eps, int mode, uint16_t* u, float* r, float* rowmax, hipStream_t s);
+                          float eps, float* r, float* rowmax, hipStream_t s);
 // e4m3 codes of fp32 rows (src) or of u recomputed from h and r (src null),
 // scaled per request by the amax over rowmax[n_part][ldp] of its rows
 hipError_t launch_quant(const float* src, const float* h, const float* r, const float* scale,

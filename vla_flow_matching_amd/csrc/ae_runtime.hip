@@ -72,7 +72,7 @@ struct ae_handle {
   // batched tiled path: bf16, or fp8 e4m3 QKV / gate-up / down projections
   bool tiled = false;
   bool fp8 = false;
-  void* ubuf = nullptr;  // GEMM input rows: adaRMS output (bf16) or e4m3 codes
+  void* ubuf = nullptr;  // fp8 GEMM input rows (e4m3 codes)
   float *rrow = nullptr, *rowmax = nullptr, *sxrow = nullptr;
   unsigned* wamax = nullptr;             // [L][6] amax bits of q, k, v, gate, up, down
   float *wmul = nullptr, *wsc = nullptr;  // [L][6] 448 / amax and amax / 448
@@ -406,16 +406,12 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
   const float eps = h->cfg.rms_eps;
   const bool f8 = h->fp8;
   const size_t ob = f8 ? 1 : 2;  // operand bytes
-  uint16_t* ub16 = static_cast<uint16_t*>(h->ubuf);
   uint8_t* ub8 = static_cast<uint8_t*>(h->ubuf);
+  // fp8: the adaRMS input of a QKV / gate-up product as e4m3 codes
   auto norm_rows = [&](const float* sc, const float* sh) -> ae_status {
-    if (!f8) {
-      AE_LAUNCH(launch_rownorm(h->h, M, D, sc, sh, eps, 0, ub16, nullptr, nullptr, s));
-    } else {
-      AE_LAUNCH(launch_rownorm(h->h, M, D, sc, sh, eps, 1, nullptr, h->rrow, h->rowmax, s));
-      AE_LAUNCH(launch_quant(nullptr, h->h, h->rrow, sc, sh, M, D, h->T, h->rowmax, 1, h->Mmax, ub8,
-                             h->sxrow, s));
-    }
+    AE_LAUNCH(launch_rownorm(h->h, M, D, sc, sh, eps, h->rrow, h->rowmax, s));
+    AE_LAUNCH(launch_quant(nullptr, h->h, h->rrow, sc, sh, M, D, h->T, h->rowmax, 1, h->Mmax, ub8,
+                           h->sxrow, s));
     return AE_OK;
   };
   uint16_t* ha = static_cast<uint16_t*>(h->ha);
@@ -444,7 +440,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
 
       TGemmArgs g = base_tgemm(h, tp.qkv, M, h->qkv_n, D);
       g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wqkv + l * h->sqkv; g.sw = h->wsc + 6 * l;
-      if (!f8) post_norm(g, h->bq + it * h->qkv_n);
+      if (!f8) post_norm(g, h->bq + it * h->qkv_n);  // (bf16: A = the norm shadow)
       g.q = h->q; g.ldq = h->qdim; g.kcache = kc; g.vtcache = vc; g.n_valid = h->n_valid;
       g.rope_cos = h->rope_cos; g.rope_sin = h->rope_sin;
       g.T = h->T; g.Hq = h->Hq; g.Hkv = h->Hkv; g.dh = h->dh; g.S_max = h->S_max;
@@ -709,7 +705,7 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
     AE_ALLOC(h->bg, static_cast<size_t>(h->Nmax) * L * 2 * F * 4);
   }
   if (h->tiled) {
-    AE_ALLOC(h->ubuf, Mm * std::max(D, F) * (h->fp8 ? 1 : 2));
+    if (h->fp8) AE_ALLOC(h->ubuf, Mm * std::max(D, F));
     AE_ALLOC(h->rrow, Mm * 4);
     AE_ALLOC(h->sxrow, Mm * 4);
     AE_ALLOC(h->rowmax, Mm * std::max<size_t>(1, 2 * F / 128) * 4);

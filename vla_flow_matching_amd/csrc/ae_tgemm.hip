@@ -8,9 +8,10 @@
 // the product restored with both scales).
 //
 // Around the GEMM:
-// * rownorm_kernel forms the adaRMS input u = h * r * (1 + scale) + shift of
-//   every row once (LoongForge blog, section 2), as bf16, or - for fp8 - only
-//   the per-row r and max |u| that the request-wide scale needs.
+// * rownorm_kernel forms, for the fp8 inputs, the per-row r and max |u| of
+//   the adaRMS input u = h * r * (1 + scale) + shift (LoongForge blog,
+//   section 2) that the request-wide scale needs (the bf16 path applies the
+//   norm after the product instead).
 // * quant_kernel turns fp32 rows (u recomputed bit-identically, or the
 //   gelu * up activations) into e4m3 codes with the per-request scale
 //   amax / 448, deciding every code in fp32.
@@ -102,16 +103,15 @@ __device__ __forceinline__ float block_max(float v, float* s_red) {
 }
 
 // ---------------------------------------------------------------------------
-// Row norm: one 256-thread workgroup per row (all of a row's loads in
-// flight at once).  mode 0: u -> bf16 [M][D].  mode 1: r[row] and
-// rowmax[row] = max_k |u|.  D <= 4 * 256 * kNormPer.
+// Row norm of the fp8 inputs: one 256-thread workgroup per row (all of a
+// row's loads in flight at once): r[row] = 1 / rms(h row) and rowmax[row] =
+// max_k |u|, u = adaRMS(h).  D <= 4 * 256 * kNormPer.
 // ---------------------------------------------------------------------------
 constexpr int kNormPer = 4;  // float4 per thread held across the two passes (D <= 4096)
 
 __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ h, int M, int D,
                                                       const float* __restrict__ scale,
                                                       const float* __restrict__ shift, float eps,
-                                                      int mode, bf16_t* __restrict__ u,
                                                       float* __restrict__ r_out,
                                                       float* __restrict__ rowmax) {
   __shared__ float s_red[4];
@@ -138,20 +138,12 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ 
     const float4 s = sc4[i], b = sh4[i];
     const float o0 = ada(v[j].x, r, s.x, b.x), o1 = ada(v[j].y, r, s.y, b.y);
     const float o2 = ada(v[j].z, r, s.z, b.z), o3 = ada(v[j].w, r, s.w, b.w);
-    if (mode == 0) {
-      reinterpret_cast<uint2*>(u + static_cast<size_t>(row) * D)[i] =
-          make_uint2(static_cast<uint32_t>(f2bf(o0)) | (static_cast<uint32_t>(f2bf(o1)) << 16),
-                     static_cast<uint32_t>(f2bf(o2)) | (static_cast<uint32_t>(f2bf(o3)) << 16));
-    } else {
-      mx = fmaxf(fmaxf(mx, fmaxf(fabsf(o0), fabsf(o1))), fmaxf(fabsf(o2), fabsf(o3)));
-    }
+    mx = fmaxf(fmaxf(mx, fmaxf(fabsf(o0), fabsf(o1))), fmaxf(fabsf(o2), fabsf(o3)));
   }
-  if (mode != 0) {
-    mx = block_max(mx, s_red);
-    if (tid == 0) {
-      r_out[row] = r;
-      rowmax[row] = mx;
-    }
+  mx = block_max(mx, s_red);
+  if (tid == 0) {
+    r_out[row] = r;
+    rowmax[row] = mx;
   }
 }
 
@@ -793,10 +785,9 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(int mode, const bf16_t* s
 }  // namespace
 
 hipError_t launch_rownorm(const float* h, int M, int D, const float* scale, const float* shift,
-                          float eps, int mode, bf16_t* u, float* r, float* rowmax, hipStream_t s) {
+                          float eps, float* r, float* rowmax, hipStream_t s) {
   if (D % 4 || D > 4 * 256 * kNormPer) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rownorm_kernel, dim3(M), dim3(256), 0, s, h, M, D, scale, shift, eps, mode, u, r,
-                     rowmax);
+  hipLaunchKernelGGL(rownorm_kernel, dim3(M), dim3(256), 0, s, h, M, D, scale, shift, eps, r, rowmax);
   return hipGetLastError();
 }
 
