@@ -110,61 +110,111 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // Action-in projection h = x W_in + b_in, plus per-64-column partial row sums
-// of h^2 for the first layer's adaRMS.  grid (M, D/64), 64 threads.
+// of h^2 for the first layer's adaRMS.  grid (ceil(M/8), ceil(D/256)), 256
+// threads: thread t owns column n of eight rows, loads its W_in column once
+// (all of it in flight) and reuses it for the rows; the rows' x values are
+// staged in LDS once per workgroup.
 // ---------------------------------------------------------------------------
+constexpr int kInRows = 8;
 
-__global__ __launch_bounds__(64) void action_in_kernel(const float* x, int A, const float* w_in,
-                                                       const float* b_in, float* h, int D,
-                                                       float* ssq, int ldssq, uint16_t* ha,
-                                                       const float* sc) {
-  const int m = blockIdx.x;
-  const int n = blockIdx.y * 64 + threadIdx.x;
-  float acc = 0.0f;
-  for (int a = 0; a < A; ++a) acc = fmaf(x[m * A + a], w_in[a * D + n], acc);
-  acc += b_in[n];
-  h[static_cast<size_t>(m) * D + n] = acc;
-  if (ha) ha[static_cast<size_t>(m) * D + n] = f2bf(acc * (1.0f + sc[n]));
-  const float sq = wave_sum(acc * acc);
-  if (threadIdx.x == 0) ssq[blockIdx.y * ldssq + m] = sq;
+template <int AMAX>
+__global__ __launch_bounds__(256) void action_in_kernel(const float* x, int M, int A, const float* w_in,
+                                                        const float* b_in, float* h, int D,
+                                                        float* ssq, int ldssq, uint16_t* ha,
+                                                        const float* sc) {
+  __shared__ float s_x[kInRows][AMAX];
+  const int m0 = blockIdx.x * kInRows;
+  const int n = blockIdx.y * 256 + threadIdx.x;
+  // the workgroup's x rows once, into LDS (rows past M and columns past A
+  // read clamped entries and are never used)
+  for (int i = threadIdx.x; i < kInRows * AMAX; i += 256)
+    s_x[i / AMAX][i % AMAX] = x[min(m0 + i / AMAX, M - 1) * A + min(i % AMAX, A - 1)];
+  __syncthreads();
+  if (n >= D) return;  // (D % 64 == 0: whole waves; no barriers below)
+  // every load unconditional and in bounds (indices clamped, masked at use),
+  // so all of them are in flight together
+  float w[AMAX];
+#pragma unroll
+  for (int a = 0; a < AMAX; ++a) w[a] = w_in[static_cast<size_t>(min(a, A - 1)) * D + n];
+  const float bn = b_in[n];
+  const float hs = ha ? 1.0f + sc[n] : 0.0f;
+  for (int r = 0; r < kInRows; ++r) {
+    const int m = m0 + r;
+    if (m >= M) break;
+    float acc = 0.0f;
+#pragma unroll
+    for (int a = 0; a < AMAX; ++a) acc = fmaf(s_x[r][a], a < A ? w[a] : 0.0f, acc);
+    acc += bn;
+    h[static_cast<size_t>(m) * D + n] = acc;
+    if (ha) ha[static_cast<size_t>(m) * D + n] = f2bf(acc * hs);
+    const float sq = wave_sum(acc * acc);
+    if (threadIdx.x % kWave == 0) ssq[static_cast<size_t>(n / 64) * ldssq + m] = sq;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Final adaRMS, action-out projection and the Euler update of one row:
 // v = adaRMS(h; scale_f, shift_f) W_out + b_out, x += dt v.  grid M, 256
-// threads; the row is normalised in fp32 and kept in LDS; W_out is held
-// transposed ([A][D]) so each wave streams one output's weights.
+// threads: thread t holds the row's columns t + 256 j (j < KJ) in registers
+// and forms partial dot products for 32 outputs at a time with all of its
+// W_out loads in flight (W_out held transposed, [A][D]: consecutive threads
+// read consecutive columns); each output is then summed over the workgroup.
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxWidth = 4096;
+constexpr int kOutChunk = 32;  // outputs per pass
 
+template <int KJ>
 __global__ __launch_bounds__(256) void action_out_kernel(float* x, int A, const float* h, int D,
                                                          const float* scale, const float* shift,
                                                          float eps, const float* w_out_t,
                                                          const float* b_out, float dt) {
-  __shared__ float su[kMaxWidth];
-  __shared__ float sred[4];
-  const int m = blockIdx.x;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  __shared__ float s_red[4][kOutChunk];
+  __shared__ float s_ss[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
   const float* hr = h + static_cast<size_t>(m) * D;
+  // columns past D: clamped loads, zero values
+  float u[KJ];
   float ss = 0.0f;
-  for (int k = threadIdx.x; k < D; k += 256) {
-    const float v = hr[k];
-    su[k] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int k = tid + 256 * j;
+    u[j] = k < D ? hr[min(k, D - 1)] : 0.0f;
+    ss = fmaf(u[j], u[j], ss);
   }
   ss = wave_sum(ss);
-  if (lane == 0) sred[wave] = ss;
+  if (lane == 0) s_ss[wave] = ss;
   __syncthreads();
-  const float tot = sred[0] + sred[1] + sred[2] + sred[3];
-  const float r = 1.0f / sqrtf(tot / static_cast<float>(D) + eps);
-  for (int k = threadIdx.x; k < D; k += 256) su[k] = su[k] * r * (1.0f + scale[k]) + shift[k];
-  __syncthreads();
-  for (int a = wave; a < A; a += 4) {
-    float s = 0.0f;
-    const float* wr = w_out_t + static_cast<size_t>(a) * D;  // W_out^T row a: coalesced
-    for (int k = lane; k < D; k += kWave) s = fmaf(su[k], wr[k], s);
-    s = wave_sum(s);
-    if (lane == 0) x[m * A + a] += dt * (s + b_out[a]);
+  const float r = 1.0f / sqrtf((s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3]) / static_cast<float>(D) + eps);
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int k = min(tid + 256 * j, D - 1);
+    const float v = u[j] * r * (1.0f + scale[k]) + shift[k];
+    u[j] = tid + 256 * j < D ? v : 0.0f;
+  }
+  for (int a0 = 0; a0 < A; a0 += kOutChunk) {
+    float acc[kOutChunk];
+#pragma unroll
+    for (int i = 0; i < kOutChunk; ++i) {
+      // outputs past A read row A - 1 and are never stored
+      const float* wr = w_out_t + static_cast<size_t>(min(a0 + i, A - 1)) * D;
+      acc[i] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < KJ; ++j) acc[i] = fmaf(u[j], wr[min(tid + 256 * j, D - 1)], acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kOutChunk; ++i) {
+      const float t = wave_sum(acc[i]);
+      if (lane == 0) s_red[wave][i] = t;
+    }
+    __syncthreads();
+    if (tid < kOutChunk && a0 + tid < A) {
+      const int a = a0 + tid;
+      const float v = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
+      x[m * A + a] += dt * (v + b_out[a]);
+    }
+    __syncthreads();
   }
 }
 
@@ -330,19 +380,34 @@ hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const 
 hipError_t launch_action_in(const float* x, int M, int A, const float* w_in, const float* b_in,
                             float* h, int D, float* ssq, int ldssq, hipStream_t s, uint16_t* ha,
                             const float* sc) {
-  if ((ha == nullptr) != (sc == nullptr)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(action_in_kernel, dim3(M, D / 64), dim3(64), 0, s, x, A, w_in, b_in, h, D,
-                     ssq, ldssq, ha, sc);
+  if ((ha == nullptr) != (sc == nullptr) || D % 64 || A < 1 || A > 64) return hipErrorInvalidValue;
+  const dim3 grid((M + kInRows - 1) / kInRows, (D + 255) / 256);
+  if (A <= 32)
+    hipLaunchKernelGGL(action_in_kernel<32>, grid, dim3(256), 0, s, x, M, A, w_in, b_in, h, D, ssq, ldssq, ha, sc);
+  else
+    hipLaunchKernelGGL(action_in_kernel<64>, grid, dim3(256), 0, s, x, M, A, w_in, b_in, h, D, ssq, ldssq, ha, sc);
   return hipGetLastError();
 }
 
 hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, const float* scale,
                              const float* shift, float eps, const float* w_out,
                              const float* b_out, float dt, hipStream_t s) {
-  if (D > kMaxWidth) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(action_out_kernel, dim3(M), dim3(256), 0, s, x, A, h, D, scale, shift, eps,
-                     w_out, b_out, dt);
-  return hipGetLastError();
+  if (D > kMaxWidth || A < 1) return hipErrorInvalidValue;
+  const int kj = (D + 255) / 256;
+#define AE_OUT(KJV)                                                                                   \
+  if (kj <= KJV) {                                                                                    \
+    hipLaunchKernelGGL(action_out_kernel<KJV>, dim3(M), dim3(256), 0, s, x, A, h, D, scale, shift, eps, \
+                       w_out, b_out, dt);                                                             \
+    return hipGetLastError();                                                                         \
+  }
+  AE_OUT(1)
+  AE_OUT(2)
+  AE_OUT(3)
+  AE_OUT(4)
+  AE_OUT(8)
+  AE_OUT(16)
+#undef AE_OUT
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_idx, int* n_valid,
