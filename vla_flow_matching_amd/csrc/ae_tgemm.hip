@@ -164,10 +164,22 @@ __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ sr
   __shared__ float s_red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int r0 = (row / T) * T;
+  // one load per thread, or (many partial columns) 16 per thread in flight
+  // per pass, clamped and masked at use
   float mx = 0.0f;
-  for (int i = tid; i < n_part * T; i += 256) {
-    const int p = i / T, t = i % T;
-    mx = fmaxf(mx, rowmax[static_cast<size_t>(p) * ldp + r0 + t]);
+  const int n = n_part * T;
+  if (n <= 256) {
+    if (tid < n) mx = rowmax[static_cast<size_t>(tid / T) * ldp + r0 + tid % T];
+  } else for (int i0 = 0; i0 < n; i0 += 16 * 256) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = min(i0 + tid + 256 * j, n - 1);
+      v[j] = rowmax[static_cast<size_t>(i / T) * ldp + r0 + i % T];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (i0 + tid + 256 * j < n) mx = fmaxf(mx, v[j]);
   }
   mx = block_max(mx, s_red);
   const float mul = fp8_mul(mx);
