@@ -111,6 +111,22 @@ def test_c1_fp32_parity(c1):
     check(g.run(K, V, m, x0), oracle(w, W, K, V, m, x0), TOL_F32, "c1")
 
 
+def test_c1_fp32_batched_per_phase():
+    """fp32 with 12 requests (96 action rows): past the whole-call kernel's
+    64-row tile, so the per-phase kernels run (the fp32 GEMM, the attention
+    kernel, action-in over 128 columns with half of each workgroup idle,
+    action-out with one column per thread); every request against the
+    oracle."""
+    _need_gpu()
+    w = synth.workload("c1", batch=12)
+    say("[case] c1 fp32, 12 requests (per-phase kernels)")
+    W = synth.make_weights(w)
+    g = Gpu(w, W)
+    K, V, m = synth.make_prefix(w)
+    x0 = synth.make_noise(w)
+    check(g.run(K, V, m, x0), oracle(w, W, K, V, m, x0), TOL_F32, "c1 batch 12")
+
+
 def test_c1_euler_closed_form(c1):
     """Constant-velocity head: x_N = x_0 + N dt v = x_0 - v."""
     w, W, _ = c1
@@ -261,8 +277,9 @@ def test_c5_batched_full():
 @pytest.mark.parametrize("name,batch", [("c5", 2), ("c5", 3), ("c5fp8", 3)])
 def test_batched_tiles_small(name, batch):
     """The batched path at reduced depth: 100 / 150 action rows leave a ragged
-    128-row tile; every request against the oracle (fp8: the oracle's e4m3
-    emulation with per-request activation scales)."""
+    32-row tile and a part-filled 8-row action-in group; every request
+    against the oracle (fp8: the oracle's e4m3 emulation with per-request
+    activation scales)."""
     _need_gpu()
     w = synth.workload(name, batch=batch, n_layers=2, n_steps=2)
     say(f"[case] {name} batch {batch}, 2 layers, 2 steps")
