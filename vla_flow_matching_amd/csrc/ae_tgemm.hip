@@ -532,13 +532,15 @@ constexpr int norm_tpr() {
   return BM >= 128 ? 2 : 4;
 }
 
-template <int OP, int EPI, int BM>
+// CPS: K chunks per LDS stage (one barrier per stage).
+template <int OP, int EPI, int BM, int CPS>
 __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   using O = TOp<OP>;
   constexpr int KC = O::KC;
   constexpr int RT = BM / 16;              // 16-row tiles per wave
   constexpr int NA = BM / 32;              // A staging pieces per thread per chunk
-  constexpr int kStageU4 = BM * 8;         // uint4 per staged A chunk
+  constexpr int kChunkU4 = BM * 8;         // uint4 per staged A chunk
+  constexpr int kStageU4 = CPS * kChunkU4;
   constexpr int kTileU4 = BM * (kBN + 1) / 4 + BM / 4;
   constexpr int kBufU4 = kTileU4 > 2 * kStageU4 ? kTileU4 : 2 * kStageU4;
   // two stages of A chunks; the finished tile reuses the space
@@ -552,8 +554,10 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   const int m0 = mt * BM;
   const int rows = min(BM, p.M - m0);
   const int n_chunks = p.K / KC;
-  const int c0 = static_cast<int>((static_cast<long long>(ks) * n_chunks) / p.ksplit);
-  const int c1 = static_cast<int>((static_cast<long long>(ks + 1) * n_chunks) / p.ksplit);
+  // stage indices (CPS chunks each) of this split
+  const int n_stages = n_chunks / CPS;
+  const int c0 = static_cast<int>((static_cast<long long>(ks) * n_stages) / p.ksplit);
+  const int c1 = static_cast<int>((static_cast<long long>(ks + 1) * n_stages) / p.ksplit);
   // the rows' 1 / rms for a norm after the product (into LDS past the
   // finished tile): loads issued after the first chunk's, summed after the
   // K loop
@@ -583,29 +587,39 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   u32x4* sv = reinterpret_cast<u32x4*>(s_buf);
 
   struct AStage {
-    u32x4 a[NA];
+    u32x4 a[CPS][NA];
   };
   struct BStage {
-    u32x4 b[2][2];
+    u32x4 b[CPS][2][2];
   };
+  // (c: a stage index, chunks CPS c .. CPS c + CPS - 1)
 #define TG_LOAD_A(R, c)                                                            \
   do {                                                                             \
-    const uint32_t co_ = static_cast<uint32_t>(c) * 128u;                          \
-    _Pragma("unroll") for (int j_ = 0; j_ < NA; ++j_)                              \
-      R.a[j_] = *reinterpret_cast<const u32x4*>(Ab + a_off[j_] + co_);             \
+    _Pragma("unroll") for (int q_ = 0; q_ < CPS; ++q_) {                           \
+      const uint32_t co_ = static_cast<uint32_t>(CPS * (c) + q_) * 128u;           \
+      _Pragma("unroll") for (int j_ = 0; j_ < NA; ++j_)                            \
+        R.a[q_][j_] = *reinterpret_cast<const u32x4*>(Ab + a_off[j_] + co_);       \
+    }                                                                              \
   } while (0)
 #define TG_LOAD_B(R, c)                                                            \
   do {                                                                             \
-    _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                               \
-      _Pragma("unroll") for (int s_ = 0; s_ < 2; ++s_)                             \
-        R.b[j_][s_] = Wv[(static_cast<size_t>(j_) * n_chunks + (c)) * 128 + s_ * 64]; \
+    _Pragma("unroll") for (int q_ = 0; q_ < CPS; ++q_)                             \
+      _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                             \
+        _Pragma("unroll") for (int s_ = 0; s_ < 2; ++s_)                           \
+          R.b[q_][j_][s_] = Wv[(static_cast<size_t>(j_) * n_chunks + CPS * (c) + q_) * 128 + s_ * 64]; \
   } while (0)
 #define TG_STORE_A(R, st)                                                          \
   do {                                                                             \
     u32x4* sa_ = sv + (st) * kStageU4;                                             \
-    _Pragma("unroll") for (int j_ = 0; j_ < NA; ++j_) sa_[a_lds[j_]] = R.a[j_];    \
+    _Pragma("unroll") for (int q_ = 0; q_ < CPS; ++q_)                             \
+      _Pragma("unroll") for (int j_ = 0; j_ < NA; ++j_)                            \
+        sa_[q_ * kChunkU4 + a_lds[j_]] = R.a[q_][j_];                              \
   } while (0)
-#define TG_COMPUTE(st, RB) tg_compute<OP, RT>(s_buf + (st) * kStageU4, RB, lane, acc)
+#define TG_COMPUTE(st, RB)                                                         \
+  do {                                                                             \
+    _Pragma("unroll") for (int q_ = 0; q_ < CPS; ++q_)                             \
+      tg_compute<OP, RT>(s_buf + (st) * kStageU4 + q_ * kChunkU4, RB[q_], lane, acc); \
+  } while (0)
 
   f32x4 acc[RT][2];
 #pragma unroll
@@ -643,7 +657,7 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
     __syncthreads();
   }
   if (c < c1) {
-    TG_COMPUTE(0, b0.b);  // odd chunk count: the last chunk sits in stage 0
+    TG_COMPUTE(0, b0.b);  // odd stage count: the last stage sits in stage buffer 0
     __syncthreads();      // every wave is done with the stages before s_y reuses them
   }
   if (norm_here) rn.finish(p, rows, s_r);  // (read after the s_y barrier below)
@@ -841,12 +855,22 @@ size_t tgemm_partial_floats(const TGemmPlan& g) {
   return g.ksplit > 1 ? static_cast<size_t>(g.m_tiles) * g.n_tiles * g.ksplit * g.bm * kBN : 0;
 }
 
+// Two K chunks per LDS stage (half the barriers) pay off only on long K
+// loops: down (64 chunks per tile) 21.5 -> 18.4 us, while 16-32 chunks lose
+// 1-4 us (gate/up fp8 20.7 -> 24.4).
+static bool two_chunk_stages(int n_chunks, int ksplit) {
+  return n_chunks % 2 == 0 && n_chunks / ksplit >= 64;
+}
+
 hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a, int blocks, hipStream_t s) {
   if (a.K % tgemm_kc(op) || a.N % kBN) return hipErrorInvalidValue;
   dim3 grid(blocks), block(kTT);
 #define AE_TG(OPV, EPV, BMV)                                                                \
   if (op == OPV && epi == EPV && a.bm == BMV) {                                             \
-    hipLaunchKernelGGL((tgemm_kernel<OPV, EPV, BMV>), grid, block, 0, s, a);                \
+    if (two_chunk_stages(a.K / tgemm_kc(op), a.ksplit))                                     \
+      hipLaunchKernelGGL((tgemm_kernel<OPV, EPV, BMV, 2>), grid, block, 0, s, a);           \
+    else                                                                                    \
+      hipLaunchKernelGGL((tgemm_kernel<OPV, EPV, BMV, 1>), grid, block, 0, s, a);           \
     if (a.ksplit > 1)                                                                       \
       hipLaunchKernelGGL((tgemm_reduce_kernel<OPV, EPV, BMV>),                              \
                          dim3(a.n_tiles * a.m_tiles * (BMV / kRedRows)), block, 0, s, a);   \
