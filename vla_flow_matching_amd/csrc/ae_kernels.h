@@ -141,7 +141,7 @@ struct TGemmArgs {
   int M, N, K;
   const uint4* W;  // packed weights (bf16 fragments or fp8 chunks)
   int n_tiles, m_tiles, ksplit;
-  int bm;  // tile rows (32)
+  int bm;  // tile rows (32 or 64)
   float* partial;
   int* counters;
   // fp8: per-row activation scale and per-tensor weight scales

@@ -835,6 +835,10 @@ TGemmPlan plan_tgemm(int M, int N, int K, int kc, int target_blocks) {
   TGemmPlan g;
   g.n_tiles = N / kBN;
   g.bm = 32;
+  // very wide bf16 products (gate/up) have tiles to spare: 64-row tiles
+  // there (800 x 8192 x 1024: 23.8 us against 26.3; the fp8 one is faster
+  // with 32-row tiles, 20.7 against 24.8)
+  if (kc == TOp<OP_BF16>::KC && ((M + 63) / 64) * g.n_tiles >= 3 * target_blocks) g.bm = 64;
   g.m_tiles = (M + g.bm - 1) / g.bm;
   const int chunks = K / kc;
   const int tiles = g.m_tiles * g.n_tiles;
@@ -876,7 +880,7 @@ hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a, int blocks, hi
                          dim3(a.n_tiles * a.m_tiles * (BMV / kRedRows)), block, 0, s, a);   \
     return hipGetLastError();                                                               \
   }
-#define AE_TG_BM(OPV, EPV) AE_TG(OPV, EPV, 32)
+#define AE_TG_BM(OPV, EPV) AE_TG(OPV, EPV, 64) AE_TG(OPV, EPV, 32)
   AE_TG_BM(OP_BF16, EPI_QKV)
   AE_TG_BM(OP_BF16, EPI_GELU)
   AE_TG_BM(OP_BF16, EPI_RESID)
