@@ -62,6 +62,25 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// A weight-prefetch workgroup (w of p.pf_blocks): its waves stream 1 KiB
+// pieces of the p.pf ranges through this workgroup's LDS (the bytes are
+// dropped; what matters is that they now sit in the last-level cache when
+// the next kernels read them), up to 32 pieces in flight per wave.
+__device__ __forceinline__ void prefetch_weights(const AttnArgs& p, int w, uint32_t lds0) {
+  const int gw = __builtin_amdgcn_readfirstlane(w * (kThreads / kWave) + static_cast<int>(threadIdx.x) / kWave);
+  const int nw = p.pf_blocks * (kThreads / kWave);
+  const uint32_t lane16 = 16u * (threadIdx.x % kWave);
+  for (int r = 0; r < 4; ++r) {
+    const int nf = p.pf_n4[r] / kWave;
+    int cnt = 0;
+    for (int f = gw; f < nf; f += nw) {
+      dma_frag(p.pf[r] + static_cast<size_t>(f) * kWave, lds0 + static_cast<uint32_t>(cnt % 32) * 1024u, lane16);
+      if (++cnt % 32 == 0) wait_vm<0>();
+    }
+  }
+  wait_vm<0>();
+}
+
 // Key blocks (KSTEP keys) in LDS, in the cache's fragment order (the
 // key-block layout): NBLK * NF K fragments (S^T = K Q^T operands), then ND
 // V^T fragments (O^T = V^T P^T operands), 1 KiB each, each a contiguous run
@@ -180,6 +199,10 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   // the units ordered by (item, split), so the query groups of a request
   // share one L2 and the splits of an item one XCD.
   const int n_units = n_items * p.nsplit, C = (n_units + kXcds - 1) / kXcds;
+  if (static_cast<int>(blockIdx.x) >= kXcds * C) {  // a weight-prefetch workgroup
+    prefetch_weights(p, blockIdx.x - kXcds * C, static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void_t*)(&s_kv[0][0]))));
+    return;
+  }
   const int li = blockIdx.x / kXcds, u = (blockIdx.x % kXcds) * C + li;
   if (li >= C || u >= n_units) return;
   const int s = u % p.nsplit;
@@ -388,7 +411,7 @@ int attention_max_splits(int items) {
 
 hipError_t launch_attention(Dt dt, const AttnArgs& a, hipStream_t s) {
   const int items = a.batch * a.Hkv * a.n_qg;
-  const int blocks = kXcds * ((items * a.nsplit + kXcds - 1) / kXcds);
+  const int blocks = kXcds * ((items * a.nsplit + kXcds - 1) / kXcds) + a.pf_blocks;
   if (dt == DT_BF16) return launch_dh<bf16_t>(a, blocks, s);
   return launch_dh<float>(a, blocks, s);
 }

@@ -72,6 +72,12 @@ struct AttnArgs {
   float scale_log2;
   float* partial;
   int* counters;
+  // Extra workgroups past the attention's that read the weights the next
+  // kernels multiply, so those arrive from the last-level cache instead of
+  // HBM (pf_blocks == 0: none).  Ranges of 16-byte words.
+  const uint4* pf[4];
+  int pf_n4[4];
+  int pf_blocks;
 };
 
 // Split-K / grid planning shared by the runtime and the launchers.

@@ -27,6 +27,7 @@ using namespace ae;
 namespace {
 
 constexpr int kTargetBlocks = 256;  // one workgroup per CU at least
+constexpr int kPrefetchBlocks = 32;  // weight-prefetch workgroups beside the batched attention
 constexpr int kMaxGraphs = 16;
 
 
@@ -454,6 +455,17 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
       at.batch = batch; at.n_qg = ap.n_qg; at.nsplit = ap.nsplit; at.kc_len = ap.kc_len;
       at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->dh)));
       at.partial = h->apart; at.counters = h->acnt;
+      // warm the last-level cache with this layer's O / gate-up / down
+      // weights and the next layer's QKV weights while attention runs
+      at.pf_blocks = kPrefetchBlocks;
+      at.pf[0] = h->wo + l * h->so;
+      at.pf_n4[0] = static_cast<int>(static_cast<size_t>(h->qdim) * D * 2 / 16);
+      at.pf[1] = h->wgu + l * h->sgu;
+      at.pf_n4[1] = static_cast<int>(static_cast<size_t>(D) * 2 * F * ob / 16);
+      at.pf[2] = h->wd + l * h->sd;
+      at.pf_n4[2] = static_cast<int>(static_cast<size_t>(F) * D * ob / 16);
+      at.pf[3] = h->wqkv + ((l + 1) % L) * h->sqkv;
+      at.pf_n4[3] = static_cast<int>(static_cast<size_t>(D) * h->qkv_n * ob / 16);
       AE_LAUNCH(launch_attention(h->dt, at, s));
 
       g = base_tgemm(h, tp.o, M, D, h->qdim);
