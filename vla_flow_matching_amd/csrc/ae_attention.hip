@@ -45,42 +45,6 @@ __device__ __forceinline__ void store4<float>(float* dst, const float* v) {
   *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One fragment copied from global memory straight into LDS: lane l's 16
-// bytes at g + lane16 (= 16 l) land at LDS byte address lds + 16 l; g and
-// lds are wave-uniform (scalar registers).  Issued as inline assembly so that
-// the compiler neither moves it nor adds waits for it; the caller waits with
-// wait_vm before a barrier.
-__device__ __forceinline__ void dma_frag(const void* g, uint32_t lds, uint32_t lane16) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(lane16), "s"(g), "s"(lds) : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector-memory operations are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// A weight-prefetch workgroup (w of p.pf_blocks): its waves stream 1 KiB
-// pieces of the p.pf ranges through this workgroup's LDS (the bytes are
-// dropped; what matters is that they now sit in the last-level cache when
-// the next kernels read them), up to 32 pieces in flight per wave.
-__device__ __forceinline__ void prefetch_weights(const AttnArgs& p, int w, uint32_t lds0) {
-  const int gw = __builtin_amdgcn_readfirstlane(w * (kThreads / kWave) + static_cast<int>(threadIdx.x) / kWave);
-  const int nw = p.pf_blocks * (kThreads / kWave);
-  const uint32_t lane16 = 16u * (threadIdx.x % kWave);
-  for (int r = 0; r < 4; ++r) {
-    const int nf = p.pf_n4[r] / kWave;
-    int cnt = 0;
-    for (int f = gw; f < nf; f += nw) {
-      dma_frag(p.pf[r] + static_cast<size_t>(f) * kWave, lds0 + static_cast<uint32_t>(cnt % 32) * 1024u, lane16);
-      if (++cnt % 32 == 0) wait_vm<0>();
-    }
-  }
-  wait_vm<0>();
-}
-
 // Key blocks (KSTEP keys) in LDS, in the cache's fragment order (the
 // key-block layout): NBLK * NF K fragments (S^T = K Q^T operands), then ND
 // V^T fragments (O^T = V^T P^T operands), 1 KiB each, each a contiguous run
@@ -200,7 +164,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   // share one L2 and the splits of an item one XCD.
   const int n_units = n_items * p.nsplit, C = (n_units + kXcds - 1) / kXcds;
   if (static_cast<int>(blockIdx.x) >= kXcds * C) {  // a weight-prefetch workgroup
-    prefetch_weights(p, blockIdx.x - kXcds * C, static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void_t*)(&s_kv[0][0]))));
+    prefetch_ranges<kThreads, 32>(p.pf, p.pf_n4, 4, blockIdx.x - kXcds * C, p.pf_blocks,
+                                  static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void_t*)(&s_kv[0][0]))));
     return;
   }
   const int li = blockIdx.x / kXcds, u = (blockIdx.x % kXcds) * C + li;

@@ -78,6 +78,48 @@ template <> struct Mma<float> {
 };
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS copies.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One fragment copied from global memory straight into LDS: lane l's 16
+// bytes at g + lane16 (= 16 l) land at LDS byte address lds + 16 l; g and
+// lds are wave-uniform (scalar registers).  Issued as inline assembly so that
+// the compiler neither moves it nor adds waits for it; the caller waits with
+// wait_vm before a barrier.
+__device__ __forceinline__ void dma_frag(const void* g, uint32_t lds, uint32_t lane16) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(lane16), "s"(g), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// A prefetch workgroup (w of nwg, NT threads): its waves stream 1 KiB pieces
+// of the ranges src[r] (n4[r] 16-byte words each, r < nr) through PIECES KiB
+// of this workgroup's LDS at byte address lds0.  The bytes are dropped; what
+// matters is that they sit in the last-level cache when the next kernels
+// read them.  Up to PIECES pieces are in flight per wave.
+template <int NT, int PIECES>
+__device__ __forceinline__ void prefetch_ranges(const uint4* const* src, const int* n4, int nr, int w, int nwg,
+                                                uint32_t lds0) {
+  const int gw = __builtin_amdgcn_readfirstlane(w * (NT / kWave) + static_cast<int>(threadIdx.x) / kWave);
+  const int nw = nwg * (NT / kWave);
+  const uint32_t lane16 = 16u * (threadIdx.x % kWave);
+  for (int r = 0; r < nr; ++r) {
+    const int nf = n4[r] / kWave;
+    int cnt = 0;
+    for (int f = gw; f < nf; f += nw) {
+      dma_frag(src[r] + static_cast<size_t>(f) * kWave, lds0 + static_cast<uint32_t>(cnt % PIECES) * 1024u, lane16);
+      if (++cnt % PIECES == 0) wait_vm<0>();
+    }
+  }
+  wait_vm<0>();
+}
+
+// ---------------------------------------------------------------------------
 // Key-block K / V cache layout.
 //
 // The keys of one (request, KV head) are stored in blocks of KB = KSTEP keys

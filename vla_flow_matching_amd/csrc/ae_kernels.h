@@ -148,6 +148,12 @@ struct TGemmArgs {
   const uint4* W;  // packed weights (bf16 fragments or fp8 chunks)
   int n_tiles, m_tiles, ksplit;
   int bm;  // tile rows (32 or 64)
+  // optional prefetch workgroups past the tile grid (as in AttnArgs): they
+  // read pf ranges into the last-level cache; main_blocks is set by
+  // launch_tgemm
+  const uint4* pf[2];
+  int pf_n4[2];
+  int pf_blocks, main_blocks;
   float* partial;
   int* counters;
   // fp8: per-row activation scale and per-tensor weight scales

@@ -415,6 +415,13 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
                            h->sxrow, s));
     return AE_OK;
   };
+  // prefetch workgroups of a GEMM launch (on the CUs its tiles leave free):
+  // layer ll's part of a K or V cache for these requests
+  auto prefetch_cache = [&](TGemmArgs& g, const void* cache, int ll, int blocks) {
+    g.pf_blocks = std::max(0, kTargetBlocks - blocks);
+    g.pf[0] = reinterpret_cast<const uint4*>(static_cast<const char*>(cache) + static_cast<size_t>(ll) * kv_layer);
+    g.pf_n4[0] = static_cast<int>(static_cast<size_t>(batch) * h->Hkv * h->S_max * h->dh * h->esz / 16);
+  };
   uint16_t* ha = static_cast<uint16_t*>(h->ha);
   // the bf16 norm-after-product inputs of a QKV / gate-up product
   auto post_norm = [&](TGemmArgs& g, const float* bias) {
@@ -470,6 +477,9 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
 
       g = base_tgemm(h, tp.o, M, D, h->qdim);
       g.A = h->o; g.lda_bytes = static_cast<size_t>(h->qdim) * 2; g.W = h->wo + l * h->so;
+      // the next layer's K cache of these requests into the last-level
+      // cache on the CUs the O-proj tiles leave free (its V: beside down)
+      prefetch_cache(g, h->kcache, (l + 1) % L, tp.o.blocks);
       g.h = h->h; g.ldh = D; g.gate = md + 2 * D;
       if (!f8) resid_out(g, md + 3 * D);
       AE_LAUNCH(launch_tgemm(OP_BF16, EPI_RESID, g, tp.o.blocks, s));
@@ -489,6 +499,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
 
       g = base_tgemm(h, tp.d, M, D, F);
       g.A = f8 ? h->ubuf : h->act; g.lda_bytes = F * ob; g.W = h->wd + l * h->sd;
+      prefetch_cache(g, h->vtcache, (l + 1) % L, tp.d.blocks);
       g.sw = h->wsc + 6 * l + 5;
       g.h = h->h; g.ldh = D; g.gate = md + 5 * D;
       // the next layer's attention norm (the last layer's h goes to the

@@ -547,7 +547,13 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   // (+ 1 / rms of the tile's rows past the finished tile)
   __shared__ __attribute__((aligned(16))) uint4 s_buf[kBufU4];
   auto s_y = reinterpret_cast<float (*)[kBN + 1]>(s_buf);
+  static_assert(kBufU4 >= 16 * 64, "16 KiB of LDS for a prefetch workgroup");
 
+  if (static_cast<int>(blockIdx.x) >= p.main_blocks) {  // a prefetch workgroup
+    prefetch_ranges<kTT, 16>(p.pf, p.pf_n4, 2, blockIdx.x - p.main_blocks, p.pf_blocks,
+                             static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void_t*)(s_buf))));
+    return;
+  }
   int nt, mt, ks;
   if (!tile_of(blockIdx.x, p.n_tiles, p.m_tiles, p.ksplit, nt, mt, ks)) return;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -866,9 +872,11 @@ static bool two_chunk_stages(int n_chunks, int ksplit) {
   return n_chunks % 2 == 0 && n_chunks / ksplit >= 64;
 }
 
-hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a, int blocks, hipStream_t s) {
-  if (a.K % tgemm_kc(op) || a.N % kBN) return hipErrorInvalidValue;
-  dim3 grid(blocks), block(kTT);
+hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a0, int blocks, hipStream_t s) {
+  if (a0.K % tgemm_kc(op) || a0.N % kBN) return hipErrorInvalidValue;
+  TGemmArgs a = a0;
+  a.main_blocks = blocks;
+  dim3 grid(blocks + a.pf_blocks), block(kTT);
 #define AE_TG(OPV, EPV, BMV)                                                                \
   if (op == OPV && epi == EPV && a.bm == BMV) {                                             \
     if (two_chunk_stages(a.K / tgemm_kc(op), a.ksplit))                                     \
