@@ -294,6 +294,44 @@ def test_batched_tiles_small(name, batch):
     check(g.run(K, V, m, x0), oracle(w, W, Kc, Vc, m, x0), TOL_BF16, f"{name} batch {batch}")
 
 
+_COVER = [(dt, dh, b, "same", 7) for dt in ("f32", "bf16") for dh in (64, 128, 256) for b in (1, 3)] + [
+    ("bf16", 128, 3, "fp8", 7),    # fp8 projections away from the Pi0.5 shape
+    ("bf16", 128, 1, "same", 40),  # action_dim above 32: the per-phase kernels at batch 1
+]
+
+
+@pytest.mark.parametrize("dtype,dh,batch,proj,adim", _COVER)
+def test_head_dim_dtype_path_coverage(dtype, dh, batch, proj, adim):
+    """Every head_dim and activation dtype the library accepts, on both
+    paths (batch 1 x 24 rows: the whole-call kernel; batch 3 x 24 = 72 rows,
+    or action_dim 40: the per-phase kernels), with grouped heads (4 query /
+    2 KV) and a ragged prefix whose visible rows have a masked hole.  The
+    gates' bias is raised to 0.5 so the residual branches carry weight: the
+    prefix V then moves the actions by 0.3-0.6, and hiding one more key row
+    moves them by 0.03-0.05, above the bf16 tolerance (with the plain
+    initialisation the attention branch moves them by under 0.04)."""
+    _need_gpu()
+    w = synth.Workload("hd", n_layers=2, width=256, n_q_heads=4, n_kv_heads=2, head_dim=dh,
+                       mlp_dim=512, action_horizon=24, action_dim=adim, n_steps=2, batch=batch,
+                       prefix_len=150, dtype=dtype, proj_dtype=proj, index=7, gate_bias=0.5)
+    label = f"{dtype} dh={dh} batch={batch} proj={proj} A={adim}"
+    say(f"[case] {label}")
+    W = synth.make_weights(w)
+    m = np.zeros((batch, w.prefix_len), dtype=np.uint8)
+    for b in range(batch):
+        m[b, :40 + 17 * b] = 1
+        m[b, 70:130 - 5 * b] = 1
+    K, V, m = synth.make_prefix(w, mask=m)
+    x0 = synth.make_noise(w)
+    out = Gpu(w, W).run(K, V, m, x0)
+    ref = oracle(w, W, K, V, m, x0)
+    if proj == "fp8":
+        tol = fp8_tolerance(w, W, K, V, m, x0, ref)
+    else:
+        tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    check(out, ref, tol, label)
+
+
 def fp8_tolerance(w, W, K, V, m, x0, ref):
     """Tolerance for a whole fp8 denoise call, derived from the arithmetic:
     every projection input is re-coded to e4m3 each layer, so a difference
