@@ -347,20 +347,28 @@ _LIMITS = [
     ("width 4096 (per-phase kernels)",
      dict(n_layers=1, width=4096, n_q_heads=8, n_kv_heads=1, head_dim=128, mlp_dim=256, action_horizon=8,
           action_dim=7, n_steps=2, batch=9, prefix_len=40)),
+    # degenerate shapes: one action token of one dimension, heads not grouped
+    ("T=1, A=1, MHA (whole-call kernel)",
+     dict(n_layers=1, width=64, n_q_heads=2, n_kv_heads=2, head_dim=64, mlp_dim=64, action_horizon=1,
+          action_dim=1, n_steps=3, batch=1, prefix_len=40)),
+    ("T=1, A=1, MHA, batch 65 (per-phase kernels; requests 14+ see no prefix)",
+     dict(n_layers=1, width=64, n_q_heads=2, n_kv_heads=2, head_dim=64, mlp_dim=64, action_horizon=1,
+          action_dim=1, n_steps=3, batch=65, prefix_len=40)),
 ]
 
 
 @pytest.mark.parametrize("label,fields", _LIMITS, ids=[c[0] for c in _LIMITS])
 def test_size_limits(label, fields):
     """The configuration limits (action_dim 64, 64 Euler steps, width 4096)
-    against the oracle, with a ragged prefix (bf16)."""
+    and degenerate shapes (one action token, ungrouped heads, requests with
+    an empty prefix) against the oracle, with a ragged prefix (bf16)."""
     _need_gpu()
     w = synth.Workload("lim", dtype="bf16", proj_dtype="same", index=8, gate_bias=0.5, **fields)
     say(f"[case] {label}")
     W = synth.make_weights(w)
     m = np.zeros((w.batch, w.prefix_len), dtype=np.uint8)
     for b in range(w.batch):
-        m[b, :w.prefix_len - 3 * b] = 1
+        m[b, :max(0, w.prefix_len - 3 * b)] = 1
     K, V, m = synth.make_prefix(w, mask=m)
     x0 = synth.make_noise(w)
     out = Gpu(w, W).run(K, V, m, x0)
