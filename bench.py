@@ -179,7 +179,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the denoise path shards by request with no "
-              "exchange, and this build runs and reports a single GPU's throughput "
+              "exchange between GPUs, so the figure it reports is a single GPU's throughput "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
 
