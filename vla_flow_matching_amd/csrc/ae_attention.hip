@@ -104,7 +104,7 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[blk * 4 + i] = st[blk][i] * scale_log2;
+      for (int i = 0; i < 4; ++i) sv[blk * 4 + i] = st[blk][i];
     if (kb0 + KSTEP > k_end) {  // ragged last block (uniform branch)
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
@@ -116,7 +116,7 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
 #pragma unroll
     for (int i = 1; i < NBLK * 4; ++i) cmax = fmaxf(cmax, sv[i]);
     cmax = xor16_max(cmax);
-    cmax = xor32_max(cmax);
+    cmax = xor32_max(cmax) * scale_log2;
     if (!__all(cmax <= m_run[c] + kSoftmaxSlack)) {  // move the reference max
       const float m_new = fmaxf(m_run[c], cmax);
       const float alpha = exp2_hw(m_run[c] - m_new);
@@ -128,12 +128,10 @@ __device__ __forceinline__ void attn_block(const uint4* fr, int kb0, int k_end, 
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < NBLK * 4; ++i) {
-      sv[i] = exp2_hw(sv[i] - m_run[c]);
+      sv[i] = exp2_hw(fmaf(sv[i], scale_log2, -m_run[c]));
       psum += sv[i];
     }
-    psum = xor16_sum(psum);
-    psum = xor32_sum(psum);
-    l_run[c] += psum;
+    l_run[c] += psum;  // this lane's keys only: summed over the lane groups after the loop
     const uint4 pf = pack_frag<T>(sv);
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[c][d] = MM::mma(fr[(NK + d) * kWave], pf, acc[c][d]);
@@ -237,6 +235,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
                              p.scale_log2, qf, acc, m_run, l_run);
   }
   // acc[c][d][i] = O^T[dim 16 d + 4 grp + i][query lane % 16 of block c] (unnormalised)
+#pragma unroll
+  for (int c = 0; c < kQB; ++c) l_run[c] = xor32_sum(xor16_sum(l_run[c]));
 
   // Key half 1 hands its (O^T, m, l) to key half 0 of the same rows through
   // LDS (the slots are free once every wave is past the loop); half 0
