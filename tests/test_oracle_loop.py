@@ -44,11 +44,77 @@ def run(w, W, K, V, m, x0, fp8=False):
 # Brute-force scalar twin
 # --------------------------------------------------------------------------
 
-def _bf_denoise(w, W, K, V, mask, x0):
-    """Scalar loops only; explicit visibility mask; independent of the oracle."""
+def _e4m3_table():
+    """Every finite non-negative OCP e4m3fn value with its code, from the
+    format's definition: exponent field e (4 bits, bias 7) and mantissa m
+    (3 bits); e = 0 is subnormal, m * 2^-9; code 0x7F is NaN, so 0x7E = 448
+    is the largest."""
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append((m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7), code))
+    return vals
+
+
+_E4M3 = _e4m3_table()
+
+
+def _e4m3_scalar(v):
+    """Nearest e4m3 value by scanning the whole table; a tie goes to the even
+    code (even mantissa); magnitudes past 448 saturate."""
+    a = abs(v)
+    best, best_code = None, None
+    for val, code in _E4M3:
+        if best is None or abs(a - val) < abs(a - best) or (
+                abs(a - val) == abs(a - best) and code % 2 == 0):
+            best, best_code = val, code
+    return math.copysign(best, v)
+
+
+def _fp8_rows(rows, wcodes, wscale):
+    """Rows of ONE request through a per-tensor fp8 linear: the request's
+    amax over every element of its rows, the multiplier 448 / amax and each
+    code decided in fp32, the product of codes summed in fp64 and scaled by
+    both scales."""
+    f32 = np.float32
+    amax = f32(max(abs(f32(v)) for r in rows for v in r))
+    amax = max(amax, f32(1e-12))
+    mul, sx = f32(448.0) / amax, amax / f32(448.0)
+    out = []
+    for r in rows:
+        codes = [_e4m3_scalar(float(f32(f32(v) * mul))) for v in r]
+        acc = [0.0] * wcodes.shape[1]
+        for j in range(wcodes.shape[1]):
+            t = 0.0
+            for i in range(len(codes)):
+                t += codes[i] * wcodes[i, j]
+            acc[j] = t * float(sx) * wscale
+        out.append(acc)
+    return out
+
+
+def _fp8_weight(Wt):
+    """One logical weight tensor: amax over the whole tensor, codes in fp32."""
+    f32 = np.float32
+    w32 = np.asarray(Wt, dtype=np.float32)
+    amax = max(f32(np.abs(w32).max()), f32(1e-12))
+    mul, s = f32(448.0) / amax, amax / f32(448.0)
+    codes = np.array([[_e4m3_scalar(float(f32(v * mul))) for v in row] for row in w32])
+    return codes, float(s)
+
+
+def _bf_denoise(w, W, K, V, mask, x0, fp8=False):
+    """Scalar loops only; explicit visibility mask; independent of the oracle.
+    fp8: the q, k, v, gate, up and down projections quantised per logical
+    tensor (weights) and per request (inputs)."""
     L, D, Hq, Hkv, dh, Fd = w.n_layers, w.width, w.n_q_heads, w.n_kv_heads, w.head_dim, w.mlp_dim
     T, A, N, B, P = w.action_horizon, w.action_dim, w.n_steps, w.batch, w.prefix_len
     g = lambda name: np.asarray(W[name], dtype=np.float64)
+    q8 = {}
+    if fp8:
+        for l in range(L):
+            for nm in ("q", "k", "v", "gate", "up", "down"):
+                q8[f"layers.{l}.{nm}"] = _fp8_weight(W[f"layers.{l}.{nm}"])
 
     def mv(vec, mat, bias=None):  # vec [in] @ mat [in, out]
         out = [0.0] * mat.shape[1]
@@ -95,9 +161,14 @@ def _bf_denoise(w, W, K, V, mask, x0):
                 mod = mv(c, g(f"layers.{l}.mod.w"), g(f"layers.{l}.mod.b"))
                 ch = [mod[j * D:(j + 1) * D] for j in range(6)]
                 u = [norm(h[i], ch[0], ch[1]) for i in range(T)]
-                qs = [mv(u[i], g(f"layers.{l}.q")) for i in range(T)]
-                ks = [mv(u[i], g(f"layers.{l}.k")) for i in range(T)]
-                vs = [mv(u[i], g(f"layers.{l}.v")) for i in range(T)]
+
+                def proj(rows, nm):
+                    key = f"layers.{l}.{nm}"
+                    if fp8:
+                        return _fp8_rows(rows, *q8[key])
+                    return [mv(r, g(key)) for r in rows]
+
+                qs, ks, vs = proj(u, "q"), proj(u, "k"), proj(u, "v")
                 o = [[0.0] * (Hq * dh) for _ in range(T)]
                 for hd in range(Hq):
                     kv = hd // (Hq // Hkv)
@@ -131,14 +202,16 @@ def _bf_denoise(w, W, K, V, mask, x0):
                 for i in range(T):
                     ob = mv(o[i], g(f"layers.{l}.o"))
                     h[i] = [h[i][d] + ch[2][d] * ob[d] for d in range(D)]
+                u2 = [norm(h[i], ch[3], ch[4]) for i in range(T)]
+                gts, ups = proj(u2, "gate"), proj(u2, "up")
+                acts = []
                 for i in range(T):
-                    u2 = norm(h[i], ch[3], ch[4])
-                    gt = mv(u2, g(f"layers.{l}.gate"))
-                    up = mv(u2, g(f"layers.{l}.up"))
-                    act = [0.5 * gt[f] * (1 + math.tanh(math.sqrt(2 / math.pi) * (gt[f] + 0.044715 * gt[f] ** 3))) * up[f]
-                           for f in range(Fd)]
-                    dn = mv(act, g(f"layers.{l}.down"))
-                    h[i] = [h[i][d] + ch[5][d] * dn[d] for d in range(D)]
+                    gt, up = gts[i], ups[i]
+                    acts.append([0.5 * gt[f] * (1 + math.tanh(math.sqrt(2 / math.pi) * (gt[f] + 0.044715 * gt[f] ** 3)))
+                                 * up[f] for f in range(Fd)])
+                dns = proj(acts, "down")
+                for i in range(T):
+                    h[i] = [h[i][d] + ch[5][d] * dns[i][d] for d in range(D)]
             fm = mv(c, g("final_mod.w"), g("final_mod.b"))
             for i in range(T):
                 vv = mv(norm(h[i], fm[:D], fm[D:]), g("action_out.w"), g("action_out.b"))
@@ -157,6 +230,47 @@ def test_oracle_matches_brute_force(hq, hkv):
     ref = _bf_denoise(w, W, K, V, mask, x0)
     assert np.abs(ours - x0).max() > 0.05  # the loop moved the actions
     assert np.allclose(ours, ref, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 1), (4, 2)])
+def test_oracle_fp8_matches_brute_force(hq, hkv):
+    """The fp8 recipe (MolmoBot PR Part 3: per-tensor dynamic e4m3, amax ->
+    cast -> scaled matmul) against the scalar twin, whose e4m3 rounding is a
+    nearest-value scan of the format's code table: per-request activation
+    amax, codes decided in fp32, y = (codes_x . codes_w) s_x s_w, a separate
+    weight scale per logical tensor.  Two requests whose inputs differ in
+    scale make a batch-wide amax, or one weight scale shared by q, k and v,
+    fail it; so does dropping either scale."""
+    w = tiny(n_q_heads=hq, n_kv_heads=hkv, width=8 if hq == 2 else 16)
+    W = synth.make_weights(w, std=0.3)
+    # per-tensor scales that differ widely between q, k and v, and gate, up
+    for l in range(w.n_layers):
+        for nm, f in (("k", 3.0), ("v", 0.25), ("up", 5.0), ("down", 0.5)):
+            W[f"layers.{l}.{nm}"] = (W[f"layers.{l}.{nm}"] * np.float32(f)).astype(np.float32)
+    mask = np.array([[1, 0, 1, 1, 0], [0, 1, 1, 1, 1]], np.uint8)
+    K, V, _ = synth.make_prefix(w, mask=mask, garbage="huge")
+    x0 = synth.make_noise(w)
+    x0[1] *= np.float32(6.0)  # request 1's inputs on another scale than request 0's
+    ours = run(w, W, K, V, mask, x0, fp8=True)
+    ref = _bf_denoise(w, W, K, V, mask, x0, fp8=True)
+    plain = run(w, W, K, V, mask, x0)
+    assert np.abs(ours - plain).max() > 1e-3  # quantisation is visible at this size
+    assert np.allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+def test_e4m3_twin_table_agrees_with_torch():
+    """The twin's table-scan rounding against torch.float8_e4m3fn on values
+    spread over every binade, the midpoints between codes and saturation."""
+    vals = [v for v, _ in _E4M3]
+    probes = set(vals)
+    for a, b in zip(vals, vals[1:]):
+        probes.update({(a + b) / 2, a + (b - a) / 3, b - (b - a) / 5})
+    probes.update({500.0, 448.0 + 16.0, 1e-4, 3e-3})
+    probes = sorted(probes)
+    x = torch.tensor(probes + [-v for v in probes], dtype=torch.float32)
+    got = [_e4m3_scalar(float(v)) for v in x]
+    want = x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).to(torch.float64).tolist()
+    assert got == want
 
 
 # --------------------------------------------------------------------------
