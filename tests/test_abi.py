@@ -13,9 +13,9 @@ from vla_flow_matching_amd import binding, synth
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    text = open(os.path.join(ROOT, "include", "ae.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:ae_status|const char\*|void)\s+(ae_\w+)\s*\(", text, re.M)))
+def _declared(header="ae.h", prefix="ae_"):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    return sorted(set(re.findall(r"^\s*(?:ae_status|const char\*|void)\s+(" + prefix + r"\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -32,6 +32,14 @@ def test_header_declares_expected_entry_points():
 
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_library_exports_test_entry_points(lib):
+    """include/ae_testing.h: the test-only entry points of the fp8 path."""
+    names = _declared("ae_testing.h", "aetest_")
+    assert len(names) == 5
+    for name in names:
         assert hasattr(lib, name), name
 
 
@@ -97,3 +105,53 @@ def test_no_gpu_reports_hip_error(lib):
     st, h = _create(lib)
     assert st == binding.AE_ERR_HIP
     assert not h.value
+
+
+@pytest.mark.parametrize("field,value", [("graph_cache_size", -1), ("graph_cache_size", 65),
+                                         ("graph_cache_evict", 2)])
+def test_invalid_graph_cache_config(lib, field, value):
+    st, h = _create(lib, **{field: value})
+    assert st == binding.AE_ERR_INVALID_ARGUMENT and not h.value
+
+
+def _unopened(name="c2", **kw):
+    """An ActionExpert whose argument checks run without a device handle:
+    the binding checks shapes and dtypes before any pointer reaches the ABI."""
+    ex = binding.ActionExpert.__new__(binding.ActionExpert)
+    ex.lib = binding.load()
+    ex.cfg = binding.make_config(synth.workload(name, **kw))
+    ex.h = None
+    return ex
+
+
+def test_binding_rejects_wrong_prefix_shapes(lib):
+    import torch
+    ex = _unopened("c2", n_layers=2)
+    L, P = 2, 712
+    good = torch.zeros((L, 1, P, 1, 256), dtype=torch.bfloat16)
+    mask = torch.ones((1, P), dtype=torch.uint8)
+    cases = [
+        (torch.zeros((L, 1, P, 1, 128), dtype=torch.bfloat16), good, mask),   # head_dim
+        (torch.zeros((L + 1, 1, P, 1, 256), dtype=torch.bfloat16), good, mask),  # layers
+        (good, torch.zeros((L, 1, P - 1, 1, 256), dtype=torch.bfloat16), mask),  # V shorter
+        (good.float(), good, mask),                                            # dtype
+        (good, good, torch.ones((1, P), dtype=torch.int32)),                   # mask dtype
+        (good, good, torch.ones((P,), dtype=torch.uint8)),                     # mask rank
+    ]
+    for K, V, m in cases:
+        with pytest.raises(binding.AeError) as e:
+            ex.set_prefix_kv(K, V, m)
+        assert e.value.status == binding.AE_ERR_SHAPE_MISMATCH
+
+
+def test_binding_rejects_wrong_noise_shapes(lib):
+    import torch
+    ex = _unopened("c2")
+    for noise in (torch.zeros((1, 50, 31)), torch.zeros((1, 49, 32)), torch.zeros((50, 32)),
+                  torch.zeros((1, 50, 32), dtype=torch.float64)):
+        with pytest.raises(binding.AeError) as e:
+            ex.denoise(noise, 10)
+        assert e.value.status == binding.AE_ERR_SHAPE_MISMATCH
+    with pytest.raises(binding.AeError) as e:
+        ex.denoise(torch.zeros((2, 50, 32)), 10, out=torch.zeros((1, 50, 32)))
+    assert e.value.status == binding.AE_ERR_SHAPE_MISMATCH

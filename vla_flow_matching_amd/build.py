@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libae.so")
 ARCH = "gfx950"
 
 SOURCES = ["ae_gemm.hip", "ae_tgemm.hip", "ae_attention.hip", "ae_misc.hip", "ae_persist.hip",
-           "ae_runtime.hip"]
+           "ae_runtime.hip", "ae_testing.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
