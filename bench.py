@@ -6,17 +6,18 @@ A "step" here is one whole denoise call: the time path, N Euler steps of the
 layer stack with attention over the resident prefix K/V, and the action
 updates, for one batch of synthetic inputs already resident in HBM.  The
 headline is the Pi0.5-shaped batch-1 workload (c2): action chunks/s.  The
-batched workload (c5, 16 requests) is measured as well and reported under
-"secondary".  Rank 0 prints one JSON line.
+batched workload (c5, 16 requests, bf16 and fp8), the three-camera (c3),
+MolmoBot-shaped (c4) and tiny fp32 (c1) workloads, prefix ingest and
+"ingest + denoise" are measured as well.  Rank 0 prints one JSON line.
 """
 
 from __future__ import annotations
 
 import argparse
 import hashlib
-import re
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,6 +35,15 @@ FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 # is reported only while their digest is the one it was taken with.
 KERNEL_SOURCES = ["ae_persist.hip", "ae_device.h", "ae_kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "persist_kernel_c2_traffic.txt")
+
+DESCRIPTIONS = {
+    "c1": "tiny fp32 expert",
+    "c2": "Pi0.5-shaped action expert",
+    "c3": "Pi0.5-shaped expert, three camera slots with one masked",
+    "c4": "MolmoBot-shaped expert",
+    "c5": "Pi0.5-shaped expert, 16 concurrent requests",
+    "c5fp8": "Pi0.5-shaped expert, 16 concurrent requests, e4m3 QKV / gate-up / down",
+}
 
 
 def kernel_digest():
@@ -95,48 +105,127 @@ def fp8_flops_split(w, n_valid):
     return f8, total - f8
 
 
-def run_gpu(name, steps, warmup):
-    import torch
+def prefix_bytes(w, n_valid):
+    """Bytes prefix ingest must move: the visible rows of K and V read once
+    and written once into the cache (the mask read and the tables are
+    negligible)."""
+    esz = 2 if w.dtype == "bf16" else 4
+    return 2 * 2 * w.n_layers * int(np.sum(n_valid)) * w.n_kv_heads * w.head_dim * esz
 
-    from vla_flow_matching_amd import binding, synth
 
+def pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+class DeviceErrors(RuntimeError):
+    pass
+
+
+def inputs_of(name):
+    """Seeded inputs of one workload (c3: the three-camera prefix built from
+    the two-camera one, its third slot masked)."""
+    from vla_flow_matching_amd import synth
+
+    if name == "c3":
+        w2 = synth.workload("c2")
+        W = synth.make_weights(synth.workload("c3"))
+        K2, V2, m2 = synth.make_prefix(w2)
+        K, V, m = synth.insert_camera_slot(synth.workload("c3"), K2, V2, m2, slot=2, garbage="nan")
+        return synth.workload("c3"), W, K, V, m, synth.make_noise(w2)
     w = synth.workload(name)
     W = synth.make_weights(w)
     K, V, m = synth.make_prefix(w, garbage="nan")
-    x0 = synth.make_noise(w)
-    ex = binding.ActionExpert(binding.make_config(w))
+    return w, W, K, V, m, synth.make_noise(w)
+
+
+def run_gpu(name, calls, warmup, prefix_reps=0):
+    """Time `calls` graph replays of one workload's denoise call (events on
+    the library's stream around all of them), then the same number with an
+    event pair per call (percentiles), then prefix ingest alone and ingest +
+    denoise.  Raises DeviceErrors if a whole-call kernel wait timed out."""
+    import torch
+
+    from vla_flow_matching_amd import binding
+
+    w, W, K, V, m, x0 = inputs_of(name)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    ex.load_weights(binding.weights_to_device(W, w.dtype))
-    del W
-    Kt = torch.from_numpy(K).to("cuda", dt)
-    Vt = torch.from_numpy(V).to("cuda", dt)
-    del K, V
-    ex.set_prefix_kv(Kt, Vt, torch.from_numpy(m).cuda())
-    x = torch.from_numpy(x0).cuda()
-    out = torch.empty_like(x)
-    for _ in range(warmup):
-        ex.denoise(x, w.n_steps, out=out)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(steps):
-        ex.denoise(x, w.n_steps, out=out)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / steps
-    assert torch.isfinite(out).all().item()
-    st = ex.stats()
-    ex.close()
-    return w, m.sum(axis=1), ms, wall, st
+    res = {}
+    with binding.ActionExpert(binding.make_config(w)) as ex:
+        ex.load_weights(binding.weights_to_device(W, w.dtype))
+        del W
+        Kt = torch.from_numpy(K).to("cuda", dt)
+        Vt = torch.from_numpy(V).to("cuda", dt)
+        mt = torch.from_numpy(m).cuda()
+        del K, V
+        ex.set_prefix_kv(Kt, Vt, mt)
+        x = torch.from_numpy(x0).cuda()
+        out = torch.empty_like(x)
+        for _ in range(warmup):
+            ex.denoise(x, w.n_steps, out=out)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        t0, t1 = ev(), ev()
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for _ in range(calls):
+            ex.denoise(x, w.n_steps, out=out)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        res["wall_s"] = time.perf_counter() - wall0
+        res["ms"] = t0.elapsed_time(t1) / calls
+        # the same calls with an event pair each (latency distribution)
+        pairs = [(ev(), ev()) for _ in range(calls)]
+        for a, b in pairs:
+            a.record(stream)
+            ex.denoise(x, w.n_steps, out=out)
+            b.record(stream)
+        torch.cuda.synchronize()
+        lat = [a.elapsed_time(b) for a, b in pairs]
+        res["p10"], res["p50"], res["p90"] = pct(lat, 10), pct(lat, 50), pct(lat, 90)
+        if prefix_reps:
+            pairs = [(ev(), ev()) for _ in range(prefix_reps)]
+            for a, b in pairs:
+                a.record(stream)
+                ex.set_prefix_kv(Kt, Vt, mt)
+                b.record(stream)
+            torch.cuda.synchronize()
+            res["prefix_ms"] = [a.elapsed_time(b) for a, b in pairs]
+            pairs = [(ev(), ev()) for _ in range(prefix_reps)]
+            for a, b in pairs:
+                a.record(stream)
+                ex.set_prefix_kv(Kt, Vt, mt)
+                ex.denoise(x, w.n_steps, out=out)
+                b.record(stream)
+            torch.cuda.synchronize()
+            res["set_denoise_ms"] = [a.elapsed_time(b) for a, b in pairs]
+        if not torch.isfinite(out).all().item():
+            raise DeviceErrors(f"{name}: non-finite actions")
+        st = ex.stats()
+        if st["device_errors"] != 0:
+            raise DeviceErrors(f"{name}: {st['device_errors']} whole-call launch(es) timed out; "
+                               "their results are invalid")
+    res["stats"] = st
+    res["w"] = w
+    res["n_valid"] = m.sum(axis=1)
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(name, budget_s):
     """The oracle as it stands, on this host's cores, over a bounded sample
-    of whole denoise calls of the same workload."""
-    from threadpoolctl import threadpool_info
+    of whole denoise calls of the same workload; then on one thread over a
+    3-step call (the per-step cost, scaled to the 10-step call)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import ae_oracle as O
     from vla_flow_matching_amd import synth
@@ -154,11 +243,59 @@ def cpu_baseline(name, budget_s):
         if el >= budget_s or calls >= 8:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    with threadpool_limits(1):
+        n1 = 3
+        t1 = time.perf_counter()
+        E.denoise(x0, K, V, m, n1)
+        el1 = time.perf_counter() - t1
+    call1 = el1 / n1 * w.n_steps
     return {"value": calls * w.batch / el, "unit": "chunks/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{calls} whole {w.name} denoise call(s) ({w.n_steps} steps, batch {w.batch}) "
                       f"in {el:.1f} s, NumPy float64 with {threads} BLAS threads "
-                      f"on {os.cpu_count()} host CPUs"}
+                      f"on {os.cpu_count()} host CPUs",
+            "cpu_model": cpu_model(),
+            "value_1thread": w.batch / call1,
+            "sample_1thread": f"one {n1}-step {w.name} call on 1 thread in {el1:.1f} s, scaled to "
+                              f"{w.n_steps} steps ({call1:.1f} s per call)"}
+
+
+def workload_line(name, r, bound):
+    w, nv = r["w"], r["n_valid"]
+    b, f = algorithmic_work(w, nv)
+    ms = r["ms"]
+    d = {"workload": f"{name}: {DESCRIPTIONS.get(name, name)}, {w.n_layers} layers, width {w.width}, "
+                     f"{w.n_q_heads}/{w.n_kv_heads} heads x {w.head_dim}, MLP {w.mlp_dim}, batch {w.batch}, "
+                     f"prefix {w.prefix_len} ({int(nv.sum())} visible), {w.action_horizon}x{w.action_dim} "
+                     f"actions, {w.n_steps} steps, {w.dtype}",
+         "value": w.batch / (ms * 1e-3), "unit": "chunks/s", "ms_per_call": ms, "us_per_call": ms * 1e3,
+         "denoise_steps_per_s": w.n_steps / (ms * 1e-3),
+         "latency_ms": {"p10": r["p10"], "p50": r["p50"], "p90": r["p90"]},
+         "persistent_calls": r["stats"]["persistent_calls"]}
+    if bound == "hbm":
+        gbs = b / (ms * 1e-3) / 1e9
+        d["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": b}
+    elif bound == "mfma":
+        tf = f / (ms * 1e-3) / 1e12
+        d["roofline"] = {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / BF16_PEAK_TFLOPS, "algorithmic_flops_per_call": f}
+    elif bound == "mfma-fp8":
+        f8 = fp8_flops_split(w, nv)
+        t_peak = f8[0] / (FP8_PEAK_TFLOPS * 1e12) + f8[1] / (BF16_PEAK_TFLOPS * 1e12)
+        d["roofline"] = {"bound": "mfma (mixed fp8 / bf16 peak)", "achieved": f / (ms * 1e-3) / 1e12,
+                         "unit": "TFLOP/s", "peak_time_ms": t_peak * 1e3, "frac": t_peak / (ms * 1e-3),
+                         "algorithmic_flops_per_call": f, "fp8_flops": f8[0], "bf16_flops": f8[1]}
+    else:
+        d["roofline"] = {"bound": "latency", "note": "a few MB per call: neither roofline applies"}
+    if "prefix_ms" in r:
+        pb = prefix_bytes(w, nv)
+        pm = float(np.median(r["prefix_ms"]))
+        d["prefix_ingest"] = {"ms_p50": pm, "ms_p10": pct(r["prefix_ms"], 10), "ms_p90": pct(r["prefix_ms"], 90),
+                              "algorithmic_bytes": pb, "achieved_GBps": pb / (pm * 1e-3) / 1e9}
+        d["set_plus_denoise_ms"] = {"p10": pct(r["set_denoise_ms"], 10), "p50": pct(r["set_denoise_ms"], 50),
+                                    "p90": pct(r["set_denoise_ms"], 90)}
+    return d
 
 
 def main():
@@ -167,8 +304,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--secondary", default="c5", help="batched workload, or 'none'")
-    ap.add_argument("--fp8", default="c5fp8", help="batched fp8 workload, or 'none'")
+    ap.add_argument("--others", default="c5,c5fp8,c4,c3,c1",
+                    help="further workloads measured after the headline, or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,73 +320,65 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
 
-    w, n_valid, ms, wall, st = run_gpu(args.workload, args.steps, args.warmup)
-    bytes_call, flops_call = algorithmic_work(w, n_valid)
-    gbs = bytes_call / (ms * 1e-3) / 1e9
-    line = {
-        "metric": "action chunks/s (10-step denoise) at batch 1; % HBM roofline",
-        "value": w.batch / (ms * 1e-3),
-        "unit": "chunks/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded random-init weights, N(0,1) prefix K/V and noise)",
-        "config": {
-            "workload": f"{w.name}: Pi0.5-shaped action expert, {w.n_layers} layers, width {w.width}, "
-                        f"{w.n_q_heads}/{w.n_kv_heads} heads x {w.head_dim}, MLP {w.mlp_dim}, "
-                        f"batch {w.batch}, prefix {w.prefix_len} ({int(n_valid.sum())} visible), "
-                        f"{w.action_horizon}x{w.action_dim} actions, {w.n_steps} Euler steps",
-            "batch": w.batch, "n_steps": w.n_steps, "prefix_len": w.prefix_len,
-            "n_valid": [int(v) for v in n_valid],
-        },
-        "denoise_steps_per_s": w.n_steps / (ms * 1e-3),
-        "roofline": {
-            "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic(w.name),
-            "kernel": "persist_kernel: one launch per denoise call (the call's graph also "
-                      "holds a 256-int counter fill)",
-            "algorithmic_bytes_per_launch": bytes_call,
-        },
-        "graph": {"captures": st["graph_captures"], "replays": st["graph_replays"]},
-        "wall_s_timed": wall,
-    }
-    if args.secondary != "none":
-        sec_steps = max(5, args.steps // 8)
-        w5, nv5, ms5, _, _ = run_gpu(args.secondary, sec_steps, max(2, args.warmup // 4))
-        b5, f5 = algorithmic_work(w5, nv5)
-        tf = f5 / (ms5 * 1e-3) / 1e12
-        line["secondary"] = {
-            "workload": f"{w5.name}: batch {w5.batch}, prefix {w5.prefix_len} (mean "
-                        f"{float(nv5.mean()):.0f} visible), {w5.n_steps} steps, {w5.dtype}",
-            "value": w5.batch / (ms5 * 1e-3), "unit": "chunks/s", "ms_per_call": ms5,
-            "calls": sec_steps,
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
-                         "algorithmic_flops_per_launch": f5},
+    try:
+        r = run_gpu(args.workload, args.steps, args.warmup, prefix_reps=20)
+        w, n_valid, ms = r["w"], r["n_valid"], r["ms"]
+        bytes_call, flops_call = algorithmic_work(w, n_valid)
+        gbs = bytes_call / (ms * 1e-3) / 1e9
+        head = workload_line(args.workload, r, "hbm")
+        line = {
+            "metric": "action chunks/s (10-step denoise) at batch 1; % HBM roofline",
+            "value": w.batch / (ms * 1e-3),
+            "unit": "chunks/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16" if w.dtype == "bf16" else "f32",
+            "data": "synthetic (seeded random-init weights, N(0,1) prefix K/V and noise)",
+            "config": {
+                "workload": head["workload"],
+                "batch": w.batch, "n_steps": w.n_steps, "prefix_len": w.prefix_len,
+                "n_valid": [int(v) for v in n_valid],
+            },
+            "denoise_steps_per_s": w.n_steps / (ms * 1e-3),
+            "latency_ms": head["latency_ms"],
+            "prefix_ingest": head.get("prefix_ingest"),
+            "set_plus_denoise_ms": head.get("set_plus_denoise_ms"),
+            "roofline": {
+                "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic(w.name),
+                "kernel": "persist_kernel: one launch per denoise call (the call's graph also "
+                          "holds a 256-int counter fill)",
+                "algorithmic_bytes_per_launch": bytes_call,
+            },
+            "graph": {"captures": r["stats"]["graph_captures"], "replays": r["stats"]["graph_replays"],
+                      "hits": r["stats"]["graph_hits"], "misses": r["stats"]["graph_misses"]},
+            "wall_s_timed": r["wall_s"],
         }
-    if args.fp8 != "none":
-        sec_steps = max(5, args.steps // 8)
-        w8, nv8, ms8, _, _ = run_gpu(args.fp8, sec_steps, max(2, args.warmup // 4))
-        b8, f8 = algorithmic_work(w8, nv8)
-        fl8 = fp8_flops_split(w8, nv8)
-        # mixed peak: the fp8 GEMMs at the fp8 rate, the rest at the bf16 rate
-        t_peak = fl8[0] / (FP8_PEAK_TFLOPS * 1e12) + fl8[1] / (BF16_PEAK_TFLOPS * 1e12)
-        line["secondary_fp8"] = {
-            "workload": f"{w8.name}: batch {w8.batch}, prefix {w8.prefix_len}, {w8.n_steps} steps, "
-                        "e4m3 QKV / gate-up / down (per-tensor weight scale, per-request activation "
-                        "scale), bf16 attention and O-proj",
-            "value": w8.batch / (ms8 * 1e-3), "unit": "chunks/s", "ms_per_call": ms8, "calls": sec_steps,
-            "roofline": {"bound": "mfma (mixed fp8 / bf16 peak)",
-                         "achieved": f8 / (ms8 * 1e-3) / 1e12, "unit": "TFLOP/s",
-                         "peak_time_ms": t_peak * 1e3, "frac": t_peak / (ms8 * 1e-3),
-                         "algorithmic_flops_per_launch": f8,
-                         "fp8_flops": fl8[0], "bf16_flops": fl8[1]},
-        }
+        others = {}
+        bounds = {"c5": "mfma", "c5fp8": "mfma-fp8", "c4": "hbm", "c3": "hbm", "c1": "latency", "c2": "hbm"}
+        if args.others != "none":
+            for name in [s for s in args.others.split(",") if s]:
+                heavy = name.startswith("c5")
+                calls = max(5, args.steps // 8) if heavy else max(10, args.steps // 2)
+                ro = run_gpu(name, calls, max(2, args.warmup // 4), prefix_reps=5 if heavy else 10)
+                others[name] = workload_line(name, ro, bounds.get(name, "hbm"))
+            if "c4" in others:
+                others["c4"]["roofline"]["note"] = (
+                    "c4's weights (208 MB per step) and its visible K/V (~20 MB) fit in the 256 MB "
+                    "last-level cache, so a call can run above the HBM bound; reported against 8 TB/s")
+        line["workloads"] = others
+        if "c5" in others:
+            line["secondary"] = others["c5"]
+        if "c5fp8" in others:
+            line["secondary_fp8"] = others["c5fp8"]
+    except DeviceErrors as e:
+        print(f"bench.py: {e}", file=sys.stderr, flush=True)
+        sys.exit(3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
     line["kernel_digest"] = kernel_digest()

@@ -81,7 +81,11 @@ typedef struct {
                                  gate/up and down projections (bf16 only) */
   float rope_theta;     /* RoPE base (10000) */
   float rms_eps;        /* adaRMS epsilon (1e-6) */
-  int use_graphs;       /* 1: replay each (batch, steps) loop as a hipGraph; 0: launch directly */
+  int use_graphs;       /* 1: replay denoise calls as captured hipGraphs; 0: launch directly */
+  int graph_cache_size; /* captured graphs kept at most, in [0, 64]; 0 turns capture off */
+  int graph_cache_evict;/* cache full and a new (batch, steps, bucket): 1 evicts the least
+                           recently used graph (released once its last replay is done);
+                           0 launches the new call directly, uncaptured */
 } ae_config;
 
 /* One named logical weight, caller-owned device memory, dtype = act_dtype.
@@ -108,48 +112,103 @@ typedef struct {
   long long graph_replays;
   long long eager_runs;      /* calls launched directly instead of replaying a graph */
   long long device_bytes;    /* bytes the handle holds on the device */
-  long long device_errors;   /* nonzero: a persistent-kernel barrier timed out (results invalid) */
+  long long device_errors;   /* whole-call launches whose waits timed out (their results are
+                                invalid); counted on the device, read by ae_get_stats */
   long long persistent;      /* workgroups of the whole-call kernel used when batch*T <= 64; 0: none */
+  long long persistent_calls;/* denoise calls that ran the whole-call kernel */
+  long long graph_hits;      /* calls replayed from the graph cache */
+  long long graph_misses;    /* calls whose signature was not cached (captured, or run directly) */
+  long long graph_evictions; /* graphs evicted to make room */
+  long long graphs_cached;   /* graphs in the cache now */
+  long long prefix_bucket;   /* key span (prefix bucket) of the last ae_set_prefix_kv */
 } ae_stats;
 
 /* Validate the config, then allocate every device buffer the handle will
  * ever use (weights, prefix K/V at max size, activations, scratch).
+ * Defined by: MolmoBot PR Part 1 (graph inputs are static buffers allocated
+ * up front, never built lazily), so a replay reads fixed addresses.
  * Errors: INVALID_ARGUMENT / UNSUPPORTED (before any HIP call), HIP (no
- * device), OUT_OF_MEMORY.  On error *out is NULL. */
+ * device), OUT_OF_MEMORY.  On error *out is NULL.  The handle owns every
+ * buffer until ae_destroy. */
 ae_status ae_create(const ae_config* cfg, ae_handle** out);
 
-/* Copy and pack the named weights (merged q|k|v and gate|up in the kernels'
- * fragment order; fp8 codes with a static per-tensor scale when configured).
- * All n views are validated (names, ranks, shapes, dtypes) before anything is
- * written.  The caller may free its tensors once the stream passes the call.
- * Drops captured graphs (they read the packed buffers by address, which stay
- * fixed, so this is only for hygiene). */
+/* Copy and pack the named weights: q|k|v merged into one projection in that
+ * shard order and gate|up into another, each packed in the kernels' fragment
+ * order; fp8 e4m3 codes with a static per-tensor scale when configured.
+ * Defined by: sglang PR 34599 summary, implementation item 1 (merged Q/K/V
+ * and gate/up projections, one GEMM each, with shard-aware loading of the
+ * q/k/v pieces); MolmoBot PR Part 3 (per-tensor fp8 weights).
+ * Arguments: n views of caller-owned device memory in act_dtype, names and
+ * shapes as listed at ae_tensor_view.  All n views are validated (names,
+ * ranks, shapes, dtypes) before anything is written: INVALID_ARGUMENT for a
+ * missing, unknown, duplicate or null weight, SHAPE_MISMATCH for a wrong
+ * shape.  Stream-ordered; the caller may free its tensors once the stream
+ * passes the call.  Captured graphs stay valid (they read the packed
+ * buffers by address); the time-path table is rebuilt on the next call. */
 ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* stream);
 
-/* Ingest one query's prefix: K and V are [L][batch][prefix_len][Hkv][dh] in
+/* Ingest one query's prefix K/V and mask into the static buffers.
+ * Defined by: MolmoBot PR Part 2 (the context K/V is computed once per query
+ * and reused by every flow step); sglang PR 34599 summary, implementation
+ * item 4 (the mutable prefix K/V and mask are refreshed in place before an
+ * action-graph replay); LoongForge blog section 1 (masked camera slots and
+ * padding are invisible; pad tokens do not advance positions).
+ * Arguments: K and V are device [L][batch][prefix_len][Hkv][dh] in
  * act_dtype, K already rotated at the prefix's own positions (the VLM's KV
- * cache); valid_mask is [batch][prefix_len] uint8 (0 = invisible: padding or
- * an empty camera slot, any pattern).  Device pointers.  The library copies
- * the visible rows, in order, into its static buffers and computes, on the
+ * cache); valid_mask is device [batch][prefix_len] uint8 (0 = invisible:
+ * padding or an empty camera slot, any pattern).  The library copies the
+ * visible rows, in order, into its static buffers and computes, on the
  * device, each request's visible count n_b (the action tokens sit at
  * positions n_b .. n_b+T-1) and RoPE tables.  Invisible rows are never read
  * into arithmetic.  prefix_len may be 0 (K, V, mask may then be NULL).  The
+ * prefix bucket is the smallest ae_set_prefix_buckets length >= prefix_len
+ * (else max_prefix_len); rows past prefix_len count as masked padding.
+ * Errors: SHAPE_MISMATCH for batch outside [1, max_batch] or prefix_len
+ * outside [0, max_prefix_len], INVALID_ARGUMENT for a null pointer with
+ * prefix_len > 0 (checked before any state change).  Stream-ordered; the
  * caller may reuse its buffers once the stream passes the call. */
 ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* K,
                            const void* V, const uint8_t* valid_mask, void* stream);
 
+/* Configure prefix-length buckets: lengths[0..n) strictly increasing, each in
+ * [1, max_prefix_len], n <= 32 (n = 0: one bucket, max_prefix_len).  Takes
+ * effect at the next ae_set_prefix_kv.
+ * Defined by: sglang PR 34599 summary, implementation items 4-5 (opt-in
+ * prompt bucketing: right padding with the mask False to the smallest bucket
+ * that holds the prompt, so one graph serves the whole bucket; bucket lengths
+ * must be positive, strictly increasing and within the maximum length).
+ * Here a bucket sizes the attention's key splits and keys the graph cache.
+ * Errors: INVALID_ARGUMENT (the handle is left unchanged). */
+ae_status ae_set_prefix_buckets(ae_handle* h, const int* lengths, int n);
+
 /* Integrate: x_0 = noise, x_{k+1} = x_k + dt * v(x_k, t_k), t_k = (N-k)/N,
- * dt = -1/N, N = steps; writes x_N.  noise and actions_out are device
- * [batch][T][A] fp32 and may alias.  batch must equal the last
- * ae_set_prefix_kv batch.  Asynchronous on `stream`. */
+ * dt = -1/N, N = steps; writes x_N.
+ * Defined by: MolmoBot PR Part 2 (generate_actions runs the expert's flow
+ * steps over the cached context; only the action queries and the timestep
+ * change between steps); LoongForge blog sections 2-3 and 5.3 (adaRMS with
+ * scale/shift/gate, gated residuals, gelu*up, rotate_half RoPE, masked
+ * attention over the visible prefix and the action tokens, time MLP, action
+ * in/out projections and final norm); sglang PR 34599 summary, items 2-3
+ * (layout and sinusoid computed once per call; calls replayed from a bounded
+ * graph cache).
+ * Arguments: noise and actions_out are device [batch][T][A] fp32 and may
+ * alias; batch must equal the last ae_set_prefix_kv batch.  Errors (before
+ * any state change): INVALID_ARGUMENT for null buffers or steps outside
+ * [1, max_steps], NOT_READY without weights or prefix, SHAPE_MISMATCH for
+ * another batch.  Asynchronous on `stream`. */
 ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps,
                      float* actions_out, void* stream);
 
-/* Counters, plus the device error flag; reading the flag synchronises with
- * the device (the one call besides create/destroy that does). */
+/* Counters, plus the device error count; reading it synchronises with the
+ * device (the one call besides create/destroy that does).  INVALID_ARGUMENT
+ * for null arguments. */
 ae_status ae_get_stats(const ae_handle* h, ae_stats* out);
+/* The handle's last error message ("" if none); "null handle" for NULL. */
 const char* ae_last_error(const ae_handle* h);
+/* A static description of a status code. */
 const char* ae_status_string(ae_status s);
+/* Synchronise the device, release every graph and buffer, free the handle.
+ * NULL is ignored. */
 void ae_destroy(ae_handle* h);
 
 #ifdef __cplusplus

@@ -8,6 +8,7 @@ pruned-slot inputs produce the same kernel inputs, and the kernels reduce in
 fixed orders (graph replays, A-B-A, graph vs direct launches).
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -15,6 +16,8 @@ import pytest
 
 from oracle import ae_oracle as O
 from vla_flow_matching_amd import synth
+
+import oracle_pool
 
 torch = pytest.importorskip("torch")
 
@@ -56,6 +59,7 @@ class Gpu:
         x = torch.from_numpy(np.ascontiguousarray(x0)).cuda()
         out = self.ex.denoise(x, self.w.n_steps if steps is None else steps)
         torch.cuda.synchronize()
+        assert self.ex.stats()["device_errors"] == 0, "a whole-call kernel wait timed out"
         return out.cpu().numpy()
 
 
@@ -245,9 +249,106 @@ def test_c4_full_parity():
         check(g.run(K, V, m, x0), oracle(w, W, K, V, m, x0), TOL_BF16, f"c4 n={n}")
 
 
+@pytest.mark.parametrize("name,batch", [("c4", 4), ("c1", 8), ("c4", 3)])
+def test_whole_call_kernel_several_requests(name, batch):
+    """Batches whose action rows fit one 64-row tile (c4: 4 x 16, c1: 8 x 8,
+    and a part-filled tile of 3 x 16) run the whole-call kernel: its
+    per-request indexing (request of a row, each request's visible count and
+    RoPE rows, one attention item per request and KV head) against the oracle
+    for every request, and each request against the same one run alone."""
+    _need_gpu()
+    w = synth.workload(name, batch=batch)
+    if name == "c4":
+        w = synth.workload(name, batch=batch, n_layers=3, n_steps=3)
+    say(f"[case] whole-call kernel, {name} x {batch} requests ({batch * w.action_horizon} rows)")
+    W = synth.make_weights(w)
+    g = Gpu(w, W)
+    m = np.zeros((batch, w.prefix_len), np.uint8)
+    for b in range(batch):  # different visible counts, the last request's with a hole
+        m[b, :w.prefix_len - 7 * b - 1] = 1
+        if b == batch - 1:
+            m[b, 5:9] = 0
+    K, V, _ = synth.make_prefix(w, mask=m, garbage="nan")
+    x0 = synth.make_noise(w)
+    out = g.run(K, V, m, x0)
+    st = g.ex.stats()
+    assert st["persistent_calls"] >= 1, st
+    tol = TOL_F32 if w.dtype == "f32" else TOL_BF16
+    refs = oracle_pool.per_request(w, W, K, V, m, x0, range(batch))
+    for b, (ref, _) in enumerate(refs):
+        check(out[b:b + 1], ref, tol, f"{name} request {b} of {batch} (n={int(m[b].sum())})")
+    g1 = Gpu(dataclasses.replace(w, batch=1), W)
+    for b in (0, batch - 1):
+        alone = g1.run(K[:, b:b + 1], V[:, b:b + 1], m[b:b + 1], x0[b:b + 1])
+        err = float(np.abs(alone - out[b:b + 1]).max())
+        say(f"[parity] {name} request {b}: batched vs alone {err:.3e}")
+        assert err <= tol
+
+
+def test_graph_cache_lru_and_capacity(c2small):
+    """The bounded graph cache (sglang PR summary, items 3 and 5): capacity 2
+    with eviction keeps the two most recently used signatures, evicts the
+    least recently used one and counts hits, misses and evictions; capacity 0
+    captures nothing; a full cache without eviction runs new signatures
+    directly.  Every result is bitwise that of direct launches."""
+    w, W, _ = c2small
+    say("[case] graph cache: LRU eviction, zero capacity, no-evict fallback")
+    K, V, m = synth.make_prefix(w)
+    x0 = synth.make_noise(w)
+    direct = Gpu(w, W, max_prefix_len=1018, max_steps=4, use_graphs=False)
+    want = {n: direct.run(K, V, m, x0, n) for n in (1, 2, 3)}
+    lru = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=2)
+    for n in (1, 2, 1, 3, 1, 2):  # misses 1, 2; hit 1; miss 3 evicts 2; hit 1; miss 2 evicts 3
+        assert np.array_equal(lru.run(K, V, m, x0, n), want[n]), n
+    st = lru.ex.stats()
+    say(f"[stats] {st}")
+    assert (st["graph_hits"], st["graph_misses"], st["graph_evictions"]) == (2, 4, 2)
+    assert st["graph_captures"] == 4 and st["graphs_cached"] == 2 and st["eager_runs"] == 0
+    off = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=0)
+    assert np.array_equal(off.run(K, V, m, x0, 2), want[2])
+    st = off.ex.stats()
+    assert st["graph_captures"] == 0 and st["eager_runs"] == 1
+    full = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=1, graph_cache_evict=False)
+    for n in (2, 3, 2):
+        assert np.array_equal(full.run(K, V, m, x0, n), want[n]), n
+    st = full.ex.stats()
+    assert (st["graph_captures"], st["graph_hits"], st["graph_evictions"], st["eager_runs"]) == (1, 1, 0, 1)
+
+
+def test_prefix_buckets(c2small):
+    """Prefix buckets (sglang PR summary, items 4-5): a prefix takes the
+    smallest bucket that holds it, the key splits and the graph key follow
+    the bucket, and the result matches the oracle (the split layout changes
+    the rounding order only); bucket lists that are not strictly increasing
+    or exceed the capacity are rejected and leave the handle unchanged."""
+    from vla_flow_matching_amd import binding
+    w, W, _ = c2small
+    say("[case] prefix buckets")
+    g = Gpu(w, W, max_prefix_len=1018, max_steps=4)
+    g.ex.set_prefix_buckets([128, 576, 712])
+    for bad in ([576, 576], [600, 128], [0, 64], [64, 2000]):
+        with pytest.raises(binding.AeError) as e:
+            g.ex.set_prefix_buckets(bad)
+        assert e.value.status == binding.AE_ERR_INVALID_ARGUMENT
+    x0 = synth.make_noise(w)
+    for P, n, bucket in ((712, 600, 712), (560, 540, 576), (100, 100, 128), (900, 700, 1018)):
+        wp = synth.workload("c2", n_layers=2, n_steps=2, prefix_len=P)
+        mk = np.zeros((1, P), np.uint8)
+        mk[0, :n] = 1
+        K, V, _ = synth.make_prefix(wp, mask=mk, garbage="nan")
+        out = g.run(K, V, mk, x0)
+        st = g.ex.stats()
+        assert st["prefix_bucket"] == bucket, st
+        Kc, Vc = K.copy(), V.copy()
+        Kc[:, mk == 0] = 0
+        Vc[:, mk == 0] = 0
+        check(out, oracle(wp, W, Kc, Vc, mk, x0), TOL_BF16, f"prefix {P} ({n} visible) in bucket {bucket}")
+    assert g.ex.stats()["graph_captures"] == 4
+
+
 def test_c5_batched_full():
-    """16 requests with their own prefixes (valid 700..1024 of 1024): sampled
-    requests against the oracle run alone, and the batched rows against the
+    """16 requests with their own prefixes (valid 700..1024 of 1024): every
+    request against the oracle run alone, and the batched rows against the
     same request run at batch 1 on the GPU."""
     _need_gpu()
     w = synth.workload("c5")
@@ -259,13 +360,12 @@ def test_c5_batched_full():
     x0 = synth.make_noise(w)
     out = g.run(K, V, m, x0)
     assert np.isfinite(out).all()
+    refs = oracle_pool.per_request(w, W, K, V, m, x0, range(w.batch))
+    errs = []
+    for b, (ref, _) in enumerate(refs):
+        errs.append(check(out[b:b + 1], ref, TOL_BF16, f"c5 request {b} (n={int(m[b].sum())})"))
+    say(f"[parity] c5 all {w.batch} requests: max {max(errs):.3e}")
     w1 = synth.workload("c5", batch=1)
-    for b in (0, 15):
-        Kc, Vc = K[:, b:b + 1].copy(), V[:, b:b + 1].copy()
-        Kc[:, m[b:b + 1] == 0] = 0
-        Vc[:, m[b:b + 1] == 0] = 0
-        ref = oracle(w1, W, Kc, Vc, m[b:b + 1], x0[b:b + 1])
-        check(out[b:b + 1], ref, TOL_BF16, f"c5 request {b} (n={int(m[b].sum())})")
     g1 = Gpu(w1, W)
     b = 7
     alone = g1.run(K[:, b:b + 1], V[:, b:b + 1], m[b:b + 1], x0[b:b + 1])
@@ -409,8 +509,13 @@ def fp8_tolerance(w, W, K, V, m, x0, ref):
 
 def test_c5_fp8_full():
     """c5 with e4m3 QKV / gate-up / down weights (static per tensor) and
-    per-request dynamic activation scales: sampled requests against the
-    oracle's emulation, and a request batched against the same one alone."""
+    per-request dynamic activation scales: every request against the
+    oracle's emulation, and a request batched against the same one alone.
+
+    Each request is held to twice the oracle's own response to a relative
+    1e-6 perturbation of its noise (never less than 2e-2; see fp8_tolerance);
+    the error is also reported against the 2e-2 contract itself, which the
+    full-size fp8 loop does not meet for every request."""
     _need_gpu()
     w = synth.workload("c5fp8")
     say("[case] c5 fp8 full: batch 16, prefix 1024")
@@ -421,21 +526,22 @@ def test_c5_fp8_full():
     x0 = synth.make_noise(w)
     out = g.run(K, V, m, x0)
     assert np.isfinite(out).all()
+    refs = oracle_pool.per_request(w, W, K, V, m, x0, range(w.batch), perturb=1e-6)
+    tols, errs = [], []
+    for b, (ref, floor) in enumerate(refs):
+        tols.append(max(TOL_BF16, 2.0 * floor))
+        say(f"[fp8] request {b}: oracle response to a 1e-6 relative noise perturbation {floor:.3e}")
+        errs.append(check(out[b:b + 1], ref, tols[-1], f"c5 fp8 request {b} (n={int(m[b].sum())})"))
+    over = [b for b, e in enumerate(errs) if e > TOL_BF16]
+    say(f"[fp8] c5 fp8 all {w.batch} requests: max error {max(errs):.3e}; "
+        f"{len(over)} of {w.batch} above the 2e-2 contract: {over}")
     w1 = synth.workload("c5fp8", batch=1)
-    tols = []
-    for b in (0, 15):
-        Kc, Vc = K[:, b:b + 1].copy(), V[:, b:b + 1].copy()
-        Kc[:, m[b:b + 1] == 0] = 0
-        Vc[:, m[b:b + 1] == 0] = 0
-        ref = oracle(w1, W, Kc, Vc, m[b:b + 1], x0[b:b + 1])
-        tols.append(fp8_tolerance(w1, W, Kc, Vc, m[b:b + 1], x0[b:b + 1], ref))
-        check(out[b:b + 1], ref, tols[-1], f"c5 fp8 request {b} (n={int(m[b].sum())})")
     g1 = Gpu(w1, W)
     b = 7
     alone = g1.run(K[:, b:b + 1], V[:, b:b + 1], m[b:b + 1], x0[b:b + 1])
     err = float(np.abs(alone - out[b:b + 1]).max())
-    say(f"[parity] c5 fp8 batched vs alone, request {b}: {err:.3e} (tol {max(tols):.3e})")
-    assert err <= max(tols)
+    say(f"[parity] c5 fp8 batched vs alone, request {b}: {err:.3e} (tol {tols[b]:.3e})")
+    assert err <= tols[b]
 
 
 # --------------------------------------------------------------------------

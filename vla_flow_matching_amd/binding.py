@@ -8,9 +8,12 @@ into a hipStream_t.  There is no CPU fallback: without the built library
 
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
-from typing import Dict, Optional
+import sys
+import weakref
+from typing import Dict, Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libae.so")
 
@@ -19,8 +22,8 @@ AE_ERR_OUT_OF_MEMORY, AE_ERR_UNSUPPORTED, AE_ERR_HIP = 4, 5, 6
 AE_F32, AE_BF16, AE_FP8_E4M3 = 0, 1, 2
 
 # every function include/ae.h declares
-EXPORTS = ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_denoise", "ae_get_stats",
-           "ae_last_error", "ae_status_string", "ae_destroy")
+EXPORTS = ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_set_prefix_buckets", "ae_denoise",
+           "ae_get_stats", "ae_last_error", "ae_status_string", "ae_destroy")
 
 
 class Config(ctypes.Structure):
@@ -31,6 +34,7 @@ class Config(ctypes.Structure):
         ("max_prefix_len", ctypes.c_int), ("max_batch", ctypes.c_int), ("max_steps", ctypes.c_int),
         ("act_dtype", ctypes.c_int), ("proj_weight_dtype", ctypes.c_int),
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("use_graphs", ctypes.c_int),
+        ("graph_cache_size", ctypes.c_int), ("graph_cache_evict", ctypes.c_int),
     ]
 
 
@@ -43,7 +47,10 @@ class Stats(ctypes.Structure):
     _fields_ = [("denoise_calls", ctypes.c_longlong), ("prefix_sets", ctypes.c_longlong),
                 ("graph_captures", ctypes.c_longlong), ("graph_replays", ctypes.c_longlong),
                 ("eager_runs", ctypes.c_longlong), ("device_bytes", ctypes.c_longlong),
-                ("device_errors", ctypes.c_longlong), ("persistent", ctypes.c_longlong)]
+                ("device_errors", ctypes.c_longlong), ("persistent", ctypes.c_longlong),
+                ("persistent_calls", ctypes.c_longlong), ("graph_hits", ctypes.c_longlong),
+                ("graph_misses", ctypes.c_longlong), ("graph_evictions", ctypes.c_longlong),
+                ("graphs_cached", ctypes.c_longlong), ("prefix_bucket", ctypes.c_longlong)]
 
 
 class AeError(RuntimeError):
@@ -67,6 +74,7 @@ def load() -> ctypes.CDLL:
     lib.ae_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(vp)]
     lib.ae_load_weights.argtypes = [vp, ctypes.POINTER(TensorView), ci, vp]
     lib.ae_set_prefix_kv.argtypes = [vp, ci, ci, vp, vp, vp, vp]
+    lib.ae_set_prefix_buckets.argtypes = [vp, ctypes.POINTER(ci), ci]
     lib.ae_denoise.argtypes = [vp, vp, ci, ci, vp, vp]
     lib.ae_get_stats.argtypes = [vp, ctypes.POINTER(Stats)]
     lib.ae_last_error.argtypes = [vp]
@@ -75,14 +83,16 @@ def load() -> ctypes.CDLL:
     lib.ae_status_string.restype = ctypes.c_char_p
     lib.ae_destroy.argtypes = [vp]
     lib.ae_destroy.restype = None
-    for f in ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_denoise", "ae_get_stats"):
+    for f in ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_set_prefix_buckets", "ae_denoise",
+              "ae_get_stats"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
 
 
 def make_config(w, max_batch: Optional[int] = None, max_prefix_len: Optional[int] = None,
-                max_steps: Optional[int] = None, use_graphs: bool = True) -> Config:
+                max_steps: Optional[int] = None, use_graphs: bool = True,
+                graph_cache_size: int = 16, graph_cache_evict: bool = True) -> Config:
     """Config from any object with the workload fields (e.g. synth.Workload)."""
     act = AE_BF16 if w.dtype == "bf16" else AE_F32
     proj = AE_FP8_E4M3 if getattr(w, "proj_dtype", "same") == "fp8" else act
@@ -91,7 +101,8 @@ def make_config(w, max_batch: Optional[int] = None, max_prefix_len: Optional[int
                   w.prefix_len if max_prefix_len is None else max_prefix_len,
                   w.batch if max_batch is None else max_batch,
                   w.n_steps if max_steps is None else max_steps,
-                  act, proj, float(w.rope_theta), float(w.rms_eps), int(bool(use_graphs)))
+                  act, proj, float(w.rope_theta), float(w.rms_eps), int(bool(use_graphs)),
+                  int(graph_cache_size), int(bool(graph_cache_evict)))
 
 
 def _stream_ptr(stream) -> ctypes.c_void_p:
@@ -117,17 +128,47 @@ def _dev(t, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name: str, shape, dtype):
+    """Raise AeError(AE_ERR_SHAPE_MISMATCH) unless t has this shape and dtype.
+
+    The C ABI receives bare pointers, so a short or mistyped buffer would be
+    read past its end on the device; the binding checks what the config
+    implies before handing the pointer over."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise AeError(AE_ERR_SHAPE_MISMATCH,
+                      f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+# Handles still open, closed in creation order at interpreter exit while the
+# HIP runtime is still up (a finaliser running later, during teardown, would
+# call into a runtime that may already be shut down).
+_open_handles: "weakref.WeakSet[ActionExpert]" = weakref.WeakSet()
+
+
+@atexit.register
+def _close_all():
+    for ex in list(_open_handles):
+        ex.close()
+
+
 class ActionExpert:
     """One library handle: weights, prefix K/V and the denoise loop."""
 
     def __init__(self, cfg: Config):
         self.lib = load()
         self.cfg = cfg
+        self.h = None
         h = ctypes.c_void_p()
         st = self.lib.ae_create(ctypes.byref(cfg), ctypes.byref(h))
         if st != AE_OK:
             raise AeError(st, "ae_create: " + self.lib.ae_status_string(st).decode())
         self.h = h
+        self.prefix_batch = None
+        _open_handles.add(self)
+
+    def _act_dtype(self):
+        import torch
+        return torch.bfloat16 if self.cfg.act_dtype == AE_BF16 else torch.float32
 
     def _check(self, st: int, what: str):
         if st != AE_OK:
@@ -149,24 +190,43 @@ class ActionExpert:
                     "ae_load_weights")
 
     def set_prefix_kv(self, K, V, mask, stream=None):
-        """K, V [L, B, P, Hkv, dh] device tensors; mask [B, P] uint8 device tensor."""
+        """K, V [L, B, P, Hkv, dh] device tensors in the activation dtype; mask
+        [B, P] uint8 device tensor."""
+        import torch
+        if mask.dim() != 2:
+            raise AeError(AE_ERR_SHAPE_MISMATCH, f"mask: expected [batch, prefix_len], got {tuple(mask.shape)}")
         B, P = int(mask.shape[0]), int(mask.shape[1])
+        c = self.cfg
         if P == 0:
             nullp = ctypes.c_void_p()
             st = self.lib.ae_set_prefix_kv(self.h, B, 0, nullp, nullp, nullp, _stream_ptr(stream))
         else:
+            kv_shape = (c.n_layers, B, P, c.n_kv_heads, c.head_dim)
+            _expect(K, "K", kv_shape, self._act_dtype())
+            _expect(V, "V", kv_shape, self._act_dtype())
+            _expect(mask, "mask", (B, P), torch.uint8)
             st = self.lib.ae_set_prefix_kv(self.h, B, P, _dev(K, "K"), _dev(V, "V"), _dev(mask, "mask"),
                                            _stream_ptr(stream))
         self._check(st, "ae_set_prefix_kv")
+        self.prefix_batch = B
+
+    def set_prefix_buckets(self, lengths: Sequence[int]):
+        """Prefix-length buckets (strictly increasing, each <= max_prefix_len)."""
+        arr = (ctypes.c_int * max(1, len(lengths)))(*[int(v) for v in lengths])
+        self._check(self.lib.ae_set_prefix_buckets(self.h, arr, len(lengths)), "ae_set_prefix_buckets")
 
     def denoise(self, noise, steps: int, out=None, stream=None):
         """noise [B, T, A] fp32 device tensor -> actions (new tensor unless ``out``)."""
         import torch
-        if noise.dtype != torch.float32:
-            raise TypeError("noise must be float32")
+        c = self.cfg
+        if noise.dim() != 3:
+            raise AeError(AE_ERR_SHAPE_MISMATCH, f"noise: expected [batch, T, A], got {tuple(noise.shape)}")
+        B = int(noise.shape[0])
+        _expect(noise, "noise", (B, c.action_horizon, c.action_dim), torch.float32)
         if out is None:
             out = torch.empty_like(noise)
-        st = self.lib.ae_denoise(self.h, _dev(noise, "noise"), int(noise.shape[0]), int(steps),
+        _expect(out, "out", (B, c.action_horizon, c.action_dim), torch.float32)
+        st = self.lib.ae_denoise(self.h, _dev(noise, "noise"), B, int(steps),
                                  _dev(out, "out"), _stream_ptr(stream))
         self._check(st, "ae_denoise")
         return out
@@ -177,11 +237,24 @@ class ActionExpert:
         return {f: getattr(s, f) for f, _ in Stats._fields_}
 
     def close(self):
+        """Release the handle (synchronises the device).  Idempotent."""
         if getattr(self, "h", None):
             self.lib.ae_destroy(self.h)
             self.h = None
+        _open_handles.discard(self)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
     def __del__(self):
+        # At interpreter shutdown the HIP runtime (and a profiler attached to
+        # it) may already be torn down; the atexit hook has closed every
+        # handle by then, so a finaliser that runs late does nothing.
+        if sys is None or sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

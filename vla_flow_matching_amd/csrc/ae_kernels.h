@@ -251,7 +251,7 @@ struct PersistArgs {
   int n_acnt;  // attention items
   int* flags;  // [G] barrier generations
   uint32_t* genp;  // generation base of the split-K packets (one word)
-  int* err;    // device error flag (a barrier timed out)
+  int* err;    // [2]: this launch's error flag (a wait timed out), launches that raised it
   PGemm pq, po, pg, pd;
   int n_qg, nsplit, kc_len;
 };

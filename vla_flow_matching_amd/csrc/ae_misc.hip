@@ -265,9 +265,9 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(const uint8_t* mask, i
 
 // copy: visible row j of K and V -> cache key comp_idx[j] (key-block layout,
 // KvLayout).  grid (L*B*Hkv, max(1, ceil(P/32))), 256 threads.  The first
-// row block of each (layer, request, head) also zeroes the keys past the
-// request's (n_valid + n_act .. S_max): attention multiplies whole key
-// blocks and relies on the cache being finite there.
+// row block of each (layer, request, head) also zeroes the keys from the
+// request's n_valid + n_act to the end of that 64-key block: attention
+// multiplies whole key blocks and relies on the cache being finite there.
 constexpr int kCopyRows = 32;
 
 template <typename T>
@@ -299,8 +299,12 @@ __global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V
     vdst[LY::v_off(ci, d, dh)] = V[src];
   }
   if (blockIdx.y == 0) {
+    // The attention kernels read whole key blocks (at most 64 keys) up to
+    // the block holding the request's last key, so only the rest of that
+    // block must hold finite values; keys past it are never read.
     const int z0 = min(n_valid[b] + n_act, S_max);
-    for (int i = threadIdx.x; i < (S_max - z0) * dh; i += 256) {
+    const int z1 = min((z0 + 63) / 64 * 64, S_max);
+    for (int i = threadIdx.x; i < (z1 - z0) * dh; i += 256) {
       const int key = z0 + i / dh, d = i % dh;
       kdst[LY::k_off(key, d, dh)] = T(0);
       vdst[LY::v_off(key, d, dh)] = T(0);

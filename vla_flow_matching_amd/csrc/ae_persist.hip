@@ -1147,8 +1147,9 @@ int occupancy_p() {
   return n;
 }
 
-// Zero the barrier flags and split counters, and advance the packet
-// generation base past every generation the previous launch used.
+// Zero the barrier flags and split counters, advance the packet generation
+// base past every generation the previous launch used, and re-arm the error
+// flag.
 __global__ void fill_int_kernel(PersistArgs args, uint32_t stride) {
   const int na = args.G;
   const int nb = args.pq.n_tiles + args.po.n_tiles + args.pg.n_tiles + args.pd.n_tiles + args.n_acnt;
@@ -1158,6 +1159,13 @@ __global__ void fill_int_kernel(PersistArgs args, uint32_t stride) {
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     args.genp[0] += stride;
+    // err[0] is this launch's flag; a flag the previous launch raised is
+    // counted into err[1] and cleared, so one timed-out barrier does not
+    // disarm the waits of every later launch
+    if (args.err[0] != 0) {
+      args.err[1] += 1;
+      args.err[0] = 0;
+    }
   }
 }
 

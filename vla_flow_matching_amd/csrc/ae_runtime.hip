@@ -1,14 +1,15 @@
 // Host runtime behind include/ae.h: config validation, the static buffer
 // plan (every device buffer is allocated in ae_create, none lazily), weight
 // ingest and packing, prefix ingest, step sequencing and hipGraph capture /
-// replay of whole denoise calls keyed by (batch, steps).
+// replay of whole denoise calls keyed by (batch, steps, prefix bucket).
 //
 // The library follows the MolmoBot PR (Part 1: graph inputs are static
 // buffers allocated up front, never lazily built; Part 2: the context K/V is
 // ingested once per query and every step reads it) and the sglang PR summary
-// (item 3: a bounded graph cache, falling back to direct launches when full;
-// item 4: the mutable prefix K/V and mask are refreshed in place before a
-// replay).
+// (item 3: a bounded LRU graph cache whose evicted graphs are released, or
+// direct launches when it is full; item 4: prefix buckets, and the mutable
+// prefix K/V and mask refreshed in place before a replay; item 5: bucket
+// lengths validated up front).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -20,6 +21,7 @@
 #include <vector>
 
 #include "../../include/ae.h"
+#include "ae_graph_cache.h"
 #include "ae_kernels.h"
 
 using namespace ae;
@@ -28,7 +30,15 @@ namespace {
 
 constexpr int kTargetBlocks = 256;  // one workgroup per CU at least
 constexpr int kPrefetchBlocks = 32;  // weight-prefetch workgroups beside the batched attention
-constexpr int kMaxGraphs = 16;
+constexpr int kMaxGraphs = 64;   // graph_cache_size at most
+constexpr int kMaxBuckets = 32;  // prefix bucket lengths at most
+
+// A cached graph and an event recorded after its latest replay: an evicted
+// graph is destroyed only once that event has completed.
+struct GraphEntry {
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t done = nullptr;
+};
 
 
 struct Buf {
@@ -91,7 +101,10 @@ struct ae_handle {
   int prefix_batch = -1;
   int table_steps = -1;  // step count the modulation table currently holds
   hipStream_t cap_stream = nullptr;
-  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  LruCache<CallKey, GraphEntry> graphs;
+  std::vector<GraphEntry> retired;  // evicted, destroyed once their last replay is done
+  std::vector<int> buckets;         // prefix bucket lengths (ascending); empty: one bucket
+  int span = 0;                     // key span of the current prefix: its bucket length
   ae_stats stats{};
   std::string err;
   std::vector<Buf> bufs;
@@ -146,6 +159,8 @@ std::string validate_config(const ae_config* c) {
   if (!(c->rope_theta > 0.0f)) return "rope_theta must be > 0";
   if (!(c->rms_eps >= 0.0f)) return "rms_eps must be >= 0";
   if (c->use_graphs != 0 && c->use_graphs != 1) return "use_graphs must be 0 or 1";
+  if (c->graph_cache_size < 0 || c->graph_cache_size > kMaxGraphs) return "graph_cache_size must be in [0, 64]";
+  if (c->graph_cache_evict != 0 && c->graph_cache_evict != 1) return "graph_cache_evict must be 0 or 1";
   return "";
 }
 
@@ -174,13 +189,14 @@ struct AttnPlan {
 
 // rows: query rows one item covers (64 in the whole-call kernel, the batched
 // kernel's attention_rows_per_item() otherwise)
-AttnPlan plan_attention(const ae_handle* h, int batch, int rows, int max_splits = 1 << 30) {
+// span: the prefix bucket (visible rows at most)
+AttnPlan plan_attention(const ae_handle* h, int batch, int span, int rows, int max_splits = 1 << 30) {
   AttnPlan a;
   const int R = h->T * (h->Hq / h->Hkv);
   a.n_qg = (R + rows - 1) / rows;
   a.items = batch * h->Hkv * a.n_qg;
   const int kstep = kstep_of(h->dt);
-  const int max_keys = h->Pmax + h->T;
+  const int max_keys = span + h->T;
   int ns = (kTargetBlocks + a.items - 1) / a.items;
   const int max_ns = (max_keys + 63) / 64;
   if (ns > max_ns) ns = max_ns;
@@ -194,11 +210,20 @@ AttnPlan plan_attention(const ae_handle* h, int batch, int rows, int max_splits 
 }
 
 // The batched attention kernel's plan.
-AttnPlan plan_attention_batched(const ae_handle* h, int batch) {
+AttnPlan plan_attention_batched(const ae_handle* h, int batch, int span) {
   const int rows = attention_rows_per_item();
   const int R = h->T * (h->Hq / h->Hkv);
   const int items = batch * h->Hkv * ((R + rows - 1) / rows);
-  return plan_attention(h, batch, rows, attention_max_splits(items));
+  return plan_attention(h, batch, span, rows, attention_max_splits(items));
+}
+
+// Largest key split count a plan can choose for `items` items at any span
+// up to the capacity (sizes the partial scratch for every bucket).
+int max_attention_splits(const ae_handle* h, int items, int max_splits) {
+  int ns = (kTargetBlocks + items - 1) / items;
+  ns = std::min(ns, (h->Pmax + h->T + 63) / 64);
+  ns = std::min(ns, max_splits);
+  return std::max(ns, 1);
 }
 
 // The projection GEMMs of one layer: qkv, o, gate/up, down.
@@ -341,7 +366,7 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
   const int D = h->D, L = h->L, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const LayerPlans lp = plan_layer(h, M);
-  const AttnPlan ap = plan_attention_batched(h, batch);
+  const AttnPlan ap = plan_attention_batched(h, batch, h->span);
   const float dt = -1.0f / static_cast<float>(steps);
   for (int k = 0; k < steps; ++k) {
     AE_LAUNCH(launch_action_in(h->x, M, h->A, h->w_in, h->b_in, h->h, D, h->ssq, h->Mmax, s));
@@ -402,7 +427,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
   const int D = h->D, L = h->L, F = h->F, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const TPlans tp = plan_tlayer(h, M);
-  const AttnPlan ap = plan_attention_batched(h, batch);
+  const AttnPlan ap = plan_attention_batched(h, batch, h->span);
   const float dt = -1.0f / static_cast<float>(steps);
   const float eps = h->cfg.rms_eps;
   const bool f8 = h->fp8;
@@ -537,16 +562,36 @@ PersistArgs persist_args(const ae_handle* h, int batch, int steps) {
   a.pcnt = h->pcnt;
   const PersistPlans pp = plan_persist(h);
   a.pq = pp.q; a.po = pp.o; a.pg = pp.g; a.pd = pp.d;
-  const AttnPlan ap = plan_attention(h, batch, kTileM);
+  const AttnPlan ap = plan_attention(h, batch, h->span, kTileM);
   a.n_qg = ap.n_qg; a.nsplit = ap.nsplit; a.kc_len = ap.kc_len;
   a.n_acnt = ap.items;
   a.acnt = h->pcnt + pp.q.n_tiles + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
   return a;
 }
 
+void destroy_entry(GraphEntry& g) {
+  if (g.exec) (void)hipGraphExecDestroy(g.exec);
+  if (g.done) (void)hipEventDestroy(g.done);
+  g = GraphEntry{};
+}
+
+// Destroy the evicted graphs whose last replay has completed (a non-blocking
+// event query each).
+void reap_retired(ae_handle* h) {
+  std::vector<GraphEntry> keep;
+  for (auto& g : h->retired) {
+    if (!g.done || hipEventQuery(g.done) == hipSuccess) destroy_entry(g);
+    else keep.push_back(g);
+  }
+  (void)hipGetLastError();
+  h->retired.swap(keep);
+}
+
+// Every graph, cached or retired (the caller has synchronised the device).
 void drop_graphs(ae_handle* h) {
-  for (auto& kv : h->graphs) (void)hipGraphExecDestroy(kv.second);
-  h->graphs.clear();
+  for (auto& g : h->graphs.drain()) destroy_entry(g);
+  for (auto& g : h->retired) destroy_entry(g);
+  h->retired.clear();
 }
 
 struct WeightSpec {
@@ -605,13 +650,17 @@ const char* ae_last_error(const ae_handle* h) { return h ? h->err.c_str() : "nul
 ae_status ae_get_stats(const ae_handle* h, ae_stats* out) {
   if (!h || !out) return AE_ERR_INVALID_ARGUMENT;
   *out = h->stats;
-  int derr = 0;
-  if (h->derr && hipMemcpy(&derr, h->derr, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) {
+  // launches whose waits timed out: the running count the counter fill
+  // keeps, plus the last launch's flag if it is raised
+  int derr[2] = {0, 0};
+  if (h->derr && hipMemcpy(derr, h->derr, sizeof(derr), hipMemcpyDeviceToHost) != hipSuccess) {
     (void)hipGetLastError();
-    derr = -1;
+    derr[0] = -1;
   }
-  out->device_errors = derr;
+  out->device_errors = derr[0] < 0 ? -1 : derr[1] + (derr[0] != 0);
   out->persistent = h->G > 0 ? h->G : 0;
+  out->graphs_cached = h->graphs.size();
+  out->prefix_bucket = h->span;
   return AE_OK;
 }
 
@@ -654,6 +703,8 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   h->L = cfg->n_layers; h->D = cfg->width; h->Hq = cfg->n_q_heads; h->Hkv = cfg->n_kv_heads;
   h->dh = cfg->head_dim; h->F = cfg->mlp_dim; h->T = cfg->action_horizon; h->A = cfg->action_dim;
   h->Pmax = cfg->max_prefix_len; h->Bmax = cfg->max_batch; h->Nmax = cfg->max_steps;
+  h->span = h->Pmax;
+  h->graphs = LruCache<CallKey, GraphEntry>(cfg->use_graphs ? cfg->graph_cache_size : 0);
   h->S_max = (h->Pmax + h->T + 63) / 64 * 64;
   h->qdim = h->Hq * h->dh;
   h->kvdim = h->Hkv * h->dh;
@@ -756,13 +807,16 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
         gcn = std::max(gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
       }
     }
+    // (split counts bounded over every prefix bucket)
     const int rows = attention_rows_per_item();
-    const AttnPlan ap = plan_attention_batched(h, b);
-    if (ap.nsplit > 1) afl = std::max(afl, attention_partial_floats(h->dh, ap.items, ap.nsplit, rows));
+    const AttnPlan ap = plan_attention_batched(h, b, h->Pmax);
+    const int ns = max_attention_splits(h, ap.items, attention_max_splits(ap.items));
+    if (ns > 1) afl = std::max(afl, attention_partial_floats(h->dh, ap.items, ns, rows));
     acn = std::max(acn, static_cast<size_t>(ap.items));
     if (h->G > 0 && b * h->T <= kTileM) {  // the whole-call kernel's attention scratch
-      const AttnPlan pa = plan_attention(h, b, kTileM);
-      if (pa.nsplit > 1) afl = std::max(afl, attention_partial_floats(h->dh, pa.items, pa.nsplit, kTileM));
+      const AttnPlan pa = plan_attention(h, b, h->Pmax, kTileM);
+      const int nsp = max_attention_splits(h, pa.items, 1 << 30);
+      if (nsp > 1) afl = std::max(afl, attention_partial_floats(h->dh, pa.items, nsp, kTileM));
     }
   }
   if (h->G > 0) {
@@ -782,12 +836,13 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
       const PersistPlans pp = plan_persist(h);
       n = static_cast<size_t>(pp.q.n_tiles) + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
       int items = 0;
-      for (int b = 1; b <= h->Bmax && b * h->T <= kTileM; ++b) items = std::max(items, plan_attention(h, b, kTileM).items);
+      for (int b = 1; b <= h->Bmax && b * h->T <= kTileM; ++b)
+        items = std::max(items, plan_attention(h, b, h->Pmax, kTileM).items);
       n += items;
     }
     AE_ALLOC(h->pcnt, n * 4);
   }
-  AE_ALLOC(h->derr, 4);
+  AE_ALLOC(h->derr, 8);
   AE_ALLOC(h->genp, 4);
   AE_ALLOC(h->gpart, gfl * 4);
   AE_ALLOC(h->gcnt, gcn * 4);
@@ -853,7 +908,8 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
   auto cp = [&](void* dst, const std::string& nm, size_t bytes) {
     return hipMemcpyAsync(dst, get(nm), bytes, hipMemcpyDeviceToDevice, st);
   };
-  drop_graphs(h);
+  // (captured graphs stay valid: they read the packed buffers by address,
+  // and the time-path table is rebuilt on the next call)
   h->weights_loaded = false;
   h->table_steps = -1;
   AE_HIP(h, cp(h->tw1, "time_mlp.1.w", D * D * es));
@@ -925,12 +981,27 @@ ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* 
   if (prefix_len > 0 && (!K || !V || !valid_mask))
     return fail(h, AE_ERR_INVALID_ARGUMENT, "null K, V or valid_mask");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // the smallest bucket holding the prefix: its rows past prefix_len count
+  // as padding (mask 0), and the calls plan their key splits for it
+  const int span = pick_bucket(h->buckets, prefix_len, h->Pmax);
+  h->prefix_batch = -1;  // (a failed launch leaves no usable prefix)
   AE_HIP(h, launch_prefix_scan(valid_mask, batch, prefix_len, h->comp_idx, h->n_valid, h->T, h->dh,
                                h->cfg.rope_theta, h->rope_cos, h->rope_sin, st));
   AE_HIP(h, launch_prefix_copy(h->dt, K, V, h->comp_idx, h->n_valid, h->T, h->L, batch, prefix_len,
                                h->Hkv, h->dh, h->Bmax, h->S_max, h->kcache, h->vtcache, st));
   h->prefix_batch = batch;
+  h->span = span;
   h->stats.prefix_sets++;
+  return AE_OK;
+}
+
+ae_status ae_set_prefix_buckets(ae_handle* h, const int* lengths, int n) {
+  if (!h) return AE_ERR_INVALID_ARGUMENT;
+  if (!valid_buckets(lengths, n, h->Pmax, kMaxBuckets))
+    return fail(h, AE_ERR_INVALID_ARGUMENT,
+                "prefix buckets must be at most " + std::to_string(kMaxBuckets) +
+                    " strictly increasing lengths in [1, max_prefix_len = " + std::to_string(h->Pmax) + "]");
+  h->buckets.assign(lengths, lengths + n);
   return AE_OK;
 }
 
@@ -966,28 +1037,42 @@ ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, flo
     return enqueue_loop(h, batch, steps, s);
   };
   bool ran = false;
-  if (h->cfg.use_graphs && !(persist && !h->persist_graph)) {
-    const auto key = std::make_pair(batch, steps);
-    auto it = h->graphs.find(key);
-    if (it == h->graphs.end() && static_cast<int>(h->graphs.size()) < kMaxGraphs) {
-      AE_HIP(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeRelaxed));
-      ae_status s = enqueue(h->cap_stream);
-      hipGraph_t graph = nullptr;
-      hipError_t e = hipStreamEndCapture(h->cap_stream, &graph);
-      hipGraphExec_t exec = nullptr;
-      if (s == AE_OK && e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-      if (graph) (void)hipGraphDestroy(graph);
-      if (s != AE_OK || e != hipSuccess) {
-        (void)hipGetLastError();
-        if (!persist) return s != AE_OK ? s : hip_fail(h, e, "graph capture");
-        h->persist_graph = false;  // cooperative launches not capturable here: launch directly
-      } else {
-        it = h->graphs.emplace(key, exec).first;
-        h->stats.graph_captures++;
+  reap_retired(h);
+  if (h->graphs.capacity() > 0 && !(persist && !h->persist_graph)) {
+    const CallKey key{batch, steps, h->span};
+    GraphEntry* ge = h->graphs.find(key);
+    if (ge) {
+      h->stats.graph_hits++;
+    } else {
+      h->stats.graph_misses++;
+      if (h->graphs.size() < h->graphs.capacity() || h->cfg.graph_cache_evict) {
+        AE_HIP(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeRelaxed));
+        ae_status s = enqueue(h->cap_stream);
+        hipGraph_t graph = nullptr;
+        hipError_t e = hipStreamEndCapture(h->cap_stream, &graph);
+        GraphEntry ne;
+        if (s == AE_OK && e == hipSuccess) e = hipGraphInstantiate(&ne.exec, graph, nullptr, nullptr, 0);
+        if (graph) (void)hipGraphDestroy(graph);
+        if (s == AE_OK && e == hipSuccess) e = hipEventCreateWithFlags(&ne.done, hipEventDisableTiming);
+        if (s != AE_OK || e != hipSuccess) {
+          (void)hipGetLastError();
+          destroy_entry(ne);
+          if (!persist) return s != AE_OK ? s : hip_fail(h, e, "graph capture");
+          h->persist_graph = false;  // cooperative launches not capturable here: launch directly
+        } else {
+          GraphEntry old;
+          if (h->graphs.insert(key, ne, &old)) {  // the least recently used graph made room
+            h->retired.push_back(old);
+            h->stats.graph_evictions++;
+          }
+          ge = h->graphs.find(key);
+          h->stats.graph_captures++;
+        }
       }
     }
-    if (it != h->graphs.end()) {
-      AE_HIP(h, hipGraphLaunch(it->second, st));
+    if (ge) {
+      AE_HIP(h, hipGraphLaunch(ge->exec, st));
+      AE_HIP(h, hipEventRecord(ge->done, st));
       h->stats.graph_replays++;
       ran = true;
     }
@@ -997,6 +1082,7 @@ ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, flo
     if (s != AE_OK) return s;
     h->stats.eager_runs++;
   }
+  if (persist) h->stats.persistent_calls++;
   AE_HIP(h, hipMemcpyAsync(actions_out, h->x, xbytes, hipMemcpyDeviceToDevice, st));
   h->stats.denoise_calls++;
   return AE_OK;
