@@ -56,7 +56,11 @@ the pages support):
 * fp8: OCP e4m3fn, round to nearest even, saturating at +-448; weights
   static per logical tensor (q, k, v, gate, up, down), activations dynamic per
   request; s = max(amax, 1e-12)/448, code = e4m3(x * (448/amax)) in fp32,
-  y = (codes_x . codes_w) * s_x * s_w.
+  y = (codes_x . codes_w) * s_x * s_w;
+* context preparation: each layer's context K/V = the context hidden states
+  times that layer's context K and V projections, K rotated at the row's
+  count position; the robot state enters through one linear layer as one
+  more visible row after the context rows.
 
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against closed forms, library routines, brute force or invariants; none is
@@ -354,3 +358,31 @@ def project_prefix_kv(hidden: np.ndarray, wk: np.ndarray, wv: np.ndarray, mask: 
         K[b] = apply_rope(k, cos, sin)
         V[b] = (hidden[b] @ wv).reshape(P, n_kv_heads, dh)
     return K, V
+
+
+def encode_state(state: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """The robot state's context row: one linear layer, state [B, S] ->
+    [B, Dc] (MolmoBot PR Part 2: the state is part of the context computed
+    once per query; the single linear layer is this build's reading)."""
+    return linear(np.asarray(state, dtype=F64), w, b)
+
+
+def prepare_prefix(hidden: np.ndarray, wk: np.ndarray, wv: np.ndarray, mask: np.ndarray,
+                   n_kv_heads: int, theta: float, state_hidden: Optional[np.ndarray] = None):
+    """The context K/V of one query, every layer at once (MolmoBot PR Part 2:
+    prepare_cross_context / precompute_kv, run once before the flow steps).
+
+    hidden [L, B, P, Dc], wk / wv [L, Dc, Hkv*dh], mask [B, P].  With
+    state_hidden [B, Dc] one more visible row follows the P context rows:
+    the state, projected by every layer like a context row and rotated at
+    its own position, the count of visible context rows.
+    Returns K, V [L, B, P(+1), Hkv, dh] and the mask [B, P(+1)]."""
+    hidden = np.asarray(hidden, dtype=F64)
+    mask = np.asarray(mask)
+    L, B, P, Dc = hidden.shape
+    if state_hidden is not None:
+        sh = np.asarray(state_hidden, dtype=F64)[None, :, None, :]
+        hidden = np.concatenate([hidden, np.broadcast_to(sh, (L, B, 1, Dc))], axis=2)
+        mask = np.concatenate([mask, np.ones((B, 1), mask.dtype)], axis=1)
+    KV = [project_prefix_kv(hidden[l], wk[l], wv[l], mask, n_kv_heads, theta) for l in range(L)]
+    return np.stack([k for k, _ in KV]), np.stack([v for _, v in KV]), mask

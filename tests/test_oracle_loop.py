@@ -13,6 +13,7 @@ invariants (MolmoBot PR "Correctness" table; LoongForge blog section 1).
   GPU parity tolerance, so the tolerance-level checks are not vacuous.
 """
 
+import cmath
 import math
 
 import numpy as np
@@ -452,3 +453,100 @@ def test_prefix_matters_at_full_size():
         K2, V2, _ = synth.make_prefix(w, mask=m, seed=99)
         b = E.denoise(x0, K2, V2, m, w.n_steps)
         assert np.abs(a - b).max() > 0.1, name
+
+
+# --------------------------------------------------------------------------
+# Context preparation (MolmoBot PR Part 2: prepare_cross_context /
+# precompute_kv, once per query)
+# --------------------------------------------------------------------------
+
+def _rotate_complex(vec, pos, theta):
+    """RoPE as a complex rotation: pair (x_j, x_{j+dh/2}) is the complex
+    number x_j + i x_{j+dh/2}, multiplied by exp(i pos theta^(-2j/dh))."""
+    dh = len(vec)
+    half = dh // 2
+    out = [0.0] * dh
+    for j in range(half):
+        z = complex(vec[j], vec[j + half]) * cmath.exp(1j * pos * theta ** (-2.0 * j / dh))
+        out[j], out[j + half] = z.real, z.imag
+    return out
+
+
+def test_project_prefix_kv_is_a_complex_rotation_at_count_positions():
+    """Each visible context row's key is its projection rotated by its count
+    position (the number of visible rows before it: pads do not advance
+    positions, LoongForge blog section 1); values are not rotated."""
+    rng = np.random.default_rng(5)
+    B, P, Dc, Hkv, dh, theta = 2, 9, 6, 2, 8, 10000.0
+    hidden = rng.standard_normal((B, P, Dc))
+    wk = rng.standard_normal((Dc, Hkv * dh))
+    wv = rng.standard_normal((Dc, Hkv * dh))
+    mask = np.array([[1, 1, 0, 1, 0, 0, 1, 1, 1], [0, 1, 1, 1, 1, 0, 1, 0, 1]], np.uint8)
+    K, V = O.project_prefix_kv(hidden, wk, wv, mask, Hkv, theta)
+    for b in range(B):
+        pos = 0
+        for r in range(P):
+            kr = [sum(hidden[b, r, c] * wk[c, j] for c in range(Dc)) for j in range(Hkv * dh)]
+            vr = [sum(hidden[b, r, c] * wv[c, j] for c in range(Dc)) for j in range(Hkv * dh)]
+            for g in range(Hkv):
+                want = _rotate_complex(kr[g * dh:(g + 1) * dh], pos, theta)
+                assert np.allclose(K[b, r, g], want, rtol=0, atol=1e-12)
+                assert np.allclose(V[b, r, g], vr[g * dh:(g + 1) * dh], rtol=0, atol=1e-12)
+            pos += int(mask[b, r] != 0)
+
+
+def test_prepare_prefix_appends_the_state_row():
+    """With a robot state, one more visible row follows the context rows:
+    its hidden state is the state through one linear layer (checked by
+    loops), its key is rotated at the count of visible context rows."""
+    rng = np.random.default_rng(6)
+    L, B, P, Dc, Hkv, dh, S, theta = 2, 2, 7, 5, 1, 4, 3, 10000.0
+    hidden = rng.standard_normal((L, B, P, Dc))
+    wk = rng.standard_normal((L, Dc, Hkv * dh))
+    wv = rng.standard_normal((L, Dc, Hkv * dh))
+    ws, bs = rng.standard_normal((S, Dc)), rng.standard_normal(Dc)
+    state = rng.standard_normal((B, S))
+    mask = np.array([[1, 1, 1, 0, 1, 0, 0], [1, 0, 1, 1, 1, 1, 0]], np.uint8)
+    hs = O.encode_state(state, ws, bs)
+    for b in range(B):
+        for c in range(Dc):
+            assert abs(hs[b, c] - (sum(state[b, i] * ws[i, c] for i in range(S)) + bs[c])) < 1e-12
+    K, V, m2 = O.prepare_prefix(hidden, wk, wv, mask, Hkv, theta, state_hidden=hs)
+    assert K.shape == (L, B, P + 1, Hkv, dh) and m2.shape == (B, P + 1)
+    assert np.array_equal(m2[:, :P], mask) and np.all(m2[:, P] == 1)
+    for l in range(L):
+        k0, v0 = O.project_prefix_kv(hidden[l], wk[l], wv[l], mask, Hkv, theta)
+        assert np.array_equal(K[l, :, :P], k0) and np.array_equal(V[l, :, :P], v0)
+        for b in range(B):
+            kr = [sum(hs[b, c] * wk[l, c, j] for c in range(Dc)) for j in range(dh)]
+            want = _rotate_complex(kr, int(mask[b].sum()), theta)
+            assert np.allclose(K[l, b, P, 0], want, rtol=0, atol=1e-12)
+
+
+def test_prepared_context_once_equals_every_step():
+    """Context (and state) projected once per query == re-projected on every
+    flow step (MolmoBot PR Part 2 / Correctness table), bitwise."""
+    w = synth.workload("c1", n_layers=2, n_steps=3)
+    W = synth.make_weights(w)
+    Dc, S = 48, 14
+    CW = synth.make_context_weights(w, Dc, S)
+    H, m = synth.make_context(w, Dc)
+    m[0, 7] = 0
+    st = synth.make_state(w, S)
+    wk = np.stack([CW[f"layers.{l}.ctx_k"] for l in range(w.n_layers)])
+    wv = np.stack([CW[f"layers.{l}.ctx_v"] for l in range(w.n_layers)])
+    hs = O.encode_state(st, CW["state_in.w"], CW["state_in.b"])
+    K, V, m2 = O.prepare_prefix(H, wk, wv, m, w.n_kv_heads, w.rope_theta, hs)
+    x0 = synth.make_noise(w)
+    E = O.Expert(W, O.Params.like(w))
+    once = E.denoise(x0, K, V, m2, w.n_steps)
+
+    def reproject(l, b):
+        hsl = O.encode_state(st, CW["state_in.w"], CW["state_in.b"])
+        k, v, mm = O.prepare_prefix(H[l:l + 1], wk[l:l + 1], wv[l:l + 1], m, w.n_kv_heads, w.rope_theta, hsl)
+        idx = np.nonzero(mm[b])[0]
+        return k[0, b, idx], v[0, b, idx]
+
+    every = E.integrate(x0, reproject, m2.sum(1), w.n_steps)
+    assert np.array_equal(once, every)
+    assert np.abs(once - E.denoise(x0, K[:, :, :-1], V[:, :, :-1], m, w.n_steps)).max() > 1e-3  # the state row counts

@@ -22,7 +22,8 @@ Workloads (shapes from the pages' models):
   valid; bf16 or fp8 e4m3 projection weights.
 
 Seeds for workload ``cN``: weights 100N+1, prefix K/V 100N+2, noise 100N+3,
-valid lengths 100N+4, garbage in masked rows 100N+5.
+valid lengths 100N+4, garbage in masked rows 100N+5, context hidden states
+100N+6, robot state 100N+7.
 """
 
 from __future__ import annotations
@@ -263,6 +264,65 @@ def fill_garbage(w: Workload, K: np.ndarray, V: np.ndarray, mask: np.ndarray,
             X[:, sel] = g
         else:
             raise ValueError(kind)
+
+
+# ----------------------------------------------------------------------------
+# Context preparation inputs: per-layer context hidden states, the robot
+# state, and the context K/V / state projections (MolmoBot PR Part 2: the
+# VLM's hidden states and the state are turned into the expert's context
+# K/V once per query)
+# ----------------------------------------------------------------------------
+
+def context_weight_shapes(w: Workload, context_width: int, state_dim: int) -> Dict[str, Tuple[int, ...]]:
+    kd = w.n_kv_heads * w.head_dim
+    shapes: Dict[str, Tuple[int, ...]] = {}
+    for l in range(w.n_layers):
+        shapes[f"layers.{l}.ctx_k"] = (context_width, kd)
+        shapes[f"layers.{l}.ctx_v"] = (context_width, kd)
+    if state_dim:
+        shapes["state_in.w"] = (state_dim, context_width)
+        shapes["state_in.b"] = (context_width,)
+    return shapes
+
+
+def make_context_weights(w: Workload, context_width: int, state_dim: int = 0,
+                         std: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Context K/V projections (and the state's input layer) ~ N(0, std^2),
+    std = 1/sqrt(context_width) by default so projected keys and values have
+    unit scale like the prefix K/V of the other workloads; drawn from the
+    weight seed's streams (seed, 10000 + i), encoded in the workload dtype."""
+    base = w.seed(1)
+    sd = (1.0 / np.sqrt(context_width)) if std is None else std
+    out = {}
+    for i, (name, shape) in enumerate(context_weight_shapes(w, context_width, state_dim).items()):
+        x = _normal((base, 10000 + i), shape, sd)
+        out[name] = _encode(x, w.dtype)
+    return out
+
+
+def make_context(w: Workload, context_width: int, mask: Optional[np.ndarray] = None,
+                 seed: Optional[int] = None, garbage: Optional[str] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-layer context hidden states [L, B, P, Dc] ~ N(0, 1) in the workload
+    dtype (layer l from stream (seed, l)), and the mask.  ``garbage="nan"``
+    fills the masked rows with NaN."""
+    if mask is None:
+        mask = valid_masks(w)
+    base = w.seed(6) if seed is None else seed
+    shape = (w.batch, w.prefix_len, context_width)
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        parts = list(ex.map(lambda l: _encode(_normal((base, l), shape), w.dtype), range(w.n_layers)))
+    H = np.stack(parts)
+    if garbage == "nan":
+        H[:, mask == 0] = np.nan
+    elif garbage is not None:
+        raise ValueError(garbage)
+    return H, mask
+
+
+def make_state(w: Workload, state_dim: int, seed: Optional[int] = None) -> np.ndarray:
+    """Robot state [B, S] ~ N(0, 1), fp32."""
+    rng = np.random.default_rng(w.seed(7) if seed is None else seed)
+    return rng.standard_normal((w.batch, state_dim), dtype=np.float32)
 
 
 def make_noise(w: Workload, seed: Optional[int] = None) -> np.ndarray:
