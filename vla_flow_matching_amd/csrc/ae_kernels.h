@@ -98,6 +98,8 @@ int attention_rows_per_item();
 int attention_max_splits(int items);
 
 hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s);
+// p[0 .. n) = 0 with a kernel (a fill a captured graph can hold)
+hipError_t launch_zero_ints(int* p, size_t n, hipStream_t s);
 // out[k][l][n] = sum_d mod[k][l][which][d] * W_l[d][n] for packed weights
 // (n in packed column order), steps k < n_steps, layers l < L.
 hipError_t launch_shift_bias(Dt dt, const uint4* W, size_t layer_stride, int K, int N, const float* mod,
@@ -117,9 +119,17 @@ hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, cons
                              const float* shift, float eps, const float* w_out,
                              const float* b_out, float dt, hipStream_t s);
 
+// (extra: visible rows that follow the P mask rows, e.g. the robot state's:
+// they count into n_valid)
 hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_idx, int* n_valid,
                               int T, int dh, float theta, float* rope_cos, float* rope_sin,
-                              hipStream_t s);
+                              hipStream_t s, int extra = 0);
+// cos / sin of RoPE at positions 0 .. n_pos - 1: [n_pos][dh / 2] fp32 (double math)
+hipError_t launch_pos_table(int n_pos, int dh, float theta, float* cos_t, float* sin_t, hipStream_t s);
+// The robot state's context row: out[b] = bf16(state[b] . W + bias) ([S] x [S][D]
+// bf16 + [D] bf16), and its key, key_out[b] = n_valid[b] - 1 (the last visible row).
+hipError_t launch_state_prep(const float* state, int batch, int S, const uint16_t* w, const uint16_t* bias,
+                             int D, const int* n_valid, uint16_t* out, int* key_out, hipStream_t s);
 hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx,
                               const int* n_valid, int n_act, int L, int batch, int P, int Hkv, int dh,
                               int Bmax, int S_max, void* kcache, void* vtcache, hipStream_t s);
@@ -177,6 +187,12 @@ struct TGemmArgs {
   const float* rope_cos;
   const float* rope_sin;
   int T, Hq, Hkv, dh, S_max;
+  // EPI_QKV on context rows (key_map set): row m of request m / T goes to
+  // cache key key_map[m] (< 0: not stored), its K rotated at that position
+  // with pos_cos / pos_sin [position][dh / 2]
+  const int* key_map;
+  const float* pos_cos;
+  const float* pos_sin;
   // bf16 norm after the product (A = bf16(h (1 + scale))): EPI_QKV / EPI_GELU
   // finish with y = r_row acc + bias[col], r_row from the row sums of squares
   // ssq[ssq_tiles][ldssq] (64-column partials over K columns); EPI_RESID
@@ -250,7 +266,7 @@ struct PersistArgs {
   int* pcnt;   // monotonic split counters: q, o, gate/up, down tiles, then attention items
   int n_acnt;  // attention items
   int* flags;  // [G] barrier generations
-  uint32_t* genp;  // generation base of the split-K packets (one word)
+  uint32_t* genp;  // [2] split-K packet generation base: next launch's, this launch's
   int* err;    // [2]: this launch's error flag (a wait timed out), launches that raised it
   PGemm pq, po, pg, pd;
   int n_qg, nsplit, kc_len;

@@ -3,6 +3,8 @@
 // and prefix ingest (once per query).
 #include <math.h>
 
+#include <algorithm>
+
 #include "ae_device.h"
 #include "ae_kernels.h"
 
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(256) void action_out_kernel(float* x, int A, const 
 
 __global__ __launch_bounds__(256) void prefix_scan_kernel(const uint8_t* mask, int P, int* comp_idx,
                                                           int* n_valid, int T, int dh, float theta,
-                                                          float* rope_cos, float* rope_sin) {
+                                                          float* rope_cos, float* rope_sin, int extra) {
   __shared__ int s_cnt[256];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(const uint8_t* mask, i
     comp_idx[static_cast<size_t>(b) * P + j] = vis ? run : -1;
     run += vis;
   }
-  const int nv = s_cnt[255];
+  const int nv = s_cnt[255] + extra;
   if (tid == 0) n_valid[b] = nv;
   const int half = dh / 2;
   for (int i = tid; i < T * half; i += 256) {
@@ -359,6 +361,21 @@ hipError_t launch_shift_bias(Dt dt, const uint4* W, size_t layer_stride, int K, 
   return hipGetLastError();
 }
 
+namespace {
+__global__ void zero_ints_kernel(int* p, size_t n) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_zero_ints(int* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int blocks = static_cast<int>(std::min<size_t>(64, (n + 255) / 256));
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s) {
   hipLaunchKernelGGL(tpath_sinusoid_kernel, dim3(n_steps), dim3(256), 0, s, e, n_steps, width);
   return hipGetLastError();
@@ -416,9 +433,55 @@ hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, cons
 
 hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_idx, int* n_valid,
                               int T, int dh, float theta, float* rope_cos, float* rope_sin,
-                              hipStream_t s) {
+                              hipStream_t s, int extra) {
   hipLaunchKernelGGL(prefix_scan_kernel, dim3(batch), dim3(256), 0, s, mask, P, comp_idx, n_valid,
-                     T, dh, theta, rope_cos, rope_sin);
+                     T, dh, theta, rope_cos, rope_sin, extra);
+  return hipGetLastError();
+}
+
+namespace {
+
+// cos / sin of RoPE at positions 0 .. n_pos - 1 (double math, fp32 table):
+// the count positions of context rows
+__global__ void pos_table_kernel(int n_pos, int dh, float theta, float* cos_t, float* sin_t) {
+  const int half = dh / 2;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_pos * half; i += gridDim.x * blockDim.x) {
+    const int pos = i / half, j = i % half;
+    const double w = pow(static_cast<double>(theta), -2.0 * j / dh);
+    const double ph = static_cast<double>(pos) * w;
+    cos_t[i] = static_cast<float>(cos(ph));
+    sin_t[i] = static_cast<float>(sin(ph));
+  }
+}
+
+// The robot state's context row (one workgroup per request): fp32 sums of
+// the state times the input layer, plus its bias, stored as bf16; its cache
+// key is the request's last visible position.
+__global__ __launch_bounds__(256) void state_prep_kernel(const float* state, int S, const bf16_t* w,
+                                                         const bf16_t* bias, int D, const int* n_valid,
+                                                         bf16_t* out, int* key_out) {
+  const int b = blockIdx.x;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float acc = bf2f(bias[c]);
+    for (int i = 0; i < S; ++i) acc = fmaf(state[static_cast<size_t>(b) * S + i], bf2f(w[static_cast<size_t>(i) * D + c]), acc);
+    out[static_cast<size_t>(b) * D + c] = f2bf(acc);
+  }
+  if (threadIdx.x == 0) key_out[b] = n_valid[b] - 1;
+}
+
+}  // namespace
+
+hipError_t launch_pos_table(int n_pos, int dh, float theta, float* cos_t, float* sin_t, hipStream_t s) {
+  if (n_pos < 1 || dh < 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pos_table_kernel, dim3(256), dim3(256), 0, s, n_pos, dh, theta, cos_t, sin_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_prep(const float* state, int batch, int S, const uint16_t* w, const uint16_t* bias,
+                             int D, const int* n_valid, uint16_t* out, int* key_out, hipStream_t s) {
+  if (batch < 1 || S < 1 || D < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(state_prep_kernel, dim3(batch), dim3(256), 0, s, state, S, w, bias, D, n_valid, out,
+                     key_out);
   return hipGetLastError();
 }
 

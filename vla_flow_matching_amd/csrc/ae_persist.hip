@@ -1068,9 +1068,9 @@ template <typename T, int DH>
 __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs) {
   // gemm: 64 KiB reduction / tile + rms scratch; out/in: smaller
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<T, DH>()];
-  // generation base of this launch's split-K packets (advanced by the
-  // counter fill that precedes every launch)
-  const uint32_t gbase = __builtin_amdgcn_readfirstlane(*kargs().genp);
+  // generation base of this launch's split-K packets (set by the counter
+  // fill that precedes every launch)
+  const uint32_t gbase = __builtin_amdgcn_readfirstlane(kargs().genp[1]);
   int gen = 0;
   outin_phase<T>(kargs(), 0, false, true, 0, smem);  // h from x_0
   bar_arrive(kargs(), ++gen);
@@ -1158,7 +1158,12 @@ __global__ void fill_int_kernel(PersistArgs args, uint32_t stride) {
     else args.pcnt[i - na] = 0;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    args.genp[0] += stride;
+    // this launch's base is the end of the previous launch's range
+    // (genp[0]); the next launch starts past every generation this one can
+    // use, whatever either one's layer count
+    const uint32_t base = args.genp[0];
+    args.genp[1] = base;
+    args.genp[0] = base + stride;
     // err[0] is this launch's flag; a flag the previous launch raised is
     // counted into err[1] and cleared, so one timed-out barrier does not
     // disarm the waits of every later launch
@@ -1190,10 +1195,9 @@ int persist_blocks_per_cu(Dt dt, int dh) {
 hipError_t launch_persist(Dt dt, const PersistArgs& a, hipStream_t s) {
   if (a.G < 1 || a.G > kMaxG) return hipErrorInvalidValue;
   const int n_cnt = a.pq.n_tiles + a.po.n_tiles + a.pg.n_tiles + a.pd.n_tiles;
-  // every launch of a handle advances by the range the longest launch can
-  // use (8 generations per layer step, at most kMaxSteps steps), so no two
-  // launches ever share a generation
-  const uint32_t stride = 8u * static_cast<uint32_t>(kMaxSteps * a.L) + 8u;
+  // a launch takes the next range of generations (8 per layer step), so no
+  // two launches ever share one
+  const uint32_t stride = 8u * static_cast<uint32_t>(a.n_steps * a.L) + 8u;
   (void)n_cnt;
   hipLaunchKernelGGL(fill_int_kernel, dim3(4), dim3(256), 0, s, a, stride);
   hipError_t e = hipGetLastError();

@@ -46,6 +46,29 @@ struct Buf {
   size_t bytes = 0;
 };
 
+// The transient device memory a denoise call's kernels work in: split-K
+// partials and counters, attention key-split partials and counters, and the
+// whole-call kernel's barrier flags, split counters and packet generation
+// base.  A handle owns one set sized for its largest call.
+struct ScratchSet {
+  float* gpart = nullptr;   // split-K partials ((value, generation) packets in the whole-call kernel)
+  int* gcnt = nullptr;      // per-tile split counters (self-resetting)
+  float* apart = nullptr;   // attention key-split partials
+  int* acnt = nullptr;      // per-item split counters (self-resetting)
+  int* flags = nullptr;     // whole-call kernel: barrier generation per workgroup
+  int* pcnt = nullptr;      // whole-call kernel: monotonic split counters
+  uint32_t* genp = nullptr; // whole-call kernel: [2] next / current packet generation base
+};
+
+// Element counts of a scratch set's parts.
+struct ScratchNeed {
+  size_t gfl = 0, gcn = 0, afl = 0, acn = 0, flags = 1, pcnt = 1;
+  void max_with(const ScratchNeed& o) {
+    gfl = std::max(gfl, o.gfl); gcn = std::max(gcn, o.gcn); afl = std::max(afl, o.afl);
+    acn = std::max(acn, o.acn); flags = std::max(flags, o.flags); pcnt = std::max(pcnt, o.pcnt);
+  }
+};
+
 }  // namespace
 
 struct ae_handle {
@@ -76,9 +99,8 @@ struct ae_handle {
   void* ha = nullptr;
   float *bq = nullptr, *bg = nullptr;
 
-  // split scratch
-  float *gpart = nullptr, *apart = nullptr;
-  int *gcnt = nullptr, *acnt = nullptr;
+  // split scratch of this handle's calls
+  ScratchSet own;
 
   // batched tiled path: bf16, or fp8 e4m3 QKV / gate-up / down projections
   bool tiled = false;
@@ -91,10 +113,9 @@ struct ae_handle {
   // persistent whole-call kernel (batch * T <= 64)
   uint4 *win_p = nullptr, *wout_p = nullptr;
   int a_frags = 0, a_blocks = 0;
-  int *flags = nullptr, *derr = nullptr;
-  int* pcnt = nullptr;  // the persistent kernel's monotonic split counters
-  uint32_t* genp = nullptr;  // its split-K packet generation base
+  int* derr = nullptr;  // [2] the whole-call kernel's error flag and count
   int G = 0;              // resident workgroups of the persistent kernel (0: unavailable)
+  int device = 0;         // the device the handle was created on
   bool persist_graph = true;  // cooperative launch can be captured
 
   bool weights_loaded = false;
@@ -293,12 +314,12 @@ TPlans plan_tlayer(const ae_handle* h, int M) {
   return p;
 }
 
-TGemmArgs base_tgemm(const ae_handle* h, const TGemmPlan& g, int M, int N, int K) {
+TGemmArgs base_tgemm(const ae_handle* h, const ScratchSet& sc, const TGemmPlan& g, int M, int N, int K) {
   TGemmArgs a;
   std::memset(&a, 0, sizeof(a));
   a.M = M; a.N = N; a.K = K;
   a.n_tiles = g.n_tiles; a.m_tiles = g.m_tiles; a.ksplit = g.ksplit; a.bm = g.bm;
-  a.partial = h->gpart; a.counters = h->gcnt;
+  a.partial = sc.gpart; a.counters = sc.gcnt;
   a.sx_row = h->sxrow;
   return a;
 }
@@ -307,7 +328,7 @@ size_t gemm_scratch_floats(const GemmPlan& g) {
   return g.ksplit > 1 ? static_cast<size_t>(g.m_tiles) * g.n_tiles * g.ksplit * kTileM * kTileN : 0;
 }
 
-GemmArgs base_gemm(const ae_handle* h, const GemmPlan& g, int M, int K) {
+GemmArgs base_gemm(const ae_handle* h, const ScratchSet& sc, const GemmPlan& g, int M, int K) {
   GemmArgs a;
   std::memset(&a, 0, sizeof(a));
   a.M = M;
@@ -316,8 +337,8 @@ GemmArgs base_gemm(const ae_handle* h, const GemmPlan& g, int M, int K) {
   a.m_tiles = g.m_tiles;
   a.k_frags = g.k_frags;
   a.ksplit = g.ksplit;
-  a.partial = h->gpart;
-  a.counters = h->gcnt;
+  a.partial = sc.gpart;
+  a.counters = sc.gcnt;
   a.ssq_tiles = h->ssq_tiles;
   a.ldssq = h->Mmax;
   a.eps = h->cfg.rms_eps;
@@ -359,10 +380,10 @@ ae_status enqueue_tpath(ae_handle* h, int steps, hipStream_t s) {
 
 // Enqueue the N Euler steps of one denoise call, reading and writing the
 // static buffers; used both directly and under stream capture.
-ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s);
+ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int steps, hipStream_t s);
 
-ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
-  if (h->tiled) return enqueue_loop_tiled(h, batch, steps, s);
+ae_status enqueue_loop(ae_handle* h, const ScratchSet& sc, int batch, int steps, hipStream_t s) {
+  if (h->tiled) return enqueue_loop_tiled(h, sc, batch, steps, s);
   const int D = h->D, L = h->L, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const LayerPlans lp = plan_layer(h, M);
@@ -375,7 +396,7 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
       char* kc = static_cast<char*>(h->kcache) + l * kv_layer;
       char* vc = static_cast<char*>(h->vtcache) + l * kv_layer;
 
-      GemmArgs g = base_gemm(h, lp.qkv, M, D);
+      GemmArgs g = base_gemm(h, sc, lp.qkv, M, D);
       g.A = h->h; g.lda = D; g.W = h->wqkv + l * h->sqkv;
       g.ssq = h->ssq; g.scale = md; g.shift = md + D;
       g.q = h->q; g.ldq = h->qdim; g.kcache = kc; g.vtcache = vc; g.n_valid = h->n_valid;
@@ -390,21 +411,21 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
       at.T = h->T; at.Hq = h->Hq; at.Hkv = h->Hkv; at.dh = h->dh;
       at.batch = batch; at.n_qg = ap.n_qg; at.nsplit = ap.nsplit; at.kc_len = ap.kc_len;
       at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->dh)));
-      at.partial = h->apart; at.counters = h->acnt;
+      at.partial = sc.apart; at.counters = sc.acnt;
       AE_LAUNCH(launch_attention(h->dt, at, s));
 
-      g = base_gemm(h, lp.o, M, h->qdim);
+      g = base_gemm(h, sc, lp.o, M, h->qdim);
       g.A = h->o; g.lda = h->qdim; g.W = h->wo + l * h->so;
       g.h = h->h; g.ldh = D; g.gate = md + 2 * D; g.ssq_out = h->ssq;
       AE_LAUNCH(launch_gemm(h->dt, PRO_NONE, EPI_RESID, g, lp.o.blocks, s));
 
-      g = base_gemm(h, lp.gu, M, D);
+      g = base_gemm(h, sc, lp.gu, M, D);
       g.A = h->h; g.lda = D; g.W = h->wgu + l * h->sgu;
       g.ssq = h->ssq; g.scale = md + 3 * D; g.shift = md + 4 * D;
       g.out = h->act; g.ldo = h->F;
       AE_LAUNCH(launch_gemm(h->dt, PRO_ADARMS, EPI_GELU, g, lp.gu.blocks, s));
 
-      g = base_gemm(h, lp.d, M, h->F);
+      g = base_gemm(h, sc, lp.d, M, h->F);
       g.A = h->act; g.lda = h->F; g.W = h->wd + l * h->sd;
       g.h = h->h; g.ldh = D; g.gate = md + 5 * D; g.ssq_out = h->ssq;
       AE_LAUNCH(launch_gemm(h->dt, PRO_NONE, EPI_RESID, g, lp.d.blocks, s));
@@ -423,7 +444,7 @@ ae_status enqueue_loop(ae_handle* h, int batch, int steps, hipStream_t s) {
 // product: the residual epilogues (and action-in) write the shadow
 // ha = bf16(h (1 + scale)) of the next norm with h's row sums of squares, and
 // QKV / gate-up finish with 1 / rms and the precomputed shift W.
-ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) {
+ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int steps, hipStream_t s) {
   const int D = h->D, L = h->L, F = h->F, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const TPlans tp = plan_tlayer(h, M);
@@ -471,7 +492,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
         if (r != AE_OK) return r;
       }
 
-      TGemmArgs g = base_tgemm(h, tp.qkv, M, h->qkv_n, D);
+      TGemmArgs g = base_tgemm(h, sc, tp.qkv, M, h->qkv_n, D);
       g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wqkv + l * h->sqkv; g.sw = h->wsc + 6 * l;
       if (!f8) post_norm(g, h->bq + it * h->qkv_n);  // (bf16: A = the norm shadow)
       g.q = h->q; g.ldq = h->qdim; g.kcache = kc; g.vtcache = vc; g.n_valid = h->n_valid;
@@ -486,7 +507,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
       at.T = h->T; at.Hq = h->Hq; at.Hkv = h->Hkv; at.dh = h->dh;
       at.batch = batch; at.n_qg = ap.n_qg; at.nsplit = ap.nsplit; at.kc_len = ap.kc_len;
       at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->dh)));
-      at.partial = h->apart; at.counters = h->acnt;
+      at.partial = sc.apart; at.counters = sc.acnt;
       // warm the last-level cache with this layer's O / gate-up / down
       // weights and the next layer's QKV weights while attention runs
       at.pf_blocks = kPrefetchBlocks;
@@ -500,7 +521,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
       at.pf_n4[3] = static_cast<int>(static_cast<size_t>(D) * h->qkv_n * ob / 16);
       AE_LAUNCH(launch_attention(h->dt, at, s));
 
-      g = base_tgemm(h, tp.o, M, D, h->qdim);
+      g = base_tgemm(h, sc, tp.o, M, D, h->qdim);
       g.A = h->o; g.lda_bytes = static_cast<size_t>(h->qdim) * 2; g.W = h->wo + l * h->so;
       // the next layer's K cache of these requests into the last-level
       // cache on the CUs the O-proj tiles leave free (its V: beside down)
@@ -513,7 +534,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
         ae_status r = norm_rows(md + 3 * D, md + 4 * D);
         if (r != AE_OK) return r;
       }
-      g = base_tgemm(h, tp.gu, M, 2 * F, D);
+      g = base_tgemm(h, sc, tp.gu, M, 2 * F, D);
       g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wgu + l * h->sgu; g.sw = h->wsc + 6 * l + 3;
       g.out = h->act; g.ldo = F; g.rowmax = h->rowmax; g.ldp = h->Mmax;
       if (!f8) post_norm(g, h->bg + it * 2 * F);
@@ -522,7 +543,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
         AE_LAUNCH(launch_quant(static_cast<const float*>(h->act), nullptr, nullptr, nullptr, nullptr, M, F,
                                h->T, h->rowmax, tp.gu.n_tiles, h->Mmax, ub8, h->sxrow, s));
 
-      g = base_tgemm(h, tp.d, M, D, F);
+      g = base_tgemm(h, sc, tp.d, M, D, F);
       g.A = f8 ? h->ubuf : h->act; g.lda_bytes = F * ob; g.W = h->wd + l * h->sd;
       prefetch_cache(g, h->vtcache, (l + 1) % L, tp.d.blocks);
       g.sw = h->wsc + 6 * l + 5;
@@ -539,7 +560,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, int batch, int steps, hipStream_t s) 
   return AE_OK;
 }
 
-PersistArgs persist_args(const ae_handle* h, int batch, int steps) {
+PersistArgs persist_args(const ae_handle* h, const ScratchSet& sc, int batch, int steps) {
   PersistArgs a;
   std::memset(&a, 0, sizeof(a));
   a.M = batch * h->T; a.D = h->D; a.L = h->L; a.n_steps = steps; a.T = h->T; a.A = h->A;
@@ -557,16 +578,55 @@ PersistArgs persist_args(const ae_handle* h, int batch, int steps) {
   a.n_valid = h->n_valid; a.rope_cos = h->rope_cos; a.rope_sin = h->rope_sin;
   a.x = h->x; a.h = h->h; a.ssq = h->ssq; a.q = h->q; a.o = h->o; a.act = h->act;
   a.ha = h->ha; a.bq = h->bq; a.bg = h->bg; a.qkv_n = h->qkv_n;
-  a.gpart = h->gpart; a.gcnt = h->gcnt; a.apart = h->apart; a.acnt = h->acnt;
-  a.flags = h->flags; a.err = h->derr; a.genp = h->genp;
-  a.pcnt = h->pcnt;
+  a.gpart = sc.gpart; a.gcnt = sc.gcnt; a.apart = sc.apart;
+  a.flags = sc.flags; a.err = h->derr; a.genp = sc.genp;
+  a.pcnt = sc.pcnt;
   const PersistPlans pp = plan_persist(h);
   a.pq = pp.q; a.po = pp.o; a.pg = pp.g; a.pd = pp.d;
   const AttnPlan ap = plan_attention(h, batch, h->span, kTileM);
   a.n_qg = ap.n_qg; a.nsplit = ap.nsplit; a.kc_len = ap.kc_len;
   a.n_acnt = ap.items;
-  a.acnt = h->pcnt + pp.q.n_tiles + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
+  a.acnt = sc.pcnt + pp.q.n_tiles + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
   return a;
+}
+
+// The scratch a call at batch b and prefix span `span` needs on the
+// whole-call path (persist) or the per-phase path; any_span bounds the
+// attention's key splits over every span up to the capacity instead.
+ScratchNeed scratch_need(const ae_handle* h, int b, int span, bool persist, bool any_span) {
+  ScratchNeed n;
+  if (persist) {
+    const AttnPlan pa = plan_attention(h, b, span, kTileM);
+    const int nsp = any_span ? max_attention_splits(h, pa.items, 1 << 30) : pa.nsplit;
+    if (nsp > 1) n.afl = attention_partial_floats(h->dh, pa.items, nsp, kTileM);
+    const PersistPlans pp = plan_persist(h);
+    n.pcnt = pa.items;
+    for (const PGemm* g : {&pp.q, &pp.o, &pp.g, &pp.d}) {
+      if (g->ksplit > 1)  // (value, generation) packets: two words per value
+        n.gfl = std::max(n.gfl, 2 * static_cast<size_t>(g->n_tiles) * g->ksplit * kTileM * kTileN);
+      n.pcnt += g->n_tiles;
+    }
+    n.flags = static_cast<size_t>(h->G);
+    return n;
+  }
+  if (h->tiled) {
+    const TPlans tp = plan_tlayer(h, b * h->T);
+    for (const TGemmPlan* g : {&tp.qkv, &tp.o, &tp.gu, &tp.d}) {
+      n.gfl = std::max(n.gfl, tgemm_partial_floats(*g));
+      n.gcn = std::max(n.gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
+    }
+  } else {
+    const LayerPlans lp = plan_layer(h, b * h->T);
+    for (const GemmPlan* g : {&lp.qkv, &lp.o, &lp.gu, &lp.d}) {
+      n.gfl = std::max(n.gfl, gemm_scratch_floats(*g));
+      n.gcn = std::max(n.gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
+    }
+  }
+  const AttnPlan ap = plan_attention_batched(h, b, span);
+  const int ns = any_span ? max_attention_splits(h, ap.items, attention_max_splits(ap.items)) : ap.nsplit;
+  if (ns > 1) n.afl = attention_partial_floats(h->dh, ap.items, ns, attention_rows_per_item());
+  n.acn = static_cast<size_t>(ap.items);
+  return n;
 }
 
 void destroy_entry(GraphEntry& g) {
@@ -626,6 +686,31 @@ std::string shape_str(const long long* s, int n) {
   std::string r = "[";
   for (int i = 0; i < n; ++i) r += (i ? "," : "") + std::to_string(s[i]);
   return r + "]";
+}
+
+// The checks of ae_denoise (before any state change).
+ae_status check_denoise(ae_handle* h, const float* noise, int batch, int steps, const float* actions_out) {
+  if (!noise || !actions_out) return fail(h, AE_ERR_INVALID_ARGUMENT, "null noise or actions_out");
+  if (!h->weights_loaded) return fail(h, AE_ERR_NOT_READY, "weights not loaded");
+  if (h->prefix_batch < 0) return fail(h, AE_ERR_NOT_READY, "prefix K/V not set");
+  if (batch != h->prefix_batch)
+    return fail(h, AE_ERR_SHAPE_MISMATCH,
+                "batch " + std::to_string(batch) + " differs from the prefix batch " +
+                    std::to_string(h->prefix_batch));
+  if (steps < 1 || steps > h->Nmax)
+    return fail(h, AE_ERR_INVALID_ARGUMENT,
+                "steps " + std::to_string(steps) + " outside [1, " + std::to_string(h->Nmax) + "]");
+  return AE_OK;
+}
+
+// The time-path table for `steps`, rebuilt only when the step count changed.
+ae_status ensure_tpath(ae_handle* h, int steps, hipStream_t st) {
+  if (h->table_steps == steps) return AE_OK;
+  h->table_steps = -1;
+  ae_status s = enqueue_tpath(h, steps, st);
+  if (s != AE_OK) return s;
+  h->table_steps = steps;
+  return AE_OK;
 }
 
 }  // namespace
@@ -719,6 +804,7 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   {
     // the persistent kernel needs every workgroup resident at once
     int dev = 0, coop = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess) h->device = dev;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
@@ -793,61 +879,22 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   AE_ALLOC(h->mod, static_cast<size_t>(h->Nmax) * L * 6 * D * 4);
   AE_ALLOC(h->fmod, static_cast<size_t>(h->Nmax) * 2 * D * 4);
 
-  size_t gfl = 0, gcn = 0, afl = 0, acn = 0;
+  // the largest call's scratch, over every batch, path and prefix bucket
+  ScratchNeed need;
   for (int b = 1; b <= h->Bmax; ++b) {
-    const LayerPlans lp = plan_layer(h, b * h->T);
-    for (const GemmPlan* g : {&lp.qkv, &lp.o, &lp.gu, &lp.d}) {
-      gfl = std::max(gfl, gemm_scratch_floats(*g));
-      gcn = std::max(gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
-    }
-    if (h->tiled) {
-      const TPlans tp = plan_tlayer(h, b * h->T);
-      for (const TGemmPlan* g : {&tp.qkv, &tp.o, &tp.gu, &tp.d}) {
-        gfl = std::max(gfl, tgemm_partial_floats(*g));
-        gcn = std::max(gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
-      }
-    }
-    // (split counts bounded over every prefix bucket)
-    const int rows = attention_rows_per_item();
-    const AttnPlan ap = plan_attention_batched(h, b, h->Pmax);
-    const int ns = max_attention_splits(h, ap.items, attention_max_splits(ap.items));
-    if (ns > 1) afl = std::max(afl, attention_partial_floats(h->dh, ap.items, ns, rows));
-    acn = std::max(acn, static_cast<size_t>(ap.items));
-    if (h->G > 0 && b * h->T <= kTileM) {  // the whole-call kernel's attention scratch
-      const AttnPlan pa = plan_attention(h, b, h->Pmax, kTileM);
-      const int nsp = max_attention_splits(h, pa.items, 1 << 30);
-      if (nsp > 1) afl = std::max(afl, attention_partial_floats(h->dh, pa.items, nsp, kTileM));
-    }
-  }
-  if (h->G > 0) {
-    const PersistPlans pp = plan_persist(h);
-    for (const PGemm* g : {&pp.q, &pp.o, &pp.g, &pp.d}) {
-      if (g->ksplit > 1)  // (value, generation) packets: two words per value
-        gfl = std::max(gfl, 2 * static_cast<size_t>(g->n_tiles) * g->ksplit * kTileM * kTileN);
-      gcn = std::max(gcn, static_cast<size_t>(g->n_tiles));
-    }
+    need.max_with(scratch_need(h, b, h->Pmax, false, true));
+    if (h->G > 0 && b * h->T <= kTileM) need.max_with(scratch_need(h, b, h->Pmax, true, true));
   }
   AE_ALLOC(h->win_p, elems_packed(h->a_frags * ks, h->D, ks) * 16);
   AE_ALLOC(h->wout_p, elems_packed(h->D, 16 * h->a_blocks, ks) * 16);
-  AE_ALLOC(h->flags, static_cast<size_t>(h->G > 0 ? h->G : 1) * 4);
-  {
-    size_t n = 1;
-    if (h->G > 0) {
-      const PersistPlans pp = plan_persist(h);
-      n = static_cast<size_t>(pp.q.n_tiles) + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
-      int items = 0;
-      for (int b = 1; b <= h->Bmax && b * h->T <= kTileM; ++b)
-        items = std::max(items, plan_attention(h, b, h->Pmax, kTileM).items);
-      n += items;
-    }
-    AE_ALLOC(h->pcnt, n * 4);
-  }
+  AE_ALLOC(h->own.flags, need.flags * 4);
+  AE_ALLOC(h->own.pcnt, need.pcnt * 4);
   AE_ALLOC(h->derr, 8);
-  AE_ALLOC(h->genp, 4);
-  AE_ALLOC(h->gpart, gfl * 4);
-  AE_ALLOC(h->gcnt, gcn * 4);
-  AE_ALLOC(h->apart, afl * 4);
-  AE_ALLOC(h->acnt, acn * 4);
+  AE_ALLOC(h->own.genp, 8);
+  AE_ALLOC(h->own.gpart, need.gfl * 4);
+  AE_ALLOC(h->own.gcnt, need.gcn * 4);
+  AE_ALLOC(h->own.apart, need.afl * 4);
+  AE_ALLOC(h->own.acnt, need.acn * 4);
 #undef AE_ALLOC
 
   // zero everything once: counters must start at 0; caches and activations
@@ -1008,33 +1055,25 @@ ae_status ae_set_prefix_buckets(ae_handle* h, const int* lengths, int n) {
 ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, float* actions_out,
                      void* stream) {
   if (!h) return AE_ERR_INVALID_ARGUMENT;
-  if (!noise || !actions_out) return fail(h, AE_ERR_INVALID_ARGUMENT, "null noise or actions_out");
-  if (!h->weights_loaded) return fail(h, AE_ERR_NOT_READY, "weights not loaded");
-  if (h->prefix_batch < 0) return fail(h, AE_ERR_NOT_READY, "prefix K/V not set");
-  if (batch != h->prefix_batch)
-    return fail(h, AE_ERR_SHAPE_MISMATCH,
-                "batch " + std::to_string(batch) + " differs from the prefix batch " +
-                    std::to_string(h->prefix_batch));
-  if (steps < 1 || steps > h->Nmax)
-    return fail(h, AE_ERR_INVALID_ARGUMENT,
-                "steps " + std::to_string(steps) + " outside [1, " + std::to_string(h->Nmax) + "]");
+  {
+    const ae_status c = check_denoise(h, noise, batch, steps, actions_out);
+    if (c != AE_OK) return c;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t xbytes = static_cast<size_t>(batch) * h->T * h->A * 4;
-  if (h->table_steps != steps) {
-    h->table_steps = -1;
-    ae_status s = enqueue_tpath(h, steps, st);
-    if (s != AE_OK) return s;
-    h->table_steps = steps;
+  {
+    const ae_status t = ensure_tpath(h, steps, st);
+    if (t != AE_OK) return t;
   }
   AE_HIP(h, hipMemcpyAsync(h->x, noise, xbytes, hipMemcpyDeviceToDevice, st));
   const bool persist = use_persist(h, batch);
   auto enqueue = [&](hipStream_t s) -> ae_status {
     if (persist) {
-      const PersistArgs a = persist_args(h, batch, steps);
+      const PersistArgs a = persist_args(h, h->own, batch, steps);
       const hipError_t e = launch_persist(h->dt, a, s);
       return e == hipSuccess ? AE_OK : hip_fail(h, e, "launch_persist");
     }
-    return enqueue_loop(h, batch, steps, s);
+    return enqueue_loop(h, h->own, batch, steps, s);
   };
   bool ran = false;
   reap_retired(h);

@@ -468,17 +468,25 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
     bf16_t* qo = static_cast<bf16_t*>(p.q);
     bf16_t* kc = static_cast<bf16_t*>(p.kcache);
     bf16_t* vt = static_cast<bf16_t*>(p.vtcache);
+    const bool ctx = p.key_map != nullptr;
     for (int rb = wave; rb < rows; rb += 4 * kEB) {
       float csv[kEB], snv[kEB], sxv[kEB];
-      int nvv[kEB];
+      int nvv[kEB];  // the row's cache key
 #pragma unroll
       for (int i = 0; i < kEB; ++i) {
         const int m = m0 + min(rb + 4 * i, rows - 1);
         const int req = m / p.T, t = m % p.T;
-        const size_t ti2 = (static_cast<size_t>(req) * p.T + t) * half + j;
-        csv[i] = p.rope_cos[ti2];
-        snv[i] = p.rope_sin[ti2];
-        nvv[i] = p.n_valid[req];
+        if (ctx) {  // a context row: its own key, rotated at that position
+          nvv[i] = p.key_map[m];
+          const size_t pi2 = static_cast<size_t>(max(nvv[i], 0)) * half + j;
+          csv[i] = p.pos_cos[pi2];
+          snv[i] = p.pos_sin[pi2];
+        } else {
+          const size_t ti2 = (static_cast<size_t>(req) * p.T + t) * half + j;
+          csv[i] = p.rope_cos[ti2];
+          snv[i] = p.rope_sin[ti2];
+          nvv[i] = p.n_valid[req] + t;
+        }
         sxv[i] = OP == OP_FP8 ? p.sx_row[m] : 1.0f;
       }
 #pragma unroll
@@ -486,7 +494,7 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
         const int row = rb + 4 * i;
         if (row >= rows) break;
         const int m = m0 + row;
-        const int req = m / p.T, t = m % p.T;
+        const int req = m / p.T;
         float a = s_y[row][32 * pr + jj], b = s_y[row][32 * pr + 16 + jj];
         if (post_norm) {
           const float r = s_r[row];
@@ -509,7 +517,8 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
           dst[j] = f2bf(a);
           dst[half + j] = f2bf(b);
         } else {
-          const int key = nvv[i] + t;
+          const int key = nvv[i];
+          if (key < 0) continue;  // an invisible context row: never stored
           const size_t base = static_cast<size_t>(req) * p.Hkv + head;
           using LY = KvLayout<bf16_t>;
           bf16_t* dst = (seg == 1 ? kc : vt) + base * p.S_max * p.dh;
