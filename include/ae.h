@@ -199,6 +199,22 @@ ae_status ae_set_prefix_buckets(ae_handle* h, const int* lengths, int n);
 ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps,
                      float* actions_out, void* stream);
 
+/* ae_denoise for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, checks and result as ae_denoise; the call allocates
+ * nothing and creates nothing (no graph, no event): it launches the kernels
+ * directly, and their scratch (split-K and attention partials, split
+ * counters, barrier flags, packet generation base) lives in a static device
+ * array of 24 MiB in the library, one copy per GPU, held until the process
+ * ends.  Errors: as ae_denoise, plus UNSUPPORTED (before any state change)
+ * when the call's scratch exceeds 24 MiB (e.g. a very large batch on the
+ * per-phase path; ae_denoise has no such limit), HIP when the array has no
+ * address on this device.  Calls on one GPU share the array and keep the last
+ * call's contents: calls that overlap on one GPU (from any handle, on any
+ * stream) race and must not be issued. */
+ae_status ae_denoise_static(ae_handle* h, const float* noise, int batch, int steps,
+                            float* actions_out, void* stream);
+
 /* Counters, plus the device error count; reading it synchronises with the
  * device (the one call besides create/destroy that does).  INVALID_ARGUMENT
  * for null arguments. */

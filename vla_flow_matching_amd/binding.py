@@ -23,7 +23,7 @@ AE_F32, AE_BF16, AE_FP8_E4M3 = 0, 1, 2
 
 # every function include/ae.h declares
 EXPORTS = ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_set_prefix_buckets", "ae_denoise",
-           "ae_get_stats", "ae_last_error", "ae_status_string", "ae_destroy")
+           "ae_denoise_static", "ae_get_stats", "ae_last_error", "ae_status_string", "ae_destroy")
 
 
 class Config(ctypes.Structure):
@@ -76,6 +76,7 @@ def load() -> ctypes.CDLL:
     lib.ae_set_prefix_kv.argtypes = [vp, ci, ci, vp, vp, vp, vp]
     lib.ae_set_prefix_buckets.argtypes = [vp, ctypes.POINTER(ci), ci]
     lib.ae_denoise.argtypes = [vp, vp, ci, ci, vp, vp]
+    lib.ae_denoise_static.argtypes = [vp, vp, ci, ci, vp, vp]
     lib.ae_get_stats.argtypes = [vp, ctypes.POINTER(Stats)]
     lib.ae_last_error.argtypes = [vp]
     lib.ae_last_error.restype = ctypes.c_char_p
@@ -84,7 +85,7 @@ def load() -> ctypes.CDLL:
     lib.ae_destroy.argtypes = [vp]
     lib.ae_destroy.restype = None
     for f in ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_set_prefix_buckets", "ae_denoise",
-              "ae_get_stats"):
+              "ae_denoise_static", "ae_get_stats"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -215,8 +216,10 @@ class ActionExpert:
         arr = (ctypes.c_int * max(1, len(lengths)))(*[int(v) for v in lengths])
         self._check(self.lib.ae_set_prefix_buckets(self.h, arr, len(lengths)), "ae_set_prefix_buckets")
 
-    def denoise(self, noise, steps: int, out=None, stream=None):
-        """noise [B, T, A] fp32 device tensor -> actions (new tensor unless ``out``)."""
+    def denoise(self, noise, steps: int, out=None, stream=None, static_scratch: bool = False):
+        """noise [B, T, A] fp32 device tensor -> actions (new tensor unless
+        ``out``).  static_scratch: the allocation-free entry point
+        (ae_denoise_static), for callers that cannot allocate."""
         import torch
         c = self.cfg
         if noise.dim() != 3:
@@ -226,9 +229,9 @@ class ActionExpert:
         if out is None:
             out = torch.empty_like(noise)
         _expect(out, "out", (B, c.action_horizon, c.action_dim), torch.float32)
-        st = self.lib.ae_denoise(self.h, _dev(noise, "noise"), B, int(steps),
-                                 _dev(out, "out"), _stream_ptr(stream))
-        self._check(st, "ae_denoise")
+        fn = self.lib.ae_denoise_static if static_scratch else self.lib.ae_denoise
+        st = fn(self.h, _dev(noise, "noise"), B, int(steps), _dev(out, "out"), _stream_ptr(stream))
+        self._check(st, "ae_denoise_static" if static_scratch else "ae_denoise")
         return out
 
     def stats(self) -> Dict[str, int]:

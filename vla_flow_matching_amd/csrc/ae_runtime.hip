@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -688,7 +689,28 @@ std::string shape_str(const long long* s, int n) {
   return r + "]";
 }
 
-// The checks of ae_denoise (before any state change).
+// Parts of a scratch set laid out from `base` (nullptr: sizes only), each
+// 256-byte aligned, the packet generation base first: its place must not move
+// between calls that share the memory, since every launch continues from the
+// range the previous one used.  Returns the bytes used.
+size_t carve(char* base, const ScratchNeed& n, ScratchSet* sc) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += (std::max<size_t>(bytes, 4) + 255) / 256 * 256;
+    return p;
+  };
+  sc->genp = reinterpret_cast<uint32_t*>(take(8));
+  sc->flags = reinterpret_cast<int*>(take(n.flags * 4));
+  sc->pcnt = reinterpret_cast<int*>(take(n.pcnt * 4));
+  sc->gcnt = reinterpret_cast<int*>(take(n.gcn * 4));
+  sc->acnt = reinterpret_cast<int*>(take(n.acn * 4));
+  sc->gpart = reinterpret_cast<float*>(take(n.gfl * 4));
+  sc->apart = reinterpret_cast<float*>(take(n.afl * 4));
+  return off;
+}
+
+// Checks shared by ae_denoise and ae_denoise_static (before any state change).
 ae_status check_denoise(ae_handle* h, const float* noise, int batch, int steps, const float* actions_out) {
   if (!noise || !actions_out) return fail(h, AE_ERR_INVALID_ARGUMENT, "null noise or actions_out");
   if (!h->weights_loaded) return fail(h, AE_ERR_NOT_READY, "weights not loaded");
@@ -711,6 +733,43 @@ ae_status ensure_tpath(ae_handle* h, int steps, hipStream_t st) {
   if (s != AE_OK) return s;
   h->table_steps = steps;
   return AE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The scratch of ae_denoise_static, for callers that cannot allocate: a
+// static device array of kStaticScratchBytes in this library's code object.
+// Every GPU the library runs on holds its own copy until the process ends;
+// its address on a device is looked up once, in ae_create, with that device
+// current.  Calls on one device share it (and its contents from the last
+// call): those calls must not overlap.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(24) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+// Look up this device's address of `scratch` (once per device; the device
+// must be current).  A failure leaves it unset: ae_denoise_static then
+// reports AE_ERR_HIP.
+void register_static_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (g_static_ptr[dev]) return;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p) g_static_ptr[dev] = p;
+  else (void)hipGetLastError();
+}
+
+void* static_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  return g_static_ptr[dev];
 }
 
 }  // namespace
@@ -804,7 +863,10 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   {
     // the persistent kernel needs every workgroup resident at once
     int dev = 0, coop = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess) h->device = dev;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      h->device = dev;
+      register_static_scratch(dev);
+    }
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
@@ -1123,6 +1185,50 @@ ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, flo
   }
   if (persist) h->stats.persistent_calls++;
   AE_HIP(h, hipMemcpyAsync(actions_out, h->x, xbytes, hipMemcpyDeviceToDevice, st));
+  h->stats.denoise_calls++;
+  return AE_OK;
+}
+
+ae_status ae_denoise_static(ae_handle* h, const float* noise, int batch, int steps, float* actions_out,
+                            void* stream) {
+  if (!h) return AE_ERR_INVALID_ARGUMENT;
+  {
+    const ae_status c = check_denoise(h, noise, batch, steps, actions_out);
+    if (c != AE_OK) return c;
+  }
+  const bool persist = use_persist(h, batch);
+  const ScratchNeed need = scratch_need(h, batch, h->span, persist, false);
+  ScratchSet sc;
+  const size_t bytes = carve(nullptr, need, &sc);
+  if (bytes > kStaticScratchBytes)
+    return fail(h, AE_ERR_UNSUPPORTED,
+                "this call needs " + std::to_string(bytes) + " bytes of scratch; the static scratch holds " +
+                    std::to_string(kStaticScratchBytes) + " (ae_denoise has no such limit)");
+  char* base = static_cast<char*>(static_scratch(h->device));
+  if (!base) return fail(h, AE_ERR_HIP, "the static scratch has no address on this device");
+  carve(base, need, &sc);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t xbytes = static_cast<size_t>(batch) * h->T * h->A * 4;
+  {
+    const ae_status t = ensure_tpath(h, steps, st);
+    if (t != AE_OK) return t;
+  }
+  AE_HIP(h, hipMemcpyAsync(h->x, noise, xbytes, hipMemcpyDeviceToDevice, st));
+  if (persist) {
+    // (the counter fill before the launch zeroes the flags and counters)
+    const PersistArgs a = persist_args(h, sc, batch, steps);
+    AE_HIP(h, launch_persist(h->dt, a, st));
+    h->stats.persistent_calls++;
+  } else {
+    // the split counters start at zero (another call may have left other
+    // data in this part of the shared memory)
+    AE_HIP(h, launch_zero_ints(sc.gcnt, need.gcn, st));
+    AE_HIP(h, launch_zero_ints(sc.acnt, need.acn, st));
+    const ae_status e = enqueue_loop(h, sc, batch, steps, st);
+    if (e != AE_OK) return e;
+  }
+  AE_HIP(h, hipMemcpyAsync(actions_out, h->x, xbytes, hipMemcpyDeviceToDevice, st));
+  h->stats.eager_runs++;
   h->stats.denoise_calls++;
   return AE_OK;
 }
