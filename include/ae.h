@@ -86,6 +86,10 @@ typedef struct {
   int graph_cache_evict;/* cache full and a new (batch, steps, bucket): 1 evicts the least
                            recently used graph (released once its last replay is done);
                            0 launches the new call directly, uncaptured */
+  int context_width;    /* Dc of the context hidden states ae_prepare_prefix projects
+                           (multiple of 64, <= 8192; bf16 only); 0: no context projection */
+  int state_dim;        /* size of the robot state ae_prepare_prefix encodes as one more
+                           context row (<= 64, needs context_width); 0: none */
 } ae_config;
 
 /* One named logical weight, caller-owned device memory, dtype = act_dtype.
@@ -96,7 +100,10 @@ typedef struct {
  *   layers.l.q [D,Hq*dh]  layers.l.k [D,Hkv*dh]  layers.l.v [D,Hkv*dh]
  *   layers.l.o [Hq*dh,D]  layers.l.gate [D,F]  layers.l.up [D,F]  layers.l.down [F,D]
  *   layers.l.mod.w [D,6D] layers.l.mod.b [6D]  (chunks: scale_a, shift_a,
- *   gate_a, scale_m, shift_m, gate_m) */
+ *   gate_a, scale_m, shift_m, gate_m)
+ * With context_width = Dc > 0 also: layers.l.ctx_k [Dc,Hkv*dh], layers.l.ctx_v
+ * [Dc,Hkv*dh] (each layer's context K and V projections); with state_dim = S > 0
+ * also: state_in.w [S,Dc], state_in.b [Dc] (the state's input layer). */
 typedef struct {
   const char* name;
   const void* data;
@@ -169,6 +176,31 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
  * caller may reuse its buffers once the stream passes the call. */
 ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* K,
                            const void* V, const uint8_t* valid_mask, void* stream);
+
+/* Prepare one query's prefix on the device from the context itself: each
+ * layer's context K/V = hidden states times that layer's ctx_k / ctx_v, K
+ * rotated at the row's count position (the number of visible rows before it),
+ * written into the static buffers as ae_set_prefix_kv would write the result.
+ * With a robot state, state_in turns it into one more context row, placed
+ * after the visible context rows (its position is their count), projected by
+ * every layer like them.
+ * Defined by: MolmoBot PR Part 2 (prepare_cross_context / precompute_kv: the
+ * context K/V and the state, projected once per query, reused by every flow
+ * step); LoongForge blog section 1 (pads do not advance positions).
+ * Arguments: hidden is device [L][batch][prefix_len][context_width] bf16 (the
+ * VLM's per-layer hidden states of the context), valid_mask device
+ * [batch][prefix_len] uint8 (0 = invisible: padding, an empty camera slot;
+ * invisible rows are never stored, so NaN there is harmless), state device
+ * [batch][state_dim] fp32 or NULL.  The prefix then holds n_b = visible rows
+ * (+1 with a state); its bucket is chosen for prefix_len (+1).
+ * Errors (before any state change): UNSUPPORTED without context_width (or a
+ * state without state_dim), SHAPE_MISMATCH for batch outside [1, max_batch]
+ * or prefix_len (+1 with a state) outside [0, max_prefix_len],
+ * INVALID_ARGUMENT for a null hidden / mask with prefix_len > 0, NOT_READY
+ * without weights.  Stream-ordered; the caller may reuse its buffers once the
+ * stream passes the call. */
+ae_status ae_prepare_prefix(ae_handle* h, int batch, int prefix_len, const void* hidden,
+                            const uint8_t* valid_mask, const float* state, void* stream);
 
 /* Configure prefix-length buckets: lengths[0..n) strictly increasing, each in
  * [1, max_prefix_len], n <= 32 (n = 0: one bucket, max_prefix_len).  Takes

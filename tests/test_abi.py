@@ -155,3 +155,18 @@ def test_binding_rejects_wrong_noise_shapes(lib):
     with pytest.raises(binding.AeError) as e:
         ex.denoise(torch.zeros((2, 50, 32)), 10, out=torch.zeros((1, 50, 32)))
     assert e.value.status == binding.AE_ERR_SHAPE_MISMATCH
+
+
+@pytest.mark.parametrize("changes", [
+    dict(context_width=100), dict(context_width=-64), dict(context_width=8256),
+    dict(state_dim=14),                      # a state needs a context width
+    dict(context_width=64, state_dim=65),
+])
+def test_invalid_context_config(lib, changes):
+    st, h = _create(lib, **changes)
+    assert st == binding.AE_ERR_INVALID_ARGUMENT and not h.value
+
+
+def test_context_needs_bf16(lib):
+    st, h = _create(lib, context_width=128)  # the c1 workload is fp32
+    assert st == binding.AE_ERR_UNSUPPORTED and not h.value

@@ -1,0 +1,204 @@
+"""GPU context preparation (ae_prepare_prefix, through the C ABI) against the
+oracle (MolmoBot PR Part 2: prepare_cross_context / precompute_kv: the
+context K/V and the robot state are projected once per query and every flow
+step reuses them; LoongForge blog section 1: pads do not advance positions).
+
+* MolmoBot-shaped expert (12/4 heads x 64) with a Qwen3-4B-wide context
+  (2560) and a 14-D state, two requests with different visible counts: the
+  actions after GPU preparation against the oracle that re-projects the
+  context and the state on every flow step (the pages' "KV projected once ==
+  re-projected every step").
+* Pi0.5-shaped expert (8/1 heads x 256) with a 2048-wide context and no
+  state, with a hole in the visible rows.
+* Invisible context rows are never stored: NaN there gives bitwise the same
+  actions as finite garbage.
+* Preparing on the GPU and handing the oracle's projected K/V to
+  ae_set_prefix_kv give the same actions within the bf16 tolerance.
+* Error paths."""
+
+import ctypes
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import ae_oracle as O
+from vla_flow_matching_amd import synth
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", torch.bfloat16)
+
+
+def expert(w, W, CW, P, Dc, S):
+    from vla_flow_matching_amd import binding
+    ex = binding.ActionExpert(binding.make_config(w, max_prefix_len=P, context_width=Dc, state_dim=S))
+    ex.load_weights({**binding.weights_to_device(W, w.dtype), **binding.weights_to_device(CW, w.dtype)})
+    return ex
+
+
+def gpu_prepare_denoise(ex, w, H, m, state, x0, steps):
+    st = None if state is None else torch.from_numpy(state).cuda()
+    ex.prepare_prefix(bf16(H), torch.from_numpy(np.ascontiguousarray(m)).cuda(), st)
+    out = ex.denoise(torch.from_numpy(x0).cuda(), steps)
+    torch.cuda.synchronize()
+    assert ex.stats()["device_errors"] == 0
+    return out.cpu().numpy()
+
+
+def oracle_every_step(w, W, CW, H, m, state, x0):
+    """The oracle with the context (and state) re-projected on every flow
+    step, per request."""
+    L = w.n_layers
+    wk = np.stack([CW[f"layers.{l}.ctx_k"] for l in range(L)]).astype(np.float64)
+    wv = np.stack([CW[f"layers.{l}.ctx_v"] for l in range(L)]).astype(np.float64)
+    E = O.Expert(W, O.Params.like(dataclasses.replace(w, batch=1)))
+    Hc = np.where(np.isnan(H), 0.0, H)
+    outs = []
+    for b in range(w.batch):
+        mb = m[b:b + 1]
+
+        def kv(l, _b, b=b, mb=mb):
+            hs = None
+            if state is not None:
+                hs = O.encode_state(state[b:b + 1], CW["state_in.w"], CW["state_in.b"])
+            K, V, m2 = O.prepare_prefix(Hc[l:l + 1, b:b + 1], wk[l:l + 1], wv[l:l + 1], mb, w.n_kv_heads,
+                                        w.rope_theta, hs)
+            idx = np.nonzero(m2[0])[0]
+            return K[0, 0, idx], V[0, 0, idx]
+
+        n = np.array([int(mb.sum()) + (0 if state is None else 1)])
+        outs.append(E.integrate(x0[b:b + 1], kv, n, w.n_steps))
+    return outs
+
+
+def test_prepare_molmobot_shaped_with_state():
+    _need_gpu()
+    w = synth.workload("c4", batch=2, n_layers=3, n_steps=3, prefix_len=2047)
+    Dc, S = 2560, 14
+    say(f"[case] prepare: MolmoBot-shaped, context {Dc} wide, {S}-D state, 2 requests")
+    W = synth.make_weights(w)
+    CW = synth.make_context_weights(w, Dc, S)
+    m = np.zeros((2, 2047), np.uint8)
+    m[0, :1600 + 34] = 1
+    m[1, :1600 + 21] = 1
+    H, _ = synth.make_context(w, Dc, mask=m, garbage="nan")
+    state = synth.make_state(w, S)
+    x0 = synth.make_noise(w)
+    with expert(w, W, CW, 2048, Dc, S) as ex:
+        out = gpu_prepare_denoise(ex, w, H, m, state, x0, w.n_steps)
+        refs = oracle_every_step(w, W, CW, H, m, state, x0)
+        for b in range(2):
+            err = float(np.abs(out[b:b + 1] - refs[b]).max())
+            say(f"[parity] prepared context, request {b} (n={int(m[b].sum())}+state): max|gpu-oracle| = {err:.3e}")
+            assert err <= TOL_BF16
+
+
+def test_prepare_pi05_shaped_hole_and_garbage():
+    _need_gpu()
+    w = synth.workload("c2", n_layers=2, n_steps=2)
+    Dc = 2048
+    say(f"[case] prepare: Pi0.5-shaped, context {Dc} wide, no state, a masked hole")
+    W = synth.make_weights(w)
+    CW = synth.make_context_weights(w, Dc, 0)
+    m = synth.valid_masks(w, n_valid=(640,))
+    m[0, 256:300] = 0  # a hole inside the image rows: later positions shift down
+    Hn, _ = synth.make_context(w, Dc, mask=m, garbage="nan")
+    Hg = Hn.copy()
+    Hg[:, m == 0] = np.float32(1e4)
+    x0 = synth.make_noise(w)
+    with expert(w, W, CW, w.prefix_len, Dc, 0) as ex:
+        out = gpu_prepare_denoise(ex, w, Hn, m, None, x0, w.n_steps)
+        again = gpu_prepare_denoise(ex, w, Hg, m, None, x0, w.n_steps)
+        assert np.array_equal(out, again)  # invisible rows are never stored
+        ref = oracle_every_step(w, W, CW, Hn, m, None, x0)[0]
+        err = float(np.abs(out - ref).max())
+        say(f"[parity] prepared context (n={int(m.sum())}, hole): max|gpu-oracle| = {err:.3e}")
+        assert err <= TOL_BF16
+        # the same K/V projected by the oracle and handed over directly
+        L = w.n_layers
+        wk = np.stack([CW[f"layers.{l}.ctx_k"] for l in range(L)]).astype(np.float64)
+        wv = np.stack([CW[f"layers.{l}.ctx_v"] for l in range(L)]).astype(np.float64)
+        K, V, m2 = O.prepare_prefix(np.where(np.isnan(Hn), 0.0, Hn), wk, wv, m, w.n_kv_heads, w.rope_theta)
+        ex.set_prefix_kv(bf16(K.astype(np.float32)), bf16(V.astype(np.float32)),
+                         torch.from_numpy(m2).cuda())
+        direct = ex.denoise(torch.from_numpy(x0).cuda(), w.n_steps).cpu().numpy()
+        d = float(np.abs(direct - out).max())
+        say(f"[parity] GPU-prepared vs oracle-projected K/V handed over: {d:.3e}")
+        assert d <= TOL_BF16
+
+
+def test_prepare_state_row_changes_actions():
+    """The state row is one more visible key: preparing with it moves the
+    actions (and matches the oracle), preparing without it matches the
+    oracle without it."""
+    _need_gpu()
+    w = synth.workload("c4", batch=1, n_layers=2, n_steps=2, prefix_len=2047)
+    Dc, S = 512, 14
+    W = synth.make_weights(w)
+    CW = synth.make_context_weights(w, Dc, S)
+    m = np.zeros((1, 2047), np.uint8)
+    m[0, :1625] = 1
+    H, _ = synth.make_context(w, Dc, mask=m)
+    state = synth.make_state(w, S)
+    x0 = synth.make_noise(w)
+    with expert(w, W, CW, 2048, Dc, S) as ex:
+        with_s = gpu_prepare_denoise(ex, w, H, m, state, x0, w.n_steps)
+        without = gpu_prepare_denoise(ex, w, H, m, None, x0, w.n_steps)
+        r_with = oracle_every_step(w, W, CW, H, m, state, x0)[0]
+        r_without = oracle_every_step(w, W, CW, H, m, None, x0)[0]
+    e1, e2 = float(np.abs(with_s - r_with).max()), float(np.abs(without - r_without).max())
+    moved = float(np.abs(r_with - r_without).max())
+    cross = float(np.abs(with_s - r_without).max())
+    say(f"[parity] with state {e1:.3e}, without {e2:.3e}; the state moves the oracle by {moved:.3e}; "
+        f"GPU with the state vs the oracle without it {cross:.3e}")
+    assert e1 <= TOL_BF16 and e2 <= TOL_BF16
+    # each GPU result sits with its own oracle, well away from the other one
+    assert e1 < 0.5 * cross and e2 < 0.5 * moved
+
+
+def test_prepare_error_paths():
+    from vla_flow_matching_amd import binding
+    _need_gpu()
+    w = synth.workload("c2", n_layers=1, n_steps=1, prefix_len=64)
+    W = synth.make_weights(w)
+    m = torch.ones((1, 64), dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    with binding.ActionExpert(binding.make_config(w)) as ex:  # no context width
+        ex.load_weights(binding.weights_to_device(W, w.dtype))
+        H0 = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+        assert ex.lib.ae_prepare_prefix(ex.h, 1, 64, ptr(H0), ptr(m), None, stream) == binding.AE_ERR_UNSUPPORTED
+    CW = synth.make_context_weights(w, 128, 0)
+    with expert(w, W, CW, 64, 128, 0) as ex:
+        H = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
+        s = torch.zeros(16, dtype=torch.float32, device="cuda")
+        # a state, but the handle has no state input layer
+        assert ex.lib.ae_prepare_prefix(ex.h, 1, 64, ptr(H), ptr(m), ptr(s), stream) == binding.AE_ERR_UNSUPPORTED
+        # a prefix longer than the capacity, a batch past max_batch
+        assert ex.lib.ae_prepare_prefix(ex.h, 1, 65, ptr(H), ptr(m), None, stream) == binding.AE_ERR_SHAPE_MISMATCH
+        assert ex.lib.ae_prepare_prefix(ex.h, 2, 64, ptr(H), ptr(m), None, stream) == binding.AE_ERR_SHAPE_MISMATCH
+        with pytest.raises(binding.AeError) as e:  # wrong context width (binding check)
+            ex.prepare_prefix(torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda"), m)
+        assert e.value.status == binding.AE_ERR_SHAPE_MISMATCH
+        ex.prepare_prefix(H, m)  # the full capacity, no state: fine
+        out = ex.denoise(torch.zeros((1, 50, 32), dtype=torch.float32, device="cuda"), 1)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all().item()

@@ -22,8 +22,8 @@ AE_ERR_OUT_OF_MEMORY, AE_ERR_UNSUPPORTED, AE_ERR_HIP = 4, 5, 6
 AE_F32, AE_BF16, AE_FP8_E4M3 = 0, 1, 2
 
 # every function include/ae.h declares
-EXPORTS = ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_set_prefix_buckets", "ae_denoise",
-           "ae_denoise_static", "ae_get_stats", "ae_last_error", "ae_status_string", "ae_destroy")
+EXPORTS = ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_prepare_prefix", "ae_set_prefix_buckets",
+           "ae_denoise", "ae_denoise_static", "ae_get_stats", "ae_last_error", "ae_status_string", "ae_destroy")
 
 
 class Config(ctypes.Structure):
@@ -35,6 +35,7 @@ class Config(ctypes.Structure):
         ("act_dtype", ctypes.c_int), ("proj_weight_dtype", ctypes.c_int),
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("use_graphs", ctypes.c_int),
         ("graph_cache_size", ctypes.c_int), ("graph_cache_evict", ctypes.c_int),
+        ("context_width", ctypes.c_int), ("state_dim", ctypes.c_int),
     ]
 
 
@@ -75,6 +76,7 @@ def load() -> ctypes.CDLL:
     lib.ae_load_weights.argtypes = [vp, ctypes.POINTER(TensorView), ci, vp]
     lib.ae_set_prefix_kv.argtypes = [vp, ci, ci, vp, vp, vp, vp]
     lib.ae_set_prefix_buckets.argtypes = [vp, ctypes.POINTER(ci), ci]
+    lib.ae_prepare_prefix.argtypes = [vp, ci, ci, vp, vp, vp, vp]
     lib.ae_denoise.argtypes = [vp, vp, ci, ci, vp, vp]
     lib.ae_denoise_static.argtypes = [vp, vp, ci, ci, vp, vp]
     lib.ae_get_stats.argtypes = [vp, ctypes.POINTER(Stats)]
@@ -84,8 +86,8 @@ def load() -> ctypes.CDLL:
     lib.ae_status_string.restype = ctypes.c_char_p
     lib.ae_destroy.argtypes = [vp]
     lib.ae_destroy.restype = None
-    for f in ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_set_prefix_buckets", "ae_denoise",
-              "ae_denoise_static", "ae_get_stats"):
+    for f in ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_prepare_prefix", "ae_set_prefix_buckets",
+              "ae_denoise", "ae_denoise_static", "ae_get_stats"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -93,7 +95,8 @@ def load() -> ctypes.CDLL:
 
 def make_config(w, max_batch: Optional[int] = None, max_prefix_len: Optional[int] = None,
                 max_steps: Optional[int] = None, use_graphs: bool = True,
-                graph_cache_size: int = 16, graph_cache_evict: bool = True) -> Config:
+                graph_cache_size: int = 16, graph_cache_evict: bool = True,
+                context_width: int = 0, state_dim: int = 0) -> Config:
     """Config from any object with the workload fields (e.g. synth.Workload)."""
     act = AE_BF16 if w.dtype == "bf16" else AE_F32
     proj = AE_FP8_E4M3 if getattr(w, "proj_dtype", "same") == "fp8" else act
@@ -103,7 +106,7 @@ def make_config(w, max_batch: Optional[int] = None, max_prefix_len: Optional[int
                   w.batch if max_batch is None else max_batch,
                   w.n_steps if max_steps is None else max_steps,
                   act, proj, float(w.rope_theta), float(w.rms_eps), int(bool(use_graphs)),
-                  int(graph_cache_size), int(bool(graph_cache_evict)))
+                  int(graph_cache_size), int(bool(graph_cache_evict)), int(context_width), int(state_dim))
 
 
 def _stream_ptr(stream) -> ctypes.c_void_p:
@@ -209,6 +212,28 @@ class ActionExpert:
             st = self.lib.ae_set_prefix_kv(self.h, B, P, _dev(K, "K"), _dev(V, "V"), _dev(mask, "mask"),
                                            _stream_ptr(stream))
         self._check(st, "ae_set_prefix_kv")
+        self.prefix_batch = B
+
+    def prepare_prefix(self, hidden, mask, state=None, stream=None):
+        """hidden [L, B, P, context_width] bf16, mask [B, P] uint8, state
+        [B, state_dim] fp32 or None; device tensors."""
+        import torch
+        c = self.cfg
+        if mask.dim() != 2:
+            raise AeError(AE_ERR_SHAPE_MISMATCH, f"mask: expected [batch, prefix_len], got {tuple(mask.shape)}")
+        B, P = int(mask.shape[0]), int(mask.shape[1])
+        nullp = ctypes.c_void_p()
+        hp = mp = nullp
+        if P > 0:
+            _expect(hidden, "hidden", (c.n_layers, B, P, c.context_width), torch.bfloat16)
+            _expect(mask, "mask", (B, P), torch.uint8)
+            hp, mp = _dev(hidden, "hidden"), _dev(mask, "mask")
+        sp = nullp
+        if state is not None:
+            _expect(state, "state", (B, c.state_dim), torch.float32)
+            sp = _dev(state, "state")
+        self._check(self.lib.ae_prepare_prefix(self.h, B, P, hp, mp, sp, _stream_ptr(stream)),
+                    "ae_prepare_prefix")
         self.prefix_batch = B
 
     def set_prefix_buckets(self, lengths: Sequence[int]):

@@ -78,6 +78,7 @@ struct ae_handle {
   int esz = 2;
   int L = 0, D = 0, Hq = 0, Hkv = 0, dh = 0, F = 0, T = 0, A = 0, Pmax = 0, Bmax = 0, Nmax = 0;
   int S_max = 0, qdim = 0, kvdim = 0, qkv_n = 0, ssq_tiles = 0, Mmax = 0;
+  int Dc = 0, Sd = 0;  // context width and robot-state size (0: no context preparation)
 
   // weights (library-owned copies)
   void *tw1 = nullptr, *tb1 = nullptr, *tw2 = nullptr, *tb2 = nullptr;
@@ -85,6 +86,15 @@ struct ae_handle {
   float *w_in = nullptr, *b_in = nullptr, *w_out = nullptr, *b_out = nullptr;
   uint4 *wqkv = nullptr, *wo = nullptr, *wgu = nullptr, *wd = nullptr;
   size_t sqkv = 0, so = 0, sgu = 0, sd = 0;  // per-layer strides in uint4
+
+  // context preparation: each layer's [ctx_k | ctx_v] packed (RoPE pairs
+  // together), RoPE tables of positions 0 .. max_prefix_len, the state's
+  // input layer, its context row and cache key per request
+  uint4* wctx = nullptr;
+  size_t sctx = 0;  // per-layer stride in uint4
+  float *pos_cos = nullptr, *pos_sin = nullptr;
+  uint16_t *st_w = nullptr, *st_b = nullptr, *st_h = nullptr;
+  int* st_key = nullptr;
 
   // prefix state
   void *kcache = nullptr, *vtcache = nullptr;
@@ -183,12 +193,18 @@ std::string validate_config(const ae_config* c) {
   if (c->use_graphs != 0 && c->use_graphs != 1) return "use_graphs must be 0 or 1";
   if (c->graph_cache_size < 0 || c->graph_cache_size > kMaxGraphs) return "graph_cache_size must be in [0, 64]";
   if (c->graph_cache_evict != 0 && c->graph_cache_evict != 1) return "graph_cache_evict must be 0 or 1";
+  if (c->context_width < 0 || c->context_width % 64 || c->context_width > 8192)
+    return "context_width must be 0 or a multiple of 64 up to 8192";
+  if (c->state_dim < 0 || c->state_dim > 64) return "state_dim must be in [0, 64]";
+  if (c->state_dim > 0 && c->context_width == 0) return "state_dim needs context_width";
   return "";
 }
 
 std::string unsupported_config(const ae_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
     return "head_dim must be 64, 128 or 256";
+  if (c->context_width > 0 && (c->act_dtype != AE_BF16 || (2 * c->n_kv_heads * c->head_dim) % 128))
+    return "context preparation needs bf16 and 2 n_kv_heads head_dim a multiple of 128";
   if (c->proj_weight_dtype != c->act_dtype) {
     if (c->proj_weight_dtype != AE_FP8_E4M3 || c->act_dtype != AE_BF16)
       return "proj_weight_dtype must equal act_dtype (or be AE_FP8_E4M3 with bf16)";
@@ -679,6 +695,14 @@ std::vector<WeightSpec> weight_specs(const ae_handle* h) {
     v.push_back({p + "down", {F, D}});
     v.push_back({p + "mod.w", {D, 6 * D}});
     v.push_back({p + "mod.b", {6 * D}});
+    if (h->Dc > 0) {
+      v.push_back({p + "ctx_k", {h->Dc, kd}});
+      v.push_back({p + "ctx_v", {h->Dc, kd}});
+    }
+  }
+  if (h->Sd > 0) {
+    v.push_back({"state_in.w", {h->Sd, h->Dc}});
+    v.push_back({"state_in.b", {h->Dc}});
   }
   return v;
 }
@@ -856,6 +880,8 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   h->ssq_tiles = h->D / 64;
   h->Mmax = h->Bmax * h->T;
   h->fp8 = cfg->proj_weight_dtype == AE_FP8_E4M3;
+  h->Dc = cfg->context_width;
+  h->Sd = cfg->state_dim;
   h->tiled = h->dt == DT_BF16 && h->D % 128 == 0 && h->qkv_n % 128 == 0 && (2 * h->F) % 128 == 0 &&
              h->qdim % 64 == 0 && h->F % 64 == 0;
 
@@ -943,6 +969,12 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
 
   // the largest call's scratch, over every batch, path and prefix bucket
   ScratchNeed need;
+  if (h->Dc > 0) {  // the context products' K splits, at any row count
+    for (int m = 1; m <= h->Bmax * std::max(1, h->Pmax); ++m) {
+      const TGemmPlan g = plan_tgemm(m, 2 * h->kvdim, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
+      need.gfl = std::max(need.gfl, tgemm_partial_floats(g));
+    }
+  }
   for (int b = 1; b <= h->Bmax; ++b) {
     need.max_with(scratch_need(h, b, h->Pmax, false, true));
     if (h->G > 0 && b * h->T <= kTileM) need.max_with(scratch_need(h, b, h->Pmax, true, true));
@@ -957,6 +989,18 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   AE_ALLOC(h->own.gcnt, need.gcn * 4);
   AE_ALLOC(h->own.apart, need.afl * 4);
   AE_ALLOC(h->own.acnt, need.acn * 4);
+  if (h->Dc > 0) {
+    h->sctx = elems_packed(h->Dc, 2 * h->kvdim, ks);
+    AE_ALLOC(h->wctx, L * h->sctx * 16);
+    AE_ALLOC(h->pos_cos, static_cast<size_t>(h->Pmax + 1) * (h->dh / 2) * 4);
+    AE_ALLOC(h->pos_sin, static_cast<size_t>(h->Pmax + 1) * (h->dh / 2) * 4);
+    if (h->Sd > 0) {
+      AE_ALLOC(h->st_w, static_cast<size_t>(h->Sd) * h->Dc * 2);
+      AE_ALLOC(h->st_b, static_cast<size_t>(h->Dc) * 2);
+      AE_ALLOC(h->st_h, static_cast<size_t>(h->Bmax) * h->Dc * 2);
+      AE_ALLOC(h->st_key, static_cast<size_t>(h->Bmax) * 4);
+    }
+  }
 #undef AE_ALLOC
 
   // zero everything once: counters must start at 0; caches and activations
@@ -969,7 +1013,9 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
       return s2;
     }
   }
-  hipError_t e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
+  hipError_t e = hipSuccess;
+  if (h->Dc > 0) e = launch_pos_table(h->Pmax + 1, h->dh, cfg->rope_theta, h->pos_cos, h->pos_sin, nullptr);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     ae_destroy(h);
@@ -1050,6 +1096,16 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
                                      sizes[i], h->wamax + 6 * l + i, st));
     AE_HIP(h, launch_fp8_scales(h->wamax, h->L * 6, h->wmul, h->wsc, st));
   }
+  for (int l = 0; l < h->L && h->Dc > 0; ++l) {
+    // [ctx_k | ctx_v] as the QKV packing with no query heads: RoPE pairs of K together
+    const std::string p = "layers." + std::to_string(l) + ".";
+    AE_HIP(h, launch_pack(h->dt, PACK_QKV, nullptr, get(p + "ctx_k"), get(p + "ctx_v"), h->Dc, 2 * h->kvdim,
+                          0, h->kvdim, h->kvdim, 0, h->Hkv, h->dh, h->wctx + l * h->sctx, st));
+  }
+  if (h->Sd > 0) {
+    AE_HIP(h, cp(h->st_w, "state_in.w", static_cast<size_t>(h->Sd) * h->Dc * 2));
+    AE_HIP(h, cp(h->st_b, "state_in.b", static_cast<size_t>(h->Dc) * 2));
+  }
   for (int l = 0; l < h->L; ++l) {
     const std::string p = "layers." + std::to_string(l) + ".";
     AE_HIP(h, cp(static_cast<char*>(h->mod_w) + l * D * 6 * D * es, p + "mod.w", D * 6 * D * es));
@@ -1098,6 +1154,68 @@ ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* 
                                h->cfg.rope_theta, h->rope_cos, h->rope_sin, st));
   AE_HIP(h, launch_prefix_copy(h->dt, K, V, h->comp_idx, h->n_valid, h->T, h->L, batch, prefix_len,
                                h->Hkv, h->dh, h->Bmax, h->S_max, h->kcache, h->vtcache, st));
+  h->prefix_batch = batch;
+  h->span = span;
+  h->stats.prefix_sets++;
+  return AE_OK;
+}
+
+ae_status ae_prepare_prefix(ae_handle* h, int batch, int prefix_len, const void* hidden,
+                            const uint8_t* valid_mask, const float* state, void* stream) {
+  if (!h) return AE_ERR_INVALID_ARGUMENT;
+  if (h->Dc == 0) return fail(h, AE_ERR_UNSUPPORTED, "context_width is 0: no context projection");
+  if (state && h->Sd == 0) return fail(h, AE_ERR_UNSUPPORTED, "state given but state_dim is 0");
+  const int extra = state ? 1 : 0;
+  if (batch < 1 || batch > h->Bmax)
+    return fail(h, AE_ERR_SHAPE_MISMATCH,
+                "batch " + std::to_string(batch) + " outside [1, " + std::to_string(h->Bmax) + "]");
+  if (prefix_len < 0 || prefix_len + extra > h->Pmax)
+    return fail(h, AE_ERR_SHAPE_MISMATCH,
+                "prefix_len " + std::to_string(prefix_len) + (extra ? " + the state row" : "") + " outside [0, " +
+                    std::to_string(h->Pmax) + "]");
+  if (prefix_len > 0 && (!hidden || !valid_mask)) return fail(h, AE_ERR_INVALID_ARGUMENT, "null hidden or valid_mask");
+  if (!h->weights_loaded) return fail(h, AE_ERR_NOT_READY, "weights not loaded");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int span = pick_bucket(h->buckets, prefix_len + extra, h->Pmax);
+  const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
+  h->prefix_batch = -1;  // (a failed launch leaves no usable prefix)
+  // counts (the state row included), compaction index, action RoPE tables
+  AE_HIP(h, launch_prefix_scan(valid_mask, batch, prefix_len, h->comp_idx, h->n_valid, h->T, h->dh,
+                               h->cfg.rope_theta, h->rope_cos, h->rope_sin, st, extra));
+  if (state)
+    AE_HIP(h, launch_state_prep(state, batch, h->Sd, h->st_w, h->st_b, h->Dc, h->n_valid, h->st_h, h->st_key, st));
+  // one product per layer: [K | V] of every context row, K rotated at the
+  // row's count position, visible rows scattered to their keys
+  auto project = [&](int l, const void* A, int rows, int rows_per_req, const int* keys) -> ae_status {
+    const TGemmPlan g = plan_tgemm(rows, 2 * h->kvdim, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
+    TGemmArgs a = base_tgemm(h, h->own, g, rows, 2 * h->kvdim, h->Dc);
+    a.A = A;
+    a.lda_bytes = static_cast<size_t>(h->Dc) * 2;
+    a.W = h->wctx + l * h->sctx;
+    a.kcache = static_cast<char*>(h->kcache) + l * kv_layer;
+    a.vtcache = static_cast<char*>(h->vtcache) + l * kv_layer;
+    a.n_valid = h->n_valid;
+    a.T = rows_per_req; a.Hq = 0; a.Hkv = h->Hkv; a.dh = h->dh; a.S_max = h->S_max;
+    a.key_map = keys;
+    a.pos_cos = h->pos_cos;
+    a.pos_sin = h->pos_sin;
+    const hipError_t e = launch_tgemm(OP_BF16, EPI_QKV, a, g.blocks, st);
+    return e == hipSuccess ? AE_OK : hip_fail(h, e, "launch_tgemm (context)");
+  };
+  for (int l = 0; l < h->L; ++l) {
+    if (prefix_len > 0) {
+      const char* Hl = static_cast<const char*>(hidden) + static_cast<size_t>(l) * batch * prefix_len * h->Dc * 2;
+      const ae_status r = project(l, Hl, batch * prefix_len, prefix_len, h->comp_idx);
+      if (r != AE_OK) return r;
+    }
+    if (state) {
+      const ae_status r = project(l, h->st_h, batch, 1, h->st_key);
+      if (r != AE_OK) return r;
+    }
+  }
+  // finite values in the rest of each request's last key block (no rows copied)
+  AE_HIP(h, launch_prefix_copy(h->dt, nullptr, nullptr, h->comp_idx, h->n_valid, h->T, h->L, batch, 0, h->Hkv,
+                               h->dh, h->Bmax, h->S_max, h->kcache, h->vtcache, st));
   h->prefix_batch = batch;
   h->span = span;
   h->stats.prefix_sets++;
