@@ -60,7 +60,12 @@ the pages support):
 * context preparation: each layer's context K/V = the context hidden states
   times that layer's context K and V projections, K rotated at the row's
   count position; the robot state enters through one linear layer as one
-  more visible row after the context rows.
+  more visible row after the context rows;
+* DiT-style block (the MolmoBot expert's attn1 / attn2): nine modulation
+  chunks per layer (scale, shift, gate of the self-attention, the
+  cross-attention and the MLP); attn1 over the action tokens only, attn2 of
+  separate q2 / o2 projections over the visible prefix only, each with its
+  own softmax; an empty prefix gives attn2 no contribution.
 
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against closed forms, library routines, brute force or invariants; none is
@@ -91,12 +96,13 @@ class Params:
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
     fp8: bool = False
+    block: str = "joint"  # "joint": one attention over [prefix | actions]; "dit": attn1 + attn2
 
     @staticmethod
     def like(obj, fp8: Optional[bool] = None) -> "Params":
         f = getattr(obj, "proj_dtype", "same") == "fp8" if fp8 is None else fp8
         return Params(obj.n_q_heads, obj.n_kv_heads, obj.head_dim,
-                      float(obj.rope_theta), float(obj.rms_eps), f)
+                      float(obj.rope_theta), float(obj.rms_eps), f, getattr(obj, "block", "joint"))
 
 
 def to64(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
@@ -153,9 +159,13 @@ def time_condition(t: np.ndarray, W: Dict[str, np.ndarray]) -> np.ndarray:
 
 
 def layer_modulation(c: np.ndarray, W: Dict[str, np.ndarray], layer: int):
-    """Six [.., D] chunks: scale_a, shift_a, gate_a, scale_m, shift_m, gate_m."""
-    m = linear(c, W[f"layers.{layer}.mod.w"], W[f"layers.{layer}.mod.b"])
-    return np.split(m, 6, axis=-1)
+    """The [.., D] chunks of a layer's modulation: six (scale_a, shift_a,
+    gate_a, scale_m, shift_m, gate_m) for the joint block, nine (scale, shift,
+    gate of the self-attention, the cross-attention and the MLP) for the
+    DiT-style block."""
+    wm = W[f"layers.{layer}.mod.w"]
+    m = linear(c, wm, W[f"layers.{layer}.mod.b"])
+    return np.split(m, wm.shape[1] // wm.shape[0], axis=-1)
 
 
 def final_modulation(c: np.ndarray, W: Dict[str, np.ndarray]):
@@ -195,6 +205,8 @@ def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray) -> np.ndarray
     o_h = softmax(q_h . K_g^T / sqrt(dh)) . V_g with g = floor(h * Hkv / Hq)."""
     T, Hq, dh = q.shape
     Hkv = keys.shape[1]
+    if keys.shape[0] == 0:  # no visible key (a cross-attention over an empty prefix): no contribution
+        return np.zeros_like(q)
     o = np.empty_like(q)
     for h in range(Hq):
         g = (h * Hkv) // Hq
@@ -276,6 +288,8 @@ class Expert:
     def velocity(self, x: np.ndarray, c: np.ndarray, kv_of_layer, n_valid: np.ndarray) -> np.ndarray:
         """v(x, t) for a batch.  x [B, T, A]; c [D] the time condition of this
         step; kv_of_layer(l, b) -> (keys, values) visible prefix rows."""
+        if self.p.block == "dit":
+            return self.velocity_dit(x, c, kv_of_layer, n_valid)
         W, p = self.W, self.p
         B, T, _ = x.shape
         Hq, Hkv, dh = p.n_q_heads, p.n_kv_heads, p.head_dim
@@ -302,6 +316,48 @@ class Expert:
                 a[b] = gelu_tanh(self.proj(u2[b], pre + "gate")) * self.proj(u2[b], pre + "up")
             d = np.stack([self.proj(a[b], pre + "down") for b in range(B)])
             h = h + gm * d
+        sf, hf = final_modulation(c, W)
+        return linear(ada_rms(h, sf, hf, p.rms_eps), W["action_out.w"], W["action_out.b"])
+
+    def velocity_dit(self, x: np.ndarray, c: np.ndarray, kv_of_layer, n_valid: np.ndarray) -> np.ndarray:
+        """v(x, t) with the DiT-style block of the MolmoBot action expert
+        (MolmoBot PR Part 2: ActionExpertBlock passes the cached context K/V
+        to attn2; Correctness table: cross_attn and self_attn): per layer
+        h += gate1 * attn1(adaRMS(h)) over the action tokens only (q, k, v, o),
+        h += gate2 * attn2(adaRMS(h)) of the action queries (q2, o2) over the
+        visible prefix K/V only, h += gate3 * MLP(adaRMS(h)); each attention
+        has its own softmax.  Action token i sits at position n_valid + i in
+        both (only position differences matter inside attn1)."""
+        W, p = self.W, self.p
+        B, T, _ = x.shape
+        Hq, Hkv, dh = p.n_q_heads, p.n_kv_heads, p.head_dim
+        h = linear(x, W["action_in.w"], W["action_in.b"])
+        for l in range(self.L):
+            s1, b1, g1, s2, b2, g2, s3, b3, g3 = layer_modulation(c, W, l)
+            pre = f"layers.{l}."
+            u = ada_rms(h, s1, b1, p.rms_eps)
+            o = np.empty((B, T, Hq * dh))
+            for b in range(B):
+                q = self.proj(u[b], pre + "q").reshape(T, Hq, dh)
+                k = self.proj(u[b], pre + "k").reshape(T, Hkv, dh)
+                v = self.proj(u[b], pre + "v").reshape(T, Hkv, dh)
+                cos, sin = rope_cos_sin(n_valid[b] + np.arange(T), dh, p.rope_theta)
+                o[b] = attention(apply_rope(q, cos, sin), apply_rope(k, cos, sin), v).reshape(T, Hq * dh)
+            h = h + g1 * (o @ W[pre + "o"])
+            u2 = ada_rms(h, s2, b2, p.rms_eps)
+            o2 = np.empty((B, T, Hq * dh))
+            for b in range(B):
+                q2 = (u2[b] @ W[pre + "q2"]).reshape(T, Hq, dh)
+                cos, sin = rope_cos_sin(n_valid[b] + np.arange(T), dh, p.rope_theta)
+                pk, pv = kv_of_layer(l, b)
+                o2[b] = attention(apply_rope(q2, cos, sin), pk, pv).reshape(T, Hq * dh)
+            h = h + g2 * (o2 @ W[pre + "o2"])
+            u3 = ada_rms(h, s3, b3, p.rms_eps)
+            a = np.empty((B, T, W[pre + "gate"].shape[1]))
+            for b in range(B):
+                a[b] = gelu_tanh(self.proj(u3[b], pre + "gate")) * self.proj(u3[b], pre + "up")
+            d = np.stack([self.proj(a[b], pre + "down") for b in range(B)])
+            h = h + g3 * d
         sf, hf = final_modulation(c, W)
         return linear(ada_rms(h, sf, hf, p.rms_eps), W["action_out.w"], W["action_out.b"])
 

@@ -550,3 +550,177 @@ def test_prepared_context_once_equals_every_step():
     every = E.integrate(x0, reproject, m2.sum(1), w.n_steps)
     assert np.array_equal(once, every)
     assert np.abs(once - E.denoise(x0, K[:, :, :-1], V[:, :, :-1], m, w.n_steps)).max() > 1e-3  # the state row counts
+
+
+# --------------------------------------------------------------------------
+# DiT-style block (MolmoBot PR Part 2: attn2 reads the cached context K/V;
+# Correctness table: cross_attn & self_attn)
+# --------------------------------------------------------------------------
+
+def _bf_denoise_dit(w, W, K, V, mask, x0):
+    """Scalar twin of the DiT-style block: per layer a self-attention over
+    the action tokens (explicit all-visible key list), a cross-attention of
+    separate q2 / o2 projections over the prefix with an explicit visibility
+    list and -inf logits for invisible rows (an empty visible set adds
+    nothing), and the MLP; nine modulation chunks."""
+    L, D, Hq, Hkv, dh, Fd = w.n_layers, w.width, w.n_q_heads, w.n_kv_heads, w.head_dim, w.mlp_dim
+    T, A, N, B, P = w.action_horizon, w.action_dim, w.n_steps, w.batch, w.prefix_len
+    g = lambda name: np.asarray(W[name], dtype=np.float64)
+
+    def mv(vec, mat, bias=None):
+        out = [0.0] * mat.shape[1]
+        for j in range(mat.shape[1]):
+            acc = 0.0
+            for i in range(mat.shape[0]):
+                acc += vec[i] * mat[i, j]
+            out[j] = acc + (0.0 if bias is None else bias[j])
+        return out
+
+    silu = lambda z: z / (1.0 + math.exp(-z))
+
+    def norm(vec, scale, shift):
+        r = 1.0 / math.sqrt(sum(v * v for v in vec) / len(vec) + w.rms_eps)
+        return [vec[i] * r * (1.0 + scale[i]) + shift[i] for i in range(len(vec))]
+
+    def rot(vec, p):
+        half = len(vec) // 2
+        out = list(vec)
+        for j in range(half):
+            ang = p * w.rope_theta ** (-2.0 * j / len(vec))
+            out[j] = vec[j] * math.cos(ang) - vec[j + half] * math.sin(ang)
+            out[j + half] = vec[j + half] * math.cos(ang) + vec[j] * math.sin(ang)
+        return out
+
+    def attend(qv, keys, vals, vis):
+        logits = [sum(qv[d] * kk[d] for d in range(dh)) / math.sqrt(dh) if vv else -math.inf
+                  for kk, vv in zip(keys, vis)]
+        if not any(vis):
+            return [0.0] * dh
+        mx = max(logits)
+        ws = [math.exp(s - mx) if s != -math.inf else 0.0 for s in logits]
+        tot = sum(ws)
+        return [sum(ws[j] * vals[j][d] for j in range(len(keys)) if ws[j] != 0.0) / tot for d in range(dh)]
+
+    x = [[[float(x0[b, i, a]) for a in range(A)] for i in range(T)] for b in range(B)]
+    for k in range(N):
+        t = 1.0 - k / N
+        half = D // 2
+        e = [math.sin(2 * math.pi * t / (4e-3 * 1000.0 ** (i / (half - 1)))) for i in range(half)]
+        e += [math.cos(2 * math.pi * t / (4e-3 * 1000.0 ** (i / (half - 1)))) for i in range(half)]
+        c = [silu(z) for z in mv([silu(z) for z in mv(e, g("time_mlp.1.w"), g("time_mlp.1.b"))],
+                                 g("time_mlp.2.w"), g("time_mlp.2.b"))]
+        for b in range(B):
+            nv = int(sum(int(mask[b, j] != 0) for j in range(P)))
+            h = [mv(x[b][i], g("action_in.w"), g("action_in.b")) for i in range(T)]
+            for l in range(L):
+                mod = mv(c, g(f"layers.{l}.mod.w"), g(f"layers.{l}.mod.b"))
+                ch = [mod[j * D:(j + 1) * D] for j in range(9)]
+                pre = f"layers.{l}."
+                # attn1: the action tokens among themselves
+                u = [norm(h[i], ch[0], ch[1]) for i in range(T)]
+                qs = [mv(r, g(pre + "q")) for r in u]
+                ks = [mv(r, g(pre + "k")) for r in u]
+                vs = [mv(r, g(pre + "v")) for r in u]
+                o = [[0.0] * (Hq * dh) for _ in range(T)]
+                for hd in range(Hq):
+                    kv = hd // (Hq // Hkv)
+                    keys = [rot(ks[j][kv * dh:(kv + 1) * dh], nv + j) for j in range(T)]
+                    vals = [vs[j][kv * dh:(kv + 1) * dh] for j in range(T)]
+                    for i in range(T):
+                        o[i][hd * dh:(hd + 1) * dh] = attend(rot(qs[i][hd * dh:(hd + 1) * dh], nv + i),
+                                                             keys, vals, [True] * T)
+                for i in range(T):
+                    ob = mv(o[i], g(pre + "o"))
+                    h[i] = [h[i][d] + ch[2][d] * ob[d] for d in range(D)]
+                # attn2: the action queries over the prefix
+                u2 = [norm(h[i], ch[3], ch[4]) for i in range(T)]
+                q2 = [mv(r, g(pre + "q2")) for r in u2]
+                o2 = [[0.0] * (Hq * dh) for _ in range(T)]
+                for hd in range(Hq):
+                    kv = hd // (Hq // Hkv)
+                    keys = [[float(K[l, b, j, kv, d]) for d in range(dh)] for j in range(P)]
+                    vals = [[float(V[l, b, j, kv, d]) for d in range(dh)] for j in range(P)]
+                    vis = [mask[b, j] != 0 for j in range(P)]
+                    for i in range(T):
+                        o2[i][hd * dh:(hd + 1) * dh] = attend(rot(q2[i][hd * dh:(hd + 1) * dh], nv + i),
+                                                              keys, vals, vis)
+                for i in range(T):
+                    ob = mv(o2[i], g(pre + "o2"))
+                    h[i] = [h[i][d] + ch[5][d] * ob[d] for d in range(D)]
+                # MLP
+                for i in range(T):
+                    u3 = norm(h[i], ch[6], ch[7])
+                    gt, up = mv(u3, g(pre + "gate")), mv(u3, g(pre + "up"))
+                    act = [0.5 * gt[f] * (1 + math.tanh(math.sqrt(2 / math.pi) * (gt[f] + 0.044715 * gt[f] ** 3)))
+                           * up[f] for f in range(Fd)]
+                    dn = mv(act, g(pre + "down"))
+                    h[i] = [h[i][d] + ch[8][d] * dn[d] for d in range(D)]
+            fm = mv(c, g("final_mod.w"), g("final_mod.b"))
+            for i in range(T):
+                vv = mv(norm(h[i], fm[:D], fm[D:]), g("action_out.w"), g("action_out.b"))
+                x[b][i] = [x[b][i][a] - vv[a] / N for a in range(A)]
+    return np.array(x)
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 1), (4, 2)])
+def test_oracle_dit_matches_brute_force(hq, hkv):
+    """With request 1's prefix entirely masked its cross-attention adds
+    nothing (and NaN there must not leak)."""
+    w = tiny(n_q_heads=hq, n_kv_heads=hkv, width=8 if hq == 2 else 16, block="dit")
+    W = synth.make_weights(w, std=0.3)
+    mask = np.array([[1, 0, 1, 1, 0], [0, 0, 0, 0, 0]], np.uint8)
+    K, V, _ = synth.make_prefix(w, mask=mask, garbage="nan")
+    x0 = synth.make_noise(w)
+    ours = run(w, W, K, V, mask, x0)
+    ref = _bf_denoise_dit(w, W, K, V, mask, x0)
+    assert np.abs(ours - x0).max() > 0.05
+    assert np.allclose(ours, ref, rtol=0, atol=1e-11)
+
+
+def test_dit_without_cross_attention_is_the_joint_block_without_prefix():
+    """With o2 = 0 the DiT block is attn1 + MLP: the joint block over an
+    empty prefix whose six chunks are the DiT's (attn1, MLP) chunks; the
+    prefix cannot matter (only position differences enter attn1)."""
+    wd = synth.workload("c1", block="dit", n_layers=2, n_steps=3)
+    Wd = synth.make_weights(wd)
+    D = wd.width
+    for l in range(wd.n_layers):
+        Wd[f"layers.{l}.o2"] = np.zeros_like(Wd[f"layers.{l}.o2"])
+    wj = synth.workload("c1", n_layers=2, n_steps=3, prefix_len=0)
+    Wj = {k: v for k, v in Wd.items() if not (k.endswith(".q2") or k.endswith(".o2"))}
+    keep = [0, 1, 2, 6, 7, 8]
+    for l in range(wd.n_layers):
+        mw, mb = Wd[f"layers.{l}.mod.w"], Wd[f"layers.{l}.mod.b"]
+        Wj[f"layers.{l}.mod.w"] = np.concatenate([mw[:, c * D:(c + 1) * D] for c in keep], axis=1)
+        Wj[f"layers.{l}.mod.b"] = np.concatenate([mb[c * D:(c + 1) * D] for c in keep])
+    K, V, m = synth.make_prefix(wd)
+    x0 = synth.make_noise(wd)
+    dit = run(wd, Wd, K, V, m, x0)
+    joint = run(wj, Wj, K[:, :, :0], V[:, :, :0], m[:, :0], x0)
+    assert np.allclose(dit, joint, rtol=0, atol=1e-10)
+
+
+def test_dit_invariants():
+    """Masked rows and garbage are invisible, batched == alone, and a single
+    visible prefix row makes attn2 return that row's V for every query."""
+    w = small_c2(layers=2, steps=2, batch=2)
+    w = synth.Workload(**{**w.__dict__, "block": "dit", "name": "c5", "prefix_len": 600})
+    W = synth.make_weights(w)
+    m = synth.valid_masks(w, n_valid=(600, 530))
+    K, V, _ = synth.make_prefix(w, mask=m)
+    x0 = synth.make_noise(w)
+    a = run(w, W, K, V, m, x0)
+    Kg, Vg = K.copy(), V.copy()
+    synth.fill_garbage(w, Kg, Vg, m, "nan")
+    assert np.array_equal(run(w, W, Kg, Vg, m, x0), a)
+    w1 = synth.Workload(**{**w.__dict__, "batch": 1})
+    for b in range(2):
+        alone = run(w1, W, K[:, b:b + 1], V[:, b:b + 1], m[b:b + 1], x0[b:b + 1])
+        assert np.allclose(alone, a[b:b + 1], rtol=0, atol=1e-12)
+    # one visible key: attn2's output is its V row (softmax of one logit)
+    q = np.random.default_rng(3).standard_normal((5, 8, 256))
+    kk = np.random.default_rng(4).standard_normal((1, 1, 256))
+    vv = np.random.default_rng(5).standard_normal((1, 1, 256))
+    o = O.attention(q, kk, vv)
+    assert np.allclose(o, np.broadcast_to(vv[0, 0], o.shape), rtol=0, atol=1e-15)
+    assert np.array_equal(O.attention(q, kk[:0], vv[:0]), np.zeros_like(q))

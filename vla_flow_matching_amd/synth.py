@@ -56,6 +56,7 @@ class Workload:
     rms_eps: float = 1e-6
     index: int = 0        # N in the seed formula 100N+k
     gate_bias: float = 0.0  # offset on the gate chunks of every layer's modulation bias
+    block: str = "joint"    # "joint" attention over [prefix | actions], or "dit" (attn1 + attn2)
 
     def seed(self, k: int) -> int:
         return 100 * self.index + k
@@ -134,13 +135,16 @@ def weight_shapes(w: Workload) -> Dict[str, Tuple[int, ...]]:
         "action_out.w": (D, A), "action_out.b": (A,),
         "final_mod.w": (D, 2 * D), "final_mod.b": (2 * D,),
     }
+    nmod = 9 if w.block == "dit" else 6
     for l in range(w.n_layers):
         p = f"layers.{l}."
         shapes.update({
             p + "q": (D, qd), p + "k": (D, kd), p + "v": (D, kd), p + "o": (qd, D),
             p + "gate": (D, F), p + "up": (D, F), p + "down": (F, D),
-            p + "mod.w": (D, 6 * D), p + "mod.b": (6 * D,),
+            p + "mod.w": (D, nmod * D), p + "mod.b": (nmod * D,),
         })
+        if w.block == "dit":
+            shapes.update({p + "q2": (D, qd), p + "o2": (qd, D)})
     return shapes
 
 
@@ -179,8 +183,8 @@ def make_weights(w: Workload, seed: Optional[int] = None, std: float = 0.02,
         name, shape = items[i]
         x = _normal((base, i), shape, std)
         if gate_bias and name.endswith("mod.b"):
-            x[2 * D:3 * D] += np.float32(gate_bias)
-            x[5 * D:6 * D] += np.float32(gate_bias)
+            for chunk in range(2, x.shape[0] // D, 3):  # the gate of every (scale, shift, gate)
+                x[chunk * D:(chunk + 1) * D] += np.float32(gate_bias)
         return _encode(x, w.dtype)
 
     with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
