@@ -211,6 +211,63 @@ def run_gpu(name, calls, warmup, prefix_reps=0):
     return res
 
 
+def run_prepare(reps, context_width=2560, state_dim=14):
+    """Time ae_prepare_prefix on the MolmoBot-shaped workload: every layer's
+    context K/V from per-layer hidden states of a Qwen3-4B-wide context
+    (2560) plus the 14-D robot state, once per query."""
+    import torch
+
+    from vla_flow_matching_amd import binding, synth
+
+    w = synth.workload("c4", prefix_len=2047)
+    W = synth.make_weights(w)
+    CW = synth.make_context_weights(w, context_width, state_dim)
+    m = np.zeros((1, w.prefix_len), np.uint8)
+    m[0, :1600 + 27] = 1
+    H, _ = synth.make_context(w, context_width, mask=m)
+    state = synth.make_state(w, state_dim)
+    cfg = binding.make_config(w, max_prefix_len=2048, context_width=context_width, state_dim=state_dim)
+    with binding.ActionExpert(cfg) as ex:
+        ex.load_weights({**binding.weights_to_device(W, w.dtype), **binding.weights_to_device(CW, w.dtype)})
+        Ht = torch.from_numpy(H).to("cuda", torch.bfloat16)
+        mt = torch.from_numpy(m).cuda()
+        st = torch.from_numpy(state).cuda()
+        x = torch.from_numpy(synth.make_noise(w)).cuda()
+        for _ in range(3):
+            ex.prepare_prefix(Ht, mt, st)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        pairs = [(ev(), ev()) for _ in range(reps)]
+        for a, b in pairs:
+            a.record(stream)
+            ex.prepare_prefix(Ht, mt, st)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in pairs]
+        pairs = [(ev(), ev()) for _ in range(reps)]
+        for a, b in pairs:
+            a.record(stream)
+            ex.prepare_prefix(Ht, mt, st)
+            ex.denoise(x, w.n_steps)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms2 = [a.elapsed_time(b) for a, b in pairs]
+        if ex.stats()["device_errors"]:
+            raise DeviceErrors("prepare: a whole-call launch timed out")
+    L, P, kd = w.n_layers, w.prefix_len, w.n_kv_heads * w.head_dim
+    n = int(m.sum()) + 1
+    flops = 2 * L * (P + 1) * context_width * 2 * kd
+    byts = 2 * (L * P * context_width + L * context_width * 2 * kd + L * n * 2 * kd)
+    p50 = float(np.median(ms))
+    return {"workload": f"c4 context preparation: {L} layers, {P} context rows ({n - 1} visible) + the "
+                        f"{state_dim}-D state, context width {context_width}, Hkv {w.n_kv_heads} x {w.head_dim}",
+            "ms_p50": p50, "ms_p10": pct(ms, 10), "ms_p90": pct(ms, 90),
+            "prepare_plus_denoise_ms_p50": float(np.median(ms2)),
+            "algorithmic_flops": flops, "algorithmic_bytes": byts,
+            "achieved_TFLOPs": flops / (p50 * 1e-3) / 1e12, "achieved_GBps": byts / (p50 * 1e-3) / 1e9}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -372,6 +429,8 @@ def main():
                     "c4's weights (208 MB per step) and its visible K/V (~20 MB) fit in the 256 MB "
                     "last-level cache, so a call can run above the HBM bound; reported against 8 TB/s")
         line["workloads"] = others
+        if args.others != "none":
+            line["context_preparation"] = run_prepare(20)
         if "c5" in others:
             line["secondary"] = others["c5"]
         if "c5fp8" in others:
