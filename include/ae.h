@@ -63,6 +63,18 @@ typedef enum {
 
 typedef enum { AE_F32 = 0, AE_BF16 = 1, AE_FP8_E4M3 = 2 } ae_dtype;
 
+/* Decoder block of the expert.
+ * AE_BLOCK_JOINT: one attention of the action tokens over [visible prefix |
+ *   action tokens] with one softmax (Pi0.5 / LoongForge blog section 3).
+ * AE_BLOCK_DIT: the DiT-style block of the MolmoBot action expert (MolmoBot
+ *   PR Part 2: the block hands the cached context K/V to its second
+ *   attention; its correctness table lists cross_attn and self_attn apart):
+ *   attn1 of the action tokens over themselves (q, k, v, o), then attn2 of
+ *   separate queries q2 over the visible prefix only (o2), each with its own
+ *   softmax and its own adaRMS (scale, shift, gate), then the MLP; an empty
+ *   prefix makes attn2 add nothing.  bf16 projections only. */
+typedef enum { AE_BLOCK_JOINT = 0, AE_BLOCK_DIT = 1 } ae_block;
+
 /* Expert shape and numerics.  Fixed for the life of a handle. */
 typedef struct {
   int n_layers;         /* decoder layers L */
@@ -90,6 +102,7 @@ typedef struct {
                            (multiple of 64, <= 8192; bf16 only); 0: no context projection */
   int state_dim;        /* size of the robot state ae_prepare_prefix encodes as one more
                            context row (<= 64, needs context_width); 0: none */
+  int block_type;       /* ae_block: AE_BLOCK_JOINT (0) or AE_BLOCK_DIT (1) */
 } ae_config;
 
 /* One named logical weight, caller-owned device memory, dtype = act_dtype.
@@ -101,6 +114,10 @@ typedef struct {
  *   layers.l.o [Hq*dh,D]  layers.l.gate [D,F]  layers.l.up [D,F]  layers.l.down [F,D]
  *   layers.l.mod.w [D,6D] layers.l.mod.b [6D]  (chunks: scale_a, shift_a,
  *   gate_a, scale_m, shift_m, gate_m)
+ * With block_type = AE_BLOCK_DIT instead: layers.l.mod.w [D,9D] and
+ * layers.l.mod.b [9D] (chunks: scale, shift, gate of attn1, of attn2, of the
+ * MLP), plus layers.l.q2 [D,Hq*dh] and layers.l.o2 [Hq*dh,D] (attn2's query
+ * and output projections; attn2 reads the prefix K/V).
  * With context_width = Dc > 0 also: layers.l.ctx_k [Dc,Hkv*dh], layers.l.ctx_v
  * [Dc,Hkv*dh] (each layer's context K and V projections); with state_dim = S > 0
  * also: state_in.w [S,Dc], state_in.b [Dc] (the state's input layer). */

@@ -170,3 +170,22 @@ def test_invalid_context_config(lib, changes):
 def test_context_needs_bf16(lib):
     st, h = _create(lib, context_width=128)  # the c1 workload is fp32
     assert st == binding.AE_ERR_UNSUPPORTED and not h.value
+
+
+def test_dit_block_configs(lib):
+    """The DiT-style block: block_type outside {0, 1} is invalid; it needs
+    bf16 weights and projections and 128-multiple widths; the c2 shapes in
+    bf16 pass every check and then find no device."""
+    st, h = _create(lib, block_type=2)
+    assert st == binding.AE_ERR_INVALID_ARGUMENT and not h.value
+    st, h = _create(lib, block_type=binding.AE_BLOCK_DIT)  # the c1 workload is fp32
+    assert st == binding.AE_ERR_UNSUPPORTED and not h.value
+    cfg = binding.make_config(synth.workload("c2", block="dit"))
+    assert cfg.block_type == binding.AE_BLOCK_DIT
+    for k, v in (("proj_weight_dtype", binding.AE_FP8_E4M3), ("width", 960)):
+        c = binding.make_config(synth.workload("c2", block="dit"))
+        setattr(c, k, v)
+        h = ctypes.c_void_p()
+        assert lib.ae_create(ctypes.byref(c), ctypes.byref(h)) == binding.AE_ERR_UNSUPPORTED and not h.value
+    h = ctypes.c_void_p()
+    assert lib.ae_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.AE_ERR_HIP and not h.value

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libae.so")
 AE_OK, AE_ERR_INVALID_ARGUMENT, AE_ERR_SHAPE_MISMATCH, AE_ERR_NOT_READY = 0, 1, 2, 3
 AE_ERR_OUT_OF_MEMORY, AE_ERR_UNSUPPORTED, AE_ERR_HIP = 4, 5, 6
 AE_F32, AE_BF16, AE_FP8_E4M3 = 0, 1, 2
+AE_BLOCK_JOINT, AE_BLOCK_DIT = 0, 1
 
 # every function include/ae.h declares
 EXPORTS = ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_prepare_prefix", "ae_set_prefix_buckets",
@@ -35,7 +36,7 @@ class Config(ctypes.Structure):
         ("act_dtype", ctypes.c_int), ("proj_weight_dtype", ctypes.c_int),
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("use_graphs", ctypes.c_int),
         ("graph_cache_size", ctypes.c_int), ("graph_cache_evict", ctypes.c_int),
-        ("context_width", ctypes.c_int), ("state_dim", ctypes.c_int),
+        ("context_width", ctypes.c_int), ("state_dim", ctypes.c_int), ("block_type", ctypes.c_int),
     ]
 
 
@@ -106,7 +107,8 @@ def make_config(w, max_batch: Optional[int] = None, max_prefix_len: Optional[int
                   w.batch if max_batch is None else max_batch,
                   w.n_steps if max_steps is None else max_steps,
                   act, proj, float(w.rope_theta), float(w.rms_eps), int(bool(use_graphs)),
-                  int(graph_cache_size), int(bool(graph_cache_evict)), int(context_width), int(state_dim))
+                  int(graph_cache_size), int(bool(graph_cache_evict)), int(context_width), int(state_dim),
+                  AE_BLOCK_DIT if getattr(w, "block", "joint") == "dit" else AE_BLOCK_JOINT)
 
 
 def _stream_ptr(stream) -> ctypes.c_void_p:

@@ -7,7 +7,10 @@
 // order), and the QKV epilogue appends the T action rows right after them, so
 // the keys of request b are the contiguous rows [0, n_valid[b] + T) of its
 // cache: masked rows are never read, and there is no per-element mask except
-// the ragged tail of the last key block.
+// the ragged tail of the last key block.  The DiT-style block (MolmoBot PR
+// Part 2) runs the same kernel twice with other key ranges: its attn1 over a
+// cache of the action rows alone (n_valid 0), its attn2 over the prefix alone
+// (no action rows appended; with no visible row the output is zero).
 //
 // One wave owns 16 query rows of one KV group (rows = (query head in group,
 // action token) pairs; all Hq/Hkv heads of a group share the keys).  Per key
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   const int wave = threadIdx.x / kWave, rg = wave % kRowWaves, kh = wave / kRowWaves;
   const int lane = threadIdx.x % kWave;
   const int grp = lane / 16;
-  const int len = p.n_valid[b] + p.T;
+  const int len = p.n_valid[b] + p.n_act;
   const int k_begin = s * p.kc_len;
   const int k_end = min(k_begin + p.kc_len, len);
   const int n_blk = k_end > k_begin ? (k_end - k_begin + KSTEP - 1) / KSTEP : 0;
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
 #pragma unroll
   for (int c = 0; c < kQB; ++c) {
     if (kh != 0 || !qvalid[c]) continue;
-    const float inv = 1.0f / l_run[c];
+    const float inv = l_run[c] > 0.0f ? 1.0f / l_run[c] : 0.0f;  // (no key: zeros)
     T* orow = static_cast<T*>(p.o) + static_cast<size_t>(b * p.T + tt[c]) * p.ldo + (g * G + hh[c]) * DH;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {

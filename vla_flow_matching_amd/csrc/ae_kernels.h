@@ -68,6 +68,10 @@ struct AttnArgs {
   void* o;
   int ldo;
   int T, Hq, Hkv, dh;
+  // keys of request b: cache rows [0, n_valid[b] + n_act) (n_act = T: the
+  // action tokens' own rows follow the prefix; 0: the prefix alone); a query
+  // with no key gets zeros
+  int n_act;
   int batch, n_qg, nsplit, kc_len;
   float scale_log2;
   float* partial;
@@ -101,9 +105,10 @@ hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s
 // p[0 .. n) = 0 with a kernel (a fill a captured graph can hold)
 hipError_t launch_zero_ints(int* p, size_t n, hipStream_t s);
 // out[k][l][n] = sum_d mod[k][l][which][d] * W_l[d][n] for packed weights
-// (n in packed column order), steps k < n_steps, layers l < L.
+// (n in packed column order), steps k < n_steps, layers l < L, with nchunk
+// modulation chunks of D per layer (6 joint, 9 DiT-style).
 hipError_t launch_shift_bias(Dt dt, const uint4* W, size_t layer_stride, int K, int N, const float* mod,
-                             int n_steps, int L, int D, int which, float* out, hipStream_t s);
+                             int n_steps, int L, int D, int nchunk, int which, float* out, hipStream_t s);
 // Y[m][n] = act(sum_k X[m][k] W[k][n] + b[n]), m < M <= 16; act 0 none, 1 SiLU.
 // grid.y = n_mat matrices with strides (W, b, Y advance by the given strides).
 hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const void* W, int ldw,

@@ -321,13 +321,13 @@ __global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V
 // (g, j) holds k-slot g of column j; fp32 sums, one step at a time.
 template <typename T>
 __global__ void shift_bias_kernel(const uint4* W, size_t layer_stride, int K, int N, const float* mod,
-                                  int n_steps, int L, int D, int which, float* out) {
+                                  int n_steps, int L, int D, int nchunk, int which, float* out) {
   constexpr int E = Mma<T>::E, KSTEP = Mma<T>::KSTEP;
   const int nb = blockIdx.x, l = blockIdx.y, lane = threadIdx.x, g = lane / 16;
   const int k_frags = K / KSTEP;
   const uint4* Wf = W + l * layer_stride + static_cast<size_t>(nb) * k_frags * kWave + lane;
   for (int k = 0; k < n_steps; ++k) {
-    const float* sh = mod + ((static_cast<size_t>(k) * L + l) * 6 + which) * D;
+    const float* sh = mod + ((static_cast<size_t>(k) * L + l) * nchunk + which) * D;
     float acc = 0.0f;
     for (int kf = 0; kf < k_frags; ++kf) {
       const uint4 w = Wf[static_cast<size_t>(kf) * kWave];
@@ -349,15 +349,16 @@ __global__ void shift_bias_kernel(const uint4* W, size_t layer_stride, int K, in
 }  // namespace
 
 hipError_t launch_shift_bias(Dt dt, const uint4* W, size_t layer_stride, int K, int N, const float* mod,
-                             int n_steps, int L, int D, int which, float* out, hipStream_t s) {
-  if (N % 16 || K % 32 || K > D || n_steps < 1 || L < 1) return hipErrorInvalidValue;
+                             int n_steps, int L, int D, int nchunk, int which, float* out, hipStream_t s) {
+  if (N % 16 || K % 32 || K > D || n_steps < 1 || L < 1 || which < 0 || which >= nchunk)
+    return hipErrorInvalidValue;
   dim3 grid(N / 16, L), block(kWave);
   if (dt == DT_BF16)
     hipLaunchKernelGGL(shift_bias_kernel<bf16_t>, grid, block, 0, s, W, layer_stride, K, N, mod, n_steps, L,
-                       D, which, out);
+                       D, nchunk, which, out);
   else
     hipLaunchKernelGGL(shift_bias_kernel<float>, grid, block, 0, s, W, layer_stride, K, N, mod, n_steps, L, D,
-                       which, out);
+                       nchunk, which, out);
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <string>
@@ -79,6 +80,8 @@ struct ae_handle {
   int L = 0, D = 0, Hq = 0, Hkv = 0, dh = 0, F = 0, T = 0, A = 0, Pmax = 0, Bmax = 0, Nmax = 0;
   int S_max = 0, qdim = 0, kvdim = 0, qkv_n = 0, ssq_tiles = 0, Mmax = 0;
   int Dc = 0, Sd = 0;  // context width and robot-state size (0: no context preparation)
+  bool dit = false;    // DiT-style block: attn1 over the action tokens, attn2 over the prefix
+  int nmod = 6;        // modulation chunks of D per layer (9 in the DiT-style block)
 
   // weights (library-owned copies)
   void *tw1 = nullptr, *tb1 = nullptr, *tw2 = nullptr, *tb2 = nullptr;
@@ -86,6 +89,9 @@ struct ae_handle {
   float *w_in = nullptr, *b_in = nullptr, *w_out = nullptr, *b_out = nullptr;
   uint4 *wqkv = nullptr, *wo = nullptr, *wgu = nullptr, *wd = nullptr;
   size_t sqkv = 0, so = 0, sgu = 0, sd = 0;  // per-layer strides in uint4
+  // DiT-style block: attn2's query and output projections (strides sq2, so)
+  uint4 *wq2 = nullptr, *wo2 = nullptr;
+  size_t sq2 = 0;
 
   // context preparation: each layer's [ctx_k | ctx_v] packed (RoPE pairs
   // together), RoPE tables of positions 0 .. max_prefix_len, the state's
@@ -98,6 +104,11 @@ struct ae_handle {
 
   // prefix state
   void *kcache = nullptr, *vtcache = nullptr;
+  // DiT-style block: attn1's K/V of the action rows alone ([L][Bmax][Hkv]
+  // [S_self][dh]), read with the all-zero visible counts `zeros`
+  void *kself = nullptr, *vtself = nullptr;
+  int S_self = 0;
+  int* zeros = nullptr;
   int *comp_idx = nullptr, *n_valid = nullptr;
   float *rope_cos = nullptr, *rope_sin = nullptr;
 
@@ -109,6 +120,7 @@ struct ae_handle {
   // folded through W_qkv / W_gate-up ([steps][L][N], packed column order)
   void* ha = nullptr;
   float *bq = nullptr, *bg = nullptr;
+  float* bq2 = nullptr;  // DiT-style block: attn2's shift through W_q2 ([steps][L][qdim])
 
   // split scratch of this handle's calls
   ScratchSet own;
@@ -197,6 +209,8 @@ std::string validate_config(const ae_config* c) {
     return "context_width must be 0 or a multiple of 64 up to 8192";
   if (c->state_dim < 0 || c->state_dim > 64) return "state_dim must be in [0, 64]";
   if (c->state_dim > 0 && c->context_width == 0) return "state_dim needs context_width";
+  if (c->block_type != AE_BLOCK_JOINT && c->block_type != AE_BLOCK_DIT)
+    return "block_type must be AE_BLOCK_JOINT or AE_BLOCK_DIT";
   return "";
 }
 
@@ -205,6 +219,14 @@ std::string unsupported_config(const ae_config* c) {
     return "head_dim must be 64, 128 or 256";
   if (c->context_width > 0 && (c->act_dtype != AE_BF16 || (2 * c->n_kv_heads * c->head_dim) % 128))
     return "context preparation needs bf16 and 2 n_kv_heads head_dim a multiple of 128";
+  if (c->block_type == AE_BLOCK_DIT) {
+    const int qd = c->n_q_heads * c->head_dim, qkv = qd + 2 * c->n_kv_heads * c->head_dim;
+    if (c->act_dtype != AE_BF16 || c->proj_weight_dtype != AE_BF16)
+      return "the DiT-style block needs bf16 weights and projections";
+    if (c->width % 128 || qkv % 128 || qd % 128 || (2 * c->mlp_dim) % 128 || c->mlp_dim % 64)
+      return "the DiT-style block needs width, n_q_heads head_dim, (n_q_heads + 2 n_kv_heads) "
+             "head_dim and 2 mlp_dim to be multiples of 128";
+  }
   if (c->proj_weight_dtype != c->act_dtype) {
     if (c->proj_weight_dtype != AE_FP8_E4M3 || c->act_dtype != AE_BF16)
       return "proj_weight_dtype must equal act_dtype (or be AE_FP8_E4M3 with bf16)";
@@ -311,13 +333,14 @@ PersistPlans plan_persist(const ae_handle* h) {
 // The whole-call kernel covers one 64-row tile and action_dim <= 32; other
 // shapes run the per-phase kernels.
 bool use_persist(const ae_handle* h, int batch) {
-  return h->G > 0 && !h->fp8 && batch * h->T <= kTileM && h->A <= 32;
+  return h->G > 0 && !h->fp8 && !h->dit && batch * h->T <= kTileM && h->A <= 32;
 }
 
 // The batched tiled path: the four projection GEMMs of a layer.
 struct TPlans {
   int op;
   TGemmPlan qkv, o, gu, d;
+  TGemmPlan q2;  // DiT-style block: attn2's queries
 };
 
 TPlans plan_tlayer(const ae_handle* h, int M) {
@@ -328,6 +351,7 @@ TPlans plan_tlayer(const ae_handle* h, int M) {
   p.o = plan_tgemm(M, h->D, h->qdim, kb, kTargetBlocks);
   p.gu = plan_tgemm(M, 2 * h->F, h->D, kc, kTargetBlocks);
   p.d = plan_tgemm(M, h->D, h->F, kc, kTargetBlocks);
+  p.q2 = plan_tgemm(M, h->qdim, h->D, kb, kTargetBlocks);
   return p;
 }
 
@@ -381,16 +405,21 @@ ae_status enqueue_tpath(ae_handle* h, int steps, hipStream_t s) {
                                D, h->z + static_cast<size_t>(r0) * D, D, 1, 1, 0, 0, 0, s));
     AE_LAUNCH(launch_gemv_rows(h->dt, h->z + static_cast<size_t>(r0) * D, D, mr, D, h->tw2, D, h->tb2,
                                D, h->c + static_cast<size_t>(r0) * D, D, 1, 1, 0, 0, 0, s));
-    AE_LAUNCH(launch_gemv_rows(h->dt, h->c + static_cast<size_t>(r0) * D, D, mr, D, h->mod_w, 6 * D,
-                               h->mod_b, 6 * D, h->mod + static_cast<size_t>(r0) * L * 6 * D,
-                               L * 6 * D, 0, L, static_cast<size_t>(D) * 6 * D, 6 * D, 6 * D, s));
+    const int nm = h->nmod * D;
+    AE_LAUNCH(launch_gemv_rows(h->dt, h->c + static_cast<size_t>(r0) * D, D, mr, D, h->mod_w, nm,
+                               h->mod_b, nm, h->mod + static_cast<size_t>(r0) * L * nm,
+                               L * nm, 0, L, static_cast<size_t>(D) * nm, nm, nm, s));
     AE_LAUNCH(launch_gemv_rows(h->dt, h->c + static_cast<size_t>(r0) * D, D, mr, D, h->fmod_w, 2 * D,
                                h->fmod_b, 2 * D, h->fmod + static_cast<size_t>(r0) * 2 * D, 2 * D, 0,
                                1, 0, 0, 0, s));
   }
-  if (h->bq) {  // shift W of the attention (row 1) and MLP (row 4) norms
-    AE_LAUNCH(launch_shift_bias(h->dt, h->wqkv, h->sqkv, D, h->qkv_n, h->mod, steps, L, D, 1, h->bq, s));
-    AE_LAUNCH(launch_shift_bias(h->dt, h->wgu, h->sgu, D, 2 * h->F, h->mod, steps, L, D, 4, h->bg, s));
+  if (h->dit) {  // shift W of the attn1 (chunk 1), attn2 (chunk 4) and MLP (chunk 7) norms
+    AE_LAUNCH(launch_shift_bias(h->dt, h->wqkv, h->sqkv, D, h->qkv_n, h->mod, steps, L, D, 9, 1, h->bq, s));
+    AE_LAUNCH(launch_shift_bias(h->dt, h->wq2, h->sq2, D, h->qdim, h->mod, steps, L, D, 9, 4, h->bq2, s));
+    AE_LAUNCH(launch_shift_bias(h->dt, h->wgu, h->sgu, D, 2 * h->F, h->mod, steps, L, D, 9, 7, h->bg, s));
+  } else if (h->bq) {  // shift W of the attention (chunk 1) and MLP (chunk 4) norms
+    AE_LAUNCH(launch_shift_bias(h->dt, h->wqkv, h->sqkv, D, h->qkv_n, h->mod, steps, L, D, 6, 1, h->bq, s));
+    AE_LAUNCH(launch_shift_bias(h->dt, h->wgu, h->sgu, D, 2 * h->F, h->mod, steps, L, D, 6, 4, h->bg, s));
   }
   return AE_OK;
 }
@@ -425,7 +454,7 @@ ae_status enqueue_loop(ae_handle* h, const ScratchSet& sc, int batch, int steps,
       std::memset(&at, 0, sizeof(at));
       at.q = h->q; at.ldq = h->qdim; at.kcache = kc; at.vtcache = vc; at.S_max = h->S_max;
       at.n_valid = h->n_valid; at.o = h->o; at.ldo = h->qdim;
-      at.T = h->T; at.Hq = h->Hq; at.Hkv = h->Hkv; at.dh = h->dh;
+      at.T = h->T; at.Hq = h->Hq; at.Hkv = h->Hkv; at.dh = h->dh; at.n_act = h->T;
       at.batch = batch; at.n_qg = ap.n_qg; at.nsplit = ap.nsplit; at.kc_len = ap.kc_len;
       at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->dh)));
       at.partial = sc.apart; at.counters = sc.acnt;
@@ -461,7 +490,10 @@ ae_status enqueue_loop(ae_handle* h, const ScratchSet& sc, int batch, int steps,
 // product: the residual epilogues (and action-in) write the shadow
 // ha = bf16(h (1 + scale)) of the next norm with h's row sums of squares, and
 // QKV / gate-up finish with 1 / rms and the precomputed shift W.
+ae_status enqueue_loop_dit(ae_handle* h, const ScratchSet& sc, int batch, int steps, hipStream_t s);
+
 ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int steps, hipStream_t s) {
+  if (h->dit) return enqueue_loop_dit(h, sc, batch, steps, s);
   const int D = h->D, L = h->L, F = h->F, M = batch * h->T;
   const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
   const TPlans tp = plan_tlayer(h, M);
@@ -521,7 +553,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int 
       std::memset(&at, 0, sizeof(at));
       at.q = h->q; at.ldq = h->qdim; at.kcache = kc; at.vtcache = vc; at.S_max = h->S_max;
       at.n_valid = h->n_valid; at.o = h->o; at.ldo = h->qdim;
-      at.T = h->T; at.Hq = h->Hq; at.Hkv = h->Hkv; at.dh = h->dh;
+      at.T = h->T; at.Hq = h->Hq; at.Hkv = h->Hkv; at.dh = h->dh; at.n_act = h->T;
       at.batch = batch; at.n_qg = ap.n_qg; at.nsplit = ap.nsplit; at.kc_len = ap.kc_len;
       at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->dh)));
       at.partial = sc.apart; at.counters = sc.acnt;
@@ -569,6 +601,134 @@ ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int 
       // final norm, which reads h itself)
       if (!f8) resid_out(g, l + 1 < L ? md + 6 * D : nullptr);
       AE_LAUNCH(launch_tgemm(tp.op, EPI_RESID, g, tp.d.blocks, s));
+    }
+    const float* fm = h->fmod + static_cast<size_t>(k) * 2 * D;
+    AE_LAUNCH(launch_action_out(h->x, M, h->A, h->h, D, fm, fm + D, h->cfg.rms_eps, h->w_out,
+                                h->b_out, dt, s));
+  }
+  return AE_OK;
+}
+
+// The N Euler steps with the DiT-style block (MolmoBot PR Part 2: the block
+// hands the cached context K/V to its second attention; its correctness
+// table lists cross_attn and self_attn apart), on the batched tiled path in
+// bf16.  Per layer, with the nine modulation chunks (scale, shift, gate of
+// attn1, attn2 and the MLP):
+//   QKV + RoPE of adaRMS_1(h) into the action-only cache; attn1 over it;
+//   O-proj + gate_1 residual;
+//   q2 + RoPE of adaRMS_2(h); attn2 over the visible prefix alone;
+//   o2 + gate_2 residual;
+//   gate/up of adaRMS_3(h) + gelu; down + gate_3 residual.
+// Action token t of request b sits at position n_b + t in both attentions
+// (only differences matter in attn1).  The norms run after the products as
+// in the joint block: each residual epilogue writes the next norm's
+// modulated shadow and row sums of squares.
+ae_status enqueue_loop_dit(ae_handle* h, const ScratchSet& sc, int batch, int steps, hipStream_t s) {
+  const int D = h->D, L = h->L, F = h->F, M = batch * h->T, NM = 9 * D;
+  const size_t kv_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_max * h->dh * h->esz;
+  const size_t self_layer = static_cast<size_t>(h->Bmax) * h->Hkv * h->S_self * h->dh * h->esz;
+  const TPlans tp = plan_tlayer(h, M);
+  const AttnPlan a_self = plan_attention_batched(h, batch, 0);
+  const AttnPlan a_cross = plan_attention_batched(h, batch, h->span);
+  const float dt = -1.0f / static_cast<float>(steps);
+  const float eps = h->cfg.rms_eps;
+  const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(h->dh)));
+  uint16_t* ha = static_cast<uint16_t*>(h->ha);
+  auto post_norm = [&](TGemmArgs& g, const float* bias) {
+    g.A = ha; g.lda_bytes = static_cast<size_t>(D) * 2;
+    g.bias = bias; g.ssq = h->ssq; g.ldssq = h->Mmax; g.ssq_tiles = h->ssq_tiles; g.eps = eps;
+  };
+  auto resid_out = [&](TGemmArgs& g, const float* next_scale) {
+    g.ssq = h->ssq; g.ldssq = h->Mmax; g.nsc = next_scale; g.ha = ha;
+  };
+  // queries (q or q2, RoPE at n_b + t) and, with a cache, the action rows' K/V
+  auto qkv_args = [&](TGemmArgs& g, void* kc, void* vc, const int* nv, int S, int Hkv) {
+    g.q = h->q; g.ldq = h->qdim; g.kcache = kc; g.vtcache = vc; g.n_valid = nv;
+    g.rope_cos = h->rope_cos; g.rope_sin = h->rope_sin;
+    g.T = h->T; g.Hq = h->Hq; g.Hkv = Hkv; g.dh = h->dh; g.S_max = S;
+  };
+  struct Pf {
+    const uint4* p;
+    int n4;
+  };
+  auto attention = [&](const AttnPlan& ap, const void* kc, const void* vc, int S, const int* nv, int n_act,
+                       std::initializer_list<Pf> pf) -> ae_status {
+    AttnArgs at;
+    std::memset(&at, 0, sizeof(at));
+    at.q = h->q; at.ldq = h->qdim; at.kcache = kc; at.vtcache = vc; at.S_max = S;
+    at.n_valid = nv; at.n_act = n_act; at.o = h->o; at.ldo = h->qdim;
+    at.T = h->T; at.Hq = h->Hq; at.Hkv = h->Hkv; at.dh = h->dh;
+    at.batch = batch; at.n_qg = ap.n_qg; at.nsplit = ap.nsplit; at.kc_len = ap.kc_len;
+    at.scale_log2 = scale_log2;
+    at.partial = sc.apart; at.counters = sc.acnt;
+    // warm the last-level cache with the next products' weights
+    at.pf_blocks = kPrefetchBlocks;
+    int i = 0;
+    for (const Pf& w : pf) {
+      at.pf[i] = w.p;
+      at.pf_n4[i++] = w.n4;
+    }
+    AE_LAUNCH(launch_attention(h->dt, at, s));
+    return AE_OK;
+  };
+  const int o_n4 = static_cast<int>(static_cast<size_t>(h->qdim) * D * 2 / 16);
+  const int q2_n4 = o_n4;
+  const int gu_n4 = static_cast<int>(static_cast<size_t>(D) * 2 * F * 2 / 16);
+  const int d_n4 = static_cast<int>(static_cast<size_t>(F) * D * 2 / 16);
+  const int qkv_n4 = static_cast<int>(static_cast<size_t>(D) * h->qkv_n * 2 / 16);
+  for (int k = 0; k < steps; ++k) {
+    const float* md0 = h->mod + static_cast<size_t>(k) * L * NM;
+    AE_LAUNCH(launch_action_in(h->x, M, h->A, h->w_in, h->b_in, h->h, D, h->ssq, h->Mmax, s, ha, md0));
+    for (int l = 0; l < L; ++l) {
+      const float* md = md0 + static_cast<size_t>(l) * NM;
+      const size_t it = static_cast<size_t>(k) * L + l;
+      char* ks = static_cast<char*>(h->kself) + l * self_layer;
+      char* vs = static_cast<char*>(h->vtself) + l * self_layer;
+      const char* kc = static_cast<const char*>(h->kcache) + l * kv_layer;
+      const char* vc = static_cast<const char*>(h->vtcache) + l * kv_layer;
+
+      // attn1: the action tokens among themselves
+      TGemmArgs g = base_tgemm(h, sc, tp.qkv, M, h->qkv_n, D);
+      g.W = h->wqkv + l * h->sqkv;
+      post_norm(g, h->bq + it * h->qkv_n);
+      qkv_args(g, ks, vs, h->zeros, h->S_self, h->Hkv);
+      AE_LAUNCH(launch_tgemm(OP_BF16, EPI_QKV, g, tp.qkv.blocks, s));
+      ae_status r = attention(a_self, ks, vs, h->S_self, h->zeros, h->T,
+                              {{h->wo + l * h->so, o_n4}, {h->wq2 + l * h->sq2, q2_n4}});
+      if (r != AE_OK) return r;
+      g = base_tgemm(h, sc, tp.o, M, D, h->qdim);
+      g.A = h->o; g.lda_bytes = static_cast<size_t>(h->qdim) * 2; g.W = h->wo + l * h->so;
+      g.h = h->h; g.ldh = D; g.gate = md + 2 * D;
+      resid_out(g, md + 3 * D);
+      AE_LAUNCH(launch_tgemm(OP_BF16, EPI_RESID, g, tp.o.blocks, s));
+
+      // attn2: the action queries over the visible prefix
+      g = base_tgemm(h, sc, tp.q2, M, h->qdim, D);
+      g.W = h->wq2 + l * h->sq2;
+      post_norm(g, h->bq2 + it * h->qdim);
+      qkv_args(g, nullptr, nullptr, h->n_valid, h->S_max, 0);
+      AE_LAUNCH(launch_tgemm(OP_BF16, EPI_QKV, g, tp.q2.blocks, s));
+      r = attention(a_cross, kc, vc, h->S_max, h->n_valid, 0,
+                    {{h->wo2 + l * h->so, o_n4}, {h->wgu + l * h->sgu, gu_n4}, {h->wd + l * h->sd, d_n4},
+                     {h->wqkv + ((l + 1) % L) * h->sqkv, qkv_n4}});
+      if (r != AE_OK) return r;
+      g = base_tgemm(h, sc, tp.o, M, D, h->qdim);
+      g.A = h->o; g.lda_bytes = static_cast<size_t>(h->qdim) * 2; g.W = h->wo2 + l * h->so;
+      g.h = h->h; g.ldh = D; g.gate = md + 5 * D;
+      resid_out(g, md + 6 * D);
+      AE_LAUNCH(launch_tgemm(OP_BF16, EPI_RESID, g, tp.o.blocks, s));
+
+      // MLP
+      g = base_tgemm(h, sc, tp.gu, M, 2 * F, D);
+      g.W = h->wgu + l * h->sgu;
+      g.out = h->act; g.ldo = F;
+      post_norm(g, h->bg + it * 2 * F);
+      AE_LAUNCH(launch_tgemm(OP_BF16, EPI_GELU, g, tp.gu.blocks, s));
+      g = base_tgemm(h, sc, tp.d, M, D, F);
+      g.A = h->act; g.lda_bytes = static_cast<size_t>(F) * 2; g.W = h->wd + l * h->sd;
+      g.h = h->h; g.ldh = D; g.gate = md + 8 * D;
+      resid_out(g, l + 1 < L ? md + NM : nullptr);  // the next layer's attn1 norm
+      AE_LAUNCH(launch_tgemm(OP_BF16, EPI_RESID, g, tp.d.blocks, s));
     }
     const float* fm = h->fmod + static_cast<size_t>(k) * 2 * D;
     AE_LAUNCH(launch_action_out(h->x, M, h->A, h->h, D, fm, fm + D, h->cfg.rms_eps, h->w_out,
@@ -628,7 +788,8 @@ ScratchNeed scratch_need(const ae_handle* h, int b, int span, bool persist, bool
   }
   if (h->tiled) {
     const TPlans tp = plan_tlayer(h, b * h->T);
-    for (const TGemmPlan* g : {&tp.qkv, &tp.o, &tp.gu, &tp.d}) {
+    for (const TGemmPlan* g : {&tp.qkv, &tp.o, &tp.gu, &tp.d, &tp.q2}) {
+      if (g == &tp.q2 && !h->dit) continue;
       n.gfl = std::max(n.gfl, tgemm_partial_floats(*g));
       n.gcn = std::max(n.gcn, static_cast<size_t>(g->m_tiles) * g->n_tiles);
     }
@@ -693,8 +854,12 @@ std::vector<WeightSpec> weight_specs(const ae_handle* h) {
     v.push_back({p + "gate", {D, F}});
     v.push_back({p + "up", {D, F}});
     v.push_back({p + "down", {F, D}});
-    v.push_back({p + "mod.w", {D, 6 * D}});
-    v.push_back({p + "mod.b", {6 * D}});
+    v.push_back({p + "mod.w", {D, h->nmod * D}});
+    v.push_back({p + "mod.b", {h->nmod * D}});
+    if (h->dit) {
+      v.push_back({p + "q2", {D, qd}});
+      v.push_back({p + "o2", {qd, D}});
+    }
     if (h->Dc > 0) {
       v.push_back({p + "ctx_k", {h->Dc, kd}});
       v.push_back({p + "ctx_v", {h->Dc, kd}});
@@ -882,6 +1047,9 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   h->fp8 = cfg->proj_weight_dtype == AE_FP8_E4M3;
   h->Dc = cfg->context_width;
   h->Sd = cfg->state_dim;
+  h->dit = cfg->block_type == AE_BLOCK_DIT;
+  h->nmod = h->dit ? 9 : 6;
+  h->S_self = (h->T + 63) / 64 * 64;
   h->tiled = h->dt == DT_BF16 && h->D % 128 == 0 && h->qkv_n % 128 == 0 && (2 * h->F) % 128 == 0 &&
              h->qdim % 64 == 0 && h->F % 64 == 0;
 
@@ -917,8 +1085,9 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   AE_ALLOC(h->tb2, D * es);
   AE_ALLOC(h->fmod_w, D * 2 * D * es);
   AE_ALLOC(h->fmod_b, 2 * D * es);
-  AE_ALLOC(h->mod_w, L * D * 6 * D * es);
-  AE_ALLOC(h->mod_b, L * 6 * D * es);
+  const size_t NM = static_cast<size_t>(h->nmod) * D;  // modulation columns per layer
+  AE_ALLOC(h->mod_w, L * D * NM * es);
+  AE_ALLOC(h->mod_b, L * NM * es);
   AE_ALLOC(h->w_in, A * D * 4);
   AE_ALLOC(h->b_in, D * 4);
   AE_ALLOC(h->w_out, D * A * 4);
@@ -931,6 +1100,16 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   AE_ALLOC(h->wo, L * h->so * 16);
   AE_ALLOC(h->wgu, L * h->sgu * 16);
   AE_ALLOC(h->wd, L * h->sd * 16);
+  if (h->dit) {
+    h->sq2 = elems_packed(h->D, h->qdim, ks);
+    AE_ALLOC(h->wq2, L * h->sq2 * 16);
+    AE_ALLOC(h->wo2, L * h->so * 16);
+    const size_t sb = L * h->Bmax * h->Hkv * static_cast<size_t>(h->S_self) * h->dh * es;
+    AE_ALLOC(h->kself, sb);
+    AE_ALLOC(h->vtself, sb);
+    AE_ALLOC(h->zeros, static_cast<size_t>(h->Bmax) * 4);
+    AE_ALLOC(h->bq2, static_cast<size_t>(h->Nmax) * L * h->qdim * 4);
+  }
 
   const size_t kvbytes = L * h->Bmax * h->Hkv * static_cast<size_t>(h->S_max) * h->dh * es;
   AE_ALLOC(h->kcache, kvbytes);
@@ -964,7 +1143,7 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   AE_ALLOC(h->e, static_cast<size_t>(h->Nmax) * D * 4);
   AE_ALLOC(h->z, static_cast<size_t>(h->Nmax) * D * 4);
   AE_ALLOC(h->c, static_cast<size_t>(h->Nmax) * D * 4);
-  AE_ALLOC(h->mod, static_cast<size_t>(h->Nmax) * L * 6 * D * 4);
+  AE_ALLOC(h->mod, static_cast<size_t>(h->Nmax) * L * NM * 4);
   AE_ALLOC(h->fmod, static_cast<size_t>(h->Nmax) * 2 * D * 4);
 
   // the largest call's scratch, over every batch, path and prefix bucket
@@ -1108,8 +1287,15 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
   }
   for (int l = 0; l < h->L; ++l) {
     const std::string p = "layers." + std::to_string(l) + ".";
-    AE_HIP(h, cp(static_cast<char*>(h->mod_w) + l * D * 6 * D * es, p + "mod.w", D * 6 * D * es));
-    AE_HIP(h, cp(static_cast<char*>(h->mod_b) + l * 6 * D * es, p + "mod.b", 6 * D * es));
+    const size_t NM = static_cast<size_t>(h->nmod) * D;
+    AE_HIP(h, cp(static_cast<char*>(h->mod_w) + l * D * NM * es, p + "mod.w", D * NM * es));
+    AE_HIP(h, cp(static_cast<char*>(h->mod_b) + l * NM * es, p + "mod.b", NM * es));
+    if (h->dit) {  // q2 in the QKV packing with no K/V heads (its RoPE pairs together)
+      AE_HIP(h, launch_pack(h->dt, PACK_QKV, get(p + "q2"), nullptr, nullptr, h->D, h->qdim, h->qdim, 0, 0,
+                            h->Hq, 0, h->dh, h->wq2 + l * h->sq2, st));
+      AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get(p + "o2"), nullptr, nullptr, h->qdim, h->D, h->D, 0,
+                            0, h->Hq, h->Hkv, h->dh, h->wo2 + l * h->so, st));
+    }
     AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get(p + "o"), nullptr, nullptr, h->qdim, h->D, h->D, 0,
                           0, h->Hq, h->Hkv, h->dh, h->wo + l * h->so, st));
     if (h->fp8) {
