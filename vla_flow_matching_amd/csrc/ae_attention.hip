@@ -33,6 +33,8 @@ constexpr int kXcds = 8;
 constexpr int kQB = 1;  // 16-row query blocks per wave
 constexpr int kMergeBatch = 2;  // key splits merged per round of loads
 constexpr int kSlots = 2;       // LDS slots of one step (two key blocks) each
+constexpr int kManyItems = 32;     // items from which two key splits suffice
+constexpr int kFewItemSplits = 8;  // key splits per item at most below that
 
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, const float* v);
@@ -371,10 +373,11 @@ int attention_rows_per_item() { return 4 * kQB * 16; }
 
 // Key splits per item at most: each split writes, and the last one re-reads,
 // a full fp32 O^T per query row, and that merge runs in one workgroup per
-// item, so few long splits beat many short ones.
+// item, so with items enough to fill the GPU few long splits beat many short
+// ones; with few items (one or two requests) the key loop of each item is
+// the critical path, and more splits shorten it.
 int attention_max_splits(int items) {
-  (void)items;
-  return 2;
+  return items >= kManyItems ? 2 : kFewItemSplits;
 }
 
 hipError_t launch_attention(Dt dt, const AttnArgs& a, hipStream_t s) {

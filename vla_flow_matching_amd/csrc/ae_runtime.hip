@@ -1148,10 +1148,11 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
 
   // the largest call's scratch, over every batch, path and prefix bucket
   ScratchNeed need;
-  if (h->Dc > 0) {  // the context products' K splits, at any row count
+  if (h->Dc > 0) {  // the context products' K splits and tile counters, at any row count
     for (int m = 1; m <= h->Bmax * std::max(1, h->Pmax); ++m) {
       const TGemmPlan g = plan_tgemm(m, 2 * h->kvdim, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
       need.gfl = std::max(need.gfl, tgemm_partial_floats(g));
+      need.gcn = std::max(need.gcn, static_cast<size_t>(g.m_tiles) * g.n_tiles);
     }
   }
   for (int b = 1; b <= h->Bmax; ++b) {
