@@ -56,7 +56,12 @@ the pages support):
 * fp8: OCP e4m3fn, round to nearest even, saturating at +-448; weights
   static per logical tensor (q, k, v, gate, up, down), activations dynamic per
   request; s = max(amax, 1e-12)/448, code = e4m3(x * (448/amax)) in fp32,
-  y = (codes_x . codes_w) * s_x * s_w;
+  y = (codes_x . codes_w) * s_x * s_w.  The row-wise variant (the MolmoBot
+  PR reports it unsupported on its GPU, so the pages fix no more of it than
+  its name) takes the plainest reading: one scale per input row (token) and
+  one per weight output column (channel), y[i, j] = (codes_x[i] .
+  codes_w[:, j]) s_x[i] s_w[j]; the attention output projection may be
+  quantised the same way (fp8_o);
 * context preparation: each layer's context K/V = the context hidden states
   times that layer's context K and V projections, K rotated at the row's
   count position; the robot state enters through one linear layer as one
@@ -97,12 +102,16 @@ class Params:
     rms_eps: float = 1e-6
     fp8: bool = False
     block: str = "joint"  # "joint": one attention over [prefix | actions]; "dit": attn1 + attn2
+    fp8_rowwise: bool = False  # fp8 scales per input row and per weight column (else per request / tensor)
+    fp8_o: bool = False        # the attention output projection in fp8 too
 
     @staticmethod
     def like(obj, fp8: Optional[bool] = None) -> "Params":
         f = getattr(obj, "proj_dtype", "same") == "fp8" if fp8 is None else fp8
         return Params(obj.n_q_heads, obj.n_kv_heads, obj.head_dim,
-                      float(obj.rope_theta), float(obj.rms_eps), f, getattr(obj, "block", "joint"))
+                      float(obj.rope_theta), float(obj.rms_eps), f, getattr(obj, "block", "joint"),
+                      f and getattr(obj, "fp8_scaling", "tensor") == "rowwise",
+                      f and bool(getattr(obj, "fp8_o", False)))
 
 
 def to64(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
@@ -254,6 +263,28 @@ def fp8_linear(x: np.ndarray, w_codes: np.ndarray, w_scale: float) -> np.ndarray
     return (xq @ w_codes) * xs * w_scale
 
 
+def quantize_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per row (token): each row quantised as its own tensor; scales [rows]."""
+    x = np.asarray(x)
+    codes = np.empty(x.shape, dtype=F64)
+    scales = np.empty(x.shape[0], dtype=F64)
+    for r in range(x.shape[0]):
+        codes[r], scales[r] = quantize_tensor(x[r])
+    return codes, scales
+
+
+def quantize_columns(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per output column (channel) of a [K, N] weight; scales [N]."""
+    c, s = quantize_rows(np.asarray(w).T)
+    return c.T.copy(), s
+
+
+def fp8_linear_rowwise(x: np.ndarray, w_codes: np.ndarray, w_scales: np.ndarray) -> np.ndarray:
+    """x [T, K]: y[i, j] = (codes_x[i] . codes_w[:, j]) s_x[i] s_w[j]."""
+    xq, xs = quantize_rows(x)
+    return (xq @ w_codes) * xs[:, None] * w_scales[None, :]
+
+
 # ---------------------------------------------------------------------------
 # One velocity evaluation and the Euler loop
 # ---------------------------------------------------------------------------
@@ -271,17 +302,22 @@ class Expert:
         self.W = to64(weights)
         self.p = params
         self.L = n_layers_of(self.W)
-        self.q8: Dict[str, Tuple[np.ndarray, float]] = {}
+        self.q8: Dict[str, tuple] = {}
         if params.fp8:
+            names = ("q", "k", "v", "gate", "up", "down") + (("o",) if params.fp8_o else ())
+            quant = quantize_columns if params.fp8_rowwise else quantize_tensor
             for l in range(self.L):
-                for nm in ("q", "k", "v", "gate", "up", "down"):
+                for nm in names:
                     key = f"layers.{l}.{nm}"
-                    self.q8[key] = quantize_tensor(weights[key])
+                    self.q8[key] = quant(weights[key])
 
     def proj(self, x: np.ndarray, key: str) -> np.ndarray:
-        """A projection that the fp8 variant quantises (q, k, v, gate, up, down)."""
-        if self.p.fp8:
+        """A projection of one request's rows [T, K]; the fp8 variant quantises
+        q, k, v, gate, up, down (and o with fp8_o)."""
+        if key in self.q8:
             codes, s = self.q8[key]
+            if self.p.fp8_rowwise:
+                return fp8_linear_rowwise(x, codes, s)
             return fp8_linear(x, codes, s)
         return x @ self.W[key]
 
@@ -309,7 +345,7 @@ class Expert:
                 keys = np.concatenate([pk, k], axis=0)
                 vals = np.concatenate([pv, v], axis=0)
                 o[b] = attention(q, keys, vals).reshape(T, Hq * dh)
-            h = h + ga * (o @ W[pre + "o"])
+            h = h + ga * np.stack([self.proj(o[b], pre + "o") for b in range(B)])
             u2 = ada_rms(h, sm, hm, p.rms_eps)
             a = np.empty((B, T, W[pre + "gate"].shape[1]))
             for b in range(B):
@@ -343,7 +379,7 @@ class Expert:
                 v = self.proj(u[b], pre + "v").reshape(T, Hkv, dh)
                 cos, sin = rope_cos_sin(n_valid[b] + np.arange(T), dh, p.rope_theta)
                 o[b] = attention(apply_rope(q, cos, sin), apply_rope(k, cos, sin), v).reshape(T, Hq * dh)
-            h = h + g1 * (o @ W[pre + "o"])
+            h = h + g1 * np.stack([self.proj(o[b], pre + "o") for b in range(B)])
             u2 = ada_rms(h, s2, b2, p.rms_eps)
             o2 = np.empty((B, T, Hq * dh))
             for b in range(B):

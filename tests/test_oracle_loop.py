@@ -14,6 +14,7 @@ invariants (MolmoBot PR "Correctness" table; LoongForge blog section 1).
 """
 
 import cmath
+import dataclasses
 import math
 
 import numpy as np
@@ -39,6 +40,10 @@ def small_c2(layers=2, steps=2, batch=1, **kw):
 
 def run(w, W, K, V, m, x0, fp8=False):
     return O.Expert(W, O.Params.like(w, fp8=fp8)).denoise(x0, K, V, m, w.n_steps)
+
+
+def run_params(W, p, K, V, m, x0, n_steps):
+    return O.Expert(W, p).denoise(x0, K, V, m, n_steps)
 
 
 # --------------------------------------------------------------------------
@@ -94,6 +99,39 @@ def _fp8_rows(rows, wcodes, wscale):
     return out
 
 
+def _fp8_rows_rowwise(rows, wcodes, wscales):
+    """Rows through a row-wise fp8 linear: each row's own amax, multiplier and
+    codes in fp32; each weight column its own scale."""
+    f32 = np.float32
+    out = []
+    for r in rows:
+        amax = max(max(abs(f32(v)) for v in r), f32(1e-12))
+        mul, sx = f32(448.0) / amax, amax / f32(448.0)
+        codes = [_e4m3_scalar(float(f32(f32(v) * mul))) for v in r]
+        acc = []
+        for j in range(wcodes.shape[1]):
+            t = 0.0
+            for i in range(len(codes)):
+                t += codes[i] * wcodes[i, j]
+            acc.append(t * float(sx) * float(wscales[j]))
+        out.append(acc)
+    return out
+
+
+def _fp8_weight_cols(Wt):
+    """One weight tensor, each output column with its own amax and codes."""
+    f32 = np.float32
+    w32 = np.asarray(Wt, dtype=np.float32)
+    codes = np.empty(w32.shape)
+    scales = []
+    for j in range(w32.shape[1]):
+        amax = max(f32(np.abs(w32[:, j]).max()), f32(1e-12))
+        mul = f32(448.0) / amax
+        scales.append(amax / f32(448.0))
+        codes[:, j] = [_e4m3_scalar(float(f32(v * mul))) for v in w32[:, j]]
+    return codes, scales
+
+
 def _fp8_weight(Wt):
     """One logical weight tensor: amax over the whole tensor, codes in fp32."""
     f32 = np.float32
@@ -104,18 +142,19 @@ def _fp8_weight(Wt):
     return codes, float(s)
 
 
-def _bf_denoise(w, W, K, V, mask, x0, fp8=False):
+def _bf_denoise(w, W, K, V, mask, x0, fp8=False, rowwise=False, fp8_o=False):
     """Scalar loops only; explicit visibility mask; independent of the oracle.
     fp8: the q, k, v, gate, up and down projections quantised per logical
-    tensor (weights) and per request (inputs)."""
+    tensor (weights) and per request (inputs); rowwise: per weight column and
+    per input row instead; fp8_o: the output projection o as well."""
     L, D, Hq, Hkv, dh, Fd = w.n_layers, w.width, w.n_q_heads, w.n_kv_heads, w.head_dim, w.mlp_dim
     T, A, N, B, P = w.action_horizon, w.action_dim, w.n_steps, w.batch, w.prefix_len
     g = lambda name: np.asarray(W[name], dtype=np.float64)
     q8 = {}
     if fp8:
         for l in range(L):
-            for nm in ("q", "k", "v", "gate", "up", "down"):
-                q8[f"layers.{l}.{nm}"] = _fp8_weight(W[f"layers.{l}.{nm}"])
+            for nm in ("q", "k", "v", "gate", "up", "down") + (("o",) if fp8_o else ()):
+                q8[f"layers.{l}.{nm}"] = (_fp8_weight_cols if rowwise else _fp8_weight)(W[f"layers.{l}.{nm}"])
 
     def mv(vec, mat, bias=None):  # vec [in] @ mat [in, out]
         out = [0.0] * mat.shape[1]
@@ -165,8 +204,8 @@ def _bf_denoise(w, W, K, V, mask, x0, fp8=False):
 
                 def proj(rows, nm):
                     key = f"layers.{l}.{nm}"
-                    if fp8:
-                        return _fp8_rows(rows, *q8[key])
+                    if key in q8:
+                        return (_fp8_rows_rowwise if rowwise else _fp8_rows)(rows, *q8[key])
                     return [mv(r, g(key)) for r in rows]
 
                 qs, ks, vs = proj(u, "q"), proj(u, "k"), proj(u, "v")
@@ -200,9 +239,9 @@ def _bf_denoise(w, W, K, V, mask, x0, fp8=False):
                                 if ws[j] != 0.0:
                                     acc += ws[j] * vals[j][d]
                             o[i][hd * dh + d] = acc / tot
+                obs = proj(o, "o")
                 for i in range(T):
-                    ob = mv(o[i], g(f"layers.{l}.o"))
-                    h[i] = [h[i][d] + ch[2][d] * ob[d] for d in range(D)]
+                    h[i] = [h[i][d] + ch[2][d] * obs[i][d] for d in range(D)]
                 u2 = [norm(h[i], ch[3], ch[4]) for i in range(T)]
                 gts, ups = proj(u2, "gate"), proj(u2, "up")
                 acts = []
@@ -257,6 +296,66 @@ def test_oracle_fp8_matches_brute_force(hq, hkv):
     plain = run(w, W, K, V, mask, x0)
     assert np.abs(ours - plain).max() > 1e-3  # quantisation is visible at this size
     assert np.allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("fp8_o", [False, True])
+def test_oracle_fp8_rowwise_matches_brute_force(fp8_o):
+    """The row-wise fp8 variant against the scalar twin: every input row its
+    own amax, every weight column its own scale, y = (codes_x . codes_w)
+    s_x[row] s_w[col]; with fp8_o the attention output projection too.  One
+    row of request 1 and one weight column scaled far from the rest make a
+    per-request or per-tensor scale fail it."""
+    w = tiny(n_q_heads=2, n_kv_heads=1, width=8)
+    W = synth.make_weights(w, std=0.3)
+    for l in range(w.n_layers):
+        for nm in ("q", "up", "down", "o"):
+            wt = W[f"layers.{l}.{nm}"].copy()
+            wt[:, 1] *= np.float32(9.0)
+            W[f"layers.{l}.{nm}"] = wt
+    mask = np.array([[1, 0, 1, 1, 0], [0, 1, 1, 1, 1]], np.uint8)
+    K, V, _ = synth.make_prefix(w, mask=mask, garbage="huge")
+    x0 = synth.make_noise(w)
+    x0[1, 2] *= np.float32(7.0)
+    p = dataclasses.replace(O.Params.like(w, fp8=True), fp8_rowwise=True, fp8_o=fp8_o)
+    ours = run_params(W, p, K, V, mask, x0, w.n_steps)
+    ref = _bf_denoise(w, W, K, V, mask, x0, fp8=True, rowwise=True, fp8_o=fp8_o)
+    tensor = run(w, W, K, V, mask, x0, fp8=True)
+    assert np.abs(ours - tensor).max() > 1e-4  # the granularity is visible
+    assert np.allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+def test_rowwise_scaling_invariances():
+    """Row-wise scales make rows and columns independent: a power-of-two
+    factor on one input row leaves its codes unchanged and scales its scale
+    (and its output row) by the same factor, exactly, and leaves every other
+    output row bit-identical; likewise for one weight column.  The per-request
+    recipe does not have the row property (its other rows' codes move)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 64)).astype(np.float32)
+    wt = (rng.standard_normal((64, 24)) * 0.1).astype(np.float32)
+    wc, ws = O.quantize_columns(wt)
+    y = O.fp8_linear_rowwise(x, wc, ws)
+    x2 = x.copy()
+    x2[3] *= np.float32(64.0)
+    y2 = O.fp8_linear_rowwise(x2, wc, ws)
+    assert np.array_equal(np.delete(y2, 3, 0), np.delete(y, 3, 0))
+    assert np.array_equal(y2[3], y[3] * 64.0)
+    c1, s1 = O.quantize_rows(x)
+    c2, s2 = O.quantize_rows(x2)
+    assert np.array_equal(c1, c2) and s2[3] == s1[3] * 64.0
+    wt2 = wt.copy()
+    wt2[:, 5] *= np.float32(0.25)
+    wc2, ws2 = O.quantize_columns(wt2)
+    y3 = O.fp8_linear_rowwise(x, wc2, ws2)
+    assert np.array_equal(np.delete(y3, 5, 1), np.delete(y, 5, 1))
+    assert np.array_equal(y3[:, 5], y[:, 5] * 0.25)
+    # a single row is its own tensor
+    ct, st = O.quantize_tensor(x[2])
+    assert np.array_equal(ct, c1[2]) and st == s1[2]
+    # per request: scaling row 3 moves the codes of the rows that set the amax with it
+    t1, _ = O.quantize_tensor(x)
+    t2, _ = O.quantize_tensor(x2)
+    assert not np.array_equal(np.delete(t1, 3, 0), np.delete(t2, 3, 0))
 
 
 def test_e4m3_twin_table_agrees_with_torch():

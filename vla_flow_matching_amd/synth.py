@@ -57,6 +57,8 @@ class Workload:
     index: int = 0        # N in the seed formula 100N+k
     gate_bias: float = 0.0  # offset on the gate chunks of every layer's modulation bias
     block: str = "joint"    # "joint" attention over [prefix | actions], or "dit" (attn1 + attn2)
+    fp8_scaling: str = "tensor"  # fp8 scales per request / tensor, or "rowwise" (per row / column)
+    fp8_o: bool = False          # the attention output projection in fp8 too
 
     def seed(self, k: int) -> int:
         return 100 * self.index + k
@@ -80,6 +82,9 @@ WORKLOADS: Dict[str, Workload] = {
                    prefix_len=2048, dtype="bf16", proj_dtype="same", index=4, gate_bias=0.1),
     "c5": Workload("c5", batch=16, prefix_len=1024, dtype="bf16", proj_dtype="same", index=5, **_PI05),
     "c5fp8": Workload("c5fp8", batch=16, prefix_len=1024, dtype="bf16", proj_dtype="fp8", index=5, **_PI05),
+    # the c5 batch with row-wise fp8 scales and the attention output projection in fp8 as well
+    "c5fp8r": Workload("c5fp8r", batch=16, prefix_len=1024, dtype="bf16", proj_dtype="fp8", index=5,
+                       fp8_scaling="rowwise", fp8_o=True, **_PI05),
 }
 
 
