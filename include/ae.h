@@ -103,6 +103,13 @@ typedef struct {
   int state_dim;        /* size of the robot state ae_prepare_prefix encodes as one more
                            context row (<= 64, needs context_width); 0: none */
   int block_type;       /* ae_block: AE_BLOCK_JOINT (0) or AE_BLOCK_DIT (1) */
+  int fp8_rowwise;      /* with AE_FP8_E4M3 projections: 0 = a weight scale per logical tensor and
+                           an activation scale per request (MolmoBot PR Part 3's per-tensor
+                           dynamic recipe); 1 = a scale per weight output column and per
+                           activation row (the row-wise recipe the PR names as unsupported on its
+                           GPU) */
+  int fp8_oproj;        /* 1: the attention output projection in fp8 as well (needs fp8_rowwise
+                           and n_q_heads * head_dim a multiple of 128); 0: bf16 */
 } ae_config;
 
 /* One named logical weight, caller-owned device memory, dtype = act_dtype.

@@ -38,34 +38,41 @@ ae_status aetest_fp8_quantize(const float* x, int M, int K, int T, uint8_t* code
 
 /* The adaRMS input of a QKV / gate-up product and its codes: per row
  * r = 1 / sqrt(mean(h^2) + eps), u = h r (1 + scale) + shift, then codes of
- * u as aetest_fp8_quantize does (K = D a multiple of 64). r_out [M]. */
+ * u as aetest_fp8_quantize does (K = D a multiple of 64). r_out [M].  T = 1
+ * is the row-wise recipe (each row its own scale), which runs the one-pass
+ * per-row kernel. */
 ae_status aetest_fp8_norm_quantize(const float* h, int M, int D, int T, const float* scale,
                                    const float* shift, float eps, uint8_t* codes, float* sx_row,
                                    float* r_out, void* stream);
 
 /* The down projection: y [M][N] fp32 = (codes . e4m3(W / s_w)) * sx_row * s_w
- * with s_w = amax|W| / 448 (one scale for the tensor), written to sw[0].
- * K and N multiples of 128. */
+ * with s_w = amax|W| / 448 (one scale for the tensor), written to sw[0];
+ * per_column = 1: the row-wise variant, s_w per output column j (amax of
+ * column j), sw[0..N).  K and N multiples of 128. */
 ae_status aetest_fp8_down(const uint8_t* codes, const float* sx_row, int M, int K,
-                          const uint16_t* w, int N, float* y, float* sw, void* stream);
+                          const uint16_t* w, int N, float* y, float* sw, int per_column, void* stream);
 
 /* The merged gate/up projection: act [M][F] fp32 = gelu_tanh(g) * u with
  * g = (codes . e4m3(Wg / s_g)) * sx_row * s_g and u likewise with W_u and its
- * own scale s_u; sw[0] = s_g, sw[1] = s_u.  K and 2F multiples of 128. */
+ * own scale s_u; sw[0] = s_g, sw[1] = s_u (per_column = 1: a scale per
+ * column, sw = [gate columns | up columns], 2F values).  K and 2F multiples
+ * of 128. */
 ae_status aetest_fp8_gate_up(const uint8_t* codes, const float* sx_row, int M, int K,
                              const uint16_t* wg, const uint16_t* wu, int F, float* act, float* sw,
-                             void* stream);
+                             int per_column, void* stream);
 
 /* The merged q|k|v projection of one request of M rows, through the
  * product's own epilogue (scatter of q, and of k and v into a key-block
  * cache) with identity rotation tables (cos 1, sin 0), so the products come
  * back unrotated: q [M][Hq dh], k and v [M][Hkv dh] fp32 holding the bf16
  * values the kernel stores, each (codes . e4m3(W / s)) * sx_row * s with the
- * tensor's own scale; sw[0..2] = s_q, s_k, s_v.
+ * tensor's own scale; sw[0..2] = s_q, s_k, s_v (per_column = 1: a scale per
+ * column, sw = [q columns | k columns | v columns]).
  * K and (Hq + 2 Hkv) dh multiples of 128, dh in {64, 128, 256}. */
 ae_status aetest_fp8_qkv(const uint8_t* codes, const float* sx_row, int M, int K,
                          const uint16_t* wq, const uint16_t* wk, const uint16_t* wv, int Hq,
-                         int Hkv, int dh, float* q, float* k, float* v, float* sw, void* stream);
+                         int Hkv, int dh, float* q, float* k, float* v, float* sw, int per_column,
+                         void* stream);
 
 #ifdef __cplusplus
 }

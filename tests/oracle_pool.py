@@ -41,6 +41,11 @@ def per_request(w, W, K, V, m, x0, requests: Sequence[int], steps: Optional[int]
             floor = float(np.abs(E.denoise(x1, Kb, Vb, mb, n) - ref).max())
         return ref, floor
 
+    def logged(b):
+        r = one(b)
+        print(f"[oracle] request {b} integrated", flush=True)  # progress for long batches
+        return r
+
     with threadpool_limits(1):
         with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
-            return list(ex.map(one, requests))
+            return list(ex.map(logged, requests))

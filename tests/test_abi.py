@@ -189,3 +189,20 @@ def test_dit_block_configs(lib):
         assert lib.ae_create(ctypes.byref(c), ctypes.byref(h)) == binding.AE_ERR_UNSUPPORTED and not h.value
     h = ctypes.c_void_p()
     assert lib.ae_create(ctypes.byref(cfg), ctypes.byref(h)) == binding.AE_ERR_HIP and not h.value
+
+
+def test_fp8_rowwise_configs(lib):
+    """Row-wise fp8 and the fp8 output projection: flags are 0 or 1, need fp8
+    projections, and the fp8 output projection needs the row-wise recipe; a
+    valid row-wise config passes every check and then finds no device."""
+    base = dict(proj_weight_dtype=binding.AE_FP8_E4M3, act_dtype=binding.AE_BF16)
+    for bad in (dict(fp8_rowwise=2), dict(fp8_oproj=-1), dict(fp8_rowwise=1, proj_weight_dtype=binding.AE_BF16,
+                                                              act_dtype=binding.AE_BF16)):
+        st, h = _create(lib, **{**base, **bad})
+        assert st == binding.AE_ERR_INVALID_ARGUMENT and not h.value, bad
+    st, h = _create(lib, **base, fp8_oproj=1)  # output projection without the row-wise recipe
+    assert st == binding.AE_ERR_UNSUPPORTED and not h.value
+    st, h = _create(lib, **base, fp8_rowwise=1, fp8_oproj=1)
+    assert st == binding.AE_ERR_HIP and not h.value
+    cfg = binding.make_config(synth.workload("c5fp8r"))
+    assert cfg.fp8_rowwise == 1 and cfg.fp8_oproj == 1

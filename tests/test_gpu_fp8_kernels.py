@@ -50,9 +50,9 @@ def lib():
     vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.aetest_fp8_quantize.argtypes = [vp, ci, ci, ci, vp, vp, vp]
     L.aetest_fp8_norm_quantize.argtypes = [vp, ci, ci, ci, vp, vp, cf, vp, vp, vp, vp]
-    L.aetest_fp8_down.argtypes = [vp, vp, ci, ci, vp, ci, vp, vp, vp]
-    L.aetest_fp8_gate_up.argtypes = [vp, vp, ci, ci, vp, vp, ci, vp, vp, vp]
-    L.aetest_fp8_qkv.argtypes = [vp, vp, ci, ci, vp, vp, vp, ci, ci, ci, vp, vp, vp, vp, vp]
+    L.aetest_fp8_down.argtypes = [vp, vp, ci, ci, vp, ci, vp, vp, ci, vp]
+    L.aetest_fp8_gate_up.argtypes = [vp, vp, ci, ci, vp, vp, ci, vp, vp, ci, vp]
+    L.aetest_fp8_qkv.argtypes = [vp, vp, ci, ci, vp, vp, vp, ci, ci, ci, vp, vp, vp, vp, ci, vp]
     for f in ("aetest_fp8_quantize", "aetest_fp8_norm_quantize", "aetest_fp8_down", "aetest_fp8_gate_up",
               "aetest_fp8_qkv"):
         getattr(L, f).restype = ci
@@ -145,11 +145,13 @@ def test_quantizer_rejects_bad_sizes(lib):
     assert lib.aetest_fp8_quantize(ptr(z), 3, 64, 2, ptr(c), ptr(z), stream()) == 1
 
 
-def test_norm_then_quantize(lib):
+@pytest.mark.parametrize("T", [50, 1])
+def test_norm_then_quantize(lib, T):
     """adaRMS rows then codes: the fp32 GPU u and the fp64 oracle u differ by
-    rounding, so a code may differ only where u lands next to a midpoint."""
+    rounding, so a code may differ only where u lands next to a midpoint.
+    T = 1: the row-wise recipe (each row its own scale, the one-pass kernel)."""
     rng = np.random.default_rng(22)
-    T, D, M = 50, 1024, 150
+    D, M = 1024, 150
     h = rng.standard_normal((M, D)).astype(np.float32) * np.float32(3.0)
     sc = (rng.standard_normal(D) * 0.3).astype(np.float32)
     sh = (rng.standard_normal(D) * 0.1).astype(np.float32)
@@ -167,7 +169,7 @@ def test_norm_then_quantize(lib):
     assert np.allclose(sx.cpu().numpy(), want_sx, rtol=2e-6, atol=0)
     got = decode(codes)
     diff = got != want_codes
-    say(f"[fp8] norm + quantiser: {int(diff.sum())} of {got.size} codes differ (near-ties)")
+    say(f"[fp8] norm + quantiser (T={T}): {int(diff.sum())} of {got.size} codes differ (near-ties)")
     assert diff.mean() <= 1e-3
     # a differing code is a neighbour: within one e4m3 step of the other
     vals = e4m3_values()
@@ -179,53 +181,76 @@ def test_norm_then_quantize(lib):
 ACC_REL = 2.0 ** -16  # of the sum of the terms' magnitudes (fp32 accumulation)
 
 
-def product_ref(xcodes, sx, wf32):
-    """(reference y, fp32 weight scale, per-element accumulation bound)."""
-    wc, s_w = O.quantize_tensor(wf32)
-    scale = sx[:, None].astype(np.float64) * s_w
+def product_ref(xcodes, sx, wf32, per_column=False):
+    """(reference y, fp32 weight scale(s), per-element accumulation bound);
+    per_column: the row-wise recipe's scale per weight column."""
+    if per_column:
+        wc, s_w = O.quantize_columns(wf32)
+        scale = sx[:, None].astype(np.float64) * s_w[None, :]
+        s_out = s_w.astype(np.float32)
+    else:
+        wc, s_w = O.quantize_tensor(wf32)
+        scale = sx[:, None].astype(np.float64) * s_w
+        s_out = np.float32(s_w)
     y = (xcodes @ wc) * scale
     mag = (np.abs(xcodes) @ np.abs(wc)) * scale
-    return y, np.float32(s_w), ACC_REL * mag + 1e-30
+    return y, s_out, ACC_REL * mag + 1e-30
 
 
 def worst(got, ref, bound):
     return float((np.abs(got - ref) / bound).max())
 
 
-@pytest.mark.parametrize("M", [100, 800])
-def test_down_product(lib, M):
+def col_spread(rng, wf, wt):
+    """Give the weight columns widely different scales (so a per-tensor scale
+    in place of per-column ones, or a column map error, shows)."""
+    f = np.float32(2.0) ** rng.integers(-4, 5, size=wf.shape[1]).astype(np.float32)
+    wf = (wf * f[None, :]).astype(np.float32)
+    return torch.from_numpy(wf).to(torch.bfloat16).cuda(), wf
+
+
+@pytest.mark.parametrize("M,per_column", [(100, 0), (800, 0), (800, 1)])
+def test_down_product(lib, M, per_column):
     rng = np.random.default_rng(23)
     T, K, N = 50, 4096, 1024
     x = rng.standard_normal((M, K)).astype(np.float32)
     x[T:2 * T] *= np.float32(7.0)
-    xc, sxr = oracle_codes(x, T)
+    xc, sxr = oracle_codes(x, 1 if per_column else T)
     wt, wf = bf16_weight(rng, K, N)
+    if per_column:
+        wt, wf = col_spread(rng, wf, wt)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    sw = torch.empty(1, dtype=torch.float32, device="cuda")
-    assert lib.aetest_fp8_down(ptr(encode(xc)), ptr(dev(sxr)), M, K, ptr(wt), N, ptr(y), ptr(sw), stream()) == 0
-    ref, s_w, bound = product_ref(xc, sxr, wf)
+    sw = torch.empty(N if per_column else 1, dtype=torch.float32, device="cuda")
+    assert lib.aetest_fp8_down(ptr(encode(xc)), ptr(dev(sxr)), M, K, ptr(wt), N, ptr(y), ptr(sw), per_column,
+                               stream()) == 0
+    ref, s_w, bound = product_ref(xc, sxr, wf, per_column)
     got = y.cpu().numpy()
     err = np.abs(got - ref).max() / np.abs(ref).max()
     w = worst(got, ref, bound)
-    say(f"[fp8] down {M}x{K}x{N}: max err {err:.2e} of max|y|; worst error / bound {w:.3f}")
-    assert sw.cpu().numpy()[0] == s_w
+    say(f"[fp8] down {M}x{K}x{N} ({'per column' if per_column else 'per tensor'}): max err {err:.2e} of max|y|; "
+        f"worst error / bound {w:.3f}")
+    assert np.array_equal(sw.cpu().numpy(), np.atleast_1d(s_w))
     assert w <= 1.0
 
 
-def test_gate_up_product(lib):
+@pytest.mark.parametrize("per_column", [0, 1])
+def test_gate_up_product(lib, per_column):
     rng = np.random.default_rng(24)
     T, K, F, M = 50, 1024, 4096, 150
     x = rng.standard_normal((M, K)).astype(np.float32)
     x[2 * T:] *= np.float32(0.1)
-    xc, sxr = oracle_codes(x, T)
+    xc, sxr = oracle_codes(x, 1 if per_column else T)
     wg, wgf = bf16_weight(rng, K, F)
     wu, wuf = bf16_weight(rng, K, F, scale=5.0)  # up's scale differs from gate's
+    if per_column:
+        wg, wgf = col_spread(rng, wgf, wg)
+        wu, wuf = col_spread(rng, wuf, wu)
     act = torch.empty((M, F), dtype=torch.float32, device="cuda")
-    sw = torch.empty(2, dtype=torch.float32, device="cuda")
+    sw = torch.empty(2 * F if per_column else 2, dtype=torch.float32, device="cuda")
     assert lib.aetest_fp8_gate_up(ptr(encode(xc)), ptr(dev(sxr)), M, K, ptr(wg), ptr(wu), F, ptr(act), ptr(sw),
-                                  stream()) == 0
-    g, sg, bg = product_ref(xc, sxr, wgf)
-    u, su, bu = product_ref(xc, sxr, wuf)
+                                  per_column, stream()) == 0
+    g, sg, bg = product_ref(xc, sxr, wgf, per_column)
+    u, su, bu = product_ref(xc, sxr, wuf, per_column)
     ref = O.gelu_tanh(g) * u
     # each factor within its own bound (|gelu'| <= 1.13), plus fp32 rounding
     # of the gelu (tanhf) and the product
@@ -233,35 +258,41 @@ def test_gate_up_product(lib):
     got = act.cpu().numpy()
     err = np.abs(got - ref).max() / np.abs(ref).max()
     w = worst(got, ref, bound)
-    say(f"[fp8] gate/up {M}x{K}x2*{F}: max err {err:.2e} of max|act|; worst error / bound {w:.3f}; "
-        f"scales {sw.tolist()}")
-    assert sw.cpu().numpy().tolist() == [sg, su]
+    say(f"[fp8] gate/up {M}x{K}x2*{F} ({'per column' if per_column else 'per tensor'}): max err {err:.2e} of "
+        f"max|act|; worst error / bound {w:.3f}")
+    assert np.array_equal(sw.cpu().numpy(), np.concatenate([np.atleast_1d(sg), np.atleast_1d(su)]))
     assert w <= 1.0
 
 
-@pytest.mark.parametrize("Hq,Hkv,dh", [(8, 1, 256), (12, 4, 64)])
-def test_qkv_product(lib, Hq, Hkv, dh):
+@pytest.mark.parametrize("Hq,Hkv,dh,per_column", [(8, 1, 256, 0), (12, 4, 64, 0), (8, 1, 256, 1),
+                                                  (12, 4, 64, 1)])
+def test_qkv_product(lib, Hq, Hkv, dh, per_column):
     rng = np.random.default_rng(25)
     K, M = 1024, 50
     x = rng.standard_normal((M, K)).astype(np.float32)
-    xc, sxr = oracle_codes(x, M)
+    xc, sxr = oracle_codes(x, 1 if per_column else M)
     wq, wqf = bf16_weight(rng, K, Hq * dh)
     wk, wkf = bf16_weight(rng, K, Hkv * dh, scale=3.0)
     wv, wvf = bf16_weight(rng, K, Hkv * dh, scale=0.25)
+    if per_column:
+        wq, wqf = col_spread(rng, wqf, wq)
+        wk, wkf = col_spread(rng, wkf, wk)
+        wv, wvf = col_spread(rng, wvf, wv)
     q = torch.empty((M, Hq * dh), dtype=torch.float32, device="cuda")
     k = torch.empty((M, Hkv * dh), dtype=torch.float32, device="cuda")
     v = torch.empty((M, Hkv * dh), dtype=torch.float32, device="cuda")
-    sw = torch.empty(3, dtype=torch.float32, device="cuda")
+    sw = torch.empty((Hq + 2 * Hkv) * dh if per_column else 3, dtype=torch.float32, device="cuda")
     assert lib.aetest_fp8_qkv(ptr(encode(xc)), ptr(dev(sxr)), M, K, ptr(wq), ptr(wk), ptr(wv), Hq, Hkv, dh,
-                              ptr(q), ptr(k), ptr(v), ptr(sw), stream()) == 0
+                              ptr(q), ptr(k), ptr(v), ptr(sw), per_column, stream()) == 0
     scales = []
     for name, got, wf in (("q", q, wqf), ("k", k, wkf), ("v", v, wvf)):
-        ref, s, acc = product_ref(xc, sxr, wf)
+        ref, s, acc = product_ref(xc, sxr, wf, per_column)
         scales.append(s)
         g = got.cpu().numpy()
         # stored as bf16: half an ulp (<= 2^-8 relative) plus accumulation rounding
         bound = 2.0 ** -8 * np.abs(ref) + acc
         w = worst(g, ref, bound)
-        say(f"[fp8] qkv {name} (Hq {Hq}, Hkv {Hkv}, dh {dh}): worst error / bound {w:.3f}")
+        say(f"[fp8] qkv {name} (Hq {Hq}, Hkv {Hkv}, dh {dh}, {'per column' if per_column else 'per tensor'}): "
+            f"worst error / bound {w:.3f}")
         assert w <= 1.0, name
-    assert sw.cpu().numpy().tolist() == scales
+    assert np.array_equal(sw.cpu().numpy(), np.concatenate([np.atleast_1d(x) for x in scales]))

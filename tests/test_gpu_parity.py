@@ -374,12 +374,15 @@ def test_c5_batched_full():
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("name,batch", [("c5", 2), ("c5", 3), ("c5fp8", 3)])
+@pytest.mark.parametrize("name,batch", [("c5", 2), ("c5", 3), ("c5fp8", 3), ("c5fp8r", 3), ("c5fp8r", 1),
+                                        ("c5fp8", 1)])
 def test_batched_tiles_small(name, batch):
     """The batched path at reduced depth: 100 / 150 action rows leave a ragged
     32-row tile and a part-filled 8-row action-in group; every request
     against the oracle (fp8: the oracle's e4m3 emulation with per-request
-    activation scales)."""
+    activation scales; c5fp8r: scales per row and per weight column, and the
+    output projection in fp8 too).  Batch 1 runs the fp8 variants on a single
+    request (fp8 never takes the whole-call kernel)."""
     _need_gpu()
     w = synth.workload(name, batch=batch, n_layers=2, n_steps=2)
     say(f"[case] {name} batch {batch}, 2 layers, 2 steps")
@@ -507,18 +510,21 @@ def fp8_tolerance(w, W, K, V, m, x0, ref):
     return max(TOL_BF16, 2.0 * floor)
 
 
-def test_c5_fp8_full():
+@pytest.mark.parametrize("name", ["c5fp8", "c5fp8r"])
+def test_c5_fp8_full(name):
     """c5 with e4m3 QKV / gate-up / down weights (static per tensor) and
-    per-request dynamic activation scales: every request against the
-    oracle's emulation, and a request batched against the same one alone.
+    per-request dynamic activation scales (c5fp8r: a scale per weight column
+    and per activation row, and the output projection in e4m3 too): every
+    request against the oracle's emulation, and a request batched against
+    the same one alone.
 
     Each request is held to twice the oracle's own response to a relative
     1e-6 perturbation of its noise (never less than 2e-2; see fp8_tolerance);
     the error is also reported against the 2e-2 contract itself, which the
     full-size fp8 loop does not meet for every request."""
     _need_gpu()
-    w = synth.workload("c5fp8")
-    say("[case] c5 fp8 full: batch 16, prefix 1024")
+    w = synth.workload(name)
+    say(f"[case] {name} full: batch 16, prefix 1024")
     W = synth.make_weights(w)
     g = Gpu(w, W)
     m = synth.valid_masks(w)
@@ -531,16 +537,16 @@ def test_c5_fp8_full():
     for b, (ref, floor) in enumerate(refs):
         tols.append(max(TOL_BF16, 2.0 * floor))
         say(f"[fp8] request {b}: oracle response to a 1e-6 relative noise perturbation {floor:.3e}")
-        errs.append(check(out[b:b + 1], ref, tols[-1], f"c5 fp8 request {b} (n={int(m[b].sum())})"))
+        errs.append(check(out[b:b + 1], ref, tols[-1], f"{name} request {b} (n={int(m[b].sum())})"))
     over = [b for b, e in enumerate(errs) if e > TOL_BF16]
-    say(f"[fp8] c5 fp8 all {w.batch} requests: max error {max(errs):.3e}; "
+    say(f"[fp8] {name} all {w.batch} requests: max error {max(errs):.3e}; "
         f"{len(over)} of {w.batch} above the 2e-2 contract: {over}")
-    w1 = synth.workload("c5fp8", batch=1)
+    w1 = synth.workload(name, batch=1)
     g1 = Gpu(w1, W)
     b = 7
     alone = g1.run(K[:, b:b + 1], V[:, b:b + 1], m[b:b + 1], x0[b:b + 1])
     err = float(np.abs(alone - out[b:b + 1]).max())
-    say(f"[parity] c5 fp8 batched vs alone, request {b}: {err:.3e} (tol {tols[b]:.3e})")
+    say(f"[parity] {name} batched vs alone, request {b}: {err:.3e} (tol {tols[b]:.3e})")
     assert err <= tols[b]
 
 

@@ -37,6 +37,7 @@ class Config(ctypes.Structure):
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("use_graphs", ctypes.c_int),
         ("graph_cache_size", ctypes.c_int), ("graph_cache_evict", ctypes.c_int),
         ("context_width", ctypes.c_int), ("state_dim", ctypes.c_int), ("block_type", ctypes.c_int),
+        ("fp8_rowwise", ctypes.c_int), ("fp8_oproj", ctypes.c_int),
     ]
 
 
@@ -108,7 +109,9 @@ def make_config(w, max_batch: Optional[int] = None, max_prefix_len: Optional[int
                   w.n_steps if max_steps is None else max_steps,
                   act, proj, float(w.rope_theta), float(w.rms_eps), int(bool(use_graphs)),
                   int(graph_cache_size), int(bool(graph_cache_evict)), int(context_width), int(state_dim),
-                  AE_BLOCK_DIT if getattr(w, "block", "joint") == "dit" else AE_BLOCK_JOINT)
+                  AE_BLOCK_DIT if getattr(w, "block", "joint") == "dit" else AE_BLOCK_JOINT,
+                  int(proj == AE_FP8_E4M3 and getattr(w, "fp8_scaling", "tensor") == "rowwise"),
+                  int(proj == AE_FP8_E4M3 and bool(getattr(w, "fp8_o", False))))
 
 
 def _stream_ptr(stream) -> ctypes.c_void_p:

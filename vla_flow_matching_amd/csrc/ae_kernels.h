@@ -171,9 +171,11 @@ struct TGemmArgs {
   int pf_blocks, main_blocks;
   float* partial;
   int* counters;
-  // fp8: per-row activation scale and per-tensor weight scales
+  // fp8: per-row activation scale and per-tensor weight scales, or (swc
+  // set: row-wise scaling) one weight scale per packed output column
   const float* sx_row;
   const float* sw;
+  const float* swc;
   // EPI_RESID
   float* h;
   int ldh;
@@ -233,9 +235,27 @@ hipError_t launch_quant(const float* src, const float* h, const float* r, const 
 hipError_t launch_weight_amax(const uint16_t* w, size_t n, unsigned* out, hipStream_t s);
 hipError_t launch_fp8_scales(const unsigned* amax_bits, int n, float* mul, float* scale,
                              hipStream_t s);
+// Row-wise fp8: per output column of a bf16 weight [K][ld] (first N
+// columns) the multiplier 448 / amax and the scale amax / 448 (amax floored
+// at 1e-12), both fp32.
+hipError_t launch_fp8_col_scales(const uint16_t* w, int K, int N, int ld, float* mul, float* scale, hipStream_t s);
+// The scale of every packed column: out[pc] = scale of the logical column
+// packed at pc (the packing's column map; sc1 / sc2 unused by PACK_PLAIN).
+hipError_t launch_pack_col_scales(PackMode mode, const float* sc0, const float* sc1, const float* sc2, int N,
+                                  int Hq, int Hkv, int dh, float* out, hipStream_t s);
+// Row-wise fp8 activations: one workgroup per row.  norm: r = 1 / rms(h),
+// u = adaRMS(h), codes of u with the row's own scale (D <= 4096); bf16 rows:
+// codes of the row as it is (K <= 4096).
+hipError_t launch_rownorm_quant(const float* h, int M, int D, const float* scale, const float* shift, float eps,
+                                float* r, uint8_t* codes, float* sx_row, hipStream_t s);
+hipError_t launch_quant_bf16_rows(const uint16_t* src, int M, int K, uint8_t* codes, float* sx_row,
+                                  hipStream_t s);
+// Packs fp8 weights; colmul (per source: its per-column multipliers, or all
+// null: mul3 per source) sets the row-wise scaling.
 hipError_t launch_pack_fp8(PackMode mode, const uint16_t* s0, const uint16_t* s1, const uint16_t* s2,
                            int K, int N, int ld0, int ld1, int ld2, int Hq, int Hkv, int dh,
-                           const float* mul3, uint4* dst, hipStream_t s);
+                           const float* mul3, uint4* dst, hipStream_t s, const float* colmul0 = nullptr,
+                           const float* colmul1 = nullptr, const float* colmul2 = nullptr);
 
 // ---------------------------------------------------------------------------
 // Persistent whole-call kernel (batch * T <= 64 rows)

@@ -12,6 +12,7 @@
 // lengths validated up front).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -128,6 +129,13 @@ struct ae_handle {
   // batched tiled path: bf16, or fp8 e4m3 QKV / gate-up / down projections
   bool tiled = false;
   bool fp8 = false;
+  bool rowwise = false;  // fp8 scales per weight column and per activation row
+  bool fp8o = false;     // fp8 attention output projection (row-wise)
+  // row-wise: each layer's weight scales per packed column of qkv, gate-up,
+  // down and (fp8o) o, at offsets 0, qkv_n, qkv_n + 2F, qkv_n + 2F + D
+  float* swc = nullptr;
+  size_t swc_layer = 0;
+  float *cmul = nullptr, *csc = nullptr;  // per logical column of one layer's tensors (weight load)
   void* ubuf = nullptr;  // fp8 GEMM input rows (e4m3 codes)
   float *rrow = nullptr, *rowmax = nullptr, *sxrow = nullptr;
   unsigned* wamax = nullptr;             // [L][6] amax bits of q, k, v, gate, up, down
@@ -211,6 +219,10 @@ std::string validate_config(const ae_config* c) {
   if (c->state_dim > 0 && c->context_width == 0) return "state_dim needs context_width";
   if (c->block_type != AE_BLOCK_JOINT && c->block_type != AE_BLOCK_DIT)
     return "block_type must be AE_BLOCK_JOINT or AE_BLOCK_DIT";
+  if ((c->fp8_rowwise != 0 && c->fp8_rowwise != 1) || (c->fp8_oproj != 0 && c->fp8_oproj != 1))
+    return "fp8_rowwise and fp8_oproj must be 0 or 1";
+  if ((c->fp8_rowwise || c->fp8_oproj) && c->proj_weight_dtype != AE_FP8_E4M3)
+    return "fp8_rowwise / fp8_oproj need proj_weight_dtype AE_FP8_E4M3";
   return "";
 }
 
@@ -219,6 +231,8 @@ std::string unsupported_config(const ae_config* c) {
     return "head_dim must be 64, 128 or 256";
   if (c->context_width > 0 && (c->act_dtype != AE_BF16 || (2 * c->n_kv_heads * c->head_dim) % 128))
     return "context preparation needs bf16 and 2 n_kv_heads head_dim a multiple of 128";
+  if (c->fp8_oproj && (!c->fp8_rowwise || (c->n_q_heads * c->head_dim) % 128))
+    return "fp8_oproj needs fp8_rowwise and n_q_heads * head_dim a multiple of 128";
   if (c->block_type == AE_BLOCK_DIT) {
     const int qd = c->n_q_heads * c->head_dim, qkv = qd + 2 * c->n_kv_heads * c->head_dim;
     if (c->act_dtype != AE_BF16 || c->proj_weight_dtype != AE_BF16)
@@ -348,7 +362,7 @@ TPlans plan_tlayer(const ae_handle* h, int M) {
   p.op = h->fp8 ? OP_FP8 : OP_BF16;
   const int kc = tgemm_kc(p.op), kb = tgemm_kc(OP_BF16);
   p.qkv = plan_tgemm(M, h->qkv_n, h->D, kc, kTargetBlocks);
-  p.o = plan_tgemm(M, h->D, h->qdim, kb, kTargetBlocks);
+  p.o = plan_tgemm(M, h->D, h->qdim, h->fp8o ? kc : kb, kTargetBlocks);
   p.gu = plan_tgemm(M, 2 * h->F, h->D, kc, kTargetBlocks);
   p.d = plan_tgemm(M, h->D, h->F, kc, kTargetBlocks);
   p.q2 = plan_tgemm(M, h->qdim, h->D, kb, kTargetBlocks);
@@ -505,6 +519,10 @@ ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int 
   uint8_t* ub8 = static_cast<uint8_t*>(h->ubuf);
   // fp8: the adaRMS input of a QKV / gate-up product as e4m3 codes
   auto norm_rows = [&](const float* sc, const float* sh) -> ae_status {
+    if (h->rowwise) {  // each row its own scale: norm and codes in one pass
+      AE_LAUNCH(launch_rownorm_quant(h->h, M, D, sc, sh, eps, h->rrow, ub8, h->sxrow, s));
+      return AE_OK;
+    }
     AE_LAUNCH(launch_rownorm(h->h, M, D, sc, sh, eps, h->rrow, h->rowmax, s));
     AE_LAUNCH(launch_quant(nullptr, h->h, h->rrow, sc, sh, M, D, h->T, h->rowmax, 1, h->Mmax, ub8,
                            h->sxrow, s));
@@ -541,8 +559,11 @@ ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int 
         if (r != AE_OK) return r;
       }
 
+      // row-wise fp8: this layer's weight scales per packed column
+      const float* swl = h->rowwise ? h->swc + l * h->swc_layer : nullptr;
       TGemmArgs g = base_tgemm(h, sc, tp.qkv, M, h->qkv_n, D);
       g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wqkv + l * h->sqkv; g.sw = h->wsc + 6 * l;
+      g.swc = swl;
       if (!f8) post_norm(g, h->bq + it * h->qkv_n);  // (bf16: A = the norm shadow)
       g.q = h->q; g.ldq = h->qdim; g.kcache = kc; g.vtcache = vc; g.n_valid = h->n_valid;
       g.rope_cos = h->rope_cos; g.rope_sin = h->rope_sin;
@@ -561,7 +582,7 @@ ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int 
       // weights and the next layer's QKV weights while attention runs
       at.pf_blocks = kPrefetchBlocks;
       at.pf[0] = h->wo + l * h->so;
-      at.pf_n4[0] = static_cast<int>(static_cast<size_t>(h->qdim) * D * 2 / 16);
+      at.pf_n4[0] = static_cast<int>(static_cast<size_t>(h->qdim) * D * (h->fp8o ? 1 : 2) / 16);
       at.pf[1] = h->wgu + l * h->sgu;
       at.pf_n4[1] = static_cast<int>(static_cast<size_t>(D) * 2 * F * ob / 16);
       at.pf[2] = h->wd + l * h->sd;
@@ -572,12 +593,17 @@ ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int 
 
       g = base_tgemm(h, sc, tp.o, M, D, h->qdim);
       g.A = h->o; g.lda_bytes = static_cast<size_t>(h->qdim) * 2; g.W = h->wo + l * h->so;
+      if (h->fp8o) {  // the attention output's codes, a scale per row
+        AE_LAUNCH(launch_quant_bf16_rows(static_cast<const uint16_t*>(h->o), M, h->qdim, ub8, h->sxrow, s));
+        g.A = h->ubuf; g.lda_bytes = static_cast<size_t>(h->qdim);
+        g.swc = swl + h->qkv_n + 2 * F + D;
+      }
       // the next layer's K cache of these requests into the last-level
       // cache on the CUs the O-proj tiles leave free (its V: beside down)
       prefetch_cache(g, h->kcache, (l + 1) % L, tp.o.blocks);
       g.h = h->h; g.ldh = D; g.gate = md + 2 * D;
       if (!f8) resid_out(g, md + 3 * D);
-      AE_LAUNCH(launch_tgemm(OP_BF16, EPI_RESID, g, tp.o.blocks, s));
+      AE_LAUNCH(launch_tgemm(h->fp8o ? OP_FP8 : OP_BF16, EPI_RESID, g, tp.o.blocks, s));
 
       if (f8) {
         ae_status r = norm_rows(md + 3 * D, md + 4 * D);
@@ -585,17 +611,19 @@ ae_status enqueue_loop_tiled(ae_handle* h, const ScratchSet& sc, int batch, int 
       }
       g = base_tgemm(h, sc, tp.gu, M, 2 * F, D);
       g.A = h->ubuf; g.lda_bytes = D * ob; g.W = h->wgu + l * h->sgu; g.sw = h->wsc + 6 * l + 3;
+      g.swc = swl ? swl + h->qkv_n : nullptr;
       g.out = h->act; g.ldo = F; g.rowmax = h->rowmax; g.ldp = h->Mmax;
       if (!f8) post_norm(g, h->bg + it * 2 * F);
       AE_LAUNCH(launch_tgemm(tp.op, EPI_GELU, g, tp.gu.blocks, s));
       if (f8)
         AE_LAUNCH(launch_quant(static_cast<const float*>(h->act), nullptr, nullptr, nullptr, nullptr, M, F,
-                               h->T, h->rowmax, tp.gu.n_tiles, h->Mmax, ub8, h->sxrow, s));
+                               h->rowwise ? 1 : h->T, h->rowmax, tp.gu.n_tiles, h->Mmax, ub8, h->sxrow, s));
 
       g = base_tgemm(h, sc, tp.d, M, D, F);
       g.A = f8 ? h->ubuf : h->act; g.lda_bytes = F * ob; g.W = h->wd + l * h->sd;
       prefetch_cache(g, h->vtcache, (l + 1) % L, tp.d.blocks);
       g.sw = h->wsc + 6 * l + 5;
+      g.swc = swl ? swl + h->qkv_n + 2 * F : nullptr;
       g.h = h->h; g.ldh = D; g.gate = md + 5 * D;
       // the next layer's attention norm (the last layer's h goes to the
       // final norm, which reads h itself)
@@ -1045,6 +1073,8 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   h->ssq_tiles = h->D / 64;
   h->Mmax = h->Bmax * h->T;
   h->fp8 = cfg->proj_weight_dtype == AE_FP8_E4M3;
+  h->rowwise = h->fp8 && cfg->fp8_rowwise;
+  h->fp8o = h->fp8 && cfg->fp8_oproj;
   h->Dc = cfg->context_width;
   h->Sd = cfg->state_dim;
   h->dit = cfg->block_type == AE_BLOCK_DIT;
@@ -1132,7 +1162,14 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
     AE_ALLOC(h->bg, static_cast<size_t>(h->Nmax) * L * 2 * F * 4);
   }
   if (h->tiled) {
-    if (h->fp8) AE_ALLOC(h->ubuf, Mm * std::max(D, F));
+    if (h->fp8) AE_ALLOC(h->ubuf, Mm * std::max({D, F, static_cast<size_t>(h->qdim)}));
+    if (h->rowwise) {
+      h->swc_layer = static_cast<size_t>(h->qkv_n) + 2 * F + 2 * D;
+      AE_ALLOC(h->swc, L * h->swc_layer * 4);
+      const size_t cols = static_cast<size_t>(h->qdim) + 2 * h->kvdim + 2 * F + 2 * D;
+      AE_ALLOC(h->cmul, cols * 4);
+      AE_ALLOC(h->csc, cols * 4);
+    }
     AE_ALLOC(h->rrow, Mm * 4);
     AE_ALLOC(h->sxrow, Mm * 4);
     AE_ALLOC(h->rowmax, Mm * std::max<size_t>(1, 2 * F / 128) * 4);
@@ -1297,10 +1334,46 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
       AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get(p + "o2"), nullptr, nullptr, h->qdim, h->D, h->D, 0,
                             0, h->Hq, h->Hkv, h->dh, h->wo2 + l * h->so, st));
     }
-    AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get(p + "o"), nullptr, nullptr, h->qdim, h->D, h->D, 0,
-                          0, h->Hq, h->Hkv, h->dh, h->wo + l * h->so, st));
+    if (!h->fp8o)
+      AE_HIP(h, launch_pack(h->dt, PACK_PLAIN, get(p + "o"), nullptr, nullptr, h->qdim, h->D, h->D, 0,
+                            0, h->Hq, h->Hkv, h->dh, h->wo + l * h->so, st));
+    auto b16 = [&](const std::string& nm) { return static_cast<const uint16_t*>(get(nm)); };
+    if (h->rowwise) {
+      // a scale per output column of every tensor: multipliers for the
+      // packing, and the scales in packed column order for the epilogues
+      const int F = h->F, Dm = h->D, qd = h->qdim, kd = h->kvdim;
+      float* cm = h->cmul;
+      float* cs = h->csc;
+      const size_t oq = 0, ok = qd, ov = ok + kd, og = ov + kd, ou = og + F, od = ou + F, oo = od + Dm;
+      AE_HIP(h, launch_fp8_col_scales(b16(p + "q"), Dm, qd, qd, cm + oq, cs + oq, st));
+      AE_HIP(h, launch_fp8_col_scales(b16(p + "k"), Dm, kd, kd, cm + ok, cs + ok, st));
+      AE_HIP(h, launch_fp8_col_scales(b16(p + "v"), Dm, kd, kd, cm + ov, cs + ov, st));
+      AE_HIP(h, launch_fp8_col_scales(b16(p + "gate"), Dm, F, F, cm + og, cs + og, st));
+      AE_HIP(h, launch_fp8_col_scales(b16(p + "up"), Dm, F, F, cm + ou, cs + ou, st));
+      AE_HIP(h, launch_fp8_col_scales(b16(p + "down"), F, Dm, Dm, cm + od, cs + od, st));
+      float* sw = h->swc + l * h->swc_layer;
+      AE_HIP(h, launch_pack_fp8(PACK_QKV, b16(p + "q"), b16(p + "k"), b16(p + "v"), Dm, h->qkv_n, qd, kd, kd,
+                                h->Hq, h->Hkv, h->dh, h->wmul, h->wqkv + l * h->sqkv, st, cm + oq, cm + ok,
+                                cm + ov));
+      AE_HIP(h, launch_pack_col_scales(PACK_QKV, cs + oq, cs + ok, cs + ov, h->qkv_n, h->Hq, h->Hkv, h->dh, sw, st));
+      AE_HIP(h, launch_pack_fp8(PACK_GU, b16(p + "gate"), b16(p + "up"), nullptr, Dm, 2 * F, F, F, 0, h->Hq,
+                                h->Hkv, h->dh, h->wmul, h->wgu + l * h->sgu, st, cm + og, cm + ou));
+      AE_HIP(h, launch_pack_col_scales(PACK_GU, cs + og, cs + ou, nullptr, 2 * F, h->Hq, h->Hkv, h->dh,
+                                       sw + h->qkv_n, st));
+      AE_HIP(h, launch_pack_fp8(PACK_PLAIN, b16(p + "down"), nullptr, nullptr, F, Dm, Dm, 0, 0, h->Hq, h->Hkv,
+                                h->dh, h->wmul, h->wd + l * h->sd, st, cm + od));
+      AE_HIP(h, launch_pack_col_scales(PACK_PLAIN, cs + od, nullptr, nullptr, Dm, h->Hq, h->Hkv, h->dh,
+                                       sw + h->qkv_n + 2 * F, st));
+      if (h->fp8o) {
+        AE_HIP(h, launch_fp8_col_scales(b16(p + "o"), qd, Dm, Dm, cm + oo, cs + oo, st));
+        AE_HIP(h, launch_pack_fp8(PACK_PLAIN, b16(p + "o"), nullptr, nullptr, qd, Dm, Dm, 0, 0, h->Hq, h->Hkv,
+                                  h->dh, h->wmul, h->wo + l * h->so, st, cm + oo));
+        AE_HIP(h, launch_pack_col_scales(PACK_PLAIN, cs + oo, nullptr, nullptr, Dm, h->Hq, h->Hkv, h->dh,
+                                         sw + h->qkv_n + 2 * F + Dm, st));
+      }
+      continue;
+    }
     if (h->fp8) {
-      auto b16 = [&](const std::string& nm) { return static_cast<const uint16_t*>(get(nm)); };
       AE_HIP(h, launch_pack_fp8(PACK_QKV, b16(p + "q"), b16(p + "k"), b16(p + "v"), h->D, h->qkv_n,
                                 h->qdim, h->kvdim, h->kvdim, h->Hq, h->Hkv, h->dh, h->wmul + 6 * l,
                                 h->wqkv + l * h->sqkv, st));

@@ -140,13 +140,17 @@ ae_status aetest_fp8_norm_quantize(const float* h, int M, int D, int T, const fl
   Scratch sc;
   float* rowmax = sc.get<float>(static_cast<size_t>(M) * 4);
   AE_T(sc.err);
+  if (T == 1) {  // a scale per row: the one-pass row-wise kernel
+    AE_T(launch_rownorm_quant(h, M, D, scale, shift, eps, r_out, codes, sx_row, s));
+    return finish(hipSuccess, s);
+  }
   AE_T(launch_rownorm(h, M, D, scale, shift, eps, r_out, rowmax, s));
   AE_T(launch_quant(nullptr, h, r_out, scale, shift, M, D, T, rowmax, 1, M, codes, sx_row, s));
   return finish(hipSuccess, s);
 }
 
 ae_status aetest_fp8_down(const uint8_t* codes, const float* sx_row, int M, int K, const uint16_t* w, int N,
-                          float* y, float* sw, void* stream) {
+                          float* y, float* sw, int per_column, void* stream) {
   if (!codes || !sx_row || !w || !y || !sw || M < 1) return AE_ERR_INVALID_ARGUMENT;
   if (K < 128 || K % 128 || N < 128 || N % 128) return AE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -157,11 +161,19 @@ ae_status aetest_fp8_down(const uint8_t* codes, const float* sx_row, int M, int 
   float* mul = sc.get<float>(4);
   float* gate = sc.get<float>(static_cast<size_t>(N) * 4);
   float* partial = sc.get<float>(tgemm_partial_floats(g) * 4);
+  float* cmul = sc.get<float>(static_cast<size_t>(N) * 4);
+  float* swc = sc.get<float>(static_cast<size_t>(N) * 4);
   AE_T(sc.err);
-  const uint16_t* ws[1] = {w};
-  const size_t ns[1] = {static_cast<size_t>(K) * N};
-  AE_T(weight_scales(ws, ns, 1, amax, mul, sw, s));
-  AE_T(launch_pack_fp8(PACK_PLAIN, w, nullptr, nullptr, K, N, N, 0, 0, 1, 1, 64, mul, packed, s));
+  if (per_column) {
+    AE_T(launch_fp8_col_scales(w, K, N, N, cmul, sw, s));
+    AE_T(launch_pack_fp8(PACK_PLAIN, w, nullptr, nullptr, K, N, N, 0, 0, 1, 1, 64, cmul, packed, s, cmul));
+    AE_T(launch_pack_col_scales(PACK_PLAIN, sw, nullptr, nullptr, N, 1, 1, 64, swc, s));
+  } else {
+    const uint16_t* ws[1] = {w};
+    const size_t ns[1] = {static_cast<size_t>(K) * N};
+    AE_T(weight_scales(ws, ns, 1, amax, mul, sw, s));
+    AE_T(launch_pack_fp8(PACK_PLAIN, w, nullptr, nullptr, K, N, N, 0, 0, 1, 1, 64, mul, packed, s));
+  }
   hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(256), 0, s, gate, static_cast<size_t>(N), 1.0f);
   AE_T(hipGetLastError());
   AE_T(hipMemsetAsync(y, 0, static_cast<size_t>(M) * N * 4, s));
@@ -170,12 +182,13 @@ ae_status aetest_fp8_down(const uint8_t* codes, const float* sx_row, int M, int 
   a.h = y;
   a.ldh = N;
   a.gate = gate;
+  if (per_column) a.swc = swc;
   AE_T(launch_tgemm(OP_FP8, EPI_RESID, a, g.blocks, s));
   return finish(hipSuccess, s);
 }
 
 ae_status aetest_fp8_gate_up(const uint8_t* codes, const float* sx_row, int M, int K, const uint16_t* wg,
-                             const uint16_t* wu, int F, float* act, float* sw, void* stream) {
+                             const uint16_t* wu, int F, float* act, float* sw, int per_column, void* stream) {
   if (!codes || !sx_row || !wg || !wu || !act || !sw || M < 1 || F < 1) return AE_ERR_INVALID_ARGUMENT;
   if (K < 128 || K % 128 || (2 * F) % 128) return AE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -187,23 +200,33 @@ ae_status aetest_fp8_gate_up(const uint8_t* codes, const float* sx_row, int M, i
   float* mul = sc.get<float>(8);
   float* rowmax = sc.get<float>(static_cast<size_t>(g.n_tiles) * M * 4);
   float* partial = sc.get<float>(tgemm_partial_floats(g) * 4);
+  float* cmul = sc.get<float>(static_cast<size_t>(N) * 4);
+  float* swc = sc.get<float>(static_cast<size_t>(N) * 4);
   AE_T(sc.err);
-  const uint16_t* ws[2] = {wg, wu};
-  const size_t ns[2] = {static_cast<size_t>(K) * F, static_cast<size_t>(K) * F};
-  AE_T(weight_scales(ws, ns, 2, amax, mul, sw, s));
-  AE_T(launch_pack_fp8(PACK_GU, wg, wu, nullptr, K, N, F, F, 0, 1, 1, 64, mul, packed, s));
+  if (per_column) {  // sw: [gate columns | up columns]
+    AE_T(launch_fp8_col_scales(wg, K, F, F, cmul, sw, s));
+    AE_T(launch_fp8_col_scales(wu, K, F, F, cmul + F, sw + F, s));
+    AE_T(launch_pack_fp8(PACK_GU, wg, wu, nullptr, K, N, F, F, 0, 1, 1, 64, cmul, packed, s, cmul, cmul + F));
+    AE_T(launch_pack_col_scales(PACK_GU, sw, sw + F, nullptr, N, 1, 1, 64, swc, s));
+  } else {
+    const uint16_t* ws[2] = {wg, wu};
+    const size_t ns[2] = {static_cast<size_t>(K) * F, static_cast<size_t>(K) * F};
+    AE_T(weight_scales(ws, ns, 2, amax, mul, sw, s));
+    AE_T(launch_pack_fp8(PACK_GU, wg, wu, nullptr, K, N, F, F, 0, 1, 1, 64, mul, packed, s));
+  }
   TGemmArgs a = gemm_args(g, codes, sx_row, M, N, K, packed, partial, sw);
   a.out = act;
   a.ldo = F;
   a.rowmax = rowmax;
   a.ldp = M;
+  if (per_column) a.swc = swc;
   AE_T(launch_tgemm(OP_FP8, EPI_GELU, a, g.blocks, s));
   return finish(hipSuccess, s);
 }
 
 ae_status aetest_fp8_qkv(const uint8_t* codes, const float* sx_row, int M, int K, const uint16_t* wq,
                          const uint16_t* wk, const uint16_t* wv, int Hq, int Hkv, int dh, float* q, float* k,
-                         float* v, float* sw, void* stream) {
+                         float* v, float* sw, int per_column, void* stream) {
   if (!codes || !sx_row || !wq || !wk || !wv || !q || !k || !v || !sw || M < 1 || Hq < 1 || Hkv < 1)
     return AE_ERR_INVALID_ARGUMENT;
   const int qdim = Hq * dh, kvdim = Hkv * dh, N = qdim + 2 * kvdim;
@@ -223,12 +246,24 @@ ae_status aetest_fp8_qkv(const uint8_t* codes, const float* sx_row, int M, int K
   int* nvalid = sc.get<int>(4);
   float* cosb = sc.get<float>(static_cast<size_t>(M) * (dh / 2) * 4);
   float* sinb = sc.get<float>(static_cast<size_t>(M) * (dh / 2) * 4);
+  float* cmul = sc.get<float>(static_cast<size_t>(N) * 4);
+  float* swc = sc.get<float>(static_cast<size_t>(N) * 4);
   AE_T(sc.err);
-  const uint16_t* ws[3] = {wq, wk, wv};
-  const size_t ns[3] = {static_cast<size_t>(K) * qdim, static_cast<size_t>(K) * kvdim,
-                        static_cast<size_t>(K) * kvdim};
-  AE_T(weight_scales(ws, ns, 3, amax, mul, sw, s));
-  AE_T(launch_pack_fp8(PACK_QKV, wq, wk, wv, K, N, qdim, kvdim, kvdim, Hq, Hkv, dh, mul, packed, s));
+  if (per_column) {  // sw: [q columns | k columns | v columns]
+    float *sq = sw, *sk = sw + qdim, *sv = sw + qdim + kvdim;
+    AE_T(launch_fp8_col_scales(wq, K, qdim, qdim, cmul, sq, s));
+    AE_T(launch_fp8_col_scales(wk, K, kvdim, kvdim, cmul + qdim, sk, s));
+    AE_T(launch_fp8_col_scales(wv, K, kvdim, kvdim, cmul + qdim + kvdim, sv, s));
+    AE_T(launch_pack_fp8(PACK_QKV, wq, wk, wv, K, N, qdim, kvdim, kvdim, Hq, Hkv, dh, cmul, packed, s, cmul,
+                         cmul + qdim, cmul + qdim + kvdim));
+    AE_T(launch_pack_col_scales(PACK_QKV, sq, sk, sv, N, Hq, Hkv, dh, swc, s));
+  } else {
+    const uint16_t* ws[3] = {wq, wk, wv};
+    const size_t ns[3] = {static_cast<size_t>(K) * qdim, static_cast<size_t>(K) * kvdim,
+                          static_cast<size_t>(K) * kvdim};
+    AE_T(weight_scales(ws, ns, 3, amax, mul, sw, s));
+    AE_T(launch_pack_fp8(PACK_QKV, wq, wk, wv, K, N, qdim, kvdim, kvdim, Hq, Hkv, dh, mul, packed, s));
+  }
   AE_T(hipMemsetAsync(nvalid, 0, 4, s));
   AE_T(hipMemsetAsync(sinb, 0, static_cast<size_t>(M) * (dh / 2) * 4, s));
   hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(256), 0, s, cosb, static_cast<size_t>(M) * (dh / 2), 1.0f);
@@ -242,6 +277,7 @@ ae_status aetest_fp8_qkv(const uint8_t* codes, const float* sx_row, int M, int K
   a.rope_cos = cosb;
   a.rope_sin = sinb;
   a.T = M; a.Hq = Hq; a.Hkv = Hkv; a.dh = dh; a.S_max = S_max;
+  if (per_column) a.swc = swc;
   AE_T(launch_tgemm(OP_FP8, EPI_QKV, a, g.blocks, s));
   hipLaunchKernelGGL(bf16_to_f32_kernel, dim3(256), dim3(256), 0, s, qb, static_cast<size_t>(M) * qdim, q);
   hipLaunchKernelGGL(unpack_cache_kernel, dim3(256), dim3(256), 0, s, kc, M, Hkv, dh, S_max, 0, k);

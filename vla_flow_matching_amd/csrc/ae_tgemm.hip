@@ -380,12 +380,14 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
     // h += gate * y (fp8: y = acc * s_x * s_w); two columns per lane; then,
     // for a norm applied after the next product, the row sums of squares
     // per 64 columns and the modulated bf16 shadow
-    float gt[2], ns[2];
+    float gt[2], ns[2], cw[2];
+    const bool colw = OP == OP_FP8 && p.swc != nullptr;  // row-wise: a weight scale per column
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
       const int n = nt * kBN + 64 * hc + lane;
       gt[hc] = p.gate[n];
       ns[hc] = p.nsc ? 1.0f + p.nsc[n] : 0.0f;
+      cw[hc] = colw ? p.swc[n] : 1.0f;
     }
     for (int rb = wave; rb < rows; rb += 4 * kEB) {
       float hv[kEB][2], sxv[kEB];
@@ -394,7 +396,7 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
         const int m = m0 + min(rb + 4 * i, rows - 1);
 #pragma unroll
         for (int hc = 0; hc < 2; ++hc) hv[i][hc] = p.h[static_cast<size_t>(m) * p.ldh + nt * kBN + 64 * hc + lane];
-        sxv[i] = OP == OP_FP8 ? p.sx_row[m] * p.sw[0] : 1.0f;
+        sxv[i] = OP == OP_FP8 ? (colw ? p.sx_row[m] : p.sx_row[m] * p.sw[0]) : 1.0f;
       }
 #pragma unroll
       for (int i = 0; i < kEB; ++i) {
@@ -405,7 +407,8 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
 #pragma unroll
         for (int hc = 0; hc < 2; ++hc) {
           const int n = nt * kBN + 64 * hc + lane;
-          const float hn = hv[i][hc] + gt[hc] * (s_y[row][64 * hc + lane] * sxv[i]);
+          const float y = colw ? (s_y[row][64 * hc + lane] * sxv[i]) * cw[hc] : s_y[row][64 * hc + lane] * sxv[i];
+          const float hn = hv[i][hc] + gt[hc] * y;
           p.h[static_cast<size_t>(m) * p.ldh + n] = hn;
           sq[hc] = hn * hn;
           if (p.nsc) p.ha[static_cast<size_t>(m) * p.ldh + n] = f2bf(hn * ns[hc]);
@@ -422,7 +425,11 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
   } else if (EPI == EPI_GELU) {
     // lanes: 64 = 4 pairs x 16; gate half at 32 pr + jj, up half at +16
     const int f = (4 * nt + pr) * 16 + jj;
-    const float sw0 = OP == OP_FP8 ? p.sw[0] : 1.0f, sw1 = OP == OP_FP8 ? p.sw[1] : 1.0f;
+    float sw0 = OP == OP_FP8 ? p.sw[0] : 1.0f, sw1 = OP == OP_FP8 ? p.sw[1] : 1.0f;
+    if (OP == OP_FP8 && p.swc) {  // row-wise: the gate column's and the up column's own scales
+      sw0 = p.swc[nt * kBN + 32 * pr + jj];
+      sw1 = p.swc[nt * kBN + 32 * pr + 16 + jj];
+    }
     for (int rb = wave; rb < rows; rb += 4 * kEB) {
       float sxv[kEB];
 #pragma unroll
@@ -464,7 +471,12 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
     else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
     else { seg = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
     const int j = 16 * pi + jj;
-    const float sw = OP == OP_FP8 ? p.sw[seg] : 1.0f;
+    // fp8 weight scales of the pair's two columns (per tensor: the segment's)
+    float swa = OP == OP_FP8 ? p.sw[seg] : 1.0f, swb = swa;
+    if (OP == OP_FP8 && p.swc) {
+      swa = p.swc[nt * kBN + 32 * pr + jj];
+      swb = p.swc[nt * kBN + 32 * pr + 16 + jj];
+    }
     bf16_t* qo = static_cast<bf16_t*>(p.q);
     bf16_t* kc = static_cast<bf16_t*>(p.kcache);
     bf16_t* vt = static_cast<bf16_t*>(p.vtcache);
@@ -502,9 +514,8 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
           b = b * r + bias_b;
         }
         if (OP == OP_FP8) {
-          const float sc = sxv[i] * sw;
-          a *= sc;
-          b *= sc;
+          a *= sxv[i] * swa;
+          b *= sxv[i] * swb;
         }
         if (seg < 2) {
           const float ra = a * csv[i] - b * snv[i];
@@ -776,10 +787,35 @@ __global__ void scales_kernel(const unsigned* __restrict__ amax_bits, int n, flo
   }
 }
 
+// The logical source (0, 1, 2) and column of packed column pc: PACK_PLAIN
+// keeps the order; PACK_GU interleaves 16-column runs of gate and up;
+// PACK_QKV puts the two halves of each RoPE pair of q, then k, then v side by
+// side (16 + 16 columns).
+__device__ __forceinline__ void packed_source(int mode, int pc, int Hq, int Hkv, int dh, int& which, int& col) {
+  if (mode == PACK_PLAIN) {
+    which = 0;
+    col = pc;
+    return;
+  }
+  const int P = pc / 32, hf = (pc / 16) % 2, jj = pc % 16;
+  if (mode == PACK_GU) {
+    which = hf;
+    col = 16 * P + jj;
+    return;
+  }
+  const int pph = dh / 32, pq = Hq * pph, pk = Hkv * pph;
+  int head, pi;
+  if (P < pq) { which = 0; head = P / pph; pi = P % pph; }
+  else if (P < pq + pk) { which = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
+  else { which = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
+  col = head * dh + hf * (dh / 2) + 16 * pi + jj;
+}
+
 __global__ __launch_bounds__(256) void pack_fp8_kernel(int mode, const bf16_t* s0, const bf16_t* s1,
                                                        const bf16_t* s2, int K, int N, int ld0,
                                                        int ld1, int ld2, int Hq, int Hkv, int dh,
                                                        const float* __restrict__ mul3,
+                                                       const float* cm0, const float* cm1, const float* cm2,
                                                        uint4* __restrict__ dst) {
   const int kch = K / 128;
   const size_t total = static_cast<size_t>(N / 16) * kch * 2 * kWave;
@@ -792,31 +828,130 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(int mode, const bf16_t* s
     const int nb = static_cast<int>(fr / kch);
     const int pc = 16 * nb + lane % 16;
     const int k0 = kf * 128 + 32 * (lane / 16) + 16 * slot;
-    const bf16_t* src;
-    int ld, col, which;
-    if (mode == PACK_PLAIN) {
-      src = s0; ld = ld0; col = pc; which = 0;
-    } else {
-      const int P = pc / 32, hf = (pc / 16) % 2, jj = pc % 16;
-      if (mode == PACK_GU) {
-        src = hf ? s1 : s0; ld = hf ? ld1 : ld0; col = 16 * P + jj; which = hf;
-      } else {
-        const int pph = dh / 32, pq = Hq * pph, pk = Hkv * pph;
-        int seg, head, pi;
-        if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
-        else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
-        else { seg = 2; head = (P - pq - pk) / pph; pi = (P - pq - pk) % pph; }
-        src = seg == 0 ? s0 : (seg == 1 ? s1 : s2);
-        ld = seg == 0 ? ld0 : (seg == 1 ? ld1 : ld2);
-        col = head * dh + hf * (dh / 2) + 16 * pi + jj;
-        which = seg;
-      }
-    }
+    int col, which;
+    packed_source(mode, pc, Hq, Hkv, dh, which, col);
+    const bf16_t* src = which == 0 ? s0 : (which == 1 ? s1 : s2);
+    const int ld = which == 0 ? ld0 : (which == 1 ? ld1 : ld2);
+    const float* cm = which == 0 ? cm0 : (which == 1 ? cm1 : cm2);
     float v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = bf2f(src[static_cast<size_t>(k0 + i) * ld + col]);
-    dst[g] = e4m3_pack16(v, mul3[which]);
+    dst[g] = e4m3_pack16(v, cm ? cm[col] : mul3[which]);
   }
+}
+
+// Row-wise fp8 weights: per column of a [K][ld] bf16 tensor, one thread per
+// column (consecutive threads, consecutive columns).
+__global__ __launch_bounds__(256) void col_scales_kernel(const bf16_t* __restrict__ w, int K, int N, int ld,
+                                                         float* __restrict__ mul, float* __restrict__ scale) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= N) return;
+  float mx = 0.0f;
+  for (int k = 0; k < K; ++k) mx = fmaxf(mx, fabsf(bf2f(w[static_cast<size_t>(k) * ld + j])));
+  mul[j] = fp8_mul(mx);
+  scale[j] = fp8_scale(mx);
+}
+
+__global__ __launch_bounds__(256) void pack_col_scales_kernel(int mode, const float* sc0, const float* sc1,
+                                                              const float* sc2, int N, int Hq, int Hkv, int dh,
+                                                              float* __restrict__ out) {
+  const int pc = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pc >= N) return;
+  int which, col;
+  packed_source(mode, pc, Hq, Hkv, dh, which, col);
+  out[pc] = (which == 0 ? sc0 : (which == 1 ? sc1 : sc2))[col];
+}
+
+// Row-wise codes of the adaRMS input: one 256-thread workgroup per row
+// (float4 tid + 256 j of the row per thread, all in flight): r = 1 / rms,
+// u = adaRMS(h) and max |u| over the row, then the row's codes (four per
+// 32-bit word) from the same registers with its own scale.
+__global__ __launch_bounds__(256) void rownorm_quant_kernel(const float* __restrict__ h, int D,
+                                                            const float* __restrict__ scale,
+                                                            const float* __restrict__ shift, float eps,
+                                                            float* __restrict__ r_out, uint8_t* __restrict__ codes,
+                                                            float* __restrict__ sx_row) {
+  __shared__ float s_red[4];
+  const int row = blockIdx.x, tid = threadIdx.x, n4 = D / 4;
+  const float4* hr = reinterpret_cast<const float4*>(h + static_cast<size_t>(row) * D);
+  float4 v[kNormPer];
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int i = tid + 256 * j;
+    v[j] = i < n4 ? hr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  }
+  ss = block_sum(ss, s_red);
+  const float r = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  const float4* sc4 = reinterpret_cast<const float4*>(scale);
+  const float4* sh4 = reinterpret_cast<const float4*>(shift);
+  float mx = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int i = tid + 256 * j;
+    if (i >= n4) break;
+    const float4 s = sc4[i], b = sh4[i];
+    v[j] = make_float4(ada(v[j].x, r, s.x, b.x), ada(v[j].y, r, s.y, b.y), ada(v[j].z, r, s.z, b.z),
+                       ada(v[j].w, r, s.w, b.w));
+    mx = fmaxf(fmaxf(mx, fmaxf(fabsf(v[j].x), fabsf(v[j].y))), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+  }
+  mx = block_max(mx, s_red);
+  const float mul = fp8_mul(mx);
+  uint32_t* out = reinterpret_cast<uint32_t*>(codes + static_cast<size_t>(row) * D);
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int i = tid + 256 * j;
+    if (i >= n4) break;
+    out[i] = e4m3_code(v[j].x * mul) | (e4m3_code(v[j].y * mul) << 8) | (e4m3_code(v[j].z * mul) << 16) |
+             (e4m3_code(v[j].w * mul) << 24);
+  }
+  if (tid == 0) {
+    r_out[row] = r;
+    sx_row[row] = fp8_scale(mx);
+  }
+}
+
+// Row-wise codes of bf16 rows (the attention output feeding an fp8 output
+// projection): one 256-thread workgroup per row, eight values per uint4.
+constexpr int kQbPer = 2;  // uint4 (8 values) per thread: K <= 256 * 8 * kQbPer
+
+__global__ __launch_bounds__(256) void quant_bf16_rows_kernel(const bf16_t* __restrict__ src, int K,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ sx_row) {
+  __shared__ float s_red[4];
+  const int row = blockIdx.x, tid = threadIdx.x, n8 = K / 8;
+  const uint4* sr = reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * K);
+  float v[kQbPer][8];
+  float mx = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kQbPer; ++j) {
+    const int i = tid + 256 * j;
+    const uint4 w = i < n8 ? sr[i] : make_uint4(0, 0, 0, 0);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[j][2 * q] = __uint_as_float(ws[q] << 16);
+      v[j][2 * q + 1] = __uint_as_float(ws[q] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) mx = fmaxf(mx, fabsf(v[j][q]));
+  }
+  mx = block_max(mx, s_red);
+  const float mul = fp8_mul(mx);
+  uint2* out = reinterpret_cast<uint2*>(codes + static_cast<size_t>(row) * K);
+#pragma unroll
+  for (int j = 0; j < kQbPer; ++j) {
+    const int i = tid + 256 * j;
+    if (i >= n8) break;
+    uint32_t wd[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      wd[h2] = e4m3_code(v[j][4 * h2] * mul) | (e4m3_code(v[j][4 * h2 + 1] * mul) << 8) |
+               (e4m3_code(v[j][4 * h2 + 2] * mul) << 16) | (e4m3_code(v[j][4 * h2 + 3] * mul) << 24);
+    out[i] = make_uint2(wd[0], wd[1]);
+  }
+  if (tid == 0) sx_row[row] = fp8_scale(mx);
 }
 
 // bf16 weights in the same chunk order: [N/16][K/32][64 lanes][16 B] is
@@ -922,10 +1057,37 @@ hipError_t launch_fp8_scales(const unsigned* amax_bits, int n, float* mul, float
 
 hipError_t launch_pack_fp8(PackMode mode, const bf16_t* s0, const bf16_t* s1, const bf16_t* s2,
                            int K, int N, int ld0, int ld1, int ld2, int Hq, int Hkv, int dh,
-                           const float* mul3, uint4* dst, hipStream_t s) {
+                           const float* mul3, uint4* dst, hipStream_t s, const float* colmul0,
+                           const float* colmul1, const float* colmul2) {
   if (K % 128 || N % 16) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pack_fp8_kernel, dim3(1024), dim3(256), 0, s, static_cast<int>(mode), s0, s1,
-                     s2, K, N, ld0, ld1, ld2, Hq, Hkv, dh, mul3, dst);
+                     s2, K, N, ld0, ld1, ld2, Hq, Hkv, dh, mul3, colmul0, colmul1, colmul2, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_col_scales(const bf16_t* w, int K, int N, int ld, float* mul, float* scale, hipStream_t s) {
+  if (K < 1 || N < 1 || ld < N) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(col_scales_kernel, dim3((N + 255) / 256), dim3(256), 0, s, w, K, N, ld, mul, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_col_scales(PackMode mode, const float* sc0, const float* sc1, const float* sc2, int N,
+                                  int Hq, int Hkv, int dh, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(pack_col_scales_kernel, dim3((N + 255) / 256), dim3(256), 0, s, static_cast<int>(mode), sc0,
+                     sc1, sc2, N, Hq, Hkv, dh, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rownorm_quant(const float* h, int M, int D, const float* scale, const float* shift, float eps,
+                                float* r, uint8_t* codes, float* sx_row, hipStream_t s) {
+  if (D % 4 || D > 4 * 256 * kNormPer) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rownorm_quant_kernel, dim3(M), dim3(256), 0, s, h, D, scale, shift, eps, r, codes, sx_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_bf16_rows(const bf16_t* src, int M, int K, uint8_t* codes, float* sx_row, hipStream_t s) {
+  if (K % 8 || K > 256 * 8 * kQbPer) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_bf16_rows_kernel, dim3(M), dim3(256), 0, s, src, K, codes, sx_row);
   return hipGetLastError();
 }
 
