@@ -43,6 +43,9 @@ DESCRIPTIONS = {
     "c4": "MolmoBot-shaped expert",
     "c5": "Pi0.5-shaped expert, 16 concurrent requests",
     "c5fp8": "Pi0.5-shaped expert, 16 concurrent requests, e4m3 QKV / gate-up / down",
+    "c5fp8r": "Pi0.5-shaped expert, 16 concurrent requests, e4m3 QKV / O / gate-up / down with row-wise "
+              "scales (per activation row, per weight column)",
+    "c4dit": "MolmoBot-shaped expert with the DiT-style block (attn1 over the actions, attn2 over the prefix)",
 }
 
 
@@ -84,6 +87,8 @@ def algorithmic_work(w, n_valid, with_time_path=False):
     qd, kd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
     esz = 2 if w.dtype == "bf16" else 4
     layer_params = D * (qd + 2 * kd) + qd * D + 2 * D * F + F * D
+    if getattr(w, "block", "joint") == "dit":  # attn2's q2 and o2
+        layer_params += 2 * D * qd
     step_params = L * layer_params + 2 * A * D
     t_params = 6 * L * D * D + 2 * D * D + 2 * D * D
     kv_bytes = L * int(np.sum(n_valid)) * 2 * kd * esz
@@ -95,11 +100,12 @@ def algorithmic_work(w, n_valid, with_time_path=False):
 
 
 def fp8_flops_split(w, n_valid):
-    """(FLOPs of the e4m3 GEMMs: QKV, gate/up, down; all other FLOPs) per call."""
+    """(FLOPs of the e4m3 GEMMs: QKV, gate/up, down and, with fp8_o, O; all
+    other FLOPs) per call."""
     D, L, F, T, N = w.width, w.n_layers, w.mlp_dim, w.action_horizon, w.n_steps
     qd, kd = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
     B = len(n_valid)
-    fp8_params = L * (D * (qd + 2 * kd) + 2 * D * F + F * D)
+    fp8_params = L * (D * (qd + 2 * kd) + 2 * D * F + F * D + (qd * D if getattr(w, "fp8_o", False) else 0))
     f8 = 2 * B * T * fp8_params * N
     _, total = algorithmic_work(w, n_valid)
     return f8, total - f8
@@ -361,10 +367,16 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--others", default="c5,c5fp8,c4,c3,c1",
+    ap.add_argument("--others", default="c5,c5fp8,c5fp8r,c4,c4dit,c3,c1",
                     help="further workloads measured after the headline, or 'none'")
+    ap.add_argument("--other-calls", type=int, default=0,
+                    help="timed calls of each further workload (0: from --steps)")
+    ap.add_argument("--no-prepare", action="store_true", help="skip the context-preparation timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--proc-maps", default="",
+                    help="write the process's memory map to this file at the end (to attribute an "
+                         "address printed by a crash in a later exit handler, e.g. a profiler's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, run two plain 256 MiB device copies (a known-size "
                          "reference for HBM byte counters)")
@@ -417,24 +429,32 @@ def main():
             "wall_s_timed": r["wall_s"],
         }
         others = {}
-        bounds = {"c5": "mfma", "c5fp8": "mfma-fp8", "c4": "hbm", "c3": "hbm", "c1": "latency", "c2": "hbm"}
+        bounds = {"c5": "mfma", "c5fp8": "mfma-fp8", "c5fp8r": "mfma-fp8", "c4": "hbm", "c4dit": "hbm", "c3": "hbm",
+                  "c1": "latency", "c2": "hbm"}
         if args.others != "none":
             for name in [s for s in args.others.split(",") if s]:
                 heavy = name.startswith("c5")
                 calls = max(5, args.steps // 8) if heavy else max(10, args.steps // 2)
-                ro = run_gpu(name, calls, max(2, args.warmup // 4), prefix_reps=5 if heavy else 10)
+                warm, reps = max(2, args.warmup // 4), 5 if heavy else 10
+                if args.other_calls > 0:  # a short run (e.g. under a counter profiler)
+                    calls, warm, reps = args.other_calls, 1, 1
+                ro = run_gpu(name, calls, warm, prefix_reps=reps)
                 others[name] = workload_line(name, ro, bounds.get(name, "hbm"))
-            if "c4" in others:
-                others["c4"]["roofline"]["note"] = (
-                    "c4's weights (208 MB per step) and its visible K/V (~20 MB) fit in the 256 MB "
-                    "last-level cache, so a call can run above the HBM bound; reported against 8 TB/s")
+            for c4 in ("c4", "c4dit"):
+                if c4 in others:
+                    others[c4]["roofline"]["note"] = (
+                        "the MolmoBot-shaped weights (208 MB per step, 236 MB with the DiT block's q2 / o2) "
+                        "and the visible K/V (~20 MB) nearly fit in the 256 MB last-level cache, so a call "
+                        "can run above the HBM bound; reported against 8 TB/s")
         line["workloads"] = others
-        if args.others != "none":
+        if args.others != "none" and not args.no_prepare:
             line["context_preparation"] = run_prepare(20)
         if "c5" in others:
             line["secondary"] = others["c5"]
         if "c5fp8" in others:
             line["secondary_fp8"] = others["c5fp8"]
+        if "c5fp8r" in others:
+            line["secondary_fp8_rowwise"] = others["c5fp8r"]
     except DeviceErrors as e:
         print(f"bench.py: {e}", file=sys.stderr, flush=True)
         sys.exit(3)
@@ -451,6 +471,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print("copy calibration: 2 copies of 268435456 bytes", file=sys.stderr, flush=True)
+    if args.proc_maps:
+        with open("/proc/self/maps") as src, open(args.proc_maps, "w") as dst:
+            dst.write(src.read())
 
 
 if __name__ == "__main__":

@@ -80,6 +80,10 @@ WORKLOADS: Dict[str, Workload] = {
     "c4": Workload("c4", n_layers=12, width=768, n_q_heads=12, n_kv_heads=4, head_dim=64,
                    mlp_dim=3072, action_horizon=16, action_dim=14, n_steps=10, batch=1,
                    prefix_len=2048, dtype="bf16", proj_dtype="same", index=4, gate_bias=0.1),
+    # the c4 shapes and inputs with the DiT-style block (its extra weights drawn after c4's)
+    "c4dit": Workload("c4dit", n_layers=12, width=768, n_q_heads=12, n_kv_heads=4, head_dim=64,
+                      mlp_dim=3072, action_horizon=16, action_dim=14, n_steps=10, batch=1,
+                      prefix_len=2048, dtype="bf16", proj_dtype="same", index=4, gate_bias=0.1, block="dit"),
     "c5": Workload("c5", batch=16, prefix_len=1024, dtype="bf16", proj_dtype="same", index=5, **_PI05),
     "c5fp8": Workload("c5fp8", batch=16, prefix_len=1024, dtype="bf16", proj_dtype="fp8", index=5, **_PI05),
     # the c5 batch with row-wise fp8 scales and the attention output projection in fp8 as well
@@ -224,7 +228,7 @@ def valid_masks(w: Workload, seed: Optional[int] = None,
             else:  # three camera slots, cam2 masked, 250 text slots
                 m[b, :512] = 1
                 m[b, 768:768 + n_text] = 1
-        elif w.name == "c4":
+        elif w.name in ("c4", "c4dit"):
             n_instr = int(rng.integers(21, 35)) if nv is None else nv - 1601
             m[b, :1600 + n_instr + 1] = 1
         else:  # c5 / c5fp8 / generic: right padding
