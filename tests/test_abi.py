@@ -5,6 +5,7 @@ reports the missing device as AE_ERR_HIP."""
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 
@@ -206,3 +207,20 @@ def test_fp8_rowwise_configs(lib):
     assert st == binding.AE_ERR_HIP and not h.value
     cfg = binding.make_config(synth.workload("c5fp8r"))
     assert cfg.fp8_rowwise == 1 and cfg.fp8_oproj == 1
+
+
+def test_bench_refuses_to_report_after_device_errors(monkeypatch, capsys):
+    """bench.py prints no JSON line and exits with status 3 when a timed
+    workload reports device errors (a whole-call wait that timed out)."""
+    import bench
+
+    def boom(*a, **k):
+        raise bench.DeviceErrors("c2: 1 whole-call launch(es) timed out; their results are invalid")
+
+    monkeypatch.setattr(bench, "run_gpu", boom)
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--no-cpu-baseline"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 3
+    out = capsys.readouterr()
+    assert '"metric"' not in out.out and "timed out" in out.err
