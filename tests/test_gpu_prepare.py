@@ -202,3 +202,30 @@ def test_prepare_error_paths():
         out = ex.denoise(torch.zeros((1, 50, 32), dtype=torch.float32, device="cuda"), 1)
         torch.cuda.synchronize()
         assert torch.isfinite(out).all().item()
+
+
+def test_prepare_takes_the_bucket_of_its_rows():
+    """Context preparation and prefix buckets: the prepared prefix (with the
+    state row) takes the smallest bucket that holds prefix_len + 1, the
+    graph key follows it, and the actions match the oracle in each bucket."""
+    _need_gpu()
+    w = synth.workload("c4", batch=1, n_layers=2, n_steps=2, prefix_len=2047)
+    Dc, S = 256, 14
+    W = synth.make_weights(w)
+    CW = synth.make_context_weights(w, Dc, S)
+    state = synth.make_state(w, S)
+    x0 = synth.make_noise(w)
+    with expert(w, W, CW, 2048, Dc, S) as ex:
+        ex.set_prefix_buckets([1024, 2048])
+        for P, n, bucket in ((1023, 900, 1024), (1024, 1000, 2048), (1700, 1620, 2048)):
+            wp = dataclasses.replace(w, prefix_len=P)
+            m = np.zeros((1, P), np.uint8)
+            m[0, :n] = 1
+            H, _ = synth.make_context(wp, Dc, mask=m, garbage="nan")
+            out = gpu_prepare_denoise(ex, wp, H, m, state, x0, w.n_steps)
+            assert ex.stats()["prefix_bucket"] == bucket
+            ref = oracle_every_step(wp, W, CW, H, m, state, x0)[0]
+            err = float(np.abs(out - ref).max())
+            say(f"[parity] prepared prefix {P} (+ state) in bucket {bucket}: max|gpu-oracle| = {err:.3e}")
+            assert err <= TOL_BF16
+        assert ex.stats()["graph_captures"] == 2

@@ -54,6 +54,10 @@ def _run(ex, w, K, V, m, x0, static):
     ("c5", 3, 2, dict(n_layers=2, n_steps=2, prefix_len=640)),
     # fp32 whole-call kernel: 8 requests (64 rows), then 2
     ("c1", 8, 2, dict()),
+    # the DiT-style block (per-phase kernels, split K at 16-row requests): 2 requests, then 1
+    ("c4dit", 2, 1, dict(n_layers=2, n_steps=2)),
+    # row-wise e4m3 with the fp8 output projection: 3 requests, then 1
+    ("c5fp8r", 3, 1, dict(n_layers=2, n_steps=2, prefix_len=640)),
 ])
 def test_static_equals_denoise(name, first, second, fields):
     from vla_flow_matching_amd import binding

@@ -35,6 +35,11 @@ constexpr int kTargetBlocks = 256;  // one workgroup per CU at least
 constexpr int kPrefetchBlocks = 32;  // weight-prefetch workgroups beside the batched attention
 constexpr int kMaxGraphs = 64;   // graph_cache_size at most
 constexpr int kMaxBuckets = 32;  // prefix bucket lengths at most
+// Key splits per attention item in the whole-call kernel at most: past ~16
+// the distributed merge costs more than the shorter key loop saves (the
+// MolmoBot-shaped expert, 4 items over 2064 keys: 33 splits 6.73 ms per call,
+// 16 splits 6.38, 8 splits 6.43; the Pi0.5 shape plans 12 either way).
+constexpr int kPersistMaxSplits = 16;
 
 // A cached graph and an event recorded after its latest replay: an evicted
 // graph is destroyed only once that event has completed.
@@ -788,7 +793,7 @@ PersistArgs persist_args(const ae_handle* h, const ScratchSet& sc, int batch, in
   a.pcnt = sc.pcnt;
   const PersistPlans pp = plan_persist(h);
   a.pq = pp.q; a.po = pp.o; a.pg = pp.g; a.pd = pp.d;
-  const AttnPlan ap = plan_attention(h, batch, h->span, kTileM);
+  const AttnPlan ap = plan_attention(h, batch, h->span, kTileM, kPersistMaxSplits);
   a.n_qg = ap.n_qg; a.nsplit = ap.nsplit; a.kc_len = ap.kc_len;
   a.n_acnt = ap.items;
   a.acnt = sc.pcnt + pp.q.n_tiles + pp.o.n_tiles + pp.g.n_tiles + pp.d.n_tiles;
@@ -801,8 +806,8 @@ PersistArgs persist_args(const ae_handle* h, const ScratchSet& sc, int batch, in
 ScratchNeed scratch_need(const ae_handle* h, int b, int span, bool persist, bool any_span) {
   ScratchNeed n;
   if (persist) {
-    const AttnPlan pa = plan_attention(h, b, span, kTileM);
-    const int nsp = any_span ? max_attention_splits(h, pa.items, 1 << 30) : pa.nsplit;
+    const AttnPlan pa = plan_attention(h, b, span, kTileM, kPersistMaxSplits);
+    const int nsp = any_span ? max_attention_splits(h, pa.items, kPersistMaxSplits) : pa.nsplit;
     if (nsp > 1) n.afl = attention_partial_floats(h->dh, pa.items, nsp, kTileM);
     const PersistPlans pp = plan_persist(h);
     n.pcnt = pa.items;
