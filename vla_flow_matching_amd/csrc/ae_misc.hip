@@ -79,12 +79,16 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_rows_kernel(
     __syncthreads();
     if (!live) continue;
     for (int kk = 0; kk < kn; kk += kGemvUnroll) {
+      // every load of the group issued at a clamped, valid row and masked
+      // at use: a guarded load would be waited for on the spot, one HBM
+      // round trip per row
       float w[kGemvUnroll][kGemvCols];
 #pragma unroll
-      for (int u = 0; u < kGemvUnroll; ++u) {
-        if (kk + u < kn) load2<T>(W + static_cast<size_t>(k0 + kk + u) * ldw + n0, w[u]);
-        else w[u][0] = w[u][1] = 0.0f;
-      }
+      for (int u = 0; u < kGemvUnroll; ++u)
+        load2<T>(W + static_cast<size_t>(k0 + min(kk + u, kn - 1)) * ldw + n0, w[u]);
+#pragma unroll
+      for (int u = 0; u < kGemvUnroll; ++u)
+        if (kk + u >= kn) w[u][0] = w[u][1] = 0.0f;
 #pragma unroll
       for (int u = 0; u < kGemvUnroll; ++u)
 #pragma unroll
