@@ -340,9 +340,20 @@ struct PersistPlans {
   PGemm q, o, g, d;
 };
 
+// K splits of the QKV phase at most: its reducers also rotate and scatter
+// q / K / V, and fewer, longer members measured faster there (Pi0.5 shape:
+// 6 splits 12.2 ms per call, 4 splits 11.75, 2 splits 11.8, 8 splits 13.3;
+// the MolmoBot shape goes from 12 to 4 at +0.1 ms); the other phases keep
+// the plan that covers the workgroups (fewer splits there measured slower).
+constexpr int kPersistQkvMaxSplits = 4;
+
 PersistPlans plan_persist(const ae_handle* h) {
   PersistPlans p;
   p.q = plan_pgemm(h, h->qkv_n, h->D);
+  {
+    const int min_s = (p.q.k_frags + 4 * persist_kpw() - 1) / (4 * persist_kpw());
+    p.q.ksplit = std::max(min_s, std::min(p.q.ksplit, kPersistQkvMaxSplits));
+  }
   p.o = plan_pgemm(h, h->D, h->qdim);
   p.g = plan_pgemm(h, 2 * h->F, h->D);
   p.d = plan_pgemm(h, h->D, h->F);
