@@ -38,6 +38,8 @@
  *    host except ae_create / ae_destroy.
  *  - One stream per handle at a time; the library does no locking.
  *  - Weight matrices are [in_features, out_features] row-major (y = x W + b).
+ *  - Fields and arguments that name an enumerator are plain ints, so a value
+ *    outside the enumeration is well defined and rejected by the checks.
  */
 #ifndef AE_H
 #define AE_H
@@ -88,8 +90,8 @@ typedef struct {
   int max_prefix_len;   /* largest prefix_len ae_set_prefix_kv accepts */
   int max_batch;        /* largest batch (requests) */
   int max_steps;        /* largest Euler step count ae_denoise accepts */
-  ae_dtype act_dtype;   /* AE_F32 or AE_BF16: weights, prefix K/V, activations */
-  ae_dtype proj_weight_dtype; /* act_dtype, or AE_FP8_E4M3 for the q/k/v,
+  int act_dtype;        /* an ae_dtype: AE_F32 or AE_BF16 (weights, prefix K/V, activations) */
+  int proj_weight_dtype;/* an ae_dtype: act_dtype, or AE_FP8_E4M3 for the q/k/v,
                                  gate/up and down projections (bf16 only) */
   float rope_theta;     /* RoPE base (10000) */
   float rms_eps;        /* adaRMS epsilon (1e-6) */
@@ -133,7 +135,7 @@ typedef struct {
   const void* data;
   int ndim;
   long long shape[4];
-  ae_dtype dtype;
+  int dtype;  /* an ae_dtype, equal to act_dtype */
 } ae_tensor_view;
 
 typedef struct {
@@ -278,7 +280,7 @@ ae_status ae_get_stats(const ae_handle* h, ae_stats* out);
 /* The handle's last error message ("" if none); "null handle" for NULL. */
 const char* ae_last_error(const ae_handle* h);
 /* A static description of a status code. */
-const char* ae_status_string(ae_status s);
+const char* ae_status_string(int s);
 /* Synchronise the device, release every graph and buffer, free the handle.
  * NULL is ignored. */
 void ae_destroy(ae_handle* h);

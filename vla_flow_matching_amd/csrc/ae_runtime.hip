@@ -1009,7 +1009,7 @@ void* static_scratch(int dev) {
 
 extern "C" {
 
-const char* ae_status_string(ae_status s) {
+const char* ae_status_string(int s) {
   switch (s) {
     case AE_OK: return "ok";
     case AE_ERR_INVALID_ARGUMENT: return "invalid argument";
