@@ -31,9 +31,10 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 
-# Sources the whole-call kernel is compiled from; a stored counter reading
-# is reported only while their digest is the one it was taken with.
-KERNEL_SOURCES = ["ae_persist.hip", "ae_device.h", "ae_kernels.h"]
+# Sources the whole-call kernel is compiled and planned from (its split
+# counts are chosen in the runtime); a stored counter reading is reported
+# only while their digest is the one it was taken with.
+KERNEL_SOURCES = ["ae_persist.hip", "ae_device.h", "ae_kernels.h", "ae_runtime.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "persist_kernel_c2_traffic.txt")
 
 DESCRIPTIONS = {
