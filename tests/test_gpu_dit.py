@@ -208,3 +208,22 @@ def test_dit_with_prepared_context_and_state():
         n = np.array([int(m[b].sum()) + 1])
         ref = E.integrate(x0[b:b + 1], kv, n, w.n_steps)
         check(out[b:b + 1], ref, TOL_BF16, f"DiT prepared context request {b}")
+
+
+def test_dit_past_one_row_tile():
+    """The DiT block at 5 MolmoBot-shaped requests (80 action rows: several
+    GEMM row tiles, and attention items of several requests), each request
+    against the oracle."""
+    _need_gpu()
+    w = synth.workload("c4", block="dit", batch=5, n_layers=2, n_steps=2, prefix_len=512)
+    say("[case] DiT block, 5 requests (80 action rows)")
+    W = synth.make_weights(w)
+    m = synth.valid_masks(w, n_valid=(512, 300, 17, 0, 450))
+    K, V, _ = synth.make_prefix(w, mask=m, garbage="nan")
+    x0 = synth.make_noise(w)
+    g = Dit(w, W)
+    out = g.run(K, V, m, x0)
+    refs = oracle_pool.per_request(w, W, K, V, m, x0, range(5))
+    for b, (ref, _) in enumerate(refs):
+        check(out[b:b + 1], ref, TOL_BF16, f"DiT request {b} of 5 (n={int(m[b].sum())})")
+    g.ex.close()

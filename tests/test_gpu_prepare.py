@@ -229,3 +229,26 @@ def test_prepare_takes_the_bucket_of_its_rows():
             say(f"[parity] prepared prefix {P} (+ state) in bucket {bucket}: max|gpu-oracle| = {err:.3e}")
             assert err <= TOL_BF16
         assert ex.stats()["graph_captures"] == 2
+
+
+def test_prepare_with_rowwise_fp8_expert():
+    """Context preparation feeding an fp8 expert (row-wise scales, fp8
+    output projection): the context products stay bf16, the denoise runs
+    the e4m3 path; two requests against the oracle's row-wise emulation at
+    reduced depth, where the fp8 loop meets the 2e-2 contract."""
+    _need_gpu()
+    w = synth.workload("c5fp8r", batch=2, n_layers=2, n_steps=2, prefix_len=700)
+    Dc = 512
+    say("[case] prepare: row-wise fp8 expert, 2 requests, context 512 wide")
+    W = synth.make_weights(w)
+    CW = synth.make_context_weights(w, Dc, 0)
+    m = synth.valid_masks(w, n_valid=(700, 560))
+    H, _ = synth.make_context(w, Dc, mask=m, garbage="nan")
+    x0 = synth.make_noise(w)
+    with expert(w, W, CW, w.prefix_len, Dc, 0) as ex:
+        out = gpu_prepare_denoise(ex, w, H, m, None, x0, w.n_steps)
+    refs = oracle_every_step(w, W, CW, H, m, None, x0)
+    for b in range(2):
+        err = float(np.abs(out[b:b + 1] - refs[b]).max())
+        say(f"[parity] row-wise fp8 with prepared context, request {b}: max|gpu-oracle| = {err:.3e}")
+        assert err <= TOL_BF16
