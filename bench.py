@@ -218,6 +218,47 @@ def run_gpu(name, calls, warmup, prefix_reps=0):
     return res
 
 
+def vendor_gemm_yardstick(name="c5", per_graph=50, replays=10):
+    """The vendor library's bf16 products (hipBLASLt through torch.matmul,
+    replayed from a graph) on one layer's four product shapes of a workload:
+    a reference point for what a general-purpose GEMM reaches at these
+    shapes, beside the fused per-phase kernels (whose per-kernel times come
+    from the kernel trace).  No part of the denoise path runs here."""
+    import torch
+    from vla_flow_matching_amd import synth
+
+    w = synth.workload(name)
+    M, D, F = w.batch * w.action_horizon, w.width, w.mlp_dim
+    qdim, kvdim = w.n_q_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    shapes = {"qkv": (M, D, qdim + 2 * kvdim), "o": (M, qdim, D), "gate_up": (M, D, 2 * F), "down": (M, F, D)}
+    out = {"library": "hipBLASLt (torch.matmul, bf16, graph replay)", "rows": M}
+    total = 0.0
+    for key, (m, k, n) in shapes.items():
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+        c = a @ b
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                c = a @ b
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (per_graph * replays)
+        tf = 2.0 * m * k * n / (us * 1e-6) / 1e12
+        out[key] = {"m": m, "k": k, "n": n, "us": us, "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS}
+        total += us
+        del g, a, b, c
+    out["us_per_layer"] = total
+    return out
+
+
 def run_prepare(reps, context_width=2560, state_dim=14):
     """Time ae_prepare_prefix on the MolmoBot-shaped workload: every layer's
     context K/V from per-layer hidden states of a Qwen3-4B-wide context
@@ -373,6 +414,8 @@ def main():
     ap.add_argument("--other-calls", type=int, default=0,
                     help="timed calls of each further workload (0: from --steps)")
     ap.add_argument("--no-prepare", action="store_true", help="skip the context-preparation timing")
+    ap.add_argument("--no-yardstick", action="store_true",
+                    help="skip timing the vendor library's products at c5's shapes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--proc-maps", default="",
@@ -451,6 +494,8 @@ def main():
         if args.others != "none" and not args.no_prepare:
             line["context_preparation"] = run_prepare(20)
         if "c5" in others:
+            if not args.no_yardstick:
+                others["c5"]["vendor_gemm_yardstick"] = vendor_gemm_yardstick("c5")
             line["secondary"] = others["c5"]
         if "c5fp8" in others:
             line["secondary_fp8"] = others["c5fp8"]
