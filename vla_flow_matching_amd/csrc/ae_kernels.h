@@ -263,6 +263,7 @@ hipError_t launch_pack_fp8(PackMode mode, const uint16_t* s0, const uint16_t* s1
 
 struct PGemm {
   int n_tiles, k_frags, ksplit;
+  int nb;  // 16-column groups per tile: 4 (64 columns) or 2 (32 columns, bf16)
 };
 
 struct PersistArgs {

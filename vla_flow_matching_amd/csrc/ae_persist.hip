@@ -64,6 +64,7 @@ __device__ __forceinline__ PGemm plan_of(const __attribute__((address_space(4)))
   r.n_tiles = g.n_tiles;
   r.k_frags = g.k_frags;
   r.ksplit = g.ksplit;
+  r.nb = g.nb;
   return r;
 }
 
@@ -192,17 +193,25 @@ __device__ __forceinline__ void finish_rms(KArgs& p, const float (&v)[16], float
   if (part == 0 && row < p.M) s_r[row] = 1.0f / sqrtf(acc / static_cast<float>(p.D) + p.eps);
 }
 
-template <typename T, int PRO, int EPI>
+// NB: 16-column groups per tile (4: 64 columns; 2: 32 columns, one RoPE or
+// gate/up pair, with twice the K fragments per wave in the same registers,
+// so a K = 1024 product needs no split).  Lane = tile column in the
+// epilogues; with 32 columns lanes 32-63 mirror 0-31 and store nothing.
+template <typename T, int PRO, int EPI, int NB = 4>
 __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLayer& ly,
                                            uint32_t llgen, int gen_wait, char* smem) {
   using MM = Mma<T>;
   constexpr int E = MM::E;
   constexpr int KSTEP = MM::KSTEP;
   constexpr int MT = kTileM / 16;
-  constexpr int NB = kTileN / 16;
+  constexpr int TN = 16 * NB;       // tile columns
+  constexpr int KPW = kKpw * 4 / NB;  // k-fragments per wave (the same weight registers)
   constexpr int kRw = kTileM / 4;  // epilogue rows per wave at most
+  constexpr int kRedPer = MT * NB / 4;  // (row tile, column group) blocks each wave sums
+  static_assert(NB == 4 || NB == 2, "64- or 32-column tiles");
+  static_assert(EPI != EPI_RESID || NB == 4, "the residual epilogues take 64-column tiles");
   auto s_red = reinterpret_cast<f32x4 (*)[MT * NB][kWave]>(smem);
-  auto s_y = reinterpret_cast<float (*)[kTileN + 1]>(smem);
+  auto s_y = reinterpret_cast<float (*)[TN + 1]>(smem);
   // row 1/rms (PRO_ADARMS), past the reduction tile
   float* s_r = reinterpret_cast<float*>(smem + 4 * MT * NB * kWave * sizeof(f32x4));
 
@@ -224,19 +233,20 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
     // wait for it on the spot, one round trip per element.
 
     // weights of this task -> registers, before waiting for the inputs
-    uint4 wb[kKpw][NB];
+    uint4 wb[KPW][NB];
     const uint4* Wt = ly.W + static_cast<size_t>(nt) * NB * g.k_frags * kWave + lane;
 #pragma unroll
-    for (int c = 0; c < kKpw; ++c) {
+    for (int c = 0; c < KPW; ++c) {
       const int kf = min(kf0 + wave + 4 * c, g.k_frags - 1);
 #pragma unroll
       for (int j = 0; j < NB; ++j) wb[c][j] = Wt[(static_cast<size_t>(j) * g.k_frags + kf) * kWave];
     }
 
     // per-column epilogue constants (they depend only on the step)
-    const float gn = EPI == EPI_RESID ? ly.gate[nt * kTileN + lane] : 0.0f;
-    const float nsc = EPI == EPI_RESID && ly.nsc ? 1.0f + ly.nsc[nt * kTileN + lane] : 0.0f;
-    const float bs = PRO == PRO_ADARMS ? ly.bias[nt * kTileN + lane] : 0.0f;
+    const int lc = lane % TN;  // the lane's tile column
+    const float gn = EPI == EPI_RESID ? ly.gate[nt * TN + lc] : 0.0f;
+    const float nsc = EPI == EPI_RESID && ly.nsc ? 1.0f + ly.nsc[nt * TN + lc] : 0.0f;
+    const float bs = PRO == PRO_ADARMS ? ly.bias[nt * TN + lc] : 0.0f;
 
     if (!waited) {
       bar_wait(p, gen_wait);
@@ -246,9 +256,9 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
     // A operand of the task, all in flight together
     const int arow = lane % 16;
     const int acol = E * (lane / 16);
-    uint4 araw[kKpw][MT];
+    uint4 araw[KPW][MT];
 #pragma unroll
-    for (int c = 0; c < kKpw; ++c)
+    for (int c = 0; c < KPW; ++c)
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const int row = min(16 * i + arow, rows - 1);
@@ -267,7 +277,7 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
       for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-    for (int c = 0; c < kKpw; ++c) {
+    for (int c = 0; c < KPW; ++c) {
       if (c < cnt) {
         uint4 a[MT];
 #pragma unroll
@@ -287,21 +297,25 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
 #pragma unroll
         for (int j = 0; j < NB; ++j) s_red[wave][i * NB + j][lane] = acc[i][j];
     __syncthreads();
-    f32x4 v[MT];
+    // wave w sums blocks w, w + 4, ... (block = row tile * NB + column group)
+    f32x4 v[kRedPer];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kRedPer; ++u) {
+      const int blk = wave + 4 * u, i = blk / NB;
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (i < mtr)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) v[i] += s_red[w][i * NB + wave][lane];
+        for (int w = 0; w < 4; ++w) v[u] += s_red[w][blk][lane];
     }
     if (PRO == PRO_ADARMS) finish_rms(p, rv, s_r);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int u = 0; u < kRedPer; ++u) {
+      const int blk = wave + 4 * u, i = blk / NB, j = blk % NB;
       if (i < mtr)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_y[16 * i + 4 * (lane / 16) + e][16 * wave + lane % 16] = v[i][e];
+        for (int e = 0; e < 4; ++e) s_y[16 * i + 4 * (lane / 16) + e][16 * j + lane % 16] = v[u][e];
+    }
     __syncthreads();
 
     int r0 = 0, r1 = rows;
@@ -318,7 +332,7 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
     int seg = 0, head = 0, jrot = 0;
     const bool hi = (lane & 16) != 0;
     if (EPI == EPI_QKV) {
-      const int P = 2 * nt + lane / 32, pq = p.Hq * pph, pk = p.Hkv * pph;
+      const int P = nt * (NB / 2) + lc / 32, pq = p.Hq * pph, pk = p.Hkv * pph;
       int pi;
       if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
       else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
@@ -332,7 +346,7 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
       if (i < nrw) {                                                                  \
         const int row = r0 + wave + 4 * i;                                            \
         if (EPI == EPI_RESID) {                                                       \
-          ein[i] = ch.ldf(4u * (row * p.D + nt * kTileN + lane));                     \
+          ein[i] = ch.ldf(4u * (row * p.D + nt * TN + lc));                           \
         } else {                                                                      \
           const int req = row / p.T, tt = row % p.T;                                  \
           const size_t ti2 = (static_cast<size_t>(req) * p.T + tt) * half + jrot;     \
@@ -353,17 +367,17 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
       // no store drain, counter or group wait sits between the members'
       // stores and the reduction.
       const Coh cp(reinterpret_cast<uint2*>(p.gpart) + static_cast<size_t>(nt) * g.ksplit * kTileF);
-      for (int i = tid; i < rows * (kTileN / 2); i += kThreads) {
-        const int r = i / (kTileN / 2), c2 = 2 * (i % (kTileN / 2));
-        cp.st16(8u * (s * kTileF + r * kTileN + c2),
+      for (int i = tid; i < rows * (TN / 2); i += kThreads) {
+        const int r = i / (TN / 2), c2 = 2 * (i % (TN / 2));
+        cp.st16(8u * (s * kTileF + r * TN + c2),
                 make_uint4(__float_as_uint(s_y[r][c2]), llgen, __float_as_uint(s_y[r][c2 + 1]), llgen));
       }
       AE_EPI_LOADS
 #undef AE_EPI_LOADS
-      const int n2 = (r1 - r0) * (kTileN / 2);  // packet pairs of the slice
+      const int n2 = (r1 - r0) * (TN / 2);  // packet pairs of the slice
       for (int i = tid; i < n2; i += kThreads) {
-        const int r = r0 + i / (kTileN / 2), c2 = 2 * (i % (kTileN / 2));
-        const uint32_t off = 8u * (r * kTileN + c2);
+        const int r = r0 + i / (TN / 2), c2 = 2 * (i % (TN / 2));
+        const uint32_t off = 8u * (r * TN + c2);
         float t0 = 0.0f, t1 = 0.0f;
         for (int s0 = 0; s0 < g.ksplit; s0 += 8) {
           uint4 buf[8];
@@ -405,9 +419,9 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
         const int row = r0 + wave + 4 * i;
         if (row >= r1) continue;
         const float hn = ein[i] + gn * s_y[row][lane];
-        ch.stf(4u * (row * p.D + nt * kTileN + lane), hn);
+        ch.stf(4u * (row * p.D + nt * TN + lane), hn);
         if (ly.nsc) {
-          const uint32_t off = sizeof(T) * (row * p.D + nt * kTileN + lane);
+          const uint32_t off = sizeof(T) * (row * p.D + nt * TN + lane);
           if (sizeof(T) == 2) cha.st2(off, f2bf(hn * nsc));
           else cha.stf(off, hn * nsc);
         }
@@ -418,29 +432,30 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
       // lanes 32p + jj (jj < 16) hold gate, 32p + 16 + jj the matching up
       const Coh co(p.act);
       for (int row = r0 + wave; row < r1; row += 4) {
-        const float y = PRO == PRO_ADARMS ? s_y[row][lane] * s_r[row] + bs : s_y[row][lane];
+        const float y = PRO == PRO_ADARMS ? s_y[row][lc] * s_r[row] + bs : s_y[row][lc];
         const float other = xor16_swap(y);
-        if (!hi) {
-          const int f = (2 * nt + lane / 32) * 16 + lane % 16;
+        if (!hi && lane < TN) {
+          const int f = (nt * (NB / 2) + lc / 32) * 16 + lane % 16;
           const float a = gelu_tanh(y) * other;
           if (sizeof(T) == 2) co.st2(2u * (row * p.F + f), f2bf(a));
           else co.stf(4u * (row * p.F + f), a);
         }
       }
-    } else if (2 * nt >= (p.Hq + p.Hkv) * pph) {
+    } else if (nt * (NB / 2) >= (p.Hq + p.Hkv) * pph) {
       // EPI_QKV, a V tile (not rotated): V^T rows are head columns, so the
       // member's rows are a run of consecutive keys per column.  Lane
       // (column c / 8, key j = lane % 8) stores column c's key j: one store
       // instruction covers eight columns' runs instead of 64 scattered keys.
       const int pv0 = (p.Hq + p.Hkv) * pph;
-      float bsv[2];
-      int colv[2], bgv[2];
+      constexpr int NU = TN / 32;  // 32-column passes
+      float bsv[NU];
+      int colv[NU], bgv[NU];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int lc = (wave + 4 * u) * 8 + lane / 8;  // tile column
-        const int P = 2 * nt + lc / 32 - pv0;
-        bsv[u] = PRO == PRO_ADARMS ? ly.bias[nt * kTileN + lc] : 0.0f;
-        colv[u] = ((lc & 16) ? half : 0) + 16 * (P % pph) + lc % 16;
+      for (int u = 0; u < NU; ++u) {
+        const int vc = (wave + 4 * u) * 8 + lane / 8;  // tile column
+        const int P = nt * (NB / 2) + vc / 32 - pv0;
+        bsv[u] = PRO == PRO_ADARMS ? ly.bias[nt * TN + vc] : 0.0f;
+        colv[u] = ((vc & 16) ? half : 0) + 16 * (P % pph) + vc % 16;
         bgv[u] = P / pph;  // head
       }
       for (int rb = r0; rb < r1; rb += 8) {
@@ -450,9 +465,9 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
         const int key = p.n_valid[req] + rc % p.T;
         const float rs = PRO == PRO_ADARMS ? s_r[rc] : 1.0f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int lc = (wave + 4 * u) * 8 + lane / 8;
-          const float y = PRO == PRO_ADARMS ? s_y[rc][lc] * rs + bsv[u] : s_y[rc][lc];
+        for (int u = 0; u < NU; ++u) {
+          const int vc = (wave + 4 * u) * 8 + lane / 8;
+          const float y = PRO == PRO_ADARMS ? s_y[rc][vc] * rs + bsv[u] : s_y[rc][vc];
           const uint32_t bgi = static_cast<uint32_t>(req * p.Hkv + bgv[u]);
           const uint32_t off =
               sizeof(T) * (bgi * p.S_max * p.dh + static_cast<uint32_t>(KvLayout<T>::v_off(key, colv[u], p.dh)));
@@ -469,11 +484,12 @@ __device__ __forceinline__ void gemm_phase(KArgs& p, const PGemm g, const GemmLa
       for (int i = 0; i < kRw; ++i) {
         const int row = r0 + wave + 4 * i;
         if (row >= r1) continue;
-        const float y = PRO == PRO_ADARMS ? s_y[row][lane] * s_r[row] + bs : s_y[row][lane];
+        const float y = PRO == PRO_ADARMS ? s_y[row][lc] * s_r[row] + bs : s_y[row][lc];
         const float other = xor16_swap(y);
         // (a, b) -> (a cos - b sin, b cos + a sin); v is not rotated
         const float cs = seg < 2 ? ecs[i] : 1.0f, sn = seg < 2 ? esn[i] : 0.0f;
         const float val = hi ? y * cs + other * sn : y * cs - other * sn;
+        if (lane >= TN) continue;  // (a 32-column tile: the mirrored half)
         if (seg == 0) {
           const uint32_t off = sizeof(T) * (row * p.qdim + head * p.dh + col);
           if (sizeof(T) == 2) cqo.st2(off, f2bf(val));
@@ -1085,7 +1101,15 @@ __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs) {
         ly.gate = nullptr;
         ly.nsc = nullptr;
         ly.W = p.wqkv + l * p.sqkv; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bq + static_cast<size_t>(it) * p.qkv_n;
-        gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, plan_of(p.pq), ly, gbase + 8 * it + 1, gen, smem);
+        const PGemm pg = plan_of(p.pq);
+        bool narrow = false;
+        if constexpr (sizeof(T) == 2) {
+          if (pg.nb == 2) {
+            gemm_phase<T, PRO_ADARMS, EPI_QKV, 2>(p, pg, ly, gbase + 8 * it + 1, gen, smem);
+            narrow = true;
+          }
+        }
+        if (!narrow) gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, pg, ly, gbase + 8 * it + 1, gen, smem);
         bar_arrive(p, ++gen);
       }
       {
@@ -1110,7 +1134,15 @@ __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs) {
         ly.kc = ly.vt = nullptr;
         ly.gate = ly.nsc = nullptr;
         ly.W = p.wgu + l * p.sgu; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bg + static_cast<size_t>(it) * 2 * p.F;
-        gemm_phase<T, PRO_ADARMS, EPI_GELU>(p, plan_of(p.pg), ly, gbase + 8 * it + 3, gen, smem);
+        const PGemm pg = plan_of(p.pg);
+        bool narrow = false;
+        if constexpr (sizeof(T) == 2) {
+          if (pg.nb == 2) {
+            gemm_phase<T, PRO_ADARMS, EPI_GELU, 2>(p, pg, ly, gbase + 8 * it + 3, gen, smem);
+            narrow = true;
+          }
+        }
+        if (!narrow) gemm_phase<T, PRO_ADARMS, EPI_GELU>(p, pg, ly, gbase + 8 * it + 3, gen, smem);
         bar_arrive(p, ++gen);
       }
       {

@@ -324,6 +324,7 @@ LayerPlans plan_layer(const ae_handle* h, int M) {
 // weight fragments in registers.
 PGemm plan_pgemm(const ae_handle* h, int N, int K) {
   PGemm g;
+  g.nb = kTileN / 16;
   g.n_tiles = N / kTileN;
   g.k_frags = K / kstep_of(h->dt);
   int s = h->G / g.n_tiles;
@@ -339,6 +340,25 @@ PGemm plan_pgemm(const ae_handle* h, int N, int K) {
 struct PersistPlans {
   PGemm q, o, g, d;
 };
+
+// The same product in 32-column tiles with the whole K range per task (bf16,
+// K / 32 <= 8 fragments per wave): no split, so no exchange of partials
+// between workgroups, but each task reads all of A (twice the A bytes per
+// workgroup).  Taken only where these tasks alone cover every workgroup;
+// with fewer the idle CUs cost more than the exchange saves.  Measured on
+// the Pi0.5 shape: gate/up (256 tasks) 11.80 -> 11.63 ms per call; QKV (80
+// tasks) 12.17, both 11.94; on the MolmoBot shape gate/up (192 tasks) 6.61
+// -> 6.73.  Returns false where it does not apply.
+bool plan_pgemm_narrow(const ae_handle* h, int N, int K, PGemm& g) {
+  if (h->dt != DT_BF16 || N % 32 || K % 32) return false;
+  const int kf = K / kstep_of(h->dt);
+  if (kf > 4 * 2 * persist_kpw() || N / 32 < h->G) return false;
+  g.nb = 2;
+  g.n_tiles = N / 32;
+  g.k_frags = kf;
+  g.ksplit = 1;
+  return true;
+}
 
 // K splits of the QKV phase at most: its reducers also rotate and scatter
 // q / K / V, and fewer, longer members measured faster there (Pi0.5 shape:
@@ -357,6 +377,9 @@ PersistPlans plan_persist(const ae_handle* h) {
   p.o = plan_pgemm(h, h->D, h->qdim);
   p.g = plan_pgemm(h, 2 * h->F, h->D);
   p.d = plan_pgemm(h, h->D, h->F);
+  PGemm n;
+  if (plan_pgemm_narrow(h, h->qkv_n, h->D, n)) p.q = n;
+  if (plan_pgemm_narrow(h, 2 * h->F, h->D, n)) p.g = n;
   return p;
 }
 
