@@ -1101,15 +1101,7 @@ __global__ __launch_bounds__(kThreads) void persist_kernel(PersistArgs) {
         ly.gate = nullptr;
         ly.nsc = nullptr;
         ly.W = p.wqkv + l * p.sqkv; ly.A = p.ha; ly.lda = p.D; ly.bias = p.bq + static_cast<size_t>(it) * p.qkv_n;
-        const PGemm pg = plan_of(p.pq);
-        bool narrow = false;
-        if constexpr (sizeof(T) == 2) {
-          if (pg.nb == 2) {
-            gemm_phase<T, PRO_ADARMS, EPI_QKV, 2>(p, pg, ly, gbase + 8 * it + 1, gen, smem);
-            narrow = true;
-          }
-        }
-        if (!narrow) gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, pg, ly, gbase + 8 * it + 1, gen, smem);
+        gemm_phase<T, PRO_ADARMS, EPI_QKV>(p, plan_of(p.pq), ly, gbase + 8 * it + 1, gen, smem);
         bar_arrive(p, ++gen);
       }
       {

@@ -377,8 +377,7 @@ PersistPlans plan_persist(const ae_handle* h) {
   p.o = plan_pgemm(h, h->D, h->qdim);
   p.g = plan_pgemm(h, 2 * h->F, h->D);
   p.d = plan_pgemm(h, h->D, h->F);
-  PGemm n;
-  if (plan_pgemm_narrow(h, h->qkv_n, h->D, n)) p.q = n;
+  PGemm n;  // (QKV keeps its split: 80 narrow tasks measured slower)
   if (plan_pgemm_narrow(h, 2 * h->F, h->D, n)) p.g = n;
   return p;
 }
