@@ -242,7 +242,7 @@ def test_c4_full_parity():
     say("[case] c4 full: 12 layers, 12/4 heads, head_dim 64, prefix 2048")
     W = synth.make_weights(w)
     g = Gpu(w, W)
-    for n in (1622, 1635):
+    for n in (1622, 1628, 1635):  # the pages' 1621-1634 visible tokens, plus the state row
         m = synth.valid_masks(w, n_valid=(n,))
         K, V, _ = synth.make_prefix(w, mask=m)
         x0 = synth.make_noise(w)
