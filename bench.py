@@ -47,6 +47,7 @@ DESCRIPTIONS = {
     "c5fp8r": "Pi0.5-shaped expert, 16 concurrent requests, e4m3 QKV / O / gate-up / down with row-wise "
               "scales (per activation row, per weight column)",
     "c4dit": "MolmoBot-shaped expert with the DiT-style block (attn1 over the actions, attn2 over the prefix)",
+    "c2fp8r": "Pi0.5-shaped action expert, e4m3 QKV / O / gate-up / down with row-wise scales",
 }
 
 
@@ -93,7 +94,12 @@ def algorithmic_work(w, n_valid, with_time_path=False):
     step_params = L * layer_params + 2 * A * D
     t_params = 6 * L * D * D + 2 * D * D + 2 * D * D
     kv_bytes = L * int(np.sum(n_valid)) * 2 * kd * esz
-    bytes_call = N * (step_params * esz + kv_bytes) + (t_params * esz if with_time_path else 0)
+    # e4m3 projections move one byte per weight (their per-column scales are negligible)
+    f8_params = 0
+    if getattr(w, "proj_dtype", "same") == "fp8":
+        f8_params = L * (D * (qd + 2 * kd) + 2 * D * F + F * D + (qd * D if getattr(w, "fp8_o", False) else 0))
+    step_bytes = f8_params + (step_params - f8_params) * esz
+    bytes_call = N * (step_bytes + kv_bytes) + (t_params * esz if with_time_path else 0)
     B = len(n_valid)
     attn_flops = sum(4 * T * w.n_q_heads * w.head_dim * (int(n) + T) for n in n_valid) * L * N
     flops_call = 2 * B * T * step_params * N + attn_flops + (2 * N * t_params if with_time_path else 0)
@@ -409,7 +415,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--others", default="c5,c5fp8,c5fp8r,c4,c4dit,c3,c1",
+    ap.add_argument("--others", default="c5,c5fp8,c5fp8r,c4,c4dit,c3,c2fp8r,c1",
                     help="further workloads measured after the headline, or 'none'")
     ap.add_argument("--other-calls", type=int, default=0,
                     help="timed calls of each further workload (0: from --steps)")
@@ -474,6 +480,7 @@ def main():
         }
         others = {}
         bounds = {"c5": "mfma", "c5fp8": "mfma-fp8", "c5fp8r": "mfma-fp8", "c4": "hbm", "c4dit": "hbm", "c3": "hbm",
+                  "c2fp8r": "hbm",
                   "c1": "latency", "c2": "hbm"}
         if args.others != "none":
             for name in [s for s in args.others.split(",") if s]:

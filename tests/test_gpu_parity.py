@@ -375,14 +375,19 @@ def test_c5_batched_full():
 
 
 @pytest.mark.parametrize("name,batch", [("c5", 2), ("c5", 3), ("c5fp8", 3), ("c5fp8r", 3), ("c5fp8r", 1),
-                                        ("c5fp8", 1)])
+                                        ("c5fp8", 1), ("c2fp8r", 1)])
 def test_batched_tiles_small(name, batch):
     """The batched path at reduced depth: 100 / 150 action rows leave a ragged
     32-row tile and a part-filled 8-row action-in group; every request
     against the oracle (fp8: the oracle's e4m3 emulation with per-request
     activation scales; c5fp8r: scales per row and per weight column, and the
     output projection in fp8 too).  Batch 1 runs the fp8 variants on a single
-    request (fp8 never takes the whole-call kernel)."""
+    request (fp8 never takes the whole-call kernel); c2fp8r is the c2 request
+    (712-row prefix, 663 visible) in row-wise fp8.  With c2's weights the
+    oracle's own output moves by 1.25e-2 when its noise is perturbed by a
+    relative 1e-6 at this depth already, so that case is held to the derived
+    fp8 tolerance (fp8_tolerance, here ~2.5e-2) and its error is printed
+    against 2e-2."""
     _need_gpu()
     w = synth.workload(name, batch=batch, n_layers=2, n_steps=2)
     say(f"[case] {name} batch {batch}, 2 layers, 2 steps")
@@ -394,7 +399,11 @@ def test_batched_tiles_small(name, batch):
     Kc, Vc = K.copy(), V.copy()
     Kc[:, m == 0] = 0.0
     Vc[:, m == 0] = 0.0
-    check(g.run(K, V, m, x0), oracle(w, W, Kc, Vc, m, x0), TOL_BF16, f"{name} batch {batch}")
+    ref = oracle(w, W, Kc, Vc, m, x0)
+    tol = fp8_tolerance(w, W, Kc, Vc, m, x0, ref) if name == "c2fp8r" else TOL_BF16
+    err = check(g.run(K, V, m, x0), ref, tol, f"{name} batch {batch}")
+    if tol > TOL_BF16:
+        say(f"[fp8] {name}: {err:.3e} against the 2e-2 contract: {'within' if err <= TOL_BF16 else 'above'}")
 
 
 _COVER = [(dt, dh, b, "same", 7) for dt in ("f32", "bf16") for dh in (64, 128, 256) for b in (1, 3)] + [

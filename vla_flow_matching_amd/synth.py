@@ -84,6 +84,9 @@ WORKLOADS: Dict[str, Workload] = {
     "c4dit": Workload("c4dit", n_layers=12, width=768, n_q_heads=12, n_kv_heads=4, head_dim=64,
                       mlp_dim=3072, action_horizon=16, action_dim=14, n_steps=10, batch=1,
                       prefix_len=2048, dtype="bf16", proj_dtype="same", index=4, gate_bias=0.1, block="dit"),
+    # the c2 request with row-wise fp8 scales and the fp8 output projection (one request in e4m3)
+    "c2fp8r": Workload("c2fp8r", batch=1, prefix_len=712, dtype="bf16", proj_dtype="fp8", index=2,
+                       fp8_scaling="rowwise", fp8_o=True, **_PI05),
     "c5": Workload("c5", batch=16, prefix_len=1024, dtype="bf16", proj_dtype="same", index=5, **_PI05),
     "c5fp8": Workload("c5fp8", batch=16, prefix_len=1024, dtype="bf16", proj_dtype="fp8", index=5, **_PI05),
     # the c5 batch with row-wise fp8 scales and the attention output projection in fp8 as well
@@ -220,9 +223,9 @@ def valid_masks(w: Workload, seed: Optional[int] = None,
         if w.name == "c1":
             nv = 48 if nv is None else nv
             m[b, :nv] = 1
-        elif w.name in ("c2", "c3"):
+        elif w.name in ("c2", "c3", "c2fp8r"):
             n_text = int(rng.integers(8, 201)) if nv is None else nv - 512
-            if w.name == "c2" or P == 712:
+            if w.name != "c3" or P == 712:
                 m[b, :512] = 1
                 m[b, 512:512 + n_text] = 1
             else:  # three camera slots, cam2 masked, 250 text slots
