@@ -455,7 +455,8 @@ def project_prefix_kv(hidden: np.ndarray, wk: np.ndarray, wv: np.ndarray, mask: 
 def encode_state(state: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:
     """The robot state's context row: one linear layer, state [B, S] ->
     [B, Dc] (MolmoBot PR Part 2: the state is part of the context computed
-    once per query; the single linear layer is this build's reading)."""
+    once per query; the pages do not give the encoder's form, and one linear
+    layer is the plainest reading)."""
     return linear(np.asarray(state, dtype=F64), w, b)
 
 
