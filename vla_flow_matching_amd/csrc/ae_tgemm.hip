@@ -297,18 +297,23 @@ __device__ __forceinline__ void tg_compute(const uint4* A, const u32x4 (&B)[2][2
   }
 }
 
-// Tile decode: the m-tiles and K splits of one n-tile run on one XCD
-// (workgroups are dealt to the 8 XCDs round-robin) so they share its L2.
+// Tile decode.  Units (n-tile, m-tile, K split) in that order are cut into
+// eight equal contiguous ranges, one per XCD (workgroups are dealt to the 8
+// XCDs round-robin), so the m-tiles of an n-tile share one L2 (or two, where
+// a range boundary falls inside them) and every XCD gets the same number of
+// units whatever the n-tile count (dealing whole n-tiles to XCDs left XCDs
+// idle below 8 n-tiles and unbalanced at 20).
 __device__ __forceinline__ bool tile_of(int bid, int n_tiles, int m_tiles, int ksplit, int& nt,
                                         int& mt, int& s) {
-  const int xcd = bid % kXcd;
-  int idx = bid / kXcd;
-  s = idx % ksplit;
-  idx /= ksplit;
-  mt = idx % m_tiles;
-  idx /= m_tiles;
-  nt = idx * kXcd + xcd;
-  return nt < n_tiles;
+  const int units = n_tiles * m_tiles * ksplit;
+  const int per_xcd = (units + kXcd - 1) / kXcd;
+  const int li = bid / kXcd;
+  const int u = (bid % kXcd) * per_xcd + li;
+  if (li >= per_xcd || u >= units) return false;
+  s = u % ksplit;
+  mt = (u / ksplit) % m_tiles;
+  nt = u / (ksplit * m_tiles);
+  return true;
 }
 
 // The GEMM epilogues on rows [m0, m0 + rows) of n-tile nt, the finished
@@ -998,8 +1003,8 @@ TGemmPlan plan_tgemm(int M, int N, int K, int kc, int target_blocks) {
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   g.ksplit = s;
-  const int nt_hi = (g.n_tiles + kXcd - 1) / kXcd;
-  g.blocks = kXcd * g.ksplit * g.m_tiles * nt_hi;
+  const int units = g.n_tiles * g.m_tiles * g.ksplit;
+  g.blocks = kXcd * ((units + kXcd - 1) / kXcd);
   return g;
 }
 
