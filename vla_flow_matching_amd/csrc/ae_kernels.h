@@ -200,6 +200,11 @@ struct TGemmArgs {
   const int* key_map;
   const float* pos_cos;
   const float* pos_sin;
+  // several layers' context products in one launch (the state rows): columns
+  // [l c, (l + 1) c) with c = ctx_layer_cols belong to layer l, whose caches
+  // start ctx_layer_elems elements past layer 0's (0: one layer)
+  int ctx_layer_cols;
+  size_t ctx_layer_elems;
   // bf16 norm after the product (A = bf16(h (1 + scale))): EPI_QKV / EPI_GELU
   // finish with y = r_row acc + bias[col], r_row from the row sums of squares
   // ssq[ssq_tiles][ldssq] (64-column partials over K columns); EPI_RESID

@@ -459,19 +459,34 @@ __global__ void pos_table_kernel(int n_pos, int dh, float theta, float* cos_t, f
   }
 }
 
-// The robot state's context row (one workgroup per request): fp32 sums of
-// the state times the input layer, plus its bias, stored as bf16; its cache
-// key is the request's last visible position.
+// The robot state's context row (256 columns of request blockIdx.y per
+// workgroup): fp32 sums of the state times the input layer in state order,
+// plus its bias, stored as bf16; its cache key is the request's last visible
+// position.  The state's weights are requested 8 rows at a time, all in
+// flight (a loop bounded at run time would wait out each load in turn).
+constexpr int kStateBatch = 8;
 __global__ __launch_bounds__(256) void state_prep_kernel(const float* state, int S, const bf16_t* w,
                                                          const bf16_t* bias, int D, const int* n_valid,
                                                          bf16_t* out, int* key_out) {
-  const int b = blockIdx.x;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+  const int b = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < D) {
     float acc = bf2f(bias[c]);
-    for (int i = 0; i < S; ++i) acc = fmaf(state[static_cast<size_t>(b) * S + i], bf2f(w[static_cast<size_t>(i) * D + c]), acc);
+    for (int i0 = 0; i0 < S; i0 += kStateBatch) {
+      float sv[kStateBatch], wv[kStateBatch];
+#pragma unroll
+      for (int u = 0; u < kStateBatch; ++u) {
+        const int i = min(i0 + u, S - 1);
+        sv[u] = state[static_cast<size_t>(b) * S + i];
+        wv[u] = bf2f(w[static_cast<size_t>(i) * D + c]);
+      }
+#pragma unroll
+      for (int u = 0; u < kStateBatch; ++u)
+        if (i0 + u < S) acc = fmaf(sv[u], wv[u], acc);
+    }
     out[static_cast<size_t>(b) * D + c] = f2bf(acc);
   }
-  if (threadIdx.x == 0) key_out[b] = n_valid[b] - 1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) key_out[b] = n_valid[b] - 1;
 }
 
 }  // namespace
@@ -485,8 +500,8 @@ hipError_t launch_pos_table(int n_pos, int dh, float theta, float* cos_t, float*
 hipError_t launch_state_prep(const float* state, int batch, int S, const uint16_t* w, const uint16_t* bias,
                              int D, const int* n_valid, uint16_t* out, int* key_out, hipStream_t s) {
   if (batch < 1 || S < 1 || D < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(state_prep_kernel, dim3(batch), dim3(256), 0, s, state, S, w, bias, D, n_valid, out,
-                     key_out);
+  hipLaunchKernelGGL(state_prep_kernel, dim3((D + 255) / 256, batch), dim3(256), 0, s, state, S, w, bias, D,
+                     n_valid, out, key_out);
   return hipGetLastError();
 }
 

@@ -1229,6 +1229,11 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
       need.gfl = std::max(need.gfl, tgemm_partial_floats(g));
       need.gcn = std::max(need.gcn, static_cast<size_t>(g.m_tiles) * g.n_tiles);
     }
+    for (int m = 1; m <= h->Bmax && h->Sd > 0; ++m) {  // the state rows, every layer in one product
+      const TGemmPlan g = plan_tgemm(m, h->L * 2 * h->kvdim, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
+      need.gfl = std::max(need.gfl, tgemm_partial_floats(g));
+      need.gcn = std::max(need.gcn, static_cast<size_t>(g.m_tiles) * g.n_tiles);
+    }
   }
   for (int b = 1; b <= h->Bmax; ++b) {
     need.max_with(scratch_need(h, b, h->Pmax, false, true));
@@ -1484,9 +1489,16 @@ ae_status ae_prepare_prefix(ae_handle* h, int batch, int prefix_len, const void*
     AE_HIP(h, launch_state_prep(state, batch, h->Sd, h->st_w, h->st_b, h->Dc, h->n_valid, h->st_h, h->st_key, st));
   // one product per layer: [K | V] of every context row, K rotated at the
   // row's count position, visible rows scattered to their keys
-  auto project = [&](int l, const void* A, int rows, int rows_per_req, const int* keys) -> ae_status {
-    const TGemmPlan g = plan_tgemm(rows, 2 * h->kvdim, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
-    TGemmArgs a = base_tgemm(h, h->own, g, rows, 2 * h->kvdim, h->Dc);
+  // (layers > 1: layers l .. l + layers - 1 in one launch, their packed
+  // weights being consecutive)
+  auto project = [&](int l, int layers, const void* A, int rows, int rows_per_req, const int* keys) -> ae_status {
+    const int N = layers * 2 * h->kvdim;
+    const TGemmPlan g = plan_tgemm(rows, N, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
+    TGemmArgs a = base_tgemm(h, h->own, g, rows, N, h->Dc);
+    if (layers > 1) {
+      a.ctx_layer_cols = 2 * h->kvdim;
+      a.ctx_layer_elems = kv_layer / h->esz;
+    }
     a.A = A;
     a.lda_bytes = static_cast<size_t>(h->Dc) * 2;
     a.W = h->wctx + l * h->sctx;
@@ -1500,16 +1512,14 @@ ae_status ae_prepare_prefix(ae_handle* h, int batch, int prefix_len, const void*
     const hipError_t e = launch_tgemm(OP_BF16, EPI_QKV, a, g.blocks, st);
     return e == hipSuccess ? AE_OK : hip_fail(h, e, "launch_tgemm (context)");
   };
-  for (int l = 0; l < h->L; ++l) {
-    if (prefix_len > 0) {
-      const char* Hl = static_cast<const char*>(hidden) + static_cast<size_t>(l) * batch * prefix_len * h->Dc * 2;
-      const ae_status r = project(l, Hl, batch * prefix_len, prefix_len, h->comp_idx);
-      if (r != AE_OK) return r;
-    }
-    if (state) {
-      const ae_status r = project(l, h->st_h, batch, 1, h->st_key);
-      if (r != AE_OK) return r;
-    }
+  for (int l = 0; l < h->L && prefix_len > 0; ++l) {
+    const char* Hl = static_cast<const char*>(hidden) + static_cast<size_t>(l) * batch * prefix_len * h->Dc * 2;
+    const ae_status r = project(l, 1, Hl, batch * prefix_len, prefix_len, h->comp_idx);
+    if (r != AE_OK) return r;
+  }
+  if (state) {  // the state row is the same input to every layer: one product over all of them
+    const ae_status r = project(0, h->L, h->st_h, batch, 1, h->st_key);
+    if (r != AE_OK) return r;
   }
   // finite values in the rest of each request's last key block (no rows copied)
   AE_HIP(h, launch_prefix_copy(h->dt, nullptr, nullptr, h->comp_idx, h->n_valid, h->T, h->L, batch, 0, h->Hkv,

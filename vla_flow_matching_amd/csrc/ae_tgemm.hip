@@ -470,7 +470,14 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
     const int pph = p.dh / 32;
     const int pq = p.Hq * pph, pk = p.Hkv * pph;
     const int half = p.dh / 2;
-    const int P = 4 * nt + pr;
+    int P = 4 * nt + pr;
+    size_t lofs = 0;  // (several layers in one product: the caches of this column's layer)
+    if (p.ctx_layer_cols > 0) {
+      const int ppl = p.ctx_layer_cols / 32;
+      const int layer = P / ppl;
+      P -= layer * ppl;
+      lofs = static_cast<size_t>(layer) * p.ctx_layer_elems;
+    }
     int seg, head, pi;
     if (P < pq) { seg = 0; head = P / pph; pi = P % pph; }
     else if (P < pq + pk) { seg = 1; head = (P - pq) / pph; pi = (P - pq) % pph; }
@@ -483,8 +490,8 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
       swb = p.swc[nt * kBN + 32 * pr + 16 + jj];
     }
     bf16_t* qo = static_cast<bf16_t*>(p.q);
-    bf16_t* kc = static_cast<bf16_t*>(p.kcache);
-    bf16_t* vt = static_cast<bf16_t*>(p.vtcache);
+    bf16_t* kc = static_cast<bf16_t*>(p.kcache) + lofs;
+    bf16_t* vt = static_cast<bf16_t*>(p.vtcache) + lofs;
     const bool ctx = p.key_map != nullptr;
     for (int rb = wave; rb < rows; rb += 4 * kEB) {
       float csv[kEB], snv[kEB], sxv[kEB];
