@@ -200,11 +200,14 @@ struct TGemmArgs {
   const int* key_map;
   const float* pos_cos;
   const float* pos_sin;
-  // several layers' context products in one launch (the state rows): columns
-  // [l c, (l + 1) c) with c = ctx_layer_cols belong to layer l, whose caches
-  // start ctx_layer_elems elements past layer 0's (0: one layer)
+  // several layers' context products in one launch: columns [l c, (l + 1) c)
+  // with c = ctx_layer_cols belong to layer l, whose A rows start
+  // a_layer_bytes past layer 0's (0: every layer multiplies the same rows,
+  // as the state rows do) and whose caches start ctx_layer_elems elements
+  // past layer 0's (ctx_layer_cols 0: one layer)
   int ctx_layer_cols;
   size_t ctx_layer_elems;
+  size_t a_layer_bytes;
   // bf16 norm after the product (A = bf16(h (1 + scale))): EPI_QKV / EPI_GELU
   // finish with y = r_row acc + bias[col], r_row from the row sums of squares
   // ssq[ssq_tiles][ldssq] (64-column partials over K columns); EPI_RESID

@@ -1224,12 +1224,7 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   // the largest call's scratch, over every batch, path and prefix bucket
   ScratchNeed need;
   if (h->Dc > 0) {  // the context products' K splits and tile counters, at any row count
-    for (int m = 1; m <= h->Bmax * std::max(1, h->Pmax); ++m) {
-      const TGemmPlan g = plan_tgemm(m, 2 * h->kvdim, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
-      need.gfl = std::max(need.gfl, tgemm_partial_floats(g));
-      need.gcn = std::max(need.gcn, static_cast<size_t>(g.m_tiles) * g.n_tiles);
-    }
-    for (int m = 1; m <= h->Bmax && h->Sd > 0; ++m) {  // the state rows, every layer in one product
+    for (int m = 1; m <= h->Bmax * std::max(1, h->Pmax); ++m) {  // (every layer in one product)
       const TGemmPlan g = plan_tgemm(m, h->L * 2 * h->kvdim, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
       need.gfl = std::max(need.gfl, tgemm_partial_floats(g));
       need.gcn = std::max(need.gcn, static_cast<size_t>(g.m_tiles) * g.n_tiles);
@@ -1489,21 +1484,20 @@ ae_status ae_prepare_prefix(ae_handle* h, int batch, int prefix_len, const void*
     AE_HIP(h, launch_state_prep(state, batch, h->Sd, h->st_w, h->st_b, h->Dc, h->n_valid, h->st_h, h->st_key, st));
   // one product per layer: [K | V] of every context row, K rotated at the
   // row's count position, visible rows scattered to their keys
-  // (layers > 1: layers l .. l + layers - 1 in one launch, their packed
-  // weights being consecutive)
-  auto project = [&](int l, int layers, const void* A, int rows, int rows_per_req, const int* keys) -> ae_status {
-    const int N = layers * 2 * h->kvdim;
+  // every layer in one launch (their packed weights are consecutive); layer
+  // l's A rows start a_layer_bytes after layer 0's (0: the same rows for all)
+  auto project = [&](const void* A, size_t a_layer_bytes, int rows, int rows_per_req, const int* keys) -> ae_status {
+    const int N = h->L * 2 * h->kvdim;
     const TGemmPlan g = plan_tgemm(rows, N, h->Dc, tgemm_kc(OP_BF16), kTargetBlocks);
     TGemmArgs a = base_tgemm(h, h->own, g, rows, N, h->Dc);
-    if (layers > 1) {
-      a.ctx_layer_cols = 2 * h->kvdim;
-      a.ctx_layer_elems = kv_layer / h->esz;
-    }
+    a.ctx_layer_cols = 2 * h->kvdim;
+    a.ctx_layer_elems = kv_layer / h->esz;
+    a.a_layer_bytes = a_layer_bytes;
     a.A = A;
     a.lda_bytes = static_cast<size_t>(h->Dc) * 2;
-    a.W = h->wctx + l * h->sctx;
-    a.kcache = static_cast<char*>(h->kcache) + l * kv_layer;
-    a.vtcache = static_cast<char*>(h->vtcache) + l * kv_layer;
+    a.W = h->wctx;
+    a.kcache = h->kcache;
+    a.vtcache = h->vtcache;
     a.n_valid = h->n_valid;
     a.T = rows_per_req; a.Hq = 0; a.Hkv = h->Hkv; a.dh = h->dh; a.S_max = h->S_max;
     a.key_map = keys;
@@ -1512,13 +1506,13 @@ ae_status ae_prepare_prefix(ae_handle* h, int batch, int prefix_len, const void*
     const hipError_t e = launch_tgemm(OP_BF16, EPI_QKV, a, g.blocks, st);
     return e == hipSuccess ? AE_OK : hip_fail(h, e, "launch_tgemm (context)");
   };
-  for (int l = 0; l < h->L && prefix_len > 0; ++l) {
-    const char* Hl = static_cast<const char*>(hidden) + static_cast<size_t>(l) * batch * prefix_len * h->Dc * 2;
-    const ae_status r = project(l, 1, Hl, batch * prefix_len, prefix_len, h->comp_idx);
+  if (prefix_len > 0) {  // hidden [L][batch][prefix_len][Dc]
+    const ae_status r = project(hidden, static_cast<size_t>(batch) * prefix_len * h->Dc * 2, batch * prefix_len,
+                                prefix_len, h->comp_idx);
     if (r != AE_OK) return r;
   }
-  if (state) {  // the state row is the same input to every layer: one product over all of them
-    const ae_status r = project(0, h->L, h->st_h, batch, 1, h->st_key);
+  if (state) {  // the state row is the same input to every layer
+    const ae_status r = project(h->st_h, 0, batch, 1, h->st_key);
     if (r != AE_OK) return r;
   }
   // finite values in the rest of each request's last key block (no rows copied)

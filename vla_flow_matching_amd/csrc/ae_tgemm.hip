@@ -605,6 +605,8 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
 
   // A staging map: item i = tid + 256 j: row i/8, 16-byte column i%8.
   const uint8_t* Ab = static_cast<const uint8_t*>(p.A);
+  if (p.ctx_layer_cols > 0)  // (several layers in one product: this tile's layer's rows)
+    Ab += static_cast<size_t>((nt * kBN) / p.ctx_layer_cols) * p.a_layer_bytes;
   uint32_t a_off[NA];
   int a_lds[NA];
 #pragma unroll
