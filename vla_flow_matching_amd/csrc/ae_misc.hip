@@ -34,84 +34,109 @@ __global__ void tpath_sinusoid_kernel(float* e, int n_steps, int width) {
 }
 
 // Y[m][n] = act(sum_k X[m][k] W[k][n] + b[n]) for m < M <= 16: a few rows
-// against a wide weight that is read once.  Two columns per thread, 512 per
-// block; the k loop keeps 16 independent weight loads in flight per thread.
+// against a wide weight that is read once.  A workgroup takes 256 columns:
+// thread (column group of 8, K slice) reads its eight columns with one
+// 16-byte load per row (bf16), eight rows in flight, over one eighth of
+// every 512-row chunk of K; the x values of the chunk sit in LDS.  The eight
+// slices' sums are added in slice order through LDS at the end.
 constexpr int kGemvThreads = 256;
-constexpr int kGemvCols = 2;
-constexpr int kGemvK = 256;
-constexpr int kGemvUnroll = 16;
+constexpr int kGvCols = 8;                      // columns per thread
+constexpr int kGvGroups = 32;                   // column groups per workgroup
+constexpr int kGvSlices = kGemvThreads / kGvGroups;  // K slices per workgroup
+constexpr int kGvChunk = 512;                   // rows of K per LDS chunk
+constexpr int kGvUnroll = 4;                    // rows in flight per thread
 
-template <typename T> __device__ __forceinline__ void load2(const T* p, float* w);
-template <> __device__ __forceinline__ void load2<bf16_t>(const bf16_t* p, float* w) {
-  const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
-  w[0] = __uint_as_float(v << 16);
-  w[1] = __uint_as_float(v & 0xffff0000u);
+__device__ __forceinline__ float to_f32(bf16_t v) { return bf2f(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* w);
+template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* w) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[2 * i] = __uint_as_float(u[i] << 16);
+    w[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
 }
-template <> __device__ __forceinline__ void load2<float>(const float* p, float* w) {
-  const float2 v = *reinterpret_cast<const float2*>(p);
-  w[0] = v.x;
-  w[1] = v.y;
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* w) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
 template <typename T>
 __global__ __launch_bounds__(kGemvThreads) void gemv_rows_kernel(
     const float* X, int ldx, int M, int K, const T* W, int ldw, const T* bias, int N, float* Y,
     int ldy, int act, size_t w_stride, size_t b_stride, size_t y_stride) {
-  __shared__ float sx[16][kGemvK];
+  __shared__ float sx[16][kGvChunk];
+  __shared__ float s_red[kGvSlices][kGvGroups * kGvCols];
   const int mat = blockIdx.y;
   W += mat * w_stride;
   bias += mat * b_stride;
   Y += mat * y_stride;
-  const int n0 = (blockIdx.x * kGemvThreads + threadIdx.x) * kGemvCols;
+  const int tid = threadIdx.x, grp = tid % kGvGroups, slice = tid / kGvGroups;
+  const int n0 = (blockIdx.x * kGvGroups + grp) * kGvCols;
   const bool live = n0 < N;
-  float acc[16][kGemvCols];
+  const int nc = min(n0, N - kGvCols);  // (a clamped, valid column for idle threads)
+  float acc[16][kGvCols];
 #pragma unroll
   for (int m = 0; m < 16; ++m)
 #pragma unroll
-    for (int c = 0; c < kGemvCols; ++c) acc[m][c] = 0.0f;
-  for (int k0 = 0; k0 < K; k0 += kGemvK) {
-    const int kn = min(kGemvK, K - k0);
+    for (int c = 0; c < kGvCols; ++c) acc[m][c] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += kGvChunk) {
+    const int kn = min(kGvChunk, K - k0);
     __syncthreads();
-    for (int i = threadIdx.x; i < M * kGemvK; i += kGemvThreads) {
-      const int m = i / kGemvK, kk = i % kGemvK;
+    for (int i = tid; i < M * kGvChunk; i += kGemvThreads) {
+      const int m = i / kGvChunk, kk = i % kGvChunk;
       sx[m][kk] = kk < kn ? X[static_cast<size_t>(m) * ldx + k0 + kk] : 0.0f;
     }
     __syncthreads();
-    if (!live) continue;
-    for (int kk = 0; kk < kn; kk += kGemvUnroll) {
-      // every load of the group issued at a clamped, valid row and masked
-      // at use: a guarded load would be waited for on the spot, one HBM
-      // round trip per row
-      float w[kGemvUnroll][kGemvCols];
+    // this slice's rows of the chunk: [ks0, ks1)
+    const int per = (kn + kGvSlices - 1) / kGvSlices;
+    const int ks0 = slice * per, ks1 = min(kn, ks0 + per);
+    for (int kk = ks0; kk < ks1; kk += kGvUnroll) {
+      // every load of the group issued at a clamped, valid row and masked at
+      // use: a guarded load would be waited for on the spot
+      float w[kGvUnroll][kGvCols];
 #pragma unroll
-      for (int u = 0; u < kGemvUnroll; ++u)
-        load2<T>(W + static_cast<size_t>(k0 + min(kk + u, kn - 1)) * ldw + n0, w[u]);
+      for (int u = 0; u < kGvUnroll; ++u)
+        load8<T>(W + static_cast<size_t>(k0 + min(kk + u, ks1 - 1)) * ldw + nc, w[u]);
 #pragma unroll
-      for (int u = 0; u < kGemvUnroll; ++u)
-        if (kk + u >= kn) w[u][0] = w[u][1] = 0.0f;
-#pragma unroll
-      for (int u = 0; u < kGemvUnroll; ++u)
+      for (int u = 0; u < kGvUnroll; ++u) {
+        if (kk + u >= ks1) continue;  // (uniform: the slice's last group)
 #pragma unroll
         for (int m = 0; m < 16; ++m)
           if (m < M) {
             const float xv = sx[m][kk + u];
 #pragma unroll
-            for (int c = 0; c < kGemvCols; ++c) acc[m][c] = fmaf(xv, w[u][c], acc[m][c]);
+            for (int c = 0; c < kGvCols; ++c) acc[m][c] = fmaf(xv, w[u][c], acc[m][c]);
           }
+      }
     }
   }
-  if (!live) return;
-  float bv[kGemvCols];
-  load2<T>(bias + n0, bv);
+  // the slices' sums, in slice order, one row at a time (plus the bias and
+  // the activation), each thread finishing one of the workgroup's columns
+  const int n = blockIdx.x * kGvGroups * kGvCols + tid;
+  const float bn = n < N ? to_f32(bias[n]) : 0.0f;
 #pragma unroll
-  for (int m = 0; m < 16; ++m)
-    if (m < M)
+  for (int m = 0; m < 16; ++m) {
+    if (m < M) {  // (uniform)
+    __syncthreads();
 #pragma unroll
-      for (int c = 0; c < kGemvCols; ++c) {
-        float y = acc[m][c] + bv[c];
-        if (act == 1) y = silu(y);
-        Y[static_cast<size_t>(m) * ldy + n0 + c] = y;
-      }
+    for (int c = 0; c < kGvCols; ++c) s_red[slice][grp * kGvCols + c] = acc[m][c];
+    __syncthreads();
+    if (n < N) {
+      float y = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kGvSlices; ++sl) y += s_red[sl][tid];
+      y += bn;
+      if (act == 1) y = silu(y);
+      Y[static_cast<size_t>(m) * ldy + n] = y;
+    }
+    }
+  }
+  (void)live;
 }
 
 // ---------------------------------------------------------------------------
@@ -321,32 +346,88 @@ __global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V
 // The shift term of a norm folded through the next projection:
 // out[k][l][n] = sum_d mod[k][l][which][d] W_l[d][n] (adaRMS(h) W =
 // r (h (1 + scale)) W + shift W), read straight from the packed fragments, so
-// n is in packed column order.  One wave per (16-column block, layer): lane
-// (g, j) holds k-slot g of column j; fp32 sums, one step at a time.
+// n is in packed column order.  One wave per (16-column block, layer), four
+// per workgroup: lane (g, j) holds k-slot g of column j; fp32 sums over d in
+// increasing order per step.  The workgroup first copies the modulation rows
+// of up to kSbSteps steps into LDS (all loads in flight), then streams its
+// weight fragments eight at a time and adds every step's products from LDS,
+// so each fragment is read once per pass instead of once per step.
+constexpr int kSbSteps = 16;     // steps per pass at most
+constexpr int kSbWaves = 4;      // column blocks per workgroup
+constexpr int kSbFill = 16;      // float4 per thread per round of the LDS fill
+constexpr int kSbLdsFloats = 16384;  // 64 KiB of modulation rows per pass at most
+
+__host__ __device__ inline int shift_bias_steps_per_pass(int K, int n_steps) {
+  int sp = kSbLdsFloats / K;
+  if (sp > kSbSteps) sp = kSbSteps;
+  if (sp > n_steps) sp = n_steps;
+  return sp < 1 ? 1 : sp;
+}
+
 template <typename T>
-__global__ void shift_bias_kernel(const uint4* W, size_t layer_stride, int K, int N, const float* mod,
-                                  int n_steps, int L, int D, int nchunk, int which, float* out) {
+__global__ __launch_bounds__(kSbWaves * kWave) void shift_bias_kernel(const uint4* W, size_t layer_stride, int K,
+                                                                      int N, const float* mod, int n_steps, int L,
+                                                                      int D, int nchunk, int which, float* out) {
   constexpr int E = Mma<T>::E, KSTEP = Mma<T>::KSTEP;
-  const int nb = blockIdx.x, l = blockIdx.y, lane = threadIdx.x, g = lane / 16;
+  extern __shared__ float s_sh[];  // [steps of the pass][K]
+  const int l = blockIdx.y, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane / 16;
+  const int nbs = N / 16;
+  const int nb = blockIdx.x * kSbWaves + wave;  // this wave's column block (past the last: idle)
   const int k_frags = K / KSTEP;
-  const uint4* Wf = W + l * layer_stride + static_cast<size_t>(nb) * k_frags * kWave + lane;
-  for (int k = 0; k < n_steps; ++k) {
-    const float* sh = mod + ((static_cast<size_t>(k) * L + l) * nchunk + which) * D;
-    float acc = 0.0f;
-    for (int kf = 0; kf < k_frags; ++kf) {
-      const uint4 w = Wf[static_cast<size_t>(kf) * kWave];
-      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-      const int d0 = kf * KSTEP + E * g;
+  const int sp = shift_bias_steps_per_pass(K, n_steps);
+  const uint4* Wf = W + l * layer_stride + static_cast<size_t>(min(nb, nbs - 1)) * k_frags * kWave + lane;
+  for (int k0 = 0; k0 < n_steps; k0 += sp) {
+    const int ns = min(sp, n_steps - k0);
+    __syncthreads();  // (the previous pass is done with the rows)
+    const int n4 = ns * (K / 4);
+    for (int i0 = 0; i0 < n4; i0 += kSbFill * kSbWaves * kWave) {
+      float4 v[kSbFill];
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const float wv = sizeof(T) == 2 ? __uint_as_float((wd[i / 2] >> (16 * (i % 2))) << 16)
-                                        : __uint_as_float(wd[i % 4]);
-        acc += sh[d0 + i] * wv;
+      for (int u = 0; u < kSbFill; ++u) {
+        const int i = min(i0 + u * kSbWaves * kWave + tid, n4 - 1);
+        const int kk = (4 * i) / K, d = (4 * i) % K;
+        v[u] = *reinterpret_cast<const float4*>(mod + ((static_cast<size_t>(k0 + kk) * L + l) * nchunk + which) * D + d);
+      }
+#pragma unroll
+      for (int u = 0; u < kSbFill; ++u) {
+        const int i = i0 + u * kSbWaves * kWave + tid;
+        if (i < n4) reinterpret_cast<float4*>(s_sh)[i] = v[u];
       }
     }
-    acc += __shfl_xor(acc, 16, kWave);
-    acc += __shfl_xor(acc, 32, kWave);
-    if (lane < 16) out[(static_cast<size_t>(k) * L + l) * N + 16 * nb + lane] = acc;
+    __syncthreads();
+    float acc[kSbSteps];
+#pragma unroll
+    for (int kk = 0; kk < kSbSteps; ++kk) acc[kk] = 0.0f;
+    for (int kf0 = 0; kf0 < k_frags; kf0 += 8) {
+      uint4 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = Wf[static_cast<size_t>(min(kf0 + u, k_frags - 1)) * kWave];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (kf0 + u >= k_frags) break;
+        const uint32_t wd[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+        float wv[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+          wv[i] = sizeof(T) == 2 ? __uint_as_float((wd[i / 2] >> (16 * (i % 2))) << 16) : __uint_as_float(wd[i % 4]);
+        const int d0 = (kf0 + u) * KSTEP + E * g;
+#pragma unroll
+        for (int kk = 0; kk < kSbSteps; ++kk) {
+          if (kk >= ns) break;
+          const float* sh = s_sh + kk * K + d0;
+#pragma unroll
+          for (int i = 0; i < E; ++i) acc[kk] += sh[i] * wv[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kSbSteps; ++kk) {
+      if (kk >= ns) break;
+      float a = acc[kk];
+      a += __shfl_xor(a, 16, kWave);
+      a += __shfl_xor(a, 32, kWave);
+      if (lane < 16 && nb < nbs) out[(static_cast<size_t>(k0 + kk) * L + l) * N + 16 * nb + lane] = a;
+    }
   }
 }
 
@@ -356,12 +437,13 @@ hipError_t launch_shift_bias(Dt dt, const uint4* W, size_t layer_stride, int K, 
                              int n_steps, int L, int D, int nchunk, int which, float* out, hipStream_t s) {
   if (N % 16 || K % 32 || K > D || n_steps < 1 || L < 1 || which < 0 || which >= nchunk)
     return hipErrorInvalidValue;
-  dim3 grid(N / 16, L), block(kWave);
+  dim3 grid((N / 16 + kSbWaves - 1) / kSbWaves, L), block(kSbWaves * kWave);
+  const size_t lds = static_cast<size_t>(shift_bias_steps_per_pass(K, n_steps)) * K * sizeof(float);
   if (dt == DT_BF16)
-    hipLaunchKernelGGL(shift_bias_kernel<bf16_t>, grid, block, 0, s, W, layer_stride, K, N, mod, n_steps, L,
+    hipLaunchKernelGGL(shift_bias_kernel<bf16_t>, grid, block, lds, s, W, layer_stride, K, N, mod, n_steps, L,
                        D, nchunk, which, out);
   else
-    hipLaunchKernelGGL(shift_bias_kernel<float>, grid, block, 0, s, W, layer_stride, K, N, mod, n_steps, L, D,
+    hipLaunchKernelGGL(shift_bias_kernel<float>, grid, block, lds, s, W, layer_stride, K, N, mod, n_steps, L, D,
                        nchunk, which, out);
   return hipGetLastError();
 }
@@ -389,8 +471,8 @@ hipError_t launch_tpath_sinusoid(float* e, int n_steps, int width, hipStream_t s
 hipError_t launch_gemv_rows(Dt dt, const float* X, int ldx, int M, int K, const void* W, int ldw,
                             const void* b, int N, float* Y, int ldy, int act, int n_mat,
                             size_t w_stride, size_t b_stride, size_t y_stride, hipStream_t s) {
-  if (M < 1 || M > 16 || N % kGemvCols || ldw % kGemvCols) return hipErrorInvalidValue;
-  const int cols_per_block = kGemvThreads * kGemvCols;
+  if (M < 1 || M > 16 || N < kGvCols || N % kGvCols || ldw % kGvCols) return hipErrorInvalidValue;
+  const int cols_per_block = kGvGroups * kGvCols;
   dim3 grid((N + cols_per_block - 1) / cols_per_block, n_mat), block(kGemvThreads);
   if (dt == DT_BF16)
     hipLaunchKernelGGL(gemv_rows_kernel<bf16_t>, grid, block, 0, s, X, ldx, M, K,
