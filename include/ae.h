@@ -187,8 +187,8 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
  * action-graph replay); LoongForge blog section 1 (masked camera slots and
  * padding are invisible; pad tokens do not advance positions).
  * Arguments: K and V are device [L][batch][prefix_len][Hkv][dh] in
- * act_dtype, K already rotated at the prefix's own positions (the VLM's KV
- * cache); valid_mask is device [batch][prefix_len] uint8 (0 = invisible:
+ * act_dtype, 16-byte aligned, K already rotated at the prefix's own
+ * positions (the VLM's KV cache); valid_mask is device [batch][prefix_len] uint8 (0 = invisible:
  * padding or an empty camera slot, any pattern).  The library copies the
  * visible rows, in order, into its static buffers and computes, on the
  * device, each request's visible count n_b (the action tokens sit at
@@ -197,9 +197,10 @@ ae_status ae_load_weights(ae_handle* h, const ae_tensor_view* w, int n, void* st
  * prefix bucket is the smallest ae_set_prefix_buckets length >= prefix_len
  * (else max_prefix_len); rows past prefix_len count as masked padding.
  * Errors: SHAPE_MISMATCH for batch outside [1, max_batch] or prefix_len
- * outside [0, max_prefix_len], INVALID_ARGUMENT for a null pointer with
- * prefix_len > 0 (checked before any state change).  Stream-ordered; the
- * caller may reuse its buffers once the stream passes the call. */
+ * outside [0, max_prefix_len], INVALID_ARGUMENT for a null or misaligned K or
+ * V, or a null mask, with prefix_len > 0 (checked before any state change).
+ * Stream-ordered; the caller may reuse its buffers once the stream passes
+ * the call. */
 ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* K,
                            const void* V, const uint8_t* valid_mask, void* stream);
 

@@ -125,17 +125,21 @@ hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, cons
                              const float* b_out, float dt, hipStream_t s);
 
 // (extra: visible rows that follow the P mask rows, e.g. the robot state's:
-// they count into n_valid)
+// they count into n_valid; src_of, when set: its inverse, src_of[b P + key]
+// = the row holding visible key `key`)
 hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_idx, int* n_valid,
                               int T, int dh, float theta, float* rope_cos, float* rope_sin,
-                              hipStream_t s, int extra = 0);
+                              hipStream_t s, int extra = 0, int* src_of = nullptr);
 // cos / sin of RoPE at positions 0 .. n_pos - 1: [n_pos][dh / 2] fp32 (double math)
 hipError_t launch_pos_table(int n_pos, int dh, float theta, float* cos_t, float* sin_t, hipStream_t s);
 // The robot state's context row: out[b] = bf16(state[b] . W + bias) ([S] x [S][D]
 // bf16 + [D] bf16), and its key, key_out[b] = n_valid[b] - 1 (the last visible row).
 hipError_t launch_state_prep(const float* state, int batch, int S, const uint16_t* w, const uint16_t* bias,
                              int D, const int* n_valid, uint16_t* out, int* key_out, hipStream_t s);
-hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx,
+// K / V [L][batch][P][Hkv][dh] visible rows -> keys 0 .. n_valid[b] - 1 of
+// the key-block caches (src_of from launch_prefix_scan); K null: only the
+// finite fill past n_valid + n_act
+hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* src_of,
                               const int* n_valid, int n_act, int L, int batch, int P, int Hkv, int dh,
                               int Bmax, int S_max, void* kcache, void* vtcache, hipStream_t s);
 

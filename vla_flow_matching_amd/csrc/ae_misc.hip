@@ -259,7 +259,8 @@ __global__ __launch_bounds__(256) void action_out_kernel(float* x, int A, const 
 
 __global__ __launch_bounds__(256) void prefix_scan_kernel(const uint8_t* mask, int P, int* comp_idx,
                                                           int* n_valid, int T, int dh, float theta,
-                                                          float* rope_cos, float* rope_sin, int extra) {
+                                                          float* rope_cos, float* rope_sin, int extra,
+                                                          int* src_of) {
   __shared__ int s_cnt[256];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -280,6 +281,7 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(const uint8_t* mask, i
   for (int j = j0; j < j1; ++j) {
     const bool vis = mask[static_cast<size_t>(b) * P + j] != 0;
     comp_idx[static_cast<size_t>(b) * P + j] = vis ? run : -1;
+    if (vis && src_of) src_of[static_cast<size_t>(b) * P + run] = j;
     run += vis;
   }
   const int nv = s_cnt[255] + extra;
@@ -294,48 +296,71 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(const uint8_t* mask, i
   }
 }
 
-// copy: visible row j of K and V -> cache key comp_idx[j] (key-block layout,
-// KvLayout).  grid (L*B*Hkv, max(1, ceil(P/32))), 256 threads.  The first
-// row block of each (layer, request, head) also zeroes the keys from the
-// request's n_valid + n_act to the end of that 64-key block: attention
-// multiplies whole key blocks and relies on the cache being finite there.
+// copy: the visible rows of K and V -> cache keys 0 .. n_valid - 1 in order
+// (key-block layout, KvLayout).  grid (L*B*Hkv, max(1, ceil(P/32))), 256
+// threads; workgroup y takes keys 32 y .. 32 y + 31, each found through
+// src_of (its source row).  K goes row by row, 16 bytes per thread: a key's
+// E consecutive dims are contiguous in the cache.  V is transposed in the
+// cache (for a dim, E consecutive keys are contiguous), so its rows pass
+// through LDS and leave as E keys of one dim per 16-byte store; the keys of
+// such a group past n_valid are action-row slots, written with zeros here
+// and overwritten by every step's QKV epilogue before attention reads them.
+// The first workgroup of each (layer, request, head) also zeroes the keys
+// from n_valid + n_act to the end of that 64-key block: attention multiplies
+// whole key blocks and relies on the cache being finite there.
 constexpr int kCopyRows = 32;
 
 template <typename T>
-__global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V, const int* comp_idx,
+__global__ __launch_bounds__(256) void prefix_copy_kernel(const T* K, const T* V, const int* src_of,
                                                           const int* n_valid, int n_act, int batch, int P,
                                                           int Hkv, int dh, int Bmax, int S_max,
                                                           T* kcache, T* vtcache) {
   using LY = KvLayout<T>;
-  __shared__ int sci[kCopyRows];
+  constexpr int E = LY::E;  // elements per 16 bytes
+  __shared__ uint4 s_v[kCopyRows * 256 * sizeof(T) / 16];  // V rows of the workgroup's keys (dh <= 256)
   const int lbg = blockIdx.x;
   const int g = lbg % Hkv;
   const int b = (lbg / Hkv) % batch;
   const int l = lbg / (Hkv * batch);
-  const int j0 = blockIdx.y * kCopyRows;
-  const int nrows = min(kCopyRows, P - j0);
-  if (threadIdx.x < kCopyRows)
-    sci[threadIdx.x] = threadIdx.x < nrows ? comp_idx[static_cast<size_t>(b) * P + j0 + threadIdx.x] : -1;
-  __syncthreads();
-  const size_t src_row0 = ((static_cast<size_t>(l) * batch + b) * P + j0) * Hkv + g;
+  const int tid = threadIdx.x;
+  const int nv = n_valid[b];
+  const int key0 = blockIdx.y * kCopyRows;
   const size_t cache_bg = (static_cast<size_t>(l) * Bmax + b) * Hkv + g;
   T* kdst = kcache + cache_bg * S_max * dh;
   T* vdst = vtcache + cache_bg * S_max * dh;
-  for (int i = threadIdx.x; i < nrows * dh; i += 256) {
-    const int r = i / dh, d = i % dh;
-    const int ci = sci[r];
-    if (ci < 0) continue;  // invisible row: never read
-    const size_t src = (src_row0 + static_cast<size_t>(r) * Hkv) * dh + d;
-    kdst[LY::k_off(ci, d, dh)] = K[src];
-    vdst[LY::v_off(ci, d, dh)] = V[src];
+  if (K != nullptr && key0 < nv) {
+    const int dq = dh / E;  // 16-byte groups per row
+    const size_t row0 = (static_cast<size_t>(l) * batch + b) * P;
+    for (int i = tid; i < kCopyRows * dq; i += 256) {
+      const int kr = i / dq, q = i % dq, key = key0 + kr;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (key < nv) {
+        const int r = src_of[static_cast<size_t>(b) * P + key];
+        const size_t src = ((row0 + r) * Hkv + g) * dh + q * E;
+        kv = *reinterpret_cast<const uint4*>(K + src);
+        vv = *reinterpret_cast<const uint4*>(V + src);
+        *reinterpret_cast<uint4*>(kdst + LY::k_off(key, q * E, dh)) = kv;
+      }
+      s_v[kr * dq + q] = vv;
+    }
+    __syncthreads();
+    const T* sv = reinterpret_cast<const T*>(s_v);
+    for (int i = tid; i < dh * (kCopyRows / E); i += 256) {
+      const int d = i % dh, kg = i / dh, k8 = key0 + kg * E;
+      if (k8 >= nv) continue;
+      T vals[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) vals[e] = sv[(kg * E + e) * dh + d];
+      *reinterpret_cast<uint4*>(vdst + LY::v_off(k8, d, dh)) = *reinterpret_cast<const uint4*>(vals);
+    }
   }
   if (blockIdx.y == 0) {
     // The attention kernels read whole key blocks (at most 64 keys) up to
     // the block holding the request's last key, so only the rest of that
     // block must hold finite values; keys past it are never read.
-    const int z0 = min(n_valid[b] + n_act, S_max);
+    const int z0 = min(nv + n_act, S_max);
     const int z1 = min((z0 + 63) / 64 * 64, S_max);
-    for (int i = threadIdx.x; i < (z1 - z0) * dh; i += 256) {
+    for (int i = tid; i < (z1 - z0) * dh; i += 256) {
       const int key = z0 + i / dh, d = i % dh;
       kdst[LY::k_off(key, d, dh)] = T(0);
       vdst[LY::v_off(key, d, dh)] = T(0);
@@ -520,9 +545,9 @@ hipError_t launch_action_out(float* x, int M, int A, const float* h, int D, cons
 
 hipError_t launch_prefix_scan(const uint8_t* mask, int batch, int P, int* comp_idx, int* n_valid,
                               int T, int dh, float theta, float* rope_cos, float* rope_sin,
-                              hipStream_t s, int extra) {
+                              hipStream_t s, int extra, int* src_of) {
   hipLaunchKernelGGL(prefix_scan_kernel, dim3(batch), dim3(256), 0, s, mask, P, comp_idx, n_valid,
-                     T, dh, theta, rope_cos, rope_sin, extra);
+                     T, dh, theta, rope_cos, rope_sin, extra, src_of);
   return hipGetLastError();
 }
 
@@ -587,19 +612,19 @@ hipError_t launch_state_prep(const float* state, int batch, int S, const uint16_
   return hipGetLastError();
 }
 
-hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* comp_idx,
+hipError_t launch_prefix_copy(Dt dt, const void* K, const void* V, const int* src_of,
                               const int* n_valid, int n_act, int L, int batch, int P, int Hkv, int dh,
                               int Bmax, int S_max, void* kcache, void* vtcache, hipStream_t s) {
   if (dh > 256) return hipErrorInvalidValue;
   dim3 grid(L * batch * Hkv, P > 0 ? (P + kCopyRows - 1) / kCopyRows : 1), block(256);
   if (dt == DT_BF16)
     hipLaunchKernelGGL(prefix_copy_kernel<bf16_t>, grid, block, 0, s,
-                       static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V), comp_idx, n_valid,
+                       static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V), src_of, n_valid,
                        n_act, batch, P, Hkv, dh, Bmax, S_max, static_cast<bf16_t*>(kcache),
                        static_cast<bf16_t*>(vtcache));
   else
     hipLaunchKernelGGL(prefix_copy_kernel<float>, grid, block, 0, s, static_cast<const float*>(K),
-                       static_cast<const float*>(V), comp_idx, n_valid, n_act, batch, P, Hkv, dh, Bmax,
+                       static_cast<const float*>(V), src_of, n_valid, n_act, batch, P, Hkv, dh, Bmax,
                        S_max, static_cast<float*>(kcache), static_cast<float*>(vtcache));
   return hipGetLastError();
 }

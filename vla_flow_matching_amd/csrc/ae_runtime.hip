@@ -116,6 +116,7 @@ struct ae_handle {
   int S_self = 0;
   int* zeros = nullptr;
   int *comp_idx = nullptr, *n_valid = nullptr;
+  int* src_of = nullptr;  // inverse of comp_idx: the row of each visible key
   float *rope_cos = nullptr, *rope_sin = nullptr;
 
   // activations
@@ -1183,6 +1184,7 @@ ae_status ae_create(const ae_config* cfg, ae_handle** out) {
   AE_ALLOC(h->kcache, kvbytes);
   AE_ALLOC(h->vtcache, kvbytes);
   AE_ALLOC(h->comp_idx, static_cast<size_t>(h->Bmax) * (h->Pmax > 0 ? h->Pmax : 1) * 4);
+  AE_ALLOC(h->src_of, static_cast<size_t>(h->Bmax) * (h->Pmax > 0 ? h->Pmax : 1) * 4);
   AE_ALLOC(h->n_valid, static_cast<size_t>(h->Bmax) * 4);
   AE_ALLOC(h->rope_cos, static_cast<size_t>(h->Bmax) * h->T * (h->dh / 2) * 4);
   AE_ALLOC(h->rope_sin, static_cast<size_t>(h->Bmax) * h->T * (h->dh / 2) * 4);
@@ -1443,14 +1445,16 @@ ae_status ae_set_prefix_kv(ae_handle* h, int batch, int prefix_len, const void* 
                 "prefix_len " + std::to_string(prefix_len) + " outside [0, " + std::to_string(h->Pmax) + "]");
   if (prefix_len > 0 && (!K || !V || !valid_mask))
     return fail(h, AE_ERR_INVALID_ARGUMENT, "null K, V or valid_mask");
+  if (prefix_len > 0 && (reinterpret_cast<uintptr_t>(K) % 16 || reinterpret_cast<uintptr_t>(V) % 16))
+    return fail(h, AE_ERR_INVALID_ARGUMENT, "K and V must be 16-byte aligned (the copy moves 16-byte pieces)");
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the smallest bucket holding the prefix: its rows past prefix_len count
   // as padding (mask 0), and the calls plan their key splits for it
   const int span = pick_bucket(h->buckets, prefix_len, h->Pmax);
   h->prefix_batch = -1;  // (a failed launch leaves no usable prefix)
   AE_HIP(h, launch_prefix_scan(valid_mask, batch, prefix_len, h->comp_idx, h->n_valid, h->T, h->dh,
-                               h->cfg.rope_theta, h->rope_cos, h->rope_sin, st));
-  AE_HIP(h, launch_prefix_copy(h->dt, K, V, h->comp_idx, h->n_valid, h->T, h->L, batch, prefix_len,
+                               h->cfg.rope_theta, h->rope_cos, h->rope_sin, st, 0, h->src_of));
+  AE_HIP(h, launch_prefix_copy(h->dt, K, V, h->src_of, h->n_valid, h->T, h->L, batch, prefix_len,
                                h->Hkv, h->dh, h->Bmax, h->S_max, h->kcache, h->vtcache, st));
   h->prefix_batch = batch;
   h->span = span;
@@ -1516,7 +1520,7 @@ ae_status ae_prepare_prefix(ae_handle* h, int batch, int prefix_len, const void*
     if (r != AE_OK) return r;
   }
   // finite values in the rest of each request's last key block (no rows copied)
-  AE_HIP(h, launch_prefix_copy(h->dt, nullptr, nullptr, h->comp_idx, h->n_valid, h->T, h->L, batch, 0, h->Hkv,
+  AE_HIP(h, launch_prefix_copy(h->dt, nullptr, nullptr, h->src_of, h->n_valid, h->T, h->L, batch, 0, h->Hkv,
                                h->dh, h->Bmax, h->S_max, h->kcache, h->vtcache, st));
   h->prefix_batch = batch;
   h->span = span;
