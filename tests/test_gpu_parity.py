@@ -644,6 +644,14 @@ def test_error_paths_leave_state_unchanged(c2small):
     with pytest.raises(binding.AeError) as e:
         g.ex.set_prefix_kv(big, big, torch.ones((1, 1100), dtype=torch.uint8, device="cuda"))
     assert e.value.status == binding.AE_ERR_SHAPE_MISMATCH
+    # K / V of the right shape and dtype but 2 bytes off a 16-byte boundary
+    n = int(np.prod(K.shape))
+    flat = torch.zeros(n + 8, dtype=torch.bfloat16, device="cuda")
+    Kmis = flat[1:n + 1].view(K.shape)
+    assert Kmis.is_contiguous() and Kmis.data_ptr() % 16 != 0
+    with pytest.raises(binding.AeError) as e:
+        g.ex.set_prefix_kv(Kmis, Kmis, torch.from_numpy(m).cuda())
+    assert e.value.status == binding.AE_ERR_INVALID_ARGUMENT
     out = g.ex.denoise(torch.from_numpy(x0).cuda(), 2)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref)
