@@ -252,3 +252,25 @@ def test_prepare_with_rowwise_fp8_expert():
         err = float(np.abs(out[b:b + 1] - refs[b]).max())
         say(f"[parity] row-wise fp8 with prepared context, request {b}: max|gpu-oracle| = {err:.3e}")
         assert err <= TOL_BF16
+
+
+def test_prepare_state_only_empty_context():
+    """No context rows at all (prefix_len 0) but a robot state: the state row
+    is the only visible key, projected for every layer in one product."""
+    _need_gpu()
+    w = synth.workload("c4", batch=2, n_layers=2, n_steps=2, prefix_len=0)
+    Dc, S = 512, 14
+    say("[case] prepare: empty context, state row only, 2 requests")
+    W = synth.make_weights(w)
+    CW = synth.make_context_weights(w, Dc, S)
+    m = np.zeros((2, 0), np.uint8)
+    H = np.zeros((w.n_layers, 2, 0, Dc), np.float32)
+    state = synth.make_state(w, S)
+    x0 = synth.make_noise(w)
+    with expert(w, W, CW, 64, Dc, S) as ex:
+        out = gpu_prepare_denoise(ex, w, H, m, state, x0, w.n_steps)
+    refs = oracle_every_step(w, W, CW, H, m, state, x0)
+    for b in range(2):
+        err = float(np.abs(out[b:b + 1] - refs[b]).max())
+        say(f"[parity] state row only, request {b}: max|gpu-oracle| = {err:.3e}")
+        assert err <= TOL_BF16
