@@ -493,6 +493,53 @@ __device__ __forceinline__ void tg_epilogue(const TGemmArgs& p, int nt, int m0, 
     bf16_t* kc = static_cast<bf16_t*>(p.kcache) + lofs;
     bf16_t* vt = static_cast<bf16_t*>(p.vtcache) + lofs;
     const bool ctx = p.key_map != nullptr;
+    if (!ctx && 4 * nt >= pq + pk) {
+      // A tile of V columns only (not rotated).  V^T rows are head dims, so
+      // lanes (tile column 8 (wave + 4 u) + lane / 8, row 8 q + lane % 8)
+      // make each store instruction cover eight columns' runs of eight
+      // consecutive keys instead of 64 dims of one key 16 bytes apart.
+      const int kr = lane % 8, cl = lane / 8;
+      float vb[4], vs[4];
+      size_t vhead[4];
+      int vd[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = 8 * (wave + 4 * u) + cl;
+        const int Pv = 4 * nt + c / 32 - pq - pk;
+        vhead[u] = static_cast<size_t>(Pv / pph) * p.S_max * p.dh;
+        vd[u] = ((c & 16) ? half : 0) + 16 * (Pv % pph) + c % 16;
+        vb[u] = post_norm ? p.bias[nt * kBN + c] : 0.0f;
+        vs[u] = OP == OP_FP8 ? (p.swc ? p.swc[nt * kBN + c] : p.sw[2]) : 1.0f;
+      }
+      constexpr int kQ = 8;  // row groups of 8 (tiles hold at most 64 rows)
+      int vkey[kQ], vreq[kQ];
+      float vrs[kQ], vsx[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int rc = min(8 * q + kr, rows - 1);
+        const int m = m0 + rc;
+        vreq[q] = m / p.T;
+        vkey[q] = p.n_valid[vreq[q]] + m % p.T;
+        vrs[q] = post_norm ? s_r[rc] : 1.0f;
+        vsx[q] = OP == OP_FP8 ? p.sx_row[m] : 1.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        if (8 * q >= rows) break;
+        const int row = 8 * q + kr, rc = min(row, rows - 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = 8 * (wave + 4 * u) + cl;
+          float y = s_y[rc][c];
+          if (post_norm) y = y * vrs[q] + vb[u];
+          if (OP == OP_FP8) y *= vsx[q] * vs[u];
+          if (row < rows)
+            vt[(static_cast<size_t>(vreq[q]) * p.Hkv) * p.S_max * p.dh + vhead[u] +
+               KvLayout<bf16_t>::v_off(vkey[q], vd[u], p.dh)] = f2bf(y);
+        }
+      }
+      return;
+    }
     for (int rb = wave; rb < rows; rb += 4 * kEB) {
       float csv[kEB], snv[kEB], sxv[kEB];
       int nvv[kEB];  // the row's cache key
