@@ -77,6 +77,19 @@ typedef enum { AE_F32 = 0, AE_BF16 = 1, AE_FP8_E4M3 = 2 } ae_dtype;
  *   prefix makes attn2 add nothing.  bf16 projections only. */
 typedef enum { AE_BLOCK_JOINT = 0, AE_BLOCK_DIT = 1 } ae_block;
 
+/* Which kernels run a denoise call (ae_config.exec_path).  The whole-call
+ * kernel (one persistent launch for the whole call) takes a call that fits
+ * it: batch * action_horizon <= 64, action_dim <= 32, bf16 or f32 projections,
+ * AE_BLOCK_JOINT, and a device with cooperative launch; any other call runs
+ * the per-phase kernels (a few launches per layer, replayed from a graph).
+ * Both compute the same function (not bitwise the same values).
+ * AE_PATH_AUTO takes the whole-call kernel for a call that fits it only when
+ * the decoder layers' projection weights exceed the last-level cache (256 MiB
+ * on MI355X): the whole-call kernel's time per layer is set by its
+ * synchronisation, while the per-phase kernels gain from weights that stay
+ * in that cache from one step to the next. */
+typedef enum { AE_PATH_AUTO = 0, AE_PATH_WHOLE_CALL = 1, AE_PATH_PER_PHASE = 2 } ae_path;
+
 /* Expert shape and numerics.  Fixed for the life of a handle. */
 typedef struct {
   int n_layers;         /* decoder layers L */
@@ -112,6 +125,8 @@ typedef struct {
                            GPU) */
   int fp8_oproj;        /* 1: the attention output projection in fp8 as well (needs fp8_rowwise
                            and n_q_heads * head_dim a multiple of 128); 0: bf16 */
+  int exec_path;        /* an ae_path: AE_PATH_AUTO (0), AE_PATH_WHOLE_CALL (1) or
+                           AE_PATH_PER_PHASE (2) */
 } ae_config;
 
 /* One named logical weight, caller-owned device memory, dtype = act_dtype.

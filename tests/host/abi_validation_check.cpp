@@ -61,6 +61,7 @@ int main() {
       {"block_type 2", [](ae_config& c) { c.block_type = 2; }},
       {"fp8_rowwise 2", [](ae_config& c) { c.fp8_rowwise = 2; }},
       {"fp8_rowwise with bf16 projections", [](ae_config& c) { c.fp8_rowwise = 1; }},
+      {"exec_path 3", [](ae_config& c) { c.exec_path = 3; }},
   };
   for (const Bad& b : invalid) {
     ae_config c = base();

@@ -63,6 +63,7 @@ def _create(lib, **changes):
     ("n_layers", 0), ("width", 100), ("width", 0), ("n_kv_heads", 3), ("mlp_dim", 48),
     ("action_dim", 65), ("max_batch", 0), ("max_steps", 0), ("max_steps", 65),
     ("max_prefix_len", -1), ("act_dtype", 7), ("rope_theta", 0.0), ("use_graphs", 2),
+    ("exec_path", 3), ("exec_path", -1),
 ])
 def test_invalid_config_rejected_before_hip(lib, field, value):
     st, h = _create(lib, **{field: value})

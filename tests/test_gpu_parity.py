@@ -41,12 +41,21 @@ def _dt(w):
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
 
+# the paths a config can ask for (ae_path): the tests pick one where it
+# matters; AE_PATH_AUTO is the library's default
+AUTO, WHOLE_CALL, PER_PHASE = 0, 1, 2
+
+
 class Gpu:
-    """A library handle with one workload's weights loaded."""
+    """A library handle with one workload's weights loaded; unless a test
+    says otherwise, calls that fit the whole-call kernel take it (the
+    per-phase kernels take the rest)."""
 
     def __init__(self, w, W, **cfg_kw):
         from vla_flow_matching_amd import binding
         self.w = w
+        cfg_kw.setdefault("exec_path", WHOLE_CALL)
+        self.exec_path = cfg_kw["exec_path"]
         self.ex = binding.ActionExpert(binding.make_config(w, **cfg_kw))
         self.ex.load_weights(binding.weights_to_device(W, w.dtype))
 
@@ -79,28 +88,32 @@ def check(gpu, ref, tol, label):
 # fixtures: one weight set per workload, shared by the tests
 # --------------------------------------------------------------------------
 
-@pytest.fixture(scope="module")
-def c1():
+@pytest.fixture(scope="module", params=[WHOLE_CALL, PER_PHASE], ids=["whole-call", "per-phase"])
+def c1(request):
     _need_gpu()
     w = synth.workload("c1")
     W = synth.make_weights(w)
-    return w, W, Gpu(w, W)
+    return w, W, Gpu(w, W, exec_path=request.param)
 
 
-@pytest.fixture(scope="module")
-def c2small():
+@pytest.fixture(scope="module", params=[WHOLE_CALL, PER_PHASE], ids=["whole-call", "per-phase"])
+def c2small(request):
+    """The Pi0.5 shape at 2 layers, 2 steps, on each path."""
     _need_gpu()
     w = synth.workload("c2", n_layers=2, n_steps=2)
     W = synth.make_weights(w)
-    return w, W, Gpu(w, W, max_prefix_len=1018, max_steps=4)
+    return w, W, Gpu(w, W, max_prefix_len=1018, max_steps=4, exec_path=request.param)
 
 
 @pytest.fixture(scope="module")
 def c2full():
+    """The Pi0.5 shape, the library's own choice of path (a step streams
+    623 MB of layer weights, past the last-level cache: the whole-call
+    kernel)."""
     _need_gpu()
     w = synth.workload("c2")
     W = synth.make_weights(w)
-    return w, W, Gpu(w, W, max_prefix_len=1018)
+    return w, W, Gpu(w, W, max_prefix_len=1018, exec_path=AUTO)
 
 
 # --------------------------------------------------------------------------
@@ -133,13 +146,13 @@ def test_c1_fp32_batched_per_phase():
 
 def test_c1_euler_closed_form(c1):
     """Constant-velocity head: x_N = x_0 + N dt v = x_0 - v."""
-    w, W, _ = c1
+    w, W, g1 = c1
     say("[case] c1 constant-velocity head")
     W2 = dict(W)
     vel = np.random.default_rng(3).standard_normal(w.action_dim).astype(np.float32)
     W2["action_out.w"] = np.zeros_like(W["action_out.w"])
     W2["action_out.b"] = vel
-    g = Gpu(w, W2)
+    g = Gpu(w, W2, exec_path=g1.exec_path)
     K, V, m = synth.make_prefix(w)
     x0 = synth.make_noise(w)
     out = g.run(K, V, m, x0)
@@ -212,7 +225,9 @@ def test_c2_full_parity(c2full):
     say("[case] c2 full: 18 layers, 10 steps, bf16")
     K, V, m = synth.make_prefix(w)
     x0 = synth.make_noise(w)
+    before = g.ex.stats()["persistent_calls"]
     check(g.run(K, V, m, x0), oracle(w, W, K, V, m, x0), TOL_BF16, "c2 full")
+    assert g.ex.stats()["persistent_calls"] == before + 1  # AE_PATH_AUTO's choice at this shape
 
 
 @pytest.mark.parametrize("slot", [2, 1])
@@ -239,14 +254,20 @@ def test_c3_masked_slot_equals_c2_pruned(c2full, slot):
 def test_c4_full_parity():
     _need_gpu()
     w = synth.workload("c4")
-    say("[case] c4 full: 12 layers, 12/4 heads, head_dim 64, prefix 2048")
+    say("[case] c4 full: 12 layers, 12/4 heads, head_dim 64, prefix 2048, both paths")
     W = synth.make_weights(w)
-    g = Gpu(w, W)
+    # the library's choice (208 MB of layer weights, within the last-level
+    # cache: the per-phase kernels) and the whole-call kernel
+    auto, whole = Gpu(w, W, exec_path=AUTO), Gpu(w, W, exec_path=WHOLE_CALL)
     for n in (1622, 1628, 1635):  # the pages' 1621-1634 visible tokens, plus the state row
         m = synth.valid_masks(w, n_valid=(n,))
         K, V, _ = synth.make_prefix(w, mask=m)
         x0 = synth.make_noise(w)
-        check(g.run(K, V, m, x0), oracle(w, W, K, V, m, x0), TOL_BF16, f"c4 n={n}")
+        ref = oracle(w, W, K, V, m, x0)
+        check(auto.run(K, V, m, x0), ref, TOL_BF16, f"c4 n={n} (per-phase kernels)")
+        check(whole.run(K, V, m, x0), ref, TOL_BF16, f"c4 n={n} (whole-call kernel)")
+    assert auto.ex.stats()["persistent_calls"] == 0
+    assert whole.ex.stats()["persistent_calls"] == 3
 
 
 @pytest.mark.parametrize("name,batch", [("c4", 4), ("c1", 8), ("c4", 3)])
@@ -291,24 +312,26 @@ def test_graph_cache_lru_and_capacity(c2small):
     least recently used one and counts hits, misses and evictions; capacity 0
     captures nothing; a full cache without eviction runs new signatures
     directly.  Every result is bitwise that of direct launches."""
-    w, W, _ = c2small
+    w, W, g = c2small
+    path = g.exec_path  # (every handle here on the fixture's path: results compared bitwise)
     say("[case] graph cache: LRU eviction, zero capacity, no-evict fallback")
     K, V, m = synth.make_prefix(w)
     x0 = synth.make_noise(w)
-    direct = Gpu(w, W, max_prefix_len=1018, max_steps=4, use_graphs=False)
+    direct = Gpu(w, W, max_prefix_len=1018, max_steps=4, use_graphs=False, exec_path=path)
     want = {n: direct.run(K, V, m, x0, n) for n in (1, 2, 3)}
-    lru = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=2)
+    lru = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=2, exec_path=path)
     for n in (1, 2, 1, 3, 1, 2):  # misses 1, 2; hit 1; miss 3 evicts 2; hit 1; miss 2 evicts 3
         assert np.array_equal(lru.run(K, V, m, x0, n), want[n]), n
     st = lru.ex.stats()
     say(f"[stats] {st}")
     assert (st["graph_hits"], st["graph_misses"], st["graph_evictions"]) == (2, 4, 2)
     assert st["graph_captures"] == 4 and st["graphs_cached"] == 2 and st["eager_runs"] == 0
-    off = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=0)
+    off = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=0, exec_path=path)
     assert np.array_equal(off.run(K, V, m, x0, 2), want[2])
     st = off.ex.stats()
     assert st["graph_captures"] == 0 and st["eager_runs"] == 1
-    full = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=1, graph_cache_evict=False)
+    full = Gpu(w, W, max_prefix_len=1018, max_steps=4, graph_cache_size=1, graph_cache_evict=False,
+               exec_path=path)
     for n in (2, 3, 2):
         assert np.array_equal(full.run(K, V, m, x0, n), want[n]), n
     st = full.ex.stats()
@@ -322,9 +345,9 @@ def test_prefix_buckets(c2small):
     the rounding order only); bucket lists that are not strictly increasing
     or exceed the capacity are rejected and leave the handle unchanged."""
     from vla_flow_matching_amd import binding
-    w, W, _ = c2small
+    w, W, g0 = c2small
     say("[case] prefix buckets")
-    g = Gpu(w, W, max_prefix_len=1018, max_steps=4)
+    g = Gpu(w, W, max_prefix_len=1018, max_steps=4, exec_path=g0.exec_path)
     g.ex.set_prefix_buckets([128, 576, 712])
     for bad in ([576, 576], [600, 128], [0, 64], [64, 2000]):
         with pytest.raises(binding.AeError) as e:
@@ -602,7 +625,7 @@ def test_graph_equals_direct_launch(c2small):
     say("[case] graph replay vs direct launches")
     K, V, m = synth.make_prefix(w)
     x0 = synth.make_noise(w)
-    direct = Gpu(w, W, max_prefix_len=1018, max_steps=4, use_graphs=False)
+    direct = Gpu(w, W, max_prefix_len=1018, max_steps=4, use_graphs=False, exec_path=g.exec_path)
     assert np.array_equal(g.run(K, V, m, x0), direct.run(K, V, m, x0))
     assert direct.ex.stats()["graph_captures"] == 0
 

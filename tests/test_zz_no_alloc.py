@@ -65,7 +65,9 @@ def test_static_equals_denoise(name, first, second, fields):
     wmax = synth.workload(name, batch=first, **fields)
     say(f"[case] ae_denoise_static vs ae_denoise: {name} batch {first} then {second}")
     W = synth.make_weights(wmax)
-    with binding.ActionExpert(binding.make_config(wmax)) as ex:
+    # (the cases named for the whole-call kernel ask for it; the rest run
+    # the per-phase kernels whatever the path)
+    with binding.ActionExpert(binding.make_config(wmax, exec_path=binding.AE_PATH_WHOLE_CALL)) as ex:
         ex.load_weights(binding.weights_to_device(W, wmax.dtype))
         for b in (first, second):
             w = dataclasses.replace(wmax, batch=b)

@@ -21,6 +21,7 @@ AE_OK, AE_ERR_INVALID_ARGUMENT, AE_ERR_SHAPE_MISMATCH, AE_ERR_NOT_READY = 0, 1, 
 AE_ERR_OUT_OF_MEMORY, AE_ERR_UNSUPPORTED, AE_ERR_HIP = 4, 5, 6
 AE_F32, AE_BF16, AE_FP8_E4M3 = 0, 1, 2
 AE_BLOCK_JOINT, AE_BLOCK_DIT = 0, 1
+AE_PATH_AUTO, AE_PATH_WHOLE_CALL, AE_PATH_PER_PHASE = 0, 1, 2
 
 # every function include/ae.h declares
 EXPORTS = ("ae_create", "ae_load_weights", "ae_set_prefix_kv", "ae_prepare_prefix", "ae_set_prefix_buckets",
@@ -37,7 +38,7 @@ class Config(ctypes.Structure):
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("use_graphs", ctypes.c_int),
         ("graph_cache_size", ctypes.c_int), ("graph_cache_evict", ctypes.c_int),
         ("context_width", ctypes.c_int), ("state_dim", ctypes.c_int), ("block_type", ctypes.c_int),
-        ("fp8_rowwise", ctypes.c_int), ("fp8_oproj", ctypes.c_int),
+        ("fp8_rowwise", ctypes.c_int), ("fp8_oproj", ctypes.c_int), ("exec_path", ctypes.c_int),
     ]
 
 
@@ -98,8 +99,9 @@ def load() -> ctypes.CDLL:
 def make_config(w, max_batch: Optional[int] = None, max_prefix_len: Optional[int] = None,
                 max_steps: Optional[int] = None, use_graphs: bool = True,
                 graph_cache_size: int = 16, graph_cache_evict: bool = True,
-                context_width: int = 0, state_dim: int = 0) -> Config:
-    """Config from any object with the workload fields (e.g. synth.Workload)."""
+                context_width: int = 0, state_dim: int = 0, exec_path: int = 0) -> Config:
+    """Config from any object with the workload fields (e.g. synth.Workload);
+    exec_path: AE_PATH_AUTO (0), AE_PATH_WHOLE_CALL (1) or AE_PATH_PER_PHASE (2)."""
     act = AE_BF16 if w.dtype == "bf16" else AE_F32
     proj = AE_FP8_E4M3 if getattr(w, "proj_dtype", "same") == "fp8" else act
     return Config(w.n_layers, w.width, w.n_q_heads, w.n_kv_heads, w.head_dim, w.mlp_dim,
@@ -111,7 +113,7 @@ def make_config(w, max_batch: Optional[int] = None, max_prefix_len: Optional[int
                   int(graph_cache_size), int(bool(graph_cache_evict)), int(context_width), int(state_dim),
                   AE_BLOCK_DIT if getattr(w, "block", "joint") == "dit" else AE_BLOCK_JOINT,
                   int(proj == AE_FP8_E4M3 and getattr(w, "fp8_scaling", "tensor") == "rowwise"),
-                  int(proj == AE_FP8_E4M3 and bool(getattr(w, "fp8_o", False))))
+                  int(proj == AE_FP8_E4M3 and bool(getattr(w, "fp8_o", False))), int(exec_path))
 
 
 def _stream_ptr(stream) -> ctypes.c_void_p:

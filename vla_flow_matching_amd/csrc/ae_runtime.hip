@@ -229,6 +229,8 @@ std::string validate_config(const ae_config* c) {
     return "fp8_rowwise and fp8_oproj must be 0 or 1";
   if ((c->fp8_rowwise || c->fp8_oproj) && c->proj_weight_dtype != AE_FP8_E4M3)
     return "fp8_rowwise / fp8_oproj need proj_weight_dtype AE_FP8_E4M3";
+  if (c->exec_path < AE_PATH_AUTO || c->exec_path > AE_PATH_PER_PHASE)
+    return "exec_path must be AE_PATH_AUTO, AE_PATH_WHOLE_CALL or AE_PATH_PER_PHASE";
   return "";
 }
 
@@ -384,9 +386,25 @@ PersistPlans plan_persist(const ae_handle* h) {
 }
 
 // The whole-call kernel covers one 64-row tile and action_dim <= 32; other
-// shapes run the per-phase kernels.
+// shapes run the per-phase kernels.  Of the calls it covers, AE_PATH_AUTO
+// gives it those whose layer weights exceed the last-level cache: below
+// that the per-phase kernels find a step's weights still cached from the
+// previous step and win (measured per call, per-phase against whole-call:
+// MolmoBot-shaped expert, 208 MB of weights, 6.22 against 6.46 ms at batch
+// 1 and 7.16 against 8.63 at batch 4; Pi0.5-shaped at 6 layers, 207 MB, 3.96
+// against 4.01; Pi0.5-shaped, 623 MB, 12.70 against 11.54), while the
+// whole-call kernel's time per layer is its synchronisation either way.
+constexpr size_t kLastLevelCacheBytes = static_cast<size_t>(256) << 20;
+
+size_t layer_weight_bytes(const ae_handle* h) {
+  return static_cast<size_t>(h->L) * (h->sqkv + h->so + h->sgu + h->sd) * 16;
+}
+
 bool use_persist(const ae_handle* h, int batch) {
-  return h->G > 0 && !h->fp8 && !h->dit && batch * h->T <= kTileM && h->A <= 32;
+  if (!(h->G > 0 && !h->fp8 && !h->dit && batch * h->T <= kTileM && h->A <= 32)) return false;
+  if (h->cfg.exec_path == AE_PATH_WHOLE_CALL) return true;
+  if (h->cfg.exec_path == AE_PATH_PER_PHASE) return false;
+  return layer_weight_bytes(h) > kLastLevelCacheBytes;
 }
 
 // The batched tiled path: the four projection GEMMs of a layer.
