@@ -778,27 +778,33 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
   tg_epilogue<OP, EPI, norm_tpr<BM>(), true>(p, nt, m0, rows, s_y, s_r);
 }
 
-// Sum of a tile's K-split partials for kRedRows rows (in split order), then
-// the epilogue of those rows.  One workgroup per (tile, row slice).
-constexpr int kRedRows = 16;
+// Sum of a tile's K-split partials for RR rows (in split order), then the
+// epilogue of those rows.  One workgroup per (tile, RR-row slice): 16-row
+// slices where the tiles give enough of them, else 4-row slices, so that a
+// few-row product (one request: 16-50 rows) spreads its reduction over four
+// times the workgroups, each with a quarter of the partial bytes in flight.
+constexpr int kRedSlicesWanted = 256;  // 16-row slices that keep every CU busy
 
-template <int OP, int EPI, int BM>
+template <int OP, int EPI, int BM, int RR>
 __global__ __launch_bounds__(kTT) void tgemm_reduce_kernel(TGemmArgs p) {
-  __shared__ float s_y[kRedRows][kBN + 1];
-  __shared__ float s_r[kRedRows];
-  const int slices = BM / kRedRows;
+  static_assert(RR == 16 || RR == 4, "16- or 4-row slices");
+  __shared__ float s_y[RR][kBN + 1];
+  __shared__ float s_r[16];
+  constexpr int slices = BM / RR;
+  constexpr int NV = RR * kBN / 4;              // float4 of the slice
+  constexpr int U = (NV + kTT - 1) / kTT;       // per thread
   const int tile = blockIdx.x / slices, sl = blockIdx.x % slices;
   const int nt = tile / p.m_tiles, mt = tile % p.m_tiles;
-  const int m0 = mt * BM + sl * kRedRows;
-  const int rows = min(kRedRows, p.M - m0);
+  const int m0 = mt * BM + sl * RR;
+  const int rows = min(RR, p.M - m0);
   if (rows <= 0) return;
   const int tid = threadIdx.x;
-  const float* part = p.partial + static_cast<size_t>(tile) * p.ksplit * (BM * kBN) + sl * kRedRows * kBN;
-  // kRedRows x kBN floats = 512 float4, two per thread, every split in flight
-  float4 v[2][kMaxSplit];
+  const float* part = p.partial + static_cast<size_t>(tile) * p.ksplit * (BM * kBN) + sl * RR * kBN;
+  // every split of the thread's float4s in flight together
+  float4 v[U][kMaxSplit];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = tid + u * kTT;
+  for (int u = 0; u < U; ++u) {
+    const int i = min(tid + u * kTT, NV - 1);
     const int r = min(i / (kBN / 4), rows - 1), c4 = 4 * (i % (kBN / 4));
 #pragma unroll
     for (int q = 0; q < kMaxSplit; ++q)
@@ -806,8 +812,9 @@ __global__ __launch_bounds__(kTT) void tgemm_reduce_kernel(TGemmArgs p) {
                                                  r * kBN + c4);
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int i = tid + u * kTT;
+    if (i >= NV) continue;
     const int r = i / (kBN / 4), c4 = 4 * (i % (kBN / 4));
     float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -818,7 +825,9 @@ __global__ __launch_bounds__(kTT) void tgemm_reduce_kernel(TGemmArgs p) {
     s_y[r][c4] = t.x; s_y[r][c4 + 1] = t.y; s_y[r][c4 + 2] = t.z; s_y[r][c4 + 3] = t.w;
   }
   __syncthreads();
-  tg_epilogue<OP, EPI, kTT / kRedRows, false>(p, nt, m0, rows, s_y, s_r);
+  // (the post-norm row scales: 16 threads per row; past `rows` they repeat
+  // the last row and store nothing)
+  tg_epilogue<OP, EPI, 16, false>(p, nt, m0, rows, s_y, s_r);
 }
 
 // ---------------------------------------------------------------------------
@@ -1088,9 +1097,15 @@ hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a0, int blocks, h
       hipLaunchKernelGGL((tgemm_kernel<OPV, EPV, BMV, 2>), grid, block, 0, s, a);           \
     else                                                                                    \
       hipLaunchKernelGGL((tgemm_kernel<OPV, EPV, BMV, 1>), grid, block, 0, s, a);           \
-    if (a.ksplit > 1)                                                                       \
-      hipLaunchKernelGGL((tgemm_reduce_kernel<OPV, EPV, BMV>),                              \
-                         dim3(a.n_tiles * a.m_tiles * (BMV / kRedRows)), block, 0, s, a);   \
+    if (a.ksplit > 1) {                                                                     \
+      const int tiles = a.n_tiles * a.m_tiles;                                              \
+      if (tiles * ((a.M + 15) / 16) >= kRedSlicesWanted)                                    \
+        hipLaunchKernelGGL((tgemm_reduce_kernel<OPV, EPV, BMV, 16>), dim3(tiles * (BMV / 16)), \
+                           block, 0, s, a);                                                 \
+      else                                                                                  \
+        hipLaunchKernelGGL((tgemm_reduce_kernel<OPV, EPV, BMV, 4>), dim3(tiles * (BMV / 4)),   \
+                           block, 0, s, a);                                                 \
+    }                                                                                       \
     return hipGetLastError();                                                               \
   }
 #define AE_TG_BM(OPV, EPV) AE_TG(OPV, EPV, 64) AE_TG(OPV, EPV, 32)
