@@ -151,11 +151,13 @@ def inputs_of(name):
     return w, W, K, V, m, synth.make_noise(w)
 
 
-def run_gpu(name, calls, warmup, prefix_reps=0):
+def run_gpu(name, calls, warmup, prefix_reps=0, exec_path=0):
     """Time `calls` graph replays of one workload's denoise call (events on
     the library's stream around all of them), then the same number with an
     event pair per call (percentiles), then prefix ingest alone and ingest +
-    denoise.  Raises DeviceErrors if a whole-call kernel wait timed out."""
+    denoise.  exec_path: the library's choice (0) or a forced path (1
+    whole-call, 2 per-phase).  Raises DeviceErrors if a whole-call kernel
+    wait timed out."""
     import torch
 
     from vla_flow_matching_amd import binding
@@ -163,7 +165,7 @@ def run_gpu(name, calls, warmup, prefix_reps=0):
     w, W, K, V, m, x0 = inputs_of(name)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     res = {}
-    with binding.ActionExpert(binding.make_config(w)) as ex:
+    with binding.ActionExpert(binding.make_config(w, exec_path=exec_path)) as ex:
         ex.load_weights(binding.weights_to_device(W, w.dtype))
         del W
         Kt = torch.from_numpy(K).to("cuda", dt)
@@ -504,6 +506,17 @@ def main():
                         "can run above the HBM bound (and the library runs it on the per-phase kernels, "
                         "which find a step's weights still cached); reported against 8 TB/s")
         line["workloads"] = others
+        if args.others != "none":
+            # the same call on the path the library did not choose (the
+            # evidence for its choice; a short run)
+            def other_path(name, chosen_calls):
+                alt = 2 if chosen_calls > 0 else 1
+                ro = run_gpu(name, 10, 2, 0, exec_path=alt)
+                return {"path": "per-phase kernels" if alt == 2 else "whole-call kernel", "ms_per_call": ro["ms"],
+                        "persistent_calls": ro["stats"]["persistent_calls"]}
+            line["other_path"] = other_path(args.workload, r["stats"]["persistent_calls"])
+            if "c4" in others:
+                others["c4"]["other_path"] = other_path("c4", others["c4"]["persistent_calls"])
         if args.others != "none" and not args.no_prepare:
             line["context_preparation"] = run_prepare(20)
         if "c5" in others:
