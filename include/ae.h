@@ -162,7 +162,8 @@ typedef struct {
   long long device_bytes;    /* bytes the handle holds on the device */
   long long device_errors;   /* whole-call launches whose waits timed out (their results are
                                 invalid); counted on the device, read by ae_get_stats */
-  long long persistent;      /* workgroups of the whole-call kernel used when batch*T <= 64; 0: none */
+  long long persistent;      /* workgroups of the whole-call kernel (for calls that take it, see
+                                ae_path); 0: the device cannot run it */
   long long persistent_calls;/* denoise calls that ran the whole-call kernel */
   long long graph_hits;      /* calls replayed from the graph cache */
   long long graph_misses;    /* calls whose signature was not cached (captured, or run directly) */
