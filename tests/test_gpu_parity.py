@@ -306,6 +306,29 @@ def test_whole_call_kernel_several_requests(name, batch):
         assert err <= tol
 
 
+@pytest.mark.parametrize("name,fields", [
+    ("c2fp8r", dict(n_layers=2, n_steps=2)),              # fp8 projections
+    ("c4dit", dict(n_layers=2, n_steps=2)),               # the DiT-style block
+    ("c4", dict(batch=5, n_layers=2, n_steps=2)),         # 80 action rows
+])
+def test_whole_call_request_outside_its_reach(name, fields):
+    """A handle that asks for the whole-call kernel runs the per-phase kernels
+    for calls the whole-call kernel does not cover (fp8, the DiT block, more
+    than 64 action rows): bitwise the same actions as the library's own
+    choice, and no whole-call launch."""
+    _need_gpu()
+    w = synth.workload(name, **fields)
+    say(f"[case] exec_path whole-call on {name} {fields}: the per-phase kernels")
+    W = synth.make_weights(w)
+    m = synth.valid_masks(w)
+    K, V, _ = synth.make_prefix(w, mask=m)
+    x0 = synth.make_noise(w)
+    forced, auto = Gpu(w, W, exec_path=WHOLE_CALL), Gpu(w, W, exec_path=AUTO)
+    a, b = forced.run(K, V, m, x0), auto.run(K, V, m, x0)
+    assert forced.ex.stats()["persistent_calls"] == 0
+    assert np.array_equal(a, b)
+
+
 def test_graph_cache_lru_and_capacity(c2small):
     """The bounded graph cache (sglang PR summary, items 3 and 5): capacity 2
     with eviction keeps the two most recently used signatures, evicts the
