@@ -779,10 +779,11 @@ __global__ __launch_bounds__(kTT, 2) void tgemm_kernel(TGemmArgs p) {
 }
 
 // Sum of a tile's K-split partials for RR rows (in split order), then the
-// epilogue of those rows.  One workgroup per (tile, RR-row slice): 16-row
-// slices where the tiles give enough of them, else 4-row slices, so that a
-// few-row product (one request: 16-50 rows) spreads its reduction over four
-// times the workgroups, each with a quarter of the partial bytes in flight.
+// epilogue of those rows.  One workgroup per (tile, RR-row slice): 4-row
+// slices for products of at most 64 rows (one request: 16-50 rows) and
+// wherever 16-row slices would leave CUs idle, so the reduction spreads over
+// four times the workgroups, each with a quarter of the partial bytes in
+// flight; 16-row slices otherwise.
 constexpr int kRedSlicesWanted = 256;  // 16-row slices that keep every CU busy
 
 template <int OP, int EPI, int BM, int RR>
@@ -1099,7 +1100,7 @@ hipError_t launch_tgemm(int op, Epilogue epi, const TGemmArgs& a0, int blocks, h
       hipLaunchKernelGGL((tgemm_kernel<OPV, EPV, BMV, 1>), grid, block, 0, s, a);           \
     if (a.ksplit > 1) {                                                                     \
       const int tiles = a.n_tiles * a.m_tiles;                                              \
-      if (tiles * ((a.M + 15) / 16) >= kRedSlicesWanted)                                    \
+      if (a.M > 64 && tiles * ((a.M + 15) / 16) >= kRedSlicesWanted)                        \
         hipLaunchKernelGGL((tgemm_reduce_kernel<OPV, EPV, BMV, 16>), dim3(tiles * (BMV / 16)), \
                            block, 0, s, a);                                                 \
       else                                                                                  \
