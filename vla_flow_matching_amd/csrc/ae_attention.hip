@@ -184,8 +184,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnArgs p) {
   const int lane = threadIdx.x % kWave;
   const int grp = lane / 16;
   const int len = p.n_valid[b] + p.n_act;
-  const int k_begin = s * p.kc_len;
-  const int k_end = min(k_begin + p.kc_len, len);
+  // the request's own keys spread evenly over the splits, in whole key
+  // blocks (the plan's kc_len covers the bucket's largest request: a
+  // request with fewer visible keys gets shorter splits, not empty ones)
+  const int kc = min(p.kc_len, ((len + p.nsplit - 1) / p.nsplit + KSTEP - 1) / KSTEP * KSTEP);
+  const int k_begin = s * kc;
+  const int k_end = min(k_begin + kc, len);
   const int n_blk = k_end > k_begin ? (k_end - k_begin + KSTEP - 1) / KSTEP : 0;
 
   const T* Kb = static_cast<const T*>(p.kcache) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;

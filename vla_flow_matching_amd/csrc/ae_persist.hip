@@ -614,8 +614,11 @@ __device__ __forceinline__ void attention_phase(KArgs& p, const void* kc_l, cons
     // cached and the coherent K/V path a scalar branch
     const int nv = __builtin_amdgcn_readfirstlane(p.n_valid[b]);
     const int len = nv + p.T;
-    const int k_begin = s * p.kc_len;
-    const int k_end = min(k_begin + p.kc_len, len);
+    // the request's own keys spread evenly over the splits, in whole key
+    // blocks (kc_len covers the bucket's largest request)
+    const int kc = min(p.kc_len, ((len + p.nsplit - 1) / p.nsplit + KSTEP - 1) / KSTEP * KSTEP);
+    const int k_begin = s * kc;
+    const int k_end = min(k_begin + kc, len);
     const int n_blk = k_end > k_begin ? (k_end - k_begin + KSTEP - 1) / KSTEP : 0;
     const T* Kb = static_cast<const T*>(kc_l) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
     const T* Vb = static_cast<const T*>(vt_l) + static_cast<size_t>(b * p.Hkv + g) * p.S_max * DH;
