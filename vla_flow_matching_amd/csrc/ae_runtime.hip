@@ -389,11 +389,11 @@ PersistPlans plan_persist(const ae_handle* h) {
 // shapes run the per-phase kernels.  Of the calls it covers, AE_PATH_AUTO
 // gives it those whose layer weights exceed the last-level cache: below
 // that the per-phase kernels find a step's weights still cached from the
-// previous step and win (measured per call, per-phase against whole-call:
-// MolmoBot-shaped expert, 208 MB of weights, 6.22 against 6.46 ms at batch
-// 1 and 7.16 against 8.63 at batch 4; Pi0.5-shaped at 6 layers, 207 MB, 3.96
-// against 4.01; Pi0.5-shaped, 623 MB, 12.70 against 11.54), while the
-// whole-call kernel's time per layer is its synchronisation either way.
+// previous step and win (the MolmoBot-shaped expert, 208 MB of weights, by
+// ~15 % at batch 1 and more at batch 4; the Pi0.5 shape cut to 6 layers,
+// 207 MB, by ~5 %), while above it the whole-call kernel wins (the Pi0.5
+// shape, 623 MB, by ~2-4 %): its time per layer is its synchronisation
+// chain whether the weights are cached or not.
 constexpr size_t kLastLevelCacheBytes = static_cast<size_t>(256) << 20;
 
 size_t layer_weight_bytes(const ae_handle* h) {
