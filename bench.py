@@ -386,7 +386,10 @@ def workload_line(name, r, bound):
          "latency_ms": {"p10": r["p10"], "p50": r["p50"], "p90": r["p90"]},
          "persistent_calls": r["stats"]["persistent_calls"],
          # the kernels the library chose for this workload (AE_PATH_AUTO)
-         "path": "whole-call kernel" if r["stats"]["persistent_calls"] > 0 else "per-phase kernels"}
+         "path": "whole-call kernel" if r["stats"]["persistent_calls"] > 0 else "per-phase kernels",
+         # launches in the call's graph (the whole-call kernel: a counter fill and itself)
+         "kernels_per_call": r["stats"]["graph_nodes"],
+         "kernels_per_step": r["stats"]["graph_nodes"] / w.n_steps}
     if bound == "hbm":
         gbs = b / (ms * 1e-3) / 1e9
         d["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -472,6 +475,7 @@ def main():
             "prefix_ingest": head.get("prefix_ingest"),
             "set_plus_denoise_ms": head.get("set_plus_denoise_ms"),
             "path": head["path"],
+            "kernels_per_call": head["kernels_per_call"],
             "roofline": {
                 "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS,

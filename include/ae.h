@@ -170,6 +170,8 @@ typedef struct {
   long long graph_evictions; /* graphs evicted to make room */
   long long graphs_cached;   /* graphs in the cache now */
   long long prefix_bucket;   /* key span (prefix bucket) of the last ae_set_prefix_kv */
+  long long graph_nodes;     /* nodes (kernel launches) of the graph the last ae_denoise call
+                                replayed; 0 if it ran directly */
 } ae_stats;
 
 /* Validate the config, then allocate every device buffer the handle will

@@ -54,7 +54,8 @@ class Stats(ctypes.Structure):
                 ("device_errors", ctypes.c_longlong), ("persistent", ctypes.c_longlong),
                 ("persistent_calls", ctypes.c_longlong), ("graph_hits", ctypes.c_longlong),
                 ("graph_misses", ctypes.c_longlong), ("graph_evictions", ctypes.c_longlong),
-                ("graphs_cached", ctypes.c_longlong), ("prefix_bucket", ctypes.c_longlong)]
+                ("graphs_cached", ctypes.c_longlong), ("prefix_bucket", ctypes.c_longlong),
+                ("graph_nodes", ctypes.c_longlong)]
 
 
 class AeError(RuntimeError):

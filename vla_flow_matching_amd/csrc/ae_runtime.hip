@@ -46,6 +46,7 @@ constexpr int kPersistMaxSplits = 16;
 struct GraphEntry {
   hipGraphExec_t exec = nullptr;
   hipEvent_t done = nullptr;
+  size_t nodes = 0;  // of the captured graph
 };
 
 
@@ -1594,6 +1595,7 @@ ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, flo
         hipGraph_t graph = nullptr;
         hipError_t e = hipStreamEndCapture(h->cap_stream, &graph);
         GraphEntry ne;
+        if (s == AE_OK && e == hipSuccess) e = hipGraphGetNodes(graph, nullptr, &ne.nodes);
         if (s == AE_OK && e == hipSuccess) e = hipGraphInstantiate(&ne.exec, graph, nullptr, nullptr, 0);
         if (graph) (void)hipGraphDestroy(graph);
         if (s == AE_OK && e == hipSuccess) e = hipEventCreateWithFlags(&ne.done, hipEventDisableTiming);
@@ -1617,6 +1619,7 @@ ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, flo
       AE_HIP(h, hipGraphLaunch(ge->exec, st));
       AE_HIP(h, hipEventRecord(ge->done, st));
       h->stats.graph_replays++;
+      h->stats.graph_nodes = static_cast<long long>(ge->nodes);
       ran = true;
     }
   }
@@ -1624,6 +1627,7 @@ ae_status ae_denoise(ae_handle* h, const float* noise, int batch, int steps, flo
     ae_status s = enqueue(st);
     if (s != AE_OK) return s;
     h->stats.eager_runs++;
+    h->stats.graph_nodes = 0;
   }
   if (persist) h->stats.persistent_calls++;
   AE_HIP(h, hipMemcpyAsync(actions_out, h->x, xbytes, hipMemcpyDeviceToDevice, st));
@@ -1671,6 +1675,7 @@ ae_status ae_denoise_static(ae_handle* h, const float* noise, int batch, int ste
   }
   AE_HIP(h, hipMemcpyAsync(actions_out, h->x, xbytes, hipMemcpyDeviceToDevice, st));
   h->stats.eager_runs++;
+  h->stats.graph_nodes = 0;
   h->stats.denoise_calls++;
   return AE_OK;
 }
