@@ -225,3 +225,34 @@ def test_bench_refuses_to_report_after_device_errors(monkeypatch, capsys):
     assert e.value.code == 3
     out = capsys.readouterr()
     assert '"metric"' not in out.out and "timed out" in out.err
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The ctypes mirrors of ae_config, ae_tensor_view and ae_stats have the
+    C header's size and field offsets (a shorter Stats would let
+    ae_get_stats write past the Python buffer)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"ae_config": binding.Config, "ae_tensor_view": binding.TensorView, "ae_stats": binding.Stats}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "ae.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([cc, "-I", os.path.join(root, "include"), str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
