@@ -651,6 +651,11 @@ def test_graph_equals_direct_launch(c2small):
     direct = Gpu(w, W, max_prefix_len=1018, max_steps=4, use_graphs=False, exec_path=g.exec_path)
     assert np.array_equal(g.run(K, V, m, x0), direct.run(K, V, m, x0))
     assert direct.ex.stats()["graph_captures"] == 0
+    # launches in the replayed graph: the whole-call kernel and its counter
+    # fill, or several per layer; none reported for direct launches
+    nodes = g.ex.stats()["graph_nodes"]
+    assert nodes == 2 if g.ex.stats()["persistent_calls"] > 0 else nodes > 2 * w.n_layers * w.n_steps
+    assert direct.ex.stats()["graph_nodes"] == 0
 
 
 # --------------------------------------------------------------------------
